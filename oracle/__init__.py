@@ -1,0 +1,194 @@
+"""CPU oracle for the binarized linear / conv2d forward (ctypes wrapper).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg may use this package; the product path never does. The
+arithmetic lives in ``bnn_oracle.c`` (plain C loops, OpenMP), built with gcc
+into ``liboracle.so`` beside it. It shares no code with the HIP library.
+
+Every function takes contiguous CPU torch tensors and returns CPU tensors.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "bnn_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+# x86-64-v3 (AVX2/FMA) so the library also runs on other x86 hosts; never fast-math:
+# the sign rule relies on IEEE compares of NaN, -0 and subnormals.
+_CFLAGS = ["-O2", "-march=x86-64-v3", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+           "-Wall", "-Wextra", "-Wno-unused-parameter"]
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so with gcc; returns its path."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.run(["gcc", *_CFLAGS, _SRC, "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        lib.oracle_num_threads.restype = I
+        lib.oracle_sign.argtypes = [P, I, I64, P]
+        lib.oracle_pack_rows.argtypes = [P, I, I64, I64, P]
+        lib.oracle_pack_nchw.argtypes = [P, I, I64, I64, I64, I64, P]
+        lib.oracle_pack_conv_weight.argtypes = [P, I, I64, I64, I64, P]
+        lib.oracle_linear_acc.argtypes = [P, I, P, I, I64, I64, I64, P, I64, P]
+        lib.oracle_linear_acc.restype = I
+        lib.oracle_conv_out_size.argtypes = [I64, I64, I64, I64, I64]
+        lib.oracle_conv_out_size.restype = I64
+        lib.oracle_conv2d_acc.argtypes = [P, I, P, I, I64, I64, I64, I64, I64, I64, I64, I64,
+                                          I64, P, I64, P]
+        lib.oracle_conv2d_acc.restype = I
+        lib.oracle_conv2d_kvalid.argtypes = [I64, I64, I64, I64, I64, I64, I64, P]
+        lib.oracle_conv2d_kvalid.restype = I
+        lib.oracle_scale.argtypes = [P, I64, ctypes.c_double, ctypes.c_double, P]
+        _lib = lib
+    return _lib
+
+
+_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+
+
+def _code(t: torch.Tensor) -> int:
+    if t.dtype not in _CODE:
+        raise TypeError(f"oracle: unsupported dtype {t.dtype}")
+    return _CODE[t.dtype]
+
+
+def _cpu(t: torch.Tensor) -> torch.Tensor:
+    if t.device.type != "cpu" or not t.is_contiguous():
+        raise ValueError("oracle: inputs must be contiguous CPU tensors")
+    return t
+
+
+def num_threads() -> int:
+    return _load().oracle_num_threads()
+
+
+def sign(x: torch.Tensor) -> torch.Tensor:
+    """sgn(x) as float32 +-1 (x >= 0 -> +1, else -1), same shape as x."""
+    x = _cpu(x)
+    out = torch.empty(x.shape, dtype=torch.float32)
+    _load().oracle_sign(x.data_ptr(), _code(x), x.numel(), out.data_ptr())
+    return out
+
+
+def _words(n: int) -> torch.Tensor:
+    return torch.empty(n, dtype=torch.int32)
+
+
+def pack_rows(x: torch.Tensor) -> torch.Tensor:
+    """x [rows, k] -> int32 words [rows, k/32] (bit j of word q = x[r, 32q+j] >= 0)."""
+    x = _cpu(x)
+    rows, k = x.shape
+    assert k % 32 == 0
+    out = _words(rows * (k // 32))
+    _load().oracle_pack_rows(x.data_ptr(), _code(x), rows, k, out.data_ptr())
+    return out.view(rows, k // 32)
+
+
+def pack_nchw(x: torch.Tensor) -> torch.Tensor:
+    """x [b, c, h, w] -> int32 words [b, h, w, c/32]."""
+    x = _cpu(x)
+    b, c, h, w = x.shape
+    assert c % 32 == 0
+    out = _words(b * h * w * (c // 32))
+    _load().oracle_pack_nchw(x.data_ptr(), _code(x), b, c, h, w, out.data_ptr())
+    return out.view(b, h, w, c // 32)
+
+
+def pack_conv_weight(w: torch.Tensor) -> torch.Tensor:
+    """OIHW w [o, c, k, k] -> int32 words [o, k, k, c/32]."""
+    w = _cpu(w)
+    o, c, kh, kw = w.shape
+    assert kh == kw and c % 32 == 0
+    out = _words(o * kh * kw * (c // 32))
+    _load().oracle_pack_conv_weight(w.data_ptr(), _code(w), o, c, kh, out.data_ptr())
+    return out.view(o, kh, kw, c // 32)
+
+
+def _index(idx, limit):
+    if idx is None:
+        return None, limit
+    t = torch.as_tensor(list(idx), dtype=torch.int64).contiguous()
+    if t.numel() and (int(t.min()) < 0 or int(t.max()) >= limit):
+        raise IndexError("oracle: index out of range")
+    return t, t.numel()
+
+
+def linear_acc(x: torch.Tensor, w: torch.Tensor, rows=None) -> torch.Tensor:
+    """int32 acc [len(rows) or M, N] = sum_k sgn(x[m,k]) * sgn(W[n,k])."""
+    x, w = _cpu(x), _cpu(w)
+    m, k = x.shape
+    n, k2 = w.shape
+    assert k == k2
+    idx, nr = _index(rows, m)
+    out = torch.empty((nr, n), dtype=torch.int32)
+    rc = _load().oracle_linear_acc(x.data_ptr(), _code(x), w.data_ptr(), _code(w), m, n, k,
+                                   idx.data_ptr() if idx is not None else None, nr,
+                                   out.data_ptr())
+    if rc != 0:
+        raise RuntimeError("oracle_linear_acc failed")
+    return out
+
+
+def conv_out_size(size, ks, stride, padding, dilation) -> int:
+    return int(_load().oracle_conv_out_size(size, ks, stride, padding, dilation))
+
+
+def conv2d_acc(x: torch.Tensor, w: torch.Tensor, stride: int, padding: int, dilation: int,
+               images=None) -> torch.Tensor:
+    """int32 acc [len(images) or B, O, Ho, Wo] of the zero-padded binary conv."""
+    x, w = _cpu(x), _cpu(w)
+    b, c, h, wd = x.shape
+    o, c2, ks, ks2 = w.shape
+    assert c == c2 and ks == ks2
+    ho = conv_out_size(h, ks, stride, padding, dilation)
+    wo = conv_out_size(wd, ks, stride, padding, dilation)
+    if ho <= 0 or wo <= 0:
+        raise ValueError("oracle: empty conv output")
+    idx, ni = _index(images, b)
+    out = torch.empty((ni, o, ho, wo), dtype=torch.int32)
+    rc = _load().oracle_conv2d_acc(x.data_ptr(), _code(x), w.data_ptr(), _code(w), b, c, h, wd, o,
+                                   ks, stride, padding, dilation,
+                                   idx.data_ptr() if idx is not None else None, ni,
+                                   out.data_ptr())
+    if rc != 0:
+        raise RuntimeError("oracle_conv2d_acc failed")
+    return out
+
+
+def conv2d_kvalid(c, h, w, ks, stride, padding, dilation) -> torch.Tensor:
+    """int32 [Ho, Wo]: number of real (unpadded) reduction terms per output pixel."""
+    ho = conv_out_size(h, ks, stride, padding, dilation)
+    wo = conv_out_size(w, ks, stride, padding, dilation)
+    out = torch.empty((ho, wo), dtype=torch.int32)
+    rc = _load().oracle_conv2d_kvalid(c, h, w, ks, stride, padding, dilation, out.data_ptr())
+    if rc != 0:
+        raise RuntimeError("oracle_conv2d_kvalid failed")
+    return out
+
+
+def scale(acc: torch.Tensor, scale_a: float, scale_w: float) -> torch.Tensor:
+    """float64 y = acc * (scale_a * scale_w)."""
+    acc = _cpu(acc)
+    assert acc.dtype == torch.int32
+    y = torch.empty(acc.shape, dtype=torch.float64)
+    _load().oracle_scale(acc.data_ptr(), acc.numel(), float(scale_a), float(scale_w), y.data_ptr())
+    return y

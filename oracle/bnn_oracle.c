@@ -1,0 +1,279 @@
+/*
+ * CPU oracle for the binarized linear and conv2d forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may link, load or
+ * call this file: only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg use it. It shares no code, header, table or constant with
+ * the HIP library; it is plain, slow and meant to be checked by eye.
+ *
+ * What it computes, and where that is defined:
+ *
+ *  - The sign rule: a value maps to +1 when it is >= 0 and to -1 otherwise.
+ *    The value is first widened exactly to float (fp16 and bf16 widen
+ *    exactly), then compared with an IEEE compare, so -0 maps to +1, NaN to
+ *    -1 (the compare is false), +-inf to +-1 and subnormals by their sign.
+ *    (Rule taken from the method's statement that x >= 0 maps to +1; the
+ *    bitorch-engine layer pages leave the sign step to their native kernel.)
+ *
+ *  - Bit packing: 32 sign bits per 32-bit word along the reduction axis,
+ *    bit j of word q holding element 32q + j, bit value 1 for +1 and 0 for
+ *    -1. (The layers pack weights once, ahead of the forward, with a native
+ *    bit-packing kernel: BinaryConv2dCutlass.generate_quantized_weight on
+ *    the qconv/binary/cutlass/layer page, BinaryLinearCuda.w_pack on the
+ *    BinaryLinearCuda page. The word width 32 and the bit order are this
+ *    build's reading; the pages fix neither.)
+ *
+ *  - Linear forward: acc[m][n] = sum_k sgn(x[m][k]) * sgn(W[n][k]), then
+ *    y = acc * (scale_a * scale_w). (BinaryLinearForward.forward on the
+ *    BinaryLinearForward page: the binary linear result scaled by the
+ *    activation and weight scaling factors; there is no bias term.)
+ *
+ *  - Conv2d forward, lowered as im2col + GEMM exactly in the order of the
+ *    banghao.live blog post, section 2 ("Implementation of im2col+gemm
+ *    operation", MyConv2d.forward): output size
+ *    Ho = floor((H + 2p - d(k-1) - 1)/s + 1), unfold into rows
+ *    r = c*k*k + kh*k + kw and columns l = oh*Wo + ow, transpose to [L, R],
+ *    multiply by the weight viewed as [O, C*k*k], reshape to [O, Ho, Wo].
+ *    Signs are taken BEFORE the zero padding, so a padded tap contributes 0.
+ *    The blog's unfold call omits the dilation although its output-size
+ *    formula uses it; the unfold here applies the dilation (the conv forward
+ *    on the qconv/binary/cutlass/layer page takes a dilation argument).
+ *    The scale product is the host-side product of the two scalar scales
+ *    (BinaryConv2dForward.forward on the qconv/binary/cutlass/layer page).
+ *
+ * Every accumulation is a sum of +-1 products; each partial sum is an
+ * integer of magnitude at most K < 2^24, so float accumulation is exact in
+ * any order (that is why the reductions may be vectorised).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <omp.h>
+
+/* Element types of the oracle's inputs (its own numbering). */
+#define ORACLE_F32 0
+#define ORACLE_F16 1
+#define ORACLE_BF16 2
+
+/* IEEE 754 binary16 -> binary32, exact, written from the format's definition:
+ * 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
+static float widen_f16(uint16_t h) {
+  int sign = h >> 15;
+  int e = (h >> 10) & 0x1f;
+  int frac = h & 0x3ff;
+  float v;
+  if (e == 0)
+    v = ldexpf((float)frac, -24);                 /* zero and subnormals: frac * 2^-24 */
+  else if (e == 31)
+    v = frac ? NAN : INFINITY;
+  else
+    v = ldexpf((float)(frac + 1024), e - 25);     /* (1 + frac/1024) * 2^(e-15) */
+  return sign ? -v : v;
+}
+
+/* bfloat16 is the upper half of a binary32: widening appends 16 zero bits. */
+static float widen_bf16(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return f;
+}
+
+static float widen(const void *x, int dtype, int64_t i) {
+  if (dtype == ORACLE_F32) return ((const float *)x)[i];
+  if (dtype == ORACLE_F16) return widen_f16(((const uint16_t *)x)[i]);
+  return widen_bf16(((const uint16_t *)x)[i]);
+}
+
+/* The sign rule: +1 for v >= 0, else -1. */
+static float sgn(float v) { return v >= 0.0f ? 1.0f : -1.0f; }
+
+int oracle_num_threads(void) { return omp_get_max_threads(); }
+
+/* s[i] = sgn(widen(x[i])) for i < count. */
+void oracle_sign(const void *x, int dtype, int64_t count, float *s) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < count; i++) s[i] = sgn(widen(x, dtype, i));
+}
+
+/* Row-major x[rows][k] -> words out[rows][k/32]; bit j of word q is 1 iff x[r][32q+j] >= 0. */
+void oracle_pack_rows(const void *x, int dtype, int64_t rows, int64_t k, uint32_t *out) {
+  int64_t kw = k / 32;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; r++)
+    for (int64_t q = 0; q < kw; q++) {
+      uint32_t word = 0;
+      for (int j = 0; j < 32; j++)
+        if (sgn(widen(x, dtype, r * k + 32 * q + j)) > 0.0f) word |= (uint32_t)1 << j;
+      out[r * kw + q] = word;
+    }
+}
+
+/* NCHW x[b][c][h][w] -> words out[b][h][w][c/32]; bit j of word q is 1 iff x[b][32q+j][h][w] >= 0. */
+void oracle_pack_nchw(const void *x, int dtype, int64_t B, int64_t C, int64_t H, int64_t W,
+                      uint32_t *out) {
+  int64_t cw = C / 32;
+#pragma omp parallel for schedule(static)
+  for (int64_t b = 0; b < B; b++)
+    for (int64_t ih = 0; ih < H; ih++)
+      for (int64_t iw = 0; iw < W; iw++)
+        for (int64_t q = 0; q < cw; q++) {
+          uint32_t word = 0;
+          for (int j = 0; j < 32; j++) {
+            int64_t idx = ((b * C + 32 * q + j) * H + ih) * W + iw;
+            if (sgn(widen(x, dtype, idx)) > 0.0f) word |= (uint32_t)1 << j;
+          }
+          out[((b * H + ih) * W + iw) * cw + q] = word;
+        }
+}
+
+/* OIHW weight w[o][c][kh][kw] -> words out[o][kh][kw][c/32]; bit j of word q is 1 iff w[o][32q+j][kh][kw] >= 0. */
+void oracle_pack_conv_weight(const void *w, int dtype, int64_t O, int64_t C, int64_t ks,
+                             uint32_t *out) {
+  int64_t cw = C / 32;
+#pragma omp parallel for schedule(static)
+  for (int64_t o = 0; o < O; o++)
+    for (int64_t kh = 0; kh < ks; kh++)
+      for (int64_t kx = 0; kx < ks; kx++)
+        for (int64_t q = 0; q < cw; q++) {
+          uint32_t word = 0;
+          for (int j = 0; j < 32; j++) {
+            int64_t idx = ((o * C + 32 * q + j) * ks + kh) * ks + kx;
+            if (sgn(widen(w, dtype, idx)) > 0.0f) word |= (uint32_t)1 << j;
+          }
+          out[((o * ks + kh) * ks + kx) * cw + q] = word;
+        }
+}
+
+/* Linear accumulators. acc[i][n] = sum_k sgn(x[m_i][k]) * sgn(W[n][k]) for the selected rows
+ * m_i = rows[i] (all M rows in order when rows == NULL, nrows then ignored). Returns 0, or -1
+ * when K is too long for the exact float accumulation or memory runs out. */
+int oracle_linear_acc(const void *x, int xdt, const void *w, int wdt, int64_t M, int64_t N,
+                      int64_t K, const int64_t *rows, int64_t nrows, int32_t *acc) {
+  if (K >= (1 << 24)) return -1;
+  if (!rows) nrows = M;
+  float *sw = (float *)malloc(sizeof(float) * (size_t)(N * K));
+  if (!sw) return -1;
+  oracle_sign(w, wdt, N * K, sw);
+  int fail = 0;
+#pragma omp parallel
+  {
+    float *sx = (float *)malloc(sizeof(float) * (size_t)K);
+    if (!sx) {
+#pragma omp atomic write
+      fail = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t i = 0; i < nrows; i++) {
+      if (!sx) continue;
+      int64_t m = rows ? rows[i] : i;
+      for (int64_t k = 0; k < K; k++) sx[k] = sgn(widen(x, xdt, m * K + k));
+      for (int64_t n = 0; n < N; n++) {
+        const float *wr = sw + n * K;
+        float s = 0.0f;
+#pragma omp simd reduction(+ : s)
+        for (int64_t k = 0; k < K; k++) s += sx[k] * wr[k];
+        acc[i * N + n] = (int32_t)s;
+      }
+    }
+    free(sx);
+  }
+  free(sw);
+  return fail ? -1 : 0;
+}
+
+/* Output extent: floor((size + 2p - d(ks-1) - 1)/s + 1), with a true floor for negative numerators. */
+int64_t oracle_conv_out_size(int64_t size, int64_t ks, int64_t s, int64_t p, int64_t d) {
+  int64_t num = size + 2 * p - d * (ks - 1) - 1;
+  int64_t q = num / s;
+  if (num % s != 0 && num < 0) q -= 1;
+  return q + 1;
+}
+
+/* Conv accumulators via zero-padded unfold + GEMM, for the selected images b_i = imgs[i]
+ * (all B in order when imgs == NULL). acc[i][o][oh][ow]. Returns 0, or -1 on a bad shape
+ * or when memory runs out. */
+int oracle_conv2d_acc(const void *x, int xdt, const void *w, int wdt, int64_t B, int64_t C,
+                      int64_t H, int64_t W, int64_t O, int64_t ks, int64_t s, int64_t p, int64_t d,
+                      const int64_t *imgs, int64_t nimgs, int32_t *acc) {
+  int64_t Ho = oracle_conv_out_size(H, ks, s, p, d);
+  int64_t Wo = oracle_conv_out_size(W, ks, s, p, d);
+  if (Ho <= 0 || Wo <= 0 || s < 1 || d < 1 || p < 0 || ks < 1) return -1;
+  int64_t R = C * ks * ks, L = Ho * Wo, Hp = H + 2 * p, Wp = W + 2 * p;
+  if (R >= (1 << 24)) return -1;
+  if (!imgs) nimgs = B;
+
+  /* weight viewed as [O, C*k*k] over the OIHW order, signed */
+  float *ws = (float *)malloc(sizeof(float) * (size_t)(O * R));
+  float *xp = (float *)malloc(sizeof(float) * (size_t)(C * Hp * Wp));
+  float *cols = (float *)malloc(sizeof(float) * (size_t)(L * R));
+  if (!ws || !xp || !cols) {
+    free(ws); free(xp); free(cols);
+    return -1;
+  }
+  oracle_sign(w, wdt, O * R, ws);
+
+  for (int64_t i = 0; i < nimgs; i++) {
+    int64_t b = imgs ? imgs[i] : i;
+    /* sign, then zero-pad by p on each side */
+    memset(xp, 0, sizeof(float) * (size_t)(C * Hp * Wp));
+#pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < C; c++)
+      for (int64_t ih = 0; ih < H; ih++)
+        for (int64_t iw = 0; iw < W; iw++)
+          xp[(c * Hp + ih + p) * Wp + iw + p] = sgn(widen(x, xdt, ((b * C + c) * H + ih) * W + iw));
+    /* unfold with kernel ks, dilation d, stride s, stored transposed as cols[l][r] */
+#pragma omp parallel for schedule(static)
+    for (int64_t l = 0; l < L; l++) {
+      int64_t oh = l / Wo, ow = l % Wo;
+      for (int64_t c = 0; c < C; c++)
+        for (int64_t kh = 0; kh < ks; kh++)
+          for (int64_t kx = 0; kx < ks; kx++) {
+            int64_t r = (c * ks + kh) * ks + kx;
+            cols[l * R + r] = xp[(c * Hp + oh * s + kh * d) * Wp + ow * s + kx * d];
+          }
+    }
+    /* [L, R] x [R, O] -> [L, O], written transposed as [O, Ho, Wo] */
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t o = 0; o < O; o++)
+      for (int64_t l = 0; l < L; l++) {
+        const float *wr = ws + o * R, *cr = cols + l * R;
+        float sum = 0.0f;
+#pragma omp simd reduction(+ : sum)
+        for (int64_t r = 0; r < R; r++) sum += cr[r] * wr[r];
+        acc[(i * O + o) * L + l] = (int32_t)sum;
+      }
+  }
+  free(ws);
+  free(xp);
+  free(cols);
+  return 0;
+}
+
+/* Number of real (unpadded) reduction terms per output pixel:
+ * kv[oh][ow] = C * #{(kh,kw) : 0 <= oh*s - p + kh*d < H and 0 <= ow*s - p + kw*d < W}. */
+int oracle_conv2d_kvalid(int64_t C, int64_t H, int64_t W, int64_t ks, int64_t s, int64_t p,
+                         int64_t d, int32_t *kv) {
+  int64_t Ho = oracle_conv_out_size(H, ks, s, p, d);
+  int64_t Wo = oracle_conv_out_size(W, ks, s, p, d);
+  if (Ho <= 0 || Wo <= 0) return -1;
+  for (int64_t oh = 0; oh < Ho; oh++)
+    for (int64_t ow = 0; ow < Wo; ow++) {
+      int64_t taps = 0;
+      for (int64_t kh = 0; kh < ks; kh++)
+        for (int64_t kx = 0; kx < ks; kx++) {
+          int64_t ih = oh * s - p + kh * d, iw = ow * s - p + kx * d;
+          if (ih >= 0 && ih < H && iw >= 0 && iw < W) taps++;
+        }
+      kv[oh * Wo + ow] = (int32_t)(C * taps);
+    }
+  return 0;
+}
+
+/* y[i] = acc[i] * (scale_a * scale_w), the product of the two scalar scales taken in double. */
+void oracle_scale(const int32_t *acc, int64_t count, double scale_a, double scale_w, double *y) {
+  double alpha = scale_a * scale_w;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < count; i++) y[i] = (double)acc[i] * alpha;
+}
