@@ -1,0 +1,242 @@
+#!/usr/bin/env python3
+"""Throughput of the binary linear / conv2d forward on one MI355X.
+
+One step = one forward pass over one batch of synthetic input with the
+weights already packed (the layers pack weights once, ahead of the forward):
+activation sign+pack, then the binary contraction with its fused scale and
+output-cast epilogue. The default workload is the 2048 x 4096 x 4096
+LLM-shaped binary linear layer with fp16 activations and output.
+
+Prints ONE JSON line: binary TOPS (2*M*N*K per second; for conv M = batch*Ho*Wo,
+N = out channels, K = C*k*k), the dominant kernel's roofline (average
+duration from HIP events recorded around it on its own stream inside the
+timed region) and the CPU oracle's throughput on the host as a baseline.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--path auto|xor|mfma]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0           # HBM3E, MI355X
+PEAK_MFMA_I8_TOPS = 5000.0      # dense int8 MFMA, MI355X
+# XOR path: 256 CUs x 64 lanes x 2.4 GHz lane-ops; one v_xor_b32 + one v_bcnt_u32_b32
+# cover 32 MACs = 64 binary ops, i.e. 32 binary ops per lane-op.
+PEAK_VALU_BINARY_TOPS = 256 * 64 * 2.4e9 * 32 / 1e12
+
+DEFAULT_WORKLOAD = "linear_2048x4096x4096_f16"
+PACK_WORKLOAD = "pack_linear_16384x8192_bf16"
+KERNEL_SOURCES = {"mfma": "gemm_mfma.hip", "xor": "gemm_xor.hip", "pack": "pack.hip"}
+KERNEL_NAMES = {"mfma": "mfma_kernel", "xor": "xor_kernel", "pack": "pack_rows_kernel"}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def src_sha(kind):
+    path = os.path.join(ROOT, "convolution_bnn_pack_amd", "csrc", KERNEL_SOURCES[kind])
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def traffic_for(kind, workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None when absent or
+    when the kernel source has changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(f"{KERNEL_NAMES[kind]}|{workload}")
+    if not rec or rec.get("src_sha") != src_sha(kind):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, x, w):
+    """The oracle as it stands on the host cores: the whole workload when it takes under
+    about 30 s, else a row / image sample sized for ~15 s, scaled to binary TOPS."""
+    import oracle
+    cores = oracle.num_threads()
+    if wl.kind == "linear":
+        probe = max(1, min(wl.m, 8))
+        t0 = time.perf_counter()
+        oracle.linear_acc(x, w, rows=range(probe))
+        t_probe = time.perf_counter() - t0
+        rows = wl.m if t_probe / probe * wl.m < 30 else max(probe, int(15 / (t_probe / probe)))
+        t0 = time.perf_counter()
+        acc = oracle.linear_acc(x, w, rows=None if rows == wl.m else range(rows))
+        oracle.scale(acc, 1.0, 1.0)
+        dt = time.perf_counter() - t0
+        ops = 2.0 * rows * wl.n * wl.k
+        sample = "whole workload" if rows == wl.m else f"first {rows} of {wl.m} rows"
+    else:
+        t0 = time.perf_counter()
+        oracle.conv2d_acc(x, w, wl.stride, wl.padding, wl.dilation, images=[0])
+        t_img = time.perf_counter() - t0
+        imgs = wl.batch if t_img * wl.batch < 30 else max(1, int(15 / t_img))
+        t0 = time.perf_counter()
+        acc = oracle.conv2d_acc(x, w, wl.stride, wl.padding, wl.dilation,
+                                images=None if imgs == wl.batch else range(imgs))
+        oracle.scale(acc, 1.0, 1.0)
+        dt = time.perf_counter() - t0
+        m, n, k = wl.gemm_mnk()
+        ops = 2.0 * (m // wl.batch) * imgs * n * k
+        sample = "whole workload" if imgs == wl.batch else f"first {imgs} of {wl.batch} images"
+    return {"value": round(ops / dt / 1e12, 6), "unit": "binary TOPS", "cores": cores,
+            "kind": "oracle", "sample": f"{sample} ({dt:.2f} s, sign + contraction + scale)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--path", default="auto", choices=["auto", "xor", "mfma"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the binary forward has no "
+              f"cross-GPU exchange here; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import convolution_bnn_pack_amd as bnn
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pack_only = args.workload == PACK_WORKLOAD
+    wl = synth.WORKLOADS["linear_16384x8192x8192_bf16" if pack_only else args.workload]
+    log(f"workload {args.workload}: generating inputs")
+    x, w, sa, sw = synth.make_inputs(wl, draw_weight=not pack_only)
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+    xd = x.to(dev)
+    lib = bnn.lib
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    xcode = bnn._DT[xd.dtype]
+
+    if pack_only:
+        # two copies of the 268 MB activation, alternated, so every pass reads HBM rather than
+        # the 256 MB last-level cache
+        xs = [xd, xd.clone()]
+        words = wl.m * wl.k // 32
+        xp = torch.empty((wl.m, wl.k // 32), dtype=torch.int32, device=dev)
+        ops = None
+        bytes_per = wl.m * wl.k * 2 + words * 4
+        path_used = None
+
+        def launches(i):
+            return [lambda: lib.bnn_pack_sign(xs[i & 1].data_ptr(), xcode, wl.m, wl.k, xp.data_ptr(),
+                                              stream)]
+    else:
+        wp = bnn.w_pack(w.to(dev))
+        m, n, k = wl.gemm_mnk()
+        ops = 2.0 * m * n * k
+        path = bnn._PATHS[args.path]
+        out = torch.empty(wl.out_shape(), dtype=tdt[wl.out_dtype], device=dev)
+        ocode = bnn._DT[out.dtype]
+        if wl.kind == "linear":
+            xp = torch.empty((wl.m, wl.k // 32), dtype=torch.int32, device=dev)
+            pack = lambda i: lib.bnn_pack_sign(xd.data_ptr(), xcode, wl.m, wl.k, xp.data_ptr(), stream)
+            core = lambda i: lib.bnn_gemm(xp.data_ptr(), bnn.U32_PACKED, wp.data_ptr(), wl.m, wl.n, wl.k,
+                                          sa, sw, path, out.data_ptr(), ocode, None, 0, stream)
+            path_used = path if path else bnn.gemm_auto_path(wl.m, wl.n, wl.k)
+        else:
+            xp = torch.empty((wl.batch, wl.h, wl.w, wl.c // 32), dtype=torch.int32, device=dev)
+            pack = lambda i: lib.bnn_pack_sign_nchw(xd.data_ptr(), xcode, wl.batch, wl.c, wl.h, wl.w,
+                                                    xp.data_ptr(), stream)
+            core = lambda i: lib.bnn_conv2d(xp.data_ptr(), bnn.U32_PACKED, wl.batch, wl.c, wl.h, wl.w,
+                                            wp.data_ptr(), wl.o, sa, sw, wl.ks, wl.stride, wl.padding,
+                                            wl.dilation, path, out.data_ptr(), ocode, None, 0, stream)
+            path_used = path if path else bnn.conv2d_auto_path(wl.batch, wl.c, wl.h, wl.w, wl.o, wl.ks,
+                                                               wl.stride, wl.padding, wl.dilation)
+
+        def launches(i):
+            return [lambda: pack(i), lambda: core(i)]
+
+    # parity spot check before timing (int32 accumulators of sampled rows / images vs the oracle)
+    parity = None
+    if not pack_only:
+        import oracle
+        if wl.kind == "linear":
+            rows = sorted({0, 1, wl.m // 2, wl.m - 1})
+            ref = oracle.linear_acc(x, w, rows=rows)
+            got = bnn.gemm(xd, wp, 1.0, 1.0, path=args.path, out_dtype=torch.int32)[rows].cpu()
+        else:
+            imgs = sorted({0, wl.batch - 1})
+            ref = oracle.conv2d_acc(x, w, wl.stride, wl.padding, wl.dilation, images=imgs)
+            got = bnn.conv2d(xd, wp, 1.0, 1.0, wl.ks, wl.stride, wl.padding, wl.dilation,
+                             path=args.path, out_dtype=torch.int32)[imgs].cpu()
+        parity = bool(torch.equal(got, ref))
+        log(f"parity spot check vs oracle: {parity}")
+
+    nk = 1 if pack_only else 2
+    for i in range(args.warmup):
+        for f in launches(i):
+            assert f() == 0
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        fs = launches(i)
+        for j, f in enumerate(fs):
+            ev[i][j].record()
+            assert f() == 0
+        ev[i][nk].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)) / args.steps
+               for j in range(nk)]
+    ms_per_step = wall * 1e3 / args.steps
+
+    if pack_only:
+        dom_ms = kern_ms[0]
+        achieved = bytes_per / (dom_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic_for("pack", args.workload),
+                "kernel": KERNEL_NAMES["pack"], "kernel_ms": round(dom_ms, 5)}
+        value = bytes_per / (ms_per_step * 1e-3) / 1e9
+        metric, unit, dtype = "sign+pack bandwidth", "GB/s", "u32"
+    else:
+        dom_ms = kern_ms[1]
+        kind = "mfma" if path_used == bnn.PATH_MFMA else "xor"
+        achieved = ops / (dom_ms * 1e-3) / 1e12
+        peak = PEAK_MFMA_I8_TOPS if kind == "mfma" else PEAK_VALU_BINARY_TOPS
+        roof = {"bound": "mfma" if kind == "mfma" else "alu", "achieved": round(achieved, 2),
+                "peak": round(peak, 1), "unit": "TOP/s", "frac": round(achieved / peak, 4),
+                "traffic": traffic_for(kind, args.workload), "kernel": KERNEL_NAMES[kind],
+                "kernel_ms": round(dom_ms, 5), "pack_kernel_ms": round(kern_ms[0], 5)}
+        value = ops / (ms_per_step * 1e-3) / 1e12
+        metric, unit = "binary TOPS (2*M*N*K/s)", "TOPS"
+        dtype = "i8" if kind == "mfma" else "u32"
+
+    result = {
+        "metric": metric, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
+        "config": {"workload": args.workload, "parallelism": "none (1 GPU)"},
+        "roofline": roof,
+    }
+    if not pack_only:
+        m, n, k = wl.gemm_mnk()
+        result["config"].update({"m": m, "n": n, "k": k, "x_dtype": wl.x_dtype,
+                                 "out_dtype": wl.out_dtype,
+                                 "path": {bnn.PATH_XOR: "xor", bnn.PATH_MFMA: "mfma"}[path_used]})
+        result["parity_spot_check"] = parity
+    if not args.no_cpu_baseline and not pack_only:
+        log("cpu baseline (oracle on host cores)")
+        result["cpu_baseline"] = cpu_baseline(wl, x, w)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,246 @@
+"""Binarized linear / conv2d forward for MI355X (gfx950): Python binding of libbnn.
+
+The compute runs in libbnn.so (hand-written HIP kernels behind a C ABI, see
+include/bnn.h); this module only marshals arguments with ctypes. PyTorch is
+used for device memory (the caller's tensors, output and workspace
+allocations) and for the current HIP stream. There is no fallback: if
+libbnn.so is missing, importing the module raises.
+
+Entry points mirror the C ABI:
+  pack_sign(x)              rows of x -> packed int32 words [rows, k/32]
+  pack_sign_nchw(x)         NCHW x -> packed words [n, h, w, c/32]
+  w_pack(weight)            linear [out, in] or OIHW conv weight -> packed words
+  gemm(x, w_packed, ...)    binary linear forward (bitorch-engine BinaryLinearForward)
+  conv2d(x, w_packed, ...)  binary conv2d forward (bitorch-engine BinaryConv2dForward)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libbnn.so")
+
+# bnn_dtype / bnn_path / bnn_status codes of include/bnn.h
+F32, F16, BF16, I32, U32_PACKED = 0, 1, 2, 3, 4
+PATH_AUTO, PATH_XOR, PATH_MFMA = 0, 1, 2
+OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIGN, ERR_WORKSPACE, ERR_PATH, ERR_HIP = range(8)
+
+EXPORTS = ("bnn_pack_sign", "bnn_pack_sign_nchw", "bnn_w_pack", "bnn_gemm", "bnn_conv2d",
+           "bnn_gemm_workspace_bytes", "bnn_conv2d_workspace_bytes", "bnn_gemm_auto_path",
+           "bnn_conv2d_auto_path", "bnn_last_path", "bnn_status_string")
+
+_PATHS = {"auto": PATH_AUTO, "xor": PATH_XOR, "mfma": PATH_MFMA}
+_DT = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16, torch.int32: I32}
+_TORCH = {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16, I32: torch.int32}
+
+
+def _bind(path: str) -> ctypes.CDLL:
+    lib = ctypes.CDLL(path)
+    P, I64, I, D, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_size_t
+    sig = {
+        "bnn_pack_sign": ([P, I, I64, I64, P, P], I),
+        "bnn_pack_sign_nchw": ([P, I, I64, I64, I64, I64, P, P], I),
+        "bnn_w_pack": ([P, I, I64, I64, I, P, P], I),
+        "bnn_gemm": ([P, I, P, I64, I64, I64, D, D, I, P, I, P, SZ, P], I),
+        "bnn_conv2d": ([P, I, I64, I64, I64, I64, P, I64, D, D, I, I, I, I, I, P, I, P, SZ, P], I),
+        "bnn_gemm_workspace_bytes": ([I64, I64, I], SZ),
+        "bnn_conv2d_workspace_bytes": ([I64, I64, I64, I64, I], SZ),
+        "bnn_gemm_auto_path": ([I64, I64, I64], I),
+        "bnn_conv2d_auto_path": ([I64, I64, I64, I64, I64, I, I, I, I], I),
+        "bnn_last_path": ([], I),
+        "bnn_status_string": ([I], ctypes.c_char_p),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950) first")
+lib = _bind(LIB_PATH)
+
+
+class BnnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {lib.bnn_status_string(status).decode()} (status {status})")
+
+
+def _check(status: int, where: str):
+    if status == OK:
+        return
+    if status == ERR_SHAPE:
+        # same message as the layer pages' divisibility assertion, plus the ABI's reason
+        raise AssertionError(f"Input tensor dimension must be divisible by 32. ({where}: "
+                             f"{lib.bnn_status_string(status).decode()})")
+    raise BnnError(status, where)
+
+
+def _dev(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _path(path) -> int:
+    if isinstance(path, str):
+        return _PATHS[path.lower()]
+    return int(path)
+
+
+def _dtype_code(t: torch.Tensor, name: str) -> int:
+    if t.dtype not in (torch.float32, torch.float16, torch.bfloat16):
+        raise TypeError(f"{name} must be float32, float16 or bfloat16, got {t.dtype}")
+    return _DT[t.dtype]
+
+
+def pack_sign(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Sign+pack along the last axis: [rows, k] -> int32 words [rows, k/32]."""
+    x = _dev(x, "x")
+    k = x.shape[-1]
+    rows = x.numel() // k if k else 0
+    if out is None:
+        out = torch.empty((*x.shape[:-1], k // 32), dtype=torch.int32, device=x.device)
+    else:
+        _dev(out, "out")
+    _check(lib.bnn_pack_sign(x.data_ptr(), _dtype_code(x, "x"), rows, k, out.data_ptr(), _stream(x)),
+           "bnn_pack_sign")
+    return out
+
+
+def pack_sign_nchw(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Sign+pack of NCHW activations along channels: [n, c, h, w] -> int32 words [n, h, w, c/32]."""
+    x = _dev(x, "x")
+    n, c, h, w = x.shape
+    if out is None:
+        out = torch.empty((n, h, w, c // 32), dtype=torch.int32, device=x.device)
+    else:
+        _dev(out, "out")
+    _check(lib.bnn_pack_sign_nchw(x.data_ptr(), _dtype_code(x, "x"), n, c, h, w, out.data_ptr(),
+                                  _stream(x)), "bnn_pack_sign_nchw")
+    return out
+
+
+def w_pack(weight: torch.Tensor) -> torch.Tensor:
+    """Weight pack: linear [out, in] -> [out, in/32]; OIHW [out, in, k, k] -> [out, k, k, in/32]."""
+    weight = _dev(weight, "weight")
+    if weight.dim() == 2:
+        o, i = weight.shape
+        ks = 0
+        shape = (o, i // 32)
+    elif weight.dim() == 4:
+        o, i, kh, kw = weight.shape
+        if kh != kw:
+            raise ValueError("square kernels only")
+        ks = kh
+        shape = (o, ks, ks, i // 32)
+    else:
+        raise ValueError("weight must be 2-D (linear) or 4-D OIHW (conv)")
+    out = torch.empty(shape, dtype=torch.int32, device=weight.device)
+    _check(lib.bnn_w_pack(weight.data_ptr(), _dtype_code(weight, "weight"), o, i, ks, out.data_ptr(),
+                          _stream(weight)), "bnn_w_pack")
+    return out
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def gemm(x: torch.Tensor, w_packed: torch.Tensor, scale_a: float, scale_w: float, path="auto",
+         out_dtype=None, k: int | None = None, out: torch.Tensor | None = None,
+         workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Binary linear forward: out = scale_a*scale_w * sgn(x) @ sgn(W)^T.
+
+    x is [m, k] float (packed here) or int32 [m, k/32] already packed (then k
+    defaults to 32 * x.shape[1]). w_packed is int32 [n, k/32] from w_pack.
+    out_dtype defaults to x's dtype (float32 for packed x); torch.int32 gives
+    the raw accumulators.
+    """
+    x = _dev(x, "x")
+    w_packed = _dev(w_packed, "w_packed")
+    packed = x.dtype == torch.int32
+    m = x.shape[0]
+    if packed:
+        k = 32 * x.shape[1] if k is None else k
+        xcode = U32_PACKED
+    else:
+        k = x.shape[1]
+        xcode = _dtype_code(x, "x")
+    n = w_packed.shape[0]
+    if out_dtype is None:
+        out_dtype = torch.float32 if packed else x.dtype
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=x.device)
+    else:
+        _dev(out, "out")
+    ws_bytes = lib.bnn_gemm_workspace_bytes(m, k, xcode)
+    if workspace is None and ws_bytes:
+        workspace = _workspace(ws_bytes, x.device)
+    _check(lib.bnn_gemm(x.data_ptr(), xcode, w_packed.data_ptr(), m, n, k, float(scale_a),
+                        float(scale_w), _path(path), out.data_ptr(), _DT[out.dtype],
+                        workspace.data_ptr() if workspace is not None else None,
+                        workspace.numel() if workspace is not None else 0, _stream(x)), "bnn_gemm")
+    return out
+
+
+def conv2d(x: torch.Tensor, w_packed: torch.Tensor, scale_a: float, scale_w: float,
+           kernel_size: int, stride: int = 1, padding: int = 0, dilation: int = 1, path="auto",
+           out_dtype=None, channels: int | None = None, out: torch.Tensor | None = None,
+           workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Binary conv2d forward, NCHW in and out; padded taps contribute 0.
+
+    x is [n, c, h, w] float, or int32 [n, h, w, c/32] already packed by
+    pack_sign_nchw. w_packed is int32 [o, k, k, c/32] from w_pack.
+    """
+    x = _dev(x, "x")
+    w_packed = _dev(w_packed, "w_packed")
+    packed = x.dtype == torch.int32
+    if packed:
+        n, h, w, cw = x.shape
+        c = 32 * cw if channels is None else channels
+        xcode = U32_PACKED
+    else:
+        n, c, h, w = x.shape
+        xcode = _dtype_code(x, "x")
+    o = w_packed.shape[0]
+    ho = (h + 2 * padding - dilation * (kernel_size - 1) - 1) // stride + 1
+    wo = (w + 2 * padding - dilation * (kernel_size - 1) - 1) // stride + 1
+    if out_dtype is None:
+        out_dtype = torch.float32 if packed else x.dtype
+    if out is None:
+        out = torch.empty((n, o, max(ho, 0), max(wo, 0)), dtype=out_dtype, device=x.device)
+    else:
+        _dev(out, "out")
+    ws_bytes = lib.bnn_conv2d_workspace_bytes(n, c, h, w, xcode)
+    if workspace is None and ws_bytes:
+        workspace = _workspace(ws_bytes, x.device)
+    _check(lib.bnn_conv2d(x.data_ptr(), xcode, n, c, h, w, w_packed.data_ptr(), o, float(scale_a),
+                          float(scale_w), kernel_size, stride, padding, dilation, _path(path),
+                          out.data_ptr(), _DT[out.dtype],
+                          workspace.data_ptr() if workspace is not None else None,
+                          workspace.numel() if workspace is not None else 0, _stream(x)),
+           "bnn_conv2d")
+    return out
+
+
+def last_path() -> int:
+    return lib.bnn_last_path()
+
+
+def gemm_auto_path(m: int, n: int, k: int) -> int:
+    return lib.bnn_gemm_auto_path(m, n, k)
+
+
+def conv2d_auto_path(n, c, h, w, o, kernel_size, stride=1, padding=0, dilation=1) -> int:
+    return lib.bnn_conv2d_auto_path(n, c, h, w, o, kernel_size, stride, padding, dilation)

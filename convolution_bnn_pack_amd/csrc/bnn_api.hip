@@ -1,0 +1,242 @@
+// C ABI of libbnn: argument validation, output shapes, the scale product,
+// per-shape path choice and kernel dispatch on the caller's stream.
+//
+// Every check runs before the first HIP call, so a rejected call enqueues
+// nothing and leaves the outputs untouched (this also makes the checks
+// testable on a host without a GPU).
+#include <math.h>
+
+#include "../../include/bnn.h"
+#include "launch.h"
+
+namespace bnn {
+int xor_conv_max_taps();
+}
+
+namespace {
+
+thread_local int g_last_path = 0;
+
+bool float_dtype(int d) { return d == BNN_F32 || d == BNN_F16 || d == BNN_BF16; }
+bool out_dtype_ok(int d) { return float_dtype(d) || d == BNN_I32; }
+int elem_bytes(int d) { return d == BNN_F32 ? 4 : 2; }
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// floor((size + 2p - d(k-1) - 1)/s + 1) with a true floor for negative numerators.
+int64_t out_size(int64_t size, int64_t k, int64_t s, int64_t p, int64_t d) {
+  const int64_t num = size + 2 * p - d * (k - 1) - 1;
+  int64_t q = num / s;
+  if (num % s != 0 && num < 0) q -= 1;
+  return q + 1;
+}
+
+// The contraction's scale: the host product of the two scalar scales in
+// double (as the layer forward computes it before calling the native
+// kernel), rounded once to float for the fp32 epilogue.
+float alpha_of(double scale_a, double scale_w) { return (float)(scale_a * scale_w); }
+
+bnn_status hip_status(hipError_t e) { return e == hipSuccess ? BNN_OK : BNN_ERR_HIP; }
+
+// Shape-based choice between the two contraction paths. The matrix-core
+// path has 4x the VALU path's peak but pays for the bit expansion and needs
+// enough 128x128 tiles to keep the chip busy; tiny contractions (a few
+// workgroups) run on the VALU path, whose tiles carry less fixed cost.
+int auto_path(int64_t m, int64_t n, int64_t k) {
+  const double work = (double)m * (double)n * (double)k;
+  if (work < 3.0e8) return BNN_PATH_XOR;
+  return BNN_PATH_MFMA;
+}
+
+bool int_fits(int64_t v) { return v >= 0 && v <= 0x7FFFFFFFLL; }
+
+}  // namespace
+
+extern "C" {
+
+const char* bnn_status_string(int s) {
+  switch (s) {
+    case BNN_OK: return "ok";
+    case BNN_ERR_NULL: return "null pointer argument";
+    case BNN_ERR_SHAPE: return "invalid shape (sizes, K or C not a multiple of 32, or empty conv output)";
+    case BNN_ERR_DTYPE: return "dtype not allowed for this argument";
+    case BNN_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case BNN_ERR_WORKSPACE: return "workspace missing or too small";
+    case BNN_ERR_PATH: return "unknown path or path cannot run this shape";
+    case BNN_ERR_HIP: return "HIP runtime error on launch";
+    default: return "unknown status";
+  }
+}
+
+int bnn_last_path(void) { return g_last_path; }
+
+size_t bnn_gemm_workspace_bytes(int64_t m, int64_t k, int x_dtype) {
+  if (x_dtype == BNN_U32_PACKED || m <= 0 || k <= 0) return 0;
+  return (size_t)m * (size_t)(k / 32) * 4u;
+}
+
+size_t bnn_conv2d_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w, int x_dtype) {
+  if (x_dtype == BNN_U32_PACKED || n <= 0 || c <= 0 || h <= 0 || w <= 0) return 0;
+  return (size_t)n * (size_t)h * (size_t)w * (size_t)(c / 32) * 4u;
+}
+
+int bnn_gemm_auto_path(int64_t m, int64_t n, int64_t k) { return auto_path(m, n, k); }
+
+int bnn_conv2d_auto_path(int64_t n, int64_t c, int64_t h, int64_t w, int64_t out_channels,
+                         int kernel_size, int stride, int padding, int dilation) {
+  if (kernel_size < 1 || stride < 1 || dilation < 1 || padding < 0) return BNN_PATH_MFMA;
+  const int64_t ho = out_size(h, kernel_size, stride, padding, dilation);
+  const int64_t wo = out_size(w, kernel_size, stride, padding, dilation);
+  if (kernel_size * kernel_size > bnn::xor_conv_max_taps()) return BNN_PATH_MFMA;
+  return auto_path(n * (ho > 0 ? ho : 0) * (wo > 0 ? wo : 0), out_channels,
+                   c * kernel_size * kernel_size);
+}
+
+bnn_status bnn_pack_sign(const void* x, int x_dtype, int64_t rows, int64_t k, uint32_t* x_packed,
+                         void* stream) {
+  if (!float_dtype(x_dtype)) return BNN_ERR_DTYPE;
+  if (rows < 0 || k <= 0 || k % 32 != 0) return BNN_ERR_SHAPE;
+  if (rows == 0) return BNN_OK;
+  if (!x || !x_packed) return BNN_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(x_packed, 4)) return BNN_ERR_ALIGN;
+  return hip_status(bnn::launch_pack_rows(x, x_dtype, rows * (k / 32), x_packed,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+bnn_status bnn_pack_sign_nchw(const void* x, int x_dtype, int64_t n, int64_t c, int64_t h,
+                              int64_t w, uint32_t* x_packed, void* stream) {
+  if (!float_dtype(x_dtype)) return BNN_ERR_DTYPE;
+  if (n < 0 || c <= 0 || c % 32 != 0 || h <= 0 || w <= 0) return BNN_ERR_SHAPE;
+  if (!int_fits(h * w) || !int_fits(n * (c / 32))) return BNN_ERR_SHAPE;
+  if (n == 0) return BNN_OK;
+  if (!x || !x_packed) return BNN_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(x_packed, 4)) return BNN_ERR_ALIGN;
+  return hip_status(bnn::launch_pack_nchw(x, x_dtype, n, c, h, w, x_packed,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+bnn_status bnn_w_pack(const void* weight, int w_dtype, int64_t out_features, int64_t in_features,
+                      int kernel_size, uint32_t* w_packed, void* stream) {
+  if (!float_dtype(w_dtype)) return BNN_ERR_DTYPE;
+  if (out_features < 0 || in_features <= 0 || in_features % 32 != 0 || kernel_size < 0)
+    return BNN_ERR_SHAPE;
+  if (out_features == 0) return BNN_OK;
+  if (!weight || !w_packed) return BNN_ERR_NULL;
+  if (!aligned(w_packed, 4)) return BNN_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (kernel_size == 0) {
+    if (!aligned(weight, 16)) return BNN_ERR_ALIGN;
+    return hip_status(bnn::launch_pack_rows(weight, w_dtype, out_features * (in_features / 32),
+                                            w_packed, s));
+  }
+  if (!aligned(weight, elem_bytes(w_dtype))) return BNN_ERR_ALIGN;
+  return hip_status(bnn::launch_pack_conv_weight(weight, w_dtype, out_features, in_features,
+                                                 kernel_size, w_packed, s));
+}
+
+bnn_status bnn_gemm(const void* x, int x_dtype, const uint32_t* w_packed, int64_t m, int64_t n,
+                    int64_t k, double scale_a, double scale_w, int path, void* out, int out_dtype,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (!(float_dtype(x_dtype) || x_dtype == BNN_U32_PACKED) || !out_dtype_ok(out_dtype))
+    return BNN_ERR_DTYPE;
+  if (m < 0 || n < 0 || k < 32 || k % 32 != 0) return BNN_ERR_SHAPE;
+  if (!int_fits(m) || !int_fits(n) || !int_fits(k / 32)) return BNN_ERR_SHAPE;
+  if (path != BNN_PATH_AUTO && path != BNN_PATH_XOR && path != BNN_PATH_MFMA) return BNN_ERR_PATH;
+  if (m == 0 || n == 0) return BNN_OK;
+  if (!x || !w_packed || !out) return BNN_ERR_NULL;
+  const bool packed = x_dtype == BNN_U32_PACKED;
+  if (!aligned(x, packed ? 4 : 16) || !aligned(w_packed, 4) || !aligned(out, 16))
+    return BNN_ERR_ALIGN;
+  const size_t need = bnn_gemm_workspace_bytes(m, k, x_dtype);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return BNN_ERR_WORKSPACE;
+  if (need > 0 && !aligned(workspace, 4)) return BNN_ERR_ALIGN;
+
+  const int use = path == BNN_PATH_AUTO ? auto_path(m, n, k) : path;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint32_t* a = static_cast<const uint32_t*>(x);
+  if (!packed) {
+    uint32_t* ws = static_cast<uint32_t*>(workspace);
+    const hipError_t e = bnn::launch_pack_rows(x, x_dtype, m * (k / 32), ws, s);
+    if (e != hipSuccess) return BNN_ERR_HIP;
+    a = ws;
+  }
+  bnn::Contraction p{};
+  p.a = a;
+  p.w = w_packed;
+  p.out = out;
+  p.M = (int)m;
+  p.N = (int)n;
+  p.KW = (int)(k / 32);
+  p.alpha = alpha_of(scale_a, scale_w);
+  const hipError_t e = use == BNN_PATH_XOR ? bnn::launch_xor(p, false, out_dtype, s)
+                                           : bnn::launch_mfma(p, false, out_dtype, s);
+  if (e != hipSuccess) return BNN_ERR_HIP;
+  g_last_path = use;
+  return BNN_OK;
+}
+
+bnn_status bnn_conv2d(const void* x, int x_dtype, int64_t n, int64_t c, int64_t h, int64_t w,
+                      const uint32_t* w_packed, int64_t out_channels, double scale_a,
+                      double scale_w, int kernel_size, int stride, int padding, int dilation,
+                      int path, void* out, int out_dtype, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  if (!(float_dtype(x_dtype) || x_dtype == BNN_U32_PACKED) || !out_dtype_ok(out_dtype))
+    return BNN_ERR_DTYPE;
+  if (n < 0 || out_channels < 0 || c <= 0 || c % 32 != 0 || h <= 0 || w <= 0) return BNN_ERR_SHAPE;
+  if (kernel_size < 1 || stride < 1 || dilation < 1 || padding < 0) return BNN_ERR_SHAPE;
+  const int64_t ho = out_size(h, kernel_size, stride, padding, dilation);
+  const int64_t wo = out_size(w, kernel_size, stride, padding, dilation);
+  if (ho <= 0 || wo <= 0) return BNN_ERR_SHAPE;
+  const int64_t kw_words = (int64_t)kernel_size * kernel_size * (c / 32);
+  if (!int_fits(n * ho * wo) || !int_fits(out_channels) || !int_fits(kw_words) ||
+      !int_fits(n * h * w * (c / 32)) || !int_fits(h + 2 * (int64_t)padding) ||
+      !int_fits(w + 2 * (int64_t)padding))
+    return BNN_ERR_SHAPE;
+  if (path != BNN_PATH_AUTO && path != BNN_PATH_XOR && path != BNN_PATH_MFMA) return BNN_ERR_PATH;
+  if (path == BNN_PATH_XOR && kernel_size * kernel_size > bnn::xor_conv_max_taps())
+    return BNN_ERR_PATH;
+  if (n == 0 || out_channels == 0) return BNN_OK;
+  if (!x || !w_packed || !out) return BNN_ERR_NULL;
+  const bool packed = x_dtype == BNN_U32_PACKED;
+  if (!aligned(x, packed ? 4 : 16) || !aligned(w_packed, 4) || !aligned(out, 16))
+    return BNN_ERR_ALIGN;
+  const size_t need = bnn_conv2d_workspace_bytes(n, c, h, w, x_dtype);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return BNN_ERR_WORKSPACE;
+  if (need > 0 && !aligned(workspace, 4)) return BNN_ERR_ALIGN;
+
+  const int use = path == BNN_PATH_AUTO
+                      ? bnn_conv2d_auto_path(n, c, h, w, out_channels, kernel_size, stride,
+                                             padding, dilation)
+                      : path;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint32_t* a = static_cast<const uint32_t*>(x);
+  if (!packed) {
+    uint32_t* ws = static_cast<uint32_t*>(workspace);
+    const hipError_t e = bnn::launch_pack_nchw(x, x_dtype, n, c, h, w, ws, s);
+    if (e != hipSuccess) return BNN_ERR_HIP;
+    a = ws;
+  }
+  bnn::Contraction p{};
+  p.a = a;
+  p.w = w_packed;
+  p.out = out;
+  p.M = (int)(n * ho * wo);
+  p.N = (int)out_channels;
+  p.KW = (int)kw_words;
+  p.alpha = alpha_of(scale_a, scale_w);
+  p.H = (int)h;
+  p.W = (int)w;
+  p.CW = (int)(c / 32);
+  p.Ho = (int)ho;
+  p.Wo = (int)wo;
+  p.ks = kernel_size;
+  p.stride = stride;
+  p.pad = padding;
+  p.dil = dilation;
+  const hipError_t e = use == BNN_PATH_XOR ? bnn::launch_xor(p, true, out_dtype, s)
+                                           : bnn::launch_mfma(p, true, out_dtype, s);
+  if (e != hipSuccess) return BNN_ERR_HIP;
+  g_last_path = use;
+  return BNN_OK;
+}
+
+}  // extern "C"

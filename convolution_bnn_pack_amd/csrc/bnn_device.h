@@ -1,0 +1,114 @@
+// Device-side helpers shared by the libbnn kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <hip/hip_bf16.h>
+#include <stdint.h>
+
+namespace bnn {
+
+// Element / output type codes (numerically equal to include/bnn.h's bnn_dtype).
+enum : int { kF32 = 0, kF16 = 1, kBF16 = 2, kI32 = 3, kPacked = 4 };
+
+// Sign bit of one element, from its raw IEEE bits: 1 when the value is >= 0
+// (+0, -0, positive numbers, +inf), 0 otherwise (negative numbers, -inf, any
+// NaN). Working on bits keeps the result independent of denormal modes.
+__device__ __forceinline__ uint32_t pos_f32(uint32_t u) {
+  return (uint32_t)(u <= 0x7F800000u) | (uint32_t)(u == 0x80000000u);
+}
+__device__ __forceinline__ uint32_t pos_f16(uint32_t h) {
+  return (uint32_t)(h <= 0x7C00u) | (uint32_t)(h == 0x8000u);
+}
+__device__ __forceinline__ uint32_t pos_bf16(uint32_t b) {
+  return (uint32_t)(b <= 0x7F80u) | (uint32_t)(b == 0x8000u);
+}
+
+// Sign bits of the two 16-bit elements in a dword (element 0 in the low half).
+template <int DT>
+__device__ __forceinline__ uint32_t pos2(uint32_t d) {
+  if constexpr (DT == kF16)
+    return pos_f16(d & 0xFFFFu) | (pos_f16(d >> 16) << 1);
+  else
+    return pos_bf16(d & 0xFFFFu) | (pos_bf16(d >> 16) << 1);
+}
+
+// Native 16-byte vector (usable with the nontemporal load builtin).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Sign bits of the elements in a 16-byte vector, element e at bit e
+// (4 bits for f32, 8 bits for f16/bf16).
+template <int DT>
+__device__ __forceinline__ uint32_t vec_bits(u32x4 v) {
+  if constexpr (DT == kF32) {
+    return pos_f32(v.x) | (pos_f32(v.y) << 1) | (pos_f32(v.z) << 2) | (pos_f32(v.w) << 3);
+  } else {
+    return pos2<DT>(v.x) | (pos2<DT>(v.y) << 2) | (pos2<DT>(v.z) << 4) | (pos2<DT>(v.w) << 6);
+  }
+}
+
+// Sign bit of one element read as raw bits from a typed array.
+template <int DT>
+__device__ __forceinline__ uint32_t elem_pos(const void* base, int64_t i) {
+  if constexpr (DT == kF32)
+    return pos_f32(reinterpret_cast<const uint32_t*>(base)[i]);
+  else if constexpr (DT == kF16)
+    return pos_f16(reinterpret_cast<const uint16_t*>(base)[i]);
+  else
+    return pos_bf16(reinterpret_cast<const uint16_t*>(base)[i]);
+}
+
+// One scaled output element: (float)acc * alpha rounded to the output type
+// (round to nearest even), or the raw accumulator for kI32.
+template <int OUT>
+__device__ __forceinline__ void store1(void* out, int64_t idx, int acc, float alpha) {
+  if constexpr (OUT == kF32) {
+    reinterpret_cast<float*>(out)[idx] = (float)acc * alpha;
+  } else if constexpr (OUT == kF16) {
+    reinterpret_cast<__half*>(out)[idx] = __float2half_rn((float)acc * alpha);
+  } else if constexpr (OUT == kBF16) {
+    reinterpret_cast<__hip_bfloat16*>(out)[idx] = __float2bfloat16((float)acc * alpha);
+  } else {
+    reinterpret_cast<int*>(out)[idx] = acc;
+  }
+}
+
+// Four consecutive output elements starting at idx (idx must be a multiple of 4).
+template <int OUT>
+__device__ __forceinline__ void store4(void* out, int64_t idx, int a0, int a1, int a2, int a3,
+                                       float alpha) {
+  if constexpr (OUT == kF32) {
+    float4 v = make_float4((float)a0 * alpha, (float)a1 * alpha, (float)a2 * alpha,
+                           (float)a3 * alpha);
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + idx) = v;
+  } else if constexpr (OUT == kI32) {
+    *reinterpret_cast<int4*>(reinterpret_cast<int*>(out) + idx) = make_int4(a0, a1, a2, a3);
+  } else if constexpr (OUT == kF16) {
+    __half h[4] = {__float2half_rn((float)a0 * alpha), __float2half_rn((float)a1 * alpha),
+                   __float2half_rn((float)a2 * alpha), __float2half_rn((float)a3 * alpha)};
+    *reinterpret_cast<uint2*>(reinterpret_cast<__half*>(out) + idx) =
+        *reinterpret_cast<const uint2*>(h);
+  } else {
+    __hip_bfloat16 h[4] = {__float2bfloat16((float)a0 * alpha), __float2bfloat16((float)a1 * alpha),
+                           __float2bfloat16((float)a2 * alpha), __float2bfloat16((float)a3 * alpha)};
+    *reinterpret_cast<uint2*>(reinterpret_cast<__hip_bfloat16*>(out) + idx) =
+        *reinterpret_cast<const uint2*>(h);
+  }
+}
+
+// Shape of one contraction, shared by the GEMM and the implicit-im2col conv.
+// Linear: A is packed activations [M][KW], W is packed weights [N][KW].
+// Conv:   A is packed activations [B][H][W][CW] read through the implicit
+//         im2col map; the reduction index q = tap * CW + cw with tap = kh*ks + kw;
+//         W is [N][ks][ks][CW] = [N][KW]; M = B*Ho*Wo, output is NCHW.
+struct Contraction {
+  const uint32_t* a;
+  const uint32_t* w;
+  void* out;
+  int M, N, KW;
+  float alpha;
+  // conv only
+  int H, W, CW, Ho, Wo, ks, stride, pad, dil;
+};
+
+}  // namespace bnn

@@ -1,0 +1,30 @@
+// Host-side launchers of the libbnn kernels. Each returns the hipError_t of
+// the launch; arguments are assumed validated by the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "bnn_device.h"
+
+namespace bnn {
+
+// Row sign+pack: x [rows][k] -> words [rows][k/32], treated as one flat stream of words.
+hipError_t launch_pack_rows(const void* x, int dtype, int64_t total_words, uint32_t* out,
+                            hipStream_t stream);
+
+// NCHW sign+pack: x [b][c][h][w] -> words [b][h][w][c/32].
+hipError_t launch_pack_nchw(const void* x, int dtype, int64_t b, int64_t c, int64_t h, int64_t w,
+                            uint32_t* out, hipStream_t stream);
+
+// OIHW conv weight pack: [o][c][ks][ks] -> [o][ks][ks][c/32].
+hipError_t launch_pack_conv_weight(const void* w, int dtype, int64_t o, int64_t c, int ks,
+                                   uint32_t* out, hipStream_t stream);
+
+// XOR + popcount contraction on the vector ALUs.
+hipError_t launch_xor(const Contraction& p, bool conv, int out_dtype, hipStream_t stream);
+
+// int8 +-1 contraction on the matrix cores.
+hipError_t launch_mfma(const Contraction& p, bool conv, int out_dtype, hipStream_t stream);
+
+}  // namespace bnn

@@ -1,0 +1,148 @@
+/*
+ * bnn.h: C ABI of libbnn, the MI355X (gfx950) forward pass of binarized
+ * linear and conv2d layers.
+ *
+ * The layers are those of bitorch-engine's binary layer pages:
+ *   - BinaryLinearForward.forward(input, weight, bmm_type, scale_a, scale_w, is_train)
+ *     (BinaryLinearForward page): the binary linear result scaled by the
+ *     activation and weight scaling factors, no bias term;
+ *   - BinaryConv2dForward.forward(x, weight, scale_a, scale_w, is_train,
+ *     kernel_size, stride, padding, dilation) (qconv/binary/cutlass/layer
+ *     page): the native forward receives the host product of the two scalar
+ *     scales and returns the output in the input's dtype;
+ *   - BinaryLinearCuda.w_pack / BinaryConv2dCutlass.generate_quantized_weight:
+ *     weights are bit-packed once, ahead of the forward, by a packing kernel.
+ *
+ * Arithmetic (the method): every activation and weight element maps to +1
+ * when it is >= 0 and to -1 otherwise (so -0 -> +1 and NaN -> -1); signs
+ * are packed 32 per uint32 word along the reduction axis, bit j of word q
+ * holding element 32q + j, bit value 1 for +1; the dot product of two
+ * packed rows of K signs is K - 2 * popcount(a XOR w), exactly. Conv2d is
+ * the im2col lowering of the banghao.live blog post, section 2 (output size
+ * floor((H + 2p - d(k-1) - 1)/s + 1)), computed implicitly, with padded
+ * taps contributing 0. The integer accumulator is scaled by
+ * (float)(scale_a * scale_w) in fp32 and rounded to the output dtype
+ * (round to nearest even).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers, allocated and owned by the
+ *     caller; the library never allocates, frees or keeps a pointer after
+ *     returning. Tensors are dense (contiguous, row-major in the stated
+ *     layout).
+ *   - `stream` is a hipStream_t (NULL = the default stream). Work is
+ *     enqueued on it and the call returns without synchronizing.
+ *   - Arguments are validated before anything is enqueued: on any error the
+ *     call returns a non-zero status, enqueues nothing and leaves every
+ *     output untouched. BNN_ERR_HIP reports a failed kernel launch.
+ *   - Packed words travel in int32/uint32 buffers; the reduction length K
+ *     (or the channel count C) must be a multiple of 32 (the pages' layers
+ *     assert that the input divides into whole binary words).
+ *   - The library holds no state except the per-thread record of the path
+ *     that the last call took (bnn_last_path).
+ */
+#ifndef BNN_H
+#define BNN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BNN_OK = 0,
+  BNN_ERR_NULL = 1,      /* a required pointer is NULL */
+  BNN_ERR_SHAPE = 2,     /* a size is negative/zero where it may not be, K or C % 32 != 0, empty conv output */
+  BNN_ERR_DTYPE = 3,     /* dtype code not allowed for that argument */
+  BNN_ERR_ALIGN = 4,     /* a pointer is not 16-byte aligned */
+  BNN_ERR_WORKSPACE = 5, /* workspace missing or smaller than the *_workspace_bytes query */
+  BNN_ERR_PATH = 6,      /* unknown path code, or the forced path cannot run this shape */
+  BNN_ERR_HIP = 7        /* the HIP runtime reported an error on launch */
+} bnn_status;
+
+typedef enum {
+  BNN_F32 = 0,
+  BNN_F16 = 1,
+  BNN_BF16 = 2,
+  BNN_I32 = 3,        /* output only: the raw integer accumulators, unscaled */
+  BNN_U32_PACKED = 4  /* input only: activations already packed by bnn_pack_sign / bnn_pack_sign_nchw */
+} bnn_dtype;
+
+/* Kernel choice; mirrors the layers' bmm_type argument (BMM.ADAPTIVE is the default there). */
+typedef enum {
+  BNN_PATH_AUTO = 0,  /* pick per shape */
+  BNN_PATH_XOR = 1,   /* XOR + popcount on the vector ALUs */
+  BNN_PATH_MFMA = 2   /* signs expanded to int8 +-1, contracted on the matrix cores */
+} bnn_path;
+
+/* Sign + pack of activations along rows.
+ *   x        [rows, k] in x_dtype (BNN_F32/F16/BF16), 16-byte aligned.
+ *   x_packed [rows, k/32] uint32 out; bit j of word q = (x[r][32q+j] >= 0).
+ * k % 32 == 0; rows == 0 is a no-op. */
+bnn_status bnn_pack_sign(const void* x, int x_dtype, int64_t rows, int64_t k,
+                         uint32_t* x_packed, void* stream);
+
+/* Sign + pack of NCHW activations along channels.
+ *   x        [n, c, h, w] in x_dtype (BNN_F32/F16/BF16), 16-byte aligned.
+ *   x_packed [n, h, w, c/32] uint32 out; bit j of word q = (x[n][32q+j][h][w] >= 0).
+ * c % 32 == 0. */
+bnn_status bnn_pack_sign_nchw(const void* x, int x_dtype, int64_t n, int64_t c, int64_t h,
+                              int64_t w, uint32_t* x_packed, void* stream);
+
+/* Weight pack (run once per layer, ahead of the forward).
+ *   kernel_size == 0: linear weight [out_features, in_features] -> [out_features, in_features/32].
+ *   kernel_size >= 1: conv weight OIHW [out_features, in_features, k, k] -> [out_features, k, k, in_features/32].
+ *   w_dtype BNN_F32/F16/BF16; in_features % 32 == 0; weight 16-byte aligned when kernel_size == 0. */
+bnn_status bnn_w_pack(const void* weight, int w_dtype, int64_t out_features, int64_t in_features,
+                      int kernel_size, uint32_t* w_packed, void* stream);
+
+/* Binary linear forward: out[m][n] = scale_a * scale_w * sum_k sgn(x[m][k]) * sgn(W[n][k]).
+ *   x         [m, k] in BNN_F32/F16/BF16 (packed here into the workspace), or
+ *             [m, k/32] BNN_U32_PACKED (already packed; no workspace needed).
+ *   w_packed  [n, k/32] from bnn_w_pack(kernel_size = 0).
+ *   out       [m, n] in out_dtype: BNN_F32/F16/BF16 (scaled) or BNN_I32 (raw accumulators).
+ *   path      a bnn_path value.
+ *   workspace device scratch of at least bnn_gemm_workspace_bytes(m, k, x_dtype) bytes
+ *             (may be NULL when that is 0).
+ * m == 0 or n == 0 is a no-op; k % 32 == 0, k >= 32. */
+bnn_status bnn_gemm(const void* x, int x_dtype, const uint32_t* w_packed, int64_t m, int64_t n,
+                    int64_t k, double scale_a, double scale_w, int path, void* out, int out_dtype,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Binary conv2d forward (square kernel, symmetric stride/padding/dilation).
+ *   x         NCHW [n, c, h, w] in BNN_F32/F16/BF16, or [n, h, w, c/32] BNN_U32_PACKED.
+ *   w_packed  [out_channels, k, k, c/32] from bnn_w_pack(kernel_size = k).
+ *   out       NCHW [n, out_channels, Ho, Wo] in out_dtype (BNN_F32/F16/BF16/I32),
+ *             Ho = floor((h + 2*padding - dilation*(k-1) - 1)/stride + 1), likewise Wo.
+ *   Padded taps contribute 0 (they are not counted in the reduction).
+ *   workspace at least bnn_conv2d_workspace_bytes(n, c, h, w, x_dtype) bytes.
+ * Requires c % 32 == 0, kernel_size >= 1, stride >= 1, dilation >= 1, padding >= 0, Ho, Wo >= 1.
+ * n == 0 or out_channels == 0 is a no-op. */
+bnn_status bnn_conv2d(const void* x, int x_dtype, int64_t n, int64_t c, int64_t h, int64_t w,
+                      const uint32_t* w_packed, int64_t out_channels, double scale_a,
+                      double scale_w, int kernel_size, int stride, int padding, int dilation,
+                      int path, void* out, int out_dtype, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* Workspace sizes (bytes) for the calls above; 0 when x is already packed. */
+size_t bnn_gemm_workspace_bytes(int64_t m, int64_t k, int x_dtype);
+size_t bnn_conv2d_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w, int x_dtype);
+
+/* The path that bnn_gemm / bnn_conv2d would take for a shape under BNN_PATH_AUTO. */
+int bnn_gemm_auto_path(int64_t m, int64_t n, int64_t k);
+int bnn_conv2d_auto_path(int64_t n, int64_t c, int64_t h, int64_t w, int64_t out_channels,
+                         int kernel_size, int stride, int padding, int dilation);
+
+/* Path (BNN_PATH_XOR or BNN_PATH_MFMA) taken by this thread's last successful
+ * bnn_gemm / bnn_conv2d call; 0 before any such call. */
+int bnn_last_path(void);
+
+/* Static, human-readable text for a status code. */
+const char* bnn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BNN_H */

@@ -1,0 +1,137 @@
+"""The C ABI on the host (no GPU): every symbol declared in include/bnn.h is
+exported by libbnn.so, and every argument check returns its status before any
+HIP call (so these calls run without a device; the fake pointers below are
+never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bnn.h")
+
+
+@pytest.fixture(scope="module")
+def bnn():
+    lib_path = os.path.join(ROOT, "convolution_bnn_pack_amd", "libbnn.so")
+    if not os.path.exists(lib_path):
+        from convolution_bnn_pack_amd import _build
+        _build.build()
+    import convolution_bnn_pack_amd as m
+    return m
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bnn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported(bnn):
+    names = _declared()
+    assert len(names) >= 11
+    for name in names:
+        assert hasattr(bnn.lib, name), name
+    assert sorted(bnn.EXPORTS) == names
+
+
+def test_status_strings(bnn):
+    for code in range(8):
+        assert bnn.lib.bnn_status_string(code)
+    assert bnn.lib.bnn_status_string(99) == b"unknown status"
+
+
+FAKE = 0x10000          # 64 KiB-aligned, never dereferenced
+MISALIGNED = 0x10004
+
+
+def _gemm(bnn, **kw):
+    a = dict(x=FAKE, x_dtype=bnn.F16, w=FAKE, m=64, n=64, k=256, sa=1.0, sw=1.0,
+             path=bnn.PATH_AUTO, out=FAKE, out_dtype=bnn.F32, ws=FAKE, ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return bnn.lib.bnn_gemm(a["x"], a["x_dtype"], a["w"], a["m"], a["n"], a["k"], a["sa"], a["sw"],
+                            a["path"], a["out"], a["out_dtype"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_gemm_argument_checks(bnn):
+    assert _gemm(bnn, k=100) == bnn.ERR_SHAPE
+    assert _gemm(bnn, k=0) == bnn.ERR_SHAPE
+    assert _gemm(bnn, m=-1) == bnn.ERR_SHAPE
+    assert _gemm(bnn, x_dtype=7) == bnn.ERR_DTYPE
+    assert _gemm(bnn, out_dtype=bnn.U32_PACKED) == bnn.ERR_DTYPE
+    assert _gemm(bnn, path=5) == bnn.ERR_PATH
+    assert _gemm(bnn, x=None) == bnn.ERR_NULL
+    assert _gemm(bnn, w=None) == bnn.ERR_NULL
+    assert _gemm(bnn, out=None) == bnn.ERR_NULL
+    assert _gemm(bnn, x=MISALIGNED) == bnn.ERR_ALIGN
+    assert _gemm(bnn, out=MISALIGNED) == bnn.ERR_ALIGN
+    assert _gemm(bnn, ws=None) == bnn.ERR_WORKSPACE
+    assert _gemm(bnn, ws_bytes=64 * 8 * 4 - 1) == bnn.ERR_WORKSPACE
+    # empty problems are no-ops and succeed without touching anything
+    assert _gemm(bnn, m=0, x=None, out=None) == bnn.OK
+    assert _gemm(bnn, n=0, x=None, out=None) == bnn.OK
+
+
+def _conv(bnn, **kw):
+    a = dict(x=FAKE, x_dtype=bnn.F32, n=2, c=64, h=14, w=14, wp=FAKE, o=32, sa=1.0, sw=1.0, ks=3,
+             s=1, p=1, d=1, path=bnn.PATH_AUTO, out=FAKE, out_dtype=bnn.F32, ws=FAKE,
+             ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return bnn.lib.bnn_conv2d(a["x"], a["x_dtype"], a["n"], a["c"], a["h"], a["w"], a["wp"], a["o"],
+                              a["sa"], a["sw"], a["ks"], a["s"], a["p"], a["d"], a["path"], a["out"],
+                              a["out_dtype"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_conv_argument_checks(bnn):
+    assert _conv(bnn, c=48) == bnn.ERR_SHAPE
+    assert _conv(bnn, ks=0) == bnn.ERR_SHAPE
+    assert _conv(bnn, s=0) == bnn.ERR_SHAPE
+    assert _conv(bnn, d=0) == bnn.ERR_SHAPE
+    assert _conv(bnn, p=-1) == bnn.ERR_SHAPE
+    assert _conv(bnn, h=2, ks=5, p=0) == bnn.ERR_SHAPE            # empty output
+    assert _conv(bnn, x_dtype=bnn.I32) == bnn.ERR_DTYPE
+    assert _conv(bnn, out_dtype=9) == bnn.ERR_DTYPE
+    assert _conv(bnn, path=3) == bnn.ERR_PATH
+    assert _conv(bnn, path=bnn.PATH_XOR, ks=9, p=4) == bnn.ERR_PATH  # 81 taps > the XOR table
+    assert _conv(bnn, wp=None) == bnn.ERR_NULL
+    assert _conv(bnn, out=MISALIGNED) == bnn.ERR_ALIGN
+    assert _conv(bnn, ws=None) == bnn.ERR_WORKSPACE
+    assert _conv(bnn, ws_bytes=2 * 14 * 14 * 2 * 4 - 1) == bnn.ERR_WORKSPACE
+    assert _conv(bnn, n=0, x=None, out=None) == bnn.OK
+    assert _conv(bnn, o=0, x=None, out=None) == bnn.OK
+
+
+def test_pack_argument_checks(bnn):
+    L = bnn.lib
+    assert L.bnn_pack_sign(FAKE, bnn.F32, 4, 33, FAKE, None) == bnn.ERR_SHAPE
+    assert L.bnn_pack_sign(FAKE, bnn.I32, 4, 32, FAKE, None) == bnn.ERR_DTYPE
+    assert L.bnn_pack_sign(None, bnn.F32, 4, 32, FAKE, None) == bnn.ERR_NULL
+    assert L.bnn_pack_sign(MISALIGNED, bnn.F32, 4, 32, FAKE, None) == bnn.ERR_ALIGN
+    assert L.bnn_pack_sign(None, bnn.F32, 0, 32, None, None) == bnn.OK
+    assert L.bnn_pack_sign_nchw(FAKE, bnn.F16, 1, 40, 4, 4, FAKE, None) == bnn.ERR_SHAPE
+    assert L.bnn_pack_sign_nchw(FAKE, bnn.F16, 1, 32, 0, 4, FAKE, None) == bnn.ERR_SHAPE
+    assert L.bnn_w_pack(FAKE, bnn.F32, 8, 48, 0, FAKE, None) == bnn.ERR_SHAPE
+    assert L.bnn_w_pack(FAKE, bnn.F32, 8, 64, -1, FAKE, None) == bnn.ERR_SHAPE
+    assert L.bnn_w_pack(FAKE, bnn.U32_PACKED, 8, 64, 3, FAKE, None) == bnn.ERR_DTYPE
+    assert L.bnn_w_pack(MISALIGNED, bnn.F32, 8, 64, 0, FAKE, None) == bnn.ERR_ALIGN
+    assert L.bnn_w_pack(None, bnn.F32, 0, 64, 3, None, None) == bnn.OK
+
+
+def test_workspace_queries(bnn):
+    L = bnn.lib
+    assert L.bnn_gemm_workspace_bytes(2048, 4096, bnn.F16) == 2048 * 128 * 4
+    assert L.bnn_gemm_workspace_bytes(2048, 4096, bnn.U32_PACKED) == 0
+    assert L.bnn_conv2d_workspace_bytes(32, 256, 14, 14, bnn.F32) == 32 * 14 * 14 * 8 * 4
+    assert L.bnn_conv2d_workspace_bytes(32, 256, 14, 14, bnn.U32_PACKED) == 0
+
+
+def test_last_path_starts_unset(bnn):
+    assert bnn.lib.bnn_last_path() in (0, bnn.PATH_XOR, bnn.PATH_MFMA)
+
+
+def test_auto_path_choices(bnn):
+    assert bnn.gemm_auto_path(64, 256, 512) in (bnn.PATH_XOR, bnn.PATH_MFMA)
+    for m, n, k in [(2048, 4096, 4096), (16384, 8192, 8192)]:
+        assert bnn.gemm_auto_path(m, n, k) == bnn.PATH_MFMA
+    assert bnn.conv2d_auto_path(1, 32, 20, 20, 8, 9, 1, 4, 1) == bnn.PATH_MFMA   # 81 taps

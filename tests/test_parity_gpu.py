@@ -1,0 +1,274 @@
+"""GPU parity: libbnn (through its C ABI) against the CPU oracle.
+
+Integer results (packed words, int32 accumulators) must be bit-exact. Scaled
+outputs: float32 within 1e-6 relative of y = acc * (scale_a * scale_w)
+computed in double by the oracle (exactly 0 where acc is 0); float16 and
+bfloat16 within one unit in the last place of the output type at y. The
+kernel's own error is float32 rounding of acc * alpha (<= 2^-23 relative)
+followed by one round-to-nearest-even to the output type.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+PATHS = ["xor", "mfma", "auto"]
+
+
+@pytest.fixture(scope="module")
+def bnn():
+    import convolution_bnn_pack_amd as m
+    return m
+
+
+@pytest.fixture(scope="module")
+def orc(oracle_lib):
+    return oracle_lib
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _ulp(y: np.ndarray, frac_bits: int, min_spacing: float) -> np.ndarray:
+    mant, exp = np.frexp(np.abs(y))                      # |y| = mant * 2^exp, mant in [0.5, 1)
+    return np.maximum(np.ldexp(1.0, exp - 1 - frac_bits), min_spacing)
+
+
+def check_scaled(out: torch.Tensor, acc: torch.Tensor, y: torch.Tensor, what: str):
+    o = out.detach().cpu().double().numpy()
+    yy = y.numpy()
+    a = acc.numpy()
+    assert o.shape == yy.shape, what
+    assert np.all(o[a == 0] == 0.0), f"{what}: zero accumulators must give exact 0"
+    if out.dtype == torch.float32:
+        err = np.abs(o - yy)
+        bad = err > 1e-6 * np.abs(yy)
+    elif out.dtype == torch.float16:
+        bad = np.abs(o - yy) > _ulp(yy, 10, 2.0 ** -24)
+    else:
+        bad = np.abs(o - yy) > _ulp(yy, 7, 2.0 ** -133)
+    assert not bad.any(), f"{what}: {int(bad.sum())} outputs outside tolerance, first at {np.argwhere(bad)[0]}"
+
+
+# ----------------------------------------------------------------------------- packing
+
+@pytest.mark.parametrize("tdt", [torch.float32, torch.float16, torch.bfloat16])
+def test_pack_rows_bit_exact(bnn, orc, tdt):
+    g = torch.Generator().manual_seed(21)
+    for rows, k in [(1, 32), (3, 64), (17, 96), (64, 512), (5, 4096), (333, 1024), (1000, 32)]:
+        x = synth.inject_edges(torch.randn((rows, k), generator=g).to(tdt), rows * 7 + k, max(1, rows * k // 20))
+        _say(f"pack_rows {tdt} {rows}x{k}")
+        got = bnn.pack_sign(x.to(DEV)).cpu()
+        assert torch.equal(got, orc.pack_rows(x)), (rows, k)
+
+
+@pytest.mark.parametrize("tdt", [torch.float32, torch.float16, torch.bfloat16])
+def test_pack_nchw_bit_exact(bnn, orc, tdt):
+    g = torch.Generator().manual_seed(22)
+    for shape in [(1, 32, 1, 1), (2, 64, 5, 3), (3, 96, 7, 9), (2, 256, 14, 14), (1, 128, 28, 28),
+                  (2, 32, 4, 4), (1, 64, 3, 8)]:
+        x = synth.inject_edges(torch.randn(shape, generator=g).to(tdt), sum(shape), max(1, math.prod(shape) // 20))
+        _say(f"pack_nchw {tdt} {shape}")
+        got = bnn.pack_sign_nchw(x.to(DEV)).cpu()
+        assert torch.equal(got, orc.pack_nchw(x)), shape
+
+
+def test_w_pack_bit_exact(bnn, orc):
+    g = torch.Generator().manual_seed(23)
+    for tdt in (torch.float32, torch.float16, torch.bfloat16):
+        w = synth.inject_edges(torch.randn((70, 160), generator=g).to(tdt), 1, 300)
+        assert torch.equal(bnn.w_pack(w.to(DEV)).cpu(), orc.pack_rows(w))
+        for ks in (1, 3, 5):
+            wc = synth.inject_edges(torch.randn((37, 64, ks, ks), generator=g).to(tdt), ks, 300)
+            assert torch.equal(bnn.w_pack(wc.to(DEV)).cpu(), orc.pack_conv_weight(wc)), (tdt, ks)
+
+
+def test_pack_rows_large_stream(bnn, orc):
+    # the activation of the large linear workload is 16384 x 8192 bf16; check a slice of rows
+    # of the same width plus a ragged word count through the flat stream
+    x = torch.randn((2049, 8192), generator=torch.Generator().manual_seed(24)).bfloat16()
+    got = bnn.pack_sign(x.to(DEV)).cpu()
+    assert torch.equal(got, orc.pack_rows(x))
+
+
+# ----------------------------------------------------------------------------- workloads
+
+LINEAR = ["linear_64x256x512_f32", "linear_2048x4096x4096_f16"]
+CONV = ["conv_resnet18_s3_f32", "conv_down_s2_f16", "conv_dil2_f16"]
+
+
+@pytest.mark.parametrize("name", LINEAR)
+def test_linear_workload(bnn, orc, name):
+    wl = synth.WORKLOADS[name]
+    x, w, sa, sw = synth.make_inputs(wl)
+    acc = orc.linear_acc(x, w)
+    y = orc.scale(acc, sa, sw)
+    xd, wp = x.to(DEV), bnn.w_pack(w.to(DEV))
+    for path in PATHS:
+        _say(f"{name} path={path}")
+        got = bnn.gemm(xd, wp, sa, sw, path=path, out_dtype=torch.int32)
+        assert torch.equal(got.cpu(), acc), f"{name} {path}: accumulators differ"
+        out = bnn.gemm(xd, wp, sa, sw, path=path, out_dtype=getattr(torch, {"f32": "float32", "f16": "float16", "bf16": "bfloat16"}[wl.out_dtype]))
+        check_scaled(out, acc, y, f"{name} {path}")
+        # pre-packed activations give the same result
+        xp = bnn.pack_sign(xd)
+        got2 = bnn.gemm(xp, wp, sa, sw, path=path, out_dtype=torch.int32, k=wl.k)
+        assert torch.equal(got2.cpu(), acc)
+    if name == "linear_64x256x512_f32":
+        out = bnn.gemm(xd, wp, sa, sw)                      # scale product 0.125 is dyadic: exact
+        assert torch.equal(out.cpu().double(), y)
+
+
+@pytest.mark.parametrize("name", CONV)
+def test_conv_workload(bnn, orc, name):
+    wl = synth.WORKLOADS[name]
+    x, w, sa, sw = synth.make_inputs(wl)
+    acc = orc.conv2d_acc(x, w, wl.stride, wl.padding, wl.dilation)
+    y = orc.scale(acc, sa, sw)
+    kv = orc.conv2d_kvalid(wl.c, wl.h, wl.w, wl.ks, wl.stride, wl.padding, wl.dilation)
+    assert bool(((acc - kv) % 2 == 0).all()) and bool((acc.abs() <= kv).all())
+    xd, wp = x.to(DEV), bnn.w_pack(w.to(DEV))
+    out_t = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[wl.out_dtype]
+    for path in PATHS:
+        _say(f"{name} path={path}")
+        got = bnn.conv2d(xd, wp, sa, sw, wl.ks, wl.stride, wl.padding, wl.dilation, path=path,
+                         out_dtype=torch.int32)
+        assert torch.equal(got.cpu(), acc), f"{name} {path}: accumulators differ"
+        out = bnn.conv2d(xd, wp, sa, sw, wl.ks, wl.stride, wl.padding, wl.dilation, path=path,
+                         out_dtype=out_t)
+        check_scaled(out, acc, y, f"{name} {path}")
+        xp = bnn.pack_sign_nchw(xd)
+        got2 = bnn.conv2d(xp, wp, sa, sw, wl.ks, wl.stride, wl.padding, wl.dilation, path=path,
+                          out_dtype=torch.int32)
+        assert torch.equal(got2.cpu(), acc)
+
+
+def test_large_linear_sampled(bnn, orc):
+    """16384 x 8192 x 8192, bf16 activations packed on the fly, f32 out, in the launch
+    configuration the benchmark uses: sampled rows against the oracle, every output
+    against the parity and bound invariants."""
+    wl = synth.WORKLOADS["linear_16384x8192x8192_bf16"]
+    x, w, sa, sw = synth.make_inputs(wl)
+    rows = list(range(0, wl.m, 331)) + [wl.m - 1, 127, 128, 8191, 8192]
+    acc_s = orc.linear_acc(x, w, rows=rows)
+    y_s = orc.scale(acc_s, sa, sw)
+    xd, wp = x.to(DEV), bnn.w_pack(w.to(DEV))
+    del w
+    for path in ("mfma", "xor"):
+        _say(f"large linear path={path}")
+        got = bnn.gemm(xd, wp, sa, sw, path=path, out_dtype=torch.int32)
+        torch.cuda.synchronize()
+        assert torch.equal(got[rows].cpu(), acc_s), path
+        assert bool(((got - wl.k) % 2 == 0).all()) and bool((got.abs() <= wl.k).all())
+        del got
+        out = bnn.gemm(xd, wp, sa, sw, path=path, out_dtype=torch.float32)
+        check_scaled(out[rows], acc_s, y_s, f"large linear {path}")
+        del out
+    assert bnn.gemm_auto_path(wl.m, wl.n, wl.k) == bnn.PATH_MFMA
+
+
+# ----------------------------------------------------------------------------- sweeps and edges
+
+def test_random_linear_sweep(bnn, orc):
+    for seed in range(40):
+        c = synth.random_linear_case(1000 + seed)
+        acc = orc.linear_acc(c["x"], c["w"])
+        y = orc.scale(acc, c["scale_a"], c["scale_w"])
+        xd, wp = c["x"].to(DEV), bnn.w_pack(c["w"].to(DEV))
+        out_t = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[c["out_dtype"]]
+        for path in PATHS:
+            got = bnn.gemm(xd, wp, c["scale_a"], c["scale_w"], path=path, out_dtype=torch.int32)
+            assert torch.equal(got.cpu(), acc), (seed, path, c["m"], c["n"], c["k"])
+            out = bnn.gemm(xd, wp, c["scale_a"], c["scale_w"], path=path, out_dtype=out_t)
+            check_scaled(out, acc, y, f"linear sweep seed {seed} {path}")
+
+
+def test_random_conv_sweep(bnn, orc):
+    for seed in range(40):
+        c = synth.random_conv_case(2000 + seed)
+        acc = orc.conv2d_acc(c["x"], c["w_"], c["stride"], c["padding"], c["dilation"])
+        y = orc.scale(acc, c["scale_a"], c["scale_w"])
+        xd, wp = c["x"].to(DEV), bnn.w_pack(c["w_"].to(DEV))
+        out_t = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[c["out_dtype"]]
+        for path in PATHS:
+            args = (c["scale_a"], c["scale_w"], c["ks"], c["stride"], c["padding"], c["dilation"])
+            got = bnn.conv2d(xd, wp, *args, path=path, out_dtype=torch.int32)
+            key = (seed, path, tuple(c["x"].shape), c["o"], c["ks"], c["stride"], c["padding"], c["dilation"])
+            assert torch.equal(got.cpu(), acc), key
+            out = bnn.conv2d(xd, wp, *args, path=path, out_dtype=out_t)
+            check_scaled(out, acc, y, f"conv sweep {key}")
+
+
+def test_edge_values_in_both_operands(bnn, orc):
+    g = torch.Generator().manual_seed(31)
+    for tdt in (torch.float32, torch.float16, torch.bfloat16):
+        x = synth.inject_edges(torch.randn((67, 320), generator=g).to(tdt), 1, 2000)
+        w = synth.inject_edges(torch.randn((45, 320), generator=g).to(tdt), 2, 2000)
+        acc = orc.linear_acc(x, w)
+        wp = bnn.w_pack(w.to(DEV))
+        for path in ("xor", "mfma"):
+            assert torch.equal(bnn.gemm(x.to(DEV), wp, 1.0, 1.0, path=path, out_dtype=torch.int32).cpu(), acc)
+        xc = synth.inject_edges(torch.randn((2, 64, 6, 5), generator=g).to(tdt), 3, 300)
+        wc = synth.inject_edges(torch.randn((9, 64, 3, 3), generator=g).to(tdt), 4, 300)
+        accc = orc.conv2d_acc(xc, wc, 1, 1, 1)
+        wpc = bnn.w_pack(wc.to(DEV))
+        for path in ("xor", "mfma"):
+            got = bnn.conv2d(xc.to(DEV), wpc, 1.0, 1.0, 3, 1, 1, 1, path=path, out_dtype=torch.int32)
+            assert torch.equal(got.cpu(), accc)
+
+
+def test_closed_form_padding_map(bnn, orc):
+    # all +1 activations and weights: every output equals its number of real taps
+    for (h, s, p, d) in [(14, 1, 1, 1), (28, 2, 1, 1), (28, 1, 2, 2), (5, 3, 3, 2)]:
+        x = torch.ones((2, 64, h, h), device=DEV)
+        wp = bnn.w_pack(torch.ones((8, 64, 3, 3), device=DEV))
+        kv = orc.conv2d_kvalid(64, h, h, 3, s, p, d)
+        for path in ("xor", "mfma"):
+            got = bnn.conv2d(x, wp, 1.0, 1.0, 3, s, p, d, path=path, out_dtype=torch.int32).cpu()
+            assert torch.equal(got, kv.expand_as(got)), (h, s, p, d, path)
+            neg = bnn.conv2d(x, bnn.w_pack(-torch.ones((8, 64, 3, 3), device=DEV)), 1.0, 1.0, 3, s, p,
+                             d, path=path, out_dtype=torch.int32).cpu()
+            assert torch.equal(neg, -kv.expand_as(neg))
+
+
+def test_determinism_and_paths_agree(bnn):
+    g = torch.Generator().manual_seed(41)
+    x = torch.randn((1000, 1024), generator=g).half().to(DEV)
+    wp = bnn.w_pack(torch.randn((777, 1024), generator=g).half().to(DEV))
+    a = bnn.gemm(x, wp, 1.0, 1.0, path="xor", out_dtype=torch.int32)
+    b = bnn.gemm(x, wp, 1.0, 1.0, path="mfma", out_dtype=torch.int32)
+    assert torch.equal(a, b)
+    for _ in range(3):
+        assert torch.equal(bnn.gemm(x, wp, 1.0, 1.0, path="mfma", out_dtype=torch.int32), b)
+        assert torch.equal(bnn.gemm(x, wp, 1.0, 1.0, path="xor", out_dtype=torch.int32), a)
+
+
+def test_last_path_and_errors_on_device(bnn):
+    x = torch.randn((64, 64), device=DEV)
+    wp = bnn.w_pack(torch.randn((32, 64), device=DEV))
+    bnn.gemm(x, wp, 1.0, 1.0, path="mfma")
+    assert bnn.last_path() == bnn.PATH_MFMA
+    bnn.gemm(x, wp, 1.0, 1.0, path="xor")
+    assert bnn.last_path() == bnn.PATH_XOR
+    # a too-small workspace is rejected and the output is left untouched
+    out = torch.full((64, 32), 7.0, device=DEV)
+    ws = torch.empty(16, dtype=torch.uint8, device=DEV)
+    with pytest.raises(bnn.BnnError) as e:
+        bnn.gemm(x, wp, 1.0, 1.0, out=out, workspace=ws)
+    assert e.value.status == bnn.ERR_WORKSPACE
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all())
+    with pytest.raises(AssertionError):
+        bnn.pack_sign(torch.randn((4, 48), device=DEV))
+    # a misaligned view is rejected with ERR_ALIGN
+    buf = torch.randn((65 * 64,), device=DEV)
+    with pytest.raises(bnn.BnnError) as e:
+        bnn.pack_sign(buf[1:1 + 64 * 64].view(64, 64))
+    assert e.value.status == bnn.ERR_ALIGN
