@@ -21,7 +21,9 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libbnn.so")
+# BNN_LIBRARY may name another build of libbnn.so (e.g. one compiled with different tile
+# parameters); the default is the in-tree build.
+LIB_PATH = os.environ.get("BNN_LIBRARY") or os.path.join(_PKG, "libbnn.so")
 
 # bnn_dtype / bnn_path / bnn_status codes of include/bnn.h
 F32, F16, BF16, I32, U32_PACKED = 0, 1, 2, 3, 4

@@ -1,33 +1,47 @@
 // +-1-as-int8 binary contraction on the gfx950 matrix cores.
 //
-// The binary dot product is a dense contraction, so it can run on
-// v_mfma_i32_32x32x32_i8 (32x32 output, 32-deep reduction, int32 sums).
-// Signs stay bit-packed in HBM (one bit per element); a workgroup loads the
-// packed words of its A and W tiles and expands each word in registers to
-// 32 int8 values before storing them to LDS:
+// The binary dot product is a dense contraction, so it runs on
+// v_mfma_i32_32x32x32_i8 (32x32 output block, 32-deep reduction, int32
+// sums). Signs stay bit-packed in HBM; a workgroup loads the packed words of
+// its A (activation) and W (weight) tiles and expands each word in registers
+// before storing it to LDS:
 //
 //   v_perm_b32 with selector bytes 8..11 replicates bits 15 and 31 of each of
-//   its two sources into whole bytes (0x00 or 0xFF). With the sources w << 2d
-//   and w << 2d+1 (d = 0..7) every bit of w lands in exactly one byte; OR-ing
-//   0x01 turns 0xFF into -1 and 0x00 into +1. That maps a set bit (+1) to -1
-//   and a clear bit to +1, i.e. both operands are negated, which leaves every
-//   product unchanged. The byte order within a word is a fixed permutation
-//   of its 32 reduction indices, the same for A and W, so the sums are the
-//   binary dot products exactly. A padded conv tap expands to 0 bytes, so it
-//   contributes 0 with no correction.
+//   its two sources into whole bytes (0x00 or 0xFF). With the sources
+//   w << 2d and w << 2d+1 (d = 0..7) every bit of w lands in exactly one of
+//   32 bytes. The byte order is a fixed permutation of the word's 32
+//   reduction indices, the same for A and W, so the sums are unchanged.
 //
-// Tiling: a 256-thread workgroup owns a 128 (rows of A) x 128 (rows of W)
-// output tile and walks the reduction 4 words (128 signs) at a time. Each
-// of its four waves computes a 64 x 64 sub-tile as 2 x 2 MFMA blocks. The
-// MFMA computes D = W_tile * A_tile^T so that each lane's four consecutive
-// accumulators are four consecutive output features of one row: linear
-// outputs leave as 16-byte (f32) or 8-byte (f16/bf16) vector stores, conv
-// outputs as lane-contiguous NCHW runs. LDS rows are 128 bytes; their 16-byte
-// chunks are XOR-swizzled by (row >> 1) & 7 so the ds_read_b128 fragment
-// reads of 16 consecutive rows hit distinct banks.
+// Encodings (b = packed bit, 1 for a +1 sign; s = 2b - 1):
+//   W bytes  w' = -b           (the raw 0x00 / 0xFF mask)
+//   A bytes  a' = 1 - 2b = -s  (mask | 0x01), and 0 for a padded conv tap or
+//            a position past K.
+// The MFMA sum is sum a'w' = sum s_a b_w over the real terms, and since
+// s_w = 2 b_w - 1 the binary dot product is
+//   dot = sum s_a s_w = 2 * mfma - sum s_a = K_valid - 2 * popA + 2 * mfma,
+// with popA the number of set bits among the row's real A words and K_valid
+// = 32 * (number of real A words). Both are counted by the thread that loads
+// the row, so padded taps need no per-weight correction.
 //
-// Conv uses the same implicit im2col map as the XOR path (banghao.live blog
-// post, section 2, lowered without materialising the column matrix).
+// Tiling: a 256-thread workgroup (4 waves as 2 x 2) owns a BM (rows of A) x
+// BN (rows of W) output tile and walks the reduction KS words (32*KS signs)
+// per stage through two LDS buffers (one barrier per stage): while the waves
+// run the MFMAs of stage s from one buffer, the loader expands stage s+1 into
+// the other and fetches stage s+2 from global memory. Each wave holds a
+// (BM/2) x (BN/2) sub-tile as (BM/64) x (BN/64) MFMA blocks; the MFMA computes
+// D = W_tile * A_tile^T so each lane's four consecutive accumulators are four
+// consecutive output features of one row (vector stores for linear outputs,
+// lane-contiguous runs for NCHW conv outputs). LDS rows are 32*KS bytes; the
+// 16-byte chunks of a row are XOR-swizzled with a Gray code of the row index
+// so the ds_read_b128 / ds_write_b128 of 8 or 16 consecutive rows hit
+// distinct banks. Tiles are numbered so that each XCD (workgroups go
+// round-robin to the 8 XCDs) receives a contiguous run of tiles sharing A rows.
+//
+// Conv is the im2col lowering of the banghao.live blog post, section 2,
+// computed implicitly: A row m is output pixel (b, oh, ow) and reduction word
+// q = tap * CW + cw reads activation word [b][oh*s - p + kh*d][ow*s - p + kw*d][cw].
+#include <utility>
+
 #include "launch.h"
 
 namespace bnn {
@@ -36,7 +50,29 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 128, BN = 128, BKW = 4, ROWB = BKW * 32;  // bytes per LDS row
+template <int BM_, int BN_, int KS_, int PD_>
+struct Tile {
+  static constexpr int BM = BM_, BN = BN_, KS = KS_;
+  static constexpr int PD = PD_;                    // stages of raw words in flight (register sets)
+  static constexpr int UNROLL = PD % 2 == 0 ? PD : 2 * PD;  // lcm(2, PD): LDS parity x register set
+  static constexpr int FM = BM / 64, FN = BN / 64;  // MFMA blocks per wave (wave tile BM/2 x BN/2)
+  static constexpr int ROWB = KS * 32;              // LDS bytes per row per stage
+  static constexpr int CHUNKS = ROWB / 16;
+  static constexpr int BUF = (BM + BN) * ROWB;      // one LDS buffer: A rows, then W rows
+  // loader split: every thread expands A_WPT consecutive words of one A row and W_WPT
+  // consecutive words of one W row per stage
+  static constexpr int A_WPT = BM * KS / 256, A_TPR = KS / A_WPT;
+  static constexpr int W_WPT = BN * KS / 256, W_TPR = KS / W_WPT;
+  static constexpr int SWZ_SHIFT = CHUNKS == 8 ? 0 : CHUNKS == 4 ? 1 : 2;
+  static_assert(A_WPT >= 1 && KS % A_WPT == 0 && W_WPT >= 1 && KS % W_WPT == 0, "loader split");
+};
+
+// Physical 16-byte chunk of logical chunk c in LDS row r.
+template <class T>
+__device__ __forceinline__ int swz(int r, int c) {
+  const int g = r >> T::SWZ_SHIFT;
+  return c ^ ((g ^ (g >> 1)) & (T::CHUNKS - 1));
+}
 
 struct PixelCoord {
   int b, ihb, iwb;
@@ -51,163 +87,318 @@ __device__ __forceinline__ PixelCoord pixel_coord(const Contraction& p, int m) {
   return {b, oh * p.stride - p.pad, ow * p.stride - p.pad};
 }
 
-// Words q0..q0+3 of one tile row plus a validity flag per word (invalid: outside
-// the matrix, past K, or a padded conv tap).
-template <bool CONV, bool IS_A>
-__device__ __forceinline__ void load_row4(const Contraction& p, int row, const PixelCoord& pc,
-                                          int q0, uint32_t r[4], bool ok[4]) {
-  if constexpr (!CONV || !IS_A) {
-    const uint32_t* src = IS_A ? p.a : p.w;
-    const int rows = IS_A ? p.M : p.N;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int q = q0 + i;
-      ok[i] = row < rows && q < p.KW;
-      r[i] = ok[i] ? src[(int64_t)row * p.KW + q] : 0u;
-    }
+__device__ __forceinline__ int clampi(int v, int hi) { return v < 0 ? 0 : (v > hi ? hi : v); }
+
+// NW consecutive words as one 4/8/16-byte load (p must be NW*4-byte aligned).
+template <int NW>
+__device__ __forceinline__ void load_vec(const uint32_t* ptr, uint32_t r[NW]) {
+  if constexpr (NW == 4) {
+    const uint4 v = *reinterpret_cast<const uint4*>(ptr);
+    r[0] = v.x; r[1] = v.y; r[2] = v.z; r[3] = v.w;
+  } else if constexpr (NW == 2) {
+    const uint2 v = *reinterpret_cast<const uint2*>(ptr);
+    r[0] = v.x; r[1] = v.y;
   } else {
+#pragma unroll
+    for (int i = 0; i < NW; i++) r[i] = ptr[i];
+  }
+}
+
+// NW consecutive A words of row m (m < M known by `mok`) from word q0, raw; ok[i] is false
+// past K or for a padded conv tap (the word must then be treated as 0). Addresses are
+// clamped into the tensor so the loads are unconditional, and the validity select is
+// applied only when the words are expanded a stage later: selecting on a loaded value
+// here would make the wave wait for the load right away and defeat the prefetch.
+// VEC: the NW words are contiguous and aligned (K, or C for conv, is a multiple of the
+// stage width and q0 % NW == 0), so they arrive in one vector load instead of NW
+// scattered dword loads -- each lane reads a different row, so fewer, wider requests
+// matter.
+template <int NW, bool CONV, bool VEC>
+__device__ __forceinline__ void load_a(const Contraction& p, int m, bool mok, const PixelCoord& pc,
+                                       int q0, uint32_t r[NW], bool ok[NW]) {
+  if constexpr (CONV) {
     int tap = q0 / p.CW;
     int cw = q0 - tap * p.CW;
     int kh = tap / p.ks;
     int kw = tap - kh * p.ks;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int q = q0 + i;
+    if constexpr (VEC) {
+      // the NW words share one tap
       const int ih = pc.ihb + kh * p.dil, iw = pc.iwb + kw * p.dil;
-      ok[i] = row < p.M && q < p.KW && ih >= 0 && ih < p.H && iw >= 0 && iw < p.W;
-      r[i] = ok[i] ? p.a[(((int64_t)pc.b * p.H + ih) * p.W + iw) * p.CW + cw] : 0u;
-      if (++cw == p.CW) {
-        cw = 0;
-        if (++kw == p.ks) {
-          kw = 0;
-          ++kh;
+      const bool tok = mok && q0 < p.KW && ih >= 0 && ih < p.H && iw >= 0 && iw < p.W;
+      const int cwc = q0 < p.KW ? cw : 0;
+      load_vec<NW>(p.a + (((int64_t)pc.b * p.H + clampi(ih, p.H - 1)) * p.W + clampi(iw, p.W - 1)) * p.CW + cwc, r);
+#pragma unroll
+      for (int i = 0; i < NW; i++) ok[i] = tok;
+    } else {
+#pragma unroll
+      for (int i = 0; i < NW; i++) {
+        const int q = q0 + i;
+        const int ih = pc.ihb + kh * p.dil, iw = pc.iwb + kw * p.dil;
+        ok[i] = mok && q < p.KW && ih >= 0 && ih < p.H && iw >= 0 && iw < p.W;
+        r[i] = p.a[(((int64_t)pc.b * p.H + clampi(ih, p.H - 1)) * p.W + clampi(iw, p.W - 1)) * p.CW + cw];
+        if (++cw == p.CW) {
+          cw = 0;
+          if (++kw == p.ks) {
+            kw = 0;
+            ++kh;
+          }
         }
+      }
+    }
+  } else {
+    const int64_t rowoff = (int64_t)(mok ? m : 0) * p.KW;
+    if constexpr (VEC) {
+      load_vec<NW>(p.a + rowoff + (q0 < p.KW ? q0 : p.KW - NW), r);
+#pragma unroll
+      for (int i = 0; i < NW; i++) ok[i] = mok && q0 < p.KW;
+    } else {
+#pragma unroll
+      for (int i = 0; i < NW; i++) {
+        const int q = q0 + i;
+        ok[i] = mok && q < p.KW;
+        r[i] = p.a[rowoff + (q < p.KW ? q : p.KW - 1)];
       }
     }
   }
 }
 
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
-
-// Expand 4 packed words of one row to 128 int8 +-1 bytes (0 bytes for invalid
-// words) and store them to the row's LDS line. Word i fills reduction chunk i
-// (32 bytes = 16-byte halves 2i and 2i+1).
-__device__ __forceinline__ void expand_store(uint8_t* line, int row, const uint32_t r[4],
-                                             const bool ok[4]) {
+// NW consecutive W words of row n from word q0, raw; ok[i] false outside the matrix or past K.
+template <int NW, bool VEC>
+__device__ __forceinline__ void load_w(const Contraction& p, int n, int q0, uint32_t r[NW],
+                                       bool ok[NW]) {
+  const bool nok = n < p.N;
+  const int64_t rowoff = (int64_t)(nok ? n : 0) * p.KW;
+  if constexpr (VEC) {
+    load_vec<NW>(p.w + rowoff + (q0 < p.KW ? q0 : p.KW - NW), r);
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const uint32_t w = r[i];
-    const uint32_t keep = ok[i] ? 0xFFFFFFFFu : 0u;
-    const uint32_t ones = ok[i] ? 0x01010101u : 0u;
-    uint32_t y[8];
+    for (int i = 0; i < NW; i++) ok[i] = nok && q0 < p.KW;
+  } else {
 #pragma unroll
-    for (int d = 0; d < 8; d++) {
-      const uint32_t m = __builtin_amdgcn_perm(w << (2 * d + 1), w << (2 * d), 0x0B0A0908u);
-      y[d] = (m & keep) | ones;
+    for (int i = 0; i < NW; i++) {
+      const int q = q0 + i;
+      ok[i] = nok && q < p.KW;
+      r[i] = p.w[rowoff + (q < p.KW ? q : p.KW - 1)];
     }
-    *reinterpret_cast<uint4*>(line + 16 * swz(row, 2 * i)) = make_uint4(y[0], y[1], y[2], y[3]);
-    *reinterpret_cast<uint4*>(line + 16 * swz(row, 2 * i + 1)) = make_uint4(y[4], y[5], y[6], y[7]);
   }
 }
 
-template <int OUT, bool CONV>
+// Expand one packed word into the 32 bytes of reduction chunk `word` of an LDS row:
+// bytes (mask & keep) | ones, mask = 0xFF per set bit.
+template <class T>
+__device__ __forceinline__ void expand_word(uint8_t* buf, int lrow, int word, uint32_t w,
+                                            uint32_t keep, uint32_t ones) {
+  uint32_t y[8];
+#pragma unroll
+  for (int d = 0; d < 8; d++) {
+    const uint32_t m = __builtin_amdgcn_perm(w << (2 * d + 1), w << (2 * d), 0x0B0A0908u);
+    y[d] = (m & keep) | ones;
+  }
+  uint8_t* line = buf + lrow * T::ROWB;
+  *reinterpret_cast<uint4*>(line + 16 * swz<T>(lrow, 2 * word)) = make_uint4(y[0], y[1], y[2], y[3]);
+  *reinterpret_cast<uint4*>(line + 16 * swz<T>(lrow, 2 * word + 1)) = make_uint4(y[4], y[5], y[6], y[7]);
+}
+
+// Tile index -> (m-tile, n-tile): contiguous runs of tiles per XCD, n fastest.
+__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int total = tiles_m * tiles_n;
+  int t = blockIdx.x;
+  if ((total & 7) == 0) t = (t & 7) * (total >> 3) + (t >> 3);
+  tm = t / tiles_n;
+  tn = t - tm * tiles_n;
+}
+
+// One LDS fragment read (16 bytes per lane) of row r, reduction chunk c.
+template <class T>
+__device__ __forceinline__ v4i lds_frag(const uint8_t* buf, int r, int c) {
+  return *reinterpret_cast<const v4i*>(buf + r * T::ROWB + 16 * swz<T>(r, c));
+}
+
+template <class T, int OUT, bool CONV, bool VEC>
 __global__ __launch_bounds__(256) void mfma_kernel(Contraction p) {
-  __shared__ __attribute__((aligned(16))) uint8_t As[BM * ROWB];
-  __shared__ __attribute__((aligned(16))) uint8_t Ws[BN * ROWB];
+  // two distinct arrays (not one array indexed by stage parity) so the compiler can
+  // tell the expansion's writes from the fragment reads
+  __shared__ __attribute__((aligned(16))) uint8_t lds0[T::BUF];
+  __shared__ __attribute__((aligned(16))) uint8_t lds1[T::BUF];
+  __shared__ int rowk[T::BM];  // K_valid - 2 * popA per A row of the tile
+
+  constexpr int MPK = T::FN * T::FM;            // MFMAs per k-step
+  constexpr int NM = MPK * T::KS;               // MFMAs per stage
+  constexpr int RPK = T::FN + T::FM;            // fragment reads per k-step
+  constexpr int NWORD = T::A_WPT + T::W_WPT;    // words this thread expands per stage
+  constexpr int NU = NWORD * 8;                 // expansion units (one output dword each)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
-  const int tiles_n = (p.N + BN - 1) / BN;
-  const int m0 = (blockIdx.x / tiles_n) * BM;
-  const int n0 = (blockIdx.x % tiles_n) * BN;
+  const int tiles_m = (p.M + T::BM - 1) / T::BM, tiles_n = (p.N + T::BN - 1) / T::BN;
+  int tm, tn;
+  tile_coords(tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * T::BM, n0 = tn * T::BN;
 
-  // loader role: threads 0..127 expand A row tid, threads 128..255 W row tid-128
-  const bool is_a = tid < BM;
-  const int lrow = is_a ? tid : tid - BM;
-  const int grow = is_a ? m0 + lrow : n0 + lrow;
-  uint8_t* line = (is_a ? As : Ws) + lrow * ROWB;
+  // loader roles
+  const int a_row = tid / T::A_TPR, a_q = (tid % T::A_TPR) * T::A_WPT;
+  const int w_row = tid / T::W_TPR, w_q = (tid % T::W_TPR) * T::W_WPT;
+  const int am = m0 + a_row, wn_row = n0 + w_row;
+  const bool amok = am < p.M;
   PixelCoord pc{0, 0, 0};
-  if constexpr (CONV) {
-    if (is_a && grow < p.M) pc = pixel_coord(p, grow);
-  }
+  if constexpr (CONV) pc = pixel_coord(p, amok ? am : 0);
+  for (int i = tid; i < T::BM; i += 256) rowk[i] = 0;
+  int rowk_part = 0;  // this thread's share of 32 * (real words) - 2 * popA
 
-  uint32_t r[4];
-  bool ok[4];
-  if (is_a)
-    load_row4<CONV, true>(p, grow, pc, 0, r, ok);
-  else
-    load_row4<CONV, false>(p, grow, pc, 0, r, ok);
+  // raw words of PD stages in flight; stage t lives in register set t % PD
+  uint32_t ra[T::PD][T::A_WPT], rw[T::PD][T::W_WPT];
+  bool oka[T::PD][T::A_WPT], okw[T::PD][T::W_WPT];
+  auto load_stage = [&](int set, int q0) {
+    load_a<T::A_WPT, CONV, VEC>(p, am, amok, pc, q0 + a_q, ra[set], oka[set]);
+    load_w<T::W_WPT, VEC>(p, wn_row, q0 + w_q, rw[set], okw[set]);
+  };
 
-  v16i acc[2][2];
+  // expansion of stage words: source value, OR term and LDS row / word slot of word wi
+  uint32_t src[NWORD], orv[NWORD];
+  auto prepare = [&](int set) {
 #pragma unroll
-  for (int i = 0; i < 2; i++)
+    for (int i = 0; i < T::A_WPT; i++) {
+      src[i] = oka[set][i] ? ra[set][i] : 0u;  // an invalid word expands to 0x00 bytes
+      orv[i] = oka[set][i] ? 0x01010101u : 0u;
+      rowk_part += oka[set][i] ? 32 - 2 * __popc(src[i]) : 0;
+    }
 #pragma unroll
-    for (int j = 0; j < 2; j++)
+    for (int i = 0; i < T::W_WPT; i++) {
+      src[T::A_WPT + i] = okw[set][i] ? rw[set][i] : 0u;
+      orv[T::A_WPT + i] = 0u;
+    }
+  };
+  uint32_t y[NU];
+  auto expand_unit = [&](uint8_t* buf, int u) {
+    const int wi = u >> 3, d = u & 7;
+    const uint32_t w = src[wi];
+    y[u] = __builtin_amdgcn_perm(w << (2 * d + 1), w << (2 * d), 0x0B0A0908u);
+    if (wi < T::A_WPT) y[u] |= orv[wi];
+    if ((d & 3) == 3) {
+      const int lrow = wi < T::A_WPT ? a_row : T::BM + w_row;
+      const int word = wi < T::A_WPT ? a_q + wi : w_q + (wi - T::A_WPT);
+      uint8_t* line = buf + lrow * T::ROWB;
+      *reinterpret_cast<uint4*>(line + 16 * swz<T>(lrow, 2 * word + (d >> 2))) =
+          make_uint4(y[u - 3], y[u - 2], y[u - 1], y[u]);
+    }
+  };
+
+  v16i acc[T::FN][T::FM];
+#pragma unroll
+  for (int i = 0; i < T::FN; i++)
+#pragma unroll
+    for (int j = 0; j < T::FM; j++)
 #pragma unroll
       for (int e = 0; e < 16; e++) acc[i][j][e] = 0;
 
   const int fr = lane & 31, half = lane >> 5;
-  for (int kt = 0; kt < p.KW; kt += BKW) {
-    __syncthreads();
-    expand_store(line, lrow, r, ok);
-    __syncthreads();
-    if (kt + BKW < p.KW) {
-      if (is_a)
-        load_row4<CONV, true>(p, grow, pc, kt + BKW, r, ok);
-      else
-        load_row4<CONV, false>(p, grow, pc, kt + BKW, r, ok);
+  v4i fa[2][T::FM], fw[2][T::FN];
+  auto read_frag = [&](const uint8_t* cur, int kk, int j) {
+    const int fb = kk & 1;
+    if (j < T::FM) {
+      fa[fb][j] = lds_frag<T>(cur, wm * (T::BM / 2) + j * 32 + fr, 2 * kk + half);
+    } else {
+      const int f = j - T::FM;
+      fw[fb][f] = lds_frag<T>(cur, T::BM + wn * (T::BN / 2) + f * 32 + fr, 2 * kk + half);
     }
+  };
+
+  // One stage: the MFMAs over the current LDS buffer, interleaved slot by slot with the
+  // reads of the next k-step's fragments and the expansion of the next stage into the
+  // other buffer; the global loads for stage s + PD go out first. Each slot is closed by
+  // a scheduling barrier so the matrix core and the vector ALU stay busy together even
+  // with one wave per SIMD. PH = s % UNROLL is a compile-time phase, which fixes the LDS
+  // buffer parity and the register sets. Past the last stage the expansion writes
+  // zero-contribution words into a buffer that is never read again, and the loads fetch
+  // clamped, invalid words.
+  auto stage = [&](auto phase, int s) {
+    constexpr int PH = decltype(phase)::value;
+    const uint8_t* cur = (PH & 1) ? lds1 : lds0;
+    uint8_t* nxt = (PH & 1) ? lds0 : lds1;
+    load_stage(PH % T::PD, (s + T::PD) * T::KS);
 #pragma unroll
-    for (int kk = 0; kk < BKW; kk++) {
-      v4i fa[2], fw[2];
+    for (int j = 0; j < RPK; j++) read_frag(cur, 0, j);
+    prepare((PH + 1) % T::PD);
 #pragma unroll
-      for (int f = 0; f < 2; f++) {
-        const int ra = wm * 64 + f * 32 + fr;
-        const int rw = wn * 64 + f * 32 + fr;
-        fa[f] = *reinterpret_cast<const v4i*>(As + ra * ROWB + 16 * swz(ra, 2 * kk + half));
-        fw[f] = *reinterpret_cast<const v4i*>(Ws + rw * ROWB + 16 * swz(rw, 2 * kk + half));
-      }
+    for (int i = 0; i < NM; i++) {
+      const int kk = i / MPK, j = i % MPK;
+      const int fn = j / T::FM, fm = j % T::FM;
+      acc[fn][fm] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fw[kk & 1][fn], fa[kk & 1][fm],
+                                                           acc[fn][fm], 0, 0, 0);
+      if (kk + 1 < T::KS && j < RPK) read_frag(cur, kk + 1, j);
 #pragma unroll
-      for (int fn = 0; fn < 2; fn++)
+      for (int u = i * NU / NM; u < (i + 1) * NU / NM; u++) expand_unit(nxt, u);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+  };
+
+  const int nstages = (p.KW + T::KS - 1) / T::KS;
 #pragma unroll
-        for (int fm = 0; fm < 2; fm++)
-          acc[fn][fm] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fw[fn], fa[fm], acc[fn][fm], 0, 0, 0);
+  for (int t = 0; t < T::PD; t++) load_stage(t, t * T::KS);  // clamped + invalid past K
+  prepare(0);
+#pragma unroll
+  for (int u = 0; u < NU; u++) expand_unit(lds0, u);
+  __syncthreads();
+  int s = 0;
+  for (; s + T::UNROLL <= nstages; s += T::UNROLL) {
+    stage(std::integral_constant<int, 0>{}, s);
+    stage(std::integral_constant<int, 1>{}, s + 1);
+    if constexpr (T::UNROLL > 2) {
+      stage(std::integral_constant<int, 2>{}, s + 2);
+      stage(std::integral_constant<int, 3>{}, s + 3);
+    }
+    if constexpr (T::UNROLL > 4) {
+      stage(std::integral_constant<int, 4>{}, s + 4);
+      stage(std::integral_constant<int, 5>{}, s + 5);
     }
   }
+  if (s < nstages) stage(std::integral_constant<int, 0>{}, s);
+  if (s + 1 < nstages) stage(std::integral_constant<int, 1>{}, s + 1);
+  if constexpr (T::UNROLL > 2) {
+    if (s + 2 < nstages) stage(std::integral_constant<int, 2>{}, s + 2);
+    if (s + 3 < nstages) stage(std::integral_constant<int, 3>{}, s + 3);
+  }
+  if constexpr (T::UNROLL > 4) {
+    if (s + 4 < nstages) stage(std::integral_constant<int, 4>{}, s + 4);
+  }
+
+  atomicAdd(&rowk[a_row], rowk_part);
+  __syncthreads();
 
   // epilogue: acc[fn][fm][e] is output (row m, feature n) with
-  //   m = m0 + wm*64 + fm*32 + (lane & 31)
-  //   n = n0 + wn*64 + fn*32 + 8*(e/4) + 4*(lane/32) + e%4
+  //   m = m0 + wm*BM/2 + fm*32 + (lane & 31)
+  //   n = n0 + wn*BN/2 + fn*32 + 8*(e/4) + 4*(lane/32) + e%4
   const int hw = CONV ? p.Ho * p.Wo : 1;
 #pragma unroll
-  for (int fm = 0; fm < 2; fm++) {
-    const int m = m0 + wm * 64 + fm * 32 + fr;
+  for (int fm = 0; fm < T::FM; fm++) {
+    const int ml = wm * (T::BM / 2) + fm * 32 + fr;
+    const int m = m0 + ml;
     if (m >= p.M) continue;
+    const int base_k = rowk[ml];
     int b = 0, pix = 0;
     if constexpr (CONV) {
       b = m / hw;
       pix = m - b * hw;
     }
 #pragma unroll
-    for (int fn = 0; fn < 2; fn++) {
+    for (int fn = 0; fn < T::FN; fn++) {
 #pragma unroll
       for (int g = 0; g < 4; g++) {
-        const int n = n0 + wn * 64 + fn * 32 + 8 * g + 4 * half;
-        const int a0 = acc[fn][fm][4 * g], a1 = acc[fn][fm][4 * g + 1];
-        const int a2 = acc[fn][fm][4 * g + 2], a3 = acc[fn][fm][4 * g + 3];
+        const int n = n0 + wn * (T::BN / 2) + fn * 32 + 8 * g + 4 * half;
+        int av[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++) av[j] = base_k + 2 * acc[fn][fm][4 * g + j];
         if constexpr (!CONV) {
           const int64_t base = (int64_t)m * p.N + n;
           if (n + 3 < p.N && (p.N & 3) == 0) {
-            store4<OUT>(p.out, base, a0, a1, a2, a3, p.alpha);
+            store4<OUT>(p.out, base, av[0], av[1], av[2], av[3], p.alpha);
           } else {
-            const int av[4] = {a0, a1, a2, a3};
 #pragma unroll
             for (int j = 0; j < 4; j++)
               if (n + j < p.N) store1<OUT>(p.out, base + j, av[j], p.alpha);
           }
         } else {
-          const int av[4] = {a0, a1, a2, a3};
 #pragma unroll
           for (int j = 0; j < 4; j++)
             if (n + j < p.N) store1<OUT>(p.out, ((int64_t)b * p.N + n + j) * hw + pix, av[j], p.alpha);
@@ -217,17 +408,52 @@ __global__ __launch_bounds__(256) void mfma_kernel(Contraction p) {
   }
 }
 
-template <bool CONV>
-hipError_t launch_mfma_t(const Contraction& p, int out_dtype, hipStream_t stream) {
-  const int64_t tiles = (int64_t)((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+template <class T, bool CONV, bool VEC>
+hipError_t launch_tile_v(const Contraction& p, int out_dtype, hipStream_t stream) {
+  const int64_t tiles = (int64_t)((p.M + T::BM - 1) / T::BM) * ((p.N + T::BN - 1) / T::BN);
   const dim3 grid((unsigned)tiles), block(256);
   switch (out_dtype) {
-    case kF32: hipLaunchKernelGGL((mfma_kernel<kF32, CONV>), grid, block, 0, stream, p); break;
-    case kF16: hipLaunchKernelGGL((mfma_kernel<kF16, CONV>), grid, block, 0, stream, p); break;
-    case kBF16: hipLaunchKernelGGL((mfma_kernel<kBF16, CONV>), grid, block, 0, stream, p); break;
-    default: hipLaunchKernelGGL((mfma_kernel<kI32, CONV>), grid, block, 0, stream, p); break;
+    case kF32: hipLaunchKernelGGL((mfma_kernel<T, kF32, CONV, VEC>), grid, block, 0, stream, p); break;
+    case kF16: hipLaunchKernelGGL((mfma_kernel<T, kF16, CONV, VEC>), grid, block, 0, stream, p); break;
+    case kBF16: hipLaunchKernelGGL((mfma_kernel<T, kBF16, CONV, VEC>), grid, block, 0, stream, p); break;
+    default: hipLaunchKernelGGL((mfma_kernel<T, kI32, CONV, VEC>), grid, block, 0, stream, p); break;
   }
   return hipGetLastError();
+}
+
+// Vector loads need every thread's words of a stage to be contiguous and aligned: the
+// stage width divides K (linear) or C/32 (conv, so a stage never straddles taps), and
+// both operand bases are 16-byte aligned.
+template <class T, bool CONV>
+hipError_t launch_tile(const Contraction& p, int out_dtype, hipStream_t stream) {
+  const bool aligned = (reinterpret_cast<uintptr_t>(p.a) % 16) == 0 &&
+                       (reinterpret_cast<uintptr_t>(p.w) % 16) == 0;
+  const bool vec = aligned && (CONV ? (p.CW % T::KS) == 0 : (p.KW % T::KS) == 0);
+  return vec ? launch_tile_v<T, CONV, true>(p, out_dtype, stream)
+             : launch_tile_v<T, CONV, false>(p, out_dtype, stream);
+}
+
+#ifndef BNN_MFMA_PD_L
+#define BNN_MFMA_PD_L 2
+#endif
+#ifndef BNN_MFMA_PD_M
+#define BNN_MFMA_PD_M 4
+#endif
+using TileL = Tile<256, 256, 4, BNN_MFMA_PD_L>;
+using TileM = Tile<128, 256, 4, BNN_MFMA_PD_M>;
+using TileS = Tile<128, 128, 4, BNN_MFMA_PD_M>;
+
+int64_t count_tiles(const Contraction& p, int bm, int bn) {
+  return (int64_t)((p.M + bm - 1) / bm) * ((p.N + bn - 1) / bn);
+}
+
+// Largest tile that still gives every compute unit a workgroup; the smallest otherwise.
+template <bool CONV>
+hipError_t launch_mfma_t(const Contraction& p, int out_dtype, hipStream_t stream) {
+  constexpr int64_t kCUs = 256;
+  if (count_tiles(p, 256, 256) >= kCUs) return launch_tile<TileL, CONV>(p, out_dtype, stream);
+  if (count_tiles(p, 128, 256) >= kCUs) return launch_tile<TileM, CONV>(p, out_dtype, stream);
+  return launch_tile<TileS, CONV>(p, out_dtype, stream);
 }
 
 }  // namespace
