@@ -119,8 +119,11 @@ def main():
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
     xd = x.to(dev)
     lib = bnn.lib
-    stream = torch.cuda.current_stream(dev).cuda_stream
     xcode = bnn._DT[xd.dtype]
+
+    def cur_stream():
+        # read at call time: under graph capture the current stream is the capture stream
+        return torch.cuda.current_stream().cuda_stream
 
     if pack_only:
         # two copies of the 268 MB activation, alternated, so every pass reads HBM rather than
@@ -128,13 +131,11 @@ def main():
         xs = [xd, xd.clone()]
         words = wl.m * wl.k // 32
         xp = torch.empty((wl.m, wl.k // 32), dtype=torch.int32, device=dev)
-        ops = None
         bytes_per = wl.m * wl.k * 2 + words * 4
         path_used = None
-
-        def launches(i):
-            return [lambda: lib.bnn_pack_sign(xs[i & 1].data_ptr(), xcode, wl.m, wl.k, xp.data_ptr(),
-                                              stream)]
+        kernels = {"pack": [lambda i: lib.bnn_pack_sign(xs[i & 1].data_ptr(), xcode, wl.m, wl.k,
+                                                        xp.data_ptr(), cur_stream())]}
+        step_fns = kernels["pack"]
     else:
         wp = bnn.w_pack(w.to(dev))
         m, n, k = wl.gemm_mnk()
@@ -144,22 +145,25 @@ def main():
         ocode = bnn._DT[out.dtype]
         if wl.kind == "linear":
             xp = torch.empty((wl.m, wl.k // 32), dtype=torch.int32, device=dev)
-            pack = lambda i: lib.bnn_pack_sign(xd.data_ptr(), xcode, wl.m, wl.k, xp.data_ptr(), stream)
-            core = lambda i: lib.bnn_gemm(xp.data_ptr(), bnn.U32_PACKED, wp.data_ptr(), wl.m, wl.n, wl.k,
-                                          sa, sw, path, out.data_ptr(), ocode, None, 0, stream)
+            pack = lambda i: lib.bnn_pack_sign(xd.data_ptr(), xcode, wl.m, wl.k, xp.data_ptr(),
+                                               cur_stream())
+            core = lambda i: lib.bnn_gemm(xp.data_ptr(), bnn.U32_PACKED, wp.data_ptr(), wl.m, wl.n,
+                                          wl.k, sa, sw, path, out.data_ptr(), ocode, None, 0,
+                                          cur_stream())
             path_used = path if path else bnn.gemm_auto_path(wl.m, wl.n, wl.k)
         else:
             xp = torch.empty((wl.batch, wl.h, wl.w, wl.c // 32), dtype=torch.int32, device=dev)
             pack = lambda i: lib.bnn_pack_sign_nchw(xd.data_ptr(), xcode, wl.batch, wl.c, wl.h, wl.w,
-                                                    xp.data_ptr(), stream)
-            core = lambda i: lib.bnn_conv2d(xp.data_ptr(), bnn.U32_PACKED, wl.batch, wl.c, wl.h, wl.w,
-                                            wp.data_ptr(), wl.o, sa, sw, wl.ks, wl.stride, wl.padding,
-                                            wl.dilation, path, out.data_ptr(), ocode, None, 0, stream)
-            path_used = path if path else bnn.conv2d_auto_path(wl.batch, wl.c, wl.h, wl.w, wl.o, wl.ks,
-                                                               wl.stride, wl.padding, wl.dilation)
-
-        def launches(i):
-            return [lambda: pack(i), lambda: core(i)]
+                                                    xp.data_ptr(), cur_stream())
+            core = lambda i: lib.bnn_conv2d(xp.data_ptr(), bnn.U32_PACKED, wl.batch, wl.c, wl.h,
+                                            wl.w, wp.data_ptr(), wl.o, sa, sw, wl.ks, wl.stride,
+                                            wl.padding, wl.dilation, path, out.data_ptr(), ocode,
+                                            None, 0, cur_stream())
+            path_used = path if path else bnn.conv2d_auto_path(wl.batch, wl.c, wl.h, wl.w, wl.o,
+                                                               wl.ks, wl.stride, wl.padding,
+                                                               wl.dilation)
+        kernels = {"pack": [pack], "core": [core]}
+        step_fns = [pack, core]
 
     # parity spot check before timing (int32 accumulators of sampled rows / images vs the oracle)
     parity = None
@@ -177,29 +181,50 @@ def main():
         parity = bool(torch.equal(got, ref))
         log(f"parity spot check vs oracle: {parity}")
 
-    nk = 1 if pack_only else 2
+    def run(fns, i):
+        for f in fns:
+            if f(i) != 0:
+                raise RuntimeError("libbnn call failed")
+
+    # Steps are replayed from a HIP graph so that host-side launch cost (Python + ctypes)
+    # does not leak into the GPU timeline: the captured kernels are exactly the eager ones.
+    def capture(fns, count):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(count):
+                run(fns, i)
+        return g
+
     for i in range(args.warmup):
-        for f in launches(i):
-            assert f() == 0
+        run(step_fns, i)
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(args.steps)]
-    log(f"timing {args.steps} steps")
+    step_graph = capture(step_fns, args.steps)
+    step_graph.replay()                      # one untimed replay: graph upload and warm caches
     torch.cuda.synchronize()
+    log(f"timing {args.steps} steps (one graph replay)")
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        fs = launches(i)
-        for j, f in enumerate(fs):
-            ev[i][j].record()
-            assert f() == 0
-        ev[i][nk].record()
+    step_graph.replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kern_ms = [sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)) / args.steps
-               for j in range(nk)]
     ms_per_step = wall * 1e3 / args.steps
 
+    # per-kernel average launch duration: a graph of back-to-back launches of one kernel,
+    # bracketed by HIP events on the stream it runs on
+    reps = max(20, min(200, args.steps))
+    kern_ms = {}
+    for name, fns in kernels.items():
+        g = capture(fns, reps)
+        g.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        kern_ms[name] = e0.elapsed_time(e1) / reps
+        del g
+
     if pack_only:
-        dom_ms = kern_ms[0]
+        dom_ms = kern_ms["pack"]
         achieved = bytes_per / (dom_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic_for("pack", args.workload),
@@ -207,14 +232,14 @@ def main():
         value = bytes_per / (ms_per_step * 1e-3) / 1e9
         metric, unit, dtype = "sign+pack bandwidth", "GB/s", "u32"
     else:
-        dom_ms = kern_ms[1]
+        dom_ms = kern_ms["core"]
         kind = "mfma" if path_used == bnn.PATH_MFMA else "xor"
         achieved = ops / (dom_ms * 1e-3) / 1e12
         peak = PEAK_MFMA_I8_TOPS if kind == "mfma" else PEAK_VALU_BINARY_TOPS
         roof = {"bound": "mfma" if kind == "mfma" else "alu", "achieved": round(achieved, 2),
                 "peak": round(peak, 1), "unit": "TOP/s", "frac": round(achieved / peak, 4),
                 "traffic": traffic_for(kind, args.workload), "kernel": KERNEL_NAMES[kind],
-                "kernel_ms": round(dom_ms, 5), "pack_kernel_ms": round(kern_ms[0], 5)}
+                "kernel_ms": round(dom_ms, 5), "pack_kernel_ms": round(kern_ms["pack"], 5)}
         value = ops / (ms_per_step * 1e-3) / 1e12
         metric, unit = "binary TOPS (2*M*N*K/s)", "TOPS"
         dtype = "i8" if kind == "mfma" else "u32"
@@ -223,7 +248,8 @@ def main():
         "metric": metric, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
-        "config": {"workload": args.workload, "parallelism": "none (1 GPU)"},
+        "config": {"workload": args.workload, "parallelism": "none (1 GPU)",
+                   "timing": "HIP graph of the timed steps, replayed once untimed then once timed"},
         "roofline": roof,
     }
     if not pack_only:
@@ -234,6 +260,7 @@ def main():
         result["parity_spot_check"] = parity
     if not args.no_cpu_baseline and not pack_only:
         log("cpu baseline (oracle on host cores)")
+        del xd, xp
         result["cpu_baseline"] = cpu_baseline(wl, x, w)
     print(json.dumps(result), flush=True)
 

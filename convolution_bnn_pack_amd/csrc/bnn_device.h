@@ -96,6 +96,38 @@ __device__ __forceinline__ void store4(void* out, int64_t idx, int a0, int a1, i
   }
 }
 
+// Output element type and a 4-element packed write (to LDS or memory) of scaled results.
+template <int OUT> struct OutType;
+template <> struct OutType<kF32> {
+  using type = float;
+  static __device__ __forceinline__ void put4(void* dst, int a0, int a1, int a2, int a3, float alpha) {
+    *reinterpret_cast<float4*>(dst) = make_float4((float)a0 * alpha, (float)a1 * alpha,
+                                                  (float)a2 * alpha, (float)a3 * alpha);
+  }
+};
+template <> struct OutType<kI32> {
+  using type = int;
+  static __device__ __forceinline__ void put4(void* dst, int a0, int a1, int a2, int a3, float) {
+    *reinterpret_cast<int4*>(dst) = make_int4(a0, a1, a2, a3);
+  }
+};
+template <> struct OutType<kF16> {
+  using type = __half;
+  static __device__ __forceinline__ void put4(void* dst, int a0, int a1, int a2, int a3, float alpha) {
+    __half h[4] = {__float2half_rn((float)a0 * alpha), __float2half_rn((float)a1 * alpha),
+                   __float2half_rn((float)a2 * alpha), __float2half_rn((float)a3 * alpha)};
+    *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(h);
+  }
+};
+template <> struct OutType<kBF16> {
+  using type = __hip_bfloat16;
+  static __device__ __forceinline__ void put4(void* dst, int a0, int a1, int a2, int a3, float alpha) {
+    __hip_bfloat16 h[4] = {__float2bfloat16((float)a0 * alpha), __float2bfloat16((float)a1 * alpha),
+                           __float2bfloat16((float)a2 * alpha), __float2bfloat16((float)a3 * alpha)};
+    *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(h);
+  }
+};
+
 // Shape of one contraction, shared by the GEMM and the implicit-im2col conv.
 // Linear: A is packed activations [M][KW], W is packed weights [N][KW].
 // Conv:   A is packed activations [B][H][W][CW] read through the implicit

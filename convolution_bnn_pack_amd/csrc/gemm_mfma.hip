@@ -50,19 +50,22 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
-template <int BM_, int BN_, int KS_, int PD_>
+template <int BM_, int BN_, int KS_, int PD_, int WGM_, int WGN_>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, KS = KS_;
   static constexpr int PD = PD_;                    // stages of raw words in flight (register sets)
   static constexpr int UNROLL = PD % 2 == 0 ? PD : 2 * PD;  // lcm(2, PD): LDS parity x register set
-  static constexpr int FM = BM / 64, FN = BN / 64;  // MFMA blocks per wave (wave tile BM/2 x BN/2)
+  static constexpr int WGM = WGM_, WGN = WGN_;      // wave grid: WGM waves along A rows, WGN along W rows
+  static constexpr int THREADS = 64 * WGM * WGN;
+  static constexpr int WTM = BM / WGM, WTN = BN / WGN;  // wave sub-tile
+  static constexpr int FM = WTM / 32, FN = WTN / 32;    // MFMA blocks per wave
   static constexpr int ROWB = KS * 32;              // LDS bytes per row per stage
   static constexpr int CHUNKS = ROWB / 16;
   static constexpr int BUF = (BM + BN) * ROWB;      // one LDS buffer: A rows, then W rows
   // loader split: every thread expands A_WPT consecutive words of one A row and W_WPT
   // consecutive words of one W row per stage
-  static constexpr int A_WPT = BM * KS / 256, A_TPR = KS / A_WPT;
-  static constexpr int W_WPT = BN * KS / 256, W_TPR = KS / W_WPT;
+  static constexpr int A_WPT = BM * KS / THREADS, A_TPR = KS / A_WPT;
+  static constexpr int W_WPT = BN * KS / THREADS, W_TPR = KS / W_WPT;
   static constexpr int SWZ_SHIFT = CHUNKS == 8 ? 0 : CHUNKS == 4 ? 1 : 2;
   static_assert(A_WPT >= 1 && KS % A_WPT == 0 && W_WPT >= 1 && KS % W_WPT == 0, "loader split");
 };
@@ -214,7 +217,7 @@ __device__ __forceinline__ v4i lds_frag(const uint8_t* buf, int r, int c) {
 }
 
 template <class T, int OUT, bool CONV, bool VEC>
-__global__ __launch_bounds__(256) void mfma_kernel(Contraction p) {
+__global__ __launch_bounds__(T::THREADS) void mfma_kernel(Contraction p) {
   // two distinct arrays (not one array indexed by stage parity) so the compiler can
   // tell the expansion's writes from the fragment reads
   __shared__ __attribute__((aligned(16))) uint8_t lds0[T::BUF];
@@ -229,7 +232,7 @@ __global__ __launch_bounds__(256) void mfma_kernel(Contraction p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % T::WGM, wn = wave / T::WGM;
   const int tiles_m = (p.M + T::BM - 1) / T::BM, tiles_n = (p.N + T::BN - 1) / T::BN;
   int tm, tn;
   tile_coords(tiles_m, tiles_n, tm, tn);
@@ -242,7 +245,7 @@ __global__ __launch_bounds__(256) void mfma_kernel(Contraction p) {
   const bool amok = am < p.M;
   PixelCoord pc{0, 0, 0};
   if constexpr (CONV) pc = pixel_coord(p, amok ? am : 0);
-  for (int i = tid; i < T::BM; i += 256) rowk[i] = 0;
+  for (int i = tid; i < T::BM; i += T::THREADS) rowk[i] = 0;
   int rowk_part = 0;  // this thread's share of 32 * (real words) - 2 * popA
 
   // raw words of PD stages in flight; stage t lives in register set t % PD
@@ -296,10 +299,10 @@ __global__ __launch_bounds__(256) void mfma_kernel(Contraction p) {
   auto read_frag = [&](const uint8_t* cur, int kk, int j) {
     const int fb = kk & 1;
     if (j < T::FM) {
-      fa[fb][j] = lds_frag<T>(cur, wm * (T::BM / 2) + j * 32 + fr, 2 * kk + half);
+      fa[fb][j] = lds_frag<T>(cur, wm * T::WTM + j * 32 + fr, 2 * kk + half);
     } else {
       const int f = j - T::FM;
-      fw[fb][f] = lds_frag<T>(cur, T::BM + wn * (T::BN / 2) + f * 32 + fr, 2 * kk + half);
+      fw[fb][f] = lds_frag<T>(cur, T::BM + wn * T::WTN + f * 32 + fr, 2 * kk + half);
     }
   };
 
@@ -325,7 +328,11 @@ __global__ __launch_bounds__(256) void mfma_kernel(Contraction p) {
       const int fn = j / T::FM, fm = j % T::FM;
       acc[fn][fm] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fw[kk & 1][fn], fa[kk & 1][fm],
                                                            acc[fn][fm], 0, 0, 0);
-      if (kk + 1 < T::KS && j < RPK) read_frag(cur, kk + 1, j);
+      // the next k-step's RPK fragment reads are spread over this k-step's MPK slots
+      if (kk + 1 < T::KS) {
+#pragma unroll
+        for (int f = j * RPK / MPK; f < (j + 1) * RPK / MPK; f++) read_frag(cur, kk + 1, f);
+      }
 #pragma unroll
       for (int u = i * NU / NM; u < (i + 1) * NU / NM; u++) expand_unit(nxt, u);
       __builtin_amdgcn_sched_barrier(0);
@@ -367,43 +374,90 @@ __global__ __launch_bounds__(256) void mfma_kernel(Contraction p) {
   __syncthreads();
 
   // epilogue: acc[fn][fm][e] is output (row m, feature n) with
-  //   m = m0 + wm*BM/2 + fm*32 + (lane & 31)
-  //   n = n0 + wn*BN/2 + fn*32 + 8*(e/4) + 4*(lane/32) + e%4
-  const int hw = CONV ? p.Ho * p.Wo : 1;
+  //   m = m0 + wm*WTM + fm*32 + (lane & 31)
+  //   n = n0 + wn*WTN + fn*32 + 8*(e/4) + 4*(lane/32) + e%4
+  // and the binary dot product is rowk[m - m0] + 2 * acc.
+  if constexpr (CONV) {
+    // NCHW: for a fixed feature the 32 lanes of a half-wave hold 32 consecutive pixels,
+    // so each store instruction writes lane-contiguous runs.
+    const int hw = p.Ho * p.Wo;
 #pragma unroll
-  for (int fm = 0; fm < T::FM; fm++) {
-    const int ml = wm * (T::BM / 2) + fm * 32 + fr;
-    const int m = m0 + ml;
-    if (m >= p.M) continue;
-    const int base_k = rowk[ml];
-    int b = 0, pix = 0;
-    if constexpr (CONV) {
-      b = m / hw;
-      pix = m - b * hw;
+    for (int fm = 0; fm < T::FM; fm++) {
+      const int ml = wm * T::WTM + fm * 32 + fr;
+      const int m = m0 + ml;
+      if (m >= p.M) continue;
+      const int base_k = rowk[ml];
+      const int b = m / hw, pix = m - b * hw;
+#pragma unroll
+      for (int fn = 0; fn < T::FN; fn++)
+#pragma unroll
+        for (int e = 0; e < 16; e++) {
+          const int n = n0 + wn * T::WTN + fn * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
+          if (n < p.N)
+            store1<OUT>(p.out, ((int64_t)b * p.N + n) * hw + pix, base_k + 2 * acc[fn][fm][e], p.alpha);
+        }
     }
+  } else {
+    // Row-major [M][N]: each lane's values are four features of one row, 32 rows per
+    // half-wave, so storing them directly would scatter 8..16-byte pieces over 32 rows.
+    // Instead each wave stages one 32-row band of its sub-tile in LDS (free after the
+    // main loop; two waves' bands per buffer) and writes it back as whole contiguous row
+    // segments, 16 bytes per lane.
+    using O = OutType<OUT>;
+    constexpr int WN = T::WTN;                          // columns of a wave's sub-tile
+    constexpr int ROWS_B = WN * (int)sizeof(typename O::type) + 16;  // padded LDS row
+    constexpr int NWAVES = T::WGM * T::WGN, HALFW = NWAVES / 2;
+    static_assert(HALFW * 32 * ROWS_B <= T::BUF, "staging bands fit in the two LDS buffers");
+    uint8_t* band = (wave < HALFW ? lds0 : lds1) + (wave % HALFW) * 32 * ROWS_B;
+    constexpr int EPV = 16 / (int)sizeof(typename O::type);  // elements per 16-byte vector
+    constexpr int VPR = WN / EPV;                            // vectors per band row
 #pragma unroll
-    for (int fn = 0; fn < T::FN; fn++) {
+    for (int fm = 0; fm < T::FM; fm++) {
+      const int base_k = rowk[wm * T::WTM + fm * 32 + fr];
+      uint8_t* myrow = band + fr * ROWS_B;
 #pragma unroll
-      for (int g = 0; g < 4; g++) {
-        const int n = n0 + wn * (T::BN / 2) + fn * 32 + 8 * g + 4 * half;
-        int av[4];
+      for (int fn = 0; fn < T::FN; fn++)
 #pragma unroll
-        for (int j = 0; j < 4; j++) av[j] = base_k + 2 * acc[fn][fm][4 * g + j];
-        if constexpr (!CONV) {
-          const int64_t base = (int64_t)m * p.N + n;
-          if (n + 3 < p.N && (p.N & 3) == 0) {
-            store4<OUT>(p.out, base, av[0], av[1], av[2], av[3], p.alpha);
-          } else {
+        for (int g = 0; g < 4; g++) {
+          const int c = fn * 32 + 8 * g + 4 * half;
+          O::put4(myrow + c * (int)sizeof(typename O::type), base_k + 2 * acc[fn][fm][4 * g],
+                  base_k + 2 * acc[fn][fm][4 * g + 1], base_k + 2 * acc[fn][fm][4 * g + 2],
+                  base_k + 2 * acc[fn][fm][4 * g + 3], p.alpha);
+        }
+      // the band is private to this wave and a wave's LDS accesses complete in order, so
+      // no fence is needed (a memory fence here would also wait for the global stores)
+      __builtin_amdgcn_wave_barrier();
+      const int mrow0 = m0 + wm * T::WTM + fm * 32;
+      const int ncol0 = n0 + wn * WN;
+      constexpr int NV = 32 * VPR / 64;  // 16-byte vectors per lane for the band
+      static_assert(NV >= 1 && (32 * VPR) % 64 == 0, "band splits evenly over the lanes");
+      uint4 vals[NV];
 #pragma unroll
-            for (int j = 0; j < 4; j++)
-              if (n + j < p.N) store1<OUT>(p.out, base + j, av[j], p.alpha);
-          }
+      for (int t = 0; t < NV; t++) {
+        const int v = lane + 64 * t;
+        const int r = v / VPR, cv = v - r * VPR;
+        vals[t] = *reinterpret_cast<const uint4*>(band + r * ROWS_B + cv * 16);
+      }
+      const bool full_rows = (p.N % EPV) == 0;
+#pragma unroll
+      for (int t = 0; t < NV; t++) {
+        const int v = lane + 64 * t;
+        const int r = v / VPR, cv = v - r * VPR;
+        const int m = mrow0 + r, n = ncol0 + cv * EPV;
+        if (m >= p.M) continue;
+        typename O::type* dst = reinterpret_cast<typename O::type*>(p.out) + (int64_t)m * p.N + n;
+        if (full_rows && n + EPV <= p.N) {
+          *reinterpret_cast<uint4*>(dst) = vals[t];
         } else {
+          const typename O::type* src = reinterpret_cast<const typename O::type*>(&vals[t]);
 #pragma unroll
-          for (int j = 0; j < 4; j++)
-            if (n + j < p.N) store1<OUT>(p.out, ((int64_t)b * p.N + n + j) * hw + pix, av[j], p.alpha);
+          for (int j = 0; j < EPV; j++)
+            if (n + j < p.N) dst[j] = src[j];
         }
       }
+      // the band is private to this wave and a wave's LDS accesses complete in order, so
+      // no fence is needed (a memory fence here would also wait for the global stores)
+      __builtin_amdgcn_wave_barrier();
     }
   }
 }
@@ -411,7 +465,7 @@ __global__ __launch_bounds__(256) void mfma_kernel(Contraction p) {
 template <class T, bool CONV, bool VEC>
 hipError_t launch_tile_v(const Contraction& p, int out_dtype, hipStream_t stream) {
   const int64_t tiles = (int64_t)((p.M + T::BM - 1) / T::BM) * ((p.N + T::BN - 1) / T::BN);
-  const dim3 grid((unsigned)tiles), block(256);
+  const dim3 grid((unsigned)tiles), block(T::THREADS);
   switch (out_dtype) {
     case kF32: hipLaunchKernelGGL((mfma_kernel<T, kF32, CONV, VEC>), grid, block, 0, stream, p); break;
     case kF16: hipLaunchKernelGGL((mfma_kernel<T, kF16, CONV, VEC>), grid, block, 0, stream, p); break;
@@ -439,9 +493,14 @@ hipError_t launch_tile(const Contraction& p, int out_dtype, hipStream_t stream) 
 #ifndef BNN_MFMA_PD_M
 #define BNN_MFMA_PD_M 4
 #endif
-using TileL = Tile<256, 256, 4, BNN_MFMA_PD_L>;
-using TileM = Tile<128, 256, 4, BNN_MFMA_PD_M>;
-using TileS = Tile<128, 128, 4, BNN_MFMA_PD_M>;
+#ifndef BNN_MFMA_WAVES_N
+#define BNN_MFMA_WAVES_N 4
+#endif
+// 2 x BNN_MFMA_WAVES_N waves per workgroup: with 4 along W there are two waves per SIMD,
+// whose MFMA and expansion streams the hardware interleaves.
+using TileL = Tile<256, 256, 4, BNN_MFMA_PD_L, 2, BNN_MFMA_WAVES_N>;
+using TileM = Tile<128, 256, 4, BNN_MFMA_PD_M, 2, BNN_MFMA_WAVES_N>;
+using TileS = Tile<128, 128, 4, BNN_MFMA_PD_M, 2, BNN_MFMA_WAVES_N>;
 
 int64_t count_tiles(const Contraction& p, int bm, int bn) {
   return (int64_t)((p.M + bm - 1) / bm) * ((p.N + bn - 1) / bn);

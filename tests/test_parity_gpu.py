@@ -272,3 +272,35 @@ def test_last_path_and_errors_on_device(bnn):
     with pytest.raises(bnn.BnnError) as e:
         bnn.pack_sign(buf[1:1 + 64 * 64].view(64, 64))
     assert e.value.status == bnn.ERR_ALIGN
+
+
+def test_graph_replay_matches_eager(bnn):
+    """The benchmark times HIP-graph replays of the step; every replay must equal the eager
+    result, with other eager work and synchronizations between replays."""
+    g = torch.Generator().manual_seed(51)
+    x = torch.randn((700, 1024), generator=g).half().to(DEV)
+    wp = bnn.w_pack(torch.randn((520, 1024), generator=g).half().to(DEV))
+    xc = torch.randn((2, 64, 11, 13), generator=g).to(DEV)
+    wpc = bnn.w_pack(torch.randn((48, 64, 3, 3), generator=g).to(DEV))
+    for path in ("xor", "mfma"):
+        eager = bnn.gemm(x, wp, 0.3, 0.7, path=path)
+        eager_c = bnn.conv2d(xc, wpc, 0.3, 0.7, 3, 2, 1, 1, path=path)
+        xp = torch.empty((700, 32), dtype=torch.int32, device=DEV)
+        xpc = torch.empty((2, 11, 13, 2), dtype=torch.int32, device=DEV)
+        out = torch.empty_like(eager)
+        out_c = torch.empty_like(eager_c)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            bnn.pack_sign(x, out=xp)
+            bnn.gemm(xp, wp, 0.3, 0.7, path=path, out=out, k=1024)
+            bnn.pack_sign_nchw(xc, out=xpc)
+            bnn.conv2d(xpc, wpc, 0.3, 0.7, 3, 2, 1, 1, path=path, out=out_c)
+        for r in range(4):
+            out.fill_(-1.0)
+            out_c.fill_(-1.0)
+            bnn.gemm(x[:64].contiguous(), wp, 1.0, 1.0, path=path)   # unrelated eager work
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, eager), (path, r)
+            assert torch.equal(out_c, eager_c), (path, r)
