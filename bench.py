@@ -57,6 +57,61 @@ def traffic_for(kind, workload):
     return rec.get("bytes_per_launch")
 
 
+def pmc_summary(args):
+    """Scaled HBM traffic per launch from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE).
+
+    Each counter is read in KiB per dispatch. The copy-calibration kernel in the same file
+    moved a known number of bytes (read = write = copy size); the ratio known/counted is the
+    scale applied to the workload kernel's reading. Writes profiles/traffic.json."""
+    import csv
+    import statistics
+
+    def read(path, counter):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    wl = args.workload
+    kind = "pack" if wl == PACK_WORKLOAD else None
+    out = {}
+    for counter, path in (("FETCH_SIZE", args.pmc_summary[0]), ("WRITE_SIZE", args.pmc_summary[1])):
+        vals = read(path, counter)
+        copy = [v for k, vs in vals.items() if args.copy_kernel in k for v in vs]
+        if not copy:
+            raise SystemExit(f"no {args.copy_kernel} kernel in {path}")
+        copy_kib = statistics.median(copy)
+        scale = (args.copy_mib << 20) / 1024.0 / copy_kib if args.copy_mib else 1.0
+        for k in (["pack"] if kind else ["mfma", "xor"]):
+            # the workload's kernel is the instantiation launched most often (the parity spot
+            # check adds single launches of other output types)
+            cands = [(len(vs), name) for name, vs in vals.items()
+                     if KERNEL_NAMES[k] + "<" in name or KERNEL_NAMES[k] + "(" in name]
+            if not cands:
+                continue
+            _, name = max(cands)
+            rec = out.setdefault(k, {"kernel": KERNEL_NAMES[k], "launches": len(vals[name])})
+            rec[counter.lower() + "_kib_median"] = statistics.median(vals[name])
+            rec[counter.lower() + "_scale"] = scale
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    db = json.load(open(path)) if os.path.exists(path) else {}
+    for k, rec in out.items():
+        if "fetch_size_kib_median" not in rec or "write_size_kib_median" not in rec:
+            continue
+        fetch = rec["fetch_size_kib_median"] * 1024 * rec["fetch_size_scale"]
+        write = rec["write_size_kib_median"] * 1024 * rec["write_size_scale"]
+        db[f"{KERNEL_NAMES[k]}|{wl}"] = {
+            "bytes_per_launch": round(fetch + write), "fetch_bytes": round(fetch),
+            "write_bytes": round(write), "fetch_scale": round(rec["fetch_size_scale"], 4),
+            "write_scale": round(rec["write_size_scale"], 4), "src_sha": src_sha(k),
+            "launches_measured": rec["launches"]}
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    json.dump(db, open(path, "w"), indent=1, sort_keys=True)
+    print(json.dumps(db, indent=1, sort_keys=True))
+
+
 def cpu_baseline(wl, x, w):
     """The oracle as it stands on the host cores: the whole workload when it takes under
     about 30 s, else a row / image sample sized for ~15 s, scaled to binary TOPS."""
@@ -99,7 +154,19 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--path", default="auto", choices=["auto", "xor", "mfma"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after the workload, run 5 plain device copies of this many MiB "
+                         "(reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE run, "
+                         "WRITE_SIZE run; each also holding the copy-calibration kernel) into HBM "
+                         "bytes per launch of the workload's dominant kernel in profiles/traffic.json")
+    ap.add_argument("--copy-kernel", default="copyBuffer",
+                    help="substring naming the copy kernel in the counter files")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the binary forward has no "
               f"cross-GPU exchange here; run with --gpus 1.", file=sys.stderr)
@@ -258,6 +325,16 @@ def main():
                                  "out_dtype": wl.out_dtype,
                                  "path": {bnn.PATH_XOR: "xor", bnn.PATH_MFMA: "mfma"}[path_used]})
         result["parity_spot_check"] = parity
+    if args.copy_mib:
+        # plain device copies of a known size, for scaling the traffic counters
+        n = args.copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty(n, dtype=torch.uint8, device=dev)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = n
+        del src, dst
     if not args.no_cpu_baseline and not pack_only:
         log("cpu baseline (oracle on host cores)")
         del xd, xp

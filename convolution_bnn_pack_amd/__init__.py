@@ -77,9 +77,9 @@ def _check(status: int, where: str):
     if status == OK:
         return
     if status == ERR_SHAPE:
-        # same message as the layer pages' divisibility assertion, plus the ABI's reason
-        raise AssertionError(f"Input tensor dimension must be divisible by 32. ({where}: "
-                             f"{lib.bnn_status_string(status).decode()})")
+        # a size the ABI rejects (e.g. a reduction length that is not a whole number of 32-bit
+        # words) is an AssertionError, the exception type the layers use for that check
+        raise AssertionError(f"{where}: {lib.bnn_status_string(status).decode()}")
     raise BnnError(status, where)
 
 

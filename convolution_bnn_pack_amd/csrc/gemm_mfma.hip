@@ -507,11 +507,14 @@ int64_t count_tiles(const Contraction& p, int bm, int bn) {
 }
 
 // Largest tile that still gives every compute unit a workgroup; the smallest otherwise.
+#ifndef BNN_MFMA_MIN_TILES
+#define BNN_MFMA_MIN_TILES 256
+#endif
 template <bool CONV>
 hipError_t launch_mfma_t(const Contraction& p, int out_dtype, hipStream_t stream) {
-  constexpr int64_t kCUs = 256;
-  if (count_tiles(p, 256, 256) >= kCUs) return launch_tile<TileL, CONV>(p, out_dtype, stream);
-  if (count_tiles(p, 128, 256) >= kCUs) return launch_tile<TileM, CONV>(p, out_dtype, stream);
+  constexpr int64_t kMinTiles = BNN_MFMA_MIN_TILES;  // one workgroup per compute unit
+  if (count_tiles(p, 256, 256) >= kMinTiles) return launch_tile<TileL, CONV>(p, out_dtype, stream);
+  if (count_tiles(p, 128, 256) >= kMinTiles) return launch_tile<TileM, CONV>(p, out_dtype, stream);
   return launch_tile<TileS, CONV>(p, out_dtype, stream);
 }
 

@@ -72,38 +72,56 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(const u32x4* __restrict_
   }
 }
 
-// NCHW pack along channels: word (b, pixel, q) collects channel 32q + j of
-// that pixel into bit j. Lanes run along the contiguous pixel axis, V pixels
-// per lane (one 16-byte load when the plane allows it), and loop over the 32
-// channels of the word, so every load instruction is coalesced.
+// NCHW pack along channels. Word (b, pixel, q) collects channel 32q + j of that pixel
+// into bit j. A 256-thread workgroup packs 64*V consecutive pixels of one (b, q): lanes
+// run along the contiguous pixel axis (V pixels each, one 16-byte load when the plane
+// allows it, so each load instruction reads one channel plane contiguously), and wave w
+// takes channels 8w .. 8w+7 of the word with its eight loads in flight at once. Each wave
+// writes byte w of every pixel's word to LDS; the assembled words then leave in pixel order.
 template <int DT, int V>
 __global__ __launch_bounds__(256) void pack_nchw_kernel(const void* __restrict__ x,
                                                         uint32_t* __restrict__ out, int64_t C,
                                                         int64_t HW, int64_t CW, int64_t nbq) {
   constexpr int ES = (DT == kF32) ? 4 : 2;
-  const int64_t p0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * V;
-  if (p0 >= HW) return;
-  for (int64_t bq = blockIdx.y; bq < nbq; bq += gridDim.y) {  // bq = b * CW + q
-  const int64_t b = bq / CW, q = bq - b * CW;
-  const char* base = reinterpret_cast<const char*>(x) + ((b * C + 32 * q) * HW + p0) * ES;
-  uint32_t word[V];
+  constexpr int PIX = 64 * V;                     // pixels per workgroup
+  __shared__ uint32_t words[PIX];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t nchunks = (HW + PIX - 1) / PIX;
+  for (int64_t bq = blockIdx.y; bq < nbq; bq += gridDim.y) {
+    const int64_t b = bq / CW, q = bq - b * CW;
+    const char* plane0 = reinterpret_cast<const char*>(x) + ((b * C + 32 * q + 8 * wave) * HW) * ES;
+    for (int64_t ch = blockIdx.x; ch < nchunks; ch += gridDim.x) {
+      const int64_t base = ch * PIX;
+      const int64_t p0 = base + (int64_t)lane * V;
+      uint32_t bits[8];
 #pragma unroll
-  for (int v = 0; v < V; v++) word[v] = 0;
-  for (int j = 0; j < 32; j++) {
-    const char* src = base + (int64_t)j * HW * ES;
-    if constexpr (V * ES == 16) {
-      const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
-      const uint32_t bits = vec_bits<DT>(t);
+      for (int c = 0; c < 8; c++) {
+        const char* src = plane0 + ((int64_t)c * HW + p0) * ES;
+        if constexpr (V * ES == 16) {
+          bits[c] = (p0 < HW) ? vec_bits<DT>(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src))) : 0u;
+        } else {
+          uint32_t bb = 0;
 #pragma unroll
-      for (int v = 0; v < V; v++) word[v] |= ((bits >> v) & 1u) << j;
-    } else {
+          for (int v = 0; v < V; v++)
+            if (p0 + v < HW) bb |= elem_pos<DT>(src, v) << v;
+          bits[c] = bb;
+        }
+      }
+      uint8_t* wbytes = reinterpret_cast<uint8_t*>(words);
 #pragma unroll
-      for (int v = 0; v < V; v++) word[v] |= elem_pos<DT>(src, v) << j;
+      for (int v = 0; v < V; v++) {
+        uint32_t byte = 0;
+#pragma unroll
+        for (int c = 0; c < 8; c++) byte |= ((bits[c] >> v) & 1u) << c;
+        wbytes[(lane * V + v) * 4 + wave] = (uint8_t)byte;
+      }
+      __syncthreads();
+      for (int i = threadIdx.x; i < PIX; i += 256) {
+        const int64_t pix = base + i;
+        if (pix < HW) out[(b * HW + pix) * CW + q] = words[i];
+      }
+      __syncthreads();
     }
-  }
-  uint32_t* dst = out + (b * HW + p0) * CW + q;
-#pragma unroll
-  for (int v = 0; v < V; v++) dst[v * CW] = word[v];
   }
 }
 
@@ -151,9 +169,10 @@ hipError_t launch_pack_nchw(const void* x, int dtype, int64_t b, int64_t c, int6
   const int vfull = 16 / es;
   const bool vec = (HW % vfull) == 0 && (reinterpret_cast<uintptr_t>(x) % 16) == 0;
   const int V = vec ? vfull : 1;
-  const int64_t lanes = (HW + V - 1) / V;
+  const int64_t nchunks = (HW + 64 * V - 1) / (64 * V);
   const int64_t nbq = b * CW;
-  const dim3 grid((unsigned)((lanes + 255) / 256), (unsigned)(nbq < 65535 ? nbq : 65535)), block(256);
+  const dim3 grid((unsigned)(nchunks < 65535 ? nchunks : 65535), (unsigned)(nbq < 65535 ? nbq : 65535)),
+      block(256);
   if (vec) {
     switch (dtype) {
       case kF32: hipLaunchKernelGGL((pack_nchw_kernel<kF32, 4>), grid, block, 0, stream, x, out, c, HW, CW, nbq); break;

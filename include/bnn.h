@@ -4,8 +4,8 @@
  *
  * The layers are those of bitorch-engine's binary layer pages:
  *   - BinaryLinearForward.forward(input, weight, bmm_type, scale_a, scale_w, is_train)
- *     (BinaryLinearForward page): the binary linear result scaled by the
- *     activation and weight scaling factors, no bias term;
+ *     (BinaryLinearForward page): the binary product multiplied by both scalar
+ *     scales; the operation has no bias;
  *   - BinaryConv2dForward.forward(x, weight, scale_a, scale_w, is_train,
  *     kernel_size, stride, padding, dilation) (qconv/binary/cutlass/layer
  *     page): the native forward receives the host product of the two scalar

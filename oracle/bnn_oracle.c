@@ -24,9 +24,9 @@
  *    build's reading; the pages fix neither.)
  *
  *  - Linear forward: acc[m][n] = sum_k sgn(x[m][k]) * sgn(W[n][k]), then
- *    y = acc * (scale_a * scale_w). (BinaryLinearForward.forward on the
- *    BinaryLinearForward page: the binary linear result scaled by the
- *    activation and weight scaling factors; there is no bias term.)
+ *    y = acc * (scale_a * scale_w): the binary product multiplied by both
+ *    scalar scales, with no bias (BinaryLinearForward.forward and .backward on
+ *    the BinaryLinearForward page).
  *
  *  - Conv2d forward, lowered as im2col + GEMM exactly in the order of the
  *    banghao.live blog post, section 2 ("Implementation of im2col+gemm
