@@ -31,9 +31,36 @@ def build(force: bool = True) -> str:
     """Compile liboracle.so with gcc; returns its path."""
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp"
-        subprocess.run(["gcc", *_CFLAGS, _SRC, "-o", tmp, "-lm"], check=True)
+        compile_library(_SRC, tmp)
         os.replace(tmp, _LIB)
     return _LIB
+
+
+def _bind(lib):
+    """Declare the C signatures on a loaded oracle library."""
+    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.oracle_num_threads.restype = I
+    lib.oracle_sign.argtypes = [P, I, I64, P]
+    lib.oracle_pack_rows.argtypes = [P, I, I64, I64, P]
+    lib.oracle_pack_nchw.argtypes = [P, I, I64, I64, I64, I64, P]
+    lib.oracle_pack_conv_weight.argtypes = [P, I, I64, I64, I64, P]
+    lib.oracle_linear_acc.argtypes = [P, I, P, I, I64, I64, I64, P, I64, P]
+    lib.oracle_linear_acc.restype = I
+    lib.oracle_conv_out_size.argtypes = [I64, I64, I64, I64, I64]
+    lib.oracle_conv_out_size.restype = I64
+    lib.oracle_conv2d_acc.argtypes = [P, I, P, I, I64, I64, I64, I64, I64, I64, I64, I64,
+                                      I64, P, I64, P]
+    lib.oracle_conv2d_acc.restype = I
+    lib.oracle_conv2d_kvalid.argtypes = [I64, I64, I64, I64, I64, I64, I64, P]
+    lib.oracle_conv2d_kvalid.restype = I
+    lib.oracle_scale.argtypes = [P, I64, ctypes.c_double, ctypes.c_double, P]
+    return lib
+
+
+def compile_library(src: str, out: str) -> str:
+    """Compile an oracle source file (this one, or a test's modified copy) into a shared library."""
+    subprocess.run(["gcc", *_CFLAGS, src, "-o", out, "-lm"], check=True)
+    return out
 
 
 def _load():
@@ -41,24 +68,7 @@ def _load():
     if _lib is None:
         if not os.path.exists(_LIB):
             build()
-        lib = ctypes.CDLL(_LIB)
-        P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
-        lib.oracle_num_threads.restype = I
-        lib.oracle_sign.argtypes = [P, I, I64, P]
-        lib.oracle_pack_rows.argtypes = [P, I, I64, I64, P]
-        lib.oracle_pack_nchw.argtypes = [P, I, I64, I64, I64, I64, P]
-        lib.oracle_pack_conv_weight.argtypes = [P, I, I64, I64, I64, P]
-        lib.oracle_linear_acc.argtypes = [P, I, P, I, I64, I64, I64, P, I64, P]
-        lib.oracle_linear_acc.restype = I
-        lib.oracle_conv_out_size.argtypes = [I64, I64, I64, I64, I64]
-        lib.oracle_conv_out_size.restype = I64
-        lib.oracle_conv2d_acc.argtypes = [P, I, P, I, I64, I64, I64, I64, I64, I64, I64, I64,
-                                          I64, P, I64, P]
-        lib.oracle_conv2d_acc.restype = I
-        lib.oracle_conv2d_kvalid.argtypes = [I64, I64, I64, I64, I64, I64, I64, P]
-        lib.oracle_conv2d_kvalid.restype = I
-        lib.oracle_scale.argtypes = [P, I64, ctypes.c_double, ctypes.c_double, P]
-        _lib = lib
+        _lib = _bind(ctypes.CDLL(_LIB))
     return _lib
 
 

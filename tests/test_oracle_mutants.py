@@ -1,0 +1,197 @@
+"""Planted mistakes in the oracle are caught by its pins (CPU only).
+
+Each case copies oracle/bnn_oracle.c, plants one plausible mistake (a dropped term, a wrong
+sign, a transposed index or operand, a wrong constant), compiles the copy with gcc and runs a
+fast subset of the pins against it. At least one pin must fail for every mutant; the
+unmodified source must pass them all. Nothing here touches the GPU or the HIP library.
+"""
+import ctypes
+import json
+import math
+import os
+import random
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "bnn_oracle.c")
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+MUTANTS = {
+    "zero_maps_to_minus_one": ("return v >= 0.0f ? 1.0f : -1.0f;", "return v > 0.0f ? 1.0f : -1.0f;"),
+    # (a wrong exponent bias only rescales magnitudes, which the sign rule never sees, so such
+    # mutants are equivalent; these two change signs)
+    "f16_nan_widened_to_inf": ("v = frac ? NAN : INFINITY;", "v = INFINITY;"),
+    "f16_subnormals_flushed": ("v = ldexpf((float)frac, -24);", "v = 0.0f;"),
+    "bf16_widen_shift": ("(uint32_t)b << 16;", "(uint32_t)b << 15;"),
+    "pack_bit_order": ("if (sgn(widen(x, dtype, r * k + 32 * q + j)) > 0.0f) word |= (uint32_t)1 << j;",
+                       "if (sgn(widen(x, dtype, r * k + 32 * q + j)) > 0.0f) word |= (uint32_t)1 << (31 - j);"),
+    "pack_nchw_hw_swapped": ("int64_t idx = ((b * C + 32 * q + j) * H + ih) * W + iw;",
+                             "int64_t idx = ((b * C + 32 * q + j) * W + iw) * H + ih;"),
+    "pack_weight_kernel_transposed": ("int64_t idx = ((o * C + 32 * q + j) * ks + kh) * ks + kx;",
+                                      "int64_t idx = ((o * C + 32 * q + j) * ks + kx) * ks + kh;"),
+    "linear_drops_last_term": ("for (int64_t k = 0; k < K; k++) s += sx[k] * wr[k];",
+                               "for (int64_t k = 0; k < K - 1; k++) s += sx[k] * wr[k];"),
+    "linear_x_transposed": ("sx[k] = sgn(widen(x, xdt, m * K + k));",
+                            "sx[k] = sgn(widen(x, xdt, (k % M) * K + (m * K + k) / M % K));"),
+    "conv_pad_value_plus_one": ("memset(xp, 0, sizeof(float) * (size_t)(C * Hp * Wp));",
+                                "for (int64_t z = 0; z < C * Hp * Wp; z++) xp[z] = 1.0f;"),
+    "conv_unfold_without_dilation": ("cols[l * R + r] = xp[(c * Hp + oh * s + kh * d) * Wp + ow * s + kx * d];",
+                                     "cols[l * R + r] = xp[(c * Hp + oh * s + kh) * Wp + ow * s + kx];"),
+    "conv_ignores_column_stride": ("cols[l * R + r] = xp[(c * Hp + oh * s + kh * d) * Wp + ow * s + kx * d];",
+                                   "cols[l * R + r] = xp[(c * Hp + oh * s + kh * d) * Wp + ow + kx * d];"),
+    "conv_row_index_transposed": ("int64_t r = (c * ks + kh) * ks + kx;", "int64_t r = (c * ks + kx) * ks + kh;"),
+    "kvalid_off_by_one": ("if (ih >= 0 && ih < H && iw >= 0 && iw < W) taps++;",
+                          "if (ih >= 0 && ih <= H && iw >= 0 && iw < W) taps++;"),
+    "scale_sum_instead_of_product": ("double alpha = scale_a * scale_w;", "double alpha = scale_a + scale_w;"),
+}
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _num(v):
+    if isinstance(v, str):
+        return {"-0": -0.0, "nan": float("nan"), "-inf": float("-inf")}[v]
+    return float(v)
+
+
+def _tensor(nested):
+    return torch.from_numpy(np.vectorize(_num, otypes=[np.float64])(np.array(nested, dtype=object)).astype(np.float32))
+
+
+def _lib_sign(t):
+    return torch.where(t.float() >= 0, 1.0, -1.0).double()
+
+
+def _pins(orc):
+    """Fast pins; returns the names of those that fail."""
+    failed = []
+
+    def check(name, fn):
+        try:
+            if not fn():
+                failed.append(name)
+        except Exception:  # a crash of the mutant counts as a caught mistake
+            failed.append(name)
+
+    g = _golden("linear_hand.json")
+    check("linear_hand", lambda: orc.linear_acc(_tensor(g["x"]), _tensor(g["w"])).tolist() == g["acc"]
+          and orc.scale(torch.tensor(g["acc"], dtype=torch.int32), g["scale_a"], g["scale_w"]).tolist() == g["y"])
+    g2 = _golden("conv_checkerboard.json")
+    check("conv_hand", lambda: orc.conv2d_acc(_tensor(g2["x"]), _tensor(g2["w"]), 1, 1, 1).tolist() == g2["acc"])
+    km = _golden("kvalid_maps.json")["cases"]
+    check("kvalid_maps", lambda: all(orc.conv2d_kvalid(1, c["h"], c["w"], 3, c["stride"], c["padding"],
+                                                       c["dilation"]).tolist() == c["kvalid"] for c in km))
+    table = _golden("sign_edges.json")
+
+    def signs_ok():
+        for dt, tdt, width in (("f32", torch.float32, 32), ("f16", torch.float16, 16), ("bf16", torch.bfloat16, 16)):
+            ints = [int(h, 16) for h, _ in table[dt]]
+            ints = [b - (1 << width) if b >= 1 << (width - 1) else b for b in ints]
+            raw = torch.tensor(ints, dtype=torch.int32 if width == 32 else torch.int16).view(tdt)
+            if orc.sign(raw).tolist() != [float(s) for _, s in table[dt]]:
+                return False
+        allbits = torch.arange(-(1 << 15), 1 << 15, dtype=torch.int32).to(torch.int16)
+        for tdt in (torch.float16, torch.bfloat16):
+            x = allbits.view(tdt).contiguous()
+            if not torch.equal(orc.sign(x).double(), _lib_sign(x)):
+                return False
+        return True
+
+    check("sign_table_and_widening", signs_ok)
+
+    def brute():
+        for k in (1, 3, 6):
+            pats = np.arange(1 << k)
+            bits = (pats[:, None] >> np.arange(k)[None, :]) & 1
+            x = torch.from_numpy(np.where(bits == 1, 1.5, -0.5).astype(np.float32))
+            acc = orc.linear_acc(x, x).numpy()
+            want = np.array([[k - 2 * bin(int(a) ^ int(b)).count("1") for b in pats] for a in pats])
+            if not np.array_equal(acc, want):
+                return False
+        return True
+
+    check("brute_force", brute)
+
+    def packs():
+        gen = torch.Generator().manual_seed(5)
+        x = torch.randn((6, 96), generator=gen)
+        bits = (orc.pack_rows(x).numpy().astype(np.uint32).astype(np.int64)[..., None] >> np.arange(32)) & 1
+        if not np.array_equal(bits.reshape(6, 96), (x >= 0).numpy().astype(np.int64)):
+            return False
+        xn = torch.randn((2, 64, 5, 3), generator=gen)
+        if not torch.equal(orc.pack_nchw(xn),
+                           orc.pack_rows(xn.permute(0, 2, 3, 1).contiguous().reshape(-1, 64)).view(2, 5, 3, 2)):
+            return False
+        wc = torch.randn((3, 32, 3, 3), generator=gen)
+        return torch.equal(orc.pack_conv_weight(wc),
+                           orc.pack_rows(wc.permute(0, 2, 3, 1).contiguous().reshape(-1, 32)).view(3, 3, 3, 1))
+
+    check("pack_layouts", packs)
+
+    def lib_linear():
+        gen = torch.Generator().manual_seed(7)
+        for m, n, k in ((5, 7, 64), (9, 3, 96), (1, 4, 32)):
+            x, w = torch.randn((m, k), generator=gen), torch.randn((n, k), generator=gen)
+            if not torch.equal(orc.linear_acc(x, w).double(), _lib_sign(x) @ _lib_sign(w).T):
+                return False
+        return True
+
+    check("linear_vs_torch", lib_linear)
+
+    def lib_conv():
+        rnd = random.Random(9)
+        gen = torch.Generator().manual_seed(9)
+        n = 0
+        while n < 25:
+            b, c, h, w = rnd.choice([1, 2]), rnd.choice([1, 3, 32]), rnd.randint(2, 7), rnd.randint(2, 7)
+            o, ks, s, p, d = rnd.choice([1, 3]), rnd.choice([1, 2, 3]), rnd.choice([1, 2]), rnd.randint(0, 2), rnd.choice([1, 2])
+            if math.floor((h + 2 * p - d * (ks - 1) - 1) / s + 1) <= 0 or math.floor((w + 2 * p - d * (ks - 1) - 1) / s + 1) <= 0:
+                continue
+            n += 1
+            x, wt = torch.randn((b, c, h, w), generator=gen), torch.randn((o, c, ks, ks), generator=gen)
+            ref = torch.nn.functional.conv2d(_lib_sign(x), _lib_sign(wt), stride=s, padding=p, dilation=d)
+            if not torch.equal(orc.conv2d_acc(x, wt, s, p, d).double(), ref):
+                return False
+        return True
+
+    check("conv_vs_torch", lib_conv)
+    return failed
+
+
+@pytest.fixture()
+def swap_oracle():
+    saved = oracle._lib
+    yield
+    oracle._lib = saved
+
+
+def _compile_variant(tmp_path, name, edit):
+    src = open(SRC).read()
+    if edit is not None:
+        old, new = edit
+        assert src.count(old) == 1, f"mutation site for {name} not unique"
+        src = src.replace(old, new)
+    path = tmp_path / f"{name}.c"
+    path.write_text(src)
+    lib = oracle.compile_library(str(path), str(tmp_path / f"lib{name}.so"))
+    return oracle._bind(ctypes.CDLL(lib))
+
+
+def test_unmodified_oracle_passes_fast_pins(tmp_path, swap_oracle):
+    oracle._lib = _compile_variant(tmp_path, "original", None)
+    assert _pins(oracle) == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(tmp_path, swap_oracle, name):
+    oracle._lib = _compile_variant(tmp_path, name, MUTANTS[name])
+    failed = _pins(oracle)
+    assert failed, f"mutant {name} passed every pin"
