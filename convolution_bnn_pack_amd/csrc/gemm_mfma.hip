@@ -4,31 +4,31 @@
 // v_mfma_i32_32x32x32_i8 (32x32 output block, 32-deep reduction, int32
 // sums). Signs stay bit-packed in HBM; a workgroup loads the packed words of
 // its A (activation) and W (weight) tiles and expands each word in registers
-// before storing it to LDS:
+// before storing it to LDS. Dword d (d = 0..7) of a word's 32 expanded bytes
+// holds bits d, d+8, d+16, d+24, one per byte:
 //
-//   v_perm_b32 with selector bytes 8..11 replicates bits 15 and 31 of each of
-//   its two sources into whole bytes (0x00 or 0xFF). With the sources
-//   w << 2d and w << 2d+1 (d = 0..7) every bit of w lands in exactly one of
-//   32 bytes. The byte order is a fixed permutation of the word's 32
-//   reduction indices, the same for A and W, so the sums are unchanged.
+//   t_d = (w >> d) & 0x01010101                   (bytes 0 / 1)
+//   W bytes  w' = t_d = b
+//   A bytes  a' = v_perm_b32(0, 0x000001FF, t_d)  (selector byte 0 or 1 picks
+//            0xFF or 0x01, so a' = 2b - 1 = s), or a table of 0 for a padded
+//            conv tap or a position past K (every byte 0).
 //
-// Encodings (b = packed bit, 1 for a +1 sign; s = 2b - 1):
-//   W bytes  w' = -b           (the raw 0x00 / 0xFF mask)
-//   A bytes  a' = 1 - 2b = -s  (mask | 0x01), and 0 for a padded conv tap or
-//            a position past K.
-// The MFMA sum is sum a'w' = sum s_a b_w over the real terms, and since
-// s_w = 2 b_w - 1 the binary dot product is
+// The byte order is a fixed permutation of the word's 32 reduction indices,
+// the same for A and W, so the sums are unchanged. With b the packed bit (1
+// for a +1 sign) and s = 2b - 1, the MFMA sum is sum a'w' = sum s_a b_w over
+// the real terms, and since s_w = 2 b_w - 1 the binary dot product is
 //   dot = sum s_a s_w = 2 * mfma - sum s_a = K_valid - 2 * popA + 2 * mfma,
 // with popA the number of set bits among the row's real A words and K_valid
 // = 32 * (number of real A words). Both are counted by the thread that loads
-// the row, so padded taps need no per-weight correction.
+// the row, so padded taps need no per-weight correction. Expanding a word
+// costs 15 VALU operations for W and 23 for A.
 //
-// Tiling: a 256-thread workgroup (4 waves as 2 x 2) owns a BM (rows of A) x
-// BN (rows of W) output tile and walks the reduction KS words (32*KS signs)
-// per stage through two LDS buffers (one barrier per stage): while the waves
-// run the MFMAs of stage s from one buffer, the loader expands stage s+1 into
-// the other and fetches stage s+2 from global memory. Each wave holds a
-// (BM/2) x (BN/2) sub-tile as (BM/64) x (BN/64) MFMA blocks; the MFMA computes
+// Tiling: a workgroup of 2 x WGN waves owns a BM (rows of A) x BN (rows of W)
+// output tile and walks the reduction KS words (32*KS signs) per stage
+// through two LDS buffers (one barrier per stage): while the waves run the
+// MFMAs of stage s from one buffer, they expand stage s+1 into the other and
+// fetch stage s+PD from global memory (PD register sets of raw words). Each
+// wave holds a (BM/2) x (BN/WGN) sub-tile of 32 x 32 MFMA blocks; the MFMA computes
 // D = W_tile * A_tile^T so each lane's four consecutive accumulators are four
 // consecutive output features of one row (vector stores for linear outputs,
 // lane-contiguous runs for NCHW conv outputs). LDS rows are 32*KS bytes; the
@@ -185,22 +185,6 @@ __device__ __forceinline__ void load_w(const Contraction& p, int n, int q0, uint
   }
 }
 
-// Expand one packed word into the 32 bytes of reduction chunk `word` of an LDS row:
-// bytes (mask & keep) | ones, mask = 0xFF per set bit.
-template <class T>
-__device__ __forceinline__ void expand_word(uint8_t* buf, int lrow, int word, uint32_t w,
-                                            uint32_t keep, uint32_t ones) {
-  uint32_t y[8];
-#pragma unroll
-  for (int d = 0; d < 8; d++) {
-    const uint32_t m = __builtin_amdgcn_perm(w << (2 * d + 1), w << (2 * d), 0x0B0A0908u);
-    y[d] = (m & keep) | ones;
-  }
-  uint8_t* line = buf + lrow * T::ROWB;
-  *reinterpret_cast<uint4*>(line + 16 * swz<T>(lrow, 2 * word)) = make_uint4(y[0], y[1], y[2], y[3]);
-  *reinterpret_cast<uint4*>(line + 16 * swz<T>(lrow, 2 * word + 1)) = make_uint4(y[4], y[5], y[6], y[7]);
-}
-
 // Tile index -> (m-tile, n-tile): contiguous runs of tiles per XCD, n fastest.
 __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
   const int total = tiles_m * tiles_n;
@@ -256,27 +240,24 @@ __global__ __launch_bounds__(T::THREADS) void mfma_kernel(Contraction p) {
     load_w<T::W_WPT, VEC>(p, wn_row, q0 + w_q, rw[set], okw[set]);
   };
 
-  // expansion of stage words: source value, OR term and LDS row / word slot of word wi
-  uint32_t src[NWORD], orv[NWORD];
+  // expansion of stage words: source word, and for A words the byte table of v_perm
+  // (0xFF for a 0 bit, 0x01 for a 1 bit; all 0 for an invalid word)
+  uint32_t src[NWORD], tab[T::A_WPT];
   auto prepare = [&](int set) {
 #pragma unroll
     for (int i = 0; i < T::A_WPT; i++) {
-      src[i] = oka[set][i] ? ra[set][i] : 0u;  // an invalid word expands to 0x00 bytes
-      orv[i] = oka[set][i] ? 0x01010101u : 0u;
-      rowk_part += oka[set][i] ? 32 - 2 * __popc(src[i]) : 0;
+      src[i] = ra[set][i];
+      tab[i] = oka[set][i] ? 0x000001FFu : 0u;
+      rowk_part += oka[set][i] ? 32 - 2 * __popc(ra[set][i]) : 0;
     }
 #pragma unroll
-    for (int i = 0; i < T::W_WPT; i++) {
-      src[T::A_WPT + i] = okw[set][i] ? rw[set][i] : 0u;
-      orv[T::A_WPT + i] = 0u;
-    }
+    for (int i = 0; i < T::W_WPT; i++) src[T::A_WPT + i] = okw[set][i] ? rw[set][i] : 0u;
   };
   uint32_t y[NU];
   auto expand_unit = [&](uint8_t* buf, int u) {
     const int wi = u >> 3, d = u & 7;
-    const uint32_t w = src[wi];
-    y[u] = __builtin_amdgcn_perm(w << (2 * d + 1), w << (2 * d), 0x0B0A0908u);
-    if (wi < T::A_WPT) y[u] |= orv[wi];
+    const uint32_t t = (src[wi] >> d) & 0x01010101u;
+    y[u] = wi < T::A_WPT ? __builtin_amdgcn_perm(0u, tab[wi], t) : t;
     if ((d & 3) == 3) {
       const int lrow = wi < T::A_WPT ? a_row : T::BM + w_row;
       const int word = wi < T::A_WPT ? a_q + wi : w_q + (wi - T::A_WPT);
