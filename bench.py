@@ -17,6 +17,7 @@ timed region) and the CPU oracle's throughput on the host as a baseline.
 import argparse
 import hashlib
 import json
+import re
 import os
 import sys
 import time
@@ -26,14 +27,32 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0           # HBM3E, MI355X
 PEAK_MFMA_I8_TOPS = 5000.0      # dense int8 MFMA, MI355X
+PEAK_MFMA_F4_TOPS = 10100.0     # dense fp4 MFMA, MI355X
 # XOR path: 256 CUs x 64 lanes x 2.4 GHz lane-ops; one v_xor_b32 + one v_bcnt_u32_b32
 # cover 32 MACs = 64 binary ops, i.e. 32 binary ops per lane-op.
 PEAK_VALU_BINARY_TOPS = 256 * 64 * 2.4e9 * 32 / 1e12
 
 DEFAULT_WORKLOAD = "linear_2048x4096x4096_f16"
 PACK_WORKLOAD = "pack_linear_16384x8192_bf16"
-KERNEL_SOURCES = {"mfma": "gemm_mfma.hip", "xor": "gemm_xor.hip", "pack": "pack.hip"}
-KERNEL_NAMES = {"mfma": "mfma_kernel", "xor": "xor_kernel", "pack": "pack_rows_kernel"}
+# kernel kinds: source file, kernel function name, roofline peak and arithmetic type
+KERNEL_SOURCES = {"mfma": "gemm_mfma.hip", "mfma_fp4": "gemm_mfma.hip", "xor": "gemm_xor.hip",
+                  "pack": "pack.hip"}
+KERNEL_NAMES = {"mfma": "mfma_kernel", "mfma_fp4": "mfma_kernel", "xor": "xor_kernel",
+                "pack": "pack_rows_kernel"}
+PEAKS = {"mfma": PEAK_MFMA_I8_TOPS, "mfma_fp4": PEAK_MFMA_F4_TOPS, "xor": PEAK_VALU_BINARY_TOPS}
+DTYPES = {"mfma": "i8", "mfma_fp4": "fp4(e2m1)", "xor": "u32"}
+
+
+def kernel_kind(name):
+    """Kind of a demangled kernel name from a rocprofv3 counter file (None: not ours)."""
+    for kind in ("pack", "xor"):
+        if KERNEL_NAMES[kind] + "<" in name or KERNEL_NAMES[kind] + "(" in name:
+            return kind
+    if "mfma_kernel<" in name:
+        # the tile's last template argument is the fp4 flag
+        m = re.search(r"Tile<[^>]*, (true|false)>", name)
+        return "mfma_fp4" if m and m.group(1) == "true" else "mfma"
+    return None
 
 
 def log(msg):
@@ -51,7 +70,7 @@ def traffic_for(kind, workload):
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
-    rec = json.load(open(path)).get(f"{KERNEL_NAMES[kind]}|{workload}")
+    rec = json.load(open(path)).get(f"{kind}|{workload}")
     if not rec or rec.get("src_sha") != src_sha(kind):
         return None
     return rec.get("bytes_per_launch")
@@ -84,11 +103,10 @@ def pmc_summary(args):
             raise SystemExit(f"no {args.copy_kernel} kernel in {path}")
         copy_kib = statistics.median(copy)
         scale = (args.copy_mib << 20) / 1024.0 / copy_kib if args.copy_mib else 1.0
-        for k in (["pack"] if kind else ["mfma", "xor"]):
+        for k in (["pack"] if kind else ["mfma", "mfma_fp4", "xor"]):
             # the workload's kernel is the instantiation launched most often (the parity spot
             # check adds single launches of other output types)
-            cands = [(len(vs), name) for name, vs in vals.items()
-                     if KERNEL_NAMES[k] + "<" in name or KERNEL_NAMES[k] + "(" in name]
+            cands = [(len(vs), name) for name, vs in vals.items() if kernel_kind(name) == k]
             if not cands:
                 continue
             _, name = max(cands)
@@ -102,7 +120,7 @@ def pmc_summary(args):
             continue
         fetch = rec["fetch_size_kib_median"] * 1024 * rec["fetch_size_scale"]
         write = rec["write_size_kib_median"] * 1024 * rec["write_size_scale"]
-        db[f"{KERNEL_NAMES[k]}|{wl}"] = {
+        db[f"{k}|{wl}"] = {"kernel": KERNEL_NAMES[k],
             "bytes_per_launch": round(fetch + write), "fetch_bytes": round(fetch),
             "write_bytes": round(write), "fetch_scale": round(rec["fetch_size_scale"], 4),
             "write_scale": round(rec["write_size_scale"], 4), "src_sha": src_sha(k),
@@ -152,7 +170,7 @@ def main():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--path", default="auto", choices=["auto", "xor", "mfma"])
+    ap.add_argument("--path", default="auto", choices=["auto", "xor", "mfma", "mfma_fp4"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the workload, run 5 plain device copies of this many MiB "
@@ -300,16 +318,16 @@ def main():
         metric, unit, dtype = "sign+pack bandwidth", "GB/s", "u32"
     else:
         dom_ms = kern_ms["core"]
-        kind = "mfma" if path_used == bnn.PATH_MFMA else "xor"
+        kind = {bnn.PATH_XOR: "xor", bnn.PATH_MFMA: "mfma", bnn.PATH_MFMA_FP4: "mfma_fp4"}[path_used]
         achieved = ops / (dom_ms * 1e-3) / 1e12
-        peak = PEAK_MFMA_I8_TOPS if kind == "mfma" else PEAK_VALU_BINARY_TOPS
-        roof = {"bound": "mfma" if kind == "mfma" else "alu", "achieved": round(achieved, 2),
+        peak = PEAKS[kind]
+        roof = {"bound": "alu" if kind == "xor" else "mfma", "achieved": round(achieved, 2),
                 "peak": round(peak, 1), "unit": "TOP/s", "frac": round(achieved / peak, 4),
                 "traffic": traffic_for(kind, args.workload), "kernel": KERNEL_NAMES[kind],
                 "kernel_ms": round(dom_ms, 5), "pack_kernel_ms": round(kern_ms["pack"], 5)}
         value = ops / (ms_per_step * 1e-3) / 1e12
         metric, unit = "binary TOPS (2*M*N*K/s)", "TOPS"
-        dtype = "i8" if kind == "mfma" else "u32"
+        dtype = DTYPES[kind]
 
     result = {
         "metric": metric, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
@@ -323,7 +341,7 @@ def main():
         m, n, k = wl.gemm_mnk()
         result["config"].update({"m": m, "n": n, "k": k, "x_dtype": wl.x_dtype,
                                  "out_dtype": wl.out_dtype,
-                                 "path": {bnn.PATH_XOR: "xor", bnn.PATH_MFMA: "mfma"}[path_used]})
+                                 "path": kind})
         result["parity_spot_check"] = parity
     if args.copy_mib:
         # plain device copies of a known size, for scaling the traffic counters

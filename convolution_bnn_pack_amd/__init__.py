@@ -27,14 +27,14 @@ LIB_PATH = os.environ.get("BNN_LIBRARY") or os.path.join(_PKG, "libbnn.so")
 
 # bnn_dtype / bnn_path / bnn_status codes of include/bnn.h
 F32, F16, BF16, I32, U32_PACKED = 0, 1, 2, 3, 4
-PATH_AUTO, PATH_XOR, PATH_MFMA = 0, 1, 2
+PATH_AUTO, PATH_XOR, PATH_MFMA, PATH_MFMA_FP4 = 0, 1, 2, 3
 OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIGN, ERR_WORKSPACE, ERR_PATH, ERR_HIP = range(8)
 
 EXPORTS = ("bnn_pack_sign", "bnn_pack_sign_nchw", "bnn_w_pack", "bnn_gemm", "bnn_conv2d",
            "bnn_gemm_workspace_bytes", "bnn_conv2d_workspace_bytes", "bnn_gemm_auto_path",
            "bnn_conv2d_auto_path", "bnn_last_path", "bnn_status_string")
 
-_PATHS = {"auto": PATH_AUTO, "xor": PATH_XOR, "mfma": PATH_MFMA}
+_PATHS = {"auto": PATH_AUTO, "xor": PATH_XOR, "mfma": PATH_MFMA, "mfma_fp4": PATH_MFMA_FP4}
 _DT = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16, torch.int32: I32}
 _TORCH = {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16, I32: torch.int32}
 

@@ -37,17 +37,33 @@ float alpha_of(double scale_a, double scale_w) { return (float)(scale_a * scale_
 
 bnn_status hip_status(hipError_t e) { return e == hipSuccess ? BNN_OK : BNN_ERR_HIP; }
 
-// Shape-based choice between the two contraction paths. The matrix-core
-// path has 4x the VALU path's peak but pays for the bit expansion and needs
-// enough 128x128 tiles to keep the chip busy; tiny contractions (a few
-// workgroups) run on the VALU path, whose tiles carry less fixed cost.
+// Shape-based choice between the contraction paths. The matrix-core paths
+// have 4x (int8) and 8x (fp4) the VALU path's peak but pay for the bit
+// expansion and need enough tiles to keep the chip busy; tiny contractions
+// (a few workgroups) run on the VALU path, whose tiles carry less fixed cost.
+// fp4 operands move half the bytes through LDS per reduction step and run
+// the MFMAs at twice the int8 rate; its fp32 sums are exact up to K = 2^24,
+// beyond which the int8 path takes over.
 int auto_path(int64_t m, int64_t n, int64_t k) {
   const double work = (double)m * (double)n * (double)k;
   if (work < 3.0e8) return BNN_PATH_XOR;
-  return BNN_PATH_MFMA;
+  return k <= bnn::kMaxFp4K ? BNN_PATH_MFMA_FP4 : BNN_PATH_MFMA;
 }
 
 bool int_fits(int64_t v) { return v >= 0 && v <= 0x7FFFFFFFLL; }
+
+bool path_known(int path) {
+  return path == BNN_PATH_AUTO || path == BNN_PATH_XOR || path == BNN_PATH_MFMA ||
+         path == BNN_PATH_MFMA_FP4;
+}
+
+hipError_t run_path(int use, const bnn::Contraction& p, bool conv, int out_dtype, hipStream_t s) {
+  switch (use) {
+    case BNN_PATH_XOR: return bnn::launch_xor(p, conv, out_dtype, s);
+    case BNN_PATH_MFMA_FP4: return bnn::launch_mfma_fp4(p, conv, out_dtype, s);
+    default: return bnn::launch_mfma(p, conv, out_dtype, s);
+  }
+}
 
 }  // namespace
 
@@ -86,7 +102,8 @@ int bnn_conv2d_auto_path(int64_t n, int64_t c, int64_t h, int64_t w, int64_t out
   if (kernel_size < 1 || stride < 1 || dilation < 1 || padding < 0) return BNN_PATH_MFMA;
   const int64_t ho = out_size(h, kernel_size, stride, padding, dilation);
   const int64_t wo = out_size(w, kernel_size, stride, padding, dilation);
-  if (kernel_size * kernel_size > bnn::xor_conv_max_taps()) return BNN_PATH_MFMA;
+  if (kernel_size * kernel_size > bnn::xor_conv_max_taps())
+    return (int64_t)kernel_size * kernel_size * c <= bnn::kMaxFp4K ? BNN_PATH_MFMA_FP4 : BNN_PATH_MFMA;
   return auto_path(n * (ho > 0 ? ho : 0) * (wo > 0 ? wo : 0), out_channels,
                    c * kernel_size * kernel_size);
 }
@@ -140,7 +157,8 @@ bnn_status bnn_gemm(const void* x, int x_dtype, const uint32_t* w_packed, int64_
     return BNN_ERR_DTYPE;
   if (m < 0 || n < 0 || k < 32 || k % 32 != 0) return BNN_ERR_SHAPE;
   if (!int_fits(m) || !int_fits(n) || !int_fits(k / 32)) return BNN_ERR_SHAPE;
-  if (path != BNN_PATH_AUTO && path != BNN_PATH_XOR && path != BNN_PATH_MFMA) return BNN_ERR_PATH;
+  if (!path_known(path)) return BNN_ERR_PATH;
+  if (path == BNN_PATH_MFMA_FP4 && k > bnn::kMaxFp4K) return BNN_ERR_PATH;
   if (m == 0 || n == 0) return BNN_OK;
   if (!x || !w_packed || !out) return BNN_ERR_NULL;
   const bool packed = x_dtype == BNN_U32_PACKED;
@@ -167,8 +185,7 @@ bnn_status bnn_gemm(const void* x, int x_dtype, const uint32_t* w_packed, int64_
   p.N = (int)n;
   p.KW = (int)(k / 32);
   p.alpha = alpha_of(scale_a, scale_w);
-  const hipError_t e = use == BNN_PATH_XOR ? bnn::launch_xor(p, false, out_dtype, s)
-                                           : bnn::launch_mfma(p, false, out_dtype, s);
+  const hipError_t e = run_path(use, p, false, out_dtype, s);
   if (e != hipSuccess) return BNN_ERR_HIP;
   g_last_path = use;
   return BNN_OK;
@@ -191,9 +208,10 @@ bnn_status bnn_conv2d(const void* x, int x_dtype, int64_t n, int64_t c, int64_t 
       !int_fits(n * h * w * (c / 32)) || !int_fits(h + 2 * (int64_t)padding) ||
       !int_fits(w + 2 * (int64_t)padding))
     return BNN_ERR_SHAPE;
-  if (path != BNN_PATH_AUTO && path != BNN_PATH_XOR && path != BNN_PATH_MFMA) return BNN_ERR_PATH;
+  if (!path_known(path)) return BNN_ERR_PATH;
   if (path == BNN_PATH_XOR && kernel_size * kernel_size > bnn::xor_conv_max_taps())
     return BNN_ERR_PATH;
+  if (path == BNN_PATH_MFMA_FP4 && 32 * kw_words > bnn::kMaxFp4K) return BNN_ERR_PATH;
   if (n == 0 || out_channels == 0) return BNN_OK;
   if (!x || !w_packed || !out) return BNN_ERR_NULL;
   const bool packed = x_dtype == BNN_U32_PACKED;
@@ -232,8 +250,7 @@ bnn_status bnn_conv2d(const void* x, int x_dtype, int64_t n, int64_t c, int64_t 
   p.stride = stride;
   p.pad = padding;
   p.dil = dilation;
-  const hipError_t e = use == BNN_PATH_XOR ? bnn::launch_xor(p, true, out_dtype, s)
-                                           : bnn::launch_mfma(p, true, out_dtype, s);
+  const hipError_t e = run_path(use, p, true, out_dtype, s);
   if (e != hipSuccess) return BNN_ERR_HIP;
   g_last_path = use;
   return BNN_OK;

@@ -1,11 +1,16 @@
-// +-1-as-int8 binary contraction on the gfx950 matrix cores.
+// Binary contraction on the gfx950 matrix cores, with the signs expanded to
+// int8 or to fp4 (e2m1) operands.
 //
 // The binary dot product is a dense contraction, so it runs on
 // v_mfma_i32_32x32x32_i8 (32x32 output block, 32-deep reduction, int32
-// sums). Signs stay bit-packed in HBM; a workgroup loads the packed words of
-// its A (activation) and W (weight) tiles and expands each word in registers
-// before storing it to LDS. Dword d (d = 0..7) of a word's 32 expanded bytes
-// holds bits d, d+8, d+16, d+24, one per byte:
+// sums) or on v_mfma_scale_f32_32x32x64_f8f6f4 with both operands fp4 and
+// unit scales (64-deep reduction at twice the int8 rate, fp32 sums). Signs
+// stay bit-packed in HBM; a workgroup loads the packed words of its A
+// (activation) and W (weight) tiles and expands each word in registers before
+// storing it to LDS.
+//
+// int8: dword d (d = 0..7) of a word's 32 expanded bytes holds bits d, d+8,
+// d+16, d+24, one per byte:
 //
 //   t_d = (w >> d) & 0x01010101                   (bytes 0 / 1)
 //   W bytes  w' = t_d = b
@@ -23,6 +28,13 @@
 // the row, so padded taps need no per-weight correction. Expanding a word
 // costs 15 VALU operations for W and 23 for A.
 //
+// fp4: a word expands to 16 bytes, nibble i of dword d (d = 0..3) holding bit
+// 4i + d: W 0x2 (1.0) for a set bit, else 0x0; A 0x2 (+1.0) or 0xA (-1.0),
+// and 0x0 throughout for an invalid word. The same sums and correction apply.
+// Every product is 0 or +-1 and every partial sum an integer of magnitude at
+// most K, exact in fp32 for K <= 2^24. A word costs 7 VALU operations for W
+// and about 10 for A, and an MFMA k-step covers two words instead of one.
+//
 // Tiling: a workgroup of 2 x WGN waves owns a BM (rows of A) x BN (rows of W)
 // output tile and walks the reduction KS words (32*KS signs) per stage
 // through two LDS buffers (one barrier per stage): while the waves run the
@@ -31,7 +43,7 @@
 // wave holds a (BM/2) x (BN/WGN) sub-tile of 32 x 32 MFMA blocks; the MFMA computes
 // D = W_tile * A_tile^T so each lane's four consecutive accumulators are four
 // consecutive output features of one row (vector stores for linear outputs,
-// lane-contiguous runs for NCHW conv outputs). LDS rows are 32*KS bytes; the
+// lane-contiguous runs for NCHW conv outputs). LDS rows are 128 bytes; the
 // 16-byte chunks of a row are XOR-swizzled with a Gray code of the row index
 // so the ds_read_b128 / ds_write_b128 of 8 or 16 consecutive rows hit
 // distinct banks. Tiles are numbered so that each XCD (workgroups go
@@ -40,6 +52,7 @@
 // Conv is the im2col lowering of the banghao.live blog post, section 2,
 // computed implicitly: A row m is output pixel (b, oh, ow) and reduction word
 // q = tap * CW + cw reads activation word [b][oh*s - p + kh*d][ow*s - p + kw*d][cw].
+#include <type_traits>
 #include <utility>
 
 #include "launch.h"
@@ -48,19 +61,29 @@ namespace bnn {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
-template <int BM_, int BN_, int KS_, int PD_, int WGM_, int WGN_>
+// fp4 e2m1 format code of the scaled MFMA, and the E8M0 scale exponent of 1.0
+constexpr int kFmtFp4 = 4;
+constexpr int kScaleOne = 127;
+
+template <int BM_, int BN_, int KS_, int PD_, int WGM_, int WGN_, bool F4_>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, KS = KS_;
+  static constexpr bool F4 = F4_;                   // fp4 (e2m1) operands instead of int8
   static constexpr int PD = PD_;                    // stages of raw words in flight (register sets)
   static constexpr int UNROLL = PD % 2 == 0 ? PD : 2 * PD;  // lcm(2, PD): LDS parity x register set
   static constexpr int WGM = WGM_, WGN = WGN_;      // wave grid: WGM waves along A rows, WGN along W rows
   static constexpr int THREADS = 64 * WGM * WGN;
   static constexpr int WTM = BM / WGM, WTN = BN / WGN;  // wave sub-tile
   static constexpr int FM = WTM / 32, FN = WTN / 32;    // MFMA blocks per wave
-  static constexpr int ROWB = KS * 32;              // LDS bytes per row per stage
+  static constexpr int CPW = F4 ? 1 : 2;            // 16-byte LDS chunks per expanded word
+  static constexpr int UPW = 4 * CPW;               // expansion units (output dwords) per word
+  static constexpr int ROWB = KS * 16 * CPW;        // LDS bytes per row per stage
   static constexpr int CHUNKS = ROWB / 16;
+  static constexpr int KSTEPS = CHUNKS / 2;         // MFMA k-steps per stage (chunks 2kk, 2kk+1)
   static constexpr int BUF = (BM + BN) * ROWB;      // one LDS buffer: A rows, then W rows
   // loader split: every thread expands A_WPT consecutive words of one A row and W_WPT
   // consecutive words of one W row per stage
@@ -209,10 +232,10 @@ __global__ __launch_bounds__(T::THREADS) void mfma_kernel(Contraction p) {
   __shared__ int rowk[T::BM];  // K_valid - 2 * popA per A row of the tile
 
   constexpr int MPK = T::FN * T::FM;            // MFMAs per k-step
-  constexpr int NM = MPK * T::KS;               // MFMAs per stage
+  constexpr int NM = MPK * T::KSTEPS;           // MFMAs per stage
   constexpr int RPK = T::FN + T::FM;            // fragment reads per k-step
   constexpr int NWORD = T::A_WPT + T::W_WPT;    // words this thread expands per stage
-  constexpr int NU = NWORD * 8;                 // expansion units (one output dword each)
+  constexpr int NU = NWORD * T::UPW;            // expansion units (one output dword each)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -240,14 +263,22 @@ __global__ __launch_bounds__(T::THREADS) void mfma_kernel(Contraction p) {
     load_w<T::W_WPT, VEC>(p, wn_row, q0 + w_q, rw[set], okw[set]);
   };
 
-  // expansion of stage words: source word, and for A words the byte table of v_perm
-  // (0xFF for a 0 bit, 0x01 for a 1 bit; all 0 for an invalid word)
-  uint32_t src[NWORD], tab[T::A_WPT];
+  // expansion of stage words. int8: the source word, and for A words the byte table of
+  // v_perm (0xFF for a 0 bit, 0x01 for a 1 bit; all 0 for an invalid word). fp4: W keeps
+  // the word; A keeps its complement with an AND mask and an OR term (both 0 for an
+  // invalid word).
+  uint32_t src[NWORD], tab[T::A_WPT], tabo[T::A_WPT];
   auto prepare = [&](int set) {
 #pragma unroll
     for (int i = 0; i < T::A_WPT; i++) {
-      src[i] = ra[set][i];
-      tab[i] = oka[set][i] ? 0x000001FFu : 0u;
+      if constexpr (T::F4) {
+        src[i] = ~ra[set][i];
+        tab[i] = oka[set][i] ? 0x88888888u : 0u;
+        tabo[i] = oka[set][i] ? 0x22222222u : 0u;
+      } else {
+        src[i] = ra[set][i];
+        tab[i] = oka[set][i] ? 0x000001FFu : 0u;
+      }
       rowk_part += oka[set][i] ? 32 - 2 * __popc(ra[set][i]) : 0;
     }
 #pragma unroll
@@ -255,25 +286,38 @@ __global__ __launch_bounds__(T::THREADS) void mfma_kernel(Contraction p) {
   };
   uint32_t y[NU];
   auto expand_unit = [&](uint8_t* buf, int u) {
-    const int wi = u >> 3, d = u & 7;
-    const uint32_t t = (src[wi] >> d) & 0x01010101u;
-    y[u] = wi < T::A_WPT ? __builtin_amdgcn_perm(0u, tab[wi], t) : t;
+    const int wi = u / T::UPW, d = u % T::UPW;
+    if constexpr (T::F4) {
+      // nibble i of dword d is bit 4i + d: W 0x2 (1.0) or 0x0; A 0x2 (+1.0) or 0xA (-1.0)
+      if (wi < T::A_WPT)
+        y[u] = ((src[wi] << (3 - d)) & tab[wi]) | tabo[wi];
+      else
+        y[u] = (d == 0 ? src[wi] << 1 : src[wi] >> (d - 1)) & 0x22222222u;
+    } else {
+      // byte j of dword d is bit 8j + d: W 0 or 1; A -1 or +1
+      const uint32_t t = (src[wi] >> d) & 0x01010101u;
+      y[u] = wi < T::A_WPT ? __builtin_amdgcn_perm(0u, tab[wi], t) : t;
+    }
     if ((d & 3) == 3) {
       const int lrow = wi < T::A_WPT ? a_row : T::BM + w_row;
       const int word = wi < T::A_WPT ? a_q + wi : w_q + (wi - T::A_WPT);
       uint8_t* line = buf + lrow * T::ROWB;
-      *reinterpret_cast<uint4*>(line + 16 * swz<T>(lrow, 2 * word + (d >> 2))) =
+      *reinterpret_cast<uint4*>(line + 16 * swz<T>(lrow, T::CPW * word + (d >> 2))) =
           make_uint4(y[u - 3], y[u - 2], y[u - 1], y[u]);
     }
   };
 
-  v16i acc[T::FN][T::FM];
+  // int32 sums (int8 operands) or fp32 sums (fp4 operands; integers of magnitude at most
+  // K <= 2^24, so every partial sum is exact)
+  using Acc = std::conditional_t<T::F4, v16f, v16i>;
+  Acc acc[T::FN][T::FM];
 #pragma unroll
   for (int i = 0; i < T::FN; i++)
 #pragma unroll
     for (int j = 0; j < T::FM; j++)
 #pragma unroll
       for (int e = 0; e < 16; e++) acc[i][j][e] = 0;
+  auto acc_int = [&](int fn, int fm, int e) -> int { return (int)acc[fn][fm][e]; };
 
   const int fr = lane & 31, half = lane >> 5;
   v4i fa[2][T::FM], fw[2][T::FN];
@@ -307,10 +351,19 @@ __global__ __launch_bounds__(T::THREADS) void mfma_kernel(Contraction p) {
     for (int i = 0; i < NM; i++) {
       const int kk = i / MPK, j = i % MPK;
       const int fn = j / T::FM, fm = j % T::FM;
-      acc[fn][fm] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fw[kk & 1][fn], fa[kk & 1][fm],
-                                                           acc[fn][fm], 0, 0, 0);
+      if constexpr (T::F4) {
+        // only the first four dwords of each operand carry fp4 data
+        const v4i w4 = fw[kk & 1][fn], a4 = fa[kk & 1][fm];
+        const v8i w8 = {w4[0], w4[1], w4[2], w4[3], 0, 0, 0, 0};
+        const v8i a8 = {a4[0], a4[1], a4[2], a4[3], 0, 0, 0, 0};
+        acc[fn][fm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            w8, a8, acc[fn][fm], kFmtFp4, kFmtFp4, 0, kScaleOne, 0, kScaleOne);
+      } else {
+        acc[fn][fm] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fw[kk & 1][fn], fa[kk & 1][fm],
+                                                             acc[fn][fm], 0, 0, 0);
+      }
       // the next k-step's RPK fragment reads are spread over this k-step's MPK slots
-      if (kk + 1 < T::KS) {
+      if (kk + 1 < T::KSTEPS) {
 #pragma unroll
         for (int f = j * RPK / MPK; f < (j + 1) * RPK / MPK; f++) read_frag(cur, kk + 1, f);
       }
@@ -375,7 +428,7 @@ __global__ __launch_bounds__(T::THREADS) void mfma_kernel(Contraction p) {
         for (int e = 0; e < 16; e++) {
           const int n = n0 + wn * T::WTN + fn * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
           if (n < p.N)
-            store1<OUT>(p.out, ((int64_t)b * p.N + n) * hw + pix, base_k + 2 * acc[fn][fm][e], p.alpha);
+            store1<OUT>(p.out, ((int64_t)b * p.N + n) * hw + pix, base_k + 2 * acc_int(fn, fm, e), p.alpha);
         }
     }
   } else {
@@ -401,9 +454,9 @@ __global__ __launch_bounds__(T::THREADS) void mfma_kernel(Contraction p) {
 #pragma unroll
         for (int g = 0; g < 4; g++) {
           const int c = fn * 32 + 8 * g + 4 * half;
-          O::put4(myrow + c * (int)sizeof(typename O::type), base_k + 2 * acc[fn][fm][4 * g],
-                  base_k + 2 * acc[fn][fm][4 * g + 1], base_k + 2 * acc[fn][fm][4 * g + 2],
-                  base_k + 2 * acc[fn][fm][4 * g + 3], p.alpha);
+          O::put4(myrow + c * (int)sizeof(typename O::type), base_k + 2 * acc_int(fn, fm, 4 * g),
+                  base_k + 2 * acc_int(fn, fm, 4 * g + 1), base_k + 2 * acc_int(fn, fm, 4 * g + 2),
+                  base_k + 2 * acc_int(fn, fm, 4 * g + 3), p.alpha);
         }
       // the band is private to this wave and a wave's LDS accesses complete in order, so
       // no fence is needed (a memory fence here would also wait for the global stores)
@@ -456,14 +509,14 @@ hipError_t launch_tile_v(const Contraction& p, int out_dtype, hipStream_t stream
   return hipGetLastError();
 }
 
-// Vector loads need every thread's words of a stage to be contiguous and aligned: the
-// stage width divides K (linear) or C/32 (conv, so a stage never straddles taps), and
-// both operand bases are 16-byte aligned.
+// Vector loads need each thread's words of a stage to be contiguous, aligned and, for
+// conv, within one tap: the per-thread word counts divide K/32 (linear) or C/32 and the
+// weight row length (conv), and both operand bases are 16-byte aligned.
 template <class T, bool CONV>
 hipError_t launch_tile(const Contraction& p, int out_dtype, hipStream_t stream) {
   const bool aligned = (reinterpret_cast<uintptr_t>(p.a) % 16) == 0 &&
                        (reinterpret_cast<uintptr_t>(p.w) % 16) == 0;
-  const bool vec = aligned && (CONV ? (p.CW % T::KS) == 0 : (p.KW % T::KS) == 0);
+  const bool vec = aligned && (CONV ? p.CW : p.KW) % T::A_WPT == 0 && p.KW % T::W_WPT == 0;
   return vec ? launch_tile_v<T, CONV, true>(p, out_dtype, stream)
              : launch_tile_v<T, CONV, false>(p, out_dtype, stream);
 }
@@ -478,10 +531,23 @@ hipError_t launch_tile(const Contraction& p, int out_dtype, hipStream_t stream) 
 #define BNN_MFMA_WAVES_N 4
 #endif
 // 2 x BNN_MFMA_WAVES_N waves per workgroup: with 4 along W there are two waves per SIMD,
-// whose MFMA and expansion streams the hardware interleaves.
-using TileL = Tile<256, 256, 4, BNN_MFMA_PD_L, 2, BNN_MFMA_WAVES_N>;
-using TileM = Tile<128, 256, 4, BNN_MFMA_PD_M, 2, BNN_MFMA_WAVES_N>;
-using TileS = Tile<128, 128, 4, BNN_MFMA_PD_M, 2, BNN_MFMA_WAVES_N>;
+// whose MFMA and expansion streams the hardware interleaves. A stage is 128 reductions
+// (4 words) for int8 and 256 (8 words) for fp4: the same LDS row of 128 bytes and the
+// same number of MFMAs per stage.
+#ifndef BNN_MFMA_PD_CF4
+#define BNN_MFMA_PD_CF4 2
+#endif
+// fp4 conv tiles keep fewer stages in flight and stop at 128 x 256: their implicit-im2col
+// loaders hold more state per word, and deeper prefetch or a 256 x 256 tile no longer fits
+// in 256 registers per lane without spilling.
+template <bool F4, bool CONV>
+struct Tiles {
+  static constexpr int KS = F4 ? 8 : 4;
+  static constexpr int PD_M = F4 && CONV ? BNN_MFMA_PD_CF4 : BNN_MFMA_PD_M;
+  using M = Tile<128, 256, KS, PD_M, 2, BNN_MFMA_WAVES_N, F4>;
+  using L = std::conditional_t<F4 && CONV, M, Tile<256, 256, KS, BNN_MFMA_PD_L, 2, BNN_MFMA_WAVES_N, F4>>;
+  using S = Tile<128, 128, KS, PD_M, 2, BNN_MFMA_WAVES_N, F4>;
+};
 
 int64_t count_tiles(const Contraction& p, int bm, int bn) {
   return (int64_t)((p.M + bm - 1) / bm) * ((p.N + bn - 1) / bn);
@@ -491,19 +557,27 @@ int64_t count_tiles(const Contraction& p, int bm, int bn) {
 #ifndef BNN_MFMA_MIN_TILES
 #define BNN_MFMA_MIN_TILES 256
 #endif
-template <bool CONV>
+template <bool CONV, bool F4>
 hipError_t launch_mfma_t(const Contraction& p, int out_dtype, hipStream_t stream) {
   constexpr int64_t kMinTiles = BNN_MFMA_MIN_TILES;  // one workgroup per compute unit
-  if (count_tiles(p, 256, 256) >= kMinTiles) return launch_tile<TileL, CONV>(p, out_dtype, stream);
-  if (count_tiles(p, 128, 256) >= kMinTiles) return launch_tile<TileM, CONV>(p, out_dtype, stream);
-  return launch_tile<TileS, CONV>(p, out_dtype, stream);
+  using TS = Tiles<F4, CONV>;
+  if (count_tiles(p, 256, 256) >= kMinTiles) return launch_tile<typename TS::L, CONV>(p, out_dtype, stream);
+  if (count_tiles(p, 128, 256) >= kMinTiles) return launch_tile<typename TS::M, CONV>(p, out_dtype, stream);
+  return launch_tile<typename TS::S, CONV>(p, out_dtype, stream);
 }
 
 }  // namespace
 
 hipError_t launch_mfma(const Contraction& p, bool conv, int out_dtype, hipStream_t stream) {
   if (p.M == 0 || p.N == 0) return hipSuccess;
-  return conv ? launch_mfma_t<true>(p, out_dtype, stream) : launch_mfma_t<false>(p, out_dtype, stream);
+  return conv ? launch_mfma_t<true, false>(p, out_dtype, stream)
+              : launch_mfma_t<false, false>(p, out_dtype, stream);
+}
+
+hipError_t launch_mfma_fp4(const Contraction& p, bool conv, int out_dtype, hipStream_t stream) {
+  if (p.M == 0 || p.N == 0) return hipSuccess;
+  return conv ? launch_mfma_t<true, true>(p, out_dtype, stream)
+              : launch_mfma_t<false, true>(p, out_dtype, stream);
 }
 
 }  // namespace bnn

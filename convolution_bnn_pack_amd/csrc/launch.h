@@ -27,4 +27,9 @@ hipError_t launch_xor(const Contraction& p, bool conv, int out_dtype, hipStream_
 // int8 +-1 contraction on the matrix cores.
 hipError_t launch_mfma(const Contraction& p, bool conv, int out_dtype, hipStream_t stream);
 
+// fp4 (e2m1) +-1 contraction on the matrix cores; exact for a reduction length K <= 2^24
+// (kMaxFp4K), checked by the caller.
+constexpr int64_t kMaxFp4K = int64_t(1) << 24;
+hipError_t launch_mfma_fp4(const Contraction& p, bool conv, int out_dtype, hipStream_t stream);
+
 }  // namespace bnn

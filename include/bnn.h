@@ -71,9 +71,12 @@ typedef enum {
 
 /* Kernel choice; mirrors the layers' bmm_type argument (BMM.ADAPTIVE is the default there). */
 typedef enum {
-  BNN_PATH_AUTO = 0,  /* pick per shape */
-  BNN_PATH_XOR = 1,   /* XOR + popcount on the vector ALUs */
-  BNN_PATH_MFMA = 2   /* signs expanded to int8 +-1, contracted on the matrix cores */
+  BNN_PATH_AUTO = 0,     /* pick per shape */
+  BNN_PATH_XOR = 1,      /* XOR + popcount on the vector ALUs */
+  BNN_PATH_MFMA = 2,     /* signs expanded to int8 +-1, contracted on the matrix cores (int32 sums) */
+  BNN_PATH_MFMA_FP4 = 3  /* signs expanded to fp4 (e2m1) +-1.0, contracted on the matrix cores
+                            with fp32 sums, exact for a reduction length K <= 2^24 (K = k for
+                            bnn_gemm, kernel_size^2 * c for bnn_conv2d; larger K: BNN_ERR_PATH) */
 } bnn_path;
 
 /* Sign + pack of activations along rows.
@@ -134,7 +137,7 @@ int bnn_gemm_auto_path(int64_t m, int64_t n, int64_t k);
 int bnn_conv2d_auto_path(int64_t n, int64_t c, int64_t h, int64_t w, int64_t out_channels,
                          int kernel_size, int stride, int padding, int dilation);
 
-/* Path (BNN_PATH_XOR or BNN_PATH_MFMA) taken by this thread's last successful
+/* Path (BNN_PATH_XOR, BNN_PATH_MFMA or BNN_PATH_MFMA_FP4) taken by this thread's last successful
  * bnn_gemm / bnn_conv2d call; 0 before any such call. */
 int bnn_last_path(void);
 

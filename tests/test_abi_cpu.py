@@ -61,6 +61,9 @@ def test_gemm_argument_checks(bnn):
     assert _gemm(bnn, x_dtype=7) == bnn.ERR_DTYPE
     assert _gemm(bnn, out_dtype=bnn.U32_PACKED) == bnn.ERR_DTYPE
     assert _gemm(bnn, path=5) == bnn.ERR_PATH
+    # the fp4 path sums in fp32, exact only while K <= 2^24
+    assert _gemm(bnn, k=(1 << 24) + 32, path=bnn.PATH_MFMA_FP4) == bnn.ERR_PATH
+    assert _gemm(bnn, k=1 << 24, path=bnn.PATH_MFMA_FP4, x=None) == bnn.ERR_NULL
     assert _gemm(bnn, x=None) == bnn.ERR_NULL
     assert _gemm(bnn, w=None) == bnn.ERR_NULL
     assert _gemm(bnn, out=None) == bnn.ERR_NULL
@@ -92,7 +95,9 @@ def test_conv_argument_checks(bnn):
     assert _conv(bnn, h=2, ks=5, p=0) == bnn.ERR_SHAPE            # empty output
     assert _conv(bnn, x_dtype=bnn.I32) == bnn.ERR_DTYPE
     assert _conv(bnn, out_dtype=9) == bnn.ERR_DTYPE
-    assert _conv(bnn, path=3) == bnn.ERR_PATH
+    assert _conv(bnn, path=4) == bnn.ERR_PATH
+    # fp4 path: K = ks^2 * c must stay <= 2^24 (here 9 * 2^21 = 18.9M)
+    assert _conv(bnn, c=1 << 21, path=bnn.PATH_MFMA_FP4) == bnn.ERR_PATH
     assert _conv(bnn, path=bnn.PATH_XOR, ks=9, p=4) == bnn.ERR_PATH  # 81 taps > the XOR table
     assert _conv(bnn, wp=None) == bnn.ERR_NULL
     assert _conv(bnn, out=MISALIGNED) == bnn.ERR_ALIGN
@@ -127,11 +132,12 @@ def test_workspace_queries(bnn):
 
 
 def test_last_path_starts_unset(bnn):
-    assert bnn.lib.bnn_last_path() in (0, bnn.PATH_XOR, bnn.PATH_MFMA)
+    assert bnn.lib.bnn_last_path() in (0, bnn.PATH_XOR, bnn.PATH_MFMA, bnn.PATH_MFMA_FP4)
 
 
 def test_auto_path_choices(bnn):
     assert bnn.gemm_auto_path(64, 256, 512) in (bnn.PATH_XOR, bnn.PATH_MFMA)
     for m, n, k in [(2048, 4096, 4096), (16384, 8192, 8192)]:
-        assert bnn.gemm_auto_path(m, n, k) == bnn.PATH_MFMA
-    assert bnn.conv2d_auto_path(1, 32, 20, 20, 8, 9, 1, 4, 1) == bnn.PATH_MFMA   # 81 taps
+        assert bnn.gemm_auto_path(m, n, k) == bnn.PATH_MFMA_FP4
+    assert bnn.gemm_auto_path(64, 64, (1 << 24) + 32) == bnn.PATH_MFMA            # fp4 sums inexact
+    assert bnn.conv2d_auto_path(1, 32, 20, 20, 8, 9, 1, 4, 1) == bnn.PATH_MFMA_FP4   # 81 taps

@@ -18,7 +18,8 @@ import synth
 pytestmark = pytest.mark.gpu
 
 DEV = torch.device("cuda:0")
-PATHS = ["xor", "mfma", "auto"]
+PATHS = ["xor", "mfma", "mfma_fp4", "auto"]
+EXPLICIT = ["xor", "mfma", "mfma_fp4"]
 
 
 @pytest.fixture(scope="module")
@@ -161,7 +162,7 @@ def test_large_linear_sampled(bnn, orc):
     y_s = orc.scale(acc_s, sa, sw)
     xd, wp = x.to(DEV), bnn.w_pack(w.to(DEV))
     del w
-    for path in ("mfma", "xor"):
+    for path in ("mfma_fp4", "mfma", "xor"):
         _say(f"large linear path={path}")
         got = bnn.gemm(xd, wp, sa, sw, path=path, out_dtype=torch.int32)
         torch.cuda.synchronize()
@@ -171,7 +172,7 @@ def test_large_linear_sampled(bnn, orc):
         out = bnn.gemm(xd, wp, sa, sw, path=path, out_dtype=torch.float32)
         check_scaled(out[rows], acc_s, y_s, f"large linear {path}")
         del out
-    assert bnn.gemm_auto_path(wl.m, wl.n, wl.k) == bnn.PATH_MFMA
+    assert bnn.gemm_auto_path(wl.m, wl.n, wl.k) == bnn.PATH_MFMA_FP4
 
 
 # ----------------------------------------------------------------------------- sweeps and edges
@@ -213,13 +214,13 @@ def test_edge_values_in_both_operands(bnn, orc):
         w = synth.inject_edges(torch.randn((45, 320), generator=g).to(tdt), 2, 2000)
         acc = orc.linear_acc(x, w)
         wp = bnn.w_pack(w.to(DEV))
-        for path in ("xor", "mfma"):
+        for path in EXPLICIT:
             assert torch.equal(bnn.gemm(x.to(DEV), wp, 1.0, 1.0, path=path, out_dtype=torch.int32).cpu(), acc)
         xc = synth.inject_edges(torch.randn((2, 64, 6, 5), generator=g).to(tdt), 3, 300)
         wc = synth.inject_edges(torch.randn((9, 64, 3, 3), generator=g).to(tdt), 4, 300)
         accc = orc.conv2d_acc(xc, wc, 1, 1, 1)
         wpc = bnn.w_pack(wc.to(DEV))
-        for path in ("xor", "mfma"):
+        for path in EXPLICIT:
             got = bnn.conv2d(xc.to(DEV), wpc, 1.0, 1.0, 3, 1, 1, 1, path=path, out_dtype=torch.int32)
             assert torch.equal(got.cpu(), accc)
 
@@ -230,7 +231,7 @@ def test_closed_form_padding_map(bnn, orc):
         x = torch.ones((2, 64, h, h), device=DEV)
         wp = bnn.w_pack(torch.ones((8, 64, 3, 3), device=DEV))
         kv = orc.conv2d_kvalid(64, h, h, 3, s, p, d)
-        for path in ("xor", "mfma"):
+        for path in EXPLICIT:
             got = bnn.conv2d(x, wp, 1.0, 1.0, 3, s, p, d, path=path, out_dtype=torch.int32).cpu()
             assert torch.equal(got, kv.expand_as(got)), (h, s, p, d, path)
             neg = bnn.conv2d(x, bnn.w_pack(-torch.ones((8, 64, 3, 3), device=DEV)), 1.0, 1.0, 3, s, p,
@@ -244,9 +245,11 @@ def test_determinism_and_paths_agree(bnn):
     wp = bnn.w_pack(torch.randn((777, 1024), generator=g).half().to(DEV))
     a = bnn.gemm(x, wp, 1.0, 1.0, path="xor", out_dtype=torch.int32)
     b = bnn.gemm(x, wp, 1.0, 1.0, path="mfma", out_dtype=torch.int32)
-    assert torch.equal(a, b)
+    c = bnn.gemm(x, wp, 1.0, 1.0, path="mfma_fp4", out_dtype=torch.int32)
+    assert torch.equal(a, b) and torch.equal(a, c)
     for _ in range(3):
         assert torch.equal(bnn.gemm(x, wp, 1.0, 1.0, path="mfma", out_dtype=torch.int32), b)
+        assert torch.equal(bnn.gemm(x, wp, 1.0, 1.0, path="mfma_fp4", out_dtype=torch.int32), c)
         assert torch.equal(bnn.gemm(x, wp, 1.0, 1.0, path="xor", out_dtype=torch.int32), a)
 
 
@@ -257,6 +260,8 @@ def test_last_path_and_errors_on_device(bnn):
     assert bnn.last_path() == bnn.PATH_MFMA
     bnn.gemm(x, wp, 1.0, 1.0, path="xor")
     assert bnn.last_path() == bnn.PATH_XOR
+    bnn.gemm(x, wp, 1.0, 1.0, path="mfma_fp4")
+    assert bnn.last_path() == bnn.PATH_MFMA_FP4
     # a too-small workspace is rejected and the output is left untouched
     out = torch.full((64, 32), 7.0, device=DEV)
     ws = torch.empty(16, dtype=torch.uint8, device=DEV)
@@ -282,7 +287,7 @@ def test_graph_replay_matches_eager(bnn):
     wp = bnn.w_pack(torch.randn((520, 1024), generator=g).half().to(DEV))
     xc = torch.randn((2, 64, 11, 13), generator=g).to(DEV)
     wpc = bnn.w_pack(torch.randn((48, 64, 3, 3), generator=g).to(DEV))
-    for path in ("xor", "mfma"):
+    for path in EXPLICIT:
         eager = bnn.gemm(x, wp, 0.3, 0.7, path=path)
         eager_c = bnn.conv2d(xc, wpc, 0.3, 0.7, 3, 2, 1, 1, path=path)
         xp = torch.empty((700, 32), dtype=torch.int32, device=DEV)
