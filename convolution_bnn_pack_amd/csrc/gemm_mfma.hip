@@ -362,10 +362,11 @@ __global__ __launch_bounds__(T::THREADS) void mfma_kernel(Contraction p) {
         acc[fn][fm] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fw[kk & 1][fn], fa[kk & 1][fm],
                                                              acc[fn][fm], 0, 0, 0);
       }
-      // the next k-step's RPK fragment reads are spread over this k-step's MPK slots
-      if (kk + 1 < T::KSTEPS) {
+      // the next k-step's RPK fragment reads all go out in its first slot, a whole k-step
+      // of MFMAs ahead of their use
+      if (kk + 1 < T::KSTEPS && j == 0) {
 #pragma unroll
-        for (int f = j * RPK / MPK; f < (j + 1) * RPK / MPK; f++) read_frag(cur, kk + 1, f);
+        for (int f = 0; f < RPK; f++) read_frag(cur, kk + 1, f);
       }
 #pragma unroll
       for (int u = i * NU / NM; u < (i + 1) * NU / NM; u++) expand_unit(nxt, u);
@@ -557,12 +558,18 @@ int64_t count_tiles(const Contraction& p, int bm, int bn) {
 #ifndef BNN_MFMA_MIN_TILES
 #define BNN_MFMA_MIN_TILES 256
 #endif
+#ifndef BNN_MFMA_MIN_TILES_CONV
+#define BNN_MFMA_MIN_TILES_CONV 128
+#endif
 template <bool CONV, bool F4>
 hipError_t launch_mfma_t(const Contraction& p, int out_dtype, hipStream_t stream) {
   constexpr int64_t kMinTiles = BNN_MFMA_MIN_TILES;  // one workgroup per compute unit
   using TS = Tiles<F4, CONV>;
   if (count_tiles(p, 256, 256) >= kMinTiles) return launch_tile<typename TS::L, CONV>(p, out_dtype, stream);
-  if (count_tiles(p, 128, 256) >= kMinTiles) return launch_tile<typename TS::M, CONV>(p, out_dtype, stream);
+  // conv outputs are written per element, so half a round of large tiles still beats two
+  // rounds of small ones
+  if (count_tiles(p, 128, 256) >= (CONV ? BNN_MFMA_MIN_TILES_CONV : kMinTiles))
+    return launch_tile<typename TS::M, CONV>(p, out_dtype, stream);
   return launch_tile<typename TS::S, CONV>(p, out_dtype, stream);
 }
 
