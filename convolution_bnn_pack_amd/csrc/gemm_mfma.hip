@@ -513,13 +513,15 @@ hipError_t launch_tile_v(const Contraction& p, int out_dtype, hipStream_t stream
 // Vector loads need each thread's words of a stage to be contiguous, aligned and, for
 // conv, within one tap: the per-thread word counts divide K/32 (linear) or C/32 and the
 // weight row length (conv), and both operand bases are 16-byte aligned.
-template <class T, bool CONV>
+// TS: the tile used when vector loads are impossible (the fp4 256 x 256 tile would spill
+// with the scalar loader's extra state).
+template <class T, bool CONV, class TS = T>
 hipError_t launch_tile(const Contraction& p, int out_dtype, hipStream_t stream) {
   const bool aligned = (reinterpret_cast<uintptr_t>(p.a) % 16) == 0 &&
                        (reinterpret_cast<uintptr_t>(p.w) % 16) == 0;
   const bool vec = aligned && (CONV ? p.CW : p.KW) % T::A_WPT == 0 && p.KW % T::W_WPT == 0;
   return vec ? launch_tile_v<T, CONV, true>(p, out_dtype, stream)
-             : launch_tile_v<T, CONV, false>(p, out_dtype, stream);
+             : launch_tile_v<TS, CONV, false>(p, out_dtype, stream);
 }
 
 #ifndef BNN_MFMA_PD_L
@@ -548,6 +550,10 @@ struct Tiles {
   using M = Tile<128, 256, KS, PD_M, 2, BNN_MFMA_WAVES_N, F4>;
   using L = std::conditional_t<F4 && CONV, M, Tile<256, 256, KS, BNN_MFMA_PD_L, 2, BNN_MFMA_WAVES_N, F4>>;
   using S = Tile<128, 128, KS, PD_M, 2, BNN_MFMA_WAVES_N, F4>;
+  // at most 64 output features (64-channel convs): 256 x 64 tiles, 4 x 2 waves, instead of
+  // leaving three quarters of a 256-wide tile's W rows empty (fp4 only: an int8 stage of
+  // 4 words has too few W words for 512 loader threads)
+  using N64 = std::conditional_t<F4, Tile<256, 64, KS, PD_M, 4, 2, F4>, S>;
 };
 
 int64_t count_tiles(const Contraction& p, int bm, int bn) {
@@ -565,7 +571,11 @@ template <bool CONV, bool F4>
 hipError_t launch_mfma_t(const Contraction& p, int out_dtype, hipStream_t stream) {
   constexpr int64_t kMinTiles = BNN_MFMA_MIN_TILES;  // one workgroup per compute unit
   using TS = Tiles<F4, CONV>;
-  if (count_tiles(p, 256, 256) >= kMinTiles) return launch_tile<typename TS::L, CONV>(p, out_dtype, stream);
+  if (F4 && p.N <= 64 && count_tiles(p, 256, 64) >= kMinTiles)
+    return launch_tile<typename TS::N64, CONV>(p, out_dtype, stream);
+  if (count_tiles(p, 256, 256) >= kMinTiles)
+    return launch_tile<typename TS::L, CONV, std::conditional_t<F4, typename TS::M, typename TS::L>>(
+        p, out_dtype, stream);
   // conv outputs are written per element, so half a round of large tiles still beats two
   // rounds of small ones
   if (count_tiles(p, 128, 256) >= (CONV ? BNN_MFMA_MIN_TILES_CONV : kMinTiles))

@@ -71,7 +71,8 @@ typedef enum {
 
 /* Kernel choice; mirrors the layers' bmm_type argument (BMM.ADAPTIVE is the default there). */
 typedef enum {
-  BNN_PATH_AUTO = 0,     /* pick per shape */
+  BNN_PATH_AUTO = 0,     /* BNN_PATH_MFMA_FP4 when its sums are exact (K <= 2^24), else BNN_PATH_MFMA
+                            (measured fastest at every tested shape, small layers included) */
   BNN_PATH_XOR = 1,      /* XOR + popcount on the vector ALUs */
   BNN_PATH_MFMA = 2,     /* signs expanded to int8 +-1, contracted on the matrix cores (int32 sums) */
   BNN_PATH_MFMA_FP4 = 3  /* signs expanded to fp4 (e2m1) +-1.0, contracted on the matrix cores
@@ -132,7 +133,8 @@ bnn_status bnn_conv2d(const void* x, int x_dtype, int64_t n, int64_t c, int64_t 
 size_t bnn_gemm_workspace_bytes(int64_t m, int64_t k, int x_dtype);
 size_t bnn_conv2d_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w, int x_dtype);
 
-/* The path that bnn_gemm / bnn_conv2d would take for a shape under BNN_PATH_AUTO. */
+/* The path that bnn_gemm / bnn_conv2d would take for a shape under BNN_PATH_AUTO (it depends only on
+ * the reduction length K = k, or kernel_size^2 * c). */
 int bnn_gemm_auto_path(int64_t m, int64_t n, int64_t k);
 int bnn_conv2d_auto_path(int64_t n, int64_t c, int64_t h, int64_t w, int64_t out_channels,
                          int kernel_size, int stride, int padding, int dilation);

@@ -136,8 +136,8 @@ def test_last_path_starts_unset(bnn):
 
 
 def test_auto_path_choices(bnn):
-    assert bnn.gemm_auto_path(64, 256, 512) in (bnn.PATH_XOR, bnn.PATH_MFMA)
-    for m, n, k in [(2048, 4096, 4096), (16384, 8192, 8192)]:
+    for m, n, k in [(64, 256, 512), (2048, 4096, 4096), (16384, 8192, 8192), (1, 1, 1 << 24)]:
         assert bnn.gemm_auto_path(m, n, k) == bnn.PATH_MFMA_FP4
     assert bnn.gemm_auto_path(64, 64, (1 << 24) + 32) == bnn.PATH_MFMA            # fp4 sums inexact
     assert bnn.conv2d_auto_path(1, 32, 20, 20, 8, 9, 1, 4, 1) == bnn.PATH_MFMA_FP4   # 81 taps
+    assert bnn.conv2d_auto_path(1, 1 << 21, 4, 4, 8, 3, 1, 1, 1) == bnn.PATH_MFMA     # K = 9 * 2^21 > 2^24
