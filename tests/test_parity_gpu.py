@@ -175,6 +175,39 @@ def test_large_linear_sampled(bnn, orc):
     assert bnn.gemm_auto_path(wl.m, wl.n, wl.k) == bnn.PATH_MFMA_FP4
 
 
+def test_tile_variants_sampled(bnn, orc):
+    """Shapes that select the matrix-core kernel's less common tiles, checked on sampled rows /
+    images against the oracle: the 256 x 64 fp4 tile (at most 64 output features and a full
+    round of such tiles), and the fp4 fallback from 256 x 256 to 128 x 256 tiles when K/32 is
+    not a multiple of 4 (no vector loads)."""
+    g = torch.Generator().manual_seed(61)
+    cases = [(65600, 40, 288), (66000, 64, 1024), (4096, 4096, 4128)]
+    for m, n, k in cases:
+        x = torch.randn((m, k), generator=g).half()
+        w = torch.randn((n, k), generator=g).half()
+        rows = [0, 1, 255, 256, m // 2, m - 2, m - 1]
+        acc = orc.linear_acc(x, w, rows=rows)
+        xd, wp = x.to(DEV), bnn.w_pack(w.to(DEV))
+        for path in ("mfma_fp4", "mfma"):
+            _say(f"tile variant linear {m}x{n}x{k} path={path}")
+            got = bnn.gemm(xd, wp, 1.0, 1.0, path=path, out_dtype=torch.int32)
+            torch.cuda.synchronize()
+            assert torch.equal(got[rows].cpu(), acc), (m, n, k, path)
+            assert bool(((got - k) % 2 == 0).all()) and bool((got.abs() <= k).all())
+            del got
+    # 64-channel 3x3 conv on 56x56 with 24 images: 75264 output pixels, 64 output channels
+    xc = torch.randn((24, 64, 56, 56), generator=g).half()
+    wc = torch.randn((64, 64, 3, 3), generator=g).half()
+    images = [0, 11, 23]
+    acc = orc.conv2d_acc(xc, wc, 1, 1, 1, images=images)
+    xcd, wpc = xc.to(DEV), bnn.w_pack(wc.to(DEV))
+    for path in ("mfma_fp4", "mfma", "xor"):
+        _say(f"tile variant conv 24x64x56x56 path={path}")
+        got = bnn.conv2d(xcd, wpc, 1.0, 1.0, 3, 1, 1, 1, path=path, out_dtype=torch.int32)
+        torch.cuda.synchronize()
+        assert torch.equal(got[images].cpu(), acc), path
+
+
 # ----------------------------------------------------------------------------- sweeps and edges
 
 def test_random_linear_sweep(bnn, orc):
