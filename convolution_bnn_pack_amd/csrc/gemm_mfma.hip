@@ -223,6 +223,106 @@ __device__ __forceinline__ v4i lds_frag(const uint8_t* buf, int r, int c) {
   return *reinterpret_cast<const v4i*>(buf + r * T::ROWB + 16 * swz<T>(r, c));
 }
 
+// Epilogue shared by the matrix-core kernels: acc[fn][fm][e] is output (row m, feature n)
+// with
+//   m = m0 + wm*WTM + fm*32 + (lane & 31)
+//   n = n0 + wn*WTN + fn*32 + 8*(e/4) + 4*(lane/32) + e%4
+// and the binary dot product is rowk[m - m0] + 2 * acc. Called by the WGM x WGN waves that
+// hold accumulators (waves 0 .. WGM*WGN-1); the LDS buffers are free by then and serve as
+// staging space.
+template <class T, int OUT, bool CONV, class Acc>
+__device__ __forceinline__ void store_tile(const Contraction& p, const Acc (&acc)[T::FN][T::FM],
+                                           const int* rowk, uint8_t* lds0, uint8_t* lds1, int m0,
+                                           int n0, int wm, int wn) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int fr = lane & 31, half = lane >> 5;
+  auto acc_int = [&](int fn, int fm, int e) -> int { return (int)acc[fn][fm][e]; };
+  if constexpr (CONV) {
+    // NCHW: for a fixed feature the 32 lanes of a half-wave hold 32 consecutive pixels,
+    // so each store instruction writes lane-contiguous runs.
+    const int hw = p.Ho * p.Wo;
+#pragma unroll
+    for (int fm = 0; fm < T::FM; fm++) {
+      const int ml = wm * T::WTM + fm * 32 + fr;
+      const int m = m0 + ml;
+      if (m >= p.M) continue;
+      const int base_k = rowk[ml];
+      const int b = m / hw, pix = m - b * hw;
+#pragma unroll
+      for (int fn = 0; fn < T::FN; fn++)
+#pragma unroll
+        for (int e = 0; e < 16; e++) {
+          const int n = n0 + wn * T::WTN + fn * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
+          if (n < p.N)
+            store1<OUT>(p.out, ((int64_t)b * p.N + n) * hw + pix, base_k + 2 * acc_int(fn, fm, e), p.alpha);
+        }
+    }
+  } else {
+    // Row-major [M][N]: each lane's values are four features of one row, 32 rows per
+    // half-wave, so storing them directly would scatter 8..16-byte pieces over 32 rows.
+    // Instead each wave stages one 32-row band of its sub-tile in LDS (free after the
+    // main loop; two waves' bands per buffer) and writes it back as whole contiguous row
+    // segments, 16 bytes per lane.
+    using O = OutType<OUT>;
+    constexpr int WN = T::WTN;                          // columns of a wave's sub-tile
+    constexpr int ROWS_B = WN * (int)sizeof(typename O::type) + 16;  // padded LDS row
+    constexpr int NWAVES = T::WGM * T::WGN, HALFW = NWAVES / 2;
+    static_assert(HALFW * 32 * ROWS_B <= T::BUF, "staging bands fit in the two LDS buffers");
+    uint8_t* band = (wave < HALFW ? lds0 : lds1) + (wave % HALFW) * 32 * ROWS_B;
+    constexpr int EPV = 16 / (int)sizeof(typename O::type);  // elements per 16-byte vector
+    constexpr int VPR = WN / EPV;                            // vectors per band row
+#pragma unroll
+    for (int fm = 0; fm < T::FM; fm++) {
+      const int base_k = rowk[wm * T::WTM + fm * 32 + fr];
+      uint8_t* myrow = band + fr * ROWS_B;
+#pragma unroll
+      for (int fn = 0; fn < T::FN; fn++)
+#pragma unroll
+        for (int g = 0; g < 4; g++) {
+          const int c = fn * 32 + 8 * g + 4 * half;
+          O::put4(myrow + c * (int)sizeof(typename O::type), base_k + 2 * acc_int(fn, fm, 4 * g),
+                  base_k + 2 * acc_int(fn, fm, 4 * g + 1), base_k + 2 * acc_int(fn, fm, 4 * g + 2),
+                  base_k + 2 * acc_int(fn, fm, 4 * g + 3), p.alpha);
+        }
+      // the band is private to this wave and a wave's LDS accesses complete in order, so
+      // no fence is needed (a memory fence here would also wait for the global stores)
+      __builtin_amdgcn_wave_barrier();
+      const int mrow0 = m0 + wm * T::WTM + fm * 32;
+      const int ncol0 = n0 + wn * WN;
+      constexpr int NV = 32 * VPR / 64;  // 16-byte vectors per lane for the band
+      static_assert(NV >= 1 && (32 * VPR) % 64 == 0, "band splits evenly over the lanes");
+      uint4 vals[NV];
+#pragma unroll
+      for (int t = 0; t < NV; t++) {
+        const int v = lane + 64 * t;
+        const int r = v / VPR, cv = v - r * VPR;
+        vals[t] = *reinterpret_cast<const uint4*>(band + r * ROWS_B + cv * 16);
+      }
+      const bool full_rows = (p.N % EPV) == 0;
+#pragma unroll
+      for (int t = 0; t < NV; t++) {
+        const int v = lane + 64 * t;
+        const int r = v / VPR, cv = v - r * VPR;
+        const int m = mrow0 + r, n = ncol0 + cv * EPV;
+        if (m >= p.M) continue;
+        typename O::type* dst = reinterpret_cast<typename O::type*>(p.out) + (int64_t)m * p.N + n;
+        if (full_rows && n + EPV <= p.N) {
+          *reinterpret_cast<uint4*>(dst) = vals[t];
+        } else {
+          const typename O::type* src = reinterpret_cast<const typename O::type*>(&vals[t]);
+#pragma unroll
+          for (int j = 0; j < EPV; j++)
+            if (n + j < p.N) dst[j] = src[j];
+        }
+      }
+      // the band is private to this wave and a wave's LDS accesses complete in order, so
+      // no fence is needed (a memory fence here would also wait for the global stores)
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+}
+
 template <class T, int OUT, bool CONV, bool VEC>
 __global__ __launch_bounds__(T::THREADS) void mfma_kernel(Contraction p) {
   // two distinct arrays (not one array indexed by stage parity) so the compiler can
@@ -317,7 +417,6 @@ __global__ __launch_bounds__(T::THREADS) void mfma_kernel(Contraction p) {
     for (int j = 0; j < T::FM; j++)
 #pragma unroll
       for (int e = 0; e < 16; e++) acc[i][j][e] = 0;
-  auto acc_int = [&](int fn, int fm, int e) -> int { return (int)acc[fn][fm][e]; };
 
   const int fr = lane & 31, half = lane >> 5;
   v4i fa[2][T::FM], fw[2][T::FN];
@@ -408,93 +507,7 @@ __global__ __launch_bounds__(T::THREADS) void mfma_kernel(Contraction p) {
   atomicAdd(&rowk[a_row], rowk_part);
   __syncthreads();
 
-  // epilogue: acc[fn][fm][e] is output (row m, feature n) with
-  //   m = m0 + wm*WTM + fm*32 + (lane & 31)
-  //   n = n0 + wn*WTN + fn*32 + 8*(e/4) + 4*(lane/32) + e%4
-  // and the binary dot product is rowk[m - m0] + 2 * acc.
-  if constexpr (CONV) {
-    // NCHW: for a fixed feature the 32 lanes of a half-wave hold 32 consecutive pixels,
-    // so each store instruction writes lane-contiguous runs.
-    const int hw = p.Ho * p.Wo;
-#pragma unroll
-    for (int fm = 0; fm < T::FM; fm++) {
-      const int ml = wm * T::WTM + fm * 32 + fr;
-      const int m = m0 + ml;
-      if (m >= p.M) continue;
-      const int base_k = rowk[ml];
-      const int b = m / hw, pix = m - b * hw;
-#pragma unroll
-      for (int fn = 0; fn < T::FN; fn++)
-#pragma unroll
-        for (int e = 0; e < 16; e++) {
-          const int n = n0 + wn * T::WTN + fn * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
-          if (n < p.N)
-            store1<OUT>(p.out, ((int64_t)b * p.N + n) * hw + pix, base_k + 2 * acc_int(fn, fm, e), p.alpha);
-        }
-    }
-  } else {
-    // Row-major [M][N]: each lane's values are four features of one row, 32 rows per
-    // half-wave, so storing them directly would scatter 8..16-byte pieces over 32 rows.
-    // Instead each wave stages one 32-row band of its sub-tile in LDS (free after the
-    // main loop; two waves' bands per buffer) and writes it back as whole contiguous row
-    // segments, 16 bytes per lane.
-    using O = OutType<OUT>;
-    constexpr int WN = T::WTN;                          // columns of a wave's sub-tile
-    constexpr int ROWS_B = WN * (int)sizeof(typename O::type) + 16;  // padded LDS row
-    constexpr int NWAVES = T::WGM * T::WGN, HALFW = NWAVES / 2;
-    static_assert(HALFW * 32 * ROWS_B <= T::BUF, "staging bands fit in the two LDS buffers");
-    uint8_t* band = (wave < HALFW ? lds0 : lds1) + (wave % HALFW) * 32 * ROWS_B;
-    constexpr int EPV = 16 / (int)sizeof(typename O::type);  // elements per 16-byte vector
-    constexpr int VPR = WN / EPV;                            // vectors per band row
-#pragma unroll
-    for (int fm = 0; fm < T::FM; fm++) {
-      const int base_k = rowk[wm * T::WTM + fm * 32 + fr];
-      uint8_t* myrow = band + fr * ROWS_B;
-#pragma unroll
-      for (int fn = 0; fn < T::FN; fn++)
-#pragma unroll
-        for (int g = 0; g < 4; g++) {
-          const int c = fn * 32 + 8 * g + 4 * half;
-          O::put4(myrow + c * (int)sizeof(typename O::type), base_k + 2 * acc_int(fn, fm, 4 * g),
-                  base_k + 2 * acc_int(fn, fm, 4 * g + 1), base_k + 2 * acc_int(fn, fm, 4 * g + 2),
-                  base_k + 2 * acc_int(fn, fm, 4 * g + 3), p.alpha);
-        }
-      // the band is private to this wave and a wave's LDS accesses complete in order, so
-      // no fence is needed (a memory fence here would also wait for the global stores)
-      __builtin_amdgcn_wave_barrier();
-      const int mrow0 = m0 + wm * T::WTM + fm * 32;
-      const int ncol0 = n0 + wn * WN;
-      constexpr int NV = 32 * VPR / 64;  // 16-byte vectors per lane for the band
-      static_assert(NV >= 1 && (32 * VPR) % 64 == 0, "band splits evenly over the lanes");
-      uint4 vals[NV];
-#pragma unroll
-      for (int t = 0; t < NV; t++) {
-        const int v = lane + 64 * t;
-        const int r = v / VPR, cv = v - r * VPR;
-        vals[t] = *reinterpret_cast<const uint4*>(band + r * ROWS_B + cv * 16);
-      }
-      const bool full_rows = (p.N % EPV) == 0;
-#pragma unroll
-      for (int t = 0; t < NV; t++) {
-        const int v = lane + 64 * t;
-        const int r = v / VPR, cv = v - r * VPR;
-        const int m = mrow0 + r, n = ncol0 + cv * EPV;
-        if (m >= p.M) continue;
-        typename O::type* dst = reinterpret_cast<typename O::type*>(p.out) + (int64_t)m * p.N + n;
-        if (full_rows && n + EPV <= p.N) {
-          *reinterpret_cast<uint4*>(dst) = vals[t];
-        } else {
-          const typename O::type* src = reinterpret_cast<const typename O::type*>(&vals[t]);
-#pragma unroll
-          for (int j = 0; j < EPV; j++)
-            if (n + j < p.N) dst[j] = src[j];
-        }
-      }
-      // the band is private to this wave and a wave's LDS accesses complete in order, so
-      // no fence is needed (a memory fence here would also wait for the global stores)
-      __builtin_amdgcn_wave_barrier();
-    }
-  }
+  store_tile<T, OUT, CONV>(p, acc, rowk, lds0, lds1, m0, n0, wm, wn);
 }
 
 template <class T, bool CONV, bool VEC>
