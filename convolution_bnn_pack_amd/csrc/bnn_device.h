@@ -58,6 +58,14 @@ __device__ __forceinline__ uint32_t elem_pos(const void* base, int64_t i) {
     return pos_bf16(reinterpret_cast<const uint16_t*>(base)[i]);
 }
 
+// Non-temporal 16-byte store, for output written once in whole 128-byte row segments:
+// streaming such lines past the caches shortens the write-out at the end of a
+// contraction (the whole output leaves at once). Scattered element stores (NCHW runs,
+// ragged tails) stay ordinary stores, which the L2 merges into lines.
+__device__ __forceinline__ void st_nt(void* p, u32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+
 // One scaled output element: (float)acc * alpha rounded to the output type
 // (round to nearest even), or the raw accumulator for kI32.
 template <int OUT>

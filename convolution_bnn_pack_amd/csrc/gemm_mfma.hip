@@ -308,7 +308,7 @@ __device__ __forceinline__ void store_tile(const Contraction& p, const Acc (&acc
         if (m >= p.M) continue;
         typename O::type* dst = reinterpret_cast<typename O::type*>(p.out) + (int64_t)m * p.N + n;
         if (full_rows && n + EPV <= p.N) {
-          *reinterpret_cast<uint4*>(dst) = vals[t];
+          st_nt(dst, u32x4{vals[t].x, vals[t].y, vals[t].z, vals[t].w});
         } else {
           const typename O::type* src = reinterpret_cast<const typename O::type*>(&vals[t]);
 #pragma unroll
