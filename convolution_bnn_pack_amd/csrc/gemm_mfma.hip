@@ -40,10 +40,11 @@
 // through two LDS buffers (one barrier per stage): while the waves run the
 // MFMAs of stage s from one buffer, they expand stage s+1 into the other and
 // fetch stage s+PD from global memory (PD register sets of raw words). Each
-// wave holds a (BM/2) x (BN/WGN) sub-tile of 32 x 32 MFMA blocks; the MFMA computes
-// D = W_tile * A_tile^T so each lane's four consecutive accumulators are four
-// consecutive output features of one row (vector stores for linear outputs,
-// lane-contiguous runs for NCHW conv outputs). LDS rows are 128 bytes; the
+// wave holds a (BM/2) x (BN/WGN) sub-tile of 32 x 32 MFMA blocks. For linear tiles
+// the MFMA computes D = W_tile * A_tile^T, so each lane's four consecutive
+// accumulators are four consecutive output features of one row (row segments staged
+// through LDS, then 16-byte stores); for conv tiles D = A_tile * W_tile^T, four
+// consecutive pixels of one feature, contiguous in the NCHW output. LDS rows are 128 bytes; the
 // 16-byte chunks of a row are XOR-swizzled with a Gray code of the row index
 // so the ds_read_b128 / ds_write_b128 of 8 or 16 consecutive rows hit
 // distinct banks. Tiles are numbered so that each XCD (workgroups go
@@ -223,11 +224,12 @@ __device__ __forceinline__ v4i lds_frag(const uint8_t* buf, int r, int c) {
   return *reinterpret_cast<const v4i*>(buf + r * T::ROWB + 16 * swz<T>(r, c));
 }
 
-// Epilogue shared by the matrix-core kernels: acc[fn][fm][e] is output (row m, feature n)
-// with
+// Epilogue of the matrix-core kernel. For linear tiles acc[fn][fm][e] is output (row m,
+// feature n) with
 //   m = m0 + wm*WTM + fm*32 + (lane & 31)
 //   n = n0 + wn*WTN + fn*32 + 8*(e/4) + 4*(lane/32) + e%4
-// and the binary dot product is rowk[m - m0] + 2 * acc. Called by the WGM x WGN waves that
+// (conv tiles swap the roles of lane and e, see below), and the binary dot product is
+// rowk[m - m0] + 2 * acc. Called by the WGM x WGN waves that
 // hold accumulators (waves 0 .. WGM*WGN-1); the LDS buffers are free by then and serve as
 // staging space.
 template <class T, int OUT, bool CONV, class Acc>
@@ -239,23 +241,40 @@ __device__ __forceinline__ void store_tile(const Contraction& p, const Acc (&acc
   const int fr = lane & 31, half = lane >> 5;
   auto acc_int = [&](int fn, int fm, int e) -> int { return (int)acc[fn][fm][e]; };
   if constexpr (CONV) {
-    // NCHW: for a fixed feature the 32 lanes of a half-wave hold 32 consecutive pixels,
-    // so each store instruction writes lane-contiguous runs.
+    // NCHW. Conv tiles compute D = A * W^T, so lane (fr, half) holds feature
+    // n = n0 + wn*WTN + fn*32 + fr and, in e = 4g .. 4g+3, the four consecutive pixels
+    // m = m0 + wm*WTM + fm*32 + 8g + 4*half + 0..3: one 8- or 16-byte store each when the
+    // output plane size is a multiple of 4 (the four pixels then share an image and the
+    // address is aligned), element stores otherwise.
     const int hw = p.Ho * p.Wo;
+    const bool quad = (hw & 3) == 0;
 #pragma unroll
-    for (int fm = 0; fm < T::FM; fm++) {
-      const int ml = wm * T::WTM + fm * 32 + fr;
-      const int m = m0 + ml;
-      if (m >= p.M) continue;
-      const int base_k = rowk[ml];
-      const int b = m / hw, pix = m - b * hw;
+    for (int fn = 0; fn < T::FN; fn++) {
+      const int n = n0 + wn * T::WTN + fn * 32 + fr;
+      if (n >= p.N) continue;
 #pragma unroll
-      for (int fn = 0; fn < T::FN; fn++)
+      for (int fm = 0; fm < T::FM; fm++)
 #pragma unroll
-        for (int e = 0; e < 16; e++) {
-          const int n = n0 + wn * T::WTN + fn * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
-          if (n < p.N)
-            store1<OUT>(p.out, ((int64_t)b * p.N + n) * hw + pix, base_k + 2 * acc_int(fn, fm, e), p.alpha);
+        for (int g = 0; g < 4; g++) {
+          const int ml = wm * T::WTM + fm * 32 + 8 * g + 4 * half;
+          const int m = m0 + ml;
+          if (m >= p.M) continue;
+          const int4 bk = *reinterpret_cast<const int4*>(rowk + ml);
+          const int v0 = bk.x + 2 * acc_int(fn, fm, 4 * g), v1 = bk.y + 2 * acc_int(fn, fm, 4 * g + 1);
+          const int v2 = bk.z + 2 * acc_int(fn, fm, 4 * g + 2), v3 = bk.w + 2 * acc_int(fn, fm, 4 * g + 3);
+          const int b = m / hw, pix = m - b * hw;
+          if (quad) {
+            store4<OUT>(p.out, ((int64_t)b * p.N + n) * hw + pix, v0, v1, v2, v3, p.alpha);
+          } else {
+            const int vals[4] = {v0, v1, v2, v3};
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+              const int mi = m + i;
+              if (mi >= p.M) break;
+              const int bi = mi / hw, pi = mi - bi * hw;
+              store1<OUT>(p.out, ((int64_t)bi * p.N + n) * hw + pi, vals[i], p.alpha);
+            }
+          }
         }
     }
   } else {
@@ -329,7 +348,7 @@ __global__ __launch_bounds__(T::THREADS) void mfma_kernel(Contraction p) {
   // tell the expansion's writes from the fragment reads
   __shared__ __attribute__((aligned(16))) uint8_t lds0[T::BUF];
   __shared__ __attribute__((aligned(16))) uint8_t lds1[T::BUF];
-  __shared__ int rowk[T::BM];  // K_valid - 2 * popA per A row of the tile
+  __shared__ __attribute__((aligned(16))) int rowk[T::BM];  // K_valid - 2 * popA per A row of the tile
 
   constexpr int MPK = T::FN * T::FM;            // MFMAs per k-step
   constexpr int NM = MPK * T::KSTEPS;           // MFMAs per stage
@@ -455,11 +474,21 @@ __global__ __launch_bounds__(T::THREADS) void mfma_kernel(Contraction p) {
         const v4i w4 = fw[kk & 1][fn], a4 = fa[kk & 1][fm];
         const v8i w8 = {w4[0], w4[1], w4[2], w4[3], 0, 0, 0, 0};
         const v8i a8 = {a4[0], a4[1], a4[2], a4[3], 0, 0, 0, 0};
-        acc[fn][fm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            w8, a8, acc[fn][fm], kFmtFp4, kFmtFp4, 0, kScaleOne, 0, kScaleOne);
+        // linear: D = W * A^T (a lane holds four features of one row); conv: D = A * W^T (a
+        // lane holds four pixels of one feature, contiguous in NCHW)
+        if constexpr (CONV)
+          acc[fn][fm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              a8, w8, acc[fn][fm], kFmtFp4, kFmtFp4, 0, kScaleOne, 0, kScaleOne);
+        else
+          acc[fn][fm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              w8, a8, acc[fn][fm], kFmtFp4, kFmtFp4, 0, kScaleOne, 0, kScaleOne);
       } else {
-        acc[fn][fm] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fw[kk & 1][fn], fa[kk & 1][fm],
-                                                             acc[fn][fm], 0, 0, 0);
+        if constexpr (CONV)
+          acc[fn][fm] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[kk & 1][fm], fw[kk & 1][fn],
+                                                               acc[fn][fm], 0, 0, 0);
+        else
+          acc[fn][fm] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fw[kk & 1][fn], fa[kk & 1][fm],
+                                                               acc[fn][fm], 0, 0, 0);
       }
       // the next k-step's RPK fragment reads all go out in its first slot, a whole k-step
       // of MFMAs ahead of their use
