@@ -53,6 +53,7 @@
 // Conv is the im2col lowering of the banghao.live blog post, section 2,
 // computed implicitly: A row m is output pixel (b, oh, ow) and reduction word
 // q = tap * CW + cw reads activation word [b][oh*s - p + kh*d][ow*s - p + kw*d][cw].
+#include <atomic>
 #include <type_traits>
 #include <utility>
 
@@ -209,10 +210,11 @@ __device__ __forceinline__ void load_w(const Contraction& p, int n, int q0, uint
   }
 }
 
-// Tile index -> (m-tile, n-tile): contiguous runs of tiles per XCD, n fastest.
-__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
+// Tile slot (the workgroup index, or slot + i * grid for a persistent workgroup) ->
+// (m-tile, n-tile): contiguous runs of tiles per XCD (slot % 8), n fastest.
+__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int slot, int& tm, int& tn) {
   const int total = tiles_m * tiles_n;
-  int t = blockIdx.x;
+  int t = slot;
   if ((total & 7) == 0) t = (t & 7) * (total >> 3) + (t >> 3);
   tm = t / tiles_n;
   tn = t - tm * tiles_n;
@@ -229,12 +231,12 @@ __device__ __forceinline__ v4i lds_frag(const uint8_t* buf, int r, int c) {
 //   m = m0 + wm*WTM + fm*32 + (lane & 31)
 //   n = n0 + wn*WTN + fn*32 + 8*(e/4) + 4*(lane/32) + e%4
 // (conv tiles swap the roles of lane and e, see below), and the binary dot product is
-// rowk[m - m0] + 2 * acc. Called by the WGM x WGN waves that
+// rowk(m - m0) + 2 * acc. Called by the WGM x WGN waves that
 // hold accumulators (waves 0 .. WGM*WGN-1); the LDS buffers are free by then and serve as
 // staging space.
-template <class T, int OUT, bool CONV, class Acc>
+template <class T, int OUT, bool CONV, class Acc, class RowK>
 __device__ __forceinline__ void store_tile(const Contraction& p, const Acc (&acc)[T::FN][T::FM],
-                                           const int* rowk, uint8_t* lds0, uint8_t* lds1, int m0,
+                                           RowK rowk, uint8_t* lds0, uint8_t* lds1, int m0,
                                            int n0, int wm, int wn) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -259,7 +261,7 @@ __device__ __forceinline__ void store_tile(const Contraction& p, const Acc (&acc
           const int ml = wm * T::WTM + fm * 32 + 8 * g + 4 * half;
           const int m = m0 + ml;
           if (m >= p.M) continue;
-          const int4 bk = *reinterpret_cast<const int4*>(rowk + ml);
+          const int4 bk = {rowk(ml), rowk(ml + 1), rowk(ml + 2), rowk(ml + 3)};
           const int v0 = bk.x + 2 * acc_int(fn, fm, 4 * g), v1 = bk.y + 2 * acc_int(fn, fm, 4 * g + 1);
           const int v2 = bk.z + 2 * acc_int(fn, fm, 4 * g + 2), v3 = bk.w + 2 * acc_int(fn, fm, 4 * g + 3);
           const int b = m / hw, pix = m - b * hw;
@@ -293,7 +295,7 @@ __device__ __forceinline__ void store_tile(const Contraction& p, const Acc (&acc
     constexpr int VPR = WN / EPV;                            // vectors per band row
 #pragma unroll
     for (int fm = 0; fm < T::FM; fm++) {
-      const int base_k = rowk[wm * T::WTM + fm * 32 + fr];
+      const int base_k = rowk(wm * T::WTM + fm * 32 + fr);
       uint8_t* myrow = band + fr * ROWS_B;
 #pragma unroll
       for (int fn = 0; fn < T::FN; fn++)
@@ -342,13 +344,23 @@ __device__ __forceinline__ void store_tile(const Contraction& p, const Acc (&acc
   }
 }
 
-template <class T, int OUT, bool CONV, bool VEC>
+// PERS (conv): a persistent workgroup takes tiles slot, slot + grid, ... and streams their
+// stages back to back: the loads and expansions run PD stages and one stage ahead across
+// tile boundaries, and a tile's epilogue (direct NCHW stores) follows the barrier of its
+// last stage while the next tile's first stage already sits in LDS. Row bases K_valid -
+// 2*popA are kept per loader thread in LDS slots of two tile parities, so no LDS atomics
+// or clearing are needed between tiles.
+template <class T, int OUT, bool CONV, bool VEC, bool PERS>
 __global__ __launch_bounds__(T::THREADS) void mfma_kernel(Contraction p) {
+  static_assert(!PERS || CONV, "persistent tiles use the direct (unstaged) conv epilogue");
   // two distinct arrays (not one array indexed by stage parity) so the compiler can
   // tell the expansion's writes from the fragment reads
   __shared__ __attribute__((aligned(16))) uint8_t lds0[T::BUF];
   __shared__ __attribute__((aligned(16))) uint8_t lds1[T::BUF];
-  __shared__ __attribute__((aligned(16))) int rowk[T::BM];  // K_valid - 2 * popA per A row of the tile
+  // K_valid - 2 * popA per A row of the tile: one sum (atomics), or A_TPR partial sums
+  // per row and tile parity (persistent)
+  constexpr int RK_SLOTS = PERS ? 2 * T::BM * T::A_TPR : T::BM;
+  __shared__ __attribute__((aligned(16))) int rowk[RK_SLOTS];
 
   constexpr int MPK = T::FN * T::FM;            // MFMAs per k-step
   constexpr int NM = MPK * T::KSTEPS;           // MFMAs per stage
@@ -360,26 +372,52 @@ __global__ __launch_bounds__(T::THREADS) void mfma_kernel(Contraction p) {
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave % T::WGM, wn = wave / T::WGM;
   const int tiles_m = (p.M + T::BM - 1) / T::BM, tiles_n = (p.N + T::BN - 1) / T::BN;
-  int tm, tn;
-  tile_coords(tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * T::BM, n0 = tn * T::BN;
+  const int total = tiles_m * tiles_n;
+  // tiles of this workgroup: slots blockIdx.x + i * gridDim.x
+  const int ntl = PERS ? (total - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x : 1;
+  auto tile_origin = [&](int i, int& m0, int& n0) __attribute__((always_inline)) {
+    int tm, tn;
+    tile_coords(tiles_m, tiles_n, (int)blockIdx.x + i * (int)gridDim.x, tm, tn);
+    m0 = tm * T::BM;
+    n0 = tn * T::BN;
+  };
 
   // loader roles
   const int a_row = tid / T::A_TPR, a_q = (tid % T::A_TPR) * T::A_WPT;
   const int w_row = tid / T::W_TPR, w_q = (tid % T::W_TPR) * T::W_WPT;
-  const int am = m0 + a_row, wn_row = n0 + w_row;
-  const bool amok = am < p.M;
+  int am = 0, wn_row = 0;
+  bool amok = false;
   PixelCoord pc{0, 0, 0};
-  if constexpr (CONV) pc = pixel_coord(p, amok ? am : 0);
-  for (int i = tid; i < T::BM; i += T::THREADS) rowk[i] = 0;
+  auto loader_tile = [&](int i) __attribute__((always_inline)) {  // A row, pixel and W row of this thread in tile i
+    int m0, n0;
+    tile_origin(i, m0, n0);
+    am = m0 + a_row;
+    wn_row = n0 + w_row;
+    amok = am < p.M;
+    if constexpr (CONV) pc = pixel_coord(p, amok ? am : 0);
+  };
+  loader_tile(0);
+  if constexpr (!PERS)
+    for (int i = tid; i < T::BM; i += T::THREADS) rowk[i] = 0;
   int rowk_part = 0;  // this thread's share of 32 * (real words) - 2 * popA
 
   // raw words of PD stages in flight; stage t lives in register set t % PD
   uint32_t ra[T::PD][T::A_WPT], rw[T::PD][T::W_WPT];
   bool oka[T::PD][T::A_WPT], okw[T::PD][T::W_WPT];
-  auto load_stage = [&](int set, int q0) {
+  auto load_words = [&](int set, int q0) {
     load_a<T::A_WPT, CONV, VEC>(p, am, amok, pc, q0 + a_q, ra[set], oka[set]);
     load_w<T::W_WPT, VEC>(p, wn_row, q0 + w_q, rw[set], okw[set]);
+  };
+  // persistent stream position of the next loads: tile lt, stage ls
+  const int nstages = (p.KW + T::KS - 1) / T::KS;
+  int lt = 0, ls = 0;
+  auto load_next = [&](int set) __attribute__((always_inline)) {
+    // past the last tile: clamped, invalid words (q0 = K/32)
+    load_words(set, lt < ntl ? ls * T::KS : p.KW);
+    if (++ls == nstages) {
+      ls = 0;
+      if (++lt < ntl) loader_tile(lt);
+    }
   };
 
   // expansion of stage words. int8: the source word, and for A words the byte table of
@@ -387,7 +425,19 @@ __global__ __launch_bounds__(T::THREADS) void mfma_kernel(Contraction p) {
   // the word; A keeps its complement with an AND mask and an OR term (both 0 for an
   // invalid word).
   uint32_t src[NWORD], tab[T::A_WPT], tabo[T::A_WPT];
+  int pt = 0, ps = 0;  // persistent stream position of the next prepare
   auto prepare = [&](int set) {
+    if constexpr (PERS) {
+      // the first stage of a new tile: the finished tile's row share goes to its LDS slot
+      if (ps == 0 && pt > 0) {
+        rowk[(((pt - 1) & 1) * T::BM + a_row) * T::A_TPR + a_q / T::A_WPT] = rowk_part;
+        rowk_part = 0;
+      }
+      if (++ps == nstages) {
+        ps = 0;
+        ++pt;
+      }
+    }
 #pragma unroll
     for (int i = 0; i < T::A_WPT; i++) {
       if constexpr (T::F4) {
@@ -430,12 +480,15 @@ __global__ __launch_bounds__(T::THREADS) void mfma_kernel(Contraction p) {
   // K <= 2^24, so every partial sum is exact)
   using Acc = std::conditional_t<T::F4, v16f, v16i>;
   Acc acc[T::FN][T::FM];
+  auto clear_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int i = 0; i < T::FN; i++)
+    for (int i = 0; i < T::FN; i++)
 #pragma unroll
-    for (int j = 0; j < T::FM; j++)
+      for (int j = 0; j < T::FM; j++)
 #pragma unroll
-      for (int e = 0; e < 16; e++) acc[i][j][e] = 0;
+        for (int e = 0; e < 16; e++) acc[i][j][e] = 0;
+  };
+  clear_acc();
 
   const int fr = lane & 31, half = lane >> 5;
   v4i fa[2][T::FM], fw[2][T::FN];
@@ -446,6 +499,27 @@ __global__ __launch_bounds__(T::THREADS) void mfma_kernel(Contraction p) {
     } else {
       const int f = j - T::FM;
       fw[fb][f] = lds_frag<T>(cur, T::BM + wn * T::WTN + f * 32 + fr, 2 * kk + half);
+    }
+  };
+
+  // epilogue of the tile whose last stage just ended (persistent: tile ct)
+  int ct = 0, cs = 0;
+  auto tile_epilogue = [&](int i) __attribute__((always_inline)) {
+    int m0, n0;
+    tile_origin(i, m0, n0);
+    if constexpr (PERS) {
+      const int* slots = rowk + (i & 1) * T::BM * T::A_TPR;
+      store_tile<T, OUT, CONV>(
+          p, acc,
+          [&](int ml) {
+            int v = 0;
+#pragma unroll
+            for (int j = 0; j < T::A_TPR; j++) v += slots[ml * T::A_TPR + j];
+            return v;
+          },
+          lds0, lds1, m0, n0, wm, wn);
+    } else {
+      store_tile<T, OUT, CONV>(p, acc, [&](int ml) { return rowk[ml]; }, lds0, lds1, m0, n0, wm, wn);
     }
   };
 
@@ -461,7 +535,10 @@ __global__ __launch_bounds__(T::THREADS) void mfma_kernel(Contraction p) {
     constexpr int PH = decltype(phase)::value;
     const uint8_t* cur = (PH & 1) ? lds1 : lds0;
     uint8_t* nxt = (PH & 1) ? lds0 : lds1;
-    load_stage(PH % T::PD, (s + T::PD) * T::KS);
+    if constexpr (PERS)
+      load_next(PH % T::PD);
+    else
+      load_words(PH % T::PD, (s + T::PD) * T::KS);
 #pragma unroll
     for (int j = 0; j < RPK; j++) read_frag(cur, 0, j);
     prepare((PH + 1) % T::PD);
@@ -501,17 +578,31 @@ __global__ __launch_bounds__(T::THREADS) void mfma_kernel(Contraction p) {
       __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
+    if constexpr (PERS) {
+      if (++cs == nstages) {
+        tile_epilogue(ct);
+        clear_acc();
+        cs = 0;
+        ++ct;
+      }
+    }
   };
 
-  const int nstages = (p.KW + T::KS - 1) / T::KS;
+  // stages of this workgroup: one tile, or ntl tiles back to back
+  const int nstream = PERS ? ntl * nstages : nstages;
 #pragma unroll
-  for (int t = 0; t < T::PD; t++) load_stage(t, t * T::KS);  // clamped + invalid past K
+  for (int t = 0; t < T::PD; t++) {
+    if constexpr (PERS)
+      load_next(t);
+    else
+      load_words(t, t * T::KS);  // clamped + invalid past K
+  }
   prepare(0);
 #pragma unroll
   for (int u = 0; u < NU; u++) expand_unit(lds0, u);
   __syncthreads();
   int s = 0;
-  for (; s + T::UNROLL <= nstages; s += T::UNROLL) {
+  for (; s + T::UNROLL <= nstream; s += T::UNROLL) {
     stage(std::integral_constant<int, 0>{}, s);
     stage(std::integral_constant<int, 1>{}, s + 1);
     if constexpr (T::UNROLL > 2) {
@@ -523,33 +614,71 @@ __global__ __launch_bounds__(T::THREADS) void mfma_kernel(Contraction p) {
       stage(std::integral_constant<int, 5>{}, s + 5);
     }
   }
-  if (s < nstages) stage(std::integral_constant<int, 0>{}, s);
-  if (s + 1 < nstages) stage(std::integral_constant<int, 1>{}, s + 1);
+  if (s < nstream) stage(std::integral_constant<int, 0>{}, s);
+  if (s + 1 < nstream) stage(std::integral_constant<int, 1>{}, s + 1);
   if constexpr (T::UNROLL > 2) {
-    if (s + 2 < nstages) stage(std::integral_constant<int, 2>{}, s + 2);
-    if (s + 3 < nstages) stage(std::integral_constant<int, 3>{}, s + 3);
+    if (s + 2 < nstream) stage(std::integral_constant<int, 2>{}, s + 2);
+    if (s + 3 < nstream) stage(std::integral_constant<int, 3>{}, s + 3);
   }
   if constexpr (T::UNROLL > 4) {
-    if (s + 4 < nstages) stage(std::integral_constant<int, 4>{}, s + 4);
+    if (s + 4 < nstream) stage(std::integral_constant<int, 4>{}, s + 4);
   }
 
-  atomicAdd(&rowk[a_row], rowk_part);
-  __syncthreads();
+  if constexpr (!PERS) {
+    atomicAdd(&rowk[a_row], rowk_part);
+    __syncthreads();
+    tile_epilogue(0);
+  }
+}
 
-  store_tile<T, OUT, CONV>(p, acc, rowk, lds0, lds1, m0, n0, wm, wn);
+// Workgroups of the persistent conv kernel for tile T that the current device holds at
+// once (compute units x resident workgroups per unit), cached per device and kernel.
+template <class T, int OUT, bool VEC>
+int persistent_slots() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_kernel<T, OUT, true, VEC, true>,
+                                                     T::THREADS, 0) != hipSuccess)
+      return 0;
+    v = cus * (per_cu > 0 ? per_cu : 1);
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+template <class T, int OUT, bool CONV, bool VEC>
+hipError_t launch_tile_o(const Contraction& p, hipStream_t stream) {
+  const int64_t tiles = (int64_t)((p.M + T::BM - 1) / T::BM) * ((p.N + T::BN - 1) / T::BN);
+  const dim3 block(T::THREADS);
+  if constexpr (CONV && T::F4) {
+    // more fp4 conv tiles than fit at once: one persistent workgroup per resident slot
+    // streams its tiles back to back instead of running them in separate rounds (the
+    // int8 256 x 256 conv tile would spill with the extra state)
+    const int slots = persistent_slots<T, OUT, VEC>();
+    if (slots > 0 && tiles > slots) {
+      hipLaunchKernelGGL((mfma_kernel<T, OUT, CONV, VEC, true>), dim3((unsigned)slots), block, 0,
+                         stream, p);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((mfma_kernel<T, OUT, CONV, VEC, false>), dim3((unsigned)tiles), block, 0,
+                     stream, p);
+  return hipGetLastError();
 }
 
 template <class T, bool CONV, bool VEC>
 hipError_t launch_tile_v(const Contraction& p, int out_dtype, hipStream_t stream) {
-  const int64_t tiles = (int64_t)((p.M + T::BM - 1) / T::BM) * ((p.N + T::BN - 1) / T::BN);
-  const dim3 grid((unsigned)tiles), block(T::THREADS);
   switch (out_dtype) {
-    case kF32: hipLaunchKernelGGL((mfma_kernel<T, kF32, CONV, VEC>), grid, block, 0, stream, p); break;
-    case kF16: hipLaunchKernelGGL((mfma_kernel<T, kF16, CONV, VEC>), grid, block, 0, stream, p); break;
-    case kBF16: hipLaunchKernelGGL((mfma_kernel<T, kBF16, CONV, VEC>), grid, block, 0, stream, p); break;
-    default: hipLaunchKernelGGL((mfma_kernel<T, kI32, CONV, VEC>), grid, block, 0, stream, p); break;
+    case kF32: return launch_tile_o<T, kF32, CONV, VEC>(p, stream);
+    case kF16: return launch_tile_o<T, kF16, CONV, VEC>(p, stream);
+    case kBF16: return launch_tile_o<T, kBF16, CONV, VEC>(p, stream);
+    default: return launch_tile_o<T, kI32, CONV, VEC>(p, stream);
   }
-  return hipGetLastError();
 }
 
 // Vector loads need each thread's words of a stage to be contiguous, aligned and, for
@@ -582,9 +711,9 @@ hipError_t launch_tile(const Contraction& p, int out_dtype, hipStream_t stream) 
 #ifndef BNN_MFMA_PD_CF4
 #define BNN_MFMA_PD_CF4 2
 #endif
-// fp4 conv tiles keep fewer stages in flight and stop at 128 x 256: their implicit-im2col
-// loaders hold more state per word, and deeper prefetch or a 256 x 256 tile no longer fits
-// in 256 registers per lane without spilling.
+// fp4 conv tiles keep two prefetched stages (measured faster than four on the conv
+// workloads, whose tiles have few stages, and spill-free) and stop at 128 x 256: with the
+// implicit-im2col loaders' extra state a 256 x 256 tile no longer fits in 256 registers.
 template <bool F4, bool CONV>
 struct Tiles {
   static constexpr int KS = F4 ? 8 : 4;

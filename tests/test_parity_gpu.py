@@ -208,6 +208,27 @@ def test_tile_variants_sampled(bnn, orc):
         assert torch.equal(got[images].cpu(), acc), path
 
 
+def test_persistent_conv_tiles(bnn, orc):
+    """Conv shapes with more fp4 128 x 256 tiles than the GPU holds at once, which run as
+    persistent workgroups streaming several tiles each (tile boundaries at every stage
+    count, ragged last tile, planes whose size is not a multiple of 4): full oracle check."""
+    g = torch.Generator().manual_seed(71)
+    cases = [(48, 32, 27, 27, 256, 3, 1, 1, 1),    # 2 stages per tile, 274 tiles, HW = 729
+             (64, 32, 24, 24, 256, 1, 1, 0, 1),    # 1 stage per tile, 288 tiles
+             (40, 64, 30, 30, 200, 3, 1, 1, 1)]    # 3 stages, ragged N, 282 tiles
+    for (b, c, h, w, o, ks, st, pd, dl) in cases:
+        x = torch.randn((b, c, h, w), generator=g).half()
+        wt = torch.randn((o, c, ks, ks), generator=g).half()
+        acc = orc.conv2d_acc(x, wt, st, pd, dl)
+        y = orc.scale(acc, 0.75, 0.5)
+        xd, wp = x.to(DEV), bnn.w_pack(wt.to(DEV))
+        _say(f"persistent conv {b}x{c}x{h}x{w} -> {o}, k{ks}")
+        got = bnn.conv2d(xd, wp, 0.75, 0.5, ks, st, pd, dl, path="mfma_fp4", out_dtype=torch.int32)
+        assert torch.equal(got.cpu(), acc), (b, c, h, w, o, ks)
+        out = bnn.conv2d(xd, wp, 0.75, 0.5, ks, st, pd, dl, path="mfma_fp4", out_dtype=torch.float16)
+        check_scaled(out, acc, y, f"persistent conv {b}x{c}x{h}x{w}")
+
+
 # ----------------------------------------------------------------------------- sweeps and edges
 
 def test_random_linear_sweep(bnn, orc):
