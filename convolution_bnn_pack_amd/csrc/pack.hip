@@ -68,7 +68,8 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(const u32x4* __restrict_
       mine = (pos == j) ? part : mine;
     }
     const int64_t myword = wbase + pos * WPI + grp;
-    if (myword < total_words) out[myword] = mine;
+    // packed words are written once: stream them past the caches (measured ~3 % faster)
+    if (myword < total_words) __builtin_nontemporal_store(mine, out + myword);
   }
 }
 
