@@ -250,10 +250,54 @@ __device__ __forceinline__ void store_tile(const Contraction& p, const Acc (&acc
     // address is aligned), element stores otherwise.
     const int hw = p.Ho * p.Wo;
     const bool quad = (hw & 3) == 0;
+    // 16-bit outputs with planes a multiple of 8: lanes fr and fr + 32 (same feature) trade
+    // halves of their pixel quads so each stores eight consecutive pixels (16 bytes) at once
+    constexpr bool HALF16 = OUT == kF16 || OUT == kBF16;
+    const bool oct = HALF16 && (hw & 7) == 0;
+    auto bits16 = [&](int v) -> uint32_t {
+      const float f = (float)v * p.alpha;
+      if constexpr (OUT == kF16) {
+        const __half h = __float2half_rn(f);
+        return *reinterpret_cast<const uint16_t*>(&h);
+      } else {
+        const __hip_bfloat16 h = __float2bfloat16(f);
+        return *reinterpret_cast<const uint16_t*>(&h);
+      }
+    };
 #pragma unroll
     for (int fn = 0; fn < T::FN; fn++) {
       const int n = n0 + wn * T::WTN + fn * 32 + fr;
-      if (n >= p.N) continue;
+      if (n >= p.N) continue;  // uniform over the lane pair fr, fr + 32
+      if constexpr (HALF16) {
+        if (oct) {
+#pragma unroll
+          for (int fm = 0; fm < T::FM; fm++)
+#pragma unroll
+            for (int j = 0; j < 2; j++) {
+              // groups g = 2j (pixels +0..7) and 2j+1 (+8..15) of this 32-pixel block
+              uint32_t q[2][2];
+#pragma unroll
+              for (int gg = 0; gg < 2; gg++) {
+                const int g = 2 * j + gg;
+                const int ml = wm * T::WTM + fm * 32 + 8 * g + 4 * half;
+                uint32_t h4[4];
+#pragma unroll
+                for (int i = 0; i < 4; i++) h4[i] = bits16(rowk(ml + i) + 2 * acc_int(fn, fm, 4 * g + i));
+                q[gg][0] = h4[0] | (h4[1] << 16);
+                q[gg][1] = h4[2] | (h4[3] << 16);
+              }
+              const uint32_t s0 = half ? q[0][0] : q[1][0], s1 = half ? q[0][1] : q[1][1];
+              const uint32_t r0 = (uint32_t)__shfl_xor((int)s0, 32), r1 = (uint32_t)__shfl_xor((int)s1, 32);
+              const int mg = m0 + wm * T::WTM + fm * 32 + 16 * j + 8 * half;
+              if (mg < p.M) {
+                const int b = mg / hw, pix = mg - b * hw;
+                const uint4 v = half ? make_uint4(r0, r1, q[1][0], q[1][1]) : make_uint4(q[0][0], q[0][1], r0, r1);
+                *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.out) + ((int64_t)b * p.N + n) * hw + pix) = v;
+              }
+            }
+          continue;
+        }
+      }
 #pragma unroll
       for (int fm = 0; fm < T::FM; fm++)
 #pragma unroll
