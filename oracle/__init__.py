@@ -54,6 +54,10 @@ def _bind(lib):
     lib.oracle_conv2d_kvalid.argtypes = [I64, I64, I64, I64, I64, I64, I64, P]
     lib.oracle_conv2d_kvalid.restype = I
     lib.oracle_scale.argtypes = [P, I64, ctypes.c_double, ctypes.c_double, P]
+    lib.oracle_pack_rows_shift.argtypes = [P, I, I64, I64, P, I, I64, P]
+    lib.oracle_pack_nchw_shift.argtypes = [P, I, I64, I64, I64, I64, P, I, P]
+    lib.oracle_abs_mean_scale.argtypes = [P, I, I64, ctypes.c_double]
+    lib.oracle_abs_mean_scale.restype = ctypes.c_double
     return lib
 
 
@@ -202,3 +206,32 @@ def scale(acc: torch.Tensor, scale_a: float, scale_w: float) -> torch.Tensor:
     y = torch.empty(acc.shape, dtype=torch.float64)
     _load().oracle_scale(acc.data_ptr(), acc.numel(), float(scale_a), float(scale_w), y.data_ptr())
     return y
+
+
+def pack_rows_shift(x: torch.Tensor, bias: torch.Tensor) -> torch.Tensor:
+    """x [rows, k] shifted by bias (one value, or [k]) -> int32 words [rows, k/32];
+    bit j of word q = (x[r, 32q+j] + bias >= 0)."""
+    x, bias = _cpu(x), _cpu(bias)
+    rows, k = x.shape
+    assert k % 32 == 0 and bias.numel() in (1, k)
+    out = _words(rows * (k // 32))
+    _load().oracle_pack_rows_shift(x.data_ptr(), _code(x), rows, k, bias.data_ptr(), _code(bias),
+                                   bias.numel(), out.data_ptr())
+    return out.view(rows, k // 32)
+
+
+def pack_nchw_shift(x: torch.Tensor, bias: torch.Tensor) -> torch.Tensor:
+    """x [b, c, h, w] shifted by bias[c] -> int32 words [b, h, w, c/32]."""
+    x, bias = _cpu(x), _cpu(bias)
+    b, c, h, w = x.shape
+    assert c % 32 == 0 and bias.numel() == c
+    out = _words(b * h * w * (c // 32))
+    _load().oracle_pack_nchw_shift(x.data_ptr(), _code(x), b, c, h, w, bias.data_ptr(), _code(bias),
+                                   out.data_ptr())
+    return out.view(b, h, w, c // 32)
+
+
+def abs_mean_scale(x: torch.Tensor, factor: float) -> float:
+    """factor * mean(|x|) over every element (the sum in double, in index order)."""
+    x = _cpu(x)
+    return float(_load().oracle_abs_mean_scale(x.data_ptr(), _code(x), x.numel(), float(factor)))

@@ -41,6 +41,25 @@
  *    The scale product is the host-side product of the two scalar scales
  *    (BinaryConv2dForward.forward on the qconv/binary/cutlass/layer page).
  *
+ *  - The activation prologue of both layers (set_activation of
+ *    BinaryConv2dCutlass on the qconv/binary/cutlass/layer page and of
+ *    BinaryLinearCuda on the BinaryLinearCuda page). The input is shifted by
+ *    the learnable bias_a before its sign is taken: one value per input
+ *    channel for the conv, broadcast over batch and pixels; the linear page
+ *    calls its bias layer-wise without giving a shape, so the linear form
+ *    takes either one value for the whole layer or one per input feature.
+ *    The bit is the sign of x + b. The exact sum of two floats keeps its
+ *    sign, and its zero-ness, when rounded to any IEEE format (a non-zero
+ *    sum is a multiple of the smallest subnormal, so it never rounds to 0;
+ *    overflow gives an infinity of the same sign), so the sign does not
+ *    depend on the dtype the layer adds in; NaN operands and opposite
+ *    infinities give NaN, hence -1. Here the sum is taken in double from
+ *    the exactly widened operands.
+ *    While scale_a is still zero the layer sets it to 2 * mean|x|
+ *    (symmetric quantization) or 4 * mean|x|, over every element of the
+ *    unshifted input: here the double sum of |x| in index order, divided by
+ *    the element count, times the factor.
+ *
  * Every accumulation is a sum of +-1 products; each partial sum is an
  * integer of magnitude at most K < 2^24, so float accumulation is exact in
  * any order (that is why the reductions may be vectorised).
@@ -276,4 +295,57 @@ void oracle_scale(const int32_t *acc, int64_t count, double scale_a, double scal
   double alpha = scale_a * scale_w;
 #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < count; i++) y[i] = (double)acc[i] * alpha;
+}
+
+/* The shifted sign rule: +1 when x + b >= 0 (the sum taken in double), else -1. */
+static float sgn_shift(float v, float b) {
+  double sum = (double)v + (double)b;
+  return sum >= 0.0 ? 1.0f : -1.0f;
+}
+
+/* Row-major x[rows][k] shifted by a bias, then packed as oracle_pack_rows does. The bias of
+ * column kk is bias[kk] when blen == k and bias[0] for every column when blen == 1; bit j of
+ * word q is 1 iff x[r][32q+j] + bias >= 0. */
+void oracle_pack_rows_shift(const void *x, int dtype, int64_t rows, int64_t k, const void *bias,
+                            int bdtype, int64_t blen, uint32_t *out) {
+  int64_t kw = k / 32;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; r++)
+    for (int64_t q = 0; q < kw; q++) {
+      uint32_t word = 0;
+      for (int j = 0; j < 32; j++) {
+        int64_t col = 32 * q + j;
+        float b = widen(bias, bdtype, blen == 1 ? 0 : col);
+        if (sgn_shift(widen(x, dtype, r * k + col), b) > 0.0f) word |= (uint32_t)1 << j;
+      }
+      out[r * kw + q] = word;
+    }
+}
+
+/* NCHW x[b][c][h][w] shifted by bias[c], then packed as oracle_pack_nchw does: bit j of word
+ * q of pixel (b, h, w) is 1 iff x[b][32q+j][h][w] + bias[32q+j] >= 0. */
+void oracle_pack_nchw_shift(const void *x, int dtype, int64_t B, int64_t C, int64_t H, int64_t W,
+                            const void *bias, int bdtype, uint32_t *out) {
+  int64_t cw = C / 32;
+#pragma omp parallel for schedule(static)
+  for (int64_t b = 0; b < B; b++)
+    for (int64_t ih = 0; ih < H; ih++)
+      for (int64_t iw = 0; iw < W; iw++)
+        for (int64_t q = 0; q < cw; q++) {
+          uint32_t word = 0;
+          for (int j = 0; j < 32; j++) {
+            int64_t c = 32 * q + j;
+            int64_t idx = ((b * C + c) * H + ih) * W + iw;
+            if (sgn_shift(widen(x, dtype, idx), widen(bias, bdtype, c)) > 0.0f) word |= (uint32_t)1 << j;
+          }
+          out[((b * H + ih) * W + iw) * cw + q] = word;
+        }
+}
+
+/* The lazily initialised activation scale: factor * mean|x| over count elements (factor 2 for
+ * symmetric quantization, 4 otherwise), the sum of |x[i]| taken in double in index order. */
+double oracle_abs_mean_scale(const void *x, int dtype, int64_t count, double factor) {
+  double sum = 0.0;
+  for (int64_t i = 0; i < count; i++) sum += fabs((double)widen(x, dtype, i));
+  return factor * (sum / (double)count);
 }

@@ -48,6 +48,15 @@ MUTANTS = {
     "kvalid_off_by_one": ("if (ih >= 0 && ih < H && iw >= 0 && iw < W) taps++;",
                           "if (ih >= 0 && ih <= H && iw >= 0 && iw < W) taps++;"),
     "scale_sum_instead_of_product": ("double alpha = scale_a * scale_w;", "double alpha = scale_a + scale_w;"),
+    "shift_subtracts_bias": ("double sum = (double)v + (double)b;", "double sum = (double)v - (double)b;"),
+    "shift_zero_sum_negative": ("return sum >= 0.0 ? 1.0f : -1.0f;", "return sum > 0.0 ? 1.0f : -1.0f;"),
+    "rows_shift_bias_by_word": ("float b = widen(bias, bdtype, blen == 1 ? 0 : col);",
+                                "float b = widen(bias, bdtype, blen == 1 ? 0 : q);"),
+    "nchw_shift_bias_by_width": ("widen(bias, bdtype, c)) > 0.0f", "widen(bias, bdtype, iw)) > 0.0f"),
+    "abs_mean_drops_abs": ("sum += fabs((double)widen(x, dtype, i));", "sum += (double)widen(x, dtype, i);"),
+    "abs_mean_count_minus_one": ("return factor * (sum / (double)count);",
+                                 "return factor * (sum / (double)(count - 1));"),
+    "abs_mean_fixed_factor": ("return factor * (sum / (double)count);", "return 2.0 * (sum / (double)count);"),
 }
 
 
@@ -163,7 +172,49 @@ def _pins(orc):
         return True
 
     check("conv_vs_torch", lib_conv)
+
+    edges = _golden("shift_sign_edges.json")["cases"]
+
+    def shift_edges():
+        for xdt, xh, bdt, bh, want, _ in edges:
+            x, b = _bits_value(xdt, xh), _bits_value(bdt, bh)
+            words = orc.pack_rows_shift(x.repeat(32).view(1, 32).contiguous(), b.repeat(32).contiguous())
+            if (1 if int(words[0, 0]) & 1 else -1) != want:
+                return False
+        return True
+
+    check("shift_sign_edges", shift_edges)
+
+    def shift_vs_torch():
+        gen = torch.Generator().manual_seed(15)
+        x = torch.randn((6, 96), generator=gen)
+        bias = 0.5 * torch.randn(96, generator=gen)
+        bits = (orc.pack_rows_shift(x, bias).numpy().astype(np.uint32).astype(np.int64)[..., None] >> np.arange(32)) & 1
+        if not np.array_equal(bits.reshape(6, 96), ((x + bias) >= 0).numpy().astype(np.int64)):
+            return False
+        xn = torch.randn((2, 64, 5, 3), generator=gen)
+        bn = 0.5 * torch.randn(64, generator=gen)
+        want = orc.pack_rows(((xn + bn.view(1, -1, 1, 1)) >= 0).float().sub(0.5)
+                             .permute(0, 2, 3, 1).contiguous().reshape(-1, 64)).view(2, 5, 3, 2)
+        return torch.equal(orc.pack_nchw_shift(xn, bn), want)
+
+    check("shift_vs_torch", shift_vs_torch)
+
+    def abs_mean():
+        ints = torch.arange(1000, dtype=torch.float32)
+        return (orc.abs_mean_scale(-ints, 4.0) == 2 * 999 and orc.abs_mean_scale(ints, 2.0) == 999
+                and orc.abs_mean_scale(torch.tensor([0.5, -2.5]), 2.0) == 3.0)
+
+    check("abs_mean_closed_forms", abs_mean)
     return failed
+
+
+def _bits_value(dt, hexbits):
+    v = int(hexbits, 16)
+    if dt == "f32":
+        return torch.tensor([v - (1 << 32) if v >= 1 << 31 else v], dtype=torch.int32).view(torch.float32)
+    tdt = torch.float16 if dt == "f16" else torch.bfloat16
+    return torch.tensor([v - (1 << 16) if v >= 1 << 15 else v], dtype=torch.int16).view(tdt)
 
 
 @pytest.fixture()
