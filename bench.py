@@ -33,19 +33,31 @@ PEAK_MFMA_F4_TOPS = 10100.0     # dense fp4 MFMA, MI355X
 PEAK_VALU_BINARY_TOPS = 256 * 64 * 2.4e9 * 32 / 1e12
 
 DEFAULT_WORKLOAD = "linear_2048x4096x4096_f16"
+# Codec workloads: one HBM-bound kernel over one workload's activation (no contraction).
+#   name -> (kernel kind, workload whose x it reads, shift dtype or None)
+CODEC_WORKLOADS = {
+    "pack_linear_16384x8192_bf16": ("pack", "linear_16384x8192x8192_bf16", None),
+    "pack_shift_linear_16384x8192_bf16": ("pack_shift", "linear_16384x8192x8192_bf16", "f32"),
+    "pack_nchw_128x128x28x28_f16": ("pack_nchw", "conv_down_s2_f16", None),
+    "pack_shift_nchw_128x128x28x28_f16": ("pack_nchw", "conv_down_s2_f16", "f16"),
+    "abs_mean_16384x8192_bf16": ("abs_mean", "linear_16384x8192x8192_bf16", None),
+}
 PACK_WORKLOAD = "pack_linear_16384x8192_bf16"
 # kernel kinds: source file, kernel function name, roofline peak and arithmetic type
 KERNEL_SOURCES = {"mfma": "gemm_mfma.hip", "mfma_fp4": "gemm_mfma.hip", "xor": "gemm_xor.hip",
-                  "pack": "pack.hip"}
+                  "pack": "pack.hip", "pack_shift": "pack.hip", "pack_nchw": "pack.hip",
+                  "abs_mean": "pack.hip"}
 KERNEL_NAMES = {"mfma": "mfma_kernel", "mfma_fp4": "mfma_kernel", "xor": "xor_kernel",
-                "pack": "pack_rows_kernel"}
+                "pack": "pack_rows_kernel", "pack_shift": "pack_rows_shift_kernel",
+                "pack_nchw": "pack_nchw_kernel", "abs_mean": "abs_sum_kernel"}
 PEAKS = {"mfma": PEAK_MFMA_I8_TOPS, "mfma_fp4": PEAK_MFMA_F4_TOPS, "xor": PEAK_VALU_BINARY_TOPS}
 DTYPES = {"mfma": "i8", "mfma_fp4": "fp4(e2m1)", "xor": "u32"}
+CODEC_KINDS = ("pack", "pack_shift", "pack_nchw", "abs_mean")
 
 
 def kernel_kind(name):
     """Kind of a demangled kernel name from a rocprofv3 counter file (None: not ours)."""
-    for kind in ("pack", "xor"):
+    for kind in CODEC_KINDS + ("xor",):
         if KERNEL_NAMES[kind] + "<" in name or KERNEL_NAMES[kind] + "(" in name:
             return kind
     if "mfma_kernel<" in name:
@@ -94,7 +106,7 @@ def pmc_summary(args):
         return vals
 
     wl = args.workload
-    kind = "pack" if wl == PACK_WORKLOAD else None
+    kind = CODEC_WORKLOADS[wl][0] if wl in CODEC_WORKLOADS else None
     out = {}
     for counter, path in (("FETCH_SIZE", args.pmc_summary[0]), ("WRITE_SIZE", args.pmc_summary[1])):
         vals = read(path, counter)
@@ -103,7 +115,7 @@ def pmc_summary(args):
             raise SystemExit(f"no {args.copy_kernel} kernel in {path}")
         copy_kib = statistics.median(copy)
         scale = (args.copy_mib << 20) / 1024.0 / copy_kib if args.copy_mib else 1.0
-        for k in (["pack"] if kind else ["mfma", "mfma_fp4", "xor"]):
+        for k in ([kind] if kind else ["mfma", "mfma_fp4", "xor"]):
             # the workload's kernel is the instantiation launched most often (the parity spot
             # check adds single launches of other output types)
             cands = [(len(vs), name) for name, vs in vals.items() if kernel_kind(name) == k]
@@ -197,8 +209,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    pack_only = args.workload == PACK_WORKLOAD
-    wl = synth.WORKLOADS["linear_16384x8192x8192_bf16" if pack_only else args.workload]
+    pack_only = args.workload in CODEC_WORKLOADS
+    codec_kind, base, shift_dt = CODEC_WORKLOADS.get(args.workload, (None, None, None))
+    wl = synth.WORKLOADS[base if pack_only else args.workload]
     log(f"workload {args.workload}: generating inputs")
     x, w, sa, sw = synth.make_inputs(wl, draw_weight=not pack_only)
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
@@ -211,15 +224,53 @@ def main():
         return torch.cuda.current_stream().cuda_stream
 
     if pack_only:
-        # two copies of the 268 MB activation, alternated, so every pass reads HBM rather than
+        # enough copies of the activation, used in turn, that every pass reads HBM rather than
         # the 256 MB last-level cache
-        xs = [xd, xd.clone()]
-        words = wl.m * wl.k // 32
-        xp = torch.empty((wl.m, wl.k // 32), dtype=torch.int32, device=dev)
-        bytes_per = wl.m * wl.k * 2 + words * 4
+        xbytes = xd.numel() * xd.element_size()
+        ncopy = max(2, -(-(640 << 20) // xbytes))
+        xs = [xd] + [xd.clone() for _ in range(ncopy - 1)]
         path_used = None
-        kernels = {"pack": [lambda i: lib.bnn_pack_sign(xs[i & 1].data_ptr(), xcode, wl.m, wl.k,
-                                                        xp.data_ptr(), cur_stream())]}
+        if wl.kind == "linear":
+            words = wl.m * wl.k // 32
+            xp = torch.empty((wl.m, wl.k // 32), dtype=torch.int32, device=dev)
+        else:
+            words = wl.batch * wl.h * wl.w * wl.c // 32
+            xp = torch.empty((wl.batch, wl.h, wl.w, wl.c // 32), dtype=torch.int32, device=dev)
+        bias = None
+        if shift_dt:
+            nb = wl.k if wl.kind == "linear" else wl.c
+            bias = synth.make_shift(nb, shift_dt, wl.seed + 50).to(dev)
+            bcode = bnn._DT[bias.dtype]
+        if codec_kind == "pack":
+            fn = lambda i: lib.bnn_pack_sign(xs[i % ncopy].data_ptr(), xcode, wl.m, wl.k,
+                                             xp.data_ptr(), cur_stream())
+        elif codec_kind == "pack_shift":
+            fn = lambda i: lib.bnn_pack_sign_shift(xs[i % ncopy].data_ptr(), xcode, wl.m, wl.k,
+                                                   bias.data_ptr(), bcode, bias.numel(),
+                                                   xp.data_ptr(), cur_stream())
+        elif codec_kind == "pack_nchw" and bias is None:
+            fn = lambda i: lib.bnn_pack_sign_nchw(xs[i % ncopy].data_ptr(), xcode, wl.batch, wl.c,
+                                                  wl.h, wl.w, xp.data_ptr(), cur_stream())
+        elif codec_kind == "pack_nchw":
+            fn = lambda i: lib.bnn_pack_sign_nchw_shift(xs[i % ncopy].data_ptr(), xcode, wl.batch,
+                                                        wl.c, wl.h, wl.w, bias.data_ptr(), bcode,
+                                                        xp.data_ptr(), cur_stream())
+        else:
+            count = xd.numel()
+            scale_out = torch.empty((), dtype=torch.float64, device=dev)
+            ws = torch.empty(lib.bnn_abs_mean_workspace_bytes(count), dtype=torch.uint8, device=dev)
+            words = 0
+            fn = lambda i: lib.bnn_abs_mean_scale(xs[i % ncopy].data_ptr(), xcode, count, 2.0,
+                                                  scale_out.data_ptr(), ws.data_ptr(), ws.numel(),
+                                                  cur_stream())
+        # algorithmic bytes: the activation read once, the packed words written once, the shift
+        # vector read once (abs-mean: its partial sums, written and read once, and the result)
+        bytes_per = xbytes + words * 4
+        if bias is not None:
+            bytes_per += bias.numel() * bias.element_size()
+        if codec_kind == "abs_mean":
+            bytes_per += 2 * ws.numel() + 8
+        kernels = {"pack": [fn]}
         step_fns = kernels["pack"]
     else:
         wp = bnn.w_pack(w.to(dev))
@@ -309,13 +360,18 @@ def main():
         del g
 
     if pack_only:
+        # the abs-mean step is two launches (partial sums, then the final one-workgroup sum):
+        # its timed average covers both, so the roofline figure is a lower bound for the first
         dom_ms = kern_ms["pack"]
         achieved = bytes_per / (dom_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic_for("pack", args.workload),
-                "kernel": KERNEL_NAMES["pack"], "kernel_ms": round(dom_ms, 5)}
+                "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "traffic": traffic_for(codec_kind, args.workload),
+                "kernel": KERNEL_NAMES[codec_kind], "kernel_ms": round(dom_ms, 5)}
         value = bytes_per / (ms_per_step * 1e-3) / 1e9
-        metric, unit, dtype = "sign+pack bandwidth", "GB/s", "u32"
+        metric, unit = {"abs_mean": ("abs-mean scale bandwidth", "GB/s")}.get(
+            codec_kind, ("sign+pack bandwidth", "GB/s"))
+        dtype = "f64" if codec_kind == "abs_mean" else "u32"
     else:
         dom_ms = kern_ms["core"]
         kind = {bnn.PATH_XOR: "xor", bnn.PATH_MFMA: "mfma", bnn.PATH_MFMA_FP4: "mfma_fp4"}[path_used]

@@ -9,6 +9,9 @@ libbnn.so is missing, importing the module raises.
 Entry points mirror the C ABI:
   pack_sign(x)              rows of x -> packed int32 words [rows, k/32]
   pack_sign_nchw(x)         NCHW x -> packed words [n, h, w, c/32]
+  pack_sign_shift(x, bias)  rows of x + bias (one value or one per column) -> packed words
+  pack_sign_nchw_shift(x, bias)  NCHW x + bias[c] -> packed words [n, h, w, c/32]
+  abs_mean_scale(x, factor) factor * mean|x| as a 0-dim float64 device tensor
   w_pack(weight)            linear [out, in] or OIHW conv weight -> packed words
   gemm(x, w_packed, ...)    binary linear forward (bitorch-engine BinaryLinearForward)
   conv2d(x, w_packed, ...)  binary conv2d forward (bitorch-engine BinaryConv2dForward)
@@ -30,7 +33,8 @@ F32, F16, BF16, I32, U32_PACKED = 0, 1, 2, 3, 4
 PATH_AUTO, PATH_XOR, PATH_MFMA, PATH_MFMA_FP4 = 0, 1, 2, 3
 OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIGN, ERR_WORKSPACE, ERR_PATH, ERR_HIP = range(8)
 
-EXPORTS = ("bnn_pack_sign", "bnn_pack_sign_nchw", "bnn_w_pack", "bnn_gemm", "bnn_conv2d",
+EXPORTS = ("bnn_pack_sign", "bnn_pack_sign_nchw", "bnn_pack_sign_shift", "bnn_pack_sign_nchw_shift",
+           "bnn_abs_mean_scale", "bnn_abs_mean_workspace_bytes", "bnn_w_pack", "bnn_gemm", "bnn_conv2d",
            "bnn_gemm_workspace_bytes", "bnn_conv2d_workspace_bytes", "bnn_gemm_auto_path",
            "bnn_conv2d_auto_path", "bnn_last_path", "bnn_status_string")
 
@@ -45,6 +49,10 @@ def _bind(path: str) -> ctypes.CDLL:
     sig = {
         "bnn_pack_sign": ([P, I, I64, I64, P, P], I),
         "bnn_pack_sign_nchw": ([P, I, I64, I64, I64, I64, P, P], I),
+        "bnn_pack_sign_shift": ([P, I, I64, I64, P, I, I64, P, P], I),
+        "bnn_pack_sign_nchw_shift": ([P, I, I64, I64, I64, I64, P, I, P, P], I),
+        "bnn_abs_mean_scale": ([P, I, I64, D, P, P, SZ, P], I),
+        "bnn_abs_mean_workspace_bytes": ([I64], SZ),
         "bnn_w_pack": ([P, I, I64, I64, I, P, P], I),
         "bnn_gemm": ([P, I, P, I64, I64, I64, D, D, I, P, I, P, SZ, P], I),
         "bnn_conv2d": ([P, I, I64, I64, I64, I64, P, I64, D, D, I, I, I, I, I, P, I, P, SZ, P], I),
@@ -131,6 +139,66 @@ def pack_sign_nchw(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Te
         _dev(out, "out")
     _check(lib.bnn_pack_sign_nchw(x.data_ptr(), _dtype_code(x, "x"), n, c, h, w, out.data_ptr(),
                                   _stream(x)), "bnn_pack_sign_nchw")
+    return out
+
+
+def _bias(bias: torch.Tensor, x: torch.Tensor) -> torch.Tensor:
+    bias = _dev(bias, "bias")
+    if bias.device != x.device:
+        raise ValueError("bias must be on x's device")
+    return bias
+
+
+def pack_sign_shift(x: torch.Tensor, bias: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Shifted sign+pack along the last axis (the linear layer's activation prologue):
+    bit = (x + bias >= 0) with bias one value ([1] or 0-dim) or one per column ([k])."""
+    x = _dev(x, "x")
+    bias = _bias(bias, x)
+    k = x.shape[-1]
+    rows = x.numel() // k if k else 0
+    if out is None:
+        out = torch.empty((*x.shape[:-1], k // 32), dtype=torch.int32, device=x.device)
+    else:
+        _dev(out, "out")
+    _check(lib.bnn_pack_sign_shift(x.data_ptr(), _dtype_code(x, "x"), rows, k, bias.data_ptr(),
+                                   _dtype_code(bias, "bias"), bias.numel(), out.data_ptr(),
+                                   _stream(x)), "bnn_pack_sign_shift")
+    return out
+
+
+def pack_sign_nchw_shift(x: torch.Tensor, bias: torch.Tensor,
+                         out: torch.Tensor | None = None) -> torch.Tensor:
+    """Shifted sign+pack of NCHW activations (the conv layer's activation prologue):
+    bit = (x[n, c, h, w] + bias[c] >= 0) -> int32 words [n, h, w, c/32]."""
+    x = _dev(x, "x")
+    bias = _bias(bias, x)
+    n, c, h, w = x.shape
+    if bias.numel() != c:
+        raise ValueError(f"bias must hold one value per channel ({c}), got {bias.numel()}")
+    if out is None:
+        out = torch.empty((n, h, w, c // 32), dtype=torch.int32, device=x.device)
+    else:
+        _dev(out, "out")
+    _check(lib.bnn_pack_sign_nchw_shift(x.data_ptr(), _dtype_code(x, "x"), n, c, h, w,
+                                        bias.data_ptr(), _dtype_code(bias, "bias"), out.data_ptr(),
+                                        _stream(x)), "bnn_pack_sign_nchw_shift")
+    return out
+
+
+def abs_mean_scale(x: torch.Tensor, factor: float, out: torch.Tensor | None = None,
+                   workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """factor * mean|x| over every element (the layers' lazy scale_a init, factor 2 or 4),
+    as a 0-dim float64 device tensor; no host synchronisation."""
+    x = _dev(x, "x")
+    if out is None:
+        out = torch.empty((), dtype=torch.float64, device=x.device)
+    need = lib.bnn_abs_mean_workspace_bytes(x.numel())
+    if workspace is None:
+        workspace = _workspace(need, x.device)
+    _check(lib.bnn_abs_mean_scale(x.data_ptr(), _dtype_code(x, "x"), x.numel(), float(factor),
+                                  out.data_ptr(), workspace.data_ptr(),
+                                  workspace.numel() * workspace.element_size(), _stream(x)),
+           "bnn_abs_mean_scale")
     return out
 
 

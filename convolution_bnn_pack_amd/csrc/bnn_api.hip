@@ -71,7 +71,7 @@ const char* bnn_status_string(int s) {
     case BNN_ERR_NULL: return "null pointer argument";
     case BNN_ERR_SHAPE: return "invalid shape (sizes, K or C not a multiple of 32, or empty conv output)";
     case BNN_ERR_DTYPE: return "dtype not allowed for this argument";
-    case BNN_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case BNN_ERR_ALIGN: return "pointer not aligned as required";
     case BNN_ERR_WORKSPACE: return "workspace missing or too small";
     case BNN_ERR_PATH: return "unknown path or path cannot run this shape";
     case BNN_ERR_HIP: return "HIP runtime error on launch";
@@ -130,6 +130,54 @@ bnn_status bnn_pack_sign_nchw(const void* x, int x_dtype, int64_t n, int64_t c, 
   if (!aligned(x, 16) || !aligned(x_packed, 4)) return BNN_ERR_ALIGN;
   return hip_status(bnn::launch_pack_nchw(x, x_dtype, n, c, h, w, x_packed,
                                           static_cast<hipStream_t>(stream)));
+}
+
+size_t bnn_abs_mean_workspace_bytes(int64_t count) {
+  if (count <= 0) return 0;
+  return (size_t)bnn::abs_mean_parts(count) * sizeof(double);
+}
+
+bnn_status bnn_pack_sign_shift(const void* x, int x_dtype, int64_t rows, int64_t k,
+                               const void* bias, int bias_dtype, int64_t bias_len,
+                               uint32_t* x_packed, void* stream) {
+  if (!float_dtype(x_dtype) || !float_dtype(bias_dtype)) return BNN_ERR_DTYPE;
+  if (rows < 0 || k <= 0 || k % 32 != 0) return BNN_ERR_SHAPE;
+  if (bias_len != 1 && bias_len != k) return BNN_ERR_SHAPE;
+  if (rows == 0) return BNN_OK;
+  if (!x || !bias || !x_packed) return BNN_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(x_packed, 4) || !aligned(bias, elem_bytes(bias_dtype)))
+    return BNN_ERR_ALIGN;
+  return hip_status(bnn::launch_pack_rows_shift(x, x_dtype, rows, k / 32, bias, bias_dtype,
+                                                bias_len == k, x_packed,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+bnn_status bnn_pack_sign_nchw_shift(const void* x, int x_dtype, int64_t n, int64_t c, int64_t h,
+                                    int64_t w, const void* bias, int bias_dtype,
+                                    uint32_t* x_packed, void* stream) {
+  if (!float_dtype(x_dtype) || !float_dtype(bias_dtype)) return BNN_ERR_DTYPE;
+  if (n < 0 || c <= 0 || c % 32 != 0 || h <= 0 || w <= 0) return BNN_ERR_SHAPE;
+  if (!int_fits(h * w) || !int_fits(n * (c / 32))) return BNN_ERR_SHAPE;
+  if (n == 0) return BNN_OK;
+  if (!x || !bias || !x_packed) return BNN_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(x_packed, 4) || !aligned(bias, elem_bytes(bias_dtype)))
+    return BNN_ERR_ALIGN;
+  return hip_status(bnn::launch_pack_nchw(x, x_dtype, n, c, h, w, x_packed,
+                                          static_cast<hipStream_t>(stream), bias, bias_dtype));
+}
+
+bnn_status bnn_abs_mean_scale(const void* x, int x_dtype, int64_t count, double factor,
+                              double* scale_out, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  if (!float_dtype(x_dtype)) return BNN_ERR_DTYPE;
+  if (count <= 0) return BNN_ERR_SHAPE;
+  if (!x || !scale_out) return BNN_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(scale_out, 8)) return BNN_ERR_ALIGN;
+  if (!workspace || workspace_bytes < bnn_abs_mean_workspace_bytes(count)) return BNN_ERR_WORKSPACE;
+  if (!aligned(workspace, 8)) return BNN_ERR_ALIGN;
+  return hip_status(bnn::launch_abs_mean(x, x_dtype, count, factor,
+                                         static_cast<double*>(workspace), scale_out,
+                                         static_cast<hipStream_t>(stream)));
 }
 
 bnn_status bnn_w_pack(const void* weight, int w_dtype, int64_t out_features, int64_t in_features,

@@ -25,6 +25,65 @@ __device__ __forceinline__ uint32_t dpp_or(uint32_t v, int ctrl_sel) {
   return v | (uint32_t)o;
 }
 
+// ---- shifted sign (the layers' activation prologue) ----
+//
+// Before the sign is taken the layers add a learnable shift bias_a to the input
+// (set_activation of BinaryConv2dCutlass / BinaryLinearCuda): one value per input
+// channel for the conv, one value for the whole layer or one per input feature for
+// the linear layer. The bit is the sign of x + b. Both operands are widened to fp32
+// (exact for f16 and bf16) and added once in fp32. The rounded sum keeps the sign
+// and the zero-ness of the exact sum: a non-zero exact sum of two fp32 values is a
+// multiple of the smallest subnormal, so it never rounds to zero while subnormals
+// are kept (the code objects of this library run with the fp32 denormal mode
+// "preserve", the compiler's default), and overflow gives an infinity of the same
+// sign. NaN operands and opposite infinities give NaN, which maps to -1 as in the
+// plain sign rule; -0 + -0 = -0 counts as >= 0.
+
+// Element e of a 16-byte vector, widened exactly to fp32.
+template <int DT>
+__device__ __forceinline__ float vec_elem(u32x4 v, int e) {
+  if constexpr (DT == kF32) {
+    return __uint_as_float(v[e]);
+  } else {
+    const uint32_t d = v[e >> 1];
+    const uint32_t h = (e & 1) ? (d >> 16) : (d & 0xFFFFu);
+    if constexpr (DT == kF16)
+      return __half2float(__ushort_as_half((unsigned short)h));
+    else
+      return __uint_as_float(h << 16);
+  }
+}
+
+// Element i of a typed array, widened exactly to fp32.
+template <int DT>
+__device__ __forceinline__ float elem_f32(const void* base, int64_t i) {
+  if constexpr (DT == kF32)
+    return reinterpret_cast<const float*>(base)[i];
+  else if constexpr (DT == kF16)
+    return __half2float(reinterpret_cast<const __half*>(base)[i]);
+  else
+    return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(base)[i] << 16);
+}
+
+// Shifted sign bits of the elements of a 16-byte vector, element e at bit e, with
+// shift b[e] (PER) or b[0] for every element. The shift must not be -0 (the callers
+// add +0 to it once, which turns -0 into +0 and leaves every other value alone), so
+// the sum is never -0 and its sign bit alone decides, once a NaN sum is turned into
+// -inf by max(s, -inf) (IEEE maxNum: the non-NaN operand; the kernels run in IEEE
+// mode and a sum is never a signalling NaN). The sign bits are gathered with
+// v_alignbit (acc << 1 | u >> 31), from the last element down, so bit e ends up as
+// the sign of element e, and the word is complemented at the end: 1 for >= 0.
+template <int DT, int EPL, bool PER>
+__device__ __forceinline__ uint32_t vec_bits_shift(u32x4 v, const float* b) {
+  uint32_t neg = 0;
+#pragma unroll
+  for (int e = EPL - 1; e >= 0; e--) {
+    const float s = fmaxf(vec_elem<DT>(v, e) + b[PER ? e : 0], -__builtin_inff());
+    neg = __builtin_amdgcn_alignbit(neg, __float_as_uint(s), 31);
+  }
+  return ~neg & ((EPL == 32) ? 0xFFFFFFFFu : ((1u << EPL) - 1u));
+}
+
 // Flat row pack. The packed output of a [rows][k] tensor with k % 32 == 0 is
 // one contiguous stream of words, word i covering elements [32i, 32i+32).
 //
@@ -73,24 +132,97 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(const u32x4* __restrict_
   }
 }
 
+// Row pack with the shift. Same lane layout as pack_rows_kernel, but a workgroup's
+// waves stay on one 64-word column chunk (blockIdx.x) and walk down the rows
+// (blockIdx.y, then the grid's row stride, two rows per step), so each lane loads the
+// shift values of its elements once and keeps them in registers for every row it
+// visits. PERCOL: one shift per column (bias[k]); otherwise bias[0] for every element.
+// Loads use clamped addresses (always in bounds) so none sits behind a branch; words
+// past the row end or rows past the last are simply not stored.
+template <int DT, int BDT, bool PERCOL>
+__global__ __launch_bounds__(256) void pack_rows_shift_kernel(const u32x4* __restrict__ x,
+                                                              const void* __restrict__ bias,
+                                                              uint32_t* __restrict__ out,
+                                                              int64_t rows, int64_t KW) {
+  constexpr int EPL = (DT == kF32) ? 4 : 8;
+  constexpr int LPW = 32 / EPL;
+  constexpr int WPI = 64 / LPW;
+  constexpr int NB = PERCOL ? EPL : 1;
+  const int lane = threadIdx.x & 63;
+  const int pos = lane % LPW;
+  const int grp = lane / LPW;
+  const int64_t q0 = (int64_t)blockIdx.x * 64;
+  float bv[LPW][NB];
+  int64_t qc[LPW];  // word of load j, clamped into the row
+#pragma unroll
+  for (int j = 0; j < LPW; j++) {
+    const int64_t q = q0 + j * WPI + grp;
+    qc[j] = q < KW ? q : KW - 1;
+#pragma unroll
+    for (int e = 0; e < NB; e++)
+      bv[j][e] = elem_f32<BDT>(bias, PERCOL ? qc[j] * 32 + pos * EPL + e : 0) + 0.0f;
+  }
+  const int64_t myq = q0 + pos * WPI + grp;
+  const int64_t step = (int64_t)gridDim.y * 4;
+  for (int64_t r = (int64_t)blockIdx.y * 4 + (threadIdx.x >> 6); r < rows; r += 2 * step) {
+    const int64_t r1 = r + step < rows ? r + step : r;
+    u32x4 v0[LPW], v1[LPW];
+#pragma unroll
+    for (int j = 0; j < LPW; j++) {
+      v0[j] = __builtin_nontemporal_load(&x[(r * KW + qc[j]) * LPW + pos]);
+      v1[j] = __builtin_nontemporal_load(&x[(r1 * KW + qc[j]) * LPW + pos]);
+    }
+    uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+    for (int j = 0; j < LPW; j++) {
+      uint32_t a0 = vec_bits_shift<DT, EPL, PERCOL>(v0[j], bv[j]) << (pos * EPL);
+      uint32_t a1 = vec_bits_shift<DT, EPL, PERCOL>(v1[j], bv[j]) << (pos * EPL);
+      a0 = dpp_or(a0, 0);
+      a1 = dpp_or(a1, 0);
+      a0 = dpp_or(a0, 1);
+      a1 = dpp_or(a1, 1);
+      if constexpr (LPW == 8) {
+        a0 = dpp_or(a0, 2);
+        a1 = dpp_or(a1, 2);
+      }
+      w0 = (pos == j) ? a0 : w0;
+      w1 = (pos == j) ? a1 : w1;
+    }
+    if (myq < KW) {
+      __builtin_nontemporal_store(w0, out + r * KW + myq);
+      if (r + step < rows) __builtin_nontemporal_store(w1, out + (r + step) * KW + myq);
+    }
+  }
+}
+
 // NCHW pack along channels. Word (b, pixel, q) collects channel 32q + j of that pixel
 // into bit j. A 256-thread workgroup packs 64*V consecutive pixels of one (b, q): lanes
 // run along the contiguous pixel axis (V pixels each, one 16-byte load when the plane
 // allows it, so each load instruction reads one channel plane contiguously), and wave w
 // takes channels 8w .. 8w+7 of the word with its eight loads in flight at once. Each wave
 // writes byte w of every pixel's word to LDS; the assembled words then leave in pixel order.
-template <int DT, int V>
+//
+// BDT >= 0: the shifted form, channel c adding bias[c] (element type BDT) before the
+// sign; the shift is uniform across a wave, so it is one scalar load per channel.
+template <int DT, int V, int BDT = -1>
 __global__ __launch_bounds__(256) void pack_nchw_kernel(const void* __restrict__ x,
                                                         uint32_t* __restrict__ out, int64_t C,
-                                                        int64_t HW, int64_t CW, int64_t nbq) {
+                                                        int64_t HW, int64_t CW, int64_t nbq,
+                                                        const void* __restrict__ bias = nullptr) {
   constexpr int ES = (DT == kF32) ? 4 : 2;
   constexpr int PIX = 64 * V;                     // pixels per workgroup
   __shared__ uint32_t words[PIX];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nchunks = (HW + PIX - 1) / PIX;
   for (int64_t bq = blockIdx.y; bq < nbq; bq += gridDim.y) {
     const int64_t b = bq / CW, q = bq - b * CW;
     const char* plane0 = reinterpret_cast<const char*>(x) + ((b * C + 32 * q + 8 * wave) * HW) * ES;
+    float shift[8];
+    if constexpr (BDT >= 0) {
+#pragma unroll
+      for (int c = 0; c < 8; c++) shift[c] = elem_f32<BDT>(bias, 32 * q + 8 * wave + c) + 0.0f;
+    }
     for (int64_t ch = blockIdx.x; ch < nchunks; ch += gridDim.x) {
       const int64_t base = ch * PIX;
       const int64_t p0 = base + (int64_t)lane * V;
@@ -99,12 +231,26 @@ __global__ __launch_bounds__(256) void pack_nchw_kernel(const void* __restrict__
       for (int c = 0; c < 8; c++) {
         const char* src = plane0 + ((int64_t)c * HW + p0) * ES;
         if constexpr (V * ES == 16) {
-          bits[c] = (p0 < HW) ? vec_bits<DT>(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src))) : 0u;
+          if (p0 < HW) {
+            const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
+            if constexpr (BDT >= 0)
+              bits[c] = vec_bits_shift<DT, V, false>(v, &shift[c]);
+            else
+              bits[c] = vec_bits<DT>(v);
+          } else {
+            bits[c] = 0u;
+          }
         } else {
           uint32_t bb = 0;
 #pragma unroll
-          for (int v = 0; v < V; v++)
-            if (p0 + v < HW) bb |= elem_pos<DT>(src, v) << v;
+          for (int v = 0; v < V; v++) {
+            if (p0 + v < HW) {
+              if constexpr (BDT >= 0)
+                bb |= (uint32_t)(elem_f32<DT>(src, v) + shift[c] >= 0.0f) << v;
+              else
+                bb |= elem_pos<DT>(src, v) << v;
+            }
+          }
           bits[c] = bb;
         }
       }
@@ -124,6 +270,78 @@ __global__ __launch_bounds__(256) void pack_nchw_kernel(const void* __restrict__
       __syncthreads();
     }
   }
+}
+
+// Sum of |x| in double (the lazy activation-scale init of the layers' set_activation:
+// scale_a = factor * mean|x| over every element while scale_a is still zero).
+// Every element is widened exactly to fp32, its magnitude converted exactly to
+// double and added in double. Stage 1: each workgroup of a fixed-size grid adds a
+// grid-strided share of the 16-byte vectors (workgroup 0 also the tail elements
+// past the last whole vector), then the workgroup's sum goes to partial[blockIdx.x].
+// Stage 2: one workgroup adds the partials in a fixed order and writes
+// factor * (sum / count). The grid size depends only on count, so the result is
+// the same on every run.
+// Sum of v over a 256-thread workgroup (fixed order); the result is valid in thread 0.
+__device__ __forceinline__ double block_sum_256(double v, double* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  double t = 0.0;
+  if (threadIdx.x == 0) t = (red[0] + red[1]) + (red[2] + red[3]);
+  return t;
+}
+
+// Sum of the magnitudes of a 16-byte vector's elements, in double (a fixed pairwise tree).
+template <int DT>
+__device__ __forceinline__ double vec_abs_sum(u32x4 v) {
+  constexpr int EPL = (DT == kF32) ? 4 : 8;
+  double t[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; e++) t[e] = (double)fabsf(vec_elem<DT>(v, e));
+#pragma unroll
+  for (int w = EPL / 2; w >= 1; w /= 2)
+#pragma unroll
+    for (int e = 0; e < w; e++) t[e] = t[e] + t[e + w];
+  return t[0];
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void abs_sum_kernel(const u32x4* __restrict__ x, int64_t nvec,
+                                                      const void* __restrict__ tail,
+                                                      int ntail, double* __restrict__ partial) {
+  constexpr int U = 4;  // vectors in flight per thread
+  __shared__ double red[4];
+  double acc0 = 0.0, acc1 = 0.0;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  for (; i + (U - 1) * stride < nvec; i += U * stride) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) v[u] = __builtin_nontemporal_load(&x[i + u * stride]);
+#pragma unroll
+    for (int u = 0; u < U; u += 2) {
+      acc0 += vec_abs_sum<DT>(v[u]);
+      acc1 += vec_abs_sum<DT>(v[u + 1]);
+    }
+  }
+  for (; i < nvec; i += stride) acc0 += vec_abs_sum<DT>(__builtin_nontemporal_load(&x[i]));
+  double acc = acc0 + acc1;
+  if (blockIdx.x == 0 && threadIdx.x < ntail) acc += (double)fabsf(elem_f32<DT>(tail, threadIdx.x));
+  const double t = block_sum_256(acc, red);
+  if (threadIdx.x == 0) partial[blockIdx.x] = t;
+}
+
+__global__ __launch_bounds__(256) void abs_mean_final_kernel(const double* __restrict__ partial,
+                                                             int nparts, double count,
+                                                             double factor,
+                                                             double* __restrict__ out) {
+  __shared__ double red[4];
+  double acc = 0.0;
+  for (int i = threadIdx.x; i < nparts; i += 256) acc += partial[i];
+  const double t = block_sum_256(acc, red);
+  if (threadIdx.x == 0) out[0] = factor * (t / count);
 }
 
 // OIHW weight pack: word (o, tap, q) collects w[o][32q + j][tap] into bit j.
@@ -162,8 +380,30 @@ hipError_t launch_pack_rows(const void* x, int dtype, int64_t total_words, uint3
   return hipGetLastError();
 }
 
+namespace {
+
+template <int DT, int V, int BDT>
+void launch_nchw_t(dim3 grid, const void* x, uint32_t* out, int64_t c, int64_t HW, int64_t CW,
+                   int64_t nbq, const void* bias, hipStream_t stream) {
+  hipLaunchKernelGGL((pack_nchw_kernel<DT, V, BDT>), grid, dim3(256), 0, stream, x, out, c, HW, CW,
+                     nbq, bias);
+}
+
+template <int DT, int V>
+void launch_nchw_b(dim3 grid, const void* x, uint32_t* out, int64_t c, int64_t HW, int64_t CW,
+                   int64_t nbq, const void* bias, int bdtype, hipStream_t stream) {
+  switch (bdtype) {
+    case kF32: launch_nchw_t<DT, V, kF32>(grid, x, out, c, HW, CW, nbq, bias, stream); break;
+    case kF16: launch_nchw_t<DT, V, kF16>(grid, x, out, c, HW, CW, nbq, bias, stream); break;
+    case kBF16: launch_nchw_t<DT, V, kBF16>(grid, x, out, c, HW, CW, nbq, bias, stream); break;
+    default: launch_nchw_t<DT, V, -1>(grid, x, out, c, HW, CW, nbq, nullptr, stream); break;
+  }
+}
+
+}  // namespace
+
 hipError_t launch_pack_nchw(const void* x, int dtype, int64_t b, int64_t c, int64_t h, int64_t w,
-                            uint32_t* out, hipStream_t stream) {
+                            uint32_t* out, hipStream_t stream, const void* bias, int bdtype) {
   const int64_t HW = h * w, CW = c / 32;
   if (b * HW * CW == 0) return hipSuccess;
   const int es = dtype == kF32 ? 4 : 2;
@@ -172,21 +412,98 @@ hipError_t launch_pack_nchw(const void* x, int dtype, int64_t b, int64_t c, int6
   const int V = vec ? vfull : 1;
   const int64_t nchunks = (HW + 64 * V - 1) / (64 * V);
   const int64_t nbq = b * CW;
-  const dim3 grid((unsigned)(nchunks < 65535 ? nchunks : 65535), (unsigned)(nbq < 65535 ? nbq : 65535)),
-      block(256);
+  const dim3 grid((unsigned)(nchunks < 65535 ? nchunks : 65535), (unsigned)(nbq < 65535 ? nbq : 65535));
+  if (!bias) bdtype = -1;
   if (vec) {
     switch (dtype) {
-      case kF32: hipLaunchKernelGGL((pack_nchw_kernel<kF32, 4>), grid, block, 0, stream, x, out, c, HW, CW, nbq); break;
-      case kF16: hipLaunchKernelGGL((pack_nchw_kernel<kF16, 8>), grid, block, 0, stream, x, out, c, HW, CW, nbq); break;
-      default: hipLaunchKernelGGL((pack_nchw_kernel<kBF16, 8>), grid, block, 0, stream, x, out, c, HW, CW, nbq); break;
+      case kF32: launch_nchw_b<kF32, 4>(grid, x, out, c, HW, CW, nbq, bias, bdtype, stream); break;
+      case kF16: launch_nchw_b<kF16, 8>(grid, x, out, c, HW, CW, nbq, bias, bdtype, stream); break;
+      default: launch_nchw_b<kBF16, 8>(grid, x, out, c, HW, CW, nbq, bias, bdtype, stream); break;
     }
   } else {
     switch (dtype) {
-      case kF32: hipLaunchKernelGGL((pack_nchw_kernel<kF32, 1>), grid, block, 0, stream, x, out, c, HW, CW, nbq); break;
-      case kF16: hipLaunchKernelGGL((pack_nchw_kernel<kF16, 1>), grid, block, 0, stream, x, out, c, HW, CW, nbq); break;
-      default: hipLaunchKernelGGL((pack_nchw_kernel<kBF16, 1>), grid, block, 0, stream, x, out, c, HW, CW, nbq); break;
+      case kF32: launch_nchw_b<kF32, 1>(grid, x, out, c, HW, CW, nbq, bias, bdtype, stream); break;
+      case kF16: launch_nchw_b<kF16, 1>(grid, x, out, c, HW, CW, nbq, bias, bdtype, stream); break;
+      default: launch_nchw_b<kBF16, 1>(grid, x, out, c, HW, CW, nbq, bias, bdtype, stream); break;
     }
   }
+  return hipGetLastError();
+}
+
+namespace {
+
+template <int DT, int BDT>
+void launch_rows_shift_t(dim3 grid, const void* x, const void* bias, bool percol, uint32_t* out,
+                         int64_t rows, int64_t KW, hipStream_t stream) {
+  const u32x4* xv = reinterpret_cast<const u32x4*>(x);
+  if (percol)
+    hipLaunchKernelGGL((pack_rows_shift_kernel<DT, BDT, true>), grid, dim3(256), 0, stream, xv, bias,
+                       out, rows, KW);
+  else
+    hipLaunchKernelGGL((pack_rows_shift_kernel<DT, BDT, false>), grid, dim3(256), 0, stream, xv,
+                       bias, out, rows, KW);
+}
+
+template <int DT>
+void launch_rows_shift_b(dim3 grid, const void* x, const void* bias, int bdtype, bool percol,
+                         uint32_t* out, int64_t rows, int64_t KW, hipStream_t stream) {
+  switch (bdtype) {
+    case kF32: launch_rows_shift_t<DT, kF32>(grid, x, bias, percol, out, rows, KW, stream); break;
+    case kF16: launch_rows_shift_t<DT, kF16>(grid, x, bias, percol, out, rows, KW, stream); break;
+    default: launch_rows_shift_t<DT, kBF16>(grid, x, bias, percol, out, rows, KW, stream); break;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_pack_rows_shift(const void* x, int dtype, int64_t rows, int64_t KW,
+                                  const void* bias, int bdtype, bool percol, uint32_t* out,
+                                  hipStream_t stream) {
+  if (rows <= 0 || KW <= 0) return hipSuccess;
+  const int64_t nchunk = (KW + 63) / 64;
+  // about 4096 workgroups in all (16 waves per compute unit), each wave walking its rows
+  int64_t gy = (4096 + nchunk - 1) / nchunk;
+  const int64_t row_groups = (rows + 3) / 4;
+  if (gy > row_groups) gy = row_groups;
+  if (gy > 65535) gy = 65535;
+  if (gy < 1) gy = 1;
+  const dim3 grid((unsigned)nchunk, (unsigned)gy);
+  switch (dtype) {
+    case kF32: launch_rows_shift_b<kF32>(grid, x, bias, bdtype, percol, out, rows, KW, stream); break;
+    case kF16: launch_rows_shift_b<kF16>(grid, x, bias, bdtype, percol, out, rows, KW, stream); break;
+    default: launch_rows_shift_b<kBF16>(grid, x, bias, bdtype, percol, out, rows, KW, stream); break;
+  }
+  return hipGetLastError();
+}
+
+int abs_mean_parts(int64_t count) {
+  // one workgroup per 2048 elements, at most 1024 (a function of count alone, so the
+  // order of the additions, hence the result, is the same on every run)
+  int64_t parts = (count + 2047) / 2048;
+  if (parts > 1024) parts = 1024;
+  if (parts < 1) parts = 1;
+  return (int)parts;
+}
+
+hipError_t launch_abs_mean(const void* x, int dtype, int64_t count, double factor, double* partial,
+                           double* out, hipStream_t stream) {
+  const int epl = dtype == kF32 ? 4 : 8;
+  const int es = dtype == kF32 ? 4 : 2;
+  const int64_t nvec = count / epl;
+  const int ntail = (int)(count - nvec * epl);
+  const void* tail = reinterpret_cast<const char*>(x) + nvec * epl * es;
+  const int parts = abs_mean_parts(count);
+  const dim3 grid((unsigned)parts), block(256);
+  const u32x4* xv = reinterpret_cast<const u32x4*>(x);
+  switch (dtype) {
+    case kF32: hipLaunchKernelGGL(abs_sum_kernel<kF32>, grid, block, 0, stream, xv, nvec, tail, ntail, partial); break;
+    case kF16: hipLaunchKernelGGL(abs_sum_kernel<kF16>, grid, block, 0, stream, xv, nvec, tail, ntail, partial); break;
+    default: hipLaunchKernelGGL(abs_sum_kernel<kBF16>, grid, block, 0, stream, xv, nvec, tail, ntail, partial); break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(abs_mean_final_kernel, dim3(1), block, 0, stream, partial, parts, (double)count,
+                     factor, out);
   return hipGetLastError();
 }
 

@@ -55,7 +55,7 @@ typedef enum {
   BNN_ERR_NULL = 1,      /* a required pointer is NULL */
   BNN_ERR_SHAPE = 2,     /* a size is negative/zero where it may not be, K or C % 32 != 0, empty conv output */
   BNN_ERR_DTYPE = 3,     /* dtype code not allowed for that argument */
-  BNN_ERR_ALIGN = 4,     /* a pointer is not 16-byte aligned */
+  BNN_ERR_ALIGN = 4,     /* a pointer is not aligned as the call requires (16 bytes for tensors read in vectors) */
   BNN_ERR_WORKSPACE = 5, /* workspace missing or smaller than the *_workspace_bytes query */
   BNN_ERR_PATH = 6,      /* unknown path code, or the forced path cannot run this shape */
   BNN_ERR_HIP = 7        /* the HIP runtime reported an error on launch */
@@ -93,6 +93,47 @@ bnn_status bnn_pack_sign(const void* x, int x_dtype, int64_t rows, int64_t k,
  * c % 32 == 0. */
 bnn_status bnn_pack_sign_nchw(const void* x, int x_dtype, int64_t n, int64_t c, int64_t h,
                               int64_t w, uint32_t* x_packed, void* stream);
+
+/* Activation prologue of the layers (set_activation of BinaryLinearCuda and BinaryConv2dCutlass):
+ * the input is shifted by the learnable bias_a before its sign is taken, and while scale_a is
+ * still zero it is initialised to 2 * mean|x| (symmetric quantization) or 4 * mean|x|.
+ *
+ * Shifted sign + pack along rows (linear layers):
+ *   x        [rows, k] in x_dtype (BNN_F32/F16/BF16), 16-byte aligned.
+ *   bias     bias_len == 1: one shift for every element; bias_len == k: bias[col] per input
+ *            feature (the linear page gives the bias no shape). bias_dtype BNN_F32/F16/BF16,
+ *            aligned to its element size.
+ *   x_packed [rows, k/32] uint32 out; bit j of word q = (x[r][32q+j] + bias >= 0), the sign of the
+ *            exact sum: -0 + -0 -> +1, a NaN operand or opposite infinities -> -1 (the sign of a
+ *            sum never depends on the precision the layer adds in).
+ * k % 32 == 0; bias_len 1 or k (else BNN_ERR_SHAPE); rows == 0 is a no-op. */
+bnn_status bnn_pack_sign_shift(const void* x, int x_dtype, int64_t rows, int64_t k,
+                               const void* bias, int bias_dtype, int64_t bias_len,
+                               uint32_t* x_packed, void* stream);
+
+/* Shifted sign + pack of NCHW activations along channels (the conv layer: bias_a has one value
+ * per input channel, broadcast over batch and pixels).
+ *   bias     [c] in bias_dtype (BNN_F32/F16/BF16), aligned to its element size.
+ *   x_packed [n, h, w, c/32]; bit j of word q = (x[n][32q+j][h][w] + bias[32q+j] >= 0), as above.
+ * Shapes and alignment as bnn_pack_sign_nchw. */
+bnn_status bnn_pack_sign_nchw_shift(const void* x, int x_dtype, int64_t n, int64_t c, int64_t h,
+                                    int64_t w, const void* bias, int bias_dtype,
+                                    uint32_t* x_packed, void* stream);
+
+/* Lazy activation scale: *scale_out (one double, device memory, 8-byte aligned) =
+ * factor * (sum_i |x[i]|) / count over count >= 1 elements of x (BNN_F32/F16/BF16, 16-byte
+ * aligned; the unshifted input, any layout). The pages use factor 2 (symmetric) or 4. Each
+ * |x[i]| is exact in double and the sum is taken in double in a fixed order that depends only on
+ * count, so the result is the same on every run (it differs from a sequential sum by at most
+ * about count * 2^-53 relative). A NaN element gives NaN, an infinite one +inf. The layer rounds
+ * the result to its dtype; that cast is the caller's.
+ *   workspace at least bnn_abs_mean_workspace_bytes(count) bytes of device memory, 8-byte aligned
+ *             (partial sums; contents on return are unspecified).
+ * count <= 0 -> BNN_ERR_SHAPE. */
+bnn_status bnn_abs_mean_scale(const void* x, int x_dtype, int64_t count, double factor,
+                              double* scale_out, void* workspace, size_t workspace_bytes,
+                              void* stream);
+size_t bnn_abs_mean_workspace_bytes(int64_t count);
 
 /* Weight pack (run once per layer, ahead of the forward).
  *   kernel_size == 0: linear weight [out_features, in_features] -> [out_features, in_features/32].

@@ -25,7 +25,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["Workload", "WORKLOADS", "make_inputs", "conv_out_size", "edge_values",
-           "random_linear_case", "random_conv_case"]
+           "random_linear_case", "random_conv_case", "make_shift"]
 
 _DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
@@ -208,3 +208,27 @@ def random_conv_case(seed: int):
     sa, sw = _draw_scale(g), _draw_scale(g)
     return dict(batch=b, c=c, h=h, w=w, o=o, ks=ks, stride=s, padding=p, dilation=d,
                 x=x, w_=wt, scale_a=sa, scale_w=sw, out_dtype=od)
+
+
+def make_shift(n: int, dtype: str, seed: int, axis_values=None) -> torch.Tensor:
+    """A learnable-shift vector of ``n`` values for the activation prologue, in ``dtype``.
+
+    Recipe: a CPU generator seeded with ``seed`` draws ``0.5 * randn(n)`` in float32. Then every
+    seventh entry is set to the negation of an input value of its own column or channel
+    (``axis_values(i)`` returns one such input as a float, or None to skip), so that the sum
+    x + bias is exactly zero there for some element; every eleventh entry takes one of the dtype's
+    special values (signed zeros, NaN, infinities, subnormals, extremes). The result is cast to
+    ``dtype`` (a cancellation survives the cast only when the input value is representable in it).
+    """
+    g = torch.Generator("cpu").manual_seed(seed)
+    b = 0.5 * torch.randn(n, generator=g, dtype=torch.float32)
+    if axis_values is not None:
+        for i in range(0, n, 7):
+            v = axis_values(i)
+            if v is not None:
+                b[i] = -v
+    b = b.to(_DT[dtype])
+    ev = edge_values(dtype)
+    for j, i in enumerate(range(3, n, 11)):
+        b[i] = ev[j % ev.numel()]
+    return b.contiguous()

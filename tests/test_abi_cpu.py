@@ -16,8 +16,13 @@ HEADER = os.path.join(ROOT, "include", "bnn.h")
 def bnn():
     lib_path = os.path.join(ROOT, "convolution_bnn_pack_amd", "libbnn.so")
     if not os.path.exists(lib_path):
-        from convolution_bnn_pack_amd import _build
-        _build.build()
+        # the build script is loaded by its path: the package itself needs the library
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "_bnn_build", os.path.join(ROOT, "convolution_bnn_pack_amd", "_build.py"))
+        build = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(build)
+        build.build()
     import convolution_bnn_pack_amd as m
     return m
 
@@ -121,6 +126,61 @@ def test_pack_argument_checks(bnn):
     assert L.bnn_w_pack(FAKE, bnn.U32_PACKED, 8, 64, 3, FAKE, None) == bnn.ERR_DTYPE
     assert L.bnn_w_pack(MISALIGNED, bnn.F32, 8, 64, 0, FAKE, None) == bnn.ERR_ALIGN
     assert L.bnn_w_pack(None, bnn.F32, 0, 64, 3, None, None) == bnn.OK
+
+
+def test_prologue_argument_checks(bnn):
+    L = bnn.lib
+    # shifted row pack: bias of one value or one per column
+    assert L.bnn_pack_sign_shift(FAKE, bnn.F16, 4, 64, FAKE, bnn.F32, 2, FAKE, None) == bnn.ERR_SHAPE
+    assert L.bnn_pack_sign_shift(FAKE, bnn.F16, 4, 48, FAKE, bnn.F32, 48, FAKE, None) == bnn.ERR_SHAPE
+    assert L.bnn_pack_sign_shift(FAKE, bnn.F16, 4, 64, FAKE, bnn.I32, 64, FAKE, None) == bnn.ERR_DTYPE
+    assert L.bnn_pack_sign_shift(FAKE, bnn.U32_PACKED, 4, 64, FAKE, bnn.F32, 1, FAKE, None) == bnn.ERR_DTYPE
+    assert L.bnn_pack_sign_shift(FAKE, bnn.F16, 4, 64, None, bnn.F32, 1, FAKE, None) == bnn.ERR_NULL
+    assert L.bnn_pack_sign_shift(FAKE, bnn.F16, 4, 64, FAKE + 2, bnn.F32, 64, FAKE, None) == bnn.ERR_ALIGN
+    assert L.bnn_pack_sign_shift(MISALIGNED, bnn.F16, 4, 64, FAKE, bnn.F32, 64, FAKE, None) == bnn.ERR_ALIGN
+    assert L.bnn_pack_sign_shift(None, bnn.F16, 0, 64, None, bnn.F32, 64, None, None) == bnn.OK
+    # shifted NCHW pack: one bias per channel
+    assert L.bnn_pack_sign_nchw_shift(FAKE, bnn.F32, 1, 40, 4, 4, FAKE, bnn.F32, FAKE, None) == bnn.ERR_SHAPE
+    assert L.bnn_pack_sign_nchw_shift(FAKE, bnn.F32, 1, 32, 4, 4, FAKE, 5, FAKE, None) == bnn.ERR_DTYPE
+    assert L.bnn_pack_sign_nchw_shift(FAKE, bnn.F32, 1, 32, 4, 4, None, bnn.F16, FAKE, None) == bnn.ERR_NULL
+    assert L.bnn_pack_sign_nchw_shift(FAKE, bnn.F32, 1, 32, 4, 4, FAKE + 1, bnn.F16, FAKE, None) == bnn.ERR_ALIGN
+    assert L.bnn_pack_sign_nchw_shift(None, bnn.F32, 0, 32, 4, 4, None, bnn.F16, None, None) == bnn.OK
+    # lazy scale: count >= 1, a workspace of the queried size
+    need = L.bnn_abs_mean_workspace_bytes(1 << 20)
+    assert need == 512 * 8 and L.bnn_abs_mean_workspace_bytes(1 << 30) == 1024 * 8
+    assert L.bnn_abs_mean_workspace_bytes(1) == 8 and L.bnn_abs_mean_workspace_bytes(0) == 0
+    assert L.bnn_abs_mean_scale(FAKE, bnn.F32, 0, 2.0, FAKE, FAKE, need, None) == bnn.ERR_SHAPE
+    assert L.bnn_abs_mean_scale(FAKE, bnn.I32, 1 << 20, 2.0, FAKE, FAKE, need, None) == bnn.ERR_DTYPE
+    assert L.bnn_abs_mean_scale(FAKE, bnn.F32, 1 << 20, 2.0, None, FAKE, need, None) == bnn.ERR_NULL
+    assert L.bnn_abs_mean_scale(FAKE, bnn.F32, 1 << 20, 2.0, FAKE + 4, FAKE, need, None) == bnn.ERR_ALIGN
+    assert L.bnn_abs_mean_scale(FAKE, bnn.F32, 1 << 20, 2.0, FAKE, FAKE, need - 1, None) == bnn.ERR_WORKSPACE
+    assert L.bnn_abs_mean_scale(FAKE, bnn.F32, 1 << 20, 2.0, FAKE, None, need, None) == bnn.ERR_WORKSPACE
+
+
+def test_shift_kernels_keep_subnormals():
+    """The shifted sign adds in fp32 and relies on subnormal results being kept: every kernel of
+    the packing code object must run with the fp32 denormal mode 'preserve' (3) in its kernel
+    descriptor (the descriptor sets the mode at dispatch, whatever the caller's state)."""
+    import subprocess
+    import sys
+    import tempfile
+    sys.path.insert(0, os.path.join(ROOT, "convolution_bnn_pack_amd"))
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "_bnn_build", os.path.join(ROOT, "convolution_bnn_pack_amd", "_build.py"))
+    build = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(build)
+    with tempfile.TemporaryDirectory() as td:
+        asm = os.path.join(td, "pack.s")
+        r = subprocess.run([build.HIPCC, *build.FLAGS, "--cuda-device-only", "-S",
+                            os.path.join(build.CSRC, "pack.hip"), "-o", asm],
+                           capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
+        text = open(asm).read()
+    modes = re.findall(r"\.amdhsa_float_denorm_mode_32\s+(\d+)", text)
+    kernels = re.findall(r"\.amdhsa_kernel\s+(\S+)", text)
+    assert any("pack_rows_shift_kernel" in k for k in kernels)
+    assert len(modes) == len(kernels) and set(modes) == {"3"}
 
 
 def test_workspace_queries(bnn):
