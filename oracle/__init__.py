@@ -28,8 +28,10 @@ _lib = None
 
 
 def build(force: bool = True) -> str:
-    """Compile liboracle.so with gcc; returns its path."""
-    if force or not os.path.exists(_LIB):
+    """Compile liboracle.so with gcc (also without force when the source is newer than the
+    library); returns its path."""
+    stale = not os.path.exists(_LIB) or os.path.getmtime(_SRC) > os.path.getmtime(_LIB)
+    if force or stale:
         tmp = _LIB + ".tmp"
         compile_library(_SRC, tmp)
         os.replace(tmp, _LIB)
@@ -107,34 +109,38 @@ def _words(n: int) -> torch.Tensor:
     return torch.empty(n, dtype=torch.int32)
 
 
+def _nw(k: int) -> int:
+    """Words that hold k signs (the last one partly, its missing bits 0)."""
+    return (k + 31) // 32
+
+
 def pack_rows(x: torch.Tensor) -> torch.Tensor:
-    """x [rows, k] -> int32 words [rows, k/32] (bit j of word q = x[r, 32q+j] >= 0)."""
+    """x [rows, k] -> int32 words [rows, ceil(k/32)] (bit j of word q = x[r, 32q+j] >= 0;
+    bits past k are 0)."""
     x = _cpu(x)
     rows, k = x.shape
-    assert k % 32 == 0
-    out = _words(rows * (k // 32))
+    out = _words(rows * _nw(k))
     _load().oracle_pack_rows(x.data_ptr(), _code(x), rows, k, out.data_ptr())
-    return out.view(rows, k // 32)
+    return out.view(rows, _nw(k))
 
 
 def pack_nchw(x: torch.Tensor) -> torch.Tensor:
-    """x [b, c, h, w] -> int32 words [b, h, w, c/32]."""
+    """x [b, c, h, w] -> int32 words [b, h, w, ceil(c/32)] (channel bits past c are 0)."""
     x = _cpu(x)
     b, c, h, w = x.shape
-    assert c % 32 == 0
-    out = _words(b * h * w * (c // 32))
+    out = _words(b * h * w * _nw(c))
     _load().oracle_pack_nchw(x.data_ptr(), _code(x), b, c, h, w, out.data_ptr())
-    return out.view(b, h, w, c // 32)
+    return out.view(b, h, w, _nw(c))
 
 
 def pack_conv_weight(w: torch.Tensor) -> torch.Tensor:
-    """OIHW w [o, c, k, k] -> int32 words [o, k, k, c/32]."""
+    """OIHW w [o, c, k, k] -> int32 words [o, k, k, ceil(c/32)] (channel bits past c are 0)."""
     w = _cpu(w)
     o, c, kh, kw = w.shape
-    assert kh == kw and c % 32 == 0
-    out = _words(o * kh * kw * (c // 32))
+    assert kh == kw
+    out = _words(o * kh * kw * _nw(c))
     _load().oracle_pack_conv_weight(w.data_ptr(), _code(w), o, c, kh, out.data_ptr())
-    return out.view(o, kh, kw, c // 32)
+    return out.view(o, kh, kw, _nw(c))
 
 
 def _index(idx, limit):
@@ -209,26 +215,26 @@ def scale(acc: torch.Tensor, scale_a: float, scale_w: float) -> torch.Tensor:
 
 
 def pack_rows_shift(x: torch.Tensor, bias: torch.Tensor) -> torch.Tensor:
-    """x [rows, k] shifted by bias (one value, or [k]) -> int32 words [rows, k/32];
-    bit j of word q = (x[r, 32q+j] + bias >= 0)."""
+    """x [rows, k] shifted by bias (one value, or [k]) -> int32 words [rows, ceil(k/32)];
+    bit j of word q = (x[r, 32q+j] + bias >= 0); bits past k are 0."""
     x, bias = _cpu(x), _cpu(bias)
     rows, k = x.shape
-    assert k % 32 == 0 and bias.numel() in (1, k)
-    out = _words(rows * (k // 32))
+    assert bias.numel() in (1, k)
+    out = _words(rows * _nw(k))
     _load().oracle_pack_rows_shift(x.data_ptr(), _code(x), rows, k, bias.data_ptr(), _code(bias),
                                    bias.numel(), out.data_ptr())
-    return out.view(rows, k // 32)
+    return out.view(rows, _nw(k))
 
 
 def pack_nchw_shift(x: torch.Tensor, bias: torch.Tensor) -> torch.Tensor:
-    """x [b, c, h, w] shifted by bias[c] -> int32 words [b, h, w, c/32]."""
+    """x [b, c, h, w] shifted by bias[c] -> int32 words [b, h, w, ceil(c/32)]."""
     x, bias = _cpu(x), _cpu(bias)
     b, c, h, w = x.shape
-    assert c % 32 == 0 and bias.numel() == c
-    out = _words(b * h * w * (c // 32))
+    assert bias.numel() == c
+    out = _words(b * h * w * _nw(c))
     _load().oracle_pack_nchw_shift(x.data_ptr(), _code(x), b, c, h, w, bias.data_ptr(), _code(bias),
                                    out.data_ptr())
-    return out.view(b, h, w, c // 32)
+    return out.view(b, h, w, _nw(c))
 
 
 def abs_mean_scale(x: torch.Tensor, factor: float) -> float:

@@ -21,7 +21,11 @@
  *    bit-packing kernel: BinaryConv2dCutlass.generate_quantized_weight on
  *    the qconv/binary/cutlass/layer page, BinaryLinearCuda.w_pack on the
  *    BinaryLinearCuda page. The word width 32 and the bit order are this
- *    build's reading; the pages fix neither.)
+ *    build's reading; the pages fix neither.) A reduction length that is
+ *    not a whole number of words (the CUTLASS layer asserts that it is)
+ *    leaves the missing bits of the last word 0: in both operands, so a
+ *    XOR of the two sets no bit there, and the contraction itself still
+ *    runs over the true length.
  *
  *  - Linear forward: acc[m][n] = sum_k sgn(x[m][k]) * sgn(W[n][k]), then
  *    y = acc * (scale_a * scale_w): the binary product multiplied by both
@@ -116,30 +120,32 @@ void oracle_sign(const void *x, int dtype, int64_t count, float *s) {
   for (int64_t i = 0; i < count; i++) s[i] = sgn(widen(x, dtype, i));
 }
 
-/* Row-major x[rows][k] -> words out[rows][k/32]; bit j of word q is 1 iff x[r][32q+j] >= 0. */
+/* Row-major x[rows][k] -> words out[rows][ceil(k/32)]; bit j of word q is 1 iff 32q+j < k and
+ * x[r][32q+j] >= 0 (a row that does not fill its last word leaves the missing bits 0). */
 void oracle_pack_rows(const void *x, int dtype, int64_t rows, int64_t k, uint32_t *out) {
-  int64_t kw = k / 32;
+  int64_t kw = (k + 31) / 32;
 #pragma omp parallel for schedule(static)
   for (int64_t r = 0; r < rows; r++)
     for (int64_t q = 0; q < kw; q++) {
       uint32_t word = 0;
-      for (int j = 0; j < 32; j++)
+      for (int j = 0; j < 32 && 32 * q + j < k; j++)
         if (sgn(widen(x, dtype, r * k + 32 * q + j)) > 0.0f) word |= (uint32_t)1 << j;
       out[r * kw + q] = word;
     }
 }
 
-/* NCHW x[b][c][h][w] -> words out[b][h][w][c/32]; bit j of word q is 1 iff x[b][32q+j][h][w] >= 0. */
+/* NCHW x[b][c][h][w] -> words out[b][h][w][ceil(C/32)]; bit j of word q is 1 iff 32q+j < C and
+ * x[b][32q+j][h][w] >= 0. */
 void oracle_pack_nchw(const void *x, int dtype, int64_t B, int64_t C, int64_t H, int64_t W,
                       uint32_t *out) {
-  int64_t cw = C / 32;
+  int64_t cw = (C + 31) / 32;
 #pragma omp parallel for schedule(static)
   for (int64_t b = 0; b < B; b++)
     for (int64_t ih = 0; ih < H; ih++)
       for (int64_t iw = 0; iw < W; iw++)
         for (int64_t q = 0; q < cw; q++) {
           uint32_t word = 0;
-          for (int j = 0; j < 32; j++) {
+          for (int j = 0; j < 32 && 32 * q + j < C; j++) {
             int64_t idx = ((b * C + 32 * q + j) * H + ih) * W + iw;
             if (sgn(widen(x, dtype, idx)) > 0.0f) word |= (uint32_t)1 << j;
           }
@@ -147,17 +153,18 @@ void oracle_pack_nchw(const void *x, int dtype, int64_t B, int64_t C, int64_t H,
         }
 }
 
-/* OIHW weight w[o][c][kh][kw] -> words out[o][kh][kw][c/32]; bit j of word q is 1 iff w[o][32q+j][kh][kw] >= 0. */
+/* OIHW weight w[o][c][kh][kw] -> words out[o][kh][kw][ceil(C/32)]; bit j of word q is 1 iff
+ * 32q+j < C and w[o][32q+j][kh][kw] >= 0. */
 void oracle_pack_conv_weight(const void *w, int dtype, int64_t O, int64_t C, int64_t ks,
                              uint32_t *out) {
-  int64_t cw = C / 32;
+  int64_t cw = (C + 31) / 32;
 #pragma omp parallel for schedule(static)
   for (int64_t o = 0; o < O; o++)
     for (int64_t kh = 0; kh < ks; kh++)
       for (int64_t kx = 0; kx < ks; kx++)
         for (int64_t q = 0; q < cw; q++) {
           uint32_t word = 0;
-          for (int j = 0; j < 32; j++) {
+          for (int j = 0; j < 32 && 32 * q + j < C; j++) {
             int64_t idx = ((o * C + 32 * q + j) * ks + kh) * ks + kx;
             if (sgn(widen(w, dtype, idx)) > 0.0f) word |= (uint32_t)1 << j;
           }
@@ -308,12 +315,12 @@ static float sgn_shift(float v, float b) {
  * word q is 1 iff x[r][32q+j] + bias >= 0. */
 void oracle_pack_rows_shift(const void *x, int dtype, int64_t rows, int64_t k, const void *bias,
                             int bdtype, int64_t blen, uint32_t *out) {
-  int64_t kw = k / 32;
+  int64_t kw = (k + 31) / 32;
 #pragma omp parallel for schedule(static)
   for (int64_t r = 0; r < rows; r++)
     for (int64_t q = 0; q < kw; q++) {
       uint32_t word = 0;
-      for (int j = 0; j < 32; j++) {
+      for (int j = 0; j < 32 && 32 * q + j < k; j++) {
         int64_t col = 32 * q + j;
         float b = widen(bias, bdtype, blen == 1 ? 0 : col);
         if (sgn_shift(widen(x, dtype, r * k + col), b) > 0.0f) word |= (uint32_t)1 << j;
@@ -326,14 +333,14 @@ void oracle_pack_rows_shift(const void *x, int dtype, int64_t rows, int64_t k, c
  * q of pixel (b, h, w) is 1 iff x[b][32q+j][h][w] + bias[32q+j] >= 0. */
 void oracle_pack_nchw_shift(const void *x, int dtype, int64_t B, int64_t C, int64_t H, int64_t W,
                             const void *bias, int bdtype, uint32_t *out) {
-  int64_t cw = C / 32;
+  int64_t cw = (C + 31) / 32;
 #pragma omp parallel for schedule(static)
   for (int64_t b = 0; b < B; b++)
     for (int64_t ih = 0; ih < H; ih++)
       for (int64_t iw = 0; iw < W; iw++)
         for (int64_t q = 0; q < cw; q++) {
           uint32_t word = 0;
-          for (int j = 0; j < 32; j++) {
+          for (int j = 0; j < 32 && 32 * q + j < C; j++) {
             int64_t c = 32 * q + j;
             int64_t idx = ((b * C + c) * H + ih) * W + iw;
             if (sgn_shift(widen(x, dtype, idx), widen(bias, bdtype, c)) > 0.0f) word |= (uint32_t)1 << j;

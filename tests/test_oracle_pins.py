@@ -333,3 +333,64 @@ def test_workload_outputs_library_and_invariants(oracle_lib, name):
     if name == "linear_64x256x512_f32":
         # scale_a * scale_w = 0.125 is dyadic: the float32 output is exact
         assert torch.equal(y.float().double(), y)
+
+
+# ---------------------------------------------------------------- reduction tails (not whole words)
+
+def _bits(words, n):
+    w = words.numpy().astype(np.uint32).astype(np.int64)
+    return ((w[..., None] >> np.arange(32)) & 1).reshape(*w.shape[:-1], -1)[..., :n], \
+        ((w[..., None] >> np.arange(32)) & 1).reshape(*w.shape[:-1], -1)[..., n:]
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.float16, torch.bfloat16])
+def test_pack_rows_tail_bits(oracle_lib, dt):
+    """A row of k signs fills ceil(k/32) words; bits 0..k-1 follow torch's compare, the rest are 0,
+    and the words equal the whole-word pack of the row padded with -1 (a plain value whose bit is 0)."""
+    g = torch.Generator().manual_seed(61)
+    for k in list(range(1, 70)) + [95, 96, 97, 1000]:
+        x = synth.inject_edges(torch.randn((3, k), generator=g).to(dt), k, max(1, k // 7))
+        words = oracle_lib.pack_rows(x)
+        assert words.shape == (3, (k + 31) // 32)
+        real, tail = _bits(words, k)
+        assert np.array_equal(real, (x >= 0).numpy().astype(np.int64)), k
+        assert not tail.any(), k
+        kp = 32 * ((k + 31) // 32)
+        padded = torch.cat([x, torch.full((3, kp - k), -1.0, dtype=dt)], dim=1).contiguous()
+        assert torch.equal(words, oracle_lib.pack_rows(padded)), k
+
+
+def test_pack_nchw_and_weight_tail_bits(oracle_lib):
+    g = torch.Generator().manual_seed(62)
+    for c in [1, 3, 17, 31, 33, 40, 63, 65, 100]:
+        x = torch.randn((2, c, 3, 4), generator=g)
+        words = oracle_lib.pack_nchw(x)                                   # [2, 3, 4, ceil(c/32)]
+        real, tail = _bits(words, c)
+        assert np.array_equal(real, (x >= 0).permute(0, 2, 3, 1).numpy().astype(np.int64)), c
+        assert not tail.any()
+        cp = 32 * ((c + 31) // 32)
+        xp = torch.cat([x, torch.full((2, cp - c, 3, 4), -1.0)], dim=1).contiguous()
+        assert torch.equal(words, oracle_lib.pack_nchw(xp))
+        w = torch.randn((5, c, 3, 3), generator=g)
+        ww = oracle_lib.pack_conv_weight(w)                               # [5, 3, 3, ceil(c/32)]
+        real, tail = _bits(ww, c)
+        assert np.array_equal(real, (w >= 0).permute(0, 2, 3, 1).numpy().astype(np.int64)), c
+        assert not tail.any()
+        bias = 0.3 * torch.randn(c, generator=g)
+        sh = oracle_lib.pack_nchw_shift(x, bias)
+        real, tail = _bits(sh, c)
+        assert np.array_equal(real, ((x + bias.view(1, -1, 1, 1)) >= 0).permute(0, 2, 3, 1).numpy().astype(np.int64))
+        assert not tail.any()
+
+
+def test_tail_popcount_identity(oracle_lib):
+    """With the missing bits 0 in both operands, K - 2*popcount(a XOR w) over the ceil(K/32) words
+    is the +-1 dot product over the true K (the oracle's contraction), for K = 1..100."""
+    g = torch.Generator().manual_seed(63)
+    for k in range(1, 101):
+        x = torch.randn((4, k), generator=g)
+        w = torch.randn((6, k), generator=g)
+        a = oracle_lib.pack_rows(x).numpy().astype(np.uint32)
+        b = oracle_lib.pack_rows(w).numpy().astype(np.uint32)
+        pop = np.vectorize(lambda v: bin(int(v)).count("1"))(a[:, None, :] ^ b[None, :, :]).sum(-1)
+        assert np.array_equal(k - 2 * pop, oracle_lib.linear_acc(x, w).numpy()), k
