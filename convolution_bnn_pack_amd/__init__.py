@@ -7,10 +7,10 @@ allocations) and for the current HIP stream. There is no fallback: if
 libbnn.so is missing, importing the module raises.
 
 Entry points mirror the C ABI:
-  pack_sign(x)              rows of x -> packed int32 words [rows, k/32]
-  pack_sign_nchw(x)         NCHW x -> packed words [n, h, w, c/32]
+  pack_sign(x)              rows of x -> packed int32 words [rows, ceil(k/32)]
+  pack_sign_nchw(x)         NCHW x -> packed words [n, h, w, ceil(c/32)]
   pack_sign_shift(x, bias)  rows of x + bias (one value or one per column) -> packed words
-  pack_sign_nchw_shift(x, bias)  NCHW x + bias[c] -> packed words [n, h, w, c/32]
+  pack_sign_nchw_shift(x, bias)  NCHW x + bias[c] -> packed words [n, h, w, ceil(c/32)]
   abs_mean_scale(x, factor) factor * mean|x| as a 0-dim float64 device tensor
   w_pack(weight)            linear [out, in] or OIHW conv weight -> packed words
   gemm(x, w_packed, ...)    binary linear forward (bitorch-engine BinaryLinearForward)
@@ -115,13 +115,18 @@ def _dtype_code(t: torch.Tensor, name: str) -> int:
     return _DT[t.dtype]
 
 
+def words(n: int) -> int:
+    """Packed words holding n signs (the last one partly when n % 32 != 0)."""
+    return (n + 31) // 32
+
+
 def pack_sign(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
-    """Sign+pack along the last axis: [rows, k] -> int32 words [rows, k/32]."""
+    """Sign+pack along the last axis: [rows, k] -> int32 words [rows, ceil(k/32)]."""
     x = _dev(x, "x")
     k = x.shape[-1]
     rows = x.numel() // k if k else 0
     if out is None:
-        out = torch.empty((*x.shape[:-1], k // 32), dtype=torch.int32, device=x.device)
+        out = torch.empty((*x.shape[:-1], words(k)), dtype=torch.int32, device=x.device)
     else:
         _dev(out, "out")
     _check(lib.bnn_pack_sign(x.data_ptr(), _dtype_code(x, "x"), rows, k, out.data_ptr(), _stream(x)),
@@ -130,11 +135,11 @@ def pack_sign(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
 
 
 def pack_sign_nchw(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
-    """Sign+pack of NCHW activations along channels: [n, c, h, w] -> int32 words [n, h, w, c/32]."""
+    """Sign+pack of NCHW activations along channels: [n, c, h, w] -> int32 words [n, h, w, ceil(c/32)]."""
     x = _dev(x, "x")
     n, c, h, w = x.shape
     if out is None:
-        out = torch.empty((n, h, w, c // 32), dtype=torch.int32, device=x.device)
+        out = torch.empty((n, h, w, words(c)), dtype=torch.int32, device=x.device)
     else:
         _dev(out, "out")
     _check(lib.bnn_pack_sign_nchw(x.data_ptr(), _dtype_code(x, "x"), n, c, h, w, out.data_ptr(),
@@ -157,7 +162,7 @@ def pack_sign_shift(x: torch.Tensor, bias: torch.Tensor, out: torch.Tensor | Non
     k = x.shape[-1]
     rows = x.numel() // k if k else 0
     if out is None:
-        out = torch.empty((*x.shape[:-1], k // 32), dtype=torch.int32, device=x.device)
+        out = torch.empty((*x.shape[:-1], words(k)), dtype=torch.int32, device=x.device)
     else:
         _dev(out, "out")
     _check(lib.bnn_pack_sign_shift(x.data_ptr(), _dtype_code(x, "x"), rows, k, bias.data_ptr(),
@@ -169,14 +174,14 @@ def pack_sign_shift(x: torch.Tensor, bias: torch.Tensor, out: torch.Tensor | Non
 def pack_sign_nchw_shift(x: torch.Tensor, bias: torch.Tensor,
                          out: torch.Tensor | None = None) -> torch.Tensor:
     """Shifted sign+pack of NCHW activations (the conv layer's activation prologue):
-    bit = (x[n, c, h, w] + bias[c] >= 0) -> int32 words [n, h, w, c/32]."""
+    bit = (x[n, c, h, w] + bias[c] >= 0) -> int32 words [n, h, w, ceil(c/32)]."""
     x = _dev(x, "x")
     bias = _bias(bias, x)
     n, c, h, w = x.shape
     if bias.numel() != c:
         raise ValueError(f"bias must hold one value per channel ({c}), got {bias.numel()}")
     if out is None:
-        out = torch.empty((n, h, w, c // 32), dtype=torch.int32, device=x.device)
+        out = torch.empty((n, h, w, words(c)), dtype=torch.int32, device=x.device)
     else:
         _dev(out, "out")
     _check(lib.bnn_pack_sign_nchw_shift(x.data_ptr(), _dtype_code(x, "x"), n, c, h, w,
@@ -208,13 +213,13 @@ def w_pack(weight: torch.Tensor) -> torch.Tensor:
     if weight.dim() == 2:
         o, i = weight.shape
         ks = 0
-        shape = (o, i // 32)
+        shape = (o, words(i))
     elif weight.dim() == 4:
         o, i, kh, kw = weight.shape
         if kh != kw:
             raise ValueError("square kernels only")
         ks = kh
-        shape = (o, ks, ks, i // 32)
+        shape = (o, ks, ks, words(i))
     else:
         raise ValueError("weight must be 2-D (linear) or 4-D OIHW (conv)")
     out = torch.empty(shape, dtype=torch.int32, device=weight.device)
@@ -232,8 +237,9 @@ def gemm(x: torch.Tensor, w_packed: torch.Tensor, scale_a: float, scale_w: float
          workspace: torch.Tensor | None = None) -> torch.Tensor:
     """Binary linear forward: out = scale_a*scale_w * sgn(x) @ sgn(W)^T.
 
-    x is [m, k] float (packed here) or int32 [m, k/32] already packed (then k
-    defaults to 32 * x.shape[1]). w_packed is int32 [n, k/32] from w_pack.
+    x is [m, k] float (packed here) or int32 [m, ceil(k/32)] already packed (then k
+    defaults to 32 * x.shape[1]; pass k when it is not a multiple of 32). w_packed is
+    int32 [n, ceil(k/32)] from w_pack.
     out_dtype defaults to x's dtype (float32 for packed x); torch.int32 gives
     the raw accumulators.
     """
@@ -270,8 +276,8 @@ def conv2d(x: torch.Tensor, w_packed: torch.Tensor, scale_a: float, scale_w: flo
            workspace: torch.Tensor | None = None) -> torch.Tensor:
     """Binary conv2d forward, NCHW in and out; padded taps contribute 0.
 
-    x is [n, c, h, w] float, or int32 [n, h, w, c/32] already packed by
-    pack_sign_nchw. w_packed is int32 [o, k, k, c/32] from w_pack.
+    x is [n, c, h, w] float, or int32 [n, h, w, ceil(c/32)] already packed by
+    pack_sign_nchw. w_packed is int32 [o, k, k, ceil(c/32)] from w_pack.
     """
     x = _dev(x, "x")
     w_packed = _dev(w_packed, "w_packed")

@@ -48,6 +48,20 @@ int auto_path(int64_t k) { return k <= bnn::kMaxFp4K ? BNN_PATH_MFMA_FP4 : BNN_P
 
 bool int_fits(int64_t v) { return v >= 0 && v <= 0x7FFFFFFFLL; }
 
+// Words holding n signs: the last one partly when n % 32 != 0 (its missing bits are 0).
+int64_t words_of(int64_t n) { return (n + 31) / 32; }
+
+// Row sign+pack of any row length: the 16-byte vector kernels when rows are whole words and
+// the tensor is 16-byte aligned, the one-element-per-lane kernel otherwise.
+hipError_t pack_rows_any(const void* x, int dtype, int64_t rows, int64_t k, const void* bias,
+                         int bdtype, bool percol, uint32_t* out, hipStream_t s) {
+  if (k % 32 == 0 && aligned(x, 16)) {
+    if (!bias) return bnn::launch_pack_rows(x, dtype, rows * (k / 32), out, s);
+    return bnn::launch_pack_rows_shift(x, dtype, rows, k / 32, bias, bdtype, percol, out, s);
+  }
+  return bnn::launch_pack_rows_ragged(x, dtype, rows, k, bias, bdtype, percol, out, s);
+}
+
 bool path_known(int path) {
   return path == BNN_PATH_AUTO || path == BNN_PATH_XOR || path == BNN_PATH_MFMA ||
          path == BNN_PATH_MFMA_FP4;
@@ -69,7 +83,7 @@ const char* bnn_status_string(int s) {
   switch (s) {
     case BNN_OK: return "ok";
     case BNN_ERR_NULL: return "null pointer argument";
-    case BNN_ERR_SHAPE: return "invalid shape (sizes, K or C not a multiple of 32, or empty conv output)";
+    case BNN_ERR_SHAPE: return "invalid shape (sizes, bias length, or empty conv output)";
     case BNN_ERR_DTYPE: return "dtype not allowed for this argument";
     case BNN_ERR_ALIGN: return "pointer not aligned as required";
     case BNN_ERR_WORKSPACE: return "workspace missing or too small";
@@ -83,12 +97,12 @@ int bnn_last_path(void) { return g_last_path; }
 
 size_t bnn_gemm_workspace_bytes(int64_t m, int64_t k, int x_dtype) {
   if (x_dtype == BNN_U32_PACKED || m <= 0 || k <= 0) return 0;
-  return (size_t)m * (size_t)(k / 32) * 4u;
+  return (size_t)m * (size_t)words_of(k) * 4u;
 }
 
 size_t bnn_conv2d_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w, int x_dtype) {
   if (x_dtype == BNN_U32_PACKED || n <= 0 || c <= 0 || h <= 0 || w <= 0) return 0;
-  return (size_t)n * (size_t)h * (size_t)w * (size_t)(c / 32) * 4u;
+  return (size_t)n * (size_t)h * (size_t)w * (size_t)words_of(c) * 4u;
 }
 
 int bnn_gemm_auto_path(int64_t m, int64_t n, int64_t k) {
@@ -112,19 +126,19 @@ int bnn_conv2d_auto_path(int64_t n, int64_t c, int64_t h, int64_t w, int64_t out
 bnn_status bnn_pack_sign(const void* x, int x_dtype, int64_t rows, int64_t k, uint32_t* x_packed,
                          void* stream) {
   if (!float_dtype(x_dtype)) return BNN_ERR_DTYPE;
-  if (rows < 0 || k <= 0 || k % 32 != 0) return BNN_ERR_SHAPE;
+  if (rows < 0 || k <= 0) return BNN_ERR_SHAPE;
   if (rows == 0) return BNN_OK;
   if (!x || !x_packed) return BNN_ERR_NULL;
-  if (!aligned(x, 16) || !aligned(x_packed, 4)) return BNN_ERR_ALIGN;
-  return hip_status(bnn::launch_pack_rows(x, x_dtype, rows * (k / 32), x_packed,
-                                          static_cast<hipStream_t>(stream)));
+  if (!aligned(x, elem_bytes(x_dtype)) || !aligned(x_packed, 4)) return BNN_ERR_ALIGN;
+  return hip_status(pack_rows_any(x, x_dtype, rows, k, nullptr, 0, false, x_packed,
+                                  static_cast<hipStream_t>(stream)));
 }
 
 bnn_status bnn_pack_sign_nchw(const void* x, int x_dtype, int64_t n, int64_t c, int64_t h,
                               int64_t w, uint32_t* x_packed, void* stream) {
   if (!float_dtype(x_dtype)) return BNN_ERR_DTYPE;
-  if (n < 0 || c <= 0 || c % 32 != 0 || h <= 0 || w <= 0) return BNN_ERR_SHAPE;
-  if (!int_fits(h * w) || !int_fits(n * (c / 32))) return BNN_ERR_SHAPE;
+  if (n < 0 || c <= 0 || h <= 0 || w <= 0) return BNN_ERR_SHAPE;
+  if (!int_fits(h * w) || !int_fits(n * words_of(c))) return BNN_ERR_SHAPE;
   if (n == 0) return BNN_OK;
   if (!x || !x_packed) return BNN_ERR_NULL;
   if (!aligned(x, 16) || !aligned(x_packed, 4)) return BNN_ERR_ALIGN;
@@ -141,23 +155,23 @@ bnn_status bnn_pack_sign_shift(const void* x, int x_dtype, int64_t rows, int64_t
                                const void* bias, int bias_dtype, int64_t bias_len,
                                uint32_t* x_packed, void* stream) {
   if (!float_dtype(x_dtype) || !float_dtype(bias_dtype)) return BNN_ERR_DTYPE;
-  if (rows < 0 || k <= 0 || k % 32 != 0) return BNN_ERR_SHAPE;
+  if (rows < 0 || k <= 0) return BNN_ERR_SHAPE;
   if (bias_len != 1 && bias_len != k) return BNN_ERR_SHAPE;
   if (rows == 0) return BNN_OK;
   if (!x || !bias || !x_packed) return BNN_ERR_NULL;
-  if (!aligned(x, 16) || !aligned(x_packed, 4) || !aligned(bias, elem_bytes(bias_dtype)))
+  if (!aligned(x, elem_bytes(x_dtype)) || !aligned(x_packed, 4) ||
+      !aligned(bias, elem_bytes(bias_dtype)))
     return BNN_ERR_ALIGN;
-  return hip_status(bnn::launch_pack_rows_shift(x, x_dtype, rows, k / 32, bias, bias_dtype,
-                                                bias_len == k, x_packed,
-                                                static_cast<hipStream_t>(stream)));
+  return hip_status(pack_rows_any(x, x_dtype, rows, k, bias, bias_dtype, bias_len == k && k > 1,
+                                  x_packed, static_cast<hipStream_t>(stream)));
 }
 
 bnn_status bnn_pack_sign_nchw_shift(const void* x, int x_dtype, int64_t n, int64_t c, int64_t h,
                                     int64_t w, const void* bias, int bias_dtype,
                                     uint32_t* x_packed, void* stream) {
   if (!float_dtype(x_dtype) || !float_dtype(bias_dtype)) return BNN_ERR_DTYPE;
-  if (n < 0 || c <= 0 || c % 32 != 0 || h <= 0 || w <= 0) return BNN_ERR_SHAPE;
-  if (!int_fits(h * w) || !int_fits(n * (c / 32))) return BNN_ERR_SHAPE;
+  if (n < 0 || c <= 0 || h <= 0 || w <= 0) return BNN_ERR_SHAPE;
+  if (!int_fits(h * w) || !int_fits(n * words_of(c))) return BNN_ERR_SHAPE;
   if (n == 0) return BNN_OK;
   if (!x || !bias || !x_packed) return BNN_ERR_NULL;
   if (!aligned(x, 16) || !aligned(x_packed, 4) || !aligned(bias, elem_bytes(bias_dtype)))
@@ -183,16 +197,15 @@ bnn_status bnn_abs_mean_scale(const void* x, int x_dtype, int64_t count, double 
 bnn_status bnn_w_pack(const void* weight, int w_dtype, int64_t out_features, int64_t in_features,
                       int kernel_size, uint32_t* w_packed, void* stream) {
   if (!float_dtype(w_dtype)) return BNN_ERR_DTYPE;
-  if (out_features < 0 || in_features <= 0 || in_features % 32 != 0 || kernel_size < 0)
-    return BNN_ERR_SHAPE;
+  if (out_features < 0 || in_features <= 0 || kernel_size < 0) return BNN_ERR_SHAPE;
   if (out_features == 0) return BNN_OK;
   if (!weight || !w_packed) return BNN_ERR_NULL;
   if (!aligned(w_packed, 4)) return BNN_ERR_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (kernel_size == 0) {
-    if (!aligned(weight, 16)) return BNN_ERR_ALIGN;
-    return hip_status(bnn::launch_pack_rows(weight, w_dtype, out_features * (in_features / 32),
-                                            w_packed, s));
+    if (!aligned(weight, elem_bytes(w_dtype))) return BNN_ERR_ALIGN;
+    return hip_status(pack_rows_any(weight, w_dtype, out_features, in_features, nullptr, 0, false,
+                                    w_packed, s));
   }
   if (!aligned(weight, elem_bytes(w_dtype))) return BNN_ERR_ALIGN;
   return hip_status(bnn::launch_pack_conv_weight(weight, w_dtype, out_features, in_features,
@@ -204,14 +217,14 @@ bnn_status bnn_gemm(const void* x, int x_dtype, const uint32_t* w_packed, int64_
                     void* workspace, size_t workspace_bytes, void* stream) {
   if (!(float_dtype(x_dtype) || x_dtype == BNN_U32_PACKED) || !out_dtype_ok(out_dtype))
     return BNN_ERR_DTYPE;
-  if (m < 0 || n < 0 || k < 32 || k % 32 != 0) return BNN_ERR_SHAPE;
-  if (!int_fits(m) || !int_fits(n) || !int_fits(k / 32)) return BNN_ERR_SHAPE;
+  if (m < 0 || n < 0 || k < 1) return BNN_ERR_SHAPE;
+  if (!int_fits(m) || !int_fits(n) || !int_fits(k)) return BNN_ERR_SHAPE;
   if (!path_known(path)) return BNN_ERR_PATH;
   if (path == BNN_PATH_MFMA_FP4 && k > bnn::kMaxFp4K) return BNN_ERR_PATH;
   if (m == 0 || n == 0) return BNN_OK;
   if (!x || !w_packed || !out) return BNN_ERR_NULL;
   const bool packed = x_dtype == BNN_U32_PACKED;
-  if (!aligned(x, packed ? 4 : 16) || !aligned(w_packed, 4) || !aligned(out, 16))
+  if (!aligned(x, packed ? 4 : elem_bytes(x_dtype)) || !aligned(w_packed, 4) || !aligned(out, 16))
     return BNN_ERR_ALIGN;
   const size_t need = bnn_gemm_workspace_bytes(m, k, x_dtype);
   if (need > 0 && (!workspace || workspace_bytes < need)) return BNN_ERR_WORKSPACE;
@@ -222,7 +235,7 @@ bnn_status bnn_gemm(const void* x, int x_dtype, const uint32_t* w_packed, int64_
   const uint32_t* a = static_cast<const uint32_t*>(x);
   if (!packed) {
     uint32_t* ws = static_cast<uint32_t*>(workspace);
-    const hipError_t e = bnn::launch_pack_rows(x, x_dtype, m * (k / 32), ws, s);
+    const hipError_t e = pack_rows_any(x, x_dtype, m, k, nullptr, 0, false, ws, s);
     if (e != hipSuccess) return BNN_ERR_HIP;
     a = ws;
   }
@@ -232,7 +245,8 @@ bnn_status bnn_gemm(const void* x, int x_dtype, const uint32_t* w_packed, int64_
   p.out = out;
   p.M = (int)m;
   p.N = (int)n;
-  p.KW = (int)(k / 32);
+  p.KW = (int)words_of(k);
+  p.KB = (int)k;
   p.alpha = alpha_of(scale_a, scale_w);
   const hipError_t e = run_path(use, p, false, out_dtype, s);
   if (e != hipSuccess) return BNN_ERR_HIP;
@@ -247,20 +261,21 @@ bnn_status bnn_conv2d(const void* x, int x_dtype, int64_t n, int64_t c, int64_t 
                       size_t workspace_bytes, void* stream) {
   if (!(float_dtype(x_dtype) || x_dtype == BNN_U32_PACKED) || !out_dtype_ok(out_dtype))
     return BNN_ERR_DTYPE;
-  if (n < 0 || out_channels < 0 || c <= 0 || c % 32 != 0 || h <= 0 || w <= 0) return BNN_ERR_SHAPE;
+  if (n < 0 || out_channels < 0 || c <= 0 || h <= 0 || w <= 0) return BNN_ERR_SHAPE;
   if (kernel_size < 1 || stride < 1 || dilation < 1 || padding < 0) return BNN_ERR_SHAPE;
   const int64_t ho = out_size(h, kernel_size, stride, padding, dilation);
   const int64_t wo = out_size(w, kernel_size, stride, padding, dilation);
   if (ho <= 0 || wo <= 0) return BNN_ERR_SHAPE;
-  const int64_t kw_words = (int64_t)kernel_size * kernel_size * (c / 32);
+  const int64_t kw_words = (int64_t)kernel_size * kernel_size * words_of(c);
   if (!int_fits(n * ho * wo) || !int_fits(out_channels) || !int_fits(kw_words) ||
-      !int_fits(n * h * w * (c / 32)) || !int_fits(h + 2 * (int64_t)padding) ||
+      !int_fits(n * h * w * words_of(c)) || !int_fits(h + 2 * (int64_t)padding) ||
       !int_fits(w + 2 * (int64_t)padding))
     return BNN_ERR_SHAPE;
   if (!path_known(path)) return BNN_ERR_PATH;
   if (path == BNN_PATH_XOR && kernel_size * kernel_size > bnn::xor_conv_max_taps())
     return BNN_ERR_PATH;
-  if (path == BNN_PATH_MFMA_FP4 && 32 * kw_words > bnn::kMaxFp4K) return BNN_ERR_PATH;
+  if (path == BNN_PATH_MFMA_FP4 && (int64_t)kernel_size * kernel_size * c > bnn::kMaxFp4K)
+    return BNN_ERR_PATH;
   if (n == 0 || out_channels == 0) return BNN_OK;
   if (!x || !w_packed || !out) return BNN_ERR_NULL;
   const bool packed = x_dtype == BNN_U32_PACKED;
@@ -289,10 +304,11 @@ bnn_status bnn_conv2d(const void* x, int x_dtype, int64_t n, int64_t c, int64_t 
   p.M = (int)(n * ho * wo);
   p.N = (int)out_channels;
   p.KW = (int)kw_words;
+  p.KB = (int)c;
   p.alpha = alpha_of(scale_a, scale_w);
   p.H = (int)h;
   p.W = (int)w;
-  p.CW = (int)(c / 32);
+  p.CW = (int)words_of(c);
   p.Ho = (int)ho;
   p.Wo = (int)wo;
   p.ks = kernel_size;

@@ -141,11 +141,15 @@ template <> struct OutType<kBF16> {
 // Conv:   A is packed activations [B][H][W][CW] read through the implicit
 //         im2col map; the reduction index q = tap * CW + cw with tap = kh*ks + kw;
 //         W is [N][ks][ks][CW] = [N][KW]; M = B*Ho*Wo, output is NCHW.
+// KB is the true number of signs per packed row (linear: K) or per tap (conv: C); when it is
+// not a whole number of words, the last word of a row (of a tap) holds KB % 32 signs and
+// zero bits above them in both operands.
 struct Contraction {
   const uint32_t* a;
   const uint32_t* w;
   void* out;
   int M, N, KW;
+  int KB;
   float alpha;
   // conv only
   int H, W, CW, Ho, Wo, ks, stride, pad, dil;

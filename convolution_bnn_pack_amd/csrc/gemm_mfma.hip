@@ -669,6 +669,23 @@ __global__ __launch_bounds__(T::THREADS) void mfma_kernel(Contraction p) {
   }
 
   if constexpr (!PERS) {
+    // rowk_part counted 32 signs per real A word; with a last word per row (linear) or per
+    // tap (conv) that holds only KB % 32 signs, the row's K_valid is lower by
+    // (32 * words - KB) per row or per real tap (the tail bits are 0 in A, so popA is right)
+    const int short_bits = (CONV ? 32 * p.CW : 32 * p.KW) - p.KB;
+    if (short_bits != 0 && a_q == 0 && amok) {
+      int units = 1;
+      if constexpr (CONV) {
+        int nh = 0, nw = 0;
+        for (int k = 0; k < p.ks; k++) {
+          const int ih = pc.ihb + k * p.dil, iw = pc.iwb + k * p.dil;
+          nh += (ih >= 0 && ih < p.H);
+          nw += (iw >= 0 && iw < p.W);
+        }
+        units = nh * nw;
+      }
+      rowk_part -= short_bits * units;
+    }
     atomicAdd(&rowk[a_row], rowk_part);
     __syncthreads();
     tile_epilogue(0);
@@ -702,8 +719,10 @@ hipError_t launch_tile_o(const Contraction& p, hipStream_t stream) {
   if constexpr (CONV && T::F4) {
     // more fp4 conv tiles than fit at once: one persistent workgroup per resident slot
     // streams its tiles back to back instead of running them in separate rounds (the
-    // int8 256 x 256 conv tile would spill with the extra state)
-    const int slots = persistent_slots<T, OUT, VEC>();
+    // int8 256 x 256 conv tile would spill with the extra state). Channel counts that are
+    // not a whole number of words take the one-tile-per-workgroup kernel, which corrects
+    // K_valid for the short last word of each tap.
+    const int slots = p.KB == 32 * p.CW ? persistent_slots<T, OUT, VEC>() : 0;
     if (slots > 0 && tiles > slots) {
       hipLaunchKernelGGL((mfma_kernel<T, OUT, CONV, VEC, true>), dim3((unsigned)slots), block, 0,
                          stream, p);

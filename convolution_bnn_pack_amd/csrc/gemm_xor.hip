@@ -16,8 +16,10 @@
 // word [b][oh*s - p + kh*d][ow*s - p + kw*d][cw]. A padded tap is loaded as
 // the word 0, which adds popcount(w) for that tap; the epilogue subtracts it
 // again (per-tap weight popcounts kept in LDS) and uses the pixel's real
-// reduction length K_valid = 32 * CW * (valid taps), so padded taps
-// contribute exactly 0.
+// reduction length K_valid = C * (valid taps), so padded taps contribute
+// exactly 0. A reduction length (K, or C per tap) that is not a whole number
+// of words leaves zero bits at the top of the last word in both operands:
+// their XOR adds nothing, and the true length enters only through K / C.
 #include "launch.h"
 
 namespace bnn {
@@ -150,7 +152,7 @@ __global__ __launch_bounds__(256) void xor_kernel(Contraction p) {
     const int m = m0 + (i < 4 ? ty * 4 + i : 64 + ty * 4 + (i - 4));
     if (m >= p.M) continue;
     if constexpr (!CONV) {
-      const int kbits = 32 * p.KW;
+      const int kbits = p.KB;
 #pragma unroll
       for (int h = 0; h < 2; h++) {
         const int n = n0 + h * 64 + tx * 4;
@@ -186,7 +188,7 @@ __global__ __launch_bounds__(256) void xor_kernel(Contraction p) {
           }
         }
       }
-      const int kvalid = 32 * p.CW * valid_taps;
+      const int kvalid = p.KB * valid_taps;
       const int hw = p.Ho * p.Wo;
       const int pix = m - q.b * hw;
 #pragma unroll

@@ -13,7 +13,8 @@ namespace bnn {
 hipError_t launch_pack_rows(const void* x, int dtype, int64_t total_words, uint32_t* out,
                             hipStream_t stream);
 
-// NCHW sign+pack: x [b][c][h][w] -> words [b][h][w][c/32]. With a bias (element type
+// NCHW sign+pack: x [b][c][h][w] -> words [b][h][w][ceil(c/32)] (channel bits at or past c
+// are 0). With a bias (element type
 // bdtype), channel c is shifted by bias[c] before its sign is taken.
 hipError_t launch_pack_nchw(const void* x, int dtype, int64_t b, int64_t c, int64_t h, int64_t w,
                             uint32_t* out, hipStream_t stream, const void* bias = nullptr,
@@ -25,13 +26,19 @@ hipError_t launch_pack_rows_shift(const void* x, int dtype, int64_t rows, int64_
                                   const void* bias, int bdtype, bool percol, uint32_t* out,
                                   hipStream_t stream);
 
+// Row sign+pack (plain when bias is null, else shifted as above) for any row length k:
+// words [rows][ceil(k/32)], bits at or past k are 0. Elements need only their natural alignment.
+hipError_t launch_pack_rows_ragged(const void* x, int dtype, int64_t rows, int64_t k,
+                                   const void* bias, int bdtype, bool percol, uint32_t* out,
+                                   hipStream_t stream);
+
 // factor * mean|x| over count elements into out[0] (double), through abs_mean_parts(count)
 // double partial sums.
 int abs_mean_parts(int64_t count);
 hipError_t launch_abs_mean(const void* x, int dtype, int64_t count, double factor, double* partial,
                            double* out, hipStream_t stream);
 
-// OIHW conv weight pack: [o][c][ks][ks] -> [o][ks][ks][c/32].
+// OIHW conv weight pack: [o][c][ks][ks] -> [o][ks][ks][ceil(c/32)].
 hipError_t launch_pack_conv_weight(const void* w, int dtype, int64_t o, int64_t c, int ks,
                                    uint32_t* out, hipStream_t stream);
 

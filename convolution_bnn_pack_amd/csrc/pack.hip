@@ -195,6 +195,43 @@ __global__ __launch_bounds__(256) void pack_rows_shift_kernel(const u32x4* __res
   }
 }
 
+// Row pack for rows that are not a whole number of words (k % 32 != 0), plain or shifted.
+// Rows then start at arbitrary element offsets, so the 16-byte vector layout above does
+// not apply: one wave packs 64 consecutive elements of one row per step, one element per
+// lane (a coalesced 64-element load), and a ballot of the 64 sign bits gives two words,
+// which lanes 0 and 1 store. Columns at or past k give 0 bits, so the last word of a row
+// holds k % 32 signs and zeros above them. SHIFT: bit = (x + b >= 0) with b = bias[col]
+// (PERCOL) or bias[0]; BDT is the shift's element type.
+template <int DT, bool SHIFT, int BDT, bool PERCOL>
+__global__ __launch_bounds__(256) void pack_rows_ragged_kernel(const void* __restrict__ x,
+                                                               const void* __restrict__ bias,
+                                                               uint32_t* __restrict__ out,
+                                                               int64_t rows, int64_t k,
+                                                               int64_t KW) {
+  const int lane = threadIdx.x & 63;
+  const int64_t chunks = (KW + 1) / 2;  // 64-element steps per row
+  const int64_t total = rows * chunks;
+  const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+  const float b0 = (SHIFT && !PERCOL) ? elem_f32<BDT>(bias, 0) + 0.0f : 0.0f;
+  for (int64_t t = wave; t < total; t += nwaves) {
+    const int64_t r = t / chunks, ch = t - r * chunks;
+    const int64_t col = ch * 64 + lane;
+    bool bit = false;
+    if (col < k) {
+      if constexpr (SHIFT) {
+        const float b = PERCOL ? elem_f32<BDT>(bias, col) + 0.0f : b0;
+        bit = elem_f32<DT>(x, r * k + col) + b >= 0.0f;
+      } else {
+        bit = elem_pos<DT>(x, r * k + col) != 0u;
+      }
+    }
+    const uint64_t m = __ballot(bit);
+    const int64_t q = ch * 2 + lane;
+    if (lane < 2 && q < KW) out[r * KW + q] = (uint32_t)(lane == 0 ? m : (m >> 32));
+  }
+}
+
 // NCHW pack along channels. Word (b, pixel, q) collects channel 32q + j of that pixel
 // into bit j. A 256-thread workgroup packs 64*V consecutive pixels of one (b, q): lanes
 // run along the contiguous pixel axis (V pixels each, one 16-byte load when the plane
@@ -218,10 +255,13 @@ __global__ __launch_bounds__(256) void pack_nchw_kernel(const void* __restrict__
   for (int64_t bq = blockIdx.y; bq < nbq; bq += gridDim.y) {
     const int64_t b = bq / CW, q = bq - b * CW;
     const char* plane0 = reinterpret_cast<const char*>(x) + ((b * C + 32 * q + 8 * wave) * HW) * ES;
+    // channels of this wave that exist (fewer than 8 only in the last word of a channel
+    // count that is not a whole number of words: the missing channels give 0 bits)
+    const int nch = (int)(C - (32 * q + 8 * wave) < 8 ? C - (32 * q + 8 * wave) : 8);
     float shift[8];
     if constexpr (BDT >= 0) {
 #pragma unroll
-      for (int c = 0; c < 8; c++) shift[c] = elem_f32<BDT>(bias, 32 * q + 8 * wave + c) + 0.0f;
+      for (int c = 0; c < 8; c++) shift[c] = c < nch ? elem_f32<BDT>(bias, 32 * q + 8 * wave + c) + 0.0f : 0.0f;
     }
     for (int64_t ch = blockIdx.x; ch < nchunks; ch += gridDim.x) {
       const int64_t base = ch * PIX;
@@ -231,7 +271,7 @@ __global__ __launch_bounds__(256) void pack_nchw_kernel(const void* __restrict__
       for (int c = 0; c < 8; c++) {
         const char* src = plane0 + ((int64_t)c * HW + p0) * ES;
         if constexpr (V * ES == 16) {
-          if (p0 < HW) {
+          if (p0 < HW && c < nch) {
             const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
             if constexpr (BDT >= 0)
               bits[c] = vec_bits_shift<DT, V, false>(v, &shift[c]);
@@ -244,7 +284,7 @@ __global__ __launch_bounds__(256) void pack_nchw_kernel(const void* __restrict__
           uint32_t bb = 0;
 #pragma unroll
           for (int v = 0; v < V; v++) {
-            if (p0 + v < HW) {
+            if (p0 + v < HW && c < nch) {
               if constexpr (BDT >= 0)
                 bb |= (uint32_t)(elem_f32<DT>(src, v) + shift[c] >= 0.0f) << v;
               else
@@ -344,7 +384,8 @@ __global__ __launch_bounds__(256) void abs_mean_final_kernel(const double* __res
   if (threadIdx.x == 0) out[0] = factor * (t / count);
 }
 
-// OIHW weight pack: word (o, tap, q) collects w[o][32q + j][tap] into bit j.
+// OIHW weight pack: word (o, tap, q) collects w[o][32q + j][tap] into bit j (channels at or
+// past C give 0 bits).
 // Runs once per layer, off the forward path.
 template <int DT>
 __global__ __launch_bounds__(256) void pack_conv_weight_kernel(const void* __restrict__ w,
@@ -357,7 +398,7 @@ __global__ __launch_bounds__(256) void pack_conv_weight_kernel(const void* __res
   const int64_t t = (idx / CW) % T;
   const int64_t o = idx / (CW * T);
   uint32_t word = 0;
-  for (int j = 0; j < 32; j++) word |= elem_pos<DT>(w, ((o * C + 32 * q + j) * T) + t) << j;
+  for (int j = 0; j < 32 && 32 * q + j < C; j++) word |= elem_pos<DT>(w, ((o * C + 32 * q + j) * T) + t) << j;
   out[idx] = word;
 }
 
@@ -404,7 +445,7 @@ void launch_nchw_b(dim3 grid, const void* x, uint32_t* out, int64_t c, int64_t H
 
 hipError_t launch_pack_nchw(const void* x, int dtype, int64_t b, int64_t c, int64_t h, int64_t w,
                             uint32_t* out, hipStream_t stream, const void* bias, int bdtype) {
-  const int64_t HW = h * w, CW = c / 32;
+  const int64_t HW = h * w, CW = (c + 31) / 32;
   if (b * HW * CW == 0) return hipSuccess;
   const int es = dtype == kF32 ? 4 : 2;
   const int vfull = 16 / es;
@@ -476,6 +517,57 @@ hipError_t launch_pack_rows_shift(const void* x, int dtype, int64_t rows, int64_
   return hipGetLastError();
 }
 
+namespace {
+
+template <int DT, bool SHIFT, int BDT, bool PERCOL>
+void launch_ragged_t(dim3 grid, const void* x, const void* bias, uint32_t* out, int64_t rows,
+                     int64_t k, int64_t KW, hipStream_t stream) {
+  hipLaunchKernelGGL((pack_rows_ragged_kernel<DT, SHIFT, BDT, PERCOL>), grid, dim3(256), 0, stream,
+                     x, bias, out, rows, k, KW);
+}
+
+template <int DT>
+void launch_ragged_b(dim3 grid, const void* x, const void* bias, int bdtype, bool percol,
+                     uint32_t* out, int64_t rows, int64_t k, int64_t KW, hipStream_t stream) {
+  if (!bias) {
+    launch_ragged_t<DT, false, kF32, false>(grid, x, nullptr, out, rows, k, KW, stream);
+    return;
+  }
+  switch (bdtype) {
+    case kF32:
+      if (percol) launch_ragged_t<DT, true, kF32, true>(grid, x, bias, out, rows, k, KW, stream);
+      else launch_ragged_t<DT, true, kF32, false>(grid, x, bias, out, rows, k, KW, stream);
+      break;
+    case kF16:
+      if (percol) launch_ragged_t<DT, true, kF16, true>(grid, x, bias, out, rows, k, KW, stream);
+      else launch_ragged_t<DT, true, kF16, false>(grid, x, bias, out, rows, k, KW, stream);
+      break;
+    default:
+      if (percol) launch_ragged_t<DT, true, kBF16, true>(grid, x, bias, out, rows, k, KW, stream);
+      else launch_ragged_t<DT, true, kBF16, false>(grid, x, bias, out, rows, k, KW, stream);
+      break;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_pack_rows_ragged(const void* x, int dtype, int64_t rows, int64_t k,
+                                   const void* bias, int bdtype, bool percol, uint32_t* out,
+                                   hipStream_t stream) {
+  if (rows <= 0 || k <= 0) return hipSuccess;
+  const int64_t KW = (k + 31) / 32;
+  const int64_t waves = rows * ((KW + 1) / 2);
+  int64_t blocks = (waves + 3) / 4;
+  if (blocks > 16384) blocks = 16384;
+  const dim3 grid((unsigned)blocks);
+  switch (dtype) {
+    case kF32: launch_ragged_b<kF32>(grid, x, bias, bdtype, percol, out, rows, k, KW, stream); break;
+    case kF16: launch_ragged_b<kF16>(grid, x, bias, bdtype, percol, out, rows, k, KW, stream); break;
+    default: launch_ragged_b<kBF16>(grid, x, bias, bdtype, percol, out, rows, k, KW, stream); break;
+  }
+  return hipGetLastError();
+}
+
 int abs_mean_parts(int64_t count) {
   // one workgroup per 2048 elements, at most 1024 (a function of count alone, so the
   // order of the additions, hence the result, is the same on every run)
@@ -510,7 +602,7 @@ hipError_t launch_abs_mean(const void* x, int dtype, int64_t count, double facto
 hipError_t launch_pack_conv_weight(const void* w, int dtype, int64_t o, int64_t c, int ks,
                                    uint32_t* out, hipStream_t stream) {
   const int T = ks * ks;
-  const int64_t CW = c / 32;
+  const int64_t CW = (c + 31) / 32;
   const int64_t total = o * T * CW;
   if (total == 0) return hipSuccess;
   const dim3 grid((unsigned)((total + 255) / 256)), block(256);

@@ -34,9 +34,12 @@
  *   - Arguments are validated before anything is enqueued: on any error the
  *     call returns a non-zero status, enqueues nothing and leaves every
  *     output untouched. BNN_ERR_HIP reports a failed kernel launch.
- *   - Packed words travel in int32/uint32 buffers; the reduction length K
- *     (or the channel count C) must be a multiple of 32 (the pages' layers
- *     assert that the input divides into whole binary words).
+ *   - Packed words travel in int32/uint32 buffers. A reduction length K (or
+ *     channel count C) that is not a multiple of 32 fills ceil(K/32) words,
+ *     the last one holding K % 32 signs in its low bits and 0 above them, in
+ *     both operands; the contraction still runs over the true K (the pages'
+ *     CUTLASS layer asserts whole binary words; this ABI also takes the
+ *     rest).
  *   - The library holds no state except the per-thread record of the path
  *     that the last call took (bnn_last_path).
  */
@@ -53,7 +56,7 @@ extern "C" {
 typedef enum {
   BNN_OK = 0,
   BNN_ERR_NULL = 1,      /* a required pointer is NULL */
-  BNN_ERR_SHAPE = 2,     /* a size is negative/zero where it may not be, K or C % 32 != 0, empty conv output */
+  BNN_ERR_SHAPE = 2,     /* a size is negative/zero where it may not be, a bias of the wrong length, empty conv output */
   BNN_ERR_DTYPE = 3,     /* dtype code not allowed for that argument */
   BNN_ERR_ALIGN = 4,     /* a pointer is not aligned as the call requires (16 bytes for tensors read in vectors) */
   BNN_ERR_WORKSPACE = 5, /* workspace missing or smaller than the *_workspace_bytes query */
@@ -81,16 +84,17 @@ typedef enum {
 } bnn_path;
 
 /* Sign + pack of activations along rows.
- *   x        [rows, k] in x_dtype (BNN_F32/F16/BF16), 16-byte aligned.
- *   x_packed [rows, k/32] uint32 out; bit j of word q = (x[r][32q+j] >= 0).
- * k % 32 == 0; rows == 0 is a no-op. */
+ *   x        [rows, k] in x_dtype (BNN_F32/F16/BF16), aligned to its element size (the fast
+ *            path needs 16-byte alignment and k % 32 == 0).
+ *   x_packed [rows, ceil(k/32)] uint32 out; bit j of word q = (x[r][32q+j] >= 0), 0 past k.
+ * k >= 1; rows == 0 is a no-op. */
 bnn_status bnn_pack_sign(const void* x, int x_dtype, int64_t rows, int64_t k,
                          uint32_t* x_packed, void* stream);
 
 /* Sign + pack of NCHW activations along channels.
  *   x        [n, c, h, w] in x_dtype (BNN_F32/F16/BF16), 16-byte aligned.
- *   x_packed [n, h, w, c/32] uint32 out; bit j of word q = (x[n][32q+j][h][w] >= 0).
- * c % 32 == 0. */
+ *   x_packed [n, h, w, ceil(c/32)] uint32 out; bit j of word q = (x[n][32q+j][h][w] >= 0), 0 past c.
+ * c >= 1. */
 bnn_status bnn_pack_sign_nchw(const void* x, int x_dtype, int64_t n, int64_t c, int64_t h,
                               int64_t w, uint32_t* x_packed, void* stream);
 
@@ -99,14 +103,14 @@ bnn_status bnn_pack_sign_nchw(const void* x, int x_dtype, int64_t n, int64_t c, 
  * still zero it is initialised to 2 * mean|x| (symmetric quantization) or 4 * mean|x|.
  *
  * Shifted sign + pack along rows (linear layers):
- *   x        [rows, k] in x_dtype (BNN_F32/F16/BF16), 16-byte aligned.
+ *   x        [rows, k] in x_dtype (BNN_F32/F16/BF16), aligned to its element size.
  *   bias     bias_len == 1: one shift for every element; bias_len == k: bias[col] per input
  *            feature (the linear page gives the bias no shape). bias_dtype BNN_F32/F16/BF16,
  *            aligned to its element size.
- *   x_packed [rows, k/32] uint32 out; bit j of word q = (x[r][32q+j] + bias >= 0), the sign of the
+ *   x_packed [rows, ceil(k/32)] uint32 out; bit j of word q = (x[r][32q+j] + bias >= 0), the sign of the
  *            exact sum: -0 + -0 -> +1, a NaN operand or opposite infinities -> -1 (the sign of a
  *            sum never depends on the precision the layer adds in).
- * k % 32 == 0; bias_len 1 or k (else BNN_ERR_SHAPE); rows == 0 is a no-op. */
+ * k >= 1; bits past k are 0; bias_len 1 or k (else BNN_ERR_SHAPE); rows == 0 is a no-op. */
 bnn_status bnn_pack_sign_shift(const void* x, int x_dtype, int64_t rows, int64_t k,
                                const void* bias, int bias_dtype, int64_t bias_len,
                                uint32_t* x_packed, void* stream);
@@ -114,7 +118,7 @@ bnn_status bnn_pack_sign_shift(const void* x, int x_dtype, int64_t rows, int64_t
 /* Shifted sign + pack of NCHW activations along channels (the conv layer: bias_a has one value
  * per input channel, broadcast over batch and pixels).
  *   bias     [c] in bias_dtype (BNN_F32/F16/BF16), aligned to its element size.
- *   x_packed [n, h, w, c/32]; bit j of word q = (x[n][32q+j][h][w] + bias[32q+j] >= 0), as above.
+ *   x_packed [n, h, w, ceil(c/32)]; bit j of word q = (x[n][32q+j][h][w] + bias[32q+j] >= 0), as above.
  * Shapes and alignment as bnn_pack_sign_nchw. */
 bnn_status bnn_pack_sign_nchw_shift(const void* x, int x_dtype, int64_t n, int64_t c, int64_t h,
                                     int64_t w, const void* bias, int bias_dtype,
@@ -136,33 +140,33 @@ bnn_status bnn_abs_mean_scale(const void* x, int x_dtype, int64_t count, double 
 size_t bnn_abs_mean_workspace_bytes(int64_t count);
 
 /* Weight pack (run once per layer, ahead of the forward).
- *   kernel_size == 0: linear weight [out_features, in_features] -> [out_features, in_features/32].
- *   kernel_size >= 1: conv weight OIHW [out_features, in_features, k, k] -> [out_features, k, k, in_features/32].
- *   w_dtype BNN_F32/F16/BF16; in_features % 32 == 0; weight 16-byte aligned when kernel_size == 0. */
+ *   kernel_size == 0: linear weight [out_features, in_features] -> [out_features, ceil(in_features/32)].
+ *   kernel_size >= 1: conv weight OIHW [out_features, in_features, k, k] -> [out_features, k, k, ceil(in_features/32)].
+ *   w_dtype BNN_F32/F16/BF16; in_features >= 1 (bits past it 0); weight aligned to its element size. */
 bnn_status bnn_w_pack(const void* weight, int w_dtype, int64_t out_features, int64_t in_features,
                       int kernel_size, uint32_t* w_packed, void* stream);
 
 /* Binary linear forward: out[m][n] = scale_a * scale_w * sum_k sgn(x[m][k]) * sgn(W[n][k]).
  *   x         [m, k] in BNN_F32/F16/BF16 (packed here into the workspace), or
- *             [m, k/32] BNN_U32_PACKED (already packed; no workspace needed).
- *   w_packed  [n, k/32] from bnn_w_pack(kernel_size = 0).
+ *             [m, ceil(k/32)] BNN_U32_PACKED (already packed, bits past k 0; no workspace needed).
+ *   w_packed  [n, ceil(k/32)] from bnn_w_pack(kernel_size = 0).
  *   out       [m, n] in out_dtype: BNN_F32/F16/BF16 (scaled) or BNN_I32 (raw accumulators).
  *   path      a bnn_path value.
  *   workspace device scratch of at least bnn_gemm_workspace_bytes(m, k, x_dtype) bytes
  *             (may be NULL when that is 0).
- * m == 0 or n == 0 is a no-op; k % 32 == 0, k >= 32. */
+ * m == 0 or n == 0 is a no-op; k >= 1. */
 bnn_status bnn_gemm(const void* x, int x_dtype, const uint32_t* w_packed, int64_t m, int64_t n,
                     int64_t k, double scale_a, double scale_w, int path, void* out, int out_dtype,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* Binary conv2d forward (square kernel, symmetric stride/padding/dilation).
- *   x         NCHW [n, c, h, w] in BNN_F32/F16/BF16, or [n, h, w, c/32] BNN_U32_PACKED.
- *   w_packed  [out_channels, k, k, c/32] from bnn_w_pack(kernel_size = k).
+ *   x         NCHW [n, c, h, w] in BNN_F32/F16/BF16, or [n, h, w, ceil(c/32)] BNN_U32_PACKED.
+ *   w_packed  [out_channels, k, k, ceil(c/32)] from bnn_w_pack(kernel_size = k).
  *   out       NCHW [n, out_channels, Ho, Wo] in out_dtype (BNN_F32/F16/BF16/I32),
  *             Ho = floor((h + 2*padding - dilation*(k-1) - 1)/stride + 1), likewise Wo.
  *   Padded taps contribute 0 (they are not counted in the reduction).
  *   workspace at least bnn_conv2d_workspace_bytes(n, c, h, w, x_dtype) bytes.
- * Requires c % 32 == 0, kernel_size >= 1, stride >= 1, dilation >= 1, padding >= 0, Ho, Wo >= 1.
+ * Requires c >= 1, kernel_size >= 1, stride >= 1, dilation >= 1, padding >= 0, Ho, Wo >= 1.
  * n == 0 or out_channels == 0 is a no-op. */
 bnn_status bnn_conv2d(const void* x, int x_dtype, int64_t n, int64_t c, int64_t h, int64_t w,
                       const uint32_t* w_packed, int64_t out_channels, double scale_a,

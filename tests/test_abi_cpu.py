@@ -60,7 +60,10 @@ def _gemm(bnn, **kw):
 
 
 def test_gemm_argument_checks(bnn):
-    assert _gemm(bnn, k=100) == bnn.ERR_SHAPE
+    # any k >= 1 passes the shape checks (ragged k packs a partial last word): a null x then
+    # stops the call before anything is enqueued
+    assert _gemm(bnn, k=100, x=None) == bnn.ERR_NULL
+    assert _gemm(bnn, k=-5) == bnn.ERR_SHAPE
     assert _gemm(bnn, k=0) == bnn.ERR_SHAPE
     assert _gemm(bnn, m=-1) == bnn.ERR_SHAPE
     assert _gemm(bnn, x_dtype=7) == bnn.ERR_DTYPE
@@ -72,7 +75,8 @@ def test_gemm_argument_checks(bnn):
     assert _gemm(bnn, x=None) == bnn.ERR_NULL
     assert _gemm(bnn, w=None) == bnn.ERR_NULL
     assert _gemm(bnn, out=None) == bnn.ERR_NULL
-    assert _gemm(bnn, x=MISALIGNED) == bnn.ERR_ALIGN
+    assert _gemm(bnn, x=FAKE + 1) == bnn.ERR_ALIGN                  # f16 x: 2-byte elements
+    assert _gemm(bnn, x=FAKE + 2, x_dtype=bnn.U32_PACKED) == bnn.ERR_ALIGN
     assert _gemm(bnn, out=MISALIGNED) == bnn.ERR_ALIGN
     assert _gemm(bnn, ws=None) == bnn.ERR_WORKSPACE
     assert _gemm(bnn, ws_bytes=64 * 8 * 4 - 1) == bnn.ERR_WORKSPACE
@@ -92,7 +96,8 @@ def _conv(bnn, **kw):
 
 
 def test_conv_argument_checks(bnn):
-    assert _conv(bnn, c=48) == bnn.ERR_SHAPE
+    assert _conv(bnn, c=48, wp=None) == bnn.ERR_NULL                # ragged C passes the shape checks
+    assert _conv(bnn, c=0) == bnn.ERR_SHAPE
     assert _conv(bnn, ks=0) == bnn.ERR_SHAPE
     assert _conv(bnn, s=0) == bnn.ERR_SHAPE
     assert _conv(bnn, d=0) == bnn.ERR_SHAPE
@@ -114,17 +119,20 @@ def test_conv_argument_checks(bnn):
 
 def test_pack_argument_checks(bnn):
     L = bnn.lib
-    assert L.bnn_pack_sign(FAKE, bnn.F32, 4, 33, FAKE, None) == bnn.ERR_SHAPE
+    assert L.bnn_pack_sign(None, bnn.F32, 4, 33, FAKE, None) == bnn.ERR_NULL     # ragged k accepted
+    assert L.bnn_pack_sign(FAKE, bnn.F32, 4, 0, FAKE, None) == bnn.ERR_SHAPE
     assert L.bnn_pack_sign(FAKE, bnn.I32, 4, 32, FAKE, None) == bnn.ERR_DTYPE
     assert L.bnn_pack_sign(None, bnn.F32, 4, 32, FAKE, None) == bnn.ERR_NULL
-    assert L.bnn_pack_sign(MISALIGNED, bnn.F32, 4, 32, FAKE, None) == bnn.ERR_ALIGN
+    assert L.bnn_pack_sign(FAKE + 2, bnn.F32, 4, 32, FAKE, None) == bnn.ERR_ALIGN
     assert L.bnn_pack_sign(None, bnn.F32, 0, 32, None, None) == bnn.OK
-    assert L.bnn_pack_sign_nchw(FAKE, bnn.F16, 1, 40, 4, 4, FAKE, None) == bnn.ERR_SHAPE
+    assert L.bnn_pack_sign_nchw(None, bnn.F16, 1, 40, 4, 4, FAKE, None) == bnn.ERR_NULL
+    assert L.bnn_pack_sign_nchw(MISALIGNED, bnn.F16, 1, 40, 4, 4, FAKE, None) == bnn.ERR_ALIGN
     assert L.bnn_pack_sign_nchw(FAKE, bnn.F16, 1, 32, 0, 4, FAKE, None) == bnn.ERR_SHAPE
-    assert L.bnn_w_pack(FAKE, bnn.F32, 8, 48, 0, FAKE, None) == bnn.ERR_SHAPE
+    assert L.bnn_w_pack(None, bnn.F32, 8, 48, 0, FAKE, None) == bnn.ERR_NULL
+    assert L.bnn_w_pack(FAKE, bnn.F32, 8, 0, 0, FAKE, None) == bnn.ERR_SHAPE
     assert L.bnn_w_pack(FAKE, bnn.F32, 8, 64, -1, FAKE, None) == bnn.ERR_SHAPE
     assert L.bnn_w_pack(FAKE, bnn.U32_PACKED, 8, 64, 3, FAKE, None) == bnn.ERR_DTYPE
-    assert L.bnn_w_pack(MISALIGNED, bnn.F32, 8, 64, 0, FAKE, None) == bnn.ERR_ALIGN
+    assert L.bnn_w_pack(FAKE + 2, bnn.F32, 8, 64, 0, FAKE, None) == bnn.ERR_ALIGN
     assert L.bnn_w_pack(None, bnn.F32, 0, 64, 3, None, None) == bnn.OK
 
 
@@ -132,15 +140,16 @@ def test_prologue_argument_checks(bnn):
     L = bnn.lib
     # shifted row pack: bias of one value or one per column
     assert L.bnn_pack_sign_shift(FAKE, bnn.F16, 4, 64, FAKE, bnn.F32, 2, FAKE, None) == bnn.ERR_SHAPE
-    assert L.bnn_pack_sign_shift(FAKE, bnn.F16, 4, 48, FAKE, bnn.F32, 48, FAKE, None) == bnn.ERR_SHAPE
+    assert L.bnn_pack_sign_shift(FAKE, bnn.F16, 4, 48, FAKE, bnn.F32, 47, FAKE, None) == bnn.ERR_SHAPE
+    assert L.bnn_pack_sign_shift(None, bnn.F16, 4, 48, FAKE, bnn.F32, 48, FAKE, None) == bnn.ERR_NULL
     assert L.bnn_pack_sign_shift(FAKE, bnn.F16, 4, 64, FAKE, bnn.I32, 64, FAKE, None) == bnn.ERR_DTYPE
     assert L.bnn_pack_sign_shift(FAKE, bnn.U32_PACKED, 4, 64, FAKE, bnn.F32, 1, FAKE, None) == bnn.ERR_DTYPE
     assert L.bnn_pack_sign_shift(FAKE, bnn.F16, 4, 64, None, bnn.F32, 1, FAKE, None) == bnn.ERR_NULL
     assert L.bnn_pack_sign_shift(FAKE, bnn.F16, 4, 64, FAKE + 2, bnn.F32, 64, FAKE, None) == bnn.ERR_ALIGN
-    assert L.bnn_pack_sign_shift(MISALIGNED, bnn.F16, 4, 64, FAKE, bnn.F32, 64, FAKE, None) == bnn.ERR_ALIGN
+    assert L.bnn_pack_sign_shift(FAKE + 1, bnn.F16, 4, 64, FAKE, bnn.F32, 64, FAKE, None) == bnn.ERR_ALIGN
     assert L.bnn_pack_sign_shift(None, bnn.F16, 0, 64, None, bnn.F32, 64, None, None) == bnn.OK
     # shifted NCHW pack: one bias per channel
-    assert L.bnn_pack_sign_nchw_shift(FAKE, bnn.F32, 1, 40, 4, 4, FAKE, bnn.F32, FAKE, None) == bnn.ERR_SHAPE
+    assert L.bnn_pack_sign_nchw_shift(FAKE, bnn.F32, 1, 0, 4, 4, FAKE, bnn.F32, FAKE, None) == bnn.ERR_SHAPE
     assert L.bnn_pack_sign_nchw_shift(FAKE, bnn.F32, 1, 32, 4, 4, FAKE, 5, FAKE, None) == bnn.ERR_DTYPE
     assert L.bnn_pack_sign_nchw_shift(FAKE, bnn.F32, 1, 32, 4, 4, None, bnn.F16, FAKE, None) == bnn.ERR_NULL
     assert L.bnn_pack_sign_nchw_shift(FAKE, bnn.F32, 1, 32, 4, 4, FAKE + 1, bnn.F16, FAKE, None) == bnn.ERR_ALIGN
@@ -189,6 +198,9 @@ def test_workspace_queries(bnn):
     assert L.bnn_gemm_workspace_bytes(2048, 4096, bnn.U32_PACKED) == 0
     assert L.bnn_conv2d_workspace_bytes(32, 256, 14, 14, bnn.F32) == 32 * 14 * 14 * 8 * 4
     assert L.bnn_conv2d_workspace_bytes(32, 256, 14, 14, bnn.U32_PACKED) == 0
+    # partial last words: ceil(k / 32) words per row, ceil(c / 32) per pixel
+    assert L.bnn_gemm_workspace_bytes(3, 33, bnn.F32) == 3 * 2 * 4
+    assert L.bnn_conv2d_workspace_bytes(2, 40, 5, 5, bnn.F16) == 2 * 5 * 5 * 2 * 4
 
 
 def test_last_path_starts_unset(bnn):

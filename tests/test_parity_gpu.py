@@ -324,13 +324,20 @@ def test_last_path_and_errors_on_device(bnn):
     assert e.value.status == bnn.ERR_WORKSPACE
     torch.cuda.synchronize()
     assert bool((out == 7.0).all())
+    # an empty reduction is a shape error (the layers' AssertionError)
     with pytest.raises(AssertionError):
-        bnn.pack_sign(torch.randn((4, 48), device=DEV))
-    # a misaligned view is rejected with ERR_ALIGN
+        bnn.pack_sign(torch.randn((4, 0), device=DEV))
+    # a view that is element-aligned but not 16-byte aligned is packed by the element-wise kernel
     buf = torch.randn((65 * 64,), device=DEV)
+    view = buf[1:1 + 64 * 64].view(64, 64)
+    assert torch.equal(bnn.pack_sign(view), bnn.pack_sign(view.clone()))
+    # an output that is not 16-byte aligned is rejected with ERR_ALIGN, nothing written
+    obuf = torch.full((64 * 32 + 1,), 7.0, device=DEV)
     with pytest.raises(bnn.BnnError) as e:
-        bnn.pack_sign(buf[1:1 + 64 * 64].view(64, 64))
+        bnn.gemm(x, wp, 1.0, 1.0, out=obuf[1:].view(64, 32))
     assert e.value.status == bnn.ERR_ALIGN
+    torch.cuda.synchronize()
+    assert bool((obuf == 7.0).all())
 
 
 def test_graph_replay_matches_eager(bnn):
