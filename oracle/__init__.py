@@ -55,6 +55,11 @@ def _bind(lib):
     lib.oracle_conv2d_acc.restype = I
     lib.oracle_conv2d_kvalid.argtypes = [I64, I64, I64, I64, I64, I64, I64, P]
     lib.oracle_conv2d_kvalid.restype = I
+    lib.oracle_conv2d_acc2.argtypes = [P, I, P, I] + [I64] * 13 + [P, I64, P]
+    lib.oracle_conv2d_acc2.restype = I
+    lib.oracle_conv2d_kvalid2.argtypes = [I64] * 11 + [P]
+    lib.oracle_conv2d_kvalid2.restype = I
+    lib.oracle_pack_conv_weight2.argtypes = [P, I, I64, I64, I64, I64, P]
     lib.oracle_scale.argtypes = [P, I64, ctypes.c_double, ctypes.c_double, P]
     lib.oracle_pack_rows_shift.argtypes = [P, I, I64, I64, P, I, I64, P]
     lib.oracle_pack_nchw_shift.argtypes = [P, I, I64, I64, I64, I64, P, I, P]
@@ -134,13 +139,19 @@ def pack_nchw(x: torch.Tensor) -> torch.Tensor:
 
 
 def pack_conv_weight(w: torch.Tensor) -> torch.Tensor:
-    """OIHW w [o, c, k, k] -> int32 words [o, k, k, ceil(c/32)] (channel bits past c are 0)."""
+    """OIHW w [o, c, kh, kw] -> int32 words [o, kh, kw, ceil(c/32)] (channel bits past c are 0)."""
     w = _cpu(w)
     o, c, kh, kw = w.shape
-    assert kh == kw
     out = _words(o * kh * kw * _nw(c))
-    _load().oracle_pack_conv_weight(w.data_ptr(), _code(w), o, c, kh, out.data_ptr())
+    if kh == kw:
+        _load().oracle_pack_conv_weight(w.data_ptr(), _code(w), o, c, kh, out.data_ptr())
+    else:
+        _load().oracle_pack_conv_weight2(w.data_ptr(), _code(w), o, c, kh, kw, out.data_ptr())
     return out.view(o, kh, kw, _nw(c))
+
+
+def _pair(v):
+    return (int(v), int(v)) if isinstance(v, int) else (int(v[0]), int(v[1]))
 
 
 def _index(idx, limit):
@@ -172,34 +183,44 @@ def conv_out_size(size, ks, stride, padding, dilation) -> int:
     return int(_load().oracle_conv_out_size(size, ks, stride, padding, dilation))
 
 
-def conv2d_acc(x: torch.Tensor, w: torch.Tensor, stride: int, padding: int, dilation: int,
+def conv2d_acc(x: torch.Tensor, w: torch.Tensor, stride, padding, dilation,
                images=None) -> torch.Tensor:
-    """int32 acc [len(images) or B, O, Ho, Wo] of the zero-padded binary conv."""
+    """int32 acc [len(images) or B, O, Ho, Wo] of the zero-padded binary conv. stride, padding
+    and dilation are ints (both axes) or (rows, columns) pairs; the kernel may be non-square."""
     x, w = _cpu(x), _cpu(w)
     b, c, h, wd = x.shape
-    o, c2, ks, ks2 = w.shape
-    assert c == c2 and ks == ks2
-    ho = conv_out_size(h, ks, stride, padding, dilation)
-    wo = conv_out_size(wd, ks, stride, padding, dilation)
+    o, c2, kh, kw = w.shape
+    assert c == c2
+    (sh, sw), (ph, pw), (dh, dw) = _pair(stride), _pair(padding), _pair(dilation)
+    ho = conv_out_size(h, kh, sh, ph, dh)
+    wo = conv_out_size(wd, kw, sw, pw, dw)
     if ho <= 0 or wo <= 0:
         raise ValueError("oracle: empty conv output")
     idx, ni = _index(images, b)
     out = torch.empty((ni, o, ho, wo), dtype=torch.int32)
-    rc = _load().oracle_conv2d_acc(x.data_ptr(), _code(x), w.data_ptr(), _code(w), b, c, h, wd, o,
-                                   ks, stride, padding, dilation,
-                                   idx.data_ptr() if idx is not None else None, ni,
-                                   out.data_ptr())
+    ip = idx.data_ptr() if idx is not None else None
+    if kh == kw and sh == sw and ph == pw and dh == dw:
+        rc = _load().oracle_conv2d_acc(x.data_ptr(), _code(x), w.data_ptr(), _code(w), b, c, h, wd, o,
+                                       kh, sh, ph, dh, ip, ni, out.data_ptr())
+    else:
+        rc = _load().oracle_conv2d_acc2(x.data_ptr(), _code(x), w.data_ptr(), _code(w), b, c, h, wd,
+                                        o, kh, kw, sh, sw, ph, pw, dh, dw, ip, ni, out.data_ptr())
     if rc != 0:
         raise RuntimeError("oracle_conv2d_acc failed")
     return out
 
 
 def conv2d_kvalid(c, h, w, ks, stride, padding, dilation) -> torch.Tensor:
-    """int32 [Ho, Wo]: number of real (unpadded) reduction terms per output pixel."""
-    ho = conv_out_size(h, ks, stride, padding, dilation)
-    wo = conv_out_size(w, ks, stride, padding, dilation)
+    """int32 [Ho, Wo]: number of real (unpadded) reduction terms per output pixel. ks, stride,
+    padding and dilation are ints or (rows, columns) pairs."""
+    (kh, kw), (sh, sw), (ph, pw), (dh, dw) = _pair(ks), _pair(stride), _pair(padding), _pair(dilation)
+    ho = conv_out_size(h, kh, sh, ph, dh)
+    wo = conv_out_size(w, kw, sw, pw, dw)
     out = torch.empty((ho, wo), dtype=torch.int32)
-    rc = _load().oracle_conv2d_kvalid(c, h, w, ks, stride, padding, dilation, out.data_ptr())
+    if kh == kw and sh == sw and ph == pw and dh == dw:
+        rc = _load().oracle_conv2d_kvalid(c, h, w, kh, sh, ph, dh, out.data_ptr())
+    else:
+        rc = _load().oracle_conv2d_kvalid2(c, h, w, kh, kw, sh, sw, ph, pw, dh, dw, out.data_ptr())
     if rc != 0:
         raise RuntimeError("oracle_conv2d_kvalid failed")
     return out

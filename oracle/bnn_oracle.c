@@ -42,6 +42,9 @@
  *    The blog's unfold call omits the dilation although its output-size
  *    formula uses it; the unfold here applies the dilation (the conv forward
  *    on the qconv/binary/cutlass/layer page takes a dilation argument).
+ *    The general form takes a KH x KW kernel and a stride, padding and
+ *    dilation per axis (rows, columns), each output extent by the same
+ *    formula along its axis; the layer's single ints are the square case.
  *    The scale product is the host-side product of the two scalar scales
  *    (BinaryConv2dForward.forward on the qconv/binary/cutlass/layer page).
  *
@@ -153,23 +156,29 @@ void oracle_pack_nchw(const void *x, int dtype, int64_t B, int64_t C, int64_t H,
         }
 }
 
-/* OIHW weight w[o][c][kh][kw] -> words out[o][kh][kw][ceil(C/32)]; bit j of word q is 1 iff
- * 32q+j < C and w[o][32q+j][kh][kw] >= 0. */
-void oracle_pack_conv_weight(const void *w, int dtype, int64_t O, int64_t C, int64_t ks,
-                             uint32_t *out) {
+/* OIHW weight w[o][c][i][j] of a KH x KW kernel -> words out[o][i][j][ceil(C/32)]; bit jj of word
+ * q is 1 iff 32q+jj < C and w[o][32q+jj][i][j] >= 0. */
+void oracle_pack_conv_weight2(const void *w, int dtype, int64_t O, int64_t C, int64_t KH,
+                              int64_t KW, uint32_t *out) {
   int64_t cw = (C + 31) / 32;
 #pragma omp parallel for schedule(static)
   for (int64_t o = 0; o < O; o++)
-    for (int64_t kh = 0; kh < ks; kh++)
-      for (int64_t kx = 0; kx < ks; kx++)
+    for (int64_t i = 0; i < KH; i++)
+      for (int64_t j = 0; j < KW; j++)
         for (int64_t q = 0; q < cw; q++) {
           uint32_t word = 0;
-          for (int j = 0; j < 32 && 32 * q + j < C; j++) {
-            int64_t idx = ((o * C + 32 * q + j) * ks + kh) * ks + kx;
-            if (sgn(widen(w, dtype, idx)) > 0.0f) word |= (uint32_t)1 << j;
+          for (int jj = 0; jj < 32 && 32 * q + jj < C; jj++) {
+            int64_t idx = ((o * C + 32 * q + jj) * KH + i) * KW + j;
+            if (sgn(widen(w, dtype, idx)) > 0.0f) word |= (uint32_t)1 << jj;
           }
-          out[((o * ks + kh) * ks + kx) * cw + q] = word;
+          out[((o * KH + i) * KW + j) * cw + q] = word;
         }
+}
+
+/* Square kernels: oracle_pack_conv_weight2 with KH = KW = ks. */
+void oracle_pack_conv_weight(const void *w, int dtype, int64_t O, int64_t C, int64_t ks,
+                             uint32_t *out) {
+  oracle_pack_conv_weight2(w, dtype, O, C, ks, ks, out);
 }
 
 /* Linear accumulators. acc[i][n] = sum_k sgn(x[m_i][k]) * sgn(W[n][k]) for the selected rows
@@ -218,19 +227,24 @@ int64_t oracle_conv_out_size(int64_t size, int64_t ks, int64_t s, int64_t p, int
 }
 
 /* Conv accumulators via zero-padded unfold + GEMM, for the selected images b_i = imgs[i]
- * (all B in order when imgs == NULL). acc[i][o][oh][ow]. Returns 0, or -1 on a bad shape
- * or when memory runs out. */
-int oracle_conv2d_acc(const void *x, int xdt, const void *w, int wdt, int64_t B, int64_t C,
-                      int64_t H, int64_t W, int64_t O, int64_t ks, int64_t s, int64_t p, int64_t d,
-                      const int64_t *imgs, int64_t nimgs, int32_t *acc) {
-  int64_t Ho = oracle_conv_out_size(H, ks, s, p, d);
-  int64_t Wo = oracle_conv_out_size(W, ks, s, p, d);
-  if (Ho <= 0 || Wo <= 0 || s < 1 || d < 1 || p < 0 || ks < 1) return -1;
-  int64_t R = C * ks * ks, L = Ho * Wo, Hp = H + 2 * p, Wp = W + 2 * p;
+ * (all B in order when imgs == NULL). acc[i][o][oh][ow]. A KH x KW kernel with stride
+ * (sh, sw), zero padding (ph, pw) and dilation (dh, dw) along (rows, columns); each output
+ * extent follows the same formula per axis. Returns 0, or -1 on a bad shape or when memory
+ * runs out. */
+int oracle_conv2d_acc2(const void *x, int xdt, const void *w, int wdt, int64_t B, int64_t C,
+                       int64_t H, int64_t W, int64_t O, int64_t KH, int64_t KW, int64_t sh,
+                       int64_t sw, int64_t ph, int64_t pw, int64_t dh, int64_t dw,
+                       const int64_t *imgs, int64_t nimgs, int32_t *acc) {
+  int64_t Ho = oracle_conv_out_size(H, KH, sh, ph, dh);
+  int64_t Wo = oracle_conv_out_size(W, KW, sw, pw, dw);
+  if (Ho <= 0 || Wo <= 0 || sh < 1 || sw < 1 || dh < 1 || dw < 1 || ph < 0 || pw < 0 || KH < 1 ||
+      KW < 1)
+    return -1;
+  int64_t R = C * KH * KW, L = Ho * Wo, Hp = H + 2 * ph, Wp = W + 2 * pw;
   if (R >= (1 << 24)) return -1;
   if (!imgs) nimgs = B;
 
-  /* weight viewed as [O, C*k*k] over the OIHW order, signed */
+  /* weight viewed as [O, C*KH*KW] over the OIHW order, signed */
   float *ws = (float *)malloc(sizeof(float) * (size_t)(O * R));
   float *xp = (float *)malloc(sizeof(float) * (size_t)(C * Hp * Wp));
   float *cols = (float *)malloc(sizeof(float) * (size_t)(L * R));
@@ -240,24 +254,24 @@ int oracle_conv2d_acc(const void *x, int xdt, const void *w, int wdt, int64_t B,
   }
   oracle_sign(w, wdt, O * R, ws);
 
-  for (int64_t i = 0; i < nimgs; i++) {
-    int64_t b = imgs ? imgs[i] : i;
-    /* sign, then zero-pad by p on each side */
+  for (int64_t n = 0; n < nimgs; n++) {
+    int64_t b = imgs ? imgs[n] : n;
+    /* sign, then zero-pad by ph rows and pw columns on each side */
     memset(xp, 0, sizeof(float) * (size_t)(C * Hp * Wp));
 #pragma omp parallel for schedule(static)
     for (int64_t c = 0; c < C; c++)
       for (int64_t ih = 0; ih < H; ih++)
         for (int64_t iw = 0; iw < W; iw++)
-          xp[(c * Hp + ih + p) * Wp + iw + p] = sgn(widen(x, xdt, ((b * C + c) * H + ih) * W + iw));
-    /* unfold with kernel ks, dilation d, stride s, stored transposed as cols[l][r] */
+          xp[(c * Hp + ih + ph) * Wp + iw + pw] = sgn(widen(x, xdt, ((b * C + c) * H + ih) * W + iw));
+    /* unfold: kernel KH x KW, dilation (dh, dw), stride (sh, sw), stored transposed as cols[l][r] */
 #pragma omp parallel for schedule(static)
     for (int64_t l = 0; l < L; l++) {
       int64_t oh = l / Wo, ow = l % Wo;
       for (int64_t c = 0; c < C; c++)
-        for (int64_t kh = 0; kh < ks; kh++)
-          for (int64_t kx = 0; kx < ks; kx++) {
-            int64_t r = (c * ks + kh) * ks + kx;
-            cols[l * R + r] = xp[(c * Hp + oh * s + kh * d) * Wp + ow * s + kx * d];
+        for (int64_t i = 0; i < KH; i++)
+          for (int64_t j = 0; j < KW; j++) {
+            int64_t r = (c * KH + i) * KW + j;
+            cols[l * R + r] = xp[(c * Hp + oh * sh + i * dh) * Wp + ow * sw + j * dw];
           }
     }
     /* [L, R] x [R, O] -> [L, O], written transposed as [O, Ho, Wo] */
@@ -268,7 +282,7 @@ int oracle_conv2d_acc(const void *x, int xdt, const void *w, int wdt, int64_t B,
         float sum = 0.0f;
 #pragma omp simd reduction(+ : sum)
         for (int64_t r = 0; r < R; r++) sum += cr[r] * wr[r];
-        acc[(i * O + o) * L + l] = (int32_t)sum;
+        acc[(n * O + o) * L + l] = (int32_t)sum;
       }
   }
   free(ws);
@@ -277,24 +291,38 @@ int oracle_conv2d_acc(const void *x, int xdt, const void *w, int wdt, int64_t B,
   return 0;
 }
 
-/* Number of real (unpadded) reduction terms per output pixel:
- * kv[oh][ow] = C * #{(kh,kw) : 0 <= oh*s - p + kh*d < H and 0 <= ow*s - p + kw*d < W}. */
-int oracle_conv2d_kvalid(int64_t C, int64_t H, int64_t W, int64_t ks, int64_t s, int64_t p,
-                         int64_t d, int32_t *kv) {
-  int64_t Ho = oracle_conv_out_size(H, ks, s, p, d);
-  int64_t Wo = oracle_conv_out_size(W, ks, s, p, d);
+/* Square kernels, one stride / padding / dilation for both axes. */
+int oracle_conv2d_acc(const void *x, int xdt, const void *w, int wdt, int64_t B, int64_t C,
+                      int64_t H, int64_t W, int64_t O, int64_t ks, int64_t s, int64_t p, int64_t d,
+                      const int64_t *imgs, int64_t nimgs, int32_t *acc) {
+  return oracle_conv2d_acc2(x, xdt, w, wdt, B, C, H, W, O, ks, ks, s, s, p, p, d, d, imgs, nimgs,
+                            acc);
+}
+
+/* Number of real (unpadded) reduction terms per output pixel, general form:
+ * kv[oh][ow] = C * #{(i,j) : 0 <= oh*sh - ph + i*dh < H and 0 <= ow*sw - pw + j*dw < W}. */
+int oracle_conv2d_kvalid2(int64_t C, int64_t H, int64_t W, int64_t KH, int64_t KW, int64_t sh,
+                          int64_t sw, int64_t ph, int64_t pw, int64_t dh, int64_t dw, int32_t *kv) {
+  int64_t Ho = oracle_conv_out_size(H, KH, sh, ph, dh);
+  int64_t Wo = oracle_conv_out_size(W, KW, sw, pw, dw);
   if (Ho <= 0 || Wo <= 0) return -1;
   for (int64_t oh = 0; oh < Ho; oh++)
     for (int64_t ow = 0; ow < Wo; ow++) {
       int64_t taps = 0;
-      for (int64_t kh = 0; kh < ks; kh++)
-        for (int64_t kx = 0; kx < ks; kx++) {
-          int64_t ih = oh * s - p + kh * d, iw = ow * s - p + kx * d;
+      for (int64_t i = 0; i < KH; i++)
+        for (int64_t j = 0; j < KW; j++) {
+          int64_t ih = oh * sh - ph + i * dh, iw = ow * sw - pw + j * dw;
           if (ih >= 0 && ih < H && iw >= 0 && iw < W) taps++;
         }
       kv[oh * Wo + ow] = (int32_t)(C * taps);
     }
   return 0;
+}
+
+/* Square kernels. */
+int oracle_conv2d_kvalid(int64_t C, int64_t H, int64_t W, int64_t ks, int64_t s, int64_t p,
+                         int64_t d, int32_t *kv) {
+  return oracle_conv2d_kvalid2(C, H, W, ks, ks, s, s, p, p, d, d, kv);
 }
 
 /* y[i] = acc[i] * (scale_a * scale_w), the product of the two scalar scales taken in double. */

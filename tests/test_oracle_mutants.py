@@ -32,19 +32,22 @@ MUTANTS = {
                        "if (sgn(widen(x, dtype, r * k + 32 * q + j)) > 0.0f) word |= (uint32_t)1 << (31 - j);"),
     "pack_nchw_hw_swapped": ("int64_t idx = ((b * C + 32 * q + j) * H + ih) * W + iw;",
                              "int64_t idx = ((b * C + 32 * q + j) * W + iw) * H + ih;"),
-    "pack_weight_kernel_transposed": ("int64_t idx = ((o * C + 32 * q + j) * ks + kh) * ks + kx;",
-                                      "int64_t idx = ((o * C + 32 * q + j) * ks + kx) * ks + kh;"),
+    "pack_weight_kernel_transposed": ("int64_t idx = ((o * C + 32 * q + jj) * KH + i) * KW + j;",
+                                      "int64_t idx = ((o * C + 32 * q + jj) * KW + j) * KH + i;"),
     "linear_drops_last_term": ("for (int64_t k = 0; k < K; k++) s += sx[k] * wr[k];",
                                "for (int64_t k = 0; k < K - 1; k++) s += sx[k] * wr[k];"),
     "linear_x_transposed": ("sx[k] = sgn(widen(x, xdt, m * K + k));",
                             "sx[k] = sgn(widen(x, xdt, (k % M) * K + (m * K + k) / M % K));"),
     "conv_pad_value_plus_one": ("memset(xp, 0, sizeof(float) * (size_t)(C * Hp * Wp));",
                                 "for (int64_t z = 0; z < C * Hp * Wp; z++) xp[z] = 1.0f;"),
-    "conv_unfold_without_dilation": ("cols[l * R + r] = xp[(c * Hp + oh * s + kh * d) * Wp + ow * s + kx * d];",
-                                     "cols[l * R + r] = xp[(c * Hp + oh * s + kh) * Wp + ow * s + kx];"),
-    "conv_ignores_column_stride": ("cols[l * R + r] = xp[(c * Hp + oh * s + kh * d) * Wp + ow * s + kx * d];",
-                                   "cols[l * R + r] = xp[(c * Hp + oh * s + kh * d) * Wp + ow + kx * d];"),
-    "conv_row_index_transposed": ("int64_t r = (c * ks + kh) * ks + kx;", "int64_t r = (c * ks + kx) * ks + kh;"),
+    "conv_unfold_without_dilation": ("cols[l * R + r] = xp[(c * Hp + oh * sh + i * dh) * Wp + ow * sw + j * dw];",
+                                     "cols[l * R + r] = xp[(c * Hp + oh * sh + i) * Wp + ow * sw + j];"),
+    "conv_ignores_column_stride": ("cols[l * R + r] = xp[(c * Hp + oh * sh + i * dh) * Wp + ow * sw + j * dw];",
+                                   "cols[l * R + r] = xp[(c * Hp + oh * sh + i * dh) * Wp + ow + j * dw];"),
+    "conv_row_index_transposed": ("int64_t r = (c * KH + i) * KW + j;", "int64_t r = (c * KW + j) * KH + i;"),
+    "conv_swaps_axis_strides": ("cols[l * R + r] = xp[(c * Hp + oh * sh + i * dh) * Wp + ow * sw + j * dw];",
+                                "cols[l * R + r] = xp[(c * Hp + oh * sw + i * dh) * Wp + ow * sh + j * dw];"),
+    "conv_pad_rows_by_columns": ("xp[(c * Hp + ih + ph) * Wp + iw + pw] =", "xp[(c * Hp + ih + pw) * Wp + iw + pw] ="),
     "kvalid_off_by_one": ("if (ih >= 0 && ih < H && iw >= 0 && iw < W) taps++;",
                           "if (ih >= 0 && ih <= H && iw >= 0 && iw < W) taps++;"),
     "scale_sum_instead_of_product": ("double alpha = scale_a * scale_w;", "double alpha = scale_a + scale_w;"),
@@ -172,6 +175,34 @@ def _pins(orc):
         return True
 
     check("conv_vs_torch", lib_conv)
+
+    def lib_conv_rect():
+        # non-square kernels, different strides / paddings / dilations per axis
+        rnd = random.Random(19)
+        gen = torch.Generator().manual_seed(19)
+        n = 0
+        while n < 25:
+            b, c, h, w = rnd.choice([1, 2]), rnd.choice([1, 3, 32]), rnd.randint(2, 8), rnd.randint(2, 8)
+            o, kh, kw = rnd.choice([1, 3]), rnd.choice([1, 2, 3]), rnd.choice([1, 2, 3, 4])
+            s, p, d = (rnd.choice([1, 2]), rnd.choice([1, 3])), (rnd.randint(0, 2), rnd.randint(0, 2)), (rnd.choice([1, 2]), rnd.choice([1, 3]))
+            if math.floor((h + 2 * p[0] - d[0] * (kh - 1) - 1) / s[0] + 1) <= 0 or \
+                    math.floor((w + 2 * p[1] - d[1] * (kw - 1) - 1) / s[1] + 1) <= 0:
+                continue
+            n += 1
+            x, wt = torch.randn((b, c, h, w), generator=gen), torch.randn((o, c, kh, kw), generator=gen)
+            ref = torch.nn.functional.conv2d(_lib_sign(x), _lib_sign(wt), stride=s, padding=p, dilation=d)
+            if not torch.equal(orc.conv2d_acc(x, wt, s, p, d).double(), ref):
+                return False
+            ones = torch.nn.functional.conv2d(torch.ones((1, c, h, w), dtype=torch.float64),
+                                              torch.ones((1, c, kh, kw), dtype=torch.float64),
+                                              stride=s, padding=p, dilation=d)[0, 0]
+            if not torch.equal(orc.conv2d_kvalid(c, h, w, (kh, kw), s, p, d).double(), ones):
+                return False
+        wc = torch.randn((3, 32, 2, 3), generator=gen)
+        return torch.equal(orc.pack_conv_weight(wc),
+                           orc.pack_rows(wc.permute(0, 2, 3, 1).contiguous().reshape(-1, 32)).view(3, 2, 3, 1))
+
+    check("conv_rect_vs_torch", lib_conv_rect)
 
     edges = _golden("shift_sign_edges.json")["cases"]
 

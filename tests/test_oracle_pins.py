@@ -394,3 +394,86 @@ def test_tail_popcount_identity(oracle_lib):
         b = oracle_lib.pack_rows(w).numpy().astype(np.uint32)
         pop = np.vectorize(lambda v: bin(int(v)).count("1"))(a[:, None, :] ^ b[None, :, :]).sum(-1)
         assert np.array_equal(k - 2 * pop, oracle_lib.linear_acc(x, w).numpy()), k
+
+
+# ---------------------------------------------------------------- non-square kernels, per-axis parameters
+
+def _direct_conv_rect(xs, ws, s, p, d):
+    """Direct definition with explicit bounds checks, (rows, columns) parameters."""
+    B, C, H, W = xs.shape
+    O, _, KH, KW = ws.shape
+    Ho = math.floor((H + 2 * p[0] - d[0] * (KH - 1) - 1) / s[0] + 1)
+    Wo = math.floor((W + 2 * p[1] - d[1] * (KW - 1) - 1) / s[1] + 1)
+    out = np.zeros((B, O, Ho, Wo), dtype=np.int64)
+    for b in range(B):
+        for o in range(O):
+            for oh in range(Ho):
+                for ow in range(Wo):
+                    tot = 0
+                    for i in range(KH):
+                        ih = oh * s[0] - p[0] + i * d[0]
+                        if ih < 0 or ih >= H:
+                            continue
+                        for j in range(KW):
+                            iw = ow * s[1] - p[1] + j * d[1]
+                            if iw < 0 or iw >= W:
+                                continue
+                            tot += int(np.dot(xs[b, :, ih, iw], ws[o, :, i, j]))
+                    out[b, o, oh, ow] = tot
+    return out
+
+
+def _rect_cases(count, seed):
+    rnd = random.Random(seed)
+    cases = []
+    while len(cases) < count:
+        b, c = rnd.choice([1, 2]), rnd.choice([1, 3, 32, 33])
+        h, w = rnd.randint(1, 8), rnd.randint(1, 8)
+        o, kh, kw = rnd.choice([1, 3]), rnd.choice([1, 2, 3, 5]), rnd.choice([1, 2, 3, 4])
+        s = (rnd.choice([1, 2, 3]), rnd.choice([1, 2, 3]))
+        p = (rnd.randint(0, 3), rnd.randint(0, 3))
+        d = (rnd.choice([1, 2, 3]), rnd.choice([1, 2, 3]))
+        ho = math.floor((h + 2 * p[0] - d[0] * (kh - 1) - 1) / s[0] + 1)
+        wo = math.floor((w + 2 * p[1] - d[1] * (kw - 1) - 1) / s[1] + 1)
+        if ho > 0 and wo > 0 and (kh != kw or s[0] != s[1] or p[0] != p[1] or d[0] != d[1]):
+            cases.append((b, c, h, w, o, kh, kw, s, p, d))
+    return cases
+
+
+def test_conv_rect_matches_direct_definition(oracle_lib):
+    g = torch.Generator().manual_seed(81)
+    for (b, c, h, w, o, kh, kw, s, p, d) in _rect_cases(50, 5):
+        x = torch.randn((b, c, h, w), generator=g)
+        wt = torch.randn((o, c, kh, kw), generator=g)
+        acc = oracle_lib.conv2d_acc(x, wt, s, p, d).numpy()
+        want = _direct_conv_rect(np.where(x.numpy() >= 0, 1, -1), np.where(wt.numpy() >= 0, 1, -1), s, p, d)
+        assert np.array_equal(acc, want), (b, c, h, w, o, kh, kw, s, p, d)
+
+
+def test_conv_rect_matches_torch_fp64_and_kvalid(oracle_lib):
+    g = torch.Generator().manual_seed(82)
+    for (b, c, h, w, o, kh, kw, s, p, d) in _rect_cases(200, 6):
+        dt = [torch.float32, torch.float16, torch.bfloat16][(b + c + h) % 3]
+        x = torch.randn((b, c, h, w), generator=g).to(dt)
+        wt = torch.randn((o, c, kh, kw), generator=g).to(dt)
+        acc = oracle_lib.conv2d_acc(x, wt, s, p, d)
+        ref = torch.nn.functional.conv2d(_lib_sign(x), _lib_sign(wt), stride=s, padding=p, dilation=d)
+        assert torch.equal(acc.double(), ref), (b, c, h, w, o, kh, kw, s, p, d)
+        ones = torch.nn.functional.conv2d(torch.ones((1, c, h, w), dtype=torch.float64),
+                                          torch.ones((1, c, kh, kw), dtype=torch.float64),
+                                          stride=s, padding=p, dilation=d)[0, 0]
+        assert torch.equal(oracle_lib.conv2d_kvalid(c, h, w, (kh, kw), s, p, d).double(), ones)
+    # equal parameters on both axes give the square entry's results
+    x = torch.randn((2, 32, 7, 6), generator=g)
+    wt = torch.randn((4, 32, 3, 3), generator=g)
+    assert torch.equal(oracle_lib.conv2d_acc(x, wt, (2, 2), (1, 1), (1, 1)), oracle_lib.conv2d_acc(x, wt, 2, 1, 1))
+
+
+def test_pack_conv_weight_rect_layout(oracle_lib):
+    g = torch.Generator().manual_seed(83)
+    for (kh, kw, c) in [(1, 3, 32), (3, 1, 64), (2, 5, 40), (5, 2, 7)]:
+        w = torch.randn((3, c, kh, kw), generator=g)
+        got = oracle_lib.pack_conv_weight(w)
+        assert got.shape == (3, kh, kw, (c + 31) // 32)
+        assert torch.equal(got, oracle_lib.pack_rows(w.permute(0, 2, 3, 1).contiguous().reshape(-1, c))
+                           .view(3, kh, kw, (c + 31) // 32))
