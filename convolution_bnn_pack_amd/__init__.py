@@ -34,7 +34,8 @@ PATH_AUTO, PATH_XOR, PATH_MFMA, PATH_MFMA_FP4 = 0, 1, 2, 3
 OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIGN, ERR_WORKSPACE, ERR_PATH, ERR_HIP = range(8)
 
 EXPORTS = ("bnn_pack_sign", "bnn_pack_sign_nchw", "bnn_pack_sign_shift", "bnn_pack_sign_nchw_shift",
-           "bnn_abs_mean_scale", "bnn_abs_mean_workspace_bytes", "bnn_w_pack", "bnn_gemm", "bnn_conv2d",
+           "bnn_abs_mean_scale", "bnn_abs_mean_workspace_bytes", "bnn_w_pack", "bnn_w_pack_conv",
+           "bnn_conv2d_ex", "bnn_gemm", "bnn_conv2d",
            "bnn_gemm_workspace_bytes", "bnn_conv2d_workspace_bytes", "bnn_gemm_auto_path",
            "bnn_conv2d_auto_path", "bnn_last_path", "bnn_status_string")
 
@@ -54,6 +55,8 @@ def _bind(path: str) -> ctypes.CDLL:
         "bnn_abs_mean_scale": ([P, I, I64, D, P, P, SZ, P], I),
         "bnn_abs_mean_workspace_bytes": ([I64], SZ),
         "bnn_w_pack": ([P, I, I64, I64, I, P, P], I),
+        "bnn_w_pack_conv": ([P, I, I64, I64, I, I, P, P], I),
+        "bnn_conv2d_ex": ([P, I, I64, I64, I64, I64, P, I64, D, D] + [I] * 9 + [P, I, P, SZ, P], I),
         "bnn_gemm": ([P, I, P, I64, I64, I64, D, D, I, P, I, P, SZ, P], I),
         "bnn_conv2d": ([P, I, I64, I64, I64, I64, P, I64, D, D, I, I, I, I, I, P, I, P, SZ, P], I),
         "bnn_gemm_workspace_bytes": ([I64, I64, I], SZ),
@@ -208,23 +211,26 @@ def abs_mean_scale(x: torch.Tensor, factor: float, out: torch.Tensor | None = No
 
 
 def w_pack(weight: torch.Tensor) -> torch.Tensor:
-    """Weight pack: linear [out, in] -> [out, in/32]; OIHW [out, in, k, k] -> [out, k, k, in/32]."""
+    """Weight pack: linear [out, in] -> [out, ceil(in/32)]; OIHW [out, in, kh, kw] ->
+    [out, kh, kw, ceil(in/32)] (square kernels through bnn_w_pack, others bnn_w_pack_conv)."""
     weight = _dev(weight, "weight")
+    code = _dtype_code(weight, "weight")
     if weight.dim() == 2:
         o, i = weight.shape
-        ks = 0
-        shape = (o, words(i))
+        out = torch.empty((o, words(i)), dtype=torch.int32, device=weight.device)
+        _check(lib.bnn_w_pack(weight.data_ptr(), code, o, i, 0, out.data_ptr(), _stream(weight)),
+               "bnn_w_pack")
     elif weight.dim() == 4:
         o, i, kh, kw = weight.shape
-        if kh != kw:
-            raise ValueError("square kernels only")
-        ks = kh
-        shape = (o, ks, ks, words(i))
+        out = torch.empty((o, kh, kw, words(i)), dtype=torch.int32, device=weight.device)
+        if kh == kw:
+            _check(lib.bnn_w_pack(weight.data_ptr(), code, o, i, kh, out.data_ptr(), _stream(weight)),
+                   "bnn_w_pack")
+        else:
+            _check(lib.bnn_w_pack_conv(weight.data_ptr(), code, o, i, kh, kw, out.data_ptr(),
+                                       _stream(weight)), "bnn_w_pack_conv")
     else:
         raise ValueError("weight must be 2-D (linear) or 4-D OIHW (conv)")
-    out = torch.empty(shape, dtype=torch.int32, device=weight.device)
-    _check(lib.bnn_w_pack(weight.data_ptr(), _dtype_code(weight, "weight"), o, i, ks, out.data_ptr(),
-                          _stream(weight)), "bnn_w_pack")
     return out
 
 
@@ -270,14 +276,24 @@ def gemm(x: torch.Tensor, w_packed: torch.Tensor, scale_a: float, scale_w: float
     return out
 
 
+def _pair(v, name):
+    if isinstance(v, int):
+        return v, v
+    if len(v) != 2:
+        raise ValueError(f"{name} must be an int or a (rows, columns) pair")
+    return int(v[0]), int(v[1])
+
+
 def conv2d(x: torch.Tensor, w_packed: torch.Tensor, scale_a: float, scale_w: float,
-           kernel_size: int, stride: int = 1, padding: int = 0, dilation: int = 1, path="auto",
+           kernel_size, stride=1, padding=0, dilation=1, path="auto",
            out_dtype=None, channels: int | None = None, out: torch.Tensor | None = None,
            workspace: torch.Tensor | None = None) -> torch.Tensor:
     """Binary conv2d forward, NCHW in and out; padded taps contribute 0.
 
     x is [n, c, h, w] float, or int32 [n, h, w, ceil(c/32)] already packed by
-    pack_sign_nchw. w_packed is int32 [o, k, k, ceil(c/32)] from w_pack.
+    pack_sign_nchw. w_packed is int32 [o, kh, kw, ceil(c/32)] from w_pack. kernel_size,
+    stride, padding and dilation are ints (bnn_conv2d) or (rows, columns) pairs
+    (bnn_conv2d_ex).
     """
     x = _dev(x, "x")
     w_packed = _dev(w_packed, "w_packed")
@@ -289,9 +305,11 @@ def conv2d(x: torch.Tensor, w_packed: torch.Tensor, scale_a: float, scale_w: flo
     else:
         n, c, h, w = x.shape
         xcode = _dtype_code(x, "x")
+    (kh, kw), (sh, sw) = _pair(kernel_size, "kernel_size"), _pair(stride, "stride")
+    (ph, pw), (dh, dw) = _pair(padding, "padding"), _pair(dilation, "dilation")
     o = w_packed.shape[0]
-    ho = (h + 2 * padding - dilation * (kernel_size - 1) - 1) // stride + 1
-    wo = (w + 2 * padding - dilation * (kernel_size - 1) - 1) // stride + 1
+    ho = (h + 2 * ph - dh * (kh - 1) - 1) // sh + 1 if sh > 0 else 0
+    wo = (w + 2 * pw - dw * (kw - 1) - 1) // sw + 1 if sw > 0 else 0
     if out_dtype is None:
         out_dtype = torch.float32 if packed else x.dtype
     if out is None:
@@ -301,12 +319,16 @@ def conv2d(x: torch.Tensor, w_packed: torch.Tensor, scale_a: float, scale_w: flo
     ws_bytes = lib.bnn_conv2d_workspace_bytes(n, c, h, w, xcode)
     if workspace is None and ws_bytes:
         workspace = _workspace(ws_bytes, x.device)
-    _check(lib.bnn_conv2d(x.data_ptr(), xcode, n, c, h, w, w_packed.data_ptr(), o, float(scale_a),
-                          float(scale_w), kernel_size, stride, padding, dilation, _path(path),
-                          out.data_ptr(), _DT[out.dtype],
-                          workspace.data_ptr() if workspace is not None else None,
-                          workspace.numel() if workspace is not None else 0, _stream(x)),
-           "bnn_conv2d")
+    wsp = workspace.data_ptr() if workspace is not None else None
+    wsn = workspace.numel() if workspace is not None else 0
+    common = (x.data_ptr(), xcode, n, c, h, w, w_packed.data_ptr(), o, float(scale_a), float(scale_w))
+    if kh == kw and sh == sw and ph == pw and dh == dw:
+        _check(lib.bnn_conv2d(*common, kh, sh, ph, dh, _path(path), out.data_ptr(), _DT[out.dtype],
+                              wsp, wsn, _stream(x)), "bnn_conv2d")
+    else:
+        _check(lib.bnn_conv2d_ex(*common, kh, kw, sh, sw, ph, pw, dh, dw, _path(path),
+                                 out.data_ptr(), _DT[out.dtype], wsp, wsn, _stream(x)),
+               "bnn_conv2d_ex")
     return out
 
 

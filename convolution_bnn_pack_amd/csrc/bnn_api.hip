@@ -207,9 +207,23 @@ bnn_status bnn_w_pack(const void* weight, int w_dtype, int64_t out_features, int
     return hip_status(pack_rows_any(weight, w_dtype, out_features, in_features, nullptr, 0, false,
                                     w_packed, s));
   }
-  if (!aligned(weight, elem_bytes(w_dtype))) return BNN_ERR_ALIGN;
+  return bnn_w_pack_conv(weight, w_dtype, out_features, in_features, kernel_size, kernel_size,
+                         w_packed, stream);
+}
+
+bnn_status bnn_w_pack_conv(const void* weight, int w_dtype, int64_t out_features,
+                           int64_t in_features, int kernel_h, int kernel_w, uint32_t* w_packed,
+                           void* stream) {
+  if (!float_dtype(w_dtype)) return BNN_ERR_DTYPE;
+  if (out_features < 0 || in_features <= 0 || kernel_h < 1 || kernel_w < 1) return BNN_ERR_SHAPE;
+  if (!int_fits((int64_t)kernel_h * kernel_w * words_of(in_features))) return BNN_ERR_SHAPE;
+  if (out_features == 0) return BNN_OK;
+  if (!weight || !w_packed) return BNN_ERR_NULL;
+  if (!aligned(w_packed, 4) || !aligned(weight, elem_bytes(w_dtype))) return BNN_ERR_ALIGN;
   return hip_status(bnn::launch_pack_conv_weight(weight, w_dtype, out_features, in_features,
-                                                 kernel_size, w_packed, s));
+                                                 kernel_h, kernel_w,
+                                                 static_cast<uint32_t*>(w_packed),
+                                                 static_cast<hipStream_t>(stream)));
 }
 
 bnn_status bnn_gemm(const void* x, int x_dtype, const uint32_t* w_packed, int64_t m, int64_t n,
@@ -254,28 +268,29 @@ bnn_status bnn_gemm(const void* x, int x_dtype, const uint32_t* w_packed, int64_
   return BNN_OK;
 }
 
-bnn_status bnn_conv2d(const void* x, int x_dtype, int64_t n, int64_t c, int64_t h, int64_t w,
-                      const uint32_t* w_packed, int64_t out_channels, double scale_a,
-                      double scale_w, int kernel_size, int stride, int padding, int dilation,
-                      int path, void* out, int out_dtype, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+bnn_status bnn_conv2d_ex(const void* x, int x_dtype, int64_t n, int64_t c, int64_t h, int64_t w,
+                         const uint32_t* w_packed, int64_t out_channels, double scale_a,
+                         double scale_w, int kernel_h, int kernel_w, int stride_h, int stride_w,
+                         int pad_h, int pad_w, int dil_h, int dil_w, int path, void* out,
+                         int out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
   if (!(float_dtype(x_dtype) || x_dtype == BNN_U32_PACKED) || !out_dtype_ok(out_dtype))
     return BNN_ERR_DTYPE;
   if (n < 0 || out_channels < 0 || c <= 0 || h <= 0 || w <= 0) return BNN_ERR_SHAPE;
-  if (kernel_size < 1 || stride < 1 || dilation < 1 || padding < 0) return BNN_ERR_SHAPE;
-  const int64_t ho = out_size(h, kernel_size, stride, padding, dilation);
-  const int64_t wo = out_size(w, kernel_size, stride, padding, dilation);
+  if (kernel_h < 1 || kernel_w < 1 || stride_h < 1 || stride_w < 1 || dil_h < 1 || dil_w < 1 ||
+      pad_h < 0 || pad_w < 0)
+    return BNN_ERR_SHAPE;
+  const int64_t ho = out_size(h, kernel_h, stride_h, pad_h, dil_h);
+  const int64_t wo = out_size(w, kernel_w, stride_w, pad_w, dil_w);
   if (ho <= 0 || wo <= 0) return BNN_ERR_SHAPE;
-  const int64_t kw_words = (int64_t)kernel_size * kernel_size * words_of(c);
+  const int64_t taps = (int64_t)kernel_h * kernel_w;
+  const int64_t kw_words = taps * words_of(c);
   if (!int_fits(n * ho * wo) || !int_fits(out_channels) || !int_fits(kw_words) ||
-      !int_fits(n * h * w * words_of(c)) || !int_fits(h + 2 * (int64_t)padding) ||
-      !int_fits(w + 2 * (int64_t)padding))
+      !int_fits(n * h * w * words_of(c)) || !int_fits(h + 2 * (int64_t)pad_h) ||
+      !int_fits(w + 2 * (int64_t)pad_w) || !int_fits(taps * c))
     return BNN_ERR_SHAPE;
   if (!path_known(path)) return BNN_ERR_PATH;
-  if (path == BNN_PATH_XOR && kernel_size * kernel_size > bnn::xor_conv_max_taps())
-    return BNN_ERR_PATH;
-  if (path == BNN_PATH_MFMA_FP4 && (int64_t)kernel_size * kernel_size * c > bnn::kMaxFp4K)
-    return BNN_ERR_PATH;
+  if (path == BNN_PATH_XOR && taps > bnn::xor_conv_max_taps()) return BNN_ERR_PATH;
+  if (path == BNN_PATH_MFMA_FP4 && taps * c > bnn::kMaxFp4K) return BNN_ERR_PATH;
   if (n == 0 || out_channels == 0) return BNN_OK;
   if (!x || !w_packed || !out) return BNN_ERR_NULL;
   const bool packed = x_dtype == BNN_U32_PACKED;
@@ -285,10 +300,7 @@ bnn_status bnn_conv2d(const void* x, int x_dtype, int64_t n, int64_t c, int64_t 
   if (need > 0 && (!workspace || workspace_bytes < need)) return BNN_ERR_WORKSPACE;
   if (need > 0 && !aligned(workspace, 4)) return BNN_ERR_ALIGN;
 
-  const int use = path == BNN_PATH_AUTO
-                      ? bnn_conv2d_auto_path(n, c, h, w, out_channels, kernel_size, stride,
-                                             padding, dilation)
-                      : path;
+  const int use = path == BNN_PATH_AUTO ? auto_path(taps * c) : path;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const uint32_t* a = static_cast<const uint32_t*>(x);
   if (!packed) {
@@ -311,14 +323,28 @@ bnn_status bnn_conv2d(const void* x, int x_dtype, int64_t n, int64_t c, int64_t 
   p.CW = (int)words_of(c);
   p.Ho = (int)ho;
   p.Wo = (int)wo;
-  p.ks = kernel_size;
-  p.stride = stride;
-  p.pad = padding;
-  p.dil = dilation;
+  p.KH = kernel_h;
+  p.KWD = kernel_w;
+  p.SH = stride_h;
+  p.SW = stride_w;
+  p.PH = pad_h;
+  p.PW = pad_w;
+  p.DH = dil_h;
+  p.DW = dil_w;
   const hipError_t e = run_path(use, p, true, out_dtype, s);
   if (e != hipSuccess) return BNN_ERR_HIP;
   g_last_path = use;
   return BNN_OK;
+}
+
+bnn_status bnn_conv2d(const void* x, int x_dtype, int64_t n, int64_t c, int64_t h, int64_t w,
+                      const uint32_t* w_packed, int64_t out_channels, double scale_a,
+                      double scale_w, int kernel_size, int stride, int padding, int dilation,
+                      int path, void* out, int out_dtype, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  return bnn_conv2d_ex(x, x_dtype, n, c, h, w, w_packed, out_channels, scale_a, scale_w,
+                       kernel_size, kernel_size, stride, stride, padding, padding, dilation,
+                       dilation, path, out, out_dtype, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

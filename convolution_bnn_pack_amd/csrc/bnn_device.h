@@ -139,8 +139,8 @@ template <> struct OutType<kBF16> {
 // Shape of one contraction, shared by the GEMM and the implicit-im2col conv.
 // Linear: A is packed activations [M][KW], W is packed weights [N][KW].
 // Conv:   A is packed activations [B][H][W][CW] read through the implicit
-//         im2col map; the reduction index q = tap * CW + cw with tap = kh*ks + kw;
-//         W is [N][ks][ks][CW] = [N][KW]; M = B*Ho*Wo, output is NCHW.
+//         im2col map; the reduction index q = tap * CW + cw with tap = kh*KWD + kw;
+//         W is [N][KH][KWD][CW] = [N][KW]; M = B*Ho*Wo, output is NCHW.
 // KB is the true number of signs per packed row (linear: K) or per tap (conv: C); when it is
 // not a whole number of words, the last word of a row (of a tap) holds KB % 32 signs and
 // zero bits above them in both operands.
@@ -152,7 +152,8 @@ struct Contraction {
   int KB;
   float alpha;
   // conv only
-  int H, W, CW, Ho, Wo, ks, stride, pad, dil;
+  // kernel KH x KWD, stride (SH, SW), padding (PH, PW), dilation (DH, DW) along (rows, columns)
+  int H, W, CW, Ho, Wo, KH, KWD, SH, SW, PH, PW, DH, DW;
 };
 
 }  // namespace bnn

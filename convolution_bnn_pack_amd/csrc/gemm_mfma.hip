@@ -112,7 +112,7 @@ __device__ __forceinline__ PixelCoord pixel_coord(const Contraction& p, int m) {
   const int r = m - b * hw;
   const int oh = r / p.Wo;
   const int ow = r - oh * p.Wo;
-  return {b, oh * p.stride - p.pad, ow * p.stride - p.pad};
+  return {b, oh * p.SH - p.PH, ow * p.SW - p.PW};
 }
 
 __device__ __forceinline__ int clampi(int v, int hi) { return v < 0 ? 0 : (v > hi ? hi : v); }
@@ -147,11 +147,11 @@ __device__ __forceinline__ void load_a(const Contraction& p, int m, bool mok, co
   if constexpr (CONV) {
     int tap = q0 / p.CW;
     int cw = q0 - tap * p.CW;
-    int kh = tap / p.ks;
-    int kw = tap - kh * p.ks;
+    int kh = tap / p.KWD;
+    int kw = tap - kh * p.KWD;
     if constexpr (VEC) {
       // the NW words share one tap
-      const int ih = pc.ihb + kh * p.dil, iw = pc.iwb + kw * p.dil;
+      const int ih = pc.ihb + kh * p.DH, iw = pc.iwb + kw * p.DW;
       const bool tok = mok && q0 < p.KW && ih >= 0 && ih < p.H && iw >= 0 && iw < p.W;
       const int cwc = q0 < p.KW ? cw : 0;
       load_vec<NW>(p.a + (((int64_t)pc.b * p.H + clampi(ih, p.H - 1)) * p.W + clampi(iw, p.W - 1)) * p.CW + cwc, r);
@@ -161,12 +161,12 @@ __device__ __forceinline__ void load_a(const Contraction& p, int m, bool mok, co
 #pragma unroll
       for (int i = 0; i < NW; i++) {
         const int q = q0 + i;
-        const int ih = pc.ihb + kh * p.dil, iw = pc.iwb + kw * p.dil;
+        const int ih = pc.ihb + kh * p.DH, iw = pc.iwb + kw * p.DW;
         ok[i] = mok && q < p.KW && ih >= 0 && ih < p.H && iw >= 0 && iw < p.W;
         r[i] = p.a[(((int64_t)pc.b * p.H + clampi(ih, p.H - 1)) * p.W + clampi(iw, p.W - 1)) * p.CW + cw];
         if (++cw == p.CW) {
           cw = 0;
-          if (++kw == p.ks) {
+          if (++kw == p.KWD) {
             kw = 0;
             ++kh;
           }
@@ -677,9 +677,12 @@ __global__ __launch_bounds__(T::THREADS) void mfma_kernel(Contraction p) {
       int units = 1;
       if constexpr (CONV) {
         int nh = 0, nw = 0;
-        for (int k = 0; k < p.ks; k++) {
-          const int ih = pc.ihb + k * p.dil, iw = pc.iwb + k * p.dil;
+        for (int k = 0; k < p.KH; k++) {
+          const int ih = pc.ihb + k * p.DH;
           nh += (ih >= 0 && ih < p.H);
+        }
+        for (int k = 0; k < p.KWD; k++) {
+          const int iw = pc.iwb + k * p.DW;
           nw += (iw >= 0 && iw < p.W);
         }
         units = nh * nw;

@@ -37,7 +37,7 @@ __device__ __forceinline__ PixelCoord pixel_coord(const Contraction& p, int m) {
   const int r = m - b * hw;
   const int oh = r / p.Wo;
   const int ow = r - oh * p.Wo;
-  return {b, oh * p.stride - p.pad, ow * p.stride - p.pad};
+  return {b, oh * p.SH - p.PH, ow * p.SW - p.PW};
 }
 
 // Load 4 consecutive reduction words q0..q0+3 of A row m (0 outside the matrix or for padded taps).
@@ -53,17 +53,17 @@ __device__ __forceinline__ void load_a4(const Contraction& p, int m, const Pixel
   } else {
     int tap = q0 / p.CW;
     int cw = q0 - tap * p.CW;
-    int kh = tap / p.ks;
-    int kw = tap - kh * p.ks;
+    int kh = tap / p.KWD;
+    int kw = tap - kh * p.KWD;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       const int q = q0 + i;
-      const int ih = pc.ihb + kh * p.dil, iw = pc.iwb + kw * p.dil;
+      const int ih = pc.ihb + kh * p.DH, iw = pc.iwb + kw * p.DW;
       const bool ok = m < p.M && q < p.KW && ih >= 0 && ih < p.H && iw >= 0 && iw < p.W;
       r[i] = ok ? p.a[(((int64_t)pc.b * p.H + ih) * p.W + iw) * p.CW + cw] : 0u;
       if (++cw == p.CW) {
         cw = 0;
-        if (++kw == p.ks) {
+        if (++kw == p.KWD) {
           kw = 0;
           ++kh;
         }
@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256) void xor_kernel(Contraction p) {
   PixelCoord pc{0, 0, 0};
   if constexpr (CONV) {
     if (am < p.M) pc = pixel_coord(p, am);
-    const int taps = p.ks * p.ks;
+    const int taps = p.KH * p.KWD;
     for (int i = tid; i < taps * BN; i += 256) {
       const int t = i / BN, nl = i - t * BN;
       const int n = n0 + nl;
@@ -174,15 +174,15 @@ __global__ __launch_bounds__(256) void xor_kernel(Contraction p) {
 #pragma unroll
       for (int j = 0; j < 8; j++) corr[j] = 0;
       int valid_taps = 0;
-      for (int kh = 0; kh < p.ks; kh++) {
-        const int ih = q.ihb + kh * p.dil;
+      for (int kh = 0; kh < p.KH; kh++) {
+        const int ih = q.ihb + kh * p.DH;
         const bool hok = ih >= 0 && ih < p.H;
-        for (int kw = 0; kw < p.ks; kw++) {
-          const int iw = q.iwb + kw * p.dil;
+        for (int kw = 0; kw < p.KWD; kw++) {
+          const int iw = q.iwb + kw * p.DW;
           if (hok && iw >= 0 && iw < p.W) {
             valid_taps++;
           } else {
-            const int t = kh * p.ks + kw;
+            const int t = kh * p.KWD + kw;
 #pragma unroll
             for (int j = 0; j < 8; j++) corr[j] += Ps[t][j < 4 ? tx * 4 + j : 64 + tx * 4 + (j - 4)];
           }

@@ -38,8 +38,8 @@ int abs_mean_parts(int64_t count);
 hipError_t launch_abs_mean(const void* x, int dtype, int64_t count, double factor, double* partial,
                            double* out, hipStream_t stream);
 
-// OIHW conv weight pack: [o][c][ks][ks] -> [o][ks][ks][ceil(c/32)].
-hipError_t launch_pack_conv_weight(const void* w, int dtype, int64_t o, int64_t c, int ks,
+// OIHW conv weight pack: [o][c][kh][kw] -> [o][kh][kw][ceil(c/32)].
+hipError_t launch_pack_conv_weight(const void* w, int dtype, int64_t o, int64_t c, int kh, int kw,
                                    uint32_t* out, hipStream_t stream);
 
 // XOR + popcount contraction on the vector ALUs.

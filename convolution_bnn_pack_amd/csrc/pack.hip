@@ -384,6 +384,71 @@ __global__ __launch_bounds__(256) void abs_mean_final_kernel(const double* __res
   if (threadIdx.x == 0) out[0] = factor * (t / count);
 }
 
+// NCHW pack over the flattened (image, pixel) axis, for planes whose pixel count is a
+// multiple of the 16-byte vector width V (and a 16-byte aligned tensor): a workgroup packs
+// word q of 64*V consecutive pixels of the whole batch, each lane's V pixels lying in one
+// image, so no chunk is left partly empty at the end of an image plane (with 28x28 planes
+// and 512-pixel chunks per image, a quarter of the lanes idled). Otherwise as
+// pack_nchw_kernel: wave w loads channels 8w..8w+7 of the word with eight 16-byte loads
+// in flight, bytes meet in LDS, words leave in pixel order.
+template <int DT, int V, int BDT>
+__global__ __launch_bounds__(256) void pack_nchw_flat_kernel(const void* __restrict__ x,
+                                                             uint32_t* __restrict__ out, int C,
+                                                             int HW, int CW, int P,
+                                                             const void* __restrict__ bias) {
+  constexpr int ES = (DT == kF32) ? 4 : 2;
+  constexpr int PIX = 64 * V;
+  static_assert(V * ES == 16, "one 16-byte vector per lane and channel");
+  __shared__ uint32_t words[PIX];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nchunks = (P + PIX - 1) / PIX;
+  for (int q = blockIdx.y; q < CW; q += gridDim.y) {
+    const int c0 = 32 * q + 8 * wave;
+    const int nch = C - c0 < 8 ? C - c0 : 8;  // fewer only in a last, partly filled word
+    float shift[8];
+    if constexpr (BDT >= 0) {
+#pragma unroll
+      for (int c = 0; c < 8; c++) shift[c] = c < nch ? elem_f32<BDT>(bias, c0 + c) + 0.0f : 0.0f;
+    }
+    for (int ch = blockIdx.x; ch < nchunks; ch += gridDim.x) {
+      const int f0 = ch * PIX + lane * V;
+      const bool ok = f0 < P;
+      const int b = ok ? f0 / HW : 0;
+      const int pix = f0 - b * HW;
+      const char* src0 = reinterpret_cast<const char*>(x) + (((int64_t)b * C + c0) * HW + pix) * ES;
+      uint32_t bits[8];
+#pragma unroll
+      for (int c = 0; c < 8; c++) {
+        if (ok && c < nch) {
+          const u32x4 v = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4*>(src0 + (int64_t)c * HW * ES));
+          if constexpr (BDT >= 0)
+            bits[c] = vec_bits_shift<DT, V, false>(v, &shift[c]);
+          else
+            bits[c] = vec_bits<DT>(v);
+        } else {
+          bits[c] = 0u;
+        }
+      }
+      uint8_t* wbytes = reinterpret_cast<uint8_t*>(words);
+#pragma unroll
+      for (int v = 0; v < V; v++) {
+        uint32_t byte = 0;
+#pragma unroll
+        for (int c = 0; c < 8; c++) byte |= ((bits[c] >> v) & 1u) << c;
+        wbytes[(lane * V + v) * 4 + wave] = (uint8_t)byte;
+      }
+      __syncthreads();
+      for (int i = threadIdx.x; i < PIX; i += 256) {
+        const int f = ch * PIX + i;
+        if (f < P) out[(int64_t)f * CW + q] = words[i];
+      }
+      __syncthreads();
+    }
+  }
+}
+
 // OIHW weight pack: word (o, tap, q) collects w[o][32q + j][tap] into bit j (channels at or
 // past C give 0 bits).
 // Runs once per layer, off the forward path.
@@ -441,6 +506,24 @@ void launch_nchw_b(dim3 grid, const void* x, uint32_t* out, int64_t c, int64_t H
   }
 }
 
+template <int DT, int V, int BDT>
+void launch_nchw_flat_t(dim3 grid, const void* x, uint32_t* out, int64_t c, int64_t HW, int64_t CW,
+                        int64_t P, const void* bias, hipStream_t stream) {
+  hipLaunchKernelGGL((pack_nchw_flat_kernel<DT, V, BDT>), grid, dim3(256), 0, stream, x, out, (int)c,
+                     (int)HW, (int)CW, (int)P, bias);
+}
+
+template <int DT, int V>
+void launch_nchw_flat_b(dim3 grid, const void* x, uint32_t* out, int64_t c, int64_t HW, int64_t CW,
+                        int64_t P, const void* bias, int bdtype, hipStream_t stream) {
+  switch (bdtype) {
+    case kF32: launch_nchw_flat_t<DT, V, kF32>(grid, x, out, c, HW, CW, P, bias, stream); break;
+    case kF16: launch_nchw_flat_t<DT, V, kF16>(grid, x, out, c, HW, CW, P, bias, stream); break;
+    case kBF16: launch_nchw_flat_t<DT, V, kBF16>(grid, x, out, c, HW, CW, P, bias, stream); break;
+    default: launch_nchw_flat_t<DT, V, -1>(grid, x, out, c, HW, CW, P, nullptr, stream); break;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_pack_nchw(const void* x, int dtype, int64_t b, int64_t c, int64_t h, int64_t w,
@@ -456,10 +539,14 @@ hipError_t launch_pack_nchw(const void* x, int dtype, int64_t b, int64_t c, int6
   const dim3 grid((unsigned)(nchunks < 65535 ? nchunks : 65535), (unsigned)(nbq < 65535 ? nbq : 65535));
   if (!bias) bdtype = -1;
   if (vec) {
+    // flattened pixel chunks (the sizes fit in int: the C ABI checks n*h*w*ceil(c/32))
+    const int64_t P = b * HW;
+    const int64_t fchunks = (P + 64 * V - 1) / (64 * V);
+    const dim3 fgrid((unsigned)(fchunks < 65535 ? fchunks : 65535), (unsigned)(CW < 65535 ? CW : 65535));
     switch (dtype) {
-      case kF32: launch_nchw_b<kF32, 4>(grid, x, out, c, HW, CW, nbq, bias, bdtype, stream); break;
-      case kF16: launch_nchw_b<kF16, 8>(grid, x, out, c, HW, CW, nbq, bias, bdtype, stream); break;
-      default: launch_nchw_b<kBF16, 8>(grid, x, out, c, HW, CW, nbq, bias, bdtype, stream); break;
+      case kF32: launch_nchw_flat_b<kF32, 4>(fgrid, x, out, c, HW, CW, P, bias, bdtype, stream); break;
+      case kF16: launch_nchw_flat_b<kF16, 8>(fgrid, x, out, c, HW, CW, P, bias, bdtype, stream); break;
+      default: launch_nchw_flat_b<kBF16, 8>(fgrid, x, out, c, HW, CW, P, bias, bdtype, stream); break;
     }
   } else {
     switch (dtype) {
@@ -599,9 +686,9 @@ hipError_t launch_abs_mean(const void* x, int dtype, int64_t count, double facto
   return hipGetLastError();
 }
 
-hipError_t launch_pack_conv_weight(const void* w, int dtype, int64_t o, int64_t c, int ks,
+hipError_t launch_pack_conv_weight(const void* w, int dtype, int64_t o, int64_t c, int kh, int kw,
                                    uint32_t* out, hipStream_t stream) {
-  const int T = ks * ks;
+  const int T = kh * kw;
   const int64_t CW = (c + 31) / 32;
   const int64_t total = o * T * CW;
   if (total == 0) return hipSuccess;

@@ -174,6 +174,26 @@ bnn_status bnn_conv2d(const void* x, int x_dtype, int64_t n, int64_t c, int64_t 
                       int path, void* out, int out_dtype, void* workspace,
                       size_t workspace_bytes, void* stream);
 
+/* Binary conv2d forward, general geometry: a kernel_h x kernel_w kernel with stride, padding and
+ * dilation given per axis (rows, then columns); each output extent follows the formula above along
+ * its axis, Ho from (h, kernel_h, stride_h, pad_h, dil_h) and Wo from the column values. The layer
+ * page's single ints are the square case, which bnn_conv2d passes here unchanged. Arguments, layouts
+ * and errors otherwise as bnn_conv2d, with w_packed [out_channels, kernel_h, kernel_w, ceil(c/32)]
+ * from bnn_w_pack_conv. BNN_PATH_XOR needs kernel_h * kernel_w <= 49; BNN_PATH_MFMA_FP4 needs
+ * kernel_h * kernel_w * c <= 2^24; AUTO picks by that K as for bnn_conv2d. */
+bnn_status bnn_conv2d_ex(const void* x, int x_dtype, int64_t n, int64_t c, int64_t h, int64_t w,
+                         const uint32_t* w_packed, int64_t out_channels, double scale_a,
+                         double scale_w, int kernel_h, int kernel_w, int stride_h, int stride_w,
+                         int pad_h, int pad_w, int dil_h, int dil_w, int path, void* out,
+                         int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Conv weight pack for any kernel shape: OIHW [out_features, in_features, kernel_h, kernel_w] ->
+ * [out_features, kernel_h, kernel_w, ceil(in_features/32)] (bits past in_features 0); weight
+ * aligned to its element size. bnn_w_pack with kernel_size >= 1 is the square case. */
+bnn_status bnn_w_pack_conv(const void* weight, int w_dtype, int64_t out_features,
+                           int64_t in_features, int kernel_h, int kernel_w, uint32_t* w_packed,
+                           void* stream);
+
 /* Workspace sizes (bytes) for the calls above; 0 when x is already packed. */
 size_t bnn_gemm_workspace_bytes(int64_t m, int64_t k, int x_dtype);
 size_t bnn_conv2d_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w, int x_dtype);

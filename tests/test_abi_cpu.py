@@ -117,6 +117,31 @@ def test_conv_argument_checks(bnn):
     assert _conv(bnn, o=0, x=None, out=None) == bnn.OK
 
 
+def test_conv_ex_argument_checks(bnn):
+    L = bnn.lib
+
+    def conv_ex(**kw):
+        a = dict(x=FAKE, x_dtype=bnn.F32, n=2, c=64, h=14, w=14, wp=FAKE, o=32, kh=3, kw=1, sh=1, sw=2,
+                 ph=1, pw=0, dh=1, dw=1, path=bnn.PATH_AUTO, out=FAKE, out_dtype=bnn.F32, ws=FAKE,
+                 ws_bytes=1 << 20)
+        a.update(kw)
+        return L.bnn_conv2d_ex(a["x"], a["x_dtype"], a["n"], a["c"], a["h"], a["w"], a["wp"], a["o"],
+                               1.0, 1.0, a["kh"], a["kw"], a["sh"], a["sw"], a["ph"], a["pw"], a["dh"],
+                               a["dw"], a["path"], a["out"], a["out_dtype"], a["ws"], a["ws_bytes"], None)
+    for bad in (dict(kw=0), dict(kh=0), dict(sw=0), dict(sh=0), dict(dw=0), dict(dh=0), dict(pw=-1),
+                dict(ph=-1), dict(w=2, kw=5, pw=0), dict(h=1, kh=3, ph=0)):
+        assert conv_ex(**bad) == bnn.ERR_SHAPE, bad
+    assert conv_ex(kh=7, kw=8, ph=3, pw=3, path=bnn.PATH_XOR) == bnn.ERR_PATH    # 56 taps > 49
+    assert conv_ex(c=1 << 20, kh=5, kw=4, ph=2, pw=2, path=bnn.PATH_MFMA_FP4) == bnn.ERR_PATH
+    assert conv_ex(wp=None) == bnn.ERR_NULL                                      # shapes accepted
+    assert conv_ex(n=0, x=None, out=None) == bnn.OK
+    assert L.bnn_w_pack_conv(FAKE, bnn.F32, 8, 64, 3, 0, FAKE, None) == bnn.ERR_SHAPE
+    assert L.bnn_w_pack_conv(FAKE, bnn.I32, 8, 64, 3, 2, FAKE, None) == bnn.ERR_DTYPE
+    assert L.bnn_w_pack_conv(None, bnn.F32, 8, 64, 3, 2, FAKE, None) == bnn.ERR_NULL
+    assert L.bnn_w_pack_conv(FAKE + 2, bnn.F32, 8, 64, 3, 2, FAKE, None) == bnn.ERR_ALIGN
+    assert L.bnn_w_pack_conv(None, bnn.F32, 0, 64, 3, 2, None, None) == bnn.OK
+
+
 def test_pack_argument_checks(bnn):
     L = bnn.lib
     assert L.bnn_pack_sign(None, bnn.F32, 4, 33, FAKE, None) == bnn.ERR_NULL     # ragged k accepted
