@@ -39,6 +39,7 @@ CODEC_WORKLOADS = {
     "pack_linear_16384x8192_bf16": ("pack", "linear_16384x8192x8192_bf16", None),
     "pack_shift_linear_16384x8192_bf16": ("pack_shift", "linear_16384x8192x8192_bf16", "f32"),
     "pack_nchw_128x128x28x28_f16": ("pack_nchw", "conv_down_s2_f16", None),
+    "pack_nchw_32x256x14x14_f32": ("pack_nchw", "conv_resnet18_s3_f32", None),
     "pack_shift_nchw_128x128x28x28_f16": ("pack_nchw", "conv_down_s2_f16", "f16"),
     "abs_mean_16384x8192_bf16": ("abs_mean", "linear_16384x8192x8192_bf16", None),
 }
@@ -49,7 +50,7 @@ KERNEL_SOURCES = {"mfma": "gemm_mfma.hip", "mfma_fp4": "gemm_mfma.hip", "xor": "
                   "abs_mean": "pack.hip"}
 KERNEL_NAMES = {"mfma": "mfma_kernel", "mfma_fp4": "mfma_kernel", "xor": "xor_kernel",
                 "pack": "pack_rows_kernel", "pack_shift": "pack_rows_shift_kernel",
-                "pack_nchw": "pack_nchw_kernel", "abs_mean": "abs_sum_kernel"}
+                "pack_nchw": "pack_nchw_flat_kernel", "abs_mean": "abs_sum_kernel"}
 PEAKS = {"mfma": PEAK_MFMA_I8_TOPS, "mfma_fp4": PEAK_MFMA_F4_TOPS, "xor": PEAK_VALU_BINARY_TOPS}
 DTYPES = {"mfma": "i8", "mfma_fp4": "fp4(e2m1)", "xor": "u32"}
 CODEC_KINDS = ("pack", "pack_shift", "pack_nchw", "abs_mean")
@@ -98,22 +99,26 @@ def pmc_summary(args):
     import statistics
 
     def read(path, counter):
-        vals = {}
+        vals, order = {}, {}
         for r in csv.DictReader(open(path)):
             if r["Counter_Name"] != counter:
                 continue
             vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
-        return vals
+            order.setdefault(r["Kernel_Name"], []).append(int(r["Dispatch_Id"]))
+        return vals, order
 
     wl = args.workload
     kind = CODEC_WORKLOADS[wl][0] if wl in CODEC_WORKLOADS else None
     out = {}
     for counter, path in (("FETCH_SIZE", args.pmc_summary[0]), ("WRITE_SIZE", args.pmc_summary[1])):
-        vals = read(path, counter)
-        copy = [v for k, vs in vals.items() if args.copy_kernel in k for v in vs]
+        vals, order = read(path, counter)
+        # the five calibration copies are the last copy dispatches of the run (copies made
+        # while setting up the workload, e.g. of the activation, come earlier)
+        copy = sorted((d, v) for k, vs in vals.items() if args.copy_kernel in k
+                      for d, v in zip(order[k], vs))[-5:]
         if not copy:
             raise SystemExit(f"no {args.copy_kernel} kernel in {path}")
-        copy_kib = statistics.median(copy)
+        copy_kib = statistics.median(v for _, v in copy)
         scale = (args.copy_mib << 20) / 1024.0 / copy_kib if args.copy_mib else 1.0
         for k in ([kind] if kind else ["mfma", "mfma_fp4", "xor"]):
             # the workload's kernel is the instantiation launched most often (the parity spot
