@@ -20,8 +20,8 @@
  *    -1. (The layers pack weights once, ahead of the forward, with a native
  *    bit-packing kernel: BinaryConv2dCutlass.generate_quantized_weight on
  *    the qconv/binary/cutlass/layer page, BinaryLinearCuda.w_pack on the
- *    BinaryLinearCuda page. The word width 32 and the bit order are this
- *    build's reading; the pages fix neither.) A reduction length that is
+ *    BinaryLinearCuda page. The word width 32 and the bit order are a
+ *    reading taken here; the pages fix neither.) A reduction length that is
  *    not a whole number of words (the CUTLASS layer asserts that it is)
  *    leaves the missing bits of the last word 0: in both operands, so a
  *    XOR of the two sets no bit there, and the contraction itself still
