@@ -14,6 +14,7 @@ import pytest
 import torch
 
 import synth
+from parity_check import check_scaled
 
 pytestmark = pytest.mark.gpu
 
@@ -35,27 +36,6 @@ def orc(oracle_lib):
 
 def _say(msg):
     print(msg, flush=True)
-
-
-def _ulp(y: np.ndarray, frac_bits: int, min_spacing: float) -> np.ndarray:
-    mant, exp = np.frexp(np.abs(y))                      # |y| = mant * 2^exp, mant in [0.5, 1)
-    return np.maximum(np.ldexp(1.0, exp - 1 - frac_bits), min_spacing)
-
-
-def check_scaled(out: torch.Tensor, acc: torch.Tensor, y: torch.Tensor, what: str):
-    o = out.detach().cpu().double().numpy()
-    yy = y.numpy()
-    a = acc.numpy()
-    assert o.shape == yy.shape, what
-    assert np.all(o[a == 0] == 0.0), f"{what}: zero accumulators must give exact 0"
-    if out.dtype == torch.float32:
-        err = np.abs(o - yy)
-        bad = err > 1e-6 * np.abs(yy)
-    elif out.dtype == torch.float16:
-        bad = np.abs(o - yy) > _ulp(yy, 10, 2.0 ** -24)
-    else:
-        bad = np.abs(o - yy) > _ulp(yy, 7, 2.0 ** -133)
-    assert not bad.any(), f"{what}: {int(bad.sum())} outputs outside tolerance, first at {np.argwhere(bad)[0]}"
 
 
 # ----------------------------------------------------------------------------- packing
