@@ -241,6 +241,8 @@ __global__ __launch_bounds__(256) void pack_rows_ragged_kernel(const void* __res
 //
 // BDT >= 0: the shifted form, channel c adding bias[c] (element type BDT) before the
 // sign; the shift is uniform across a wave, so it is one scalar load per channel.
+// The launcher uses this kernel with V = 1 (planes whose pixel count is not a multiple of
+// the 16-byte vector width, or an unaligned tensor); pack_nchw_flat_kernel takes the rest.
 template <int DT, int V, int BDT = -1>
 __global__ __launch_bounds__(256) void pack_nchw_kernel(const void* __restrict__ x,
                                                         uint32_t* __restrict__ out, int64_t C,
