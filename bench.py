@@ -73,8 +73,15 @@ def log(msg):
 
 
 def src_sha(kind):
+    """Hash of the kernel's source file with comments and blank lines removed, so that a
+    traffic record survives comment edits but not code changes."""
     path = os.path.join(ROOT, "convolution_bnn_pack_amd", "csrc", KERNEL_SOURCES[kind])
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    code = []
+    for line in open(path).read().splitlines():
+        line = line.split("//", 1)[0].rstrip()
+        if line:
+            code.append(line)
+    return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 
 def traffic_for(kind, workload):
