@@ -60,6 +60,10 @@ def _bind(lib):
     lib.oracle_conv2d_kvalid2.argtypes = [I64] * 11 + [P]
     lib.oracle_conv2d_kvalid2.restype = I
     lib.oracle_pack_conv_weight2.argtypes = [P, I, I64, I64, I64, I64, P]
+    lib.oracle_quant_i8.argtypes = [P, I, I64, ctypes.c_float, P]
+    lib.oracle_w8a8_conv2d_acc.argtypes = [P, I, P, I] + [I64] * 13 + [ctypes.c_float, ctypes.c_float,
+                                                                       P, I64, P]
+    lib.oracle_w8a8_conv2d_acc.restype = I
     lib.oracle_scale.argtypes = [P, I64, ctypes.c_double, ctypes.c_double, P]
     lib.oracle_pack_rows_shift.argtypes = [P, I, I64, I64, P, I, I64, P]
     lib.oracle_pack_nchw_shift.argtypes = [P, I, I64, I64, I64, I64, P, I, P]
@@ -262,3 +266,35 @@ def abs_mean_scale(x: torch.Tensor, factor: float) -> float:
     """factor * mean(|x|) over every element (the sum in double, in index order)."""
     x = _cpu(x)
     return float(_load().oracle_abs_mean_scale(x.data_ptr(), _code(x), x.numel(), float(factor)))
+
+
+def quant_i8(x: torch.Tensor, amax: float) -> torch.Tensor:
+    """int8 codes of the symmetric per-tensor quantizer: clamp(rint(x / (amax/127)), -127, 127)
+    with fp32 arithmetic, NaN -> 0; same shape as x."""
+    x = _cpu(x)
+    out = torch.empty(x.shape, dtype=torch.int8)
+    _load().oracle_quant_i8(x.data_ptr(), _code(x), x.numel(), float(amax), out.data_ptr())
+    return out
+
+
+def w8a8_conv2d_acc(x: torch.Tensor, w: torch.Tensor, stride, padding, dilation, amax_x: float,
+                    amax_w: float, images=None) -> torch.Tensor:
+    """int32 acc [len(images) or B, O, Ho, Wo] = sum over the zero-padded unfold of
+    q(x) * q(w) (W8A8 conv; scale by (amax_x/127) * (amax_w/127) for the output)."""
+    x, w = _cpu(x), _cpu(w)
+    b, c, h, wd = x.shape
+    o, c2, kh, kw = w.shape
+    assert c == c2
+    (sh, sw), (ph, pw), (dh, dw) = _pair(stride), _pair(padding), _pair(dilation)
+    ho = conv_out_size(h, kh, sh, ph, dh)
+    wo = conv_out_size(wd, kw, sw, pw, dw)
+    if ho <= 0 or wo <= 0:
+        raise ValueError("oracle: empty conv output")
+    idx, ni = _index(images, b)
+    out = torch.empty((ni, o, ho, wo), dtype=torch.int32)
+    rc = _load().oracle_w8a8_conv2d_acc(x.data_ptr(), _code(x), w.data_ptr(), _code(w), b, c, h, wd, o,
+                                        kh, kw, sh, sw, ph, pw, dh, dw, float(amax_x), float(amax_w),
+                                        idx.data_ptr() if idx is not None else None, ni, out.data_ptr())
+    if rc != 0:
+        raise RuntimeError("oracle_w8a8_conv2d_acc failed")
+    return out

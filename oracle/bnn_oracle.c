@@ -384,3 +384,87 @@ double oracle_abs_mean_scale(const void *x, int dtype, int64_t count, double fac
   for (int64_t i = 0; i < count; i++) sum += fabs((double)widen(x, dtype, i));
   return factor * (sum / (double)count);
 }
+
+/* ---- W8A8 conv: the blog's im2col + GEMM with INT8 quantizers (section 3,
+ * MyInitQuantConv2d: the unfolded input and the flattened weight each pass
+ * through a quantizer before the mm). The quantizers are not defined on the
+ * page; the reading taken here is per-tensor symmetric 8-bit with a given
+ * amax: step s = amax / 127 (fp32), code q = clamp(rint(v / s), -127, 127)
+ * with the division in fp32 and rint rounding half to even; NaN codes as 0.
+ * The fake-quantized product then equals (s_x * s_w) * sum q_x * q_w, and
+ * padded taps (zeros) code as 0. */
+
+/* Step of the symmetric quantizer: amax / 127 in fp32. */
+static float q_step(float amax) { return amax / 127.0f; }
+
+static int8_t q_code(float v, float step) {
+  if (v != v) return 0;
+  float r = rintf(v / step);
+  if (r > 127.0f) r = 127.0f;
+  if (r < -127.0f) r = -127.0f;
+  return (int8_t)r;
+}
+
+/* codes[i] = q(x[i]) for count elements, step amax / 127. */
+void oracle_quant_i8(const void *x, int dtype, int64_t count, float amax, int8_t *codes) {
+  float step = q_step(amax);
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < count; i++) codes[i] = q_code(widen(x, dtype, i), step);
+}
+
+/* W8A8 conv accumulators acc[i][o][oh][ow] = sum over the unfolded reduction of
+ * q(x) * q(w), by zero-padded unfold + GEMM as oracle_conv2d_acc2 (codes in place of signs),
+ * summed in double (exact: |acc| < 127 * 127 * R < 2^53). Returns 0 or -1. */
+int oracle_w8a8_conv2d_acc(const void *x, int xdt, const void *w, int wdt, int64_t B, int64_t C,
+                           int64_t H, int64_t W, int64_t O, int64_t KH, int64_t KW, int64_t sh,
+                           int64_t sw, int64_t ph, int64_t pw, int64_t dh, int64_t dw,
+                           float amax_x, float amax_w, const int64_t *imgs, int64_t nimgs,
+                           int32_t *acc) {
+  int64_t Ho = oracle_conv_out_size(H, KH, sh, ph, dh);
+  int64_t Wo = oracle_conv_out_size(W, KW, sw, pw, dw);
+  if (Ho <= 0 || Wo <= 0 || sh < 1 || sw < 1 || dh < 1 || dw < 1 || ph < 0 || pw < 0 || KH < 1 ||
+      KW < 1)
+    return -1;
+  int64_t R = C * KH * KW, L = Ho * Wo, Hp = H + 2 * ph, Wp = W + 2 * pw;
+  if (!imgs) nimgs = B;
+  float step_x = q_step(amax_x), step_w = q_step(amax_w);
+  double *wq = (double *)malloc(sizeof(double) * (size_t)(O * R));
+  double *xp = (double *)malloc(sizeof(double) * (size_t)(C * Hp * Wp));
+  double *cols = (double *)malloc(sizeof(double) * (size_t)(L * R));
+  if (!wq || !xp || !cols) {
+    free(wq); free(xp); free(cols);
+    return -1;
+  }
+  for (int64_t i = 0; i < O * R; i++) wq[i] = (double)q_code(widen(w, wdt, i), step_w);
+  for (int64_t n = 0; n < nimgs; n++) {
+    int64_t b = imgs ? imgs[n] : n;
+    /* quantize, then zero-pad (the unfold pads the input with zeros, whose code is 0) */
+    memset(xp, 0, sizeof(double) * (size_t)(C * Hp * Wp));
+#pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < C; c++)
+      for (int64_t ih = 0; ih < H; ih++)
+        for (int64_t iw = 0; iw < W; iw++)
+          xp[(c * Hp + ih + ph) * Wp + iw + pw] =
+              (double)q_code(widen(x, xdt, ((b * C + c) * H + ih) * W + iw), step_x);
+#pragma omp parallel for schedule(static)
+    for (int64_t l = 0; l < L; l++) {
+      int64_t oh = l / Wo, ow = l % Wo;
+      for (int64_t c = 0; c < C; c++)
+        for (int64_t i = 0; i < KH; i++)
+          for (int64_t j = 0; j < KW; j++)
+            cols[l * R + (c * KH + i) * KW + j] = xp[(c * Hp + oh * sh + i * dh) * Wp + ow * sw + j * dw];
+    }
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t o = 0; o < O; o++)
+      for (int64_t l = 0; l < L; l++) {
+        const double *wr = wq + o * R, *cr = cols + l * R;
+        double sum = 0.0;
+        for (int64_t r = 0; r < R; r++) sum += cr[r] * wr[r];
+        acc[(n * O + o) * L + l] = (int32_t)sum;
+      }
+  }
+  free(wq);
+  free(xp);
+  free(cols);
+  return 0;
+}

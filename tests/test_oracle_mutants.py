@@ -47,7 +47,7 @@ MUTANTS = {
     "conv_row_index_transposed": ("int64_t r = (c * KH + i) * KW + j;", "int64_t r = (c * KW + j) * KH + i;"),
     "conv_swaps_axis_strides": ("cols[l * R + r] = xp[(c * Hp + oh * sh + i * dh) * Wp + ow * sw + j * dw];",
                                 "cols[l * R + r] = xp[(c * Hp + oh * sw + i * dh) * Wp + ow * sh + j * dw];"),
-    "conv_pad_rows_by_columns": ("xp[(c * Hp + ih + ph) * Wp + iw + pw] =", "xp[(c * Hp + ih + pw) * Wp + iw + pw] ="),
+    "conv_pad_rows_by_columns": ("xp[(c * Hp + ih + ph) * Wp + iw + pw] = sgn(", "xp[(c * Hp + ih + pw) * Wp + iw + pw] = sgn("),
     "kvalid_off_by_one": ("if (ih >= 0 && ih < H && iw >= 0 && iw < W) taps++;",
                           "if (ih >= 0 && ih <= H && iw >= 0 && iw < W) taps++;"),
     "scale_sum_instead_of_product": ("double alpha = scale_a * scale_w;", "double alpha = scale_a + scale_w;"),
@@ -59,6 +59,10 @@ MUTANTS = {
     "abs_mean_drops_abs": ("sum += fabs((double)widen(x, dtype, i));", "sum += (double)widen(x, dtype, i);"),
     "abs_mean_count_minus_one": ("return factor * (sum / (double)count);",
                                  "return factor * (sum / (double)(count - 1));"),
+    "quant_truncates": ("float r = rintf(v / step);", "float r = truncf(v / step);"),
+    "quant_clamp_128": ("if (r < -127.0f) r = -127.0f;", "if (r < -128.0f) r = -128.0f;"),
+    "w8a8_step_255": ("static float q_step(float amax) { return amax / 127.0f; }",
+                      "static float q_step(float amax) { return amax / 255.0f; }"),
     "abs_mean_fixed_factor": ("return factor * (sum / (double)count);", "return 2.0 * (sum / (double)count);"),
 }
 
@@ -203,6 +207,22 @@ def _pins(orc):
                            orc.pack_rows(wc.permute(0, 2, 3, 1).contiguous().reshape(-1, 32)).view(3, 2, 3, 1))
 
     check("conv_rect_vs_torch", lib_conv_rect)
+
+    def w8a8_vs_torch():
+        gen = torch.Generator().manual_seed(29)
+        x = 2 * torch.randn((2, 6, 7, 5), generator=gen)
+        wt = torch.randn((3, 6, 3, 2), generator=gen)
+
+        def codes(v, amax):
+            step = torch.tensor(amax, dtype=torch.float32) / 127.0
+            return torch.round(v.float() / step).clamp(-127, 127)
+        if not torch.equal(orc.quant_i8(x, 3.0).double(), codes(x, 3.0).double()):
+            return False
+        ref = torch.nn.functional.conv2d(codes(x, 3.0).double(), codes(wt, 1.0).double(),
+                                         stride=(1, 2), padding=(1, 0), dilation=(2, 1))
+        return torch.equal(orc.w8a8_conv2d_acc(x, wt, (1, 2), (1, 0), (2, 1), 3.0, 1.0).double(), ref)
+
+    check("w8a8_vs_torch", w8a8_vs_torch)
 
     edges = _golden("shift_sign_edges.json")["cases"]
 
