@@ -35,7 +35,7 @@ OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIGN, ERR_WORKSPACE, ERR_PATH, ERR_HIP 
 
 EXPORTS = ("bnn_pack_sign", "bnn_pack_sign_nchw", "bnn_pack_sign_shift", "bnn_pack_sign_nchw_shift",
            "bnn_abs_mean_scale", "bnn_abs_mean_workspace_bytes", "bnn_w_pack", "bnn_w_pack_conv",
-           "bnn_conv2d_ex", "bnn_gemm", "bnn_conv2d",
+           "bnn_conv2d_ex", "bnn_quant_i8_nhwc", "bnn_quant_i8_weight", "bnn_w8a8_conv2d", "bnn_gemm", "bnn_conv2d",
            "bnn_gemm_workspace_bytes", "bnn_conv2d_workspace_bytes", "bnn_gemm_auto_path",
            "bnn_conv2d_auto_path", "bnn_last_path", "bnn_status_string")
 
@@ -56,6 +56,9 @@ def _bind(path: str) -> ctypes.CDLL:
         "bnn_abs_mean_workspace_bytes": ([I64], SZ),
         "bnn_w_pack": ([P, I, I64, I64, I, P, P], I),
         "bnn_w_pack_conv": ([P, I, I64, I64, I, I, P, P], I),
+        "bnn_quant_i8_nhwc": ([P, I, I64, I64, I64, I64, D, P, P], I),
+        "bnn_quant_i8_weight": ([P, I, I64, I64, I, I, D, P, P], I),
+        "bnn_w8a8_conv2d": ([P, I64, I64, I64, I64, P, I64, D, D] + [I] * 8 + [P, I, P], I),
         "bnn_conv2d_ex": ([P, I, I64, I64, I64, I64, P, I64, D, D] + [I] * 9 + [P, I, P, SZ, P], I),
         "bnn_gemm": ([P, I, P, I64, I64, I64, D, D, I, P, I, P, SZ, P], I),
         "bnn_conv2d": ([P, I, I64, I64, I64, I64, P, I64, D, D, I, I, I, I, I, P, I, P, SZ, P], I),
@@ -342,3 +345,50 @@ def gemm_auto_path(m: int, n: int, k: int) -> int:
 
 def conv2d_auto_path(n, c, h, w, o, kernel_size, stride=1, padding=0, dilation=1) -> int:
     return lib.bnn_conv2d_auto_path(n, c, h, w, o, kernel_size, stride, padding, dilation)
+
+
+# ---- W8A8 conv (int8 codes of per-tensor symmetric quantizers; see include/bnn.h)
+
+def quant_i8_nhwc(x: torch.Tensor, amax: float) -> torch.Tensor:
+    """NCHW float -> NHWC int8 codes clamp(rint(x / (amax/127)), -127, 127)."""
+    x = _dev(x, "x")
+    n, c, h, w = x.shape
+    out = torch.empty((n, h, w, c), dtype=torch.int8, device=x.device)
+    _check(lib.bnn_quant_i8_nhwc(x.data_ptr(), _dtype_code(x, "x"), n, c, h, w, float(amax),
+                                 out.data_ptr(), _stream(x)), "bnn_quant_i8_nhwc")
+    return out
+
+
+def quant_i8_weight(weight: torch.Tensor, amax: float) -> torch.Tensor:
+    """OIHW float -> int8 codes [o, kh, kw, c]."""
+    weight = _dev(weight, "weight")
+    o, c, kh, kw = weight.shape
+    out = torch.empty((o, kh, kw, c), dtype=torch.int8, device=weight.device)
+    _check(lib.bnn_quant_i8_weight(weight.data_ptr(), _dtype_code(weight, "weight"), o, c, kh, kw,
+                                   float(amax), out.data_ptr(), _stream(weight)), "bnn_quant_i8_weight")
+    return out
+
+
+def w8a8_conv2d(x_q: torch.Tensor, w_q: torch.Tensor, amax_x: float, amax_w: float, kernel_size,
+                stride=1, padding=0, dilation=1, out_dtype=torch.float32,
+                out: torch.Tensor | None = None) -> torch.Tensor:
+    """W8A8 conv on int8 codes: x_q NHWC [n, h, w, c], w_q [o, kh, kw, c]; NCHW output
+    (amax_x/127) * (amax_w/127) * sum q_x q_w, or the raw int32 sums for out_dtype=torch.int32."""
+    x_q, w_q = _dev(x_q, "x_q"), _dev(w_q, "w_q")
+    n, h, w, c = x_q.shape
+    o, kh, kw, c2 = w_q.shape
+    if c != c2:
+        raise ValueError("x_q and w_q disagree on the channel count")
+    if tuple(_pair(kernel_size, "kernel_size")) != (kh, kw):
+        raise ValueError("kernel_size does not match w_q")
+    (sh, sw), (ph, pw), (dh, dw) = _pair(stride, "stride"), _pair(padding, "padding"), _pair(dilation, "dilation")
+    ho = (h + 2 * ph - dh * (kh - 1) - 1) // sh + 1 if sh > 0 else 0
+    wo = (w + 2 * pw - dw * (kw - 1) - 1) // sw + 1 if sw > 0 else 0
+    if out is None:
+        out = torch.empty((n, o, max(ho, 0), max(wo, 0)), dtype=out_dtype, device=x_q.device)
+    else:
+        _dev(out, "out")
+    _check(lib.bnn_w8a8_conv2d(x_q.data_ptr(), n, c, h, w, w_q.data_ptr(), o, float(amax_x),
+                               float(amax_w), kh, kw, sh, sw, ph, pw, dh, dw, out.data_ptr(),
+                               _DT[out.dtype], _stream(x_q)), "bnn_w8a8_conv2d")
+    return out

@@ -347,4 +347,64 @@ bnn_status bnn_conv2d(const void* x, int x_dtype, int64_t n, int64_t c, int64_t 
                        dilation, path, out, out_dtype, workspace, workspace_bytes, stream);
 }
 
+// ---- W8A8 conv (the blog's im2col + GEMM with INT8 quantizers)
+
+// Step of the per-tensor symmetric quantizer: amax / 127 in fp32.
+static float w8a8_step(double amax) { return (float)amax / 127.0f; }
+static bool amax_ok(double amax) { return amax > 0.0 && amax <= 3.0e38; }
+// |acc| <= 127 * 127 * K must fit int32
+static constexpr int64_t kMaxW8A8K = 0x7FFFFFFFLL / (127 * 127);
+
+bnn_status bnn_quant_i8_nhwc(const void* x, int x_dtype, int64_t n, int64_t c, int64_t h, int64_t w,
+                             double amax, int8_t* x_q, void* stream) {
+  if (!float_dtype(x_dtype)) return BNN_ERR_DTYPE;
+  if (n < 0 || c <= 0 || c % 16 != 0 || h <= 0 || w <= 0 || !amax_ok(amax)) return BNN_ERR_SHAPE;
+  if (!int_fits(n * h * w) || !int_fits(c)) return BNN_ERR_SHAPE;
+  if (n == 0) return BNN_OK;
+  if (!x || !x_q) return BNN_ERR_NULL;
+  if (!aligned(x, elem_bytes(x_dtype)) || !aligned(x_q, 16)) return BNN_ERR_ALIGN;
+  return hip_status(bnn::launch_quant_nhwc(x, x_dtype, n, c, h, w, w8a8_step(amax), x_q,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+bnn_status bnn_quant_i8_weight(const void* weight, int w_dtype, int64_t out_channels, int64_t c,
+                               int kernel_h, int kernel_w, double amax, int8_t* w_q, void* stream) {
+  if (!float_dtype(w_dtype)) return BNN_ERR_DTYPE;
+  if (out_channels < 0 || c <= 0 || c % 16 != 0 || kernel_h < 1 || kernel_w < 1 || !amax_ok(amax))
+    return BNN_ERR_SHAPE;
+  if (!int_fits((int64_t)kernel_h * kernel_w * c)) return BNN_ERR_SHAPE;
+  if (out_channels == 0) return BNN_OK;
+  if (!weight || !w_q) return BNN_ERR_NULL;
+  if (!aligned(weight, elem_bytes(w_dtype)) || !aligned(w_q, 16)) return BNN_ERR_ALIGN;
+  return hip_status(bnn::launch_quant_weight(weight, w_dtype, out_channels, c, kernel_h, kernel_w,
+                                             w8a8_step(amax), w_q, static_cast<hipStream_t>(stream)));
+}
+
+bnn_status bnn_w8a8_conv2d(const int8_t* x_q, int64_t n, int64_t c, int64_t h, int64_t w,
+                           const int8_t* w_q, int64_t out_channels, double amax_x, double amax_w,
+                           int kernel_h, int kernel_w, int stride_h, int stride_w, int pad_h,
+                           int pad_w, int dil_h, int dil_w, void* out, int out_dtype,
+                           void* stream) {
+  if (!out_dtype_ok(out_dtype)) return BNN_ERR_DTYPE;
+  if (n < 0 || out_channels < 0 || c <= 0 || c % 16 != 0 || h <= 0 || w <= 0) return BNN_ERR_SHAPE;
+  if (!amax_ok(amax_x) || !amax_ok(amax_w)) return BNN_ERR_SHAPE;
+  if (kernel_h < 1 || kernel_w < 1 || stride_h < 1 || stride_w < 1 || dil_h < 1 || dil_w < 1 ||
+      pad_h < 0 || pad_w < 0)
+    return BNN_ERR_SHAPE;
+  const int64_t ho = out_size(h, kernel_h, stride_h, pad_h, dil_h);
+  const int64_t wo = out_size(w, kernel_w, stride_w, pad_w, dil_w);
+  if (ho <= 0 || wo <= 0) return BNN_ERR_SHAPE;
+  const int64_t k = (int64_t)kernel_h * kernel_w * c;
+  if (k > kMaxW8A8K || !int_fits(n * ho * wo) || !int_fits(out_channels) || !int_fits(n * h * w * c))
+    return BNN_ERR_SHAPE;
+  if (n == 0 || out_channels == 0) return BNN_OK;
+  if (!x_q || !w_q || !out) return BNN_ERR_NULL;
+  if (!aligned(x_q, 16) || !aligned(w_q, 16) || !aligned(out, 16)) return BNN_ERR_ALIGN;
+  // the output scale: the host product of the two fp32 steps, rounded once to float
+  const float alpha = (float)((double)w8a8_step(amax_x) * (double)w8a8_step(amax_w));
+  return hip_status(bnn::launch_w8a8_conv(x_q, w_q, out, out_dtype, n, c, h, w, out_channels, ho,
+                                          wo, kernel_h, kernel_w, stride_h, stride_w, pad_h, pad_w,
+                                          dil_h, dil_w, alpha, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -53,4 +53,17 @@ hipError_t launch_mfma(const Contraction& p, bool conv, int out_dtype, hipStream
 constexpr int64_t kMaxFp4K = int64_t(1) << 24;
 hipError_t launch_mfma_fp4(const Contraction& p, bool conv, int out_dtype, hipStream_t stream);
 
+// W8A8 conv (int8 codes of per-tensor symmetric quantizers, int32 sums on the matrix cores).
+// NCHW float -> NHWC int8 codes with step amax/127 (c % 16 == 0, 16-byte aligned out).
+hipError_t launch_quant_nhwc(const void* x, int dtype, int64_t n, int64_t c, int64_t h, int64_t w,
+                             float step, int8_t* out, hipStream_t stream);
+// OIHW float -> [o][kh][kw][c] int8 codes.
+hipError_t launch_quant_weight(const void* w, int dtype, int64_t o, int64_t c, int kh, int kw,
+                               float step, int8_t* out, hipStream_t stream);
+// Implicit-im2col int8 conv, out = alpha * sum q_x q_w (NCHW, out_dtype); c % 16 == 0.
+hipError_t launch_w8a8_conv(const int8_t* xq, const int8_t* wq, void* out, int out_dtype,
+                            int64_t n, int64_t c, int64_t h, int64_t w, int64_t o, int64_t ho,
+                            int64_t wo, int kh, int kw, int sh, int sw, int ph, int pw, int dh,
+                            int dw, float alpha, hipStream_t stream);
+
 }  // namespace bnn

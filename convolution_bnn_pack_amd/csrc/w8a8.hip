@@ -1,0 +1,296 @@
+// W8A8 conv on the gfx950 matrix cores: the im2col + GEMM lowering with INT8 quantizers
+// (banghao.live blog post, section 3, "Add INT8-quantizer to im2col+gemm"), computed
+// implicitly.
+//
+// Quantizer (a reading: the page names input and weight quantizers without defining
+// them): per-tensor symmetric 8-bit with a given amax, step = amax / 127 in fp32 and
+// code = clamp(rint(v / step), -127, 127) with a correctly rounded fp32 division and
+// round-half-to-even; NaN codes as 0. The fake-quantized product of the page equals
+// step_x * step_w * sum(q_x * q_w), so the contraction runs on int8 codes with int32 sums
+// and the epilogue scales once.
+//
+// Layouts: activations NHWC int8 [N][H][W][C] (a conv tap reads C contiguous codes),
+// weights [O][KH][KW][C] int8, so reduction byte r = tap * C + c of a weight row is plain
+// row-major. C must be a multiple of 16, so a 16-byte chunk of the reduction never leaves
+// its tap; padded taps load zeros.
+#include "launch.h"
+
+namespace bnn {
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ int8_t quant_code(float v, float step) {
+  if (v != v) return 0;
+  float r = rintf(v / step);
+  r = fminf(fmaxf(r, -127.0f), 127.0f);
+  return (int8_t)(int)r;
+}
+
+template <int DT>
+__device__ __forceinline__ float load_f32(const void* base, int64_t i) {
+  if constexpr (DT == kF32)
+    return reinterpret_cast<const float*>(base)[i];
+  else if constexpr (DT == kF16)
+    return __half2float(reinterpret_cast<const __half*>(base)[i]);
+  else
+    return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(base)[i] << 16);
+}
+
+// NCHW float -> NHWC int8 codes. A 256-thread workgroup takes 64 pixels (of the flattened
+// batch x plane axis) x 64 channels: threads read along pixels (coalesced per channel
+// plane), codes meet in LDS as [pixel][channel], and each pixel's 64 channel codes leave
+// as one contiguous run.
+template <int DT>
+__global__ __launch_bounds__(256) void quant_nhwc_kernel(const void* __restrict__ x,
+                                                         int8_t* __restrict__ out, int C, int HW,
+                                                         int P, float step) {
+  __shared__ int8_t tile[64][64 + 4];
+  const int p0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;  // pixel lane, channel group
+  const int p = p0 + tx;
+  if (p < P) {
+    const int b = p / HW, pix = p - b * HW;
+#pragma unroll 4
+    for (int k = 0; k < 16; k++) {
+      const int cl = ty + 4 * k, c = c0 + cl;
+      tile[tx][cl] = c < C ? quant_code(load_f32<DT>(x, ((int64_t)b * C + c) * HW + pix), step) : 0;
+    }
+  }
+  __syncthreads();
+  // write: thread -> (pixel row, 16-byte column); 64 pixels x 4 columns = 256 stores
+  const int pr = threadIdx.x >> 2, col = (threadIdx.x & 3) * 16;
+  const int pw = p0 + pr;
+  if (pw < P) {
+    int8_t* dst = out + (int64_t)pw * C + c0 + col;
+    if (c0 + col + 16 <= C) {
+      uint32_t v[4];
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+        v[i] = (uint32_t)(uint8_t)tile[pr][col + 4 * i] | ((uint32_t)(uint8_t)tile[pr][col + 4 * i + 1] << 8) |
+               ((uint32_t)(uint8_t)tile[pr][col + 4 * i + 2] << 16) |
+               ((uint32_t)(uint8_t)tile[pr][col + 4 * i + 3] << 24);
+      *reinterpret_cast<uint4*>(dst) = make_uint4(v[0], v[1], v[2], v[3]);
+    } else {
+      for (int i = 0; i < 16 && c0 + col + i < C; i++) dst[i] = tile[pr][col + i];
+    }
+  }
+}
+
+// OIHW float -> [O][KH][KW][C] int8 codes, one thread per code (run once per layer).
+template <int DT>
+__global__ __launch_bounds__(256) void quant_weight_kernel(const void* __restrict__ w,
+                                                           int8_t* __restrict__ out,
+                                                           int64_t total, int C, int T,
+                                                           float step) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const int c = (int)(idx % C);
+  const int64_t ot = idx / C;  // o * T + t
+  const int t = (int)(ot % T);
+  const int64_t o = ot / T;
+  out[idx] = quant_code(load_f32<DT>(w, (o * C + c) * T + t), step);
+}
+
+// Implicit-im2col int8 contraction. Tile 128 output pixels x 128 output channels, four
+// waves in a 2 x 2 grid, each a 64 x 64 sub-tile of 2 x 2 blocks of
+// v_mfma_i32_32x32x32_i8. A stage is 64 reduction bytes (two MFMA k-steps): the A tile
+// (pixels) and the W tile (channels) are loaded as 16-byte chunks into registers, written
+// to one of two LDS buffers (rows padded to 80 bytes to spread the banks), and consumed
+// after one barrier while the next stage's chunks are in flight. The MFMA computes
+// D = A * W^T, so a lane's four consecutive accumulators are four consecutive pixels of
+// one output channel (as in the binary conv tiles).
+constexpr int kBM = 128, kBN = 128, kSK = 64, kRow = kSK + 16;
+
+struct W8A8Conv {
+  const int8_t* a;  // NHWC codes
+  const int8_t* w;  // [O][K] codes
+  void* out;        // NCHW
+  int M, N, K, C, H, W, Ho, Wo, KWD, SH, SW, PH, PW, DH, DW;
+  float alpha;
+};
+
+template <int OUT>
+__global__ __launch_bounds__(256) void w8a8_conv_kernel(W8A8Conv p) {
+  __shared__ __attribute__((aligned(16))) int8_t lds[2][(kBM + kBN) * kRow];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int tiles_n = (p.N + kBN - 1) / kBN;
+  const int m0 = (blockIdx.x / tiles_n) * kBM, n0 = (blockIdx.x % tiles_n) * kBN;
+
+  // loader: chunk (row, j) for row = tid >> 1 (0..127), j = 2 * (tid & 1) + {0, 1}
+  const int lrow = tid >> 1, lj = 2 * (tid & 1);
+  const int am = m0 + lrow, wnr = n0 + lrow;
+  const bool amok = am < p.M, wnok = wnr < p.N;
+  int ab = 0, aih = 0, aiw = 0;  // image and top-left input coordinate of this A row
+  if (amok) {
+    const int hw = p.Ho * p.Wo;
+    ab = am / hw;
+    const int r = am - ab * hw;
+    const int oh = r / p.Wo, ow = r - oh * p.Wo;
+    aih = oh * p.SH - p.PH;
+    aiw = ow * p.SW - p.PW;
+  }
+  auto load_stage = [&](int s, uint4 (&ra)[2], uint4 (&rw)[2]) {
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+      const int r0 = s * kSK + 16 * (lj + i);
+      ra[i] = make_uint4(0u, 0u, 0u, 0u);
+      rw[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (r0 < p.K) {
+        if (amok) {
+          const int tap = r0 / p.C, c = r0 - tap * p.C;
+          const int kh = tap / p.KWD, kw = tap - kh * p.KWD;
+          const int ih = aih + kh * p.DH, iw = aiw + kw * p.DW;
+          if (ih >= 0 && ih < p.H && iw >= 0 && iw < p.W)
+            ra[i] = *reinterpret_cast<const uint4*>(p.a + (((int64_t)ab * p.H + ih) * p.W + iw) * p.C + c);
+        }
+        if (wnok) rw[i] = *reinterpret_cast<const uint4*>(p.w + (int64_t)wnr * p.K + r0);
+      }
+    }
+  };
+  auto store_stage = [&](int buf, const uint4 (&ra)[2], const uint4 (&rw)[2]) {
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+      *reinterpret_cast<uint4*>(&lds[buf][lrow * kRow + 16 * (lj + i)]) = ra[i];
+      *reinterpret_cast<uint4*>(&lds[buf][(kBM + lrow) * kRow + 16 * (lj + i)]) = rw[i];
+    }
+  };
+
+  v16i acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; i++)
+#pragma unroll
+    for (int j = 0; j < 2; j++)
+#pragma unroll
+      for (int e = 0; e < 16; e++) acc[i][j][e] = 0;
+
+  const int fr = lane & 31, half = lane >> 5;
+  const int nstages = (p.K + kSK - 1) / kSK;
+  uint4 ra[2], rw[2];
+  load_stage(0, ra, rw);
+  store_stage(0, ra, rw);
+  __syncthreads();
+  for (int s = 0; s < nstages; s++) {
+    const int buf = s & 1;
+    if (s + 1 < nstages) load_stage(s + 1, ra, rw);
+#pragma unroll
+    for (int kk = 0; kk < kSK / 32; kk++) {
+      v4i fa[2], fw[2];
+#pragma unroll
+      for (int f = 0; f < 2; f++) {
+        fa[f] = *reinterpret_cast<const v4i*>(&lds[buf][(wm * 64 + f * 32 + fr) * kRow + 16 * (2 * kk + half)]);
+        fw[f] = *reinterpret_cast<const v4i*>(&lds[buf][(kBM + wn * 64 + f * 32 + fr) * kRow + 16 * (2 * kk + half)]);
+      }
+#pragma unroll
+      for (int fn = 0; fn < 2; fn++)
+#pragma unroll
+        for (int fm = 0; fm < 2; fm++)
+          acc[fn][fm] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[fm], fw[fn], acc[fn][fm], 0, 0, 0);
+    }
+    if (s + 1 < nstages) store_stage(buf ^ 1, ra, rw);
+    __syncthreads();
+  }
+
+  // epilogue: lane (fr, half) holds channel n = n0 + wn*64 + fn*32 + fr and, in e = 4g..4g+3,
+  // the pixels m = m0 + wm*64 + fm*32 + 8g + 4*half + 0..3
+  const int hw = p.Ho * p.Wo;
+#pragma unroll
+  for (int fn = 0; fn < 2; fn++) {
+    const int n = n0 + wn * 64 + fn * 32 + fr;
+    if (n >= p.N) continue;
+#pragma unroll
+    for (int fm = 0; fm < 2; fm++)
+#pragma unroll
+      for (int g = 0; g < 4; g++) {
+        const int m = m0 + wm * 64 + fm * 32 + 8 * g + 4 * half;
+        if (m >= p.M) continue;
+        const int b = m / hw, pix = m - b * hw;
+        const int v0 = acc[fn][fm][4 * g], v1 = acc[fn][fm][4 * g + 1];
+        const int v2 = acc[fn][fm][4 * g + 2], v3 = acc[fn][fm][4 * g + 3];
+        if ((hw & 3) == 0) {
+          store4<OUT>(p.out, ((int64_t)b * p.N + n) * hw + pix, v0, v1, v2, v3, p.alpha);
+        } else {
+          const int vals[4] = {v0, v1, v2, v3};
+          int bi = b, pi = pix;
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            if (m + i >= p.M) break;
+            store1<OUT>(p.out, ((int64_t)bi * p.N + n) * hw + pi, vals[i], p.alpha);
+            if (++pi == hw) {
+              pi = 0;
+              ++bi;
+            }
+          }
+        }
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quant_nhwc(const void* x, int dtype, int64_t n, int64_t c, int64_t h, int64_t w,
+                             float step, int8_t* out, hipStream_t stream) {
+  const int64_t P = n * h * w;
+  if (P == 0 || c == 0) return hipSuccess;
+  const dim3 grid((unsigned)((P + 63) / 64), (unsigned)((c + 63) / 64)), block(256);
+  switch (dtype) {
+    case kF32: hipLaunchKernelGGL(quant_nhwc_kernel<kF32>, grid, block, 0, stream, x, out, (int)c, (int)(h * w), (int)P, step); break;
+    case kF16: hipLaunchKernelGGL(quant_nhwc_kernel<kF16>, grid, block, 0, stream, x, out, (int)c, (int)(h * w), (int)P, step); break;
+    default: hipLaunchKernelGGL(quant_nhwc_kernel<kBF16>, grid, block, 0, stream, x, out, (int)c, (int)(h * w), (int)P, step); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_weight(const void* w, int dtype, int64_t o, int64_t c, int kh, int kw,
+                               float step, int8_t* out, hipStream_t stream) {
+  const int64_t total = o * kh * kw * c;
+  if (total == 0) return hipSuccess;
+  const dim3 grid((unsigned)((total + 255) / 256)), block(256);
+  const int T = kh * kw;
+  switch (dtype) {
+    case kF32: hipLaunchKernelGGL(quant_weight_kernel<kF32>, grid, block, 0, stream, w, out, total, (int)c, T, step); break;
+    case kF16: hipLaunchKernelGGL(quant_weight_kernel<kF16>, grid, block, 0, stream, w, out, total, (int)c, T, step); break;
+    default: hipLaunchKernelGGL(quant_weight_kernel<kBF16>, grid, block, 0, stream, w, out, total, (int)c, T, step); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_w8a8_conv(const int8_t* xq, const int8_t* wq, void* out, int out_dtype,
+                            int64_t n, int64_t c, int64_t h, int64_t w, int64_t o, int64_t ho,
+                            int64_t wo, int kh, int kw, int sh, int sw, int ph, int pw, int dh,
+                            int dw, float alpha, hipStream_t stream) {
+  W8A8Conv p{};
+  p.a = xq;
+  p.w = wq;
+  p.out = out;
+  p.M = (int)(n * ho * wo);
+  p.N = (int)o;
+  p.K = (int)(kh * kw * c);
+  p.C = (int)c;
+  p.H = (int)h;
+  p.W = (int)w;
+  p.Ho = (int)ho;
+  p.Wo = (int)wo;
+  p.KWD = kw;
+  p.SH = sh;
+  p.SW = sw;
+  p.PH = ph;
+  p.PW = pw;
+  p.DH = dh;
+  p.DW = dw;
+  p.alpha = alpha;
+  if (p.M == 0 || p.N == 0) return hipSuccess;
+  const int64_t tiles = (int64_t)((p.M + kBM - 1) / kBM) * ((p.N + kBN - 1) / kBN);
+  const dim3 grid((unsigned)tiles), block(256);
+  switch (out_dtype) {
+    case kF32: hipLaunchKernelGGL(w8a8_conv_kernel<kF32>, grid, block, 0, stream, p); break;
+    case kF16: hipLaunchKernelGGL(w8a8_conv_kernel<kF16>, grid, block, 0, stream, p); break;
+    case kBF16: hipLaunchKernelGGL(w8a8_conv_kernel<kBF16>, grid, block, 0, stream, p); break;
+    default: hipLaunchKernelGGL(w8a8_conv_kernel<kI32>, grid, block, 0, stream, p); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace bnn

@@ -194,6 +194,32 @@ bnn_status bnn_w_pack_conv(const void* weight, int w_dtype, int64_t out_features
                            int64_t in_features, int kernel_h, int kernel_w, uint32_t* w_packed,
                            void* stream);
 
+/* W8A8 conv: the im2col + GEMM lowering with INT8 quantizers of the banghao.live blog post,
+ * section 3 ("Add INT8-quantizer to im2col+gemm"), computed implicitly on the matrix cores.
+ * The page does not define its quantizers; here they are per-tensor symmetric 8-bit with a
+ * given amax > 0: step = (float)amax / 127 in fp32, code = clamp(rint(v / step), -127, 127)
+ * (correctly rounded fp32 division, round half to even), NaN codes as 0. The page's
+ * fake-quantized product is then step_x * step_w * sum(q_x * q_w), computed here as int32
+ * sums scaled once in fp32 by (float)(step_x * step_w) and rounded to out_dtype (BNN_I32:
+ * the raw sums). Padded taps contribute 0. Channel counts must be multiples of 16;
+ * kernel_h * kernel_w * c <= 133144 (so |sum| < 2^31).
+ *
+ * Activation codes: x NCHW [n, c, h, w] (BNN_F32/F16/BF16) -> x_q NHWC int8 [n, h, w, c],
+ * 16-byte aligned. */
+bnn_status bnn_quant_i8_nhwc(const void* x, int x_dtype, int64_t n, int64_t c, int64_t h, int64_t w,
+                             double amax, int8_t* x_q, void* stream);
+/* Weight codes (once per layer): OIHW [out_channels, c, kernel_h, kernel_w] ->
+ * w_q int8 [out_channels, kernel_h, kernel_w, c], 16-byte aligned. */
+bnn_status bnn_quant_i8_weight(const void* weight, int w_dtype, int64_t out_channels, int64_t c,
+                               int kernel_h, int kernel_w, double amax, int8_t* w_q, void* stream);
+/* out NCHW [n, out_channels, Ho, Wo] = step_x * step_w * conv(x_q, w_q), geometry as
+ * bnn_conv2d_ex; amax_x / amax_w are the amax values the codes were made with. */
+bnn_status bnn_w8a8_conv2d(const int8_t* x_q, int64_t n, int64_t c, int64_t h, int64_t w,
+                           const int8_t* w_q, int64_t out_channels, double amax_x, double amax_w,
+                           int kernel_h, int kernel_w, int stride_h, int stride_w, int pad_h,
+                           int pad_w, int dil_h, int dil_w, void* out, int out_dtype,
+                           void* stream);
+
 /* Workspace sizes (bytes) for the calls above; 0 when x is already packed. */
 size_t bnn_gemm_workspace_bytes(int64_t m, int64_t k, int x_dtype);
 size_t bnn_conv2d_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w, int x_dtype);

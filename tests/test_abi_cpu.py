@@ -142,6 +142,36 @@ def test_conv_ex_argument_checks(bnn):
     assert L.bnn_w_pack_conv(None, bnn.F32, 0, 64, 3, 2, None, None) == bnn.OK
 
 
+def test_w8a8_argument_checks(bnn):
+    L = bnn.lib
+
+    def conv(**kw):
+        a = dict(xq=FAKE, n=2, c=32, h=8, w=8, wq=FAKE, o=16, ax=2.0, aw=1.0, kh=3, kw=3, sh=1, sw=1,
+                 ph=1, pw=1, dh=1, dw=1, out=FAKE, odt=bnn.F32)
+        a.update(kw)
+        return L.bnn_w8a8_conv2d(a["xq"], a["n"], a["c"], a["h"], a["w"], a["wq"], a["o"], a["ax"],
+                                 a["aw"], a["kh"], a["kw"], a["sh"], a["sw"], a["ph"], a["pw"], a["dh"],
+                                 a["dw"], a["out"], a["odt"], None)
+    assert conv(c=24) == bnn.ERR_SHAPE                  # channels must be a multiple of 16
+    assert conv(ax=0.0) == bnn.ERR_SHAPE and conv(aw=-1.0) == bnn.ERR_SHAPE
+    assert conv(c=16 * 1000, kh=3, kw=3) == bnn.ERR_SHAPE     # 127^2 * K would overflow int32
+    assert conv(h=2, kh=5, ph=0) == bnn.ERR_SHAPE
+    assert conv(odt=bnn.U32_PACKED) == bnn.ERR_DTYPE
+    assert conv(wq=None) == bnn.ERR_NULL
+    assert conv(xq=FAKE + 8) == bnn.ERR_ALIGN
+    assert conv(n=0, xq=None, out=None) == bnn.OK
+    q = L.bnn_quant_i8_nhwc
+    assert q(FAKE, bnn.F32, 1, 20, 4, 4, 1.0, FAKE, None) == bnn.ERR_SHAPE
+    assert q(FAKE, bnn.F32, 1, 32, 4, 4, 0.0, FAKE, None) == bnn.ERR_SHAPE
+    assert q(FAKE, bnn.I32, 1, 32, 4, 4, 1.0, FAKE, None) == bnn.ERR_DTYPE
+    assert q(None, bnn.F32, 1, 32, 4, 4, 1.0, FAKE, None) == bnn.ERR_NULL
+    assert q(FAKE, bnn.F32, 1, 32, 4, 4, 1.0, FAKE + 4, None) == bnn.ERR_ALIGN
+    qw = L.bnn_quant_i8_weight
+    assert qw(FAKE, bnn.F32, 4, 32, 0, 3, 1.0, FAKE, None) == bnn.ERR_SHAPE
+    assert qw(None, bnn.F32, 4, 32, 3, 3, 1.0, FAKE, None) == bnn.ERR_NULL
+    assert qw(None, bnn.F32, 0, 32, 3, 3, 1.0, None, None) == bnn.OK
+
+
 def test_pack_argument_checks(bnn):
     L = bnn.lib
     assert L.bnn_pack_sign(None, bnn.F32, 4, 33, FAKE, None) == bnn.ERR_NULL     # ragged k accepted
