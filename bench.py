@@ -43,22 +43,30 @@ CODEC_WORKLOADS = {
     "pack_shift_nchw_128x128x28x28_f16": ("pack_nchw", "conv_down_s2_f16", "f16"),
     "abs_mean_16384x8192_bf16": ("abs_mean", "linear_16384x8192x8192_bf16", None),
 }
+# W8A8 conv workloads (the blog's quantized im2col + GEMM): name -> (conv workload, amax_x, amax_w)
+W8A8_WORKLOADS = {
+    "w8a8_conv_128x128x28x28_s2_f16": ("conv_down_s2_f16", 4.0, 3.0),
+    "w8a8_conv_128x128x28x28_d2_f16": ("conv_dil2_f16", 4.0, 3.0),
+}
 PACK_WORKLOAD = "pack_linear_16384x8192_bf16"
 # kernel kinds: source file, kernel function name, roofline peak and arithmetic type
 KERNEL_SOURCES = {"mfma": "gemm_mfma.hip", "mfma_fp4": "gemm_mfma.hip", "xor": "gemm_xor.hip",
+                  "w8a8": "w8a8.hip",
                   "pack": "pack.hip", "pack_shift": "pack.hip", "pack_nchw": "pack.hip",
                   "abs_mean": "pack.hip"}
 KERNEL_NAMES = {"mfma": "mfma_kernel", "mfma_fp4": "mfma_kernel", "xor": "xor_kernel",
+                "w8a8": "w8a8_conv_kernel",
                 "pack": "pack_rows_kernel", "pack_shift": "pack_rows_shift_kernel",
                 "pack_nchw": "pack_nchw_flat_kernel", "abs_mean": "abs_sum_kernel"}
-PEAKS = {"mfma": PEAK_MFMA_I8_TOPS, "mfma_fp4": PEAK_MFMA_F4_TOPS, "xor": PEAK_VALU_BINARY_TOPS}
-DTYPES = {"mfma": "i8", "mfma_fp4": "fp4(e2m1)", "xor": "u32"}
+PEAKS = {"mfma": PEAK_MFMA_I8_TOPS, "mfma_fp4": PEAK_MFMA_F4_TOPS, "xor": PEAK_VALU_BINARY_TOPS,
+         "w8a8": PEAK_MFMA_I8_TOPS}
+DTYPES = {"mfma": "i8", "mfma_fp4": "fp4(e2m1)", "xor": "u32", "w8a8": "i8"}
 CODEC_KINDS = ("pack", "pack_shift", "pack_nchw", "abs_mean")
 
 
 def kernel_kind(name):
     """Kind of a demangled kernel name from a rocprofv3 counter file (None: not ours)."""
-    for kind in CODEC_KINDS + ("xor",):
+    for kind in CODEC_KINDS + ("xor", "w8a8"):
         if KERNEL_NAMES[kind] + "<" in name or KERNEL_NAMES[kind] + "(" in name:
             return kind
     if "mfma_kernel<" in name:
@@ -127,7 +135,7 @@ def pmc_summary(args):
             raise SystemExit(f"no {args.copy_kernel} kernel in {path}")
         copy_kib = statistics.median(v for _, v in copy)
         scale = (args.copy_mib << 20) / 1024.0 / copy_kib if args.copy_mib else 1.0
-        for k in ([kind] if kind else ["mfma", "mfma_fp4", "xor"]):
+        for k in ([kind] if kind else ["mfma", "mfma_fp4", "xor", "w8a8"]):
             # the workload's kernel is the instantiation launched most often (the parity spot
             # check adds single launches of other output types)
             cands = [(len(vs), name) for name, vs in vals.items() if kernel_kind(name) == k]
@@ -222,8 +230,11 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     pack_only = args.workload in CODEC_WORKLOADS
+    w8a8 = args.workload in W8A8_WORKLOADS
     codec_kind, base, shift_dt = CODEC_WORKLOADS.get(args.workload, (None, None, None))
-    wl = synth.WORKLOADS[base if pack_only else args.workload]
+    if w8a8:
+        base, amax_x, amax_w = W8A8_WORKLOADS[args.workload]
+    wl = synth.WORKLOADS[base if (pack_only or w8a8) else args.workload]
     log(f"workload {args.workload}: generating inputs")
     x, w, sa, sw = synth.make_inputs(wl, draw_weight=not pack_only)
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
@@ -284,6 +295,24 @@ def main():
             bytes_per += 2 * ws.numel() + 8
         kernels = {"pack": [fn]}
         step_fns = kernels["pack"]
+    elif w8a8:
+        # step: activation codes (NCHW -> NHWC int8), then the int8 conv; weight codes are made
+        # once ahead, as the layer's weights are
+        wq = bnn.quant_i8_weight(w.to(dev), amax_w)
+        m, n, k = wl.gemm_mnk()
+        ops = 2.0 * m * n * k
+        out = torch.empty(wl.out_shape(), dtype=tdt[wl.out_dtype], device=dev)
+        ocode = bnn._DT[out.dtype]
+        xp = torch.empty((wl.batch, wl.h, wl.w, wl.c), dtype=torch.int8, device=dev)
+        pack = lambda i: lib.bnn_quant_i8_nhwc(xd.data_ptr(), xcode, wl.batch, wl.c, wl.h, wl.w,
+                                               amax_x, xp.data_ptr(), cur_stream())
+        core = lambda i: lib.bnn_w8a8_conv2d(xp.data_ptr(), wl.batch, wl.c, wl.h, wl.w, wq.data_ptr(),
+                                             wl.o, amax_x, amax_w, wl.ks, wl.ks, wl.stride, wl.stride,
+                                             wl.padding, wl.padding, wl.dilation, wl.dilation,
+                                             out.data_ptr(), ocode, cur_stream())
+        path_used = None
+        kernels = {"pack": [pack], "core": [core]}
+        step_fns = [pack, core]
     else:
         wp = bnn.w_pack(w.to(dev))
         m, n, k = wl.gemm_mnk()
@@ -315,7 +344,18 @@ def main():
 
     # parity spot check before timing (int32 accumulators of sampled rows / images vs the oracle)
     parity = None
-    if not pack_only:
+    if w8a8:
+        import oracle
+        imgs = sorted({0, wl.batch - 1})
+        ref = oracle.w8a8_conv2d_acc(x, w, wl.stride, wl.padding, wl.dilation, amax_x, amax_w,
+                                     images=imgs)
+        if pack(0) != 0:
+            raise RuntimeError("libbnn call failed")
+        got = bnn.w8a8_conv2d(xp, wq, amax_x, amax_w, wl.ks, wl.stride, wl.padding, wl.dilation,
+                              out_dtype=torch.int32)[imgs].cpu()
+        parity = bool(torch.equal(got, ref))
+        log(f"parity spot check vs oracle: {parity}")
+    elif not pack_only:
         import oracle
         if wl.kind == "linear":
             rows = sorted({0, 1, wl.m // 2, wl.m - 1})
@@ -386,7 +426,8 @@ def main():
         dtype = "f64" if codec_kind == "abs_mean" else "u32"
     else:
         dom_ms = kern_ms["core"]
-        kind = {bnn.PATH_XOR: "xor", bnn.PATH_MFMA: "mfma", bnn.PATH_MFMA_FP4: "mfma_fp4"}[path_used]
+        kind = "w8a8" if w8a8 else {bnn.PATH_XOR: "xor", bnn.PATH_MFMA: "mfma",
+                                    bnn.PATH_MFMA_FP4: "mfma_fp4"}[path_used]
         achieved = ops / (dom_ms * 1e-3) / 1e12
         peak = PEAKS[kind]
         roof = {"bound": "alu" if kind == "xor" else "mfma", "achieved": round(achieved, 2),
@@ -394,7 +435,7 @@ def main():
                 "traffic": traffic_for(kind, args.workload), "kernel": KERNEL_NAMES[kind],
                 "kernel_ms": round(dom_ms, 5), "pack_kernel_ms": round(kern_ms["pack"], 5)}
         value = ops / (ms_per_step * 1e-3) / 1e12
-        metric, unit = "binary TOPS (2*M*N*K/s)", "TOPS"
+        metric, unit = ("int8 TOPS (2*M*N*K/s)", "TOPS") if w8a8 else ("binary TOPS (2*M*N*K/s)", "TOPS")
         dtype = DTYPES[kind]
 
     result = {
@@ -421,7 +462,16 @@ def main():
         torch.cuda.synchronize()
         result["copy_calibration_bytes"] = n
         del src, dst
-    if not args.no_cpu_baseline and not pack_only:
+    if not args.no_cpu_baseline and w8a8:
+        import oracle
+        log("cpu baseline (oracle on host cores, one image)")
+        t0 = time.perf_counter()
+        oracle.w8a8_conv2d_acc(x, w, wl.stride, wl.padding, wl.dilation, amax_x, amax_w, images=[0])
+        dt_cpu = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": round(ops / wl.batch / dt_cpu / 1e12, 6), "unit": "int8 TOPS",
+                                  "cores": oracle.num_threads(), "kind": "oracle",
+                                  "sample": f"first 1 of {wl.batch} images ({dt_cpu:.2f} s, quantize + contraction)"}
+    elif not args.no_cpu_baseline and not pack_only:
         log("cpu baseline (oracle on host cores)")
         del xd, xp
         result["cpu_baseline"] = cpu_baseline(wl, x, w)
