@@ -31,7 +31,9 @@ def _step(amax):
 @pytest.mark.parametrize("dt", DT)
 def test_activation_and_weight_codes(bnn, orc, dt):
     g = torch.Generator().manual_seed(101)
-    for (n, c, h, w) in [(1, 16, 1, 1), (2, 48, 5, 7), (3, 80, 9, 9), (2, 128, 14, 14), (1, 16, 65, 3)]:
+    # partial last 64-pixel chunks, channel counts that are not a multiple of 64
+    for (n, c, h, w) in [(1, 16, 1, 1), (2, 48, 5, 7), (3, 80, 9, 9), (2, 128, 14, 14), (1, 16, 65, 3),
+                         (2, 64, 8, 8), (1, 80, 4, 6), (3, 16, 28, 28), (2, 144, 4, 4)]:
         x = synth.inject_edges((2 * torch.randn((n, c, h, w), generator=g)).to(dt), n + c + h, max(1, n * c * h * w // 30))
         print(f"codes {dt} {(n, c, h, w)}", flush=True)
         got = bnn.quant_i8_nhwc(x.to(DEV), 2.5).cpu()
