@@ -93,15 +93,22 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const void* __restric
   out[idx] = quant_code(load_f32<DT>(w, (o * C + c) * T + t), step);
 }
 
-// Implicit-im2col int8 contraction. Tile 128 output pixels x 128 output channels, four
-// waves in a 2 x 2 grid, each a 64 x 64 sub-tile of 2 x 2 blocks of
-// v_mfma_i32_32x32x32_i8. A stage is 64 reduction bytes (two MFMA k-steps): the A tile
+// Implicit-im2col int8 contraction. Tile 128 output pixels x 128 output channels, eight
+// waves in a 2 x 4 grid (two per SIMD), each a 64 x 32 sub-tile of 2 x 1 blocks of
+// v_mfma_i32_32x32x32_i8. A stage is 128 reduction bytes (four MFMA k-steps): the A tile
 // (pixels) and the W tile (channels) are loaded as 16-byte chunks into registers, written
-// to one of two LDS buffers (rows padded to 80 bytes to spread the banks), and consumed
+// to one of two LDS buffers (rows padded to 144 bytes to spread the banks), and consumed
 // after one barrier while the next stage's chunks are in flight. The MFMA computes
 // D = A * W^T, so a lane's four consecutive accumulators are four consecutive pixels of
 // one output channel (as in the binary conv tiles).
-constexpr int kBM = 128, kBN = 128, kSK = 64, kRow = kSK + 16;
+constexpr int kBM = 128, kBN = 128, kSK = 128, kRow = kSK + 16;
+constexpr int kThreads = 512, kWGM = 2, kWGN = 4;              // wave grid
+constexpr int kWTM = kBM / kWGM, kWTN = kBN / kWGN;            // wave sub-tile
+constexpr int kFM = kWTM / 32, kFN = kWTN / 32;                // MFMA blocks per wave
+constexpr int kCPR = kSK / 16;                                 // 16-byte chunks per row and stage
+constexpr int kLPT = kCPR * kBM / kThreads;                    // chunks per thread (A, and W)
+constexpr int kTPR = kCPR / kLPT;                              // loader threads per row
+static_assert(kBM == kBN && kLPT * kTPR == kCPR && kTPR * kBM == kThreads, "loader split");
 
 struct W8A8Conv {
   const int8_t* a;  // NHWC codes
@@ -112,15 +119,15 @@ struct W8A8Conv {
 };
 
 template <int OUT>
-__global__ __launch_bounds__(256) void w8a8_conv_kernel(W8A8Conv p) {
+__global__ __launch_bounds__(kThreads) void w8a8_conv_kernel(W8A8Conv p) {
   __shared__ __attribute__((aligned(16))) int8_t lds[2][(kBM + kBN) * kRow];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % kWGM, wn = wave / kWGM;
   const int tiles_n = (p.N + kBN - 1) / kBN;
   const int m0 = (blockIdx.x / tiles_n) * kBM, n0 = (blockIdx.x % tiles_n) * kBN;
 
-  // loader: chunk (row, j) for row = tid >> 1 (0..127), j = 2 * (tid & 1) + {0, 1}
-  const int lrow = tid >> 1, lj = 2 * (tid & 1);
+  // loader: chunks lj .. lj + kLPT - 1 of row lrow
+  const int lrow = tid / kTPR, lj = (tid % kTPR) * kLPT;
   const int am = m0 + lrow, wnr = n0 + lrow;
   const bool amok = am < p.M, wnok = wnr < p.N;
   int ab = 0, aih = 0, aiw = 0;  // image and top-left input coordinate of this A row
@@ -132,9 +139,9 @@ __global__ __launch_bounds__(256) void w8a8_conv_kernel(W8A8Conv p) {
     aih = oh * p.SH - p.PH;
     aiw = ow * p.SW - p.PW;
   }
-  auto load_stage = [&](int s, uint4 (&ra)[2], uint4 (&rw)[2]) {
+  auto load_stage = [&](int s, uint4 (&ra)[kLPT], uint4 (&rw)[kLPT]) {
 #pragma unroll
-    for (int i = 0; i < 2; i++) {
+    for (int i = 0; i < kLPT; i++) {
       const int r0 = s * kSK + 16 * (lj + i);
       ra[i] = make_uint4(0u, 0u, 0u, 0u);
       rw[i] = make_uint4(0u, 0u, 0u, 0u);
@@ -150,25 +157,25 @@ __global__ __launch_bounds__(256) void w8a8_conv_kernel(W8A8Conv p) {
       }
     }
   };
-  auto store_stage = [&](int buf, const uint4 (&ra)[2], const uint4 (&rw)[2]) {
+  auto store_stage = [&](int buf, const uint4 (&ra)[kLPT], const uint4 (&rw)[kLPT]) {
 #pragma unroll
-    for (int i = 0; i < 2; i++) {
+    for (int i = 0; i < kLPT; i++) {
       *reinterpret_cast<uint4*>(&lds[buf][lrow * kRow + 16 * (lj + i)]) = ra[i];
       *reinterpret_cast<uint4*>(&lds[buf][(kBM + lrow) * kRow + 16 * (lj + i)]) = rw[i];
     }
   };
 
-  v16i acc[2][2];
+  v16i acc[kFN][kFM];
 #pragma unroll
-  for (int i = 0; i < 2; i++)
+  for (int i = 0; i < kFN; i++)
 #pragma unroll
-    for (int j = 0; j < 2; j++)
+    for (int j = 0; j < kFM; j++)
 #pragma unroll
       for (int e = 0; e < 16; e++) acc[i][j][e] = 0;
 
   const int fr = lane & 31, half = lane >> 5;
   const int nstages = (p.K + kSK - 1) / kSK;
-  uint4 ra[2], rw[2];
+  uint4 ra[kLPT], rw[kLPT];
   load_stage(0, ra, rw);
   store_stage(0, ra, rw);
   __syncthreads();
@@ -177,34 +184,35 @@ __global__ __launch_bounds__(256) void w8a8_conv_kernel(W8A8Conv p) {
     if (s + 1 < nstages) load_stage(s + 1, ra, rw);
 #pragma unroll
     for (int kk = 0; kk < kSK / 32; kk++) {
-      v4i fa[2], fw[2];
+      v4i fa[kFM], fw[kFN];
 #pragma unroll
-      for (int f = 0; f < 2; f++) {
-        fa[f] = *reinterpret_cast<const v4i*>(&lds[buf][(wm * 64 + f * 32 + fr) * kRow + 16 * (2 * kk + half)]);
-        fw[f] = *reinterpret_cast<const v4i*>(&lds[buf][(kBM + wn * 64 + f * 32 + fr) * kRow + 16 * (2 * kk + half)]);
-      }
+      for (int f = 0; f < kFM; f++)
+        fa[f] = *reinterpret_cast<const v4i*>(&lds[buf][(wm * kWTM + f * 32 + fr) * kRow + 16 * (2 * kk + half)]);
 #pragma unroll
-      for (int fn = 0; fn < 2; fn++)
+      for (int f = 0; f < kFN; f++)
+        fw[f] = *reinterpret_cast<const v4i*>(&lds[buf][(kBM + wn * kWTN + f * 32 + fr) * kRow + 16 * (2 * kk + half)]);
 #pragma unroll
-        for (int fm = 0; fm < 2; fm++)
+      for (int fn = 0; fn < kFN; fn++)
+#pragma unroll
+        for (int fm = 0; fm < kFM; fm++)
           acc[fn][fm] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[fm], fw[fn], acc[fn][fm], 0, 0, 0);
     }
     if (s + 1 < nstages) store_stage(buf ^ 1, ra, rw);
     __syncthreads();
   }
 
-  // epilogue: lane (fr, half) holds channel n = n0 + wn*64 + fn*32 + fr and, in e = 4g..4g+3,
-  // the pixels m = m0 + wm*64 + fm*32 + 8g + 4*half + 0..3
+  // epilogue: lane (fr, half) holds channel n = n0 + wn*kWTN + fn*32 + fr and, in e = 4g..4g+3,
+  // the pixels m = m0 + wm*kWTM + fm*32 + 8g + 4*half + 0..3
   const int hw = p.Ho * p.Wo;
 #pragma unroll
-  for (int fn = 0; fn < 2; fn++) {
-    const int n = n0 + wn * 64 + fn * 32 + fr;
+  for (int fn = 0; fn < kFN; fn++) {
+    const int n = n0 + wn * kWTN + fn * 32 + fr;
     if (n >= p.N) continue;
 #pragma unroll
-    for (int fm = 0; fm < 2; fm++)
+    for (int fm = 0; fm < kFM; fm++)
 #pragma unroll
       for (int g = 0; g < 4; g++) {
-        const int m = m0 + wm * 64 + fm * 32 + 8 * g + 4 * half;
+        const int m = m0 + wm * kWTM + fm * 32 + 8 * g + 4 * half;
         if (m >= p.M) continue;
         const int b = m / hw, pix = m - b * hw;
         const int v0 = acc[fn][fm][4 * g], v1 = acc[fn][fm][4 * g + 1];
@@ -283,7 +291,7 @@ hipError_t launch_w8a8_conv(const int8_t* xq, const int8_t* wq, void* out, int o
   p.alpha = alpha;
   if (p.M == 0 || p.N == 0) return hipSuccess;
   const int64_t tiles = (int64_t)((p.M + kBM - 1) / kBM) * ((p.N + kBN - 1) / kBN);
-  const dim3 grid((unsigned)tiles), block(256);
+  const dim3 grid((unsigned)tiles), block(kThreads);
   switch (out_dtype) {
     case kF32: hipLaunchKernelGGL(w8a8_conv_kernel<kF32>, grid, block, 0, stream, p); break;
     case kF16: hipLaunchKernelGGL(w8a8_conv_kernel<kF16>, grid, block, 0, stream, p); break;
