@@ -13,6 +13,8 @@
 // weights [O][KH][KW][C] int8, so reduction byte r = tap * C + c of a weight row is plain
 // row-major. C must be a multiple of 16, so a 16-byte chunk of the reduction never leaves
 // its tap; padded taps load zeros.
+#include <type_traits>
+
 #include "launch.h"
 
 namespace bnn {
@@ -175,13 +177,10 @@ __global__ __launch_bounds__(kThreads) void w8a8_conv_kernel(W8A8Conv p) {
 
   const int fr = lane & 31, half = lane >> 5;
   const int nstages = (p.K + kSK - 1) / kSK;
-  uint4 ra[kLPT], rw[kLPT];
-  load_stage(0, ra, rw);
-  store_stage(0, ra, rw);
-  __syncthreads();
-  for (int s = 0; s < nstages; s++) {
-    const int buf = s & 1;
-    if (s + 1 < nstages) load_stage(s + 1, ra, rw);
+  // raw chunks two stages ahead: stage t is fetched into register set t % 2 two stages
+  // before its MFMAs, and stored to LDS buffer t % 2 right after the MFMAs of stage t - 1
+  uint4 ra[2][kLPT], rw[2][kLPT];
+  auto compute = [&](int buf) {
 #pragma unroll
     for (int kk = 0; kk < kSK / 32; kk++) {
       v4i fa[kFM], fw[kFN];
@@ -197,9 +196,26 @@ __global__ __launch_bounds__(kThreads) void w8a8_conv_kernel(W8A8Conv p) {
         for (int fm = 0; fm < kFM; fm++)
           acc[fn][fm] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[fm], fw[fn], acc[fn][fm], 0, 0, 0);
     }
-    if (s + 1 < nstages) store_stage(buf ^ 1, ra, rw);
+  };
+  // one stage: fetch stage s + 2 into set PH (stage s's set, already in LDS), run stage s from
+  // buffer PH, store stage s + 1 (set PH ^ 1) into buffer PH ^ 1; PH = s % 2 at compile time
+  auto stage = [&](auto phase, int s) {
+    constexpr int PH = decltype(phase)::value;
+    if (s + 2 < nstages) load_stage(s + 2, ra[PH], rw[PH]);
+    compute(PH);
+    if (s + 1 < nstages) store_stage(PH ^ 1, ra[PH ^ 1], rw[PH ^ 1]);
     __syncthreads();
+  };
+  load_stage(0, ra[0], rw[0]);
+  if (nstages > 1) load_stage(1, ra[1], rw[1]);
+  store_stage(0, ra[0], rw[0]);
+  __syncthreads();
+  int s = 0;
+  for (; s + 2 <= nstages; s += 2) {
+    stage(std::integral_constant<int, 0>{}, s);
+    stage(std::integral_constant<int, 1>{}, s + 1);
   }
+  if (s < nstages) stage(std::integral_constant<int, 0>{}, s);
 
   // epilogue: lane (fr, half) holds channel n = n0 + wn*kWTN + fn*32 + fr and, in e = 4g..4g+3,
   // the pixels m = m0 + wm*kWTM + fm*32 + 8g + 4*half + 0..3
