@@ -787,9 +787,10 @@ struct Tiles {
   using M = Tile<128, 256, KS, PD_M, 2, BNN_MFMA_WAVES_N, F4>;
   using L = std::conditional_t<F4 && CONV, M, Tile<256, 256, KS, BNN_MFMA_PD_L, 2, BNN_MFMA_WAVES_N, F4>>;
   using S = Tile<128, 128, KS, PD_M, 2, BNN_MFMA_WAVES_N, F4>;
-  // fp4 layers with fewer 128 x 128 tiles than half the compute units: 64 x 128 tiles, 1 x 4
-  // waves (twice the workgroups; the 32x256x14x14 stage-3 conv: 12.6 -> 10.7 us, linear
-  // layers from 64x256x512 to 16x8192x8192: 13-20 % faster)
+  // fp4 layers whose 64 x 128 tiles fit in one round of workgroups: 64 x 128 tiles, 1 x 4
+  // waves, twice the workgroups of 128 x 128 (the 32x256x14x14 stage-3 conv: 12.6 -> 10.7 us,
+  // linear layers from 64x256x512 to 1024x2048x4096: 13-20 % faster; a 1536x2048x2048 layer,
+  // whose 64 x 128 tiles would take two rounds, is faster on 128 x 128)
   using T64 = Tile<64, 128, KS, PD_M, 1, 4, F4>;
   // at most 64 output features (64-channel convs): 256 x 64 tiles, 4 x 2 waves, instead of
   // leaving three quarters of a 256-wide tile's W rows empty (fp4 only: an int8 stage of
@@ -821,7 +822,7 @@ hipError_t launch_mfma_t(const Contraction& p, int out_dtype, hipStream_t stream
   // rounds of small ones
   if (count_tiles(p, 128, 256) >= (CONV ? BNN_MFMA_MIN_TILES_CONV : kMinTiles))
     return launch_tile<typename TS::M, CONV>(p, out_dtype, stream);
-  if (F4 && count_tiles(p, 128, 128) < BNN_MFMA_MIN_TILES_CONV)
+  if (F4 && count_tiles(p, 64, 128) <= kMinTiles)
     return launch_tile<typename TS::T64, CONV>(p, out_dtype, stream);
   return launch_tile<typename TS::S, CONV>(p, out_dtype, stream);
 }
