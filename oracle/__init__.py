@@ -68,6 +68,9 @@ def _bind(lib):
     lib.oracle_pack_rows_shift.argtypes = [P, I, I64, I64, P, I, I64, P]
     lib.oracle_pack_nchw_shift.argtypes = [P, I, I64, I64, I64, I64, P, I, P]
     lib.oracle_abs_mean_scale.argtypes = [P, I, I64, ctypes.c_double]
+    lib.oracle_linear_grad_input.argtypes = [P, I, P, I, P, I, I64, I64, I64, ctypes.c_float,
+                                             ctypes.c_float, P, P]
+    lib.oracle_linear_grad_weight.argtypes = [P, I, P, I, I64, I64, I64, ctypes.c_float, P]
     lib.oracle_abs_mean_scale.restype = ctypes.c_double
     return lib
 
@@ -297,4 +300,35 @@ def w8a8_conv2d_acc(x: torch.Tensor, w: torch.Tensor, stride, padding, dilation,
                                         idx.data_ptr() if idx is not None else None, ni, out.data_ptr())
     if rc != 0:
         raise RuntimeError("oracle_w8a8_conv2d_acc failed")
+    return out
+
+
+def linear_grad_input(g: torch.Tensor, w: torch.Tensor, x: torch.Tensor, scale_a: float,
+                      scale_w: float):
+    """Straight-through backward of the binarized linear layer, input side: returns
+    (grad_in float64 [M, K], grad_scale_a float) for g [M, N], W [N, K], x [M, K]:
+    grad_in = (scale_w * g @ sign0(W)) * mid(x), mid = 0 where the fp32 x / scale_a is outside
+    [-1, 1]; grad_scale_a = sum(grad_in * sign0(x)) / sqrt(M * K)."""
+    g, w, x = _cpu(g), _cpu(w), _cpu(x)
+    m, n = g.shape
+    n2, k = w.shape
+    assert n == n2 and tuple(x.shape) == (m, k)
+    out = torch.empty((m, k), dtype=torch.float64)
+    gsa = ctypes.c_double(0.0)
+    _load().oracle_linear_grad_input(g.data_ptr(), _code(g), w.data_ptr(), _code(w), x.data_ptr(),
+                                     _code(x), m, n, k, float(scale_a), float(scale_w),
+                                     out.data_ptr(), ctypes.addressof(gsa))
+    return out, gsa.value
+
+
+def linear_grad_weight(g: torch.Tensor, x: torch.Tensor, scale_a: float) -> torch.Tensor:
+    """Straight-through backward of the binarized linear layer, weight side: float64 [N, K] =
+    g^T @ (sign0(x) * scale_a) for g [M, N], x [M, K]."""
+    g, x = _cpu(g), _cpu(x)
+    m, n = g.shape
+    assert x.shape[0] == m
+    k = x.shape[1]
+    out = torch.empty((n, k), dtype=torch.float64)
+    _load().oracle_linear_grad_weight(g.data_ptr(), _code(g), x.data_ptr(), _code(x), m, n, k,
+                                      float(scale_a), out.data_ptr())
     return out

@@ -468,3 +468,78 @@ int oracle_w8a8_conv2d_acc(const void *x, int xdt, const void *w, int wdt, int64
   free(cols);
   return 0;
 }
+
+/* ---------------------------------------------------------------------------
+ * Straight-through backward of the binarized linear layer.
+ *
+ * The BinaryLinearForward page describes its backward in words: the output
+ * gradient meets the signed, scaled weights for grad_input and the signed,
+ * scaled activations for grad_weight, grad_input is clipped, grad_scale_a is
+ * returned and scale_w gets none. The qconv/binary/cutlass/layer page prints
+ * the same steps for the conv (BinaryConv2dForward.backward). The linear form
+ * here is that conv form with a 1x1 kernel on a 1x1 image (batch M, C = K
+ * input features, O = N outputs), a reading taken here:
+ *
+ *   grad_in[m][k]  = (scale_w * sum_n g[m][n] * sign0(W[n][k])) * mid(x[m][k])
+ *   mid(v)         = 0 if the fp32 quotient v / scale_a is < -1 or > 1, else 1
+ *   grad_scale_a   = sum_{m,k} grad_in[m][k] * sign0(x[m][k]) / sqrt(M * K)
+ *   grad_w[n][k]   = sum_m g[m][n] * (sign0(x[m][k]) * scale_a)
+ *
+ * sign0 is torch.sign as the backward uses it (unlike the forward's rule):
+ * 0 for +-0, NaN for NaN, +-1 otherwise. The clip quotient is one IEEE fp32
+ * division of the widened input by scale_a (a reading taken here: the page
+ * divides in the layer's dtype); a NaN quotient fails both tests, so its mask
+ * is 1, as the page's 1 - small - large gives. The mask multiplies (0 * inf
+ * is NaN, as on the page). Sums are in double, products exact.
+ * ------------------------------------------------------------------------- */
+static double sign0(float v) {
+  if (v != v) return NAN;
+  return v > 0.0f ? 1.0 : (v < 0.0f ? -1.0 : 0.0);
+}
+
+static double clip_mid(float v, float scale_a) {
+  float q = v / scale_a;
+  double small = q < -1.0f ? 1.0 : 0.0, large = q > 1.0f ? 1.0 : 0.0;
+  return 1.0 - small - large;
+}
+
+/* grad_in [M][K] and *grad_scale_a; g [M][N], W [N][K], x [M][K] in their dtypes. */
+void oracle_linear_grad_input(const void *g, int gdt, const void *w, int wdt, const void *x, int xdt,
+                              int64_t M, int64_t N, int64_t K, float scale_a, float scale_w,
+                              double *grad_in, double *grad_scale_a) {
+  double *ws = (double *)malloc(sizeof(double) * (size_t)(N * K));
+  if (!ws) {
+    *grad_scale_a = NAN;
+    return;
+  }
+  for (int64_t i = 0; i < N * K; i++) ws[i] = sign0(widen(w, wdt, i)) * (double)scale_w;
+#pragma omp parallel for schedule(static)
+  for (int64_t m = 0; m < M; m++) {
+    double *row = grad_in + m * K;
+    for (int64_t k = 0; k < K; k++) row[k] = 0.0;
+    for (int64_t n = 0; n < N; n++) {
+      double gv = (double)widen(g, gdt, m * N + n);
+      const double *wr = ws + n * K;
+      for (int64_t k = 0; k < K; k++) row[k] += gv * wr[k];
+    }
+    for (int64_t k = 0; k < K; k++) row[k] *= clip_mid(widen(x, xdt, m * K + k), scale_a);
+  }
+  free(ws);
+  double total = 0.0;
+  for (int64_t i = 0; i < M * K; i++) total += grad_in[i] * sign0(widen(x, xdt, i));
+  *grad_scale_a = total / sqrt((double)M * (double)K);
+}
+
+/* grad_w [N][K]; g [M][N], x [M][K] in their dtypes. */
+void oracle_linear_grad_weight(const void *g, int gdt, const void *x, int xdt, int64_t M, int64_t N,
+                               int64_t K, float scale_a, double *grad_w) {
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; n++) {
+    double *row = grad_w + n * K;
+    for (int64_t k = 0; k < K; k++) row[k] = 0.0;
+    for (int64_t m = 0; m < M; m++) {
+      double gv = (double)widen(g, gdt, m * N + n);
+      for (int64_t k = 0; k < K; k++) row[k] += gv * (sign0(widen(x, xdt, m * K + k)) * (double)scale_a);
+    }
+  }
+}

@@ -16,6 +16,7 @@ import pytest
 import torch
 
 import oracle
+from backward_pins import PINS as BACKWARD_PINS
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "bnn_oracle.c")
@@ -64,6 +65,16 @@ MUTANTS = {
     "w8a8_step_255": ("static float q_step(float amax) { return amax / 127.0f; }",
                       "static float q_step(float amax) { return amax / 255.0f; }"),
     "abs_mean_fixed_factor": ("return factor * (sum / (double)count);", "return 2.0 * (sum / (double)count);"),
+    "bwd_sign0_zero_is_one": ("return v > 0.0f ? 1.0 : (v < 0.0f ? -1.0 : 0.0);", "return v >= 0.0f ? 1.0 : -1.0;"),
+    "bwd_clip_inclusive": ("double small = q < -1.0f ? 1.0 : 0.0", "double small = q <= -1.0f ? 1.0 : 0.0"),
+    "bwd_clip_on_x_not_quotient": ("float q = v / scale_a;", "float q = v;"),
+    "bwd_drops_sqrt": ("*grad_scale_a = total / sqrt((double)M * (double)K);",
+                       "*grad_scale_a = total / ((double)M * (double)K);"),
+    "bwd_weight_transposed": ("ws[i] = sign0(widen(w, wdt, i)) * (double)scale_w;",
+                              "ws[i] = sign0(widen(w, wdt, (i % N) * K + (i / N) % K)) * (double)scale_w;"),
+    "bwd_grad_w_drops_scale_a": ("row[k] += gv * (sign0(widen(x, xdt, m * K + k)) * (double)scale_a);",
+                                 "row[k] += gv * (sign0(widen(x, xdt, m * K + k)));"),
+    "bwd_grad_scale_a_unsigned": ("total += grad_in[i] * sign0(widen(x, xdt, i));", "total += grad_in[i];"),
 }
 
 
@@ -257,6 +268,8 @@ def _pins(orc):
                 and orc.abs_mean_scale(torch.tensor([0.5, -2.5]), 2.0) == 3.0)
 
     check("abs_mean_closed_forms", abs_mean)
+    for name, pin in BACKWARD_PINS.items():
+        check(name, lambda pin=pin: pin(orc))
     return failed
 
 
