@@ -37,7 +37,8 @@ EXPORTS = ("bnn_pack_sign", "bnn_pack_sign_nchw", "bnn_pack_sign_shift", "bnn_pa
            "bnn_abs_mean_scale", "bnn_abs_mean_workspace_bytes", "bnn_w_pack", "bnn_w_pack_conv",
            "bnn_conv2d_ex", "bnn_quant_i8_nhwc", "bnn_quant_i8_weight", "bnn_w8a8_conv2d", "bnn_gemm", "bnn_conv2d",
            "bnn_gemm_workspace_bytes", "bnn_conv2d_workspace_bytes", "bnn_gemm_auto_path",
-           "bnn_conv2d_auto_path", "bnn_last_path", "bnn_status_string")
+           "bnn_conv2d_auto_path", "bnn_last_path", "bnn_status_string",
+           "bnn_linear_grad_input", "bnn_linear_grad_input_workspace_bytes", "bnn_linear_grad_weight")
 
 _PATHS = {"auto": PATH_AUTO, "xor": PATH_XOR, "mfma": PATH_MFMA, "mfma_fp4": PATH_MFMA_FP4}
 _DT = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16, torch.int32: I32}
@@ -47,6 +48,7 @@ _TORCH = {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16, I32: tor
 def _bind(path: str) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     P, I64, I, D, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_size_t
+    F = ctypes.c_float
     sig = {
         "bnn_pack_sign": ([P, I, I64, I64, P, P], I),
         "bnn_pack_sign_nchw": ([P, I, I64, I64, I64, I64, P, P], I),
@@ -54,6 +56,9 @@ def _bind(path: str) -> ctypes.CDLL:
         "bnn_pack_sign_nchw_shift": ([P, I, I64, I64, I64, I64, P, I, P, P], I),
         "bnn_abs_mean_scale": ([P, I, I64, D, P, P, SZ, P], I),
         "bnn_abs_mean_workspace_bytes": ([I64], SZ),
+        "bnn_linear_grad_input": ([P, P, P, I, I64, I64, I64, F, F, P, P, P, SZ, P], I),
+        "bnn_linear_grad_input_workspace_bytes": ([I64, I64], SZ),
+        "bnn_linear_grad_weight": ([P, P, I, I64, I64, I64, F, P, P], I),
         "bnn_w_pack": ([P, I, I64, I64, I, P, P], I),
         "bnn_w_pack_conv": ([P, I, I64, I64, I, I, P, P], I),
         "bnn_quant_i8_nhwc": ([P, I, I64, I64, I64, I64, D, P, P], I),
@@ -391,4 +396,61 @@ def w8a8_conv2d(x_q: torch.Tensor, w_q: torch.Tensor, amax_x: float, amax_w: flo
     _check(lib.bnn_w8a8_conv2d(x_q.data_ptr(), n, c, h, w, w_q.data_ptr(), o, float(amax_x),
                                float(amax_w), kh, kw, sh, sw, ph, pw, dh, dw, out.data_ptr(),
                                _DT[out.dtype], _stream(x_q)), "bnn_w8a8_conv2d")
+    return out
+
+
+def _half_pair(t: torch.Tensor, name: str) -> int:
+    if t.dtype not in (torch.float16, torch.bfloat16):
+        raise TypeError(f"{name} must be float16 or bfloat16, got {t.dtype}")
+    return _DT[t.dtype]
+
+
+def linear_grad_input(grad_out: torch.Tensor, weight: torch.Tensor, x: torch.Tensor,
+                      scale_a: float, scale_w: float, out: torch.Tensor | None = None,
+                      grad_scale_a: torch.Tensor | None = None,
+                      workspace: torch.Tensor | None = None):
+    """Straight-through backward of the binarized linear layer, input side. grad_out [M, N],
+    weight [N, K] (the float weight) and x [M, K] share one 16-bit dtype. Returns
+    (grad_input fp32 [M, K], grad_scale_a 0-dim float64), both on the device:
+    grad_input = (scale_w * grad_out @ sign(weight)) * mid(x), mid = 0 where the fp32
+    x / scale_a is outside [-1, 1]; grad_scale_a = sum(grad_input * sign(x)) / sqrt(M * K)."""
+    g, w, x = _dev(grad_out, "grad_out"), _dev(weight, "weight"), _dev(x, "x")
+    dt = _half_pair(g, "grad_out")
+    if w.dtype != g.dtype or x.dtype != g.dtype:
+        raise TypeError("grad_out, weight and x must share one dtype")
+    m, n = g.shape
+    n2, k = w.shape
+    if n2 != n or tuple(x.shape) != (m, k):
+        raise ValueError(f"shape mismatch: grad_out {tuple(g.shape)}, weight {tuple(w.shape)}, x {tuple(x.shape)}")
+    if out is None:
+        out = torch.empty((m, k), dtype=torch.float32, device=g.device)
+    if grad_scale_a is None:
+        grad_scale_a = torch.empty((), dtype=torch.float64, device=g.device)
+    need = lib.bnn_linear_grad_input_workspace_bytes(m, k)
+    if workspace is None:
+        workspace = _workspace(need, g.device)
+    _check(lib.bnn_linear_grad_input(g.data_ptr(), w.data_ptr(), x.data_ptr(), dt, m, n, k,
+                                     float(scale_a), float(scale_w), out.data_ptr(),
+                                     grad_scale_a.data_ptr(), workspace.data_ptr(),
+                                     workspace.numel() * workspace.element_size(), _stream(g)),
+           "bnn_linear_grad_input")
+    return out, grad_scale_a
+
+
+def linear_grad_weight(grad_out: torch.Tensor, x: torch.Tensor, scale_a: float,
+                       out: torch.Tensor | None = None) -> torch.Tensor:
+    """Straight-through backward of the binarized linear layer, weight side: fp32 [N, K] =
+    scale_a * grad_out^T @ sign(x) for grad_out [M, N] and x [M, K] of one 16-bit dtype."""
+    g, x = _dev(grad_out, "grad_out"), _dev(x, "x")
+    dt = _half_pair(g, "grad_out")
+    if x.dtype != g.dtype:
+        raise TypeError("grad_out and x must share one dtype")
+    m, n = g.shape
+    if x.shape[0] != m:
+        raise ValueError(f"shape mismatch: grad_out {tuple(g.shape)}, x {tuple(x.shape)}")
+    k = x.shape[1]
+    if out is None:
+        out = torch.empty((n, k), dtype=torch.float32, device=g.device)
+    _check(lib.bnn_linear_grad_weight(g.data_ptr(), x.data_ptr(), dt, m, n, k, float(scale_a),
+                                      out.data_ptr(), _stream(g)), "bnn_linear_grad_weight")
     return out

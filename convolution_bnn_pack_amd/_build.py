@@ -11,7 +11,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libbnn.so")
 OBJDIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["pack.hip", "gemm_xor.hip", "gemm_mfma.hip", "w8a8.hip", "bnn_api.hip"]
+SOURCES = ["pack.hip", "gemm_xor.hip", "gemm_mfma.hip", "w8a8.hip", "backward.hip", "bnn_api.hip"]
 HEADERS = ["bnn_device.h", "launch.h"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -1,0 +1,256 @@
+// Straight-through backward of the binarized linear layer on the matrix cores.
+//
+// Both gradients are dense contractions of the 16-bit output gradient g with a
+// matrix of signs (torch.sign: -1, 0, +1, NaN for NaN), so they run on the
+// 32x32x16 bf16 / f16 MFMA with fp32 sums; every product is exact.
+//   grad_input [M][K] = (scale_w * g[M][N] @ sign(W)[N][K]) * mid(x)
+//   grad_weight[N][K] = scale_a * g^T[N][M] @ sign(x)[M][K]
+// (BinaryConv2dForward.backward on the qconv/binary/cutlass/layer page, read
+// with a 1x1 kernel, as the BinaryLinearForward page describes its backward.)
+// mid is 0 where the fp32 quotient x / scale_a is below -1 or above 1 and 1
+// elsewhere; the grad_input epilogue also forms each workgroup's double sum of
+// grad_input * sign(x), and one more kernel reduces them into grad_scale_a.
+//
+// One kernel serves both: C[i][j] = scale * sum_r A(i, r) * sign(F[r][j]),
+// where A is stored [I][R] (grad_input: g) or [R][I] (grad_weight: g read
+// transposed) and F is [R][J] (W, or x). A 128x128 tile per workgroup of
+// four waves (2x2, 64x64 each), 32-deep stages double-buffered in LDS with the
+// reduction index innermost, so each lane's MFMA operand is one 16-byte read.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launch.h"
+
+namespace bnn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kBM = 128, kBN = 128, kBK = 32;
+constexpr int kPitch = kBK + 8;  // u16 per LDS row: 80 bytes keeps rows 16-byte aligned
+constexpr int kThreads = 256;
+
+struct BwdArgs {
+  const uint16_t* a;  // [I][R] or [R][I]
+  const uint16_t* f;  // [R][J]; the operand is its sign
+  const uint16_t* x;  // grad_input epilogue: x [I][J]
+  float* out;         // [I][J]
+  double* part;       // grad_input epilogue: one sum per workgroup
+  int I, J, R;
+  float scale;        // scale_w (grad_input) or scale_a (grad_weight)
+  float scale_a;      // divisor of the clip test
+};
+
+// torch.sign of a 16-bit float, as bits of the same format.
+template <bool BF>
+__device__ inline uint32_t sign_bits(uint32_t v) {
+  constexpr uint32_t inf = BF ? 0x7f80u : 0x7c00u, one = BF ? 0x3f80u : 0x3c00u,
+                     nan = BF ? 0x7fc0u : 0x7e00u;
+  const uint32_t a = v & 0x7fffu;
+  return a == 0 ? 0u : (a > inf ? nan : ((v & 0x8000u) | one));
+}
+
+template <bool BF>
+__device__ inline float widen16(uint16_t v) {
+  if (BF) return __uint_as_float((uint32_t)v << 16);
+  return (float)__ushort_as_half(v);
+}
+
+__device__ inline uint16_t u16_of(const uint4& v, int e) {
+  const uint32_t w = e < 2 ? (e == 0 ? v.x : v.x >> 16) : e < 4 ? (e == 2 ? v.y : v.y >> 16)
+                   : e < 6 ? (e == 4 ? v.z : v.z >> 16) : (e == 6 ? v.w : v.w >> 16);
+  return (uint16_t)w;
+}
+
+template <bool BF>
+__device__ inline void mfma(const uint16_t* pa, const uint16_t* pb, f32x16& acc) {
+  if constexpr (BF) {
+    const bf16x8 va = *reinterpret_cast<const bf16x8*>(pa);
+    const bf16x8 vb = *reinterpret_cast<const bf16x8*>(pb);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, vb, acc, 0, 0, 0);
+  } else {
+    const f16x8 va = *reinterpret_cast<const f16x8*>(pa);
+    const f16x8 vb = *reinterpret_cast<const f16x8*>(pb);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, vb, acc, 0, 0, 0);
+  }
+}
+
+// AT: A stored [R][I]. GI: grad_input epilogue (clip mask, scale_a partial sums).
+template <bool BF, bool AT, bool GI>
+__global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(BwdArgs p) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][kBM * kPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][kBN * kPitch];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int tiles_j = (p.J + kBN - 1) / kBN;
+  const int i0 = (int)(blockIdx.x / tiles_j) * kBM, j0 = (int)(blockIdx.x % tiles_j) * kBN;
+  const uint4 zero = make_uint4(0, 0, 0, 0);
+
+  // Per stage each thread moves 32 bytes of A and 32 of F.
+  //  A, [I][R]: chunks (row, 8 r) = tid and tid + 256 -> row = c / 4, r8 = c % 4.
+  //  A, [R][I] and F, [R][J]: rows 2q, 2q + 1 (q = tid / 16) of 8 columns (tid % 16),
+  //  stored transposed as 32-bit pairs of consecutive r.
+  uint4 ra[2], rf[2];
+  auto load = [&](int r0) {
+    if constexpr (!AT) {
+#pragma unroll
+      for (int u = 0; u < 2; u++) {
+        const int c = tid + u * kThreads, row = c >> 2, r = r0 + (c & 3) * 8;
+        ra[u] = (i0 + row < p.I && r < p.R)
+                    ? *reinterpret_cast<const uint4*>(p.a + (int64_t)(i0 + row) * p.R + r) : zero;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 2; u++) {
+        const int r = r0 + 2 * (tid >> 4) + u, i = i0 + (tid & 15) * 8;
+        ra[u] = (r < p.R && i < p.I) ? *reinterpret_cast<const uint4*>(p.a + (int64_t)r * p.I + i) : zero;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+      const int r = r0 + 2 * (tid >> 4) + u, j = j0 + (tid & 15) * 8;
+      rf[u] = (r < p.R && j < p.J) ? *reinterpret_cast<const uint4*>(p.f + (int64_t)r * p.J + j) : zero;
+    }
+  };
+  auto store = [&](int buf) {
+    if constexpr (!AT) {
+#pragma unroll
+      for (int u = 0; u < 2; u++) {
+        const int c = tid + u * kThreads;
+        *reinterpret_cast<uint4*>(&sA[buf][(c >> 2) * kPitch + (c & 3) * 8]) = ra[u];
+      }
+    } else {
+      const int rr = 2 * (tid >> 4), ii = (tid & 15) * 8;
+#pragma unroll
+      for (int e = 0; e < 8; e++)
+        *reinterpret_cast<uint32_t*>(&sA[buf][(ii + e) * kPitch + rr]) =
+            (uint32_t)u16_of(ra[0], e) | ((uint32_t)u16_of(ra[1], e) << 16);
+    }
+    const int rr = 2 * (tid >> 4), jj = (tid & 15) * 8;
+#pragma unroll
+    for (int e = 0; e < 8; e++)
+      *reinterpret_cast<uint32_t*>(&sB[buf][(jj + e) * kPitch + rr]) =
+          sign_bits<BF>(u16_of(rf[0], e)) | (sign_bits<BF>(u16_of(rf[1], e)) << 16);
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; a++)
+#pragma unroll
+    for (int b = 0; b < 2; b++)
+#pragma unroll
+      for (int v = 0; v < 16; v++) acc[a][b][v] = 0.0f;
+
+  const int nk = (p.R + kBK - 1) / kBK;
+  if (nk > 0) {
+    load(0);
+    store(0);
+  }
+  __syncthreads();
+  const int half = (lane >> 5) * 8, l32 = lane & 31;
+  for (int kt = 0; kt < nk; kt++) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) load((kt + 1) * kBK);
+#pragma unroll
+    for (int ks = 0; ks < kBK; ks += 16) {
+#pragma unroll
+      for (int ti = 0; ti < 2; ti++)
+#pragma unroll
+        for (int tj = 0; tj < 2; tj++)
+          mfma<BF>(&sA[buf][(wm * 64 + ti * 32 + l32) * kPitch + ks + half],
+                   &sB[buf][(wn * 64 + tj * 32 + l32) * kPitch + ks + half], acc[ti][tj]);
+    }
+    if (kt + 1 < nk) store(buf ^ 1);
+    __syncthreads();
+  }
+
+  // Lane (l32, half) of tile (ti, tj) holds column j = .. + l32 and rows 8g + half/2 + t.
+  double part = 0.0;
+#pragma unroll
+  for (int ti = 0; ti < 2; ti++)
+#pragma unroll
+    for (int tj = 0; tj < 2; tj++) {
+      const int j = j0 + wn * 64 + tj * 32 + l32;
+#pragma unroll
+      for (int v = 0; v < 16; v++) {
+        const int i = i0 + wm * 64 + ti * 32 + 8 * (v >> 2) + (half >> 1) + (v & 3);
+        if (i >= p.I || j >= p.J) continue;
+        const int64_t o = (int64_t)i * p.J + j;
+        float val = acc[ti][tj][v] * p.scale;
+        if constexpr (GI) {
+          const float xv = widen16<BF>(p.x[o]);
+          const float q = xv / p.scale_a;
+          val *= 1.0f - (q < -1.0f ? 1.0f : 0.0f) - (q > 1.0f ? 1.0f : 0.0f);
+          const double s = xv != xv ? (double)NAN : (xv > 0.0f ? 1.0 : (xv < 0.0f ? -1.0 : 0.0));
+          part += (double)val * s;
+        }
+        p.out[o] = val;
+      }
+    }
+  if constexpr (GI) {
+    __shared__ double red[kThreads];
+    red[tid] = part;
+    __syncthreads();
+    for (int s = kThreads / 2; s > 0; s >>= 1) {
+      if (tid < s) red[tid] += red[tid + s];
+      __syncthreads();
+    }
+    if (tid == 0) p.part[blockIdx.x] = red[0];
+  }
+}
+
+// grad_scale_a = (sum of the workgroup sums, in double) / sqrt(count).
+__global__ __launch_bounds__(kThreads) void bwd_scale_a_kernel(const double* part, int n,
+                                                                double count, double* out) {
+  __shared__ double red[kThreads];
+  double s = 0.0;
+  for (int i = threadIdx.x; i < n; i += kThreads) s += part[i];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int h = kThreads / 2; h > 0; h >>= 1) {
+    if ((int)threadIdx.x < h) red[threadIdx.x] += red[threadIdx.x + h];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[0] = red[0] / sqrt(count);
+}
+
+template <bool AT, bool GI>
+hipError_t launch_bwd(bool bf, const BwdArgs& a, hipStream_t s) {
+  const int64_t tiles = (int64_t)((a.I + kBM - 1) / kBM) * ((a.J + kBN - 1) / kBN);
+  if (tiles == 0) return hipSuccess;
+  if (bf)
+    hipLaunchKernelGGL((bwd_gemm_kernel<true, AT, GI>), dim3((unsigned)tiles), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((bwd_gemm_kernel<false, AT, GI>), dim3((unsigned)tiles), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int64_t bwd_grad_input_parts(int64_t m, int64_t k) {
+  return ((m + kBM - 1) / kBM) * ((k + kBN - 1) / kBN);
+}
+
+hipError_t launch_linear_grad_input(const void* g, const void* w, const void* x, bool bf,
+                                    int64_t m, int64_t n, int64_t k, float scale_a, float scale_w,
+                                    float* grad_in, double* part, double* grad_scale_a,
+                                    hipStream_t s) {
+  BwdArgs a{static_cast<const uint16_t*>(g), static_cast<const uint16_t*>(w),
+            static_cast<const uint16_t*>(x), grad_in, part, (int)m, (int)k, (int)n, scale_w, scale_a};
+  hipError_t e = launch_bwd<false, true>(bf, a, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_scale_a_kernel, dim3(1), dim3(kThreads), 0, s, part,
+                     (int)bwd_grad_input_parts(m, k), (double)m * (double)k, grad_scale_a);
+  return hipGetLastError();
+}
+
+hipError_t launch_linear_grad_weight(const void* g, const void* x, bool bf, int64_t m, int64_t n,
+                                     int64_t k, float scale_a, float* grad_w, hipStream_t s) {
+  BwdArgs a{static_cast<const uint16_t*>(g), static_cast<const uint16_t*>(x), nullptr, grad_w,
+            nullptr, (int)n, (int)k, (int)m, scale_a, scale_a};
+  return launch_bwd<true, false>(bf, a, s);
+}
+
+}  // namespace bnn

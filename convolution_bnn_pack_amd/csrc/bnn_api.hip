@@ -18,6 +18,7 @@ namespace {
 thread_local int g_last_path = 0;
 
 bool float_dtype(int d) { return d == BNN_F32 || d == BNN_F16 || d == BNN_BF16; }
+bool half_dtype(int d) { return d == BNN_F16 || d == BNN_BF16; }
 bool out_dtype_ok(int d) { return float_dtype(d) || d == BNN_I32; }
 int elem_bytes(int d) { return d == BNN_F32 ? 4 : 2; }
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -405,6 +406,44 @@ bnn_status bnn_w8a8_conv2d(const int8_t* x_q, int64_t n, int64_t c, int64_t h, i
   return hip_status(bnn::launch_w8a8_conv(x_q, w_q, out, out_dtype, n, c, h, w, out_channels, ho,
                                           wo, kernel_h, kernel_w, stride_h, stride_w, pad_h, pad_w,
                                           dil_h, dil_w, alpha, static_cast<hipStream_t>(stream)));
+}
+
+size_t bnn_linear_grad_input_workspace_bytes(int64_t m, int64_t k) {
+  if (m <= 0 || k <= 0) return 0;
+  return (size_t)bnn::bwd_grad_input_parts(m, k) * sizeof(double);
+}
+
+bnn_status bnn_linear_grad_input(const void* grad_out, const void* weight, const void* x,
+                                 int dtype, int64_t m, int64_t n, int64_t k, float scale_a,
+                                 float scale_w, float* grad_in, double* grad_scale_a,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  if (!half_dtype(dtype)) return BNN_ERR_DTYPE;
+  if (m <= 0 || k <= 0 || n < 0 || n % 8 != 0 || k % 8 != 0) return BNN_ERR_SHAPE;
+  if (!int_fits(m * k) || !int_fits(n * k) || !int_fits(m * n)) return BNN_ERR_SHAPE;
+  if (!x || !grad_in || !grad_scale_a || (n > 0 && (!grad_out || !weight))) return BNN_ERR_NULL;
+  if (!aligned(x, 2) || !aligned(grad_in, 4) || !aligned(grad_scale_a, 8)) return BNN_ERR_ALIGN;
+  if (n > 0 && (!aligned(grad_out, 16) || !aligned(weight, 16))) return BNN_ERR_ALIGN;
+  if (!workspace || workspace_bytes < bnn_linear_grad_input_workspace_bytes(m, k))
+    return BNN_ERR_WORKSPACE;
+  if (!aligned(workspace, 8)) return BNN_ERR_ALIGN;
+  return hip_status(bnn::launch_linear_grad_input(
+      grad_out, weight, x, dtype == BNN_BF16, m, n, k, scale_a, scale_w, grad_in,
+      static_cast<double*>(workspace), grad_scale_a, static_cast<hipStream_t>(stream)));
+}
+
+bnn_status bnn_linear_grad_weight(const void* grad_out, const void* x, int dtype, int64_t m,
+                                  int64_t n, int64_t k, float scale_a, float* grad_w,
+                                  void* stream) {
+  if (!half_dtype(dtype)) return BNN_ERR_DTYPE;
+  if (m < 0 || n < 0 || k < 0 || n % 8 != 0 || k % 8 != 0) return BNN_ERR_SHAPE;
+  if (!int_fits(m * k) || !int_fits(n * k) || !int_fits(m * n)) return BNN_ERR_SHAPE;
+  if (n == 0 || k == 0) return BNN_OK;
+  if (!grad_w || (m > 0 && (!grad_out || !x))) return BNN_ERR_NULL;
+  if (!aligned(grad_w, 4)) return BNN_ERR_ALIGN;
+  if (m > 0 && (!aligned(grad_out, 16) || !aligned(x, 16))) return BNN_ERR_ALIGN;
+  return hip_status(bnn::launch_linear_grad_weight(grad_out, x, dtype == BNN_BF16, m, n, k,
+                                                   scale_a, grad_w,
+                                                   static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

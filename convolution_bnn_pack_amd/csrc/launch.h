@@ -66,4 +66,15 @@ hipError_t launch_w8a8_conv(const int8_t* xq, const int8_t* wq, void* out, int o
                             int64_t wo, int kh, int kw, int sh, int sw, int ph, int pw, int dh,
                             int dw, float alpha, hipStream_t stream);
 
+// Straight-through linear backward (bf = bfloat16 operands, else float16).
+// grad_in [m][k] fp32, grad_scale_a one double, through bwd_grad_input_parts(m, k) doubles of part.
+int64_t bwd_grad_input_parts(int64_t m, int64_t k);
+hipError_t launch_linear_grad_input(const void* g, const void* w, const void* x, bool bf,
+                                    int64_t m, int64_t n, int64_t k, float scale_a, float scale_w,
+                                    float* grad_in, double* part, double* grad_scale_a,
+                                    hipStream_t s);
+// grad_w [n][k] fp32.
+hipError_t launch_linear_grad_weight(const void* g, const void* x, bool bf, int64_t m, int64_t n,
+                                     int64_t k, float scale_a, float* grad_w, hipStream_t s);
+
 }  // namespace bnn

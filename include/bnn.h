@@ -220,6 +220,37 @@ bnn_status bnn_w8a8_conv2d(const int8_t* x_q, int64_t n, int64_t c, int64_t h, i
                            int pad_w, int dil_h, int dil_w, void* out, int out_dtype,
                            void* stream);
 
+/* ---- Straight-through backward of the binarized linear layer ----
+ * BinaryConv2dForward.backward on the qconv/binary/cutlass/layer page gives the steps for the
+ * conv; the BinaryLinearForward page describes the linear layer's backward in the same terms
+ * (signs and scales, clipped grad_input, grad_scale_a, no gradient for scale_w). These calls are
+ * those steps with a 1x1 kernel:
+ *   grad_in[m][k]  = (scale_w * sum_n g[m][n] * sign(W[n][k])) * mid(x[m][k])
+ *   mid(v)         = 0 if the fp32 quotient v / scale_a is < -1 or > 1, else 1 (NaN -> 1)
+ *   grad_scale_a   = sum over m, k of grad_in * sign(x), divided by sqrt(m * k)
+ *   grad_w[n][k]   = scale_a * sum_m g[m][n] * sign(x[m][k])
+ * with sign = torch.sign (0 for +-0, NaN for NaN), unlike the forward's x >= 0 rule.
+ * g [m][n] (output gradient), W [n][k] (the float weight the layer keeps) and x [m][k] (the
+ * layer's input) share one dtype, BNN_F16 or BNN_BF16; products are exact and sums fp32 (the
+ * scale is applied once to the fp32 sum); grad_in and grad_w are fp32, grad_scale_a double
+ * (summed in double). n and k must be multiples of 8; g, W and x 16-byte aligned. The int8
+ * quantization of grad_w on the page is not part of these calls.
+ *
+ * grad_input: m, k > 0 (the page divides by sqrt(m * k)); grad_in [m][k] and grad_scale_a
+ * (one double) are device outputs; workspace: at least
+ * bnn_linear_grad_input_workspace_bytes(m, k) bytes of device memory, 8-byte aligned, whose
+ * contents are overwritten. */
+size_t bnn_linear_grad_input_workspace_bytes(int64_t m, int64_t k);
+bnn_status bnn_linear_grad_input(const void* grad_out, const void* weight, const void* x,
+                                 int dtype, int64_t m, int64_t n, int64_t k, float scale_a,
+                                 float scale_w, float* grad_in, double* grad_scale_a,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+/* grad_weight: grad_w [n][k] fp32 device output; m = 0 writes zeros; n = 0 or k = 0 does
+ * nothing. */
+bnn_status bnn_linear_grad_weight(const void* grad_out, const void* x, int dtype, int64_t m,
+                                  int64_t n, int64_t k, float scale_a, float* grad_w,
+                                  void* stream);
+
 /* Workspace sizes (bytes) for the calls above; 0 when x is already packed. */
 size_t bnn_gemm_workspace_bytes(int64_t m, int64_t k, int x_dtype);
 size_t bnn_conv2d_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w, int x_dtype);

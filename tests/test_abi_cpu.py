@@ -268,3 +268,35 @@ def test_auto_path_choices(bnn):
     assert bnn.gemm_auto_path(64, 64, (1 << 24) + 32) == bnn.PATH_MFMA            # fp4 sums inexact
     assert bnn.conv2d_auto_path(1, 32, 20, 20, 8, 9, 1, 4, 1) == bnn.PATH_MFMA_FP4   # 81 taps
     assert bnn.conv2d_auto_path(1, 1 << 21, 4, 4, 8, 3, 1, 1, 1) == bnn.PATH_MFMA     # K = 9 * 2^21 > 2^24
+
+
+def test_backward_argument_checks(bnn):
+    L = bnn.lib
+
+    def gi(**kw):
+        a = dict(g=FAKE, w=FAKE, x=FAKE, dt=bnn.BF16, m=64, n=64, k=128, sa=1.0, sw=1.0, out=FAKE,
+                 gsa=FAKE, ws=FAKE, wsb=1 << 20)
+        a.update(kw)
+        return L.bnn_linear_grad_input(a["g"], a["w"], a["x"], a["dt"], a["m"], a["n"], a["k"], a["sa"],
+                                       a["sw"], a["out"], a["gsa"], a["ws"], a["wsb"], None)
+    assert L.bnn_linear_grad_input_workspace_bytes(300, 130) == 3 * 2 * 8   # one double per 128x128 tile
+    assert L.bnn_linear_grad_input_workspace_bytes(0, 130) == 0
+    assert gi(dt=bnn.F32) == bnn.ERR_DTYPE and gi(dt=bnn.I32) == bnn.ERR_DTYPE
+    assert gi(m=0) == bnn.ERR_SHAPE and gi(k=0) == bnn.ERR_SHAPE   # the page divides by sqrt(m * k)
+    assert gi(n=60) == bnn.ERR_SHAPE and gi(k=100) == bnn.ERR_SHAPE and gi(n=-8) == bnn.ERR_SHAPE
+    assert gi(m=1 << 20, k=1 << 12) == bnn.ERR_SHAPE
+    assert gi(x=None) == bnn.ERR_NULL and gi(g=None) == bnn.ERR_NULL and gi(gsa=None) == bnn.ERR_NULL
+    assert gi(g=FAKE + 8) == bnn.ERR_ALIGN and gi(w=FAKE + 2) == bnn.ERR_ALIGN
+    assert gi(out=FAKE + 2) == bnn.ERR_ALIGN and gi(gsa=FAKE + 4) == bnn.ERR_ALIGN
+    assert gi(ws=None) == bnn.ERR_WORKSPACE and gi(wsb=7) == bnn.ERR_WORKSPACE
+    assert gi(ws=FAKE + 4) == bnn.ERR_ALIGN
+
+    def gw(**kw):
+        a = dict(g=FAKE, x=FAKE, dt=bnn.F16, m=64, n=64, k=128, sa=1.0, out=FAKE)
+        a.update(kw)
+        return L.bnn_linear_grad_weight(a["g"], a["x"], a["dt"], a["m"], a["n"], a["k"], a["sa"], a["out"], None)
+    assert gw(dt=bnn.F32) == bnn.ERR_DTYPE
+    assert gw(n=12) == bnn.ERR_SHAPE and gw(k=4) == bnn.ERR_SHAPE and gw(m=-1) == bnn.ERR_SHAPE
+    assert gw(out=None) == bnn.ERR_NULL and gw(x=None) == bnn.ERR_NULL
+    assert gw(g=FAKE + 2) == bnn.ERR_ALIGN and gw(out=FAKE + 1) == bnn.ERR_ALIGN
+    assert gw(n=0, g=None, x=None, out=None) == bnn.OK and gw(k=0, out=None) == bnn.OK
