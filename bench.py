@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0           # HBM3E, MI355X
 PEAK_MFMA_I8_TOPS = 5000.0      # dense int8 MFMA, MI355X
 PEAK_MFMA_F4_TOPS = 10100.0     # dense fp4 MFMA, MI355X
+PEAK_MFMA_BF16_TFLOPS = 2500.0  # dense bf16 / fp16 MFMA, MI355X
 # XOR path: 256 CUs x 64 lanes x 2.4 GHz lane-ops; one v_xor_b32 + one v_bcnt_u32_b32
 # cover 32 MACs = 64 binary ops, i.e. 32 binary ops per lane-op.
 PEAK_VALU_BINARY_TOPS = 256 * 64 * 2.4e9 * 32 / 1e12
@@ -48,25 +49,31 @@ W8A8_WORKLOADS = {
     "w8a8_conv_128x128x28x28_s2_f16": ("conv_down_s2_f16", 4.0, 3.0),
     "w8a8_conv_128x128x28x28_d2_f16": ("conv_dil2_f16", 4.0, 3.0),
 }
+# straight-through linear backward (grad_input with clip mask and grad_scale_a, grad_weight):
+# name -> linear workload whose x, W and output shape it differentiates
+BWD_WORKLOADS = {
+    "bwd_linear_2048x4096x4096_f16": "linear_2048x4096x4096_f16",
+    "bwd_linear_16384x8192x8192_bf16": "linear_16384x8192x8192_bf16",
+}
 PACK_WORKLOAD = "pack_linear_16384x8192_bf16"
 # kernel kinds: source file, kernel function name, roofline peak and arithmetic type
 KERNEL_SOURCES = {"mfma": "gemm_mfma.hip", "mfma_fp4": "gemm_mfma.hip", "xor": "gemm_xor.hip",
-                  "w8a8": "w8a8.hip",
+                  "w8a8": "w8a8.hip", "bwd": "backward.hip",
                   "pack": "pack.hip", "pack_shift": "pack.hip", "pack_nchw": "pack.hip",
                   "abs_mean": "pack.hip"}
 KERNEL_NAMES = {"mfma": "mfma_kernel", "mfma_fp4": "mfma_kernel", "xor": "xor_kernel",
-                "w8a8": "w8a8_conv_kernel",
+                "w8a8": "w8a8_conv_kernel", "bwd": "bwd_gemm_kernel",
                 "pack": "pack_rows_kernel", "pack_shift": "pack_rows_shift_kernel",
                 "pack_nchw": "pack_nchw_flat_kernel", "abs_mean": "abs_sum_kernel"}
 PEAKS = {"mfma": PEAK_MFMA_I8_TOPS, "mfma_fp4": PEAK_MFMA_F4_TOPS, "xor": PEAK_VALU_BINARY_TOPS,
-         "w8a8": PEAK_MFMA_I8_TOPS}
+         "w8a8": PEAK_MFMA_I8_TOPS, "bwd": PEAK_MFMA_BF16_TFLOPS}
 DTYPES = {"mfma": "i8", "mfma_fp4": "fp4(e2m1)", "xor": "u32", "w8a8": "i8"}
 CODEC_KINDS = ("pack", "pack_shift", "pack_nchw", "abs_mean")
 
 
 def kernel_kind(name):
     """Kind of a demangled kernel name from a rocprofv3 counter file (None: not ours)."""
-    for kind in CODEC_KINDS + ("xor", "w8a8"):
+    for kind in CODEC_KINDS + ("xor", "w8a8", "bwd"):
         if KERNEL_NAMES[kind] + "<" in name or KERNEL_NAMES[kind] + "(" in name:
             return kind
     if "mfma_kernel<" in name:
@@ -135,7 +142,7 @@ def pmc_summary(args):
             raise SystemExit(f"no {args.copy_kernel} kernel in {path}")
         copy_kib = statistics.median(v for _, v in copy)
         scale = (args.copy_mib << 20) / 1024.0 / copy_kib if args.copy_mib else 1.0
-        for k in ([kind] if kind else ["mfma", "mfma_fp4", "xor", "w8a8"]):
+        for k in ([kind] if kind else ["mfma", "mfma_fp4", "xor", "w8a8", "bwd"]):
             # the workload's kernel is the instantiation launched most often (the parity spot
             # check adds single launches of other output types)
             cands = [(len(vs), name) for name, vs in vals.items() if kernel_kind(name) == k]
@@ -231,10 +238,13 @@ def main():
     torch.cuda.set_device(dev)
     pack_only = args.workload in CODEC_WORKLOADS
     w8a8 = args.workload in W8A8_WORKLOADS
+    bwd = args.workload in BWD_WORKLOADS
     codec_kind, base, shift_dt = CODEC_WORKLOADS.get(args.workload, (None, None, None))
     if w8a8:
         base, amax_x, amax_w = W8A8_WORKLOADS[args.workload]
-    wl = synth.WORKLOADS[base if (pack_only or w8a8) else args.workload]
+    if bwd:
+        base = BWD_WORKLOADS[args.workload]
+    wl = synth.WORKLOADS[base if (pack_only or w8a8 or bwd) else args.workload]
     log(f"workload {args.workload}: generating inputs")
     x, w, sa, sw = synth.make_inputs(wl, draw_weight=not pack_only)
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
@@ -295,6 +305,28 @@ def main():
             bytes_per += 2 * ws.numel() + 8
         kernels = {"pack": [fn]}
         step_fns = kernels["pack"]
+    elif bwd:
+        # step: grad_input (GEMM with the clip mask and the grad_scale_a sums in its epilogue, then
+        # the one-workgroup grad_scale_a reduction) and grad_weight; W is the layer's float weight
+        # in the gradient's dtype
+        m, n, k = wl.gemm_mnk()
+        ops = 2 * 2.0 * m * n * k
+        gdt = wl.x_dtype
+        gcpu = synth.make_grad(m, n, gdt, wl.seed + 70)
+        w = w.to(x.dtype).contiguous()
+        gd, wd = gcpu.to(dev), w.to(dev)
+        gi = torch.empty((m, k), dtype=torch.float32, device=dev)
+        gsa = torch.empty((), dtype=torch.float64, device=dev)
+        gw = torch.empty((n, k), dtype=torch.float32, device=dev)
+        ws = torch.empty(lib.bnn_linear_grad_input_workspace_bytes(m, k), dtype=torch.uint8, device=dev)
+        pack = lambda i: lib.bnn_linear_grad_input(gd.data_ptr(), wd.data_ptr(), xd.data_ptr(), xcode,
+                                                   m, n, k, sa, sw, gi.data_ptr(), gsa.data_ptr(),
+                                                   ws.data_ptr(), ws.numel(), cur_stream())
+        core = lambda i: lib.bnn_linear_grad_weight(gd.data_ptr(), xd.data_ptr(), xcode, m, n, k, sa,
+                                                    gw.data_ptr(), cur_stream())
+        path_used = None
+        kernels = {"pack": [pack], "core": [core]}
+        step_fns = [pack, core]
     elif w8a8:
         # step: activation codes (NCHW -> NHWC int8), then the int8 conv; weight codes are made
         # once ahead, as the layer's weights are
@@ -344,7 +376,24 @@ def main():
 
     # parity spot check before timing (int32 accumulators of sampled rows / images vs the oracle)
     parity = None
-    if w8a8:
+    if bwd:
+        import oracle
+        rows = sorted({0, 1, m // 2, m - 1})
+        if pack(0) != 0 or core(0) != 0:
+            raise RuntimeError("libbnn call failed")
+        torch.cuda.synchronize()
+        ref, _ = oracle.linear_grad_input(gcpu[rows], w, x[rows], sa, sw)
+        got = gi[rows].cpu().double()
+        # fp32 sums of n exact products: within n * 2^-24 * sum|g| * scale_w, plus the scale rounding
+        bound = ((n + 1) * sw * gcpu[rows].double().abs().sum(1, keepdim=True) + ref.abs()) * 2.0 ** -24
+        ok_in = bool(((got - ref).abs() <= bound).all())
+        cols = sorted({0, n // 2, n - 1})
+        refw = oracle.linear_grad_weight(gcpu[:, cols].contiguous(), x, sa)
+        gotw = gw[cols].cpu().double()
+        boundw = ((m + 1) * sa * gcpu[:, cols].double().abs().sum(0).unsqueeze(1) + refw.abs()) * 2.0 ** -24
+        parity = ok_in and bool(((gotw - refw).abs() <= boundw).all())
+        log(f"parity spot check vs oracle (within the fp32 summation bound): {parity}")
+    elif w8a8:
         import oracle
         imgs = sorted({0, wl.batch - 1})
         ref = oracle.w8a8_conv2d_acc(x, w, wl.stride, wl.padding, wl.dilation, amax_x, amax_w,
@@ -424,6 +473,20 @@ def main():
         metric, unit = {"abs_mean": ("abs-mean scale bandwidth", "GB/s")}.get(
             codec_kind, ("sign+pack bandwidth", "GB/s"))
         dtype = "f64" if codec_kind == "abs_mean" else "u32"
+    elif bwd:
+        # both launches are 2*M*N*K-flop contractions; the slower one is the roofline kernel
+        kind = "bwd"
+        name, dom_ms = max((("grad_input", kern_ms["pack"]), ("grad_weight", kern_ms["core"])),
+                           key=lambda t: t[1])
+        achieved = ops / 2 / (dom_ms * 1e-3) / 1e12
+        peak = PEAKS[kind]
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": traffic_for(kind, args.workload),
+                "kernel": f"{KERNEL_NAMES[kind]} ({name})", "kernel_ms": round(dom_ms, 5),
+                "grad_input_ms": round(kern_ms["pack"], 5), "grad_weight_ms": round(kern_ms["core"], 5)}
+        value = ops / (ms_per_step * 1e-3) / 1e12
+        metric, unit = "backward TFLOP/s (2 contractions of 2*M*N*K)", "TFLOP/s"
+        dtype = wl.x_dtype
     else:
         dom_ms = kern_ms["core"]
         kind = "w8a8" if w8a8 else {bnn.PATH_XOR: "xor", bnn.PATH_MFMA: "mfma",
@@ -446,7 +509,11 @@ def main():
                    "timing": "HIP graph of the timed steps, replayed once untimed then once timed"},
         "roofline": roof,
     }
-    if not pack_only:
+    if bwd:
+        result["config"].update({"m": m, "n": n, "k": k, "dtype": wl.x_dtype,
+                                 "outputs": "grad_input fp32 [m, k], grad_scale_a f64, grad_weight fp32 [n, k]"})
+        result["parity_spot_check"] = parity
+    elif not pack_only:
         m, n, k = wl.gemm_mnk()
         result["config"].update({"m": m, "n": n, "k": k, "x_dtype": wl.x_dtype,
                                  "out_dtype": wl.out_dtype,
@@ -462,7 +529,17 @@ def main():
         torch.cuda.synchronize()
         result["copy_calibration_bytes"] = n
         del src, dst
-    if not args.no_cpu_baseline and w8a8:
+    if not args.no_cpu_baseline and bwd:
+        import oracle
+        rows = min(m, 512)          # about 5-15 s of host work at the layer sizes
+        log(f"cpu baseline (oracle on host cores, grad_input of {rows} rows)")
+        t0 = time.perf_counter()
+        oracle.linear_grad_input(gcpu[:rows].contiguous(), w, x[:rows].contiguous(), sa, sw)
+        dt_cpu = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": round(2.0 * rows * n * k / dt_cpu / 1e12, 6), "unit": "TFLOP/s",
+                                  "cores": oracle.num_threads(), "kind": "oracle",
+                                  "sample": f"grad_input of the first {rows} of {m} rows ({dt_cpu:.2f} s)"}
+    elif not args.no_cpu_baseline and w8a8:
         import oracle
         log("cpu baseline (oracle on host cores, one image)")
         t0 = time.perf_counter()

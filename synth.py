@@ -24,7 +24,7 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "conv_out_size", "edge_values",
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "make_grad", "conv_out_size", "edge_values",
            "random_linear_case", "random_conv_case", "make_shift"]
 
 _DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
@@ -232,3 +232,10 @@ def make_shift(n: int, dtype: str, seed: int, axis_values=None) -> torch.Tensor:
     for j, i in enumerate(range(3, n, 11)):
         b[i] = ev[j % ev.numel()]
     return b.contiguous()
+
+
+def make_grad(m: int, n: int, dtype: str, seed: int) -> torch.Tensor:
+    """An output gradient [m, n] for the straight-through backward: ``randn`` in float32 from a
+    CPU generator seeded with ``seed``, cast to ``dtype``."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    return torch.randn((m, n), generator=g, dtype=torch.float32).to(_DT[dtype]).contiguous()
