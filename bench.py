@@ -531,7 +531,7 @@ def main():
         del src, dst
     if not args.no_cpu_baseline and bwd:
         import oracle
-        rows = min(m, 512)          # about 5-15 s of host work at the layer sizes
+        rows = min(m, 4096)         # about 2-10 s of host work at the layer sizes
         log(f"cpu baseline (oracle on host cores, grad_input of {rows} rows)")
         t0 = time.perf_counter()
         oracle.linear_grad_input(gcpu[:rows].contiguous(), w, x[:rows].contiguous(), sa, sw)

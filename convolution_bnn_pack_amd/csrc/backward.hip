@@ -28,8 +28,15 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 128, kBN = 128, kBK = 32;
-constexpr int kPitch = kBK + 8;  // u16 per LDS row: 80 bytes keeps rows 16-byte aligned
+#ifndef BWD_BK
+#define BWD_BK 32
+#endif
+#ifndef BWD_BN
+#define BWD_BN 128
+#endif
+constexpr int kBM = 128, kBN = BWD_BN, kBK = BWD_BK;
+constexpr int kTJ = kBN / 64;    // 32-wide MFMA tiles per wave along j (each wave: 64 x kBN/2)
+constexpr int kPitch = kBK + 8;  // u16 per LDS row: keeps rows 16-byte aligned, staggers banks
 constexpr int kThreads = 256;
 
 struct BwdArgs {
@@ -78,8 +85,14 @@ __device__ inline void mfma(const uint16_t* pa, const uint16_t* pb, f32x16& acc)
 }
 
 // AT: A stored [R][I]. GI: grad_input epilogue (clip mask, scale_a partial sums).
+// Three waves per SIMD (at most 168 registers a lane): the grad_input epilogue would otherwise
+// take the kernel to 177 and two waves, which leaves the LDS and barrier latency exposed.
+#ifndef BWD_WAVES
+#define BWD_WAVES 3
+#endif
 template <bool BF, bool AT, bool GI>
-__global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(BwdArgs p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BWD_WAVES)))
+void bwd_gemm_kernel(BwdArgs p) {
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][kBM * kPitch];
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][kBN * kPitch];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -88,58 +101,82 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(BwdArgs p) {
   const int i0 = (int)(blockIdx.x / tiles_j) * kBM, j0 = (int)(blockIdx.x % tiles_j) * kBN;
   const uint4 zero = make_uint4(0, 0, 0, 0);
 
-  // Per stage each thread moves 32 bytes of A and 32 of F.
-  //  A, [I][R]: chunks (row, 8 r) = tid and tid + 256 -> row = c / 4, r8 = c % 4.
-  //  A, [R][I] and F, [R][J]: rows 2q, 2q + 1 (q = tid / 16) of 8 columns (tid % 16),
-  //  stored transposed as 32-bit pairs of consecutive r.
-  uint4 ra[2], rf[2];
+  // Per stage: A [I][R] in 16-byte chunks (row, 8 consecutive r); A [R][I] and F [R][J] in
+  // pairs of rows (2p, 2p + 1) of 8 consecutive columns, stored transposed as 32-bit pairs of
+  // consecutive r so that the reduction index is innermost in LDS.
+  constexpr int kRowChunks = kBK / 8;                       // A [I][R]: chunks per row
+  constexpr int kNA = AT ? (kBK / 2) * (kBM / 8) / kThreads : kBM * kRowChunks / kThreads;
+  constexpr int kNF = (kBK / 2) * (kBN / 8) / kThreads;     // F: row-pair chunks per thread
+  static_assert(kNA >= 1 && kNF >= 1, "tile too small for the loader");
+  // Transposed chunk c: its row pair and its 8-column chunk. Consecutive lanes take consecutive
+  // row pairs, so a wave's 32-bit LDS stores (one LDS row per column) spread over the banks:
+  // 2-way conflicts, where column-major lanes (rows 8 columns apart, 160 bytes) give 8-way.
+  auto pair_of = [](int c) { return c % (kBK / 2); };
+  auto col_of = [](int c) { return c / (kBK / 2); };
+  uint4 ra[AT ? 2 * kNA : kNA], rf[2 * kNF];
   auto load = [&](int r0) {
     if constexpr (!AT) {
 #pragma unroll
-      for (int u = 0; u < 2; u++) {
-        const int c = tid + u * kThreads, row = c >> 2, r = r0 + (c & 3) * 8;
+      for (int u = 0; u < kNA; u++) {
+        const int c = tid + u * kThreads, row = c / kRowChunks, r = r0 + (c % kRowChunks) * 8;
         ra[u] = (i0 + row < p.I && r < p.R)
                     ? *reinterpret_cast<const uint4*>(p.a + (int64_t)(i0 + row) * p.R + r) : zero;
       }
     } else {
 #pragma unroll
-      for (int u = 0; u < 2; u++) {
-        const int r = r0 + 2 * (tid >> 4) + u, i = i0 + (tid & 15) * 8;
-        ra[u] = (r < p.R && i < p.I) ? *reinterpret_cast<const uint4*>(p.a + (int64_t)r * p.I + i) : zero;
+      for (int u = 0; u < kNA; u++) {
+        const int c = tid + u * kThreads, i = i0 + col_of(c) * 8;
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+          const int r = r0 + 2 * pair_of(c) + h;
+          ra[2 * u + h] = (r < p.R && i < p.I)
+                              ? *reinterpret_cast<const uint4*>(p.a + (int64_t)r * p.I + i) : zero;
+        }
       }
     }
 #pragma unroll
-    for (int u = 0; u < 2; u++) {
-      const int r = r0 + 2 * (tid >> 4) + u, j = j0 + (tid & 15) * 8;
-      rf[u] = (r < p.R && j < p.J) ? *reinterpret_cast<const uint4*>(p.f + (int64_t)r * p.J + j) : zero;
+    for (int u = 0; u < kNF; u++) {
+      const int c = tid + u * kThreads, j = j0 + col_of(c) * 8;
+#pragma unroll
+      for (int h = 0; h < 2; h++) {
+        const int r = r0 + 2 * pair_of(c) + h;
+        rf[2 * u + h] = (r < p.R && j < p.J)
+                            ? *reinterpret_cast<const uint4*>(p.f + (int64_t)r * p.J + j) : zero;
+      }
     }
   };
   auto store = [&](int buf) {
     if constexpr (!AT) {
 #pragma unroll
-      for (int u = 0; u < 2; u++) {
+      for (int u = 0; u < kNA; u++) {
         const int c = tid + u * kThreads;
-        *reinterpret_cast<uint4*>(&sA[buf][(c >> 2) * kPitch + (c & 3) * 8]) = ra[u];
+        *reinterpret_cast<uint4*>(&sA[buf][(c / kRowChunks) * kPitch + (c % kRowChunks) * 8]) = ra[u];
       }
     } else {
-      const int rr = 2 * (tid >> 4), ii = (tid & 15) * 8;
+#pragma unroll
+      for (int u = 0; u < kNA; u++) {
+        const int c = tid + u * kThreads, rr = 2 * pair_of(c), ii = col_of(c) * 8;
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+          *reinterpret_cast<uint32_t*>(&sA[buf][(ii + e) * kPitch + rr]) =
+              (uint32_t)u16_of(ra[2 * u], e) | ((uint32_t)u16_of(ra[2 * u + 1], e) << 16);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kNF; u++) {
+      const int c = tid + u * kThreads, rr = 2 * pair_of(c), jj = col_of(c) * 8;
 #pragma unroll
       for (int e = 0; e < 8; e++)
-        *reinterpret_cast<uint32_t*>(&sA[buf][(ii + e) * kPitch + rr]) =
-            (uint32_t)u16_of(ra[0], e) | ((uint32_t)u16_of(ra[1], e) << 16);
+        *reinterpret_cast<uint32_t*>(&sB[buf][(jj + e) * kPitch + rr]) =
+            sign_bits<BF>(u16_of(rf[2 * u], e)) | (sign_bits<BF>(u16_of(rf[2 * u + 1], e)) << 16);
     }
-    const int rr = 2 * (tid >> 4), jj = (tid & 15) * 8;
-#pragma unroll
-    for (int e = 0; e < 8; e++)
-      *reinterpret_cast<uint32_t*>(&sB[buf][(jj + e) * kPitch + rr]) =
-          sign_bits<BF>(u16_of(rf[0], e)) | (sign_bits<BF>(u16_of(rf[1], e)) << 16);
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[2][kTJ];
 #pragma unroll
   for (int a = 0; a < 2; a++)
 #pragma unroll
-    for (int b = 0; b < 2; b++)
+    for (int b = 0; b < kTJ; b++)
 #pragma unroll
       for (int v = 0; v < 16; v++) acc[a][b][v] = 0.0f;
 
@@ -158,9 +195,9 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(BwdArgs p) {
 #pragma unroll
       for (int ti = 0; ti < 2; ti++)
 #pragma unroll
-        for (int tj = 0; tj < 2; tj++)
+        for (int tj = 0; tj < kTJ; tj++)
           mfma<BF>(&sA[buf][(wm * 64 + ti * 32 + l32) * kPitch + ks + half],
-                   &sB[buf][(wn * 64 + tj * 32 + l32) * kPitch + ks + half], acc[ti][tj]);
+                   &sB[buf][(wn * (kBN / 2) + tj * 32 + l32) * kPitch + ks + half], acc[ti][tj]);
     }
     if (kt + 1 < nk) store(buf ^ 1);
     __syncthreads();
@@ -171,8 +208,8 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(BwdArgs p) {
 #pragma unroll
   for (int ti = 0; ti < 2; ti++)
 #pragma unroll
-    for (int tj = 0; tj < 2; tj++) {
-      const int j = j0 + wn * 64 + tj * 32 + l32;
+    for (int tj = 0; tj < kTJ; tj++) {
+      const int j = j0 + wn * (kBN / 2) + tj * 32 + l32;
 #pragma unroll
       for (int v = 0; v < 16; v++) {
         const int i = i0 + wm * 64 + ti * 32 + 8 * (v >> 2) + (half >> 1) + (v & 3);
