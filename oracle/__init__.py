@@ -71,6 +71,7 @@ def _bind(lib):
     lib.oracle_linear_grad_input.argtypes = [P, I, P, I, P, I, I64, I64, I64, ctypes.c_float,
                                              ctypes.c_float, P, P]
     lib.oracle_linear_grad_weight.argtypes = [P, I, P, I, I64, I64, I64, ctypes.c_float, P]
+    lib.oracle_quant_grad_i8.argtypes = [P, I64, P, P]
     lib.oracle_abs_mean_scale.restype = ctypes.c_double
     return lib
 
@@ -332,3 +333,13 @@ def linear_grad_weight(g: torch.Tensor, x: torch.Tensor, scale_a: float) -> torc
     _load().oracle_linear_grad_weight(g.data_ptr(), _code(g), x.data_ptr(), _code(x), m, n, k,
                                       float(scale_a), out.data_ptr())
     return out
+
+
+def quant_grad_i8(grad_w: torch.Tensor):
+    """int8 codes of a gradient held in fp32 (the conv page's nv_tensor_quant read as the per-tensor
+    symmetric quantizer with amax = max|v|): returns (codes int8, same shape; amax float)."""
+    gw = _cpu(grad_w).to(torch.float64).contiguous()
+    codes = torch.empty(gw.shape, dtype=torch.int8)
+    amax = ctypes.c_float(0.0)
+    _load().oracle_quant_grad_i8(gw.data_ptr(), gw.numel(), codes.data_ptr(), ctypes.addressof(amax))
+    return codes, amax.value

@@ -543,3 +543,31 @@ void oracle_linear_grad_weight(const void *g, int gdt, const void *x, int xdt, i
     }
   }
 }
+
+/* int8 codes of grad_w, as the conv page's backward ends (grad_weight =
+ * nv_tensor_quant(grad_weight)[0]). nv_tensor_quant is not on the pages; it is
+ * read as the same per-tensor symmetric quantizer as the W8A8 conv, with amax
+ * taken from the tensor itself: the gradient is held in fp32 (the value the
+ * contraction produces), amax = max |v| (NaN if any v is NaN), step =
+ * amax / 127 in fp32, code = clamp(rint(v / step), -127, 127), and a NaN
+ * quotient (0 / 0 when every gradient is 0, a NaN amax, inf / inf) codes as 0. */
+void oracle_quant_grad_i8(const double *grad_w, int64_t count, int8_t *codes, float *amax_out) {
+  float amax = 0.0f;
+  for (int64_t i = 0; i < count; i++) {
+    float v = fabsf((float)grad_w[i]);
+    if (v != v) {
+      amax = v;
+      break;
+    }
+    if (v > amax) amax = v;
+  }
+  *amax_out = amax;
+  float step = amax / 127.0f;
+  for (int64_t i = 0; i < count; i++) {
+    float r = rintf((float)grad_w[i] / step);
+    if (r != r) r = 0.0f;
+    if (r > 127.0f) r = 127.0f;
+    if (r < -127.0f) r = -127.0f;
+    codes[i] = (int8_t)r;
+  }
+}

@@ -111,7 +111,37 @@ def pin_edges(orc):
     return gi.tolist() == [[1.0, 1.0]] and math.isnan(gsa)
 
 
+def pin_quant_grad(orc):
+    """Codes against torch's half-even round and clamp with the step from torch's amax; the largest
+    element codes to +-127; every code times the step is within half a step of the value; all-zero
+    and NaN gradients code to 0."""
+    gen = torch.Generator().manual_seed(8)
+    gw = (torch.randn((12, 40), generator=gen) * 3).double()
+    gw[4, 7] = -(gw.abs().max() + 0.5)          # the largest magnitude is negative
+    codes, amax = orc.quant_grad_i8(gw)
+    v = gw.float()
+    want_amax = float(v.abs().max())
+    step = torch.tensor(want_amax, dtype=torch.float32) / 127.0
+    if amax != want_amax:
+        return False
+    if not torch.equal(codes, torch.round(v / step).clamp(-127, 127).to(torch.int8)):
+        return False
+    i = int(v.abs().argmax())
+    if abs(int(codes.view(-1)[i])) != 127:
+        return False
+    if not bool(((codes.double() * float(step) - v.double()).abs() <= float(step) / 2 * (1 + 1e-6)).all()):
+        return False
+    zc, za = orc.quant_grad_i8(torch.zeros((3, 8), dtype=torch.float64))
+    if za != 0.0 or bool(zc.any()):
+        return False
+    gn = gw.clone()
+    gn[1, 2] = float("nan")
+    nc, na = orc.quant_grad_i8(gn)
+    return math.isnan(na) and not bool(nc.any())
+
+
 PINS = {
+    "bwd_quant_grad": pin_quant_grad,
     "bwd_vs_torch_grad": pin_vs_torch_grad,
     "bwd_autograd": pin_autograd,
     "bwd_closed_forms": pin_closed_forms,

@@ -75,6 +75,9 @@ MUTANTS = {
     "bwd_grad_w_drops_scale_a": ("row[k] += gv * (sign0(widen(x, xdt, m * K + k)) * (double)scale_a);",
                                  "row[k] += gv * (sign0(widen(x, xdt, m * K + k)));"),
     "bwd_grad_scale_a_unsigned": ("total += grad_in[i] * sign0(widen(x, xdt, i));", "total += grad_in[i];"),
+    "bwd_quant_step_by_255": ("  float step = amax / 127.0f;\n  for (int64_t i = 0; i < count; i++) {\n    float r = rintf((float)grad_w[i] / step);",
+                              "  float step = amax / 255.0f;\n  for (int64_t i = 0; i < count; i++) {\n    float r = rintf((float)grad_w[i] / step);"),
+    "bwd_quant_amax_signed": ("    float v = fabsf((float)grad_w[i]);", "    float v = (float)grad_w[i];"),
 }
 
 
