@@ -38,7 +38,8 @@ EXPORTS = ("bnn_pack_sign", "bnn_pack_sign_nchw", "bnn_pack_sign_shift", "bnn_pa
            "bnn_conv2d_ex", "bnn_quant_i8_nhwc", "bnn_quant_i8_weight", "bnn_w8a8_conv2d", "bnn_gemm", "bnn_conv2d",
            "bnn_gemm_workspace_bytes", "bnn_conv2d_workspace_bytes", "bnn_gemm_auto_path",
            "bnn_conv2d_auto_path", "bnn_last_path", "bnn_status_string",
-           "bnn_linear_grad_input", "bnn_linear_grad_input_workspace_bytes", "bnn_linear_grad_weight")
+           "bnn_linear_grad_input", "bnn_linear_grad_input_workspace_bytes", "bnn_linear_grad_weight",
+           "bnn_linear_grad_weight_i8", "bnn_linear_grad_weight_i8_workspace_bytes")
 
 _PATHS = {"auto": PATH_AUTO, "xor": PATH_XOR, "mfma": PATH_MFMA, "mfma_fp4": PATH_MFMA_FP4}
 _DT = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16, torch.int32: I32}
@@ -59,6 +60,8 @@ def _bind(path: str) -> ctypes.CDLL:
         "bnn_linear_grad_input": ([P, P, P, I, I64, I64, I64, F, F, P, P, P, SZ, P], I),
         "bnn_linear_grad_input_workspace_bytes": ([I64, I64], SZ),
         "bnn_linear_grad_weight": ([P, P, I, I64, I64, I64, F, P, P], I),
+        "bnn_linear_grad_weight_i8": ([P, P, I, I64, I64, I64, F, P, P, P, P, SZ, P], I),
+        "bnn_linear_grad_weight_i8_workspace_bytes": ([I64, I64], SZ),
         "bnn_w_pack": ([P, I, I64, I64, I, P, P], I),
         "bnn_w_pack_conv": ([P, I, I64, I64, I, I, P, P], I),
         "bnn_quant_i8_nhwc": ([P, I, I64, I64, I64, I64, D, P, P], I),
@@ -454,3 +457,26 @@ def linear_grad_weight(grad_out: torch.Tensor, x: torch.Tensor, scale_a: float,
     _check(lib.bnn_linear_grad_weight(g.data_ptr(), x.data_ptr(), dt, m, n, k, float(scale_a),
                                       out.data_ptr(), _stream(g)), "bnn_linear_grad_weight")
     return out
+
+
+def linear_grad_weight_i8(grad_out: torch.Tensor, x: torch.Tensor, scale_a: float):
+    """grad_weight and its int8 codes (per-tensor symmetric, amax = max|grad_weight|): returns
+    (grad_w fp32 [N, K], codes int8 [N, K], amax 0-dim float32), all on the device; the
+    dequantized gradient is codes * amax / 127."""
+    g, x = _dev(grad_out, "grad_out"), _dev(x, "x")
+    dt = _half_pair(g, "grad_out")
+    if x.dtype != g.dtype:
+        raise TypeError("grad_out and x must share one dtype")
+    m, n = g.shape
+    if x.shape[0] != m:
+        raise ValueError(f"shape mismatch: grad_out {tuple(g.shape)}, x {tuple(x.shape)}")
+    k = x.shape[1]
+    gw = torch.empty((n, k), dtype=torch.float32, device=g.device)
+    codes = torch.empty((n, k), dtype=torch.int8, device=g.device)
+    amax = torch.empty((), dtype=torch.float32, device=g.device)
+    ws = _workspace(lib.bnn_linear_grad_weight_i8_workspace_bytes(n, k), g.device)
+    _check(lib.bnn_linear_grad_weight_i8(g.data_ptr(), x.data_ptr(), dt, m, n, k, float(scale_a),
+                                         gw.data_ptr(), codes.data_ptr(), amax.data_ptr(),
+                                         ws.data_ptr(), ws.numel(), _stream(g)),
+           "bnn_linear_grad_weight_i8")
+    return gw, codes, amax

@@ -253,6 +253,63 @@ __global__ __launch_bounds__(kThreads) void bwd_scale_a_kernel(const double* par
   if (threadIdx.x == 0) out[0] = red[0] / sqrt(count);
 }
 
+// ---- int8 codes of grad_w: amax = max |v| (NaN if any v is NaN), step = amax / 127, code =
+// clamp(rint(v / step), -127, 127), a NaN quotient coding as 0 (the same symmetric quantizer as
+// the W8A8 conv, its amax taken from the gradient itself).
+constexpr int kAmaxParts = 1024;
+
+__device__ inline float nan_max(float a, float b) { return a != a ? a : (b != b ? b : fmaxf(a, b)); }
+
+__device__ inline float block_nan_max(float v, float* red) {
+  red[threadIdx.x] = v;
+  __syncthreads();
+  for (int h = kThreads / 2; h > 0; h >>= 1) {
+    if ((int)threadIdx.x < h) red[threadIdx.x] = nan_max(red[threadIdx.x], red[threadIdx.x + h]);
+    __syncthreads();
+  }
+  return red[0];
+}
+
+__global__ __launch_bounds__(kThreads) void bwd_amax_kernel(const float4* v, int64_t n4, float* part) {
+  __shared__ float red[kThreads];
+  float m = 0.0f;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n4; i += (int64_t)gridDim.x * kThreads) {
+    const float4 q = v[i];
+    m = nan_max(m, nan_max(nan_max(fabsf(q.x), fabsf(q.y)), nan_max(fabsf(q.z), fabsf(q.w))));
+  }
+  const float b = block_nan_max(m, red);
+  if (threadIdx.x == 0) part[blockIdx.x] = b;
+}
+
+__global__ __launch_bounds__(kThreads) void bwd_amax_final_kernel(const float* part, int n, float* amax) {
+  __shared__ float red[kThreads];
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < n; i += kThreads) m = nan_max(m, part[i]);
+  const float b = block_nan_max(m, red);
+  if (threadIdx.x == 0) amax[0] = b;
+}
+
+__device__ inline int8_t grad_code(float v, float step) {
+  float r = rintf(v / step);
+  r = r != r ? 0.0f : fminf(fmaxf(r, -127.0f), 127.0f);
+  return (int8_t)r;
+}
+
+__global__ __launch_bounds__(kThreads) void bwd_quant_kernel(const float4* v, int64_t n4, const float* amax,
+                                                             char4* codes) {
+  const float step = amax[0] / 127.0f;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n4; i += (int64_t)gridDim.x * kThreads) {
+    const float4 q = v[i];
+    codes[i] = make_char4(grad_code(q.x, step), grad_code(q.y, step), grad_code(q.z, step),
+                          grad_code(q.w, step));
+  }
+}
+
+int amax_parts(int64_t n4) {
+  const int64_t blocks = (n4 + 4 * kThreads - 1) / (4 * kThreads);  // four vectors per thread
+  return (int)(blocks < 1 ? 1 : (blocks > kAmaxParts ? kAmaxParts : blocks));
+}
+
 template <bool AT, bool GI>
 hipError_t launch_bwd(bool bf, const BwdArgs& a, hipStream_t s) {
   const int64_t tiles = (int64_t)((a.I + kBM - 1) / kBM) * ((a.J + kBN - 1) / kBN);
@@ -280,6 +337,22 @@ hipError_t launch_linear_grad_input(const void* g, const void* w, const void* x,
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_scale_a_kernel, dim3(1), dim3(kThreads), 0, s, part,
                      (int)bwd_grad_input_parts(m, k), (double)m * (double)k, grad_scale_a);
+  return hipGetLastError();
+}
+
+int64_t bwd_grad_weight_i8_parts(int64_t n, int64_t k) { return amax_parts(n * k / 4); }
+
+hipError_t launch_quant_grad(const float* grad_w, int64_t count, float* part, float* amax,
+                             int8_t* codes, hipStream_t s) {
+  const int64_t n4 = count / 4;
+  const int parts = amax_parts(n4);
+  hipLaunchKernelGGL(bwd_amax_kernel, dim3(parts), dim3(kThreads), 0, s,
+                     reinterpret_cast<const float4*>(grad_w), n4, part);
+  hipLaunchKernelGGL(bwd_amax_final_kernel, dim3(1), dim3(kThreads), 0, s, part, parts, amax);
+  const int64_t qblocks = (n4 + 4 * kThreads - 1) / (4 * kThreads);
+  hipLaunchKernelGGL(bwd_quant_kernel, dim3((unsigned)(qblocks < 1 ? 1 : (qblocks > 8192 ? 8192 : qblocks))),
+                     dim3(kThreads), 0, s, reinterpret_cast<const float4*>(grad_w), n4, amax,
+                     reinterpret_cast<char4*>(codes));
   return hipGetLastError();
 }
 

@@ -446,4 +446,31 @@ bnn_status bnn_linear_grad_weight(const void* grad_out, const void* x, int dtype
                                                    static_cast<hipStream_t>(stream)));
 }
 
+size_t bnn_linear_grad_weight_i8_workspace_bytes(int64_t n, int64_t k) {
+  if (n <= 0 || k <= 0) return 0;
+  return (size_t)bnn::bwd_grad_weight_i8_parts(n, k) * sizeof(float);
+}
+
+bnn_status bnn_linear_grad_weight_i8(const void* grad_out, const void* x, int dtype, int64_t m,
+                                     int64_t n, int64_t k, float scale_a, float* grad_w,
+                                     int8_t* grad_w_q, float* amax, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  if (!half_dtype(dtype)) return BNN_ERR_DTYPE;
+  if (m < 0 || n < 0 || k < 0 || n % 8 != 0 || k % 8 != 0) return BNN_ERR_SHAPE;
+  if (!int_fits(m * k) || !int_fits(n * k) || !int_fits(m * n)) return BNN_ERR_SHAPE;
+  if (n == 0 || k == 0) return BNN_OK;
+  if (!grad_w || !grad_w_q || !amax || (m > 0 && (!grad_out || !x))) return BNN_ERR_NULL;
+  if (!aligned(grad_w, 16) || !aligned(grad_w_q, 4) || !aligned(amax, 4)) return BNN_ERR_ALIGN;
+  if (m > 0 && (!aligned(grad_out, 16) || !aligned(x, 16))) return BNN_ERR_ALIGN;
+  if (!workspace || workspace_bytes < bnn_linear_grad_weight_i8_workspace_bytes(n, k))
+    return BNN_ERR_WORKSPACE;
+  if (!aligned(workspace, 4)) return BNN_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e =
+      bnn::launch_linear_grad_weight(grad_out, x, dtype == BNN_BF16, m, n, k, scale_a, grad_w, s);
+  if (e != hipSuccess) return BNN_ERR_HIP;
+  return hip_status(bnn::launch_quant_grad(grad_w, n * k, static_cast<float*>(workspace), amax,
+                                           grad_w_q, s));
+}
+
 }  // extern "C"

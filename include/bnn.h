@@ -234,7 +234,7 @@ bnn_status bnn_w8a8_conv2d(const int8_t* x_q, int64_t n, int64_t c, int64_t h, i
  * layer's input) share one dtype, BNN_F16 or BNN_BF16; products are exact and sums fp32 (the
  * scale is applied once to the fp32 sum); grad_in and grad_w are fp32, grad_scale_a double
  * (summed in double). n and k must be multiples of 8; g, W and x 16-byte aligned. The int8
- * quantization of grad_w on the page is not part of these calls.
+ * quantization of grad_w on the page is bnn_linear_grad_weight_i8 below.
  *
  * grad_input: m, k > 0 (the page divides by sqrt(m * k)); grad_in [m][k] and grad_scale_a
  * (one double) are device outputs; workspace: at least
@@ -250,6 +250,21 @@ bnn_status bnn_linear_grad_input(const void* grad_out, const void* weight, const
 bnn_status bnn_linear_grad_weight(const void* grad_out, const void* x, int dtype, int64_t m,
                                   int64_t n, int64_t k, float scale_a, float* grad_w,
                                   void* stream);
+
+/* grad_weight with the page's int8 step (grad_weight = nv_tensor_quant(grad_weight)[0] at the end of
+ * BinaryConv2dForward.backward on the qconv/binary/cutlass/layer page). The quantizer is not on the
+ * pages; it is the per-tensor symmetric one of the W8A8 calls with amax taken from the gradient:
+ * amax = max |grad_w| over the fp32 gradient (NaN if any element is NaN), step = amax / 127 in fp32,
+ * code = clamp(rint(grad_w / step), -127, 127) with ties to even, and a NaN quotient (every gradient
+ * 0, a NaN amax, inf / inf) codes as 0. Outputs (device): grad_w [n][k] fp32 as bnn_linear_grad_weight
+ * (16-byte aligned), grad_w_q [n][k] int8 (4-byte aligned), amax (one float; dequantized gradient =
+ * code * amax / 127). workspace: at least bnn_linear_grad_weight_i8_workspace_bytes(n, k) bytes,
+ * 4-byte aligned, overwritten. Shapes and dtypes as bnn_linear_grad_weight. */
+size_t bnn_linear_grad_weight_i8_workspace_bytes(int64_t n, int64_t k);
+bnn_status bnn_linear_grad_weight_i8(const void* grad_out, const void* x, int dtype, int64_t m,
+                                     int64_t n, int64_t k, float scale_a, float* grad_w,
+                                     int8_t* grad_w_q, float* amax, void* workspace,
+                                     size_t workspace_bytes, void* stream);
 
 /* Workspace sizes (bytes) for the calls above; 0 when x is already packed. */
 size_t bnn_gemm_workspace_bytes(int64_t m, int64_t k, int x_dtype);

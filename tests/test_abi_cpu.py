@@ -300,3 +300,23 @@ def test_backward_argument_checks(bnn):
     assert gw(out=None) == bnn.ERR_NULL and gw(x=None) == bnn.ERR_NULL
     assert gw(g=FAKE + 2) == bnn.ERR_ALIGN and gw(out=FAKE + 1) == bnn.ERR_ALIGN
     assert gw(n=0, g=None, x=None, out=None) == bnn.OK and gw(k=0, out=None) == bnn.OK
+
+
+def test_backward_i8_argument_checks(bnn):
+    L = bnn.lib
+
+    def gq(**kw):
+        a = dict(g=FAKE, x=FAKE, dt=bnn.BF16, m=64, n=64, k=128, sa=1.0, out=FAKE, q=FAKE, amax=FAKE,
+                 ws=FAKE, wsb=1 << 20)
+        a.update(kw)
+        return L.bnn_linear_grad_weight_i8(a["g"], a["x"], a["dt"], a["m"], a["n"], a["k"], a["sa"], a["out"],
+                                           a["q"], a["amax"], a["ws"], a["wsb"], None)
+    assert L.bnn_linear_grad_weight_i8_workspace_bytes(64, 128) == 2 * 4      # 2048 vectors, 1024 a part
+    assert L.bnn_linear_grad_weight_i8_workspace_bytes(8192, 8192) == 1024 * 4
+    assert L.bnn_linear_grad_weight_i8_workspace_bytes(0, 128) == 0
+    assert gq(dt=bnn.F32) == bnn.ERR_DTYPE
+    assert gq(n=12) == bnn.ERR_SHAPE and gq(k=4) == bnn.ERR_SHAPE
+    assert gq(q=None) == bnn.ERR_NULL and gq(amax=None) == bnn.ERR_NULL and gq(out=None) == bnn.ERR_NULL
+    assert gq(out=FAKE + 4) == bnn.ERR_ALIGN and gq(q=FAKE + 2) == bnn.ERR_ALIGN and gq(amax=FAKE + 2) == bnn.ERR_ALIGN
+    assert gq(ws=None) == bnn.ERR_WORKSPACE and gq(wsb=3) == bnn.ERR_WORKSPACE
+    assert gq(n=0, g=None, x=None, out=None, q=None, amax=None) == bnn.OK

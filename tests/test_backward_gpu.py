@@ -156,3 +156,55 @@ def test_errors(bnn):
         bnn.linear_grad_input(g, w, x, 1.0, 1.0)            # n = 12 is not a multiple of 8
     with pytest.raises(TypeError):
         bnn.linear_grad_weight(g.float(), x.float(), 1.0)  # fp32 operands are not taken
+
+
+@pytest.mark.parametrize("dt", HALF)
+@pytest.mark.parametrize("shape", [(1, 8, 8), (300, 200, 392), (129, 520, 264), (0, 64, 128), (700, 96, 1000)])
+def test_grad_weight_codes(bnn, orc, dt, shape):
+    """int8 codes of grad_weight bit-exact against the oracle (dyadic gradients: the fp32 gradient
+    is exact, so amax and every rounding decision are the same on both sides); m = 0 gives a zero
+    gradient, amax 0 and zero codes."""
+    m, n, k = shape
+    print(f"codes {dt} {shape}", flush=True)
+    g, _, x = _inputs(3 * m + n + k, m, n, k, dt, dyadic=True)
+    gw, codes, amax = bnn.linear_grad_weight_i8(g.to(DEV), x.to(DEV), 0.5)
+    torch.cuda.synchronize()
+    ref = orc.linear_grad_weight(g, x, 0.5)
+    want, want_amax = orc.quant_grad_i8(ref)
+    assert torch.equal(gw.cpu().double(), ref)
+    assert float(amax.cpu()) == want_amax
+    assert torch.equal(codes.cpu(), want)
+    if m == 0:
+        assert want_amax == 0.0 and not bool(want.any())
+
+
+def test_grad_weight_codes_nan(bnn, orc):
+    g, _, x = _inputs(5, 64, 32, 40, torch.bfloat16, dyadic=True)
+    x[3, 9] = float("nan")
+    gw, codes, amax = bnn.linear_grad_weight_i8(g.to(DEV), x.to(DEV), 0.5)
+    torch.cuda.synchronize()
+    want, want_amax = orc.quant_grad_i8(orc.linear_grad_weight(g, x, 0.5))
+    assert math.isnan(float(amax.cpu())) and math.isnan(want_amax)
+    assert torch.equal(codes.cpu(), want) and not bool(want.any())
+
+
+def test_grad_weight_codes_full_size(bnn, orc):
+    """The 16384 x 8192 x 8192 layer: amax is the max of the kernel's own fp32 gradient, sampled
+    gradient rows equal the oracle's (dyadic gradients), and the codes of those rows equal the
+    oracle quantizer's with that amax; every code is the quantizer of its fp32 value."""
+    m, n, k = 16384, 8192, 8192
+    print(f"codes full {(m, n, k)}", flush=True)
+    gen = torch.Generator(device=DEV).manual_seed(12)
+    g = (torch.randint(-16, 17, (m, n), generator=gen, device=DEV).float() / 8).to(torch.bfloat16)
+    x = (0.8 * torch.randn((m, k), generator=gen, device=DEV)).to(torch.bfloat16)
+    gw, codes, amax = bnn.linear_grad_weight_i8(g, x, 0.5)
+    torch.cuda.synchronize()
+    a = float(amax.cpu())
+    assert a == float(gw.abs().max().cpu())
+    cols = torch.tensor([0, 77, n - 1])
+    ref = orc.linear_grad_weight(g[:, cols.to(DEV)].contiguous().cpu(), x.cpu(), 0.5)
+    assert torch.equal(gw[cols.to(DEV)].cpu().double(), ref)
+    assert torch.equal(codes[cols.to(DEV)].cpu(), orc.quant_i8(ref.float(), a))
+    gwc = gw.cpu()
+    step = torch.tensor(a, dtype=torch.float32) / 127.0
+    assert torch.equal(codes.cpu(), torch.round(gwc / step).clamp(-127, 127).to(torch.int8))
