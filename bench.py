@@ -324,9 +324,17 @@ def main():
                                                    ws.data_ptr(), ws.numel(), cur_stream())
         core = lambda i: lib.bnn_linear_grad_weight(gd.data_ptr(), xd.data_ptr(), xcode, m, n, k, sa,
                                                     gw.data_ptr(), cur_stream())
+        # the page's backward ends with the int8 codes of grad_weight: the step runs the
+        # contraction + amax + coder call; the contraction alone is timed for the roofline
+        gq = torch.empty((n, k), dtype=torch.int8, device=dev)
+        gamax = torch.empty((), dtype=torch.float32, device=dev)
+        qws = torch.empty(lib.bnn_linear_grad_weight_i8_workspace_bytes(n, k), dtype=torch.uint8, device=dev)
+        core_q = lambda i: lib.bnn_linear_grad_weight_i8(gd.data_ptr(), xd.data_ptr(), xcode, m, n, k, sa,
+                                                         gw.data_ptr(), gq.data_ptr(), gamax.data_ptr(),
+                                                         qws.data_ptr(), qws.numel(), cur_stream())
         path_used = None
-        kernels = {"pack": [pack], "core": [core]}
-        step_fns = [pack, core]
+        kernels = {"pack": [pack], "core": [core], "core_q": [core_q]}
+        step_fns = [pack, core_q]
     elif w8a8:
         # step: activation codes (NCHW -> NHWC int8), then the int8 conv; weight codes are made
         # once ahead, as the layer's weights are
@@ -392,6 +400,16 @@ def main():
         gotw = gw[cols].cpu().double()
         boundw = ((m + 1) * sa * gcpu[:, cols].double().abs().sum(0).unsqueeze(1) + refw.abs()) * 2.0 ** -24
         parity = ok_in and bool(((gotw - refw).abs() <= boundw).all())
+        if core_q(0) != 0:
+            raise RuntimeError("libbnn call failed")
+        torch.cuda.synchronize()
+        # codes (a property of the kernel's own outputs at any size): amax is the max of the fp32
+        # gradient and each sampled code is the half-even rounding of gradient / (amax / 127), clamped
+        amax_v = float(gamax.cpu())
+        step = torch.tensor(amax_v, dtype=torch.float32) / 127.0
+        want_q = torch.round(gw[cols].cpu() / step).clamp(-127, 127).to(torch.int8)
+        parity = parity and amax_v == float(gw.abs().max().cpu())
+        parity = parity and bool(torch.equal(gq[cols].cpu(), want_q))
         log(f"parity spot check vs oracle (within the fp32 summation bound): {parity}")
     elif w8a8:
         import oracle
@@ -483,7 +501,8 @@ def main():
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": traffic_for(kind, args.workload),
                 "kernel": f"{KERNEL_NAMES[kind]} ({name})", "kernel_ms": round(dom_ms, 5),
-                "grad_input_ms": round(kern_ms["pack"], 5), "grad_weight_ms": round(kern_ms["core"], 5)}
+                "grad_input_ms": round(kern_ms["pack"], 5), "grad_weight_ms": round(kern_ms["core"], 5),
+                "grad_weight_int8_codes_ms": round(kern_ms["core_q"] - kern_ms["core"], 5)}
         value = ops / (ms_per_step * 1e-3) / 1e12
         metric, unit = "backward TFLOP/s (2 contractions of 2*M*N*K)", "TFLOP/s"
         dtype = wl.x_dtype
@@ -511,7 +530,7 @@ def main():
     }
     if bwd:
         result["config"].update({"m": m, "n": n, "k": k, "dtype": wl.x_dtype,
-                                 "outputs": "grad_input fp32 [m, k], grad_scale_a f64, grad_weight fp32 [n, k]"})
+                                 "outputs": "grad_input fp32 [m, k], grad_scale_a f64, grad_weight fp32 [n, k] and its int8 codes + amax"})
         result["parity_spot_check"] = parity
     elif not pack_only:
         m, n, k = wl.gemm_mnk()
