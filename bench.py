@@ -73,7 +73,11 @@ CODEC_KINDS = ("pack", "pack_shift", "pack_nchw", "abs_mean")
 
 def kernel_kind(name):
     """Kind of a demangled kernel name from a rocprofv3 counter file (None: not ours)."""
-    for kind in CODEC_KINDS + ("xor", "w8a8", "bwd"):
+    if "bwd_gemm_kernel<" in name:
+        # template arguments <bf16, A transposed, grad_input epilogue>: the roofline line of the
+        # backward is the grad_input contraction
+        return "bwd" if re.search(r"bwd_gemm_kernel<\w+, false, true>", name) else None
+    for kind in CODEC_KINDS + ("xor", "w8a8"):
         if KERNEL_NAMES[kind] + "<" in name or KERNEL_NAMES[kind] + "(" in name:
             return kind
     if "mfma_kernel<" in name:
@@ -501,6 +505,7 @@ def main():
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": traffic_for(kind, args.workload),
                 "kernel": f"{KERNEL_NAMES[kind]} ({name})", "kernel_ms": round(dom_ms, 5),
+                "traffic_kernel": "grad_input",
                 "grad_input_ms": round(kern_ms["pack"], 5), "grad_weight_ms": round(kern_ms["core"], 5),
                 "grad_weight_int8_codes_ms": round(kern_ms["core_q"] - kern_ms["core"], 5)}
         value = ops / (ms_per_step * 1e-3) / 1e12
