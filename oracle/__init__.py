@@ -72,6 +72,8 @@ def _bind(lib):
                                              ctypes.c_float, P, P]
     lib.oracle_linear_grad_weight.argtypes = [P, I, P, I, I64, I64, I64, ctypes.c_float, P]
     lib.oracle_quant_grad_i8.argtypes = [P, I64, P, P]
+    lib.oracle_conv2d_grad.argtypes = [P, I, P, I, P, I] + [I64] * 13 + [ctypes.c_float, ctypes.c_float,
+                                                                        P, P, P]
     lib.oracle_abs_mean_scale.restype = ctypes.c_double
     return lib
 
@@ -343,3 +345,25 @@ def quant_grad_i8(grad_w: torch.Tensor):
     amax = ctypes.c_float(0.0)
     _load().oracle_quant_grad_i8(gw.data_ptr(), gw.numel(), codes.data_ptr(), ctypes.addressof(amax))
     return codes, amax.value
+
+
+def conv2d_grad(g: torch.Tensor, w: torch.Tensor, x: torch.Tensor, stride, padding, dilation,
+                scale_a: float, scale_w: float):
+    """Straight-through backward of the binarized conv: returns (grad_in float64 [B, C, H, W],
+    grad_scale_a float, grad_w float64 [O, C, KH, KW]) for g [B, O, Ho, Wo], W [O, C, KH, KW],
+    x [B, C, H, W]; stride / padding / dilation are ints or (rows, columns) pairs."""
+    g, w, x = _cpu(g), _cpu(w), _cpu(x)
+    b, c, h, wd = x.shape
+    o, c2, kh, kw = w.shape
+    assert c == c2 and g.shape[0] == b and g.shape[1] == o
+    (sh, sw), (ph, pw), (dh, dw) = _pair(stride), _pair(padding), _pair(dilation)
+    assert tuple(g.shape[2:]) == (conv_out_size(h, kh, sh, ph, dh), conv_out_size(wd, kw, sw, pw, dw))
+    gi = torch.empty((b, c, h, wd), dtype=torch.float64)
+    gw = torch.empty((o, c, kh, kw), dtype=torch.float64)
+    gsa = ctypes.c_double(0.0)
+    rc = _load().oracle_conv2d_grad(g.data_ptr(), _code(g), w.data_ptr(), _code(w), x.data_ptr(), _code(x),
+                                    b, c, h, wd, o, kh, kw, sh, sw, ph, pw, dh, dw, float(scale_a),
+                                    float(scale_w), gi.data_ptr(), ctypes.addressof(gsa), gw.data_ptr())
+    if rc != 0:
+        raise RuntimeError("oracle_conv2d_grad failed")
+    return gi, gsa.value, gw

@@ -571,3 +571,54 @@ void oracle_quant_grad_i8(const double *grad_w, int64_t count, int8_t *codes, fl
     codes[i] = (int8_t)r;
   }
 }
+
+/* Straight-through backward of the binarized conv, BinaryConv2dForward.backward on the
+ * qconv/binary/cutlass/layer page, with a KH x KW kernel and a stride, padding and dilation per
+ * axis (the forward's general form). Output gradient g [B][O][Ho][Wo], weight W [O][C][KH][KW],
+ * input x [B][C][H][W]; a tap (oh, ow, i, j) reads input row oh*sh - ph + i*dh and column
+ * ow*sw - pw + j*dw, and taps in the padding carry nothing (the page's gradient convolutions take
+ * the same padding as the forward):
+ *   grad_in[b][c][ih][iw] = (scale_w * sum of g[b][o][oh][ow] * sign0(W[o][c][i][j]) over the
+ *                            taps that read (ih, iw)) * mid(x[b][c][ih][iw])
+ *   grad_scale_a          = sum of grad_in * sign0(x) over every element / sqrt(B*C*H*W)
+ *   grad_w[o][c][i][j]    = sum over b, oh, ow of g[b][o][oh][ow] * (sign0(x at the tap) * scale_a)
+ * (torch.nn.grad.conv2d_input and conv2d_weight on the page), with sign0 and mid as for the
+ * linear layer. Sums in double. Returns 0, or -1 for an empty output or a bad geometry. */
+int oracle_conv2d_grad(const void *g, int gdt, const void *w, int wdt, const void *x, int xdt,
+                       int64_t B, int64_t C, int64_t H, int64_t W, int64_t O, int64_t KH, int64_t KW,
+                       int64_t sh, int64_t sw, int64_t ph, int64_t pw, int64_t dh, int64_t dw,
+                       float scale_a, float scale_w, double *grad_in, double *grad_scale_a,
+                       double *grad_w) {
+  int64_t Ho = oracle_conv_out_size(H, KH, sh, ph, dh);
+  int64_t Wo = oracle_conv_out_size(W, KW, sw, pw, dw);
+  if (Ho <= 0 || Wo <= 0 || sh < 1 || sw < 1 || dh < 1 || dw < 1 || ph < 0 || pw < 0 || KH < 1 ||
+      KW < 1 || B < 1 || C < 1)
+    return -1;
+  for (int64_t i = 0; i < B * C * H * W; i++) grad_in[i] = 0.0;
+  for (int64_t i = 0; i < O * C * KH * KW; i++) grad_w[i] = 0.0;
+  /* one input channel per thread: it owns grad_in[:, c] and grad_w[:, c] */
+#pragma omp parallel for schedule(static)
+  for (int64_t c = 0; c < C; c++)
+    for (int64_t b = 0; b < B; b++)
+      for (int64_t o = 0; o < O; o++)
+        for (int64_t oh = 0; oh < Ho; oh++)
+          for (int64_t ow = 0; ow < Wo; ow++) {
+            double gv = (double)widen(g, gdt, ((b * O + o) * Ho + oh) * Wo + ow);
+            for (int64_t i = 0; i < KH; i++)
+              for (int64_t j = 0; j < KW; j++) {
+                int64_t ih = oh * sh - ph + i * dh, iw = ow * sw - pw + j * dw;
+                if (ih < 0 || ih >= H || iw < 0 || iw >= W) continue;
+                int64_t xi = ((b * C + c) * H + ih) * W + iw, wi = ((o * C + c) * KH + i) * KW + j;
+                grad_in[xi] += gv * (sign0(widen(w, wdt, wi)) * (double)scale_w);
+                grad_w[wi] += gv * (sign0(widen(x, xdt, xi)) * (double)scale_a);
+              }
+          }
+  double total = 0.0;
+  for (int64_t i = 0; i < B * C * H * W; i++) {
+    float v = widen(x, xdt, i);
+    grad_in[i] *= clip_mid(v, scale_a);
+    total += grad_in[i] * sign0(v);
+  }
+  *grad_scale_a = total / sqrt((double)(B * C * H * W));
+  return 0;
+}

@@ -140,7 +140,87 @@ def pin_quant_grad(orc):
     return math.isnan(na) and not bool(nc.any())
 
 
+def _conv_cases(seed, count):
+    import random
+    rnd = random.Random(seed)
+    out = []
+    while len(out) < count:
+        b, c, h, w = rnd.choice([1, 2]), rnd.choice([1, 3, 5]), rnd.randint(2, 7), rnd.randint(2, 7)
+        o, kh, kw = rnd.choice([1, 2, 4]), rnd.choice([1, 2, 3]), rnd.choice([1, 2, 3])
+        s, p, d = (rnd.choice([1, 2]), rnd.choice([1, 3])), (rnd.randint(0, 2), rnd.randint(0, 1)), \
+            (rnd.choice([1, 2]), rnd.choice([1, 2]))
+        ho = (h + 2 * p[0] - d[0] * (kh - 1) - 1) // s[0] + 1
+        wo = (w + 2 * p[1] - d[1] * (kw - 1) - 1) // s[1] + 1
+        if ho > 0 and wo > 0:
+            out.append(((b, c, h, w), (o, kh, kw), s, p, d, (ho, wo)))
+    return out
+
+
+def pin_conv_vs_torch_grad(orc):
+    """The conv page's backward with torch's gradient routines (float64), over random
+    geometries with non-square kernels and per-axis stride / padding / dilation."""
+    gen = torch.Generator().manual_seed(21)
+    sa, sw = 0.7, 0.3
+    sa32, sw32 = float(np.float32(sa)), float(np.float32(sw))
+    for (b, c, h, w), (o, kh, kw), s, p, d, (ho, wo) in _conv_cases(21, 12):
+        x = torch.randn((b, c, h, w), generator=gen)
+        wt = torch.randn((o, c, kh, kw), generator=gen)
+        g = torch.randn((b, o, ho, wo), generator=gen)
+        gi, gsa, gw = orc.conv2d_grad(g, wt, x, s, p, d, sa, sw)
+        ref = torch.nn.grad.conv2d_input((b, c, h, w), sign0(wt) * sw32, g.double(), stride=s,
+                                         padding=p, dilation=d)
+        ref = ref * mid_fp32(x, sa)
+        if not torch.allclose(gi, ref, rtol=1e-12, atol=1e-12):
+            return False
+        want = float((ref * sign0(x)).sum() / math.sqrt(x.numel()))
+        if not math.isclose(gsa, want, rel_tol=1e-12, abs_tol=1e-12):
+            return False
+        refw = torch.nn.grad.conv2d_weight(sign0(x) * sa32, (o, c, kh, kw), g.double(), stride=s,
+                                           padding=p, dilation=d)
+        if not torch.allclose(gw, refw, rtol=1e-12, atol=1e-12):
+            return False
+    return True
+
+
+def pin_conv_autograd(orc):
+    """grad_in is d/dx of sum(g * conv(sa * hardtanh(x / sa), sign(W) * sw)); grad_w is d/dW of
+    sum(g * conv(sign(x) * sa, W))."""
+    gen = torch.Generator().manual_seed(22)
+    sa, sw = 0.75, 0.5
+    for (b, c, h, w), (o, kh, kw), s, p, d, (ho, wo) in _conv_cases(22, 6):
+        x = torch.randn((b, c, h, w), generator=gen)
+        wt = torch.randn((o, c, kh, kw), generator=gen)
+        g = torch.randn((b, o, ho, wo), generator=gen)
+        gi, _, gw = orc.conv2d_grad(g, wt, x, s, p, d, sa, sw)
+        xd = x.double().requires_grad_(True)
+        y = torch.nn.functional.conv2d(sa * torch.nn.functional.hardtanh(xd / sa), sign0(wt) * sw,
+                                       stride=s, padding=p, dilation=d)
+        (y * g.double()).sum().backward()
+        if not torch.allclose(gi, xd.grad, rtol=1e-12, atol=1e-12):
+            return False
+        wd = wt.double().requires_grad_(True)
+        y = torch.nn.functional.conv2d(sign0(x) * sa, wd, stride=s, padding=p, dilation=d)
+        (y * g.double()).sum().backward()
+        if not torch.allclose(gw, wd.grad, rtol=1e-12, atol=1e-12):
+            return False
+    return True
+
+
+def pin_conv_as_linear(orc):
+    """A 1x1 kernel on 1x1 images is the linear layer: the conv form equals the linear form
+    (two separate code paths of the oracle)."""
+    g, w, x = _data(23, 7, 5, 9)
+    gi, gsa, gw = orc.conv2d_grad(g.view(7, 5, 1, 1), w.view(5, 9, 1, 1), x.view(7, 9, 1, 1), 1, 0, 1,
+                                  0.6, 0.4)
+    li, lsa = orc.linear_grad_input(g, w, x, 0.6, 0.4)
+    lw = orc.linear_grad_weight(g, x, 0.6)
+    return torch.equal(gi.view(7, 9), li) and gsa == lsa and torch.equal(gw.view(5, 9), lw)
+
+
 PINS = {
+    "bwd_conv_vs_torch_grad": pin_conv_vs_torch_grad,
+    "bwd_conv_autograd": pin_conv_autograd,
+    "bwd_conv_as_linear": pin_conv_as_linear,
     "bwd_quant_grad": pin_quant_grad,
     "bwd_vs_torch_grad": pin_vs_torch_grad,
     "bwd_autograd": pin_autograd,

@@ -61,7 +61,7 @@ MUTANTS = {
     "abs_mean_count_minus_one": ("return factor * (sum / (double)count);",
                                  "return factor * (sum / (double)(count - 1));"),
     "quant_truncates": ("float r = rintf(v / step);", "float r = truncf(v / step);"),
-    "quant_clamp_128": ("if (r < -127.0f) r = -127.0f;", "if (r < -128.0f) r = -128.0f;"),
+    "quant_clamp_128": ("  if (r < -127.0f) r = -127.0f;\n  return (int8_t)r;", "  if (r < -128.0f) r = -128.0f;\n  return (int8_t)r;"),
     "w8a8_step_255": ("static float q_step(float amax) { return amax / 127.0f; }",
                       "static float q_step(float amax) { return amax / 255.0f; }"),
     "abs_mean_fixed_factor": ("return factor * (sum / (double)count);", "return 2.0 * (sum / (double)count);"),
@@ -78,6 +78,13 @@ MUTANTS = {
     "bwd_quant_step_by_255": ("  float step = amax / 127.0f;\n  for (int64_t i = 0; i < count; i++) {\n    float r = rintf((float)grad_w[i] / step);",
                               "  float step = amax / 255.0f;\n  for (int64_t i = 0; i < count; i++) {\n    float r = rintf((float)grad_w[i] / step);"),
     "bwd_quant_amax_signed": ("    float v = fabsf((float)grad_w[i]);", "    float v = (float)grad_w[i];"),
+    "bwd_conv_tap_without_dilation": ("int64_t ih = oh * sh - ph + i * dh, iw = ow * sw - pw + j * dw;\n                if (ih < 0 || ih >= H || iw < 0 || iw >= W) continue;\n                int64_t xi",
+                                      "int64_t ih = oh * sh - ph + i, iw = ow * sw - pw + j * dw;\n                if (ih < 0 || ih >= H || iw < 0 || iw >= W) continue;\n                int64_t xi"),
+    "bwd_conv_pad_added": ("int64_t ih = oh * sh - ph + i * dh, iw = ow * sw - pw + j * dw;\n                if (ih < 0 || ih >= H || iw < 0 || iw >= W) continue;\n                int64_t xi",
+                           "int64_t ih = oh * sh + ph + i * dh, iw = ow * sw - pw + j * dw;\n                if (ih < 0 || ih >= H || iw < 0 || iw >= W) continue;\n                int64_t xi"),
+    "bwd_conv_kernel_transposed": ("wi = ((o * C + c) * KH + i) * KW + j;", "wi = ((o * C + c) * KW + j) * KH + i;"),
+    "bwd_conv_weight_grad_unsigned": ("grad_w[wi] += gv * (sign0(widen(x, xdt, xi)) * (double)scale_a);",
+                                      "grad_w[wi] += gv * ((double)widen(x, xdt, xi) * (double)scale_a);"),
 }
 
 
