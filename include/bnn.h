@@ -1,6 +1,7 @@
 /*
  * bnn.h: C ABI of libbnn, the MI355X (gfx950) forward pass of binarized
- * linear and conv2d layers.
+ * linear and conv2d layers, the W8A8 int8 conv, and the straight-through
+ * backward of the binarized linear layer.
  *
  * The layers are those of bitorch-engine's binary layer pages:
  *   - BinaryLinearForward.forward(input, weight, bmm_type, scale_a, scale_w, is_train)
