@@ -39,7 +39,8 @@ EXPORTS = ("bnn_pack_sign", "bnn_pack_sign_nchw", "bnn_pack_sign_shift", "bnn_pa
            "bnn_gemm_workspace_bytes", "bnn_conv2d_workspace_bytes", "bnn_gemm_auto_path",
            "bnn_conv2d_auto_path", "bnn_last_path", "bnn_status_string",
            "bnn_linear_grad_input", "bnn_linear_grad_input_workspace_bytes", "bnn_linear_grad_weight",
-           "bnn_linear_grad_weight_i8", "bnn_linear_grad_weight_i8_workspace_bytes")
+           "bnn_linear_grad_weight_i8", "bnn_linear_grad_weight_i8_workspace_bytes",
+           "bnn_quant_grad_i8", "bnn_quant_grad_i8_workspace_bytes")
 
 _PATHS = {"auto": PATH_AUTO, "xor": PATH_XOR, "mfma": PATH_MFMA, "mfma_fp4": PATH_MFMA_FP4}
 _DT = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16, torch.int32: I32}
@@ -62,6 +63,8 @@ def _bind(path: str) -> ctypes.CDLL:
         "bnn_linear_grad_weight": ([P, P, I, I64, I64, I64, F, P, P], I),
         "bnn_linear_grad_weight_i8": ([P, P, I, I64, I64, I64, F, P, P, P, P, SZ, P], I),
         "bnn_linear_grad_weight_i8_workspace_bytes": ([I64, I64], SZ),
+        "bnn_quant_grad_i8": ([P, I64, P, P, P, SZ, P], I),
+        "bnn_quant_grad_i8_workspace_bytes": ([I64], SZ),
         "bnn_w_pack": ([P, I, I64, I64, I, P, P], I),
         "bnn_w_pack_conv": ([P, I, I64, I64, I, I, P, P], I),
         "bnn_quant_i8_nhwc": ([P, I, I64, I64, I64, I64, D, P, P], I),
@@ -480,3 +483,17 @@ def linear_grad_weight_i8(grad_out: torch.Tensor, x: torch.Tensor, scale_a: floa
                                          ws.data_ptr(), ws.numel(), _stream(g)),
            "bnn_linear_grad_weight_i8")
     return gw, codes, amax
+
+
+def quant_grad_i8(grad: torch.Tensor):
+    """int8 codes of an fp32 gradient (per-tensor symmetric, amax = max|grad|): returns (codes int8,
+    same shape; amax 0-dim float32) on the device; numel must be a multiple of 4."""
+    g = _dev(grad, "grad")
+    if g.dtype != torch.float32:
+        raise TypeError(f"grad must be float32, got {g.dtype}")
+    codes = torch.empty(g.shape, dtype=torch.int8, device=g.device)
+    amax = torch.empty((), dtype=torch.float32, device=g.device)
+    ws = _workspace(lib.bnn_quant_grad_i8_workspace_bytes(g.numel()), g.device)
+    _check(lib.bnn_quant_grad_i8(g.data_ptr(), g.numel(), codes.data_ptr(), amax.data_ptr(), ws.data_ptr(),
+                                 ws.numel(), _stream(g)), "bnn_quant_grad_i8")
+    return codes, amax

@@ -342,6 +342,8 @@ hipError_t launch_linear_grad_input(const void* g, const void* w, const void* x,
 
 int64_t bwd_grad_weight_i8_parts(int64_t n, int64_t k) { return amax_parts(n * k / 4); }
 
+int64_t bwd_quant_grad_parts(int64_t count) { return amax_parts(count / 4); }
+
 hipError_t launch_quant_grad(const float* grad_w, int64_t count, float* part, float* amax,
                              int8_t* codes, hipStream_t s) {
   const int64_t n4 = count / 4;

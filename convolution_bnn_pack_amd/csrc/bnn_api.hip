@@ -473,4 +473,22 @@ bnn_status bnn_linear_grad_weight_i8(const void* grad_out, const void* x, int dt
                                            grad_w_q, s));
 }
 
+size_t bnn_quant_grad_i8_workspace_bytes(int64_t count) {
+  if (count <= 0) return 0;
+  return (size_t)bnn::bwd_quant_grad_parts(count) * sizeof(float);
+}
+
+bnn_status bnn_quant_grad_i8(const float* grad, int64_t count, int8_t* codes, float* amax,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  if (count < 0 || count % 4 != 0) return BNN_ERR_SHAPE;
+  if (count == 0) return BNN_OK;
+  if (!grad || !codes || !amax) return BNN_ERR_NULL;
+  if (!aligned(grad, 16) || !aligned(codes, 4) || !aligned(amax, 4)) return BNN_ERR_ALIGN;
+  if (!workspace || workspace_bytes < bnn_quant_grad_i8_workspace_bytes(count))
+    return BNN_ERR_WORKSPACE;
+  if (!aligned(workspace, 4)) return BNN_ERR_ALIGN;
+  return hip_status(bnn::launch_quant_grad(grad, count, static_cast<float*>(workspace), amax,
+                                           codes, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

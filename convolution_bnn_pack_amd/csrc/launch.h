@@ -76,6 +76,7 @@ hipError_t launch_linear_grad_input(const void* g, const void* w, const void* x,
 // int8 codes of an fp32 gradient (count a multiple of 4, 16-byte aligned), amax to one device
 // float, through bwd_grad_weight_i8_parts(n, k) floats of part.
 int64_t bwd_grad_weight_i8_parts(int64_t n, int64_t k);
+int64_t bwd_quant_grad_parts(int64_t count);
 hipError_t launch_quant_grad(const float* grad_w, int64_t count, float* part, float* amax,
                              int8_t* codes, hipStream_t s);
 // grad_w [n][k] fp32.

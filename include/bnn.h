@@ -267,6 +267,15 @@ bnn_status bnn_linear_grad_weight_i8(const void* grad_out, const void* x, int dt
                                      int8_t* grad_w_q, float* amax, void* workspace,
                                      size_t workspace_bytes, void* stream);
 
+/* The int8 coder of bnn_linear_grad_weight_i8 on its own, for a gradient that was reduced
+ * elsewhere first (e.g. summed over data-parallel ranks, whose amax is that of the sum): grad is
+ * count fp32 values (count a multiple of 4, 16-byte aligned), codes count int8 (4-byte aligned),
+ * amax one float, all device memory; workspace at least bnn_quant_grad_i8_workspace_bytes(count)
+ * bytes, 4-byte aligned, overwritten. Same quantizer as bnn_linear_grad_weight_i8. */
+size_t bnn_quant_grad_i8_workspace_bytes(int64_t count);
+bnn_status bnn_quant_grad_i8(const float* grad, int64_t count, int8_t* codes, float* amax,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace sizes (bytes) for the calls above; 0 when x is already packed. */
 size_t bnn_gemm_workspace_bytes(int64_t m, int64_t k, int x_dtype);
 size_t bnn_conv2d_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w, int x_dtype);

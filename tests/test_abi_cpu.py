@@ -320,3 +320,14 @@ def test_backward_i8_argument_checks(bnn):
     assert gq(out=FAKE + 4) == bnn.ERR_ALIGN and gq(q=FAKE + 2) == bnn.ERR_ALIGN and gq(amax=FAKE + 2) == bnn.ERR_ALIGN
     assert gq(ws=None) == bnn.ERR_WORKSPACE and gq(wsb=3) == bnn.ERR_WORKSPACE
     assert gq(n=0, g=None, x=None, out=None, q=None, amax=None) == bnn.OK
+
+
+def test_quant_grad_argument_checks(bnn):
+    L = bnn.lib
+    assert L.bnn_quant_grad_i8_workspace_bytes(0) == 0 and L.bnn_quant_grad_i8_workspace_bytes(4) == 4
+    assert L.bnn_quant_grad_i8(FAKE, 6, FAKE, FAKE, FAKE, 1 << 20, None) == bnn.ERR_SHAPE
+    assert L.bnn_quant_grad_i8(FAKE, -4, FAKE, FAKE, FAKE, 1 << 20, None) == bnn.ERR_SHAPE
+    assert L.bnn_quant_grad_i8(None, 0, None, None, None, 0, None) == bnn.OK
+    assert L.bnn_quant_grad_i8(None, 8, FAKE, FAKE, FAKE, 1 << 20, None) == bnn.ERR_NULL
+    assert L.bnn_quant_grad_i8(FAKE + 4, 8, FAKE, FAKE, FAKE, 1 << 20, None) == bnn.ERR_ALIGN
+    assert L.bnn_quant_grad_i8(FAKE, 8, FAKE, FAKE, None, 0, None) == bnn.ERR_WORKSPACE

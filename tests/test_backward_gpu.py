@@ -208,3 +208,18 @@ def test_grad_weight_codes_full_size(bnn, orc):
     gwc = gw.cpu()
     step = torch.tensor(a, dtype=torch.float32) / 127.0
     assert torch.equal(codes.cpu(), torch.round(gwc / step).clamp(-127, 127).to(torch.int8))
+
+
+@pytest.mark.parametrize("count", [4, 1000, 4096 * 1024 + 4])
+def test_quant_grad_alone(bnn, orc, count):
+    """The stand-alone coder on seeded fp32 gradients (with zeros) equals the oracle quantizer,
+    codes and amax."""
+    print(f"quant alone {count}", flush=True)
+    gen = torch.Generator().manual_seed(count)
+    v = 3 * torch.randn(count, generator=gen)
+    v[::97] = 0.0
+    codes, amax = bnn.quant_grad_i8(v.to(DEV))
+    torch.cuda.synchronize()
+    want, want_amax = orc.quant_grad_i8(v.double())
+    assert float(amax.cpu()) == want_amax
+    assert torch.equal(codes.cpu(), want)
