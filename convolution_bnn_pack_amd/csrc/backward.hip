@@ -65,6 +65,25 @@ __device__ inline float widen16(uint16_t v) {
   return (float)__ushort_as_half(v);
 }
 
+// 16-byte load from global memory. The pointers arrive inside a by-value argument struct, where
+// the compiler no longer knows they are global and would issue flat loads, which it then waits on
+// one by one; an explicit global pointer gives global loads that stay in flight.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ inline uint4 ldg16(const uint16_t* p) {
+  const u32x4 v = *reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(
+      reinterpret_cast<uintptr_t>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ inline uint16_t ldg2(const uint16_t* p) {
+  return *reinterpret_cast<const __attribute__((address_space(1))) uint16_t*>(
+      reinterpret_cast<uintptr_t>(p));
+}
+
+__device__ inline void stg4(float* p, float v) {
+  *reinterpret_cast<__attribute__((address_space(1))) float*>(reinterpret_cast<uintptr_t>(p)) = v;
+}
+
 __device__ inline uint16_t u16_of(const uint4& v, int e) {
   const uint32_t w = e < 2 ? (e == 0 ? v.x : v.x >> 16) : e < 4 ? (e == 2 ? v.y : v.y >> 16)
                    : e < 6 ? (e == 4 ? v.z : v.z >> 16) : (e == 6 ? v.w : v.w >> 16);
@@ -119,8 +138,7 @@ void bwd_gemm_kernel(BwdArgs p) {
 #pragma unroll
       for (int u = 0; u < kNA; u++) {
         const int c = tid + u * kThreads, row = c / kRowChunks, r = r0 + (c % kRowChunks) * 8;
-        ra[u] = (i0 + row < p.I && r < p.R)
-                    ? *reinterpret_cast<const uint4*>(p.a + (int64_t)(i0 + row) * p.R + r) : zero;
+        ra[u] = (i0 + row < p.I && r < p.R) ? ldg16(p.a + (int64_t)(i0 + row) * p.R + r) : zero;
       }
     } else {
 #pragma unroll
@@ -129,8 +147,7 @@ void bwd_gemm_kernel(BwdArgs p) {
 #pragma unroll
         for (int h = 0; h < 2; h++) {
           const int r = r0 + 2 * pair_of(c) + h;
-          ra[2 * u + h] = (r < p.R && i < p.I)
-                              ? *reinterpret_cast<const uint4*>(p.a + (int64_t)r * p.I + i) : zero;
+          ra[2 * u + h] = (r < p.R && i < p.I) ? ldg16(p.a + (int64_t)r * p.I + i) : zero;
         }
       }
     }
@@ -140,8 +157,7 @@ void bwd_gemm_kernel(BwdArgs p) {
 #pragma unroll
       for (int h = 0; h < 2; h++) {
         const int r = r0 + 2 * pair_of(c) + h;
-        rf[2 * u + h] = (r < p.R && j < p.J)
-                            ? *reinterpret_cast<const uint4*>(p.f + (int64_t)r * p.J + j) : zero;
+        rf[2 * u + h] = (r < p.R && j < p.J) ? ldg16(p.f + (int64_t)r * p.J + j) : zero;
       }
     }
   };
@@ -217,13 +233,13 @@ void bwd_gemm_kernel(BwdArgs p) {
         const int64_t o = (int64_t)i * p.J + j;
         float val = acc[ti][tj][v] * p.scale;
         if constexpr (GI) {
-          const float xv = widen16<BF>(p.x[o]);
+          const float xv = widen16<BF>(ldg2(p.x + o));
           const float q = xv / p.scale_a;
           val *= 1.0f - (q < -1.0f ? 1.0f : 0.0f) - (q > 1.0f ? 1.0f : 0.0f);
           const double s = xv != xv ? (double)NAN : (xv > 0.0f ? 1.0 : (xv < 0.0f ? -1.0 : 0.0));
           part += (double)val * s;
         }
-        p.out[o] = val;
+        stg4(p.out + o, val);
       }
     }
   if constexpr (GI) {
