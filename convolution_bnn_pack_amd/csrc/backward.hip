@@ -286,13 +286,21 @@ __device__ inline float block_nan_max(float v, float* red) {
   return red[0];
 }
 
+__device__ inline float abs_max4(const float4& q) {
+  return nan_max(nan_max(fabsf(q.x), fabsf(q.y)), nan_max(fabsf(q.z), fabsf(q.w)));
+}
+
 __global__ __launch_bounds__(kThreads) void bwd_amax_kernel(const float4* v, int64_t n4, float* part) {
   __shared__ float red[kThreads];
   float m = 0.0f;
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n4; i += (int64_t)gridDim.x * kThreads) {
-    const float4 q = v[i];
-    m = nan_max(m, nan_max(nan_max(fabsf(q.x), fabsf(q.y)), nan_max(fabsf(q.z), fabsf(q.w))));
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  // four independent 16-byte loads in flight per thread, then the remainder one at a time
+  for (; i + 3 * stride < n4; i += 4 * stride) {
+    const float4 q0 = v[i], q1 = v[i + stride], q2 = v[i + 2 * stride], q3 = v[i + 3 * stride];
+    m = nan_max(m, nan_max(nan_max(abs_max4(q0), abs_max4(q1)), nan_max(abs_max4(q2), abs_max4(q3))));
   }
+  for (; i < n4; i += stride) m = nan_max(m, abs_max4(v[i]));
   const float b = block_nan_max(m, red);
   if (threadIdx.x == 0) part[blockIdx.x] = b;
 }
