@@ -4,8 +4,9 @@
 One step = one forward pass over one batch of synthetic input with the
 weights already packed (the layers pack weights once, ahead of the forward):
 activation sign+pack, then the binary contraction with its fused scale and
-output-cast epilogue. The default workload is the 2048 x 4096 x 4096
-LLM-shaped binary linear layer with fp16 activations and output.
+output-cast epilogue. The default workload is the largest one: the
+16384 x 8192 x 8192 binary linear layer whose bf16 activations are signed and
+packed inside each step, with fp32 output.
 
 Prints ONE JSON line: binary TOPS (2*M*N*K per second; for conv M = batch*Ho*Wo,
 N = out channels, K = C*k*k), the dominant kernel's roofline (average
@@ -33,7 +34,7 @@ PEAK_MFMA_BF16_TFLOPS = 2500.0  # dense bf16 / fp16 MFMA, MI355X
 # cover 32 MACs = 64 binary ops, i.e. 32 binary ops per lane-op.
 PEAK_VALU_BINARY_TOPS = 256 * 64 * 2.4e9 * 32 / 1e12
 
-DEFAULT_WORKLOAD = "linear_2048x4096x4096_f16"
+DEFAULT_WORKLOAD = "linear_16384x8192x8192_bf16"
 # Codec workloads: one HBM-bound kernel over one workload's activation (no contraction).
 #   name -> (kernel kind, workload whose x it reads, shift dtype or None)
 CODEC_WORKLOADS = {
@@ -173,13 +174,25 @@ def pmc_summary(args):
     print(json.dumps(db, indent=1, sort_keys=True))
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None where it is not readable."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(wl, x, w):
     """The oracle as it stands on the host cores: the whole workload when it takes under
     about 30 s, else a row / image sample sized for ~15 s, scaled to binary TOPS."""
     import oracle
     cores = oracle.num_threads()
     if wl.kind == "linear":
-        probe = max(1, min(wl.m, 8))
+        # a probe of a few hundred rows: a handful of rows is too short to time with 16 threads
+        probe = max(1, min(wl.m, 256))
         t0 = time.perf_counter()
         oracle.linear_acc(x, w, rows=range(probe))
         t_probe = time.perf_counter() - t0
@@ -204,7 +217,8 @@ def cpu_baseline(wl, x, w):
         ops = 2.0 * (m // wl.batch) * imgs * n * k
         sample = "whole workload" if imgs == wl.batch else f"first {imgs} of {wl.batch} images"
     return {"value": round(ops / dt / 1e12, 6), "unit": "binary TOPS", "cores": cores,
-            "kind": "oracle", "sample": f"{sample} ({dt:.2f} s, sign + contraction + scale)"}
+            "cpu_model": cpu_model(), "kind": "oracle",
+            "sample": f"{sample} ({dt:.2f} s, sign + contraction + scale)"}
 
 
 def main():
@@ -561,7 +575,7 @@ def main():
         oracle.linear_grad_input(gcpu[:rows].contiguous(), w, x[:rows].contiguous(), sa, sw)
         dt_cpu = time.perf_counter() - t0
         result["cpu_baseline"] = {"value": round(2.0 * rows * n * k / dt_cpu / 1e12, 6), "unit": "TFLOP/s",
-                                  "cores": oracle.num_threads(), "kind": "oracle",
+                                  "cores": oracle.num_threads(), "cpu_model": cpu_model(), "kind": "oracle",
                                   "sample": f"grad_input of the first {rows} of {m} rows ({dt_cpu:.2f} s)"}
     elif not args.no_cpu_baseline and w8a8:
         import oracle
@@ -570,7 +584,7 @@ def main():
         oracle.w8a8_conv2d_acc(x, w, wl.stride, wl.padding, wl.dilation, amax_x, amax_w, images=[0])
         dt_cpu = time.perf_counter() - t0
         result["cpu_baseline"] = {"value": round(ops / wl.batch / dt_cpu / 1e12, 6), "unit": "int8 TOPS",
-                                  "cores": oracle.num_threads(), "kind": "oracle",
+                                  "cores": oracle.num_threads(), "cpu_model": cpu_model(), "kind": "oracle",
                                   "sample": f"first 1 of {wl.batch} images ({dt_cpu:.2f} s, quantize + contraction)"}
     elif not args.no_cpu_baseline and not pack_only:
         log("cpu baseline (oracle on host cores)")

@@ -108,12 +108,49 @@ def _check(status: int, where: str):
     raise BnnError(status, where)
 
 
+# Device types accepted for tensor arguments (HIP devices appear as "cuda" in torch).
+_DEVICE_TYPES = ("cuda",)
+
+
 def _dev(t: torch.Tensor, name: str) -> torch.Tensor:
-    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+    if not isinstance(t, torch.Tensor) or t.device.type not in _DEVICE_TYPES:
         raise ValueError(f"{name} must be a device (HIP) tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return t
+
+
+def _expect(t: torch.Tensor, name: str, dtype, shape) -> torch.Tensor:
+    """Raise before any library call unless t (a device tensor) has exactly this dtype (one
+    dtype or a tuple of allowed ones) and shape: the C ABI takes raw pointers, so a wrongly
+    sized buffer would be read or written out of bounds on the device."""
+    _dev(t, name)
+    allowed = dtype if isinstance(dtype, tuple) else (dtype,)
+    if t.dtype not in allowed:
+        raise TypeError(f"{name} must be {' or '.join(str(d) for d in allowed)}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+_OUT_DTYPES = (torch.float32, torch.float16, torch.bfloat16, torch.int32)
+
+
+def _packed_len(x: torch.Tensor, n: int | None, what: str) -> int:
+    """Sign count of a packed int32 tensor whose last axis holds the words: n when given (it
+    must need exactly that many words), else 32 per word."""
+    cw = x.shape[-1]
+    if n is None:
+        return 32 * cw
+    n = int(n)
+    if n < 1 or words(n) != cw:
+        raise ValueError(f"{what} = {n} needs {words(max(n, 1))} packed words, x holds {cw}")
+    return n
+
+
+def _same_device(name: str, t: torch.Tensor, ref: torch.Tensor):
+    if t.device != ref.device:
+        raise ValueError(f"{name} must be on {ref.device}, got {t.device}")
 
 
 def _stream(t: torch.Tensor) -> int:
@@ -145,7 +182,8 @@ def pack_sign(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     if out is None:
         out = torch.empty((*x.shape[:-1], words(k)), dtype=torch.int32, device=x.device)
     else:
-        _dev(out, "out")
+        _expect(out, "out", torch.int32, (*x.shape[:-1], words(k)))
+        _same_device("out", out, x)
     _check(lib.bnn_pack_sign(x.data_ptr(), _dtype_code(x, "x"), rows, k, out.data_ptr(), _stream(x)),
            "bnn_pack_sign")
     return out
@@ -154,11 +192,14 @@ def pack_sign(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
 def pack_sign_nchw(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     """Sign+pack of NCHW activations along channels: [n, c, h, w] -> int32 words [n, h, w, ceil(c/32)]."""
     x = _dev(x, "x")
+    if x.dim() != 4:
+        raise ValueError(f"x must be NCHW (4-D), got {x.dim()}-D")
     n, c, h, w = x.shape
     if out is None:
         out = torch.empty((n, h, w, words(c)), dtype=torch.int32, device=x.device)
     else:
-        _dev(out, "out")
+        _expect(out, "out", torch.int32, (n, h, w, words(c)))
+        _same_device("out", out, x)
     _check(lib.bnn_pack_sign_nchw(x.data_ptr(), _dtype_code(x, "x"), n, c, h, w, out.data_ptr(),
                                   _stream(x)), "bnn_pack_sign_nchw")
     return out
@@ -178,10 +219,13 @@ def pack_sign_shift(x: torch.Tensor, bias: torch.Tensor, out: torch.Tensor | Non
     bias = _bias(bias, x)
     k = x.shape[-1]
     rows = x.numel() // k if k else 0
+    if bias.numel() not in (1, k):
+        raise ValueError(f"bias must hold one value or one per column ({k}), got {bias.numel()}")
     if out is None:
         out = torch.empty((*x.shape[:-1], words(k)), dtype=torch.int32, device=x.device)
     else:
-        _dev(out, "out")
+        _expect(out, "out", torch.int32, (*x.shape[:-1], words(k)))
+        _same_device("out", out, x)
     _check(lib.bnn_pack_sign_shift(x.data_ptr(), _dtype_code(x, "x"), rows, k, bias.data_ptr(),
                                    _dtype_code(bias, "bias"), bias.numel(), out.data_ptr(),
                                    _stream(x)), "bnn_pack_sign_shift")
@@ -194,13 +238,16 @@ def pack_sign_nchw_shift(x: torch.Tensor, bias: torch.Tensor,
     bit = (x[n, c, h, w] + bias[c] >= 0) -> int32 words [n, h, w, ceil(c/32)]."""
     x = _dev(x, "x")
     bias = _bias(bias, x)
+    if x.dim() != 4:
+        raise ValueError(f"x must be NCHW (4-D), got {x.dim()}-D")
     n, c, h, w = x.shape
     if bias.numel() != c:
         raise ValueError(f"bias must hold one value per channel ({c}), got {bias.numel()}")
     if out is None:
         out = torch.empty((n, h, w, words(c)), dtype=torch.int32, device=x.device)
     else:
-        _dev(out, "out")
+        _expect(out, "out", torch.int32, (n, h, w, words(c)))
+        _same_device("out", out, x)
     _check(lib.bnn_pack_sign_nchw_shift(x.data_ptr(), _dtype_code(x, "x"), n, c, h, w,
                                         bias.data_ptr(), _dtype_code(bias, "bias"), out.data_ptr(),
                                         _stream(x)), "bnn_pack_sign_nchw_shift")
@@ -214,12 +261,18 @@ def abs_mean_scale(x: torch.Tensor, factor: float, out: torch.Tensor | None = No
     x = _dev(x, "x")
     if out is None:
         out = torch.empty((), dtype=torch.float64, device=x.device)
+    else:
+        _expect(out, "out", torch.float64, ())
+        _same_device("out", out, x)
     need = lib.bnn_abs_mean_workspace_bytes(x.numel())
     if workspace is None:
         workspace = _workspace(need, x.device)
+    else:
+        _dev(workspace, "workspace")
+        _same_device("workspace", workspace, x)
     _check(lib.bnn_abs_mean_scale(x.data_ptr(), _dtype_code(x, "x"), x.numel(), float(factor),
                                   out.data_ptr(), workspace.data_ptr(),
-                                  workspace.numel() * workspace.element_size(), _stream(x)),
+                                  _nbytes(workspace), _stream(x)),
            "bnn_abs_mean_scale")
     return out
 
@@ -252,6 +305,10 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
+def _nbytes(t: torch.Tensor | None) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
 def gemm(x: torch.Tensor, w_packed: torch.Tensor, scale_a: float, scale_w: float, path="auto",
          out_dtype=None, k: int | None = None, out: torch.Tensor | None = None,
          workspace: torch.Tensor | None = None) -> torch.Tensor:
@@ -265,28 +322,40 @@ def gemm(x: torch.Tensor, w_packed: torch.Tensor, scale_a: float, scale_w: float
     """
     x = _dev(x, "x")
     w_packed = _dev(w_packed, "w_packed")
+    _same_device("w_packed", w_packed, x)
+    if x.dim() != 2:
+        raise ValueError(f"x must be 2-D [m, k] (or packed [m, words]), got {x.dim()}-D")
     packed = x.dtype == torch.int32
     m = x.shape[0]
     if packed:
-        k = 32 * x.shape[1] if k is None else k
+        k = _packed_len(x, k, "k")
         xcode = U32_PACKED
     else:
         k = x.shape[1]
         xcode = _dtype_code(x, "x")
+    if w_packed.dim() != 2:
+        raise ValueError(f"w_packed must be 2-D [n, words(k)], got {w_packed.dim()}-D")
     n = w_packed.shape[0]
+    _expect(w_packed, "w_packed", torch.int32, (n, words(k)))
     if out_dtype is None:
         out_dtype = torch.float32 if packed else x.dtype
     if out is None:
+        if out_dtype not in _OUT_DTYPES:
+            raise TypeError(f"out_dtype must be one of {_OUT_DTYPES}, got {out_dtype}")
         out = torch.empty((m, n), dtype=out_dtype, device=x.device)
     else:
-        _dev(out, "out")
+        _expect(out, "out", _OUT_DTYPES, (m, n))
+        _same_device("out", out, x)
     ws_bytes = lib.bnn_gemm_workspace_bytes(m, k, xcode)
     if workspace is None and ws_bytes:
         workspace = _workspace(ws_bytes, x.device)
+    elif workspace is not None:
+        _dev(workspace, "workspace")
+        _same_device("workspace", workspace, x)
     _check(lib.bnn_gemm(x.data_ptr(), xcode, w_packed.data_ptr(), m, n, k, float(scale_a),
                         float(scale_w), _path(path), out.data_ptr(), _DT[out.dtype],
                         workspace.data_ptr() if workspace is not None else None,
-                        workspace.numel() if workspace is not None else 0, _stream(x)), "bnn_gemm")
+                        _nbytes(workspace), _stream(x)), "bnn_gemm")
     return out
 
 
@@ -311,30 +380,42 @@ def conv2d(x: torch.Tensor, w_packed: torch.Tensor, scale_a: float, scale_w: flo
     """
     x = _dev(x, "x")
     w_packed = _dev(w_packed, "w_packed")
+    _same_device("w_packed", w_packed, x)
+    if x.dim() != 4:
+        raise ValueError(f"x must be 4-D (NCHW float or packed [n, h, w, words]), got {x.dim()}-D")
     packed = x.dtype == torch.int32
     if packed:
         n, h, w, cw = x.shape
-        c = 32 * cw if channels is None else channels
+        c = _packed_len(x, channels, "channels")
         xcode = U32_PACKED
     else:
         n, c, h, w = x.shape
         xcode = _dtype_code(x, "x")
     (kh, kw), (sh, sw) = _pair(kernel_size, "kernel_size"), _pair(stride, "stride")
     (ph, pw), (dh, dw) = _pair(padding, "padding"), _pair(dilation, "dilation")
+    if w_packed.dim() != 4:
+        raise ValueError(f"w_packed must be 4-D [o, kh, kw, words(c)], got {w_packed.dim()}-D")
     o = w_packed.shape[0]
+    _expect(w_packed, "w_packed", torch.int32, (o, kh, kw, words(c)))
     ho = (h + 2 * ph - dh * (kh - 1) - 1) // sh + 1 if sh > 0 else 0
     wo = (w + 2 * pw - dw * (kw - 1) - 1) // sw + 1 if sw > 0 else 0
     if out_dtype is None:
         out_dtype = torch.float32 if packed else x.dtype
     if out is None:
+        if out_dtype not in _OUT_DTYPES:
+            raise TypeError(f"out_dtype must be one of {_OUT_DTYPES}, got {out_dtype}")
         out = torch.empty((n, o, max(ho, 0), max(wo, 0)), dtype=out_dtype, device=x.device)
     else:
-        _dev(out, "out")
+        _expect(out, "out", _OUT_DTYPES, (n, o, max(ho, 0), max(wo, 0)))
+        _same_device("out", out, x)
     ws_bytes = lib.bnn_conv2d_workspace_bytes(n, c, h, w, xcode)
     if workspace is None and ws_bytes:
         workspace = _workspace(ws_bytes, x.device)
+    elif workspace is not None:
+        _dev(workspace, "workspace")
+        _same_device("workspace", workspace, x)
     wsp = workspace.data_ptr() if workspace is not None else None
-    wsn = workspace.numel() if workspace is not None else 0
+    wsn = _nbytes(workspace)
     common = (x.data_ptr(), xcode, n, c, h, w, w_packed.data_ptr(), o, float(scale_a), float(scale_w))
     if kh == kw and sh == sw and ph == pw and dh == dw:
         _check(lib.bnn_conv2d(*common, kh, sh, ph, dh, _path(path), out.data_ptr(), _DT[out.dtype],
@@ -386,6 +467,9 @@ def w8a8_conv2d(x_q: torch.Tensor, w_q: torch.Tensor, amax_x: float, amax_w: flo
     """W8A8 conv on int8 codes: x_q NHWC [n, h, w, c], w_q [o, kh, kw, c]; NCHW output
     (amax_x/127) * (amax_w/127) * sum q_x q_w, or the raw int32 sums for out_dtype=torch.int32."""
     x_q, w_q = _dev(x_q, "x_q"), _dev(w_q, "w_q")
+    _same_device("w_q", w_q, x_q)
+    if x_q.dim() != 4 or w_q.dim() != 4 or x_q.dtype != torch.int8 or w_q.dtype != torch.int8:
+        raise ValueError("x_q [n, h, w, c] and w_q [o, kh, kw, c] must be 4-D int8 tensors")
     n, h, w, c = x_q.shape
     o, kh, kw, c2 = w_q.shape
     if c != c2:
@@ -396,9 +480,12 @@ def w8a8_conv2d(x_q: torch.Tensor, w_q: torch.Tensor, amax_x: float, amax_w: flo
     ho = (h + 2 * ph - dh * (kh - 1) - 1) // sh + 1 if sh > 0 else 0
     wo = (w + 2 * pw - dw * (kw - 1) - 1) // sw + 1 if sw > 0 else 0
     if out is None:
+        if out_dtype not in _OUT_DTYPES:
+            raise TypeError(f"out_dtype must be one of {_OUT_DTYPES}, got {out_dtype}")
         out = torch.empty((n, o, max(ho, 0), max(wo, 0)), dtype=out_dtype, device=x_q.device)
     else:
-        _dev(out, "out")
+        _expect(out, "out", _OUT_DTYPES, (n, o, max(ho, 0), max(wo, 0)))
+        _same_device("out", out, x_q)
     _check(lib.bnn_w8a8_conv2d(x_q.data_ptr(), n, c, h, w, w_q.data_ptr(), o, float(amax_x),
                                float(amax_w), kh, kw, sh, sw, ph, pw, dh, dw, out.data_ptr(),
                                _DT[out.dtype], _stream(x_q)), "bnn_w8a8_conv2d")
@@ -424,21 +511,34 @@ def linear_grad_input(grad_out: torch.Tensor, weight: torch.Tensor, x: torch.Ten
     dt = _half_pair(g, "grad_out")
     if w.dtype != g.dtype or x.dtype != g.dtype:
         raise TypeError("grad_out, weight and x must share one dtype")
+    if g.dim() != 2 or w.dim() != 2 or x.dim() != 2:
+        raise ValueError("grad_out, weight and x must be 2-D")
+    _same_device("weight", w, g)
+    _same_device("x", x, g)
     m, n = g.shape
     n2, k = w.shape
     if n2 != n or tuple(x.shape) != (m, k):
         raise ValueError(f"shape mismatch: grad_out {tuple(g.shape)}, weight {tuple(w.shape)}, x {tuple(x.shape)}")
     if out is None:
         out = torch.empty((m, k), dtype=torch.float32, device=g.device)
+    else:
+        _expect(out, "out", torch.float32, (m, k))
+        _same_device("out", out, g)
     if grad_scale_a is None:
         grad_scale_a = torch.empty((), dtype=torch.float64, device=g.device)
+    else:
+        _expect(grad_scale_a, "grad_scale_a", torch.float64, ())
+        _same_device("grad_scale_a", grad_scale_a, g)
     need = lib.bnn_linear_grad_input_workspace_bytes(m, k)
     if workspace is None:
         workspace = _workspace(need, g.device)
+    else:
+        _dev(workspace, "workspace")
+        _same_device("workspace", workspace, g)
     _check(lib.bnn_linear_grad_input(g.data_ptr(), w.data_ptr(), x.data_ptr(), dt, m, n, k,
                                      float(scale_a), float(scale_w), out.data_ptr(),
                                      grad_scale_a.data_ptr(), workspace.data_ptr(),
-                                     workspace.numel() * workspace.element_size(), _stream(g)),
+                                     _nbytes(workspace), _stream(g)),
            "bnn_linear_grad_input")
     return out, grad_scale_a
 
@@ -451,12 +551,18 @@ def linear_grad_weight(grad_out: torch.Tensor, x: torch.Tensor, scale_a: float,
     dt = _half_pair(g, "grad_out")
     if x.dtype != g.dtype:
         raise TypeError("grad_out and x must share one dtype")
+    if g.dim() != 2 or x.dim() != 2:
+        raise ValueError("grad_out and x must be 2-D")
+    _same_device("x", x, g)
     m, n = g.shape
     if x.shape[0] != m:
         raise ValueError(f"shape mismatch: grad_out {tuple(g.shape)}, x {tuple(x.shape)}")
     k = x.shape[1]
     if out is None:
         out = torch.empty((n, k), dtype=torch.float32, device=g.device)
+    else:
+        _expect(out, "out", torch.float32, (n, k))
+        _same_device("out", out, g)
     _check(lib.bnn_linear_grad_weight(g.data_ptr(), x.data_ptr(), dt, m, n, k, float(scale_a),
                                       out.data_ptr(), _stream(g)), "bnn_linear_grad_weight")
     return out
@@ -470,6 +576,9 @@ def linear_grad_weight_i8(grad_out: torch.Tensor, x: torch.Tensor, scale_a: floa
     dt = _half_pair(g, "grad_out")
     if x.dtype != g.dtype:
         raise TypeError("grad_out and x must share one dtype")
+    if g.dim() != 2 or x.dim() != 2:
+        raise ValueError("grad_out and x must be 2-D")
+    _same_device("x", x, g)
     m, n = g.shape
     if x.shape[0] != m:
         raise ValueError(f"shape mismatch: grad_out {tuple(g.shape)}, x {tuple(x.shape)}")
@@ -480,7 +589,7 @@ def linear_grad_weight_i8(grad_out: torch.Tensor, x: torch.Tensor, scale_a: floa
     ws = _workspace(lib.bnn_linear_grad_weight_i8_workspace_bytes(n, k), g.device)
     _check(lib.bnn_linear_grad_weight_i8(g.data_ptr(), x.data_ptr(), dt, m, n, k, float(scale_a),
                                          gw.data_ptr(), codes.data_ptr(), amax.data_ptr(),
-                                         ws.data_ptr(), ws.numel(), _stream(g)),
+                                         ws.data_ptr(), _nbytes(ws), _stream(g)),
            "bnn_linear_grad_weight_i8")
     return gw, codes, amax
 
@@ -495,5 +604,5 @@ def quant_grad_i8(grad: torch.Tensor):
     amax = torch.empty((), dtype=torch.float32, device=g.device)
     ws = _workspace(lib.bnn_quant_grad_i8_workspace_bytes(g.numel()), g.device)
     _check(lib.bnn_quant_grad_i8(g.data_ptr(), g.numel(), codes.data_ptr(), amax.data_ptr(), ws.data_ptr(),
-                                 ws.numel(), _stream(g)), "bnn_quant_grad_i8")
+                                 _nbytes(ws), _stream(g)), "bnn_quant_grad_i8")
     return codes, amax

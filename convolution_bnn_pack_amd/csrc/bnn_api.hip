@@ -52,6 +52,10 @@ bool int_fits(int64_t v) { return v >= 0 && v <= 0x7FFFFFFFLL; }
 // Words holding n signs: the last one partly when n % 32 != 0 (its missing bits are 0).
 int64_t words_of(int64_t n) { return (n + 31) / 32; }
 
+// A reduction length the kernels can index: the contraction kernels count 32 signs per
+// word in int, so 32 * words_of(n) must fit as well as n itself.
+bool bits_fit(int64_t n) { return int_fits(n) && int_fits(32 * words_of(n)); }
+
 // Row sign+pack of any row length: the 16-byte vector kernels when rows are whole words and
 // the tensor is 16-byte aligned, the one-element-per-lane kernel otherwise.
 hipError_t pack_rows_any(const void* x, int dtype, int64_t rows, int64_t k, const void* bias,
@@ -233,7 +237,7 @@ bnn_status bnn_gemm(const void* x, int x_dtype, const uint32_t* w_packed, int64_
   if (!(float_dtype(x_dtype) || x_dtype == BNN_U32_PACKED) || !out_dtype_ok(out_dtype))
     return BNN_ERR_DTYPE;
   if (m < 0 || n < 0 || k < 1) return BNN_ERR_SHAPE;
-  if (!int_fits(m) || !int_fits(n) || !int_fits(k)) return BNN_ERR_SHAPE;
+  if (!int_fits(m) || !int_fits(n) || !bits_fit(k)) return BNN_ERR_SHAPE;
   if (!path_known(path)) return BNN_ERR_PATH;
   if (path == BNN_PATH_MFMA_FP4 && k > bnn::kMaxFp4K) return BNN_ERR_PATH;
   if (m == 0 || n == 0) return BNN_OK;
@@ -287,7 +291,7 @@ bnn_status bnn_conv2d_ex(const void* x, int x_dtype, int64_t n, int64_t c, int64
   const int64_t kw_words = taps * words_of(c);
   if (!int_fits(n * ho * wo) || !int_fits(out_channels) || !int_fits(kw_words) ||
       !int_fits(n * h * w * words_of(c)) || !int_fits(h + 2 * (int64_t)pad_h) ||
-      !int_fits(w + 2 * (int64_t)pad_w) || !int_fits(taps * c))
+      !int_fits(w + 2 * (int64_t)pad_w) || !int_fits(taps * c) || !bits_fit(c))
     return BNN_ERR_SHAPE;
   if (!path_known(path)) return BNN_ERR_PATH;
   if (path == BNN_PATH_XOR && taps > bnn::xor_conv_max_taps()) return BNN_ERR_PATH;

@@ -83,6 +83,11 @@ def test_gemm_argument_checks(bnn):
     # empty problems are no-ops and succeed without touching anything
     assert _gemm(bnn, m=0, x=None, out=None) == bnn.OK
     assert _gemm(bnn, n=0, x=None, out=None) == bnn.OK
+    # reduction lengths whose 32 * words no longer fit an int are rejected (the kernels count
+    # 32 signs per word in int); the largest that fits passes the shape checks
+    for k in ((1 << 31) - 1, (1 << 31) - 31):
+        assert _gemm(bnn, k=k, path=bnn.PATH_MFMA, x=None) == bnn.ERR_SHAPE
+    assert _gemm(bnn, k=(1 << 31) - 32, path=bnn.PATH_MFMA, x=None) == bnn.ERR_NULL
 
 
 def _conv(bnn, **kw):
@@ -97,6 +102,8 @@ def _conv(bnn, **kw):
 
 def test_conv_argument_checks(bnn):
     assert _conv(bnn, c=48, wp=None) == bnn.ERR_NULL                # ragged C passes the shape checks
+    # a channel count whose 32 * words overflows int is rejected before anything else runs
+    assert _conv(bnn, c=(1 << 31) - 1, ks=1, p=0, n=1, h=1, w=1, path=bnn.PATH_MFMA) == bnn.ERR_SHAPE
     assert _conv(bnn, c=0) == bnn.ERR_SHAPE
     assert _conv(bnn, ks=0) == bnn.ERR_SHAPE
     assert _conv(bnn, s=0) == bnn.ERR_SHAPE
