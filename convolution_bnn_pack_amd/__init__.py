@@ -28,6 +28,9 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 # parameters); the default is the in-tree build.
 LIB_PATH = os.environ.get("BNN_LIBRARY") or os.path.join(_PKG, "libbnn.so")
 
+# size of bnn_gemm_noalloc's static device array (BNN_NOALLOC_SCRATCH_BYTES of include/bnn.h)
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
 # bnn_dtype / bnn_path / bnn_status codes of include/bnn.h
 F32, F16, BF16, I32, U32_PACKED = 0, 1, 2, 3, 4
 PATH_AUTO, PATH_XOR, PATH_MFMA, PATH_MFMA_FP4 = 0, 1, 2, 3
@@ -36,7 +39,7 @@ OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIGN, ERR_WORKSPACE, ERR_PATH, ERR_HIP 
 EXPORTS = ("bnn_pack_sign", "bnn_pack_sign_nchw", "bnn_pack_sign_shift", "bnn_pack_sign_nchw_shift",
            "bnn_abs_mean_scale", "bnn_abs_mean_workspace_bytes", "bnn_w_pack", "bnn_w_pack_conv",
            "bnn_conv2d_ex", "bnn_quant_i8_nhwc", "bnn_quant_i8_weight", "bnn_w8a8_conv2d", "bnn_gemm", "bnn_conv2d",
-           "bnn_gemm_workspace_bytes", "bnn_conv2d_workspace_bytes", "bnn_gemm_auto_path",
+           "bnn_gemm_noalloc", "bnn_gemm_workspace_bytes", "bnn_conv2d_workspace_bytes", "bnn_gemm_auto_path",
            "bnn_conv2d_auto_path", "bnn_last_path", "bnn_status_string",
            "bnn_linear_grad_input", "bnn_linear_grad_input_workspace_bytes", "bnn_linear_grad_weight",
            "bnn_linear_grad_weight_i8", "bnn_linear_grad_weight_i8_workspace_bytes",
@@ -72,6 +75,7 @@ def _bind(path: str) -> ctypes.CDLL:
         "bnn_w8a8_conv2d": ([P, I64, I64, I64, I64, P, I64, D, D] + [I] * 8 + [P, I, P], I),
         "bnn_conv2d_ex": ([P, I, I64, I64, I64, I64, P, I64, D, D] + [I] * 9 + [P, I, P, SZ, P], I),
         "bnn_gemm": ([P, I, P, I64, I64, I64, D, D, I, P, I, P, SZ, P], I),
+        "bnn_gemm_noalloc": ([P, I, P, I64, I64, I64, D, D, I, P, I, P], I),
         "bnn_conv2d": ([P, I, I64, I64, I64, I64, P, I64, D, D, I, I, I, I, I, P, I, P, SZ, P], I),
         "bnn_gemm_workspace_bytes": ([I64, I64, I], SZ),
         "bnn_conv2d_workspace_bytes": ([I64, I64, I64, I64, I], SZ),
@@ -356,6 +360,30 @@ def gemm(x: torch.Tensor, w_packed: torch.Tensor, scale_a: float, scale_w: float
                         float(scale_w), _path(path), out.data_ptr(), _DT[out.dtype],
                         workspace.data_ptr() if workspace is not None else None,
                         _nbytes(workspace), _stream(x)), "bnn_gemm")
+    return out
+
+
+def gemm_noalloc(x: torch.Tensor, w_packed: torch.Tensor, scale_a: float, scale_w: float,
+                 out: torch.Tensor, path="auto", k: int | None = None) -> torch.Tensor:
+    """gemm without any device allocation: the caller passes `out`, and float activations are
+    packed into the library's static device array (at most NOALLOC_SCRATCH_BYTES; calls that
+    overlap on one device race for it)."""
+    x = _dev(x, "x")
+    w_packed = _dev(w_packed, "w_packed")
+    _same_device("w_packed", w_packed, x)
+    if x.dim() != 2 or w_packed.dim() != 2:
+        raise ValueError("x and w_packed must be 2-D")
+    packed = x.dtype == torch.int32
+    m = x.shape[0]
+    k = _packed_len(x, k, "k") if packed else x.shape[1]
+    xcode = U32_PACKED if packed else _dtype_code(x, "x")
+    n = w_packed.shape[0]
+    _expect(w_packed, "w_packed", torch.int32, (n, words(k)))
+    _expect(out, "out", _OUT_DTYPES, (m, n))
+    _same_device("out", out, x)
+    _check(lib.bnn_gemm_noalloc(x.data_ptr(), xcode, w_packed.data_ptr(), m, n, k, float(scale_a),
+                                float(scale_w), _path(path), out.data_ptr(), _DT[out.dtype],
+                                _stream(x)), "bnn_gemm_noalloc")
     return out
 
 

@@ -6,6 +6,8 @@
 // testable on a host without a GPU).
 #include <math.h>
 
+#include <mutex>
+
 #include "../../include/bnn.h"
 #include "launch.h"
 
@@ -79,6 +81,40 @@ hipError_t run_path(int use, const bnn::Contraction& p, bool conv, int out_dtype
     default: return bnn::launch_mfma(p, conv, out_dtype, s);
   }
 }
+
+// Device memory of bnn_gemm_noalloc: the packed activations it would otherwise need a
+// workspace for live in this file-scope array, which each device holds from the library's
+// load until the process ends. Host code must never use the array's name as an address
+// (on the host it is only a stand-in for the symbol): the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current and kept here.
+constexpr size_t kScratchBytes = BNN_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) uint32_t scratch[kScratchBytes / sizeof(uint32_t)];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The current device's copy of `scratch` (its address there), resolved on the first call on
+// that device.
+bnn_status scratch_of_current_device(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return BNN_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return BNN_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return BNN_OK;
+}
+
+// bnn_gemm's body. With use_scratch the packed activations go to the current device's
+// `scratch` (at most kScratchBytes) instead of the caller's workspace.
+bnn_status gemm_impl(const void* x, int x_dtype, const uint32_t* w_packed, int64_t m, int64_t n,
+                     int64_t k, double scale_a, double scale_w, int path, void* out,
+                     int out_dtype, void* workspace, size_t workspace_bytes, bool use_scratch,
+                     void* stream);
 
 }  // namespace
 
@@ -234,43 +270,15 @@ bnn_status bnn_w_pack_conv(const void* weight, int w_dtype, int64_t out_features
 bnn_status bnn_gemm(const void* x, int x_dtype, const uint32_t* w_packed, int64_t m, int64_t n,
                     int64_t k, double scale_a, double scale_w, int path, void* out, int out_dtype,
                     void* workspace, size_t workspace_bytes, void* stream) {
-  if (!(float_dtype(x_dtype) || x_dtype == BNN_U32_PACKED) || !out_dtype_ok(out_dtype))
-    return BNN_ERR_DTYPE;
-  if (m < 0 || n < 0 || k < 1) return BNN_ERR_SHAPE;
-  if (!int_fits(m) || !int_fits(n) || !bits_fit(k)) return BNN_ERR_SHAPE;
-  if (!path_known(path)) return BNN_ERR_PATH;
-  if (path == BNN_PATH_MFMA_FP4 && k > bnn::kMaxFp4K) return BNN_ERR_PATH;
-  if (m == 0 || n == 0) return BNN_OK;
-  if (!x || !w_packed || !out) return BNN_ERR_NULL;
-  const bool packed = x_dtype == BNN_U32_PACKED;
-  if (!aligned(x, packed ? 4 : elem_bytes(x_dtype)) || !aligned(w_packed, 4) || !aligned(out, 16))
-    return BNN_ERR_ALIGN;
-  const size_t need = bnn_gemm_workspace_bytes(m, k, x_dtype);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return BNN_ERR_WORKSPACE;
-  if (need > 0 && !aligned(workspace, 4)) return BNN_ERR_ALIGN;
+  return gemm_impl(x, x_dtype, w_packed, m, n, k, scale_a, scale_w, path, out, out_dtype,
+                   workspace, workspace_bytes, false, stream);
+}
 
-  const int use = path == BNN_PATH_AUTO ? auto_path(k) : path;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const uint32_t* a = static_cast<const uint32_t*>(x);
-  if (!packed) {
-    uint32_t* ws = static_cast<uint32_t*>(workspace);
-    const hipError_t e = pack_rows_any(x, x_dtype, m, k, nullptr, 0, false, ws, s);
-    if (e != hipSuccess) return BNN_ERR_HIP;
-    a = ws;
-  }
-  bnn::Contraction p{};
-  p.a = a;
-  p.w = w_packed;
-  p.out = out;
-  p.M = (int)m;
-  p.N = (int)n;
-  p.KW = (int)words_of(k);
-  p.KB = (int)k;
-  p.alpha = alpha_of(scale_a, scale_w);
-  const hipError_t e = run_path(use, p, false, out_dtype, s);
-  if (e != hipSuccess) return BNN_ERR_HIP;
-  g_last_path = use;
-  return BNN_OK;
+bnn_status bnn_gemm_noalloc(const void* x, int x_dtype, const uint32_t* w_packed, int64_t m,
+                            int64_t n, int64_t k, double scale_a, double scale_w, int path,
+                            void* out, int out_dtype, void* stream) {
+  return gemm_impl(x, x_dtype, w_packed, m, n, k, scale_a, scale_w, path, out, out_dtype, nullptr,
+                   0, true, stream);
 }
 
 bnn_status bnn_conv2d_ex(const void* x, int x_dtype, int64_t n, int64_t c, int64_t h, int64_t w,
@@ -496,3 +504,58 @@ bnn_status bnn_quant_grad_i8(const float* grad, int64_t count, int8_t* codes, fl
 }
 
 }  // extern "C"
+
+namespace {
+bnn_status gemm_impl(const void* x, int x_dtype, const uint32_t* w_packed, int64_t m, int64_t n,
+                     int64_t k, double scale_a, double scale_w, int path, void* out,
+                     int out_dtype, void* workspace, size_t workspace_bytes, bool use_scratch,
+                     void* stream) {
+  if (!(float_dtype(x_dtype) || x_dtype == BNN_U32_PACKED) || !out_dtype_ok(out_dtype))
+    return BNN_ERR_DTYPE;
+  if (m < 0 || n < 0 || k < 1) return BNN_ERR_SHAPE;
+  if (!int_fits(m) || !int_fits(n) || !bits_fit(k)) return BNN_ERR_SHAPE;
+  if (!path_known(path)) return BNN_ERR_PATH;
+  if (path == BNN_PATH_MFMA_FP4 && k > bnn::kMaxFp4K) return BNN_ERR_PATH;
+  if (m == 0 || n == 0) return BNN_OK;
+  if (!x || !w_packed || !out) return BNN_ERR_NULL;
+  const bool packed = x_dtype == BNN_U32_PACKED;
+  if (!aligned(x, packed ? 4 : elem_bytes(x_dtype)) || !aligned(w_packed, 4) || !aligned(out, 16))
+    return BNN_ERR_ALIGN;
+  const size_t need = bnn_gemm_workspace_bytes(m, k, x_dtype);
+  if (use_scratch) {
+    // every argument is checked by now; resolving the scratch address enqueues nothing
+    if (need > kScratchBytes) return BNN_ERR_WORKSPACE;
+    if (need > 0) {
+      const bnn_status st = scratch_of_current_device(&workspace);
+      if (st != BNN_OK) return st;
+      workspace_bytes = kScratchBytes;
+    }
+  }
+  if (need > 0 && (!workspace || workspace_bytes < need)) return BNN_ERR_WORKSPACE;
+  if (need > 0 && !aligned(workspace, 4)) return BNN_ERR_ALIGN;
+
+  const int use = path == BNN_PATH_AUTO ? auto_path(k) : path;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint32_t* a = static_cast<const uint32_t*>(x);
+  if (!packed) {
+    uint32_t* ws = static_cast<uint32_t*>(workspace);
+    const hipError_t e = pack_rows_any(x, x_dtype, m, k, nullptr, 0, false, ws, s);
+    if (e != hipSuccess) return BNN_ERR_HIP;
+    a = ws;
+  }
+  bnn::Contraction p{};
+  p.a = a;
+  p.w = w_packed;
+  p.out = out;
+  p.M = (int)m;
+  p.N = (int)n;
+  p.KW = (int)words_of(k);
+  p.KB = (int)k;
+  p.alpha = alpha_of(scale_a, scale_w);
+  const hipError_t e = run_path(use, p, false, out_dtype, s);
+  if (e != hipSuccess) return BNN_ERR_HIP;
+  g_last_path = use;
+  return BNN_OK;
+}
+
+}  // namespace

@@ -160,6 +160,23 @@ bnn_status bnn_gemm(const void* x, int x_dtype, const uint32_t* w_packed, int64_
                     int64_t k, double scale_a, double scale_w, int path, void* out, int out_dtype,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): bnn_gemm without a workspace argument. Float
+ * activations are packed into a static device array of BNN_NOALLOC_SCRATCH_BYTES bytes that
+ * the library holds on every device it runs on until the process ends; the call itself
+ * allocates and frees nothing. Arguments, layouts, results and errors as bnn_gemm, plus:
+ *   - m * ceil(k/32) * 4 > BNN_NOALLOC_SCRATCH_BYTES (float x) -> BNN_ERR_WORKSPACE, nothing
+ *     enqueued; packed x (BNN_U32_PACKED) needs no scratch and has no such limit;
+ *   - the array belongs to the current device, which must be the device of `stream`; its
+ *     address is looked up on the first call on each device (BNN_ERR_HIP if that fails);
+ *   - every call on a device shares that device's array and it keeps the last call's
+ *     contents: calls that overlap on one device (other streams, other host threads) race.
+ *     Calls on one stream are ordered and safe. */
+#define BNN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+bnn_status bnn_gemm_noalloc(const void* x, int x_dtype, const uint32_t* w_packed, int64_t m,
+                            int64_t n, int64_t k, double scale_a, double scale_w, int path,
+                            void* out, int out_dtype, void* stream);
+
 /* Binary conv2d forward (square kernel, symmetric stride/padding/dilation).
  *   x         NCHW [n, c, h, w] in BNN_F32/F16/BF16, or [n, h, w, ceil(c/32)] BNN_U32_PACKED.
  *   w_packed  [out_channels, k, k, ceil(c/32)] from bnn_w_pack(kernel_size = k).
