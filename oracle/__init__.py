@@ -60,6 +60,9 @@ def _bind(lib):
     lib.oracle_conv2d_kvalid2.argtypes = [I64] * 11 + [P]
     lib.oracle_conv2d_kvalid2.restype = I
     lib.oracle_pack_conv_weight2.argtypes = [P, I, I64, I64, I64, I64, P]
+    lib.oracle_pack_rows_u8.argtypes = [P, I, I64, I64, P]
+    lib.oracle_pack_nchw_u8.argtypes = [P, I, I64, I64, I64, I64, P]
+    lib.oracle_pack_conv_weight_u8.argtypes = [P, I, I64, I64, I64, I64, P]
     lib.oracle_quant_i8.argtypes = [P, I, I64, ctypes.c_float, P]
     lib.oracle_w8a8_conv2d_acc.argtypes = [P, I, P, I] + [I64] * 13 + [ctypes.c_float, ctypes.c_float,
                                                                        P, I64, P]
@@ -158,6 +161,38 @@ def pack_conv_weight(w: torch.Tensor) -> torch.Tensor:
     else:
         _load().oracle_pack_conv_weight2(w.data_ptr(), _code(w), o, c, kh, kw, out.data_ptr())
     return out.view(o, kh, kw, _nw(c))
+
+
+def _nb(n: int) -> int:
+    return (n + 7) // 8
+
+
+def pack_rows_u8(x: torch.Tensor) -> torch.Tensor:
+    """8-bit containers: x [rows, k] -> uint8 [rows, ceil(k/8)] (bit j of byte q = x[r, 8q+j] >= 0;
+    bits past k are 0)."""
+    x = _cpu(x)
+    rows, k = x.shape
+    out = torch.empty((rows, _nb(k)), dtype=torch.uint8)
+    _load().oracle_pack_rows_u8(x.data_ptr(), _code(x), rows, k, out.data_ptr())
+    return out
+
+
+def pack_nchw_u8(x: torch.Tensor) -> torch.Tensor:
+    """8-bit containers: x [b, c, h, w] -> uint8 [b, h, w, ceil(c/8)] (channel bits past c are 0)."""
+    x = _cpu(x)
+    b, c, h, w = x.shape
+    out = torch.empty((b, h, w, _nb(c)), dtype=torch.uint8)
+    _load().oracle_pack_nchw_u8(x.data_ptr(), _code(x), b, c, h, w, out.data_ptr())
+    return out
+
+
+def pack_conv_weight_u8(w: torch.Tensor) -> torch.Tensor:
+    """8-bit containers: OIHW w [o, c, kh, kw] -> uint8 [o, kh, kw, ceil(c/8)]."""
+    w = _cpu(w)
+    o, c, kh, kw = w.shape
+    out = torch.empty((o, kh, kw, _nb(c)), dtype=torch.uint8)
+    _load().oracle_pack_conv_weight_u8(w.data_ptr(), _code(w), o, c, kh, kw, out.data_ptr())
+    return out
 
 
 def _pair(v):

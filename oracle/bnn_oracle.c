@@ -181,6 +181,64 @@ void oracle_pack_conv_weight(const void *w, int dtype, int64_t O, int64_t C, int
   oracle_pack_conv_weight2(w, dtype, O, C, ks, ks, out);
 }
 
+/* 8-bit containers. The CUTLASS conv layer keeps its packed signs in uint8_t containers
+ * (bits_binary_word = 8, BinaryConv2dCutlass.__init__ and _check_forward on the
+ * qconv/binary/cutlass/layer page); the page does not print the bit order. Reading taken here:
+ * the same order as the 32-bit words, bit j of byte b holding element 8b + j, so the four bytes
+ * of a little-endian 32-bit word are four containers in row order. A row that does not fill its
+ * last byte leaves the missing bits 0.
+ *
+ * Row-major x[rows][k] -> bytes out[rows][ceil(k/8)]. */
+void oracle_pack_rows_u8(const void *x, int dtype, int64_t rows, int64_t k, uint8_t *out) {
+  int64_t kb = (k + 7) / 8;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; r++)
+    for (int64_t q = 0; q < kb; q++) {
+      unsigned byte = 0;
+      for (int j = 0; j < 8 && 8 * q + j < k; j++)
+        if (sgn(widen(x, dtype, r * k + 8 * q + j)) > 0.0f) byte |= 1u << j;
+      out[r * kb + q] = (uint8_t)byte;
+    }
+}
+
+/* NCHW x[b][c][h][w] -> bytes out[b][h][w][ceil(C/8)]; bit j of byte q is 1 iff 8q+j < C and
+ * x[b][8q+j][h][w] >= 0. */
+void oracle_pack_nchw_u8(const void *x, int dtype, int64_t B, int64_t C, int64_t H, int64_t W,
+                         uint8_t *out) {
+  int64_t cb = (C + 7) / 8;
+#pragma omp parallel for schedule(static)
+  for (int64_t b = 0; b < B; b++)
+    for (int64_t ih = 0; ih < H; ih++)
+      for (int64_t iw = 0; iw < W; iw++)
+        for (int64_t q = 0; q < cb; q++) {
+          unsigned byte = 0;
+          for (int j = 0; j < 8 && 8 * q + j < C; j++) {
+            int64_t idx = ((b * C + 8 * q + j) * H + ih) * W + iw;
+            if (sgn(widen(x, dtype, idx)) > 0.0f) byte |= 1u << j;
+          }
+          out[((b * H + ih) * W + iw) * cb + q] = (uint8_t)byte;
+        }
+}
+
+/* OIHW weight w[o][c][i][j] of a KH x KW kernel -> bytes out[o][i][j][ceil(C/8)]; bit jj of byte
+ * q is 1 iff 8q+jj < C and w[o][8q+jj][i][j] >= 0. */
+void oracle_pack_conv_weight_u8(const void *w, int dtype, int64_t O, int64_t C, int64_t KH,
+                                int64_t KW, uint8_t *out) {
+  int64_t cb = (C + 7) / 8;
+#pragma omp parallel for schedule(static)
+  for (int64_t o = 0; o < O; o++)
+    for (int64_t i = 0; i < KH; i++)
+      for (int64_t j = 0; j < KW; j++)
+        for (int64_t q = 0; q < cb; q++) {
+          unsigned byte = 0;
+          for (int jj = 0; jj < 8 && 8 * q + jj < C; jj++) {
+            int64_t idx = ((o * C + 8 * q + jj) * KH + i) * KW + j;
+            if (sgn(widen(w, dtype, idx)) > 0.0f) byte |= 1u << jj;
+          }
+          out[((o * KH + i) * KW + j) * cb + q] = (uint8_t)byte;
+        }
+}
+
 /* Linear accumulators. acc[i][n] = sum_k sgn(x[m_i][k]) * sgn(W[n][k]) for the selected rows
  * m_i = rows[i] (all M rows in order when rows == NULL, nrows then ignored). Returns 0, or -1
  * when K is too long for the exact float accumulation or memory runs out. */

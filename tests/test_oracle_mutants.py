@@ -83,6 +83,13 @@ MUTANTS = {
     "bwd_conv_pad_added": ("int64_t ih = oh * sh - ph + i * dh, iw = ow * sw - pw + j * dw;\n                if (ih < 0 || ih >= H || iw < 0 || iw >= W) continue;\n                int64_t xi",
                            "int64_t ih = oh * sh + ph + i * dh, iw = ow * sw - pw + j * dw;\n                if (ih < 0 || ih >= H || iw < 0 || iw >= W) continue;\n                int64_t xi"),
     "bwd_conv_kernel_transposed": ("wi = ((o * C + c) * KH + i) * KW + j;", "wi = ((o * C + c) * KW + j) * KH + i;"),
+    "u8_bit_order_reversed": ("if (sgn(widen(x, dtype, r * k + 8 * q + j)) > 0.0f) byte |= 1u << j;",
+                              "if (sgn(widen(x, dtype, r * k + 8 * q + j)) > 0.0f) byte |= 1u << (7 - j);"),
+    "u8_nchw_hw_swapped": ("int64_t idx = ((b * C + 8 * q + j) * H + ih) * W + iw;",
+                           "int64_t idx = ((b * C + 8 * q + j) * W + iw) * H + ih;"),
+    "u8_weight_kernel_transposed": ("int64_t idx = ((o * C + 8 * q + jj) * KH + i) * KW + j;",
+                                    "int64_t idx = ((o * C + 8 * q + jj) * KW + j) * KH + i;"),
+    "u8_nibble_container": ("      out[r * kb + q] = (uint8_t)byte;", "      out[r * kb + q] = (uint8_t)(byte & 0x0f);"),
     "bwd_conv_weight_grad_unsigned": ("grad_w[wi] += gv * (sign0(widen(x, xdt, xi)) * (double)scale_a);",
                                       "grad_w[wi] += gv * ((double)widen(x, xdt, xi) * (double)scale_a);"),
 }
@@ -95,7 +102,7 @@ def _golden(name):
 
 def _num(v):
     if isinstance(v, str):
-        return {"-0": -0.0, "nan": float("nan"), "-inf": float("-inf")}[v]
+        return {"-0": -0.0, "nan": float("nan"), "-inf": float("-inf"), "inf": float("inf")}[v]
     return float(v)
 
 
@@ -278,6 +285,40 @@ def _pins(orc):
                 and orc.abs_mean_scale(torch.tensor([0.5, -2.5]), 2.0) == 3.0)
 
     check("abs_mean_closed_forms", abs_mean)
+
+    u8 = _golden("u8_container.json")
+
+    def u8_golden():
+        for row in u8["rows"]:
+            got = orc.pack_rows_u8(_tensor([row["x"]]))[0].tolist()
+            if got != [int(h, 16) for h in row["bytes"]]:
+                return False
+        nc = u8["nchw"]
+        x = torch.stack([_tensor(nc["pixel0"]), _tensor(nc["pixel1"])], dim=1).view(1, 10, 1, 2).contiguous()
+        got = orc.pack_nchw_u8(x)
+        return (got[0, 0, 0].tolist() == [int(h, 16) for h in nc["bytes0"]]
+                and got[0, 0, 1].tolist() == [int(h, 16) for h in nc["bytes1"]])
+
+    check("u8_golden", u8_golden)
+
+    def u8_vs_torch():
+        gen = torch.Generator().manual_seed(35)
+
+        def bits(t, n):
+            return np.unpackbits(t.numpy(), axis=-1, bitorder="little")[..., :n]
+
+        x = torch.randn((5, 70), generator=gen)
+        if not np.array_equal(bits(orc.pack_rows_u8(x), 70), (x >= 0).numpy()):
+            return False
+        if np.unpackbits(orc.pack_rows_u8(x).numpy(), axis=-1, bitorder="little")[:, 70:].any():
+            return False
+        xn = torch.randn((2, 20, 3, 4), generator=gen)
+        if not np.array_equal(bits(orc.pack_nchw_u8(xn), 20), (xn >= 0).permute(0, 2, 3, 1).numpy()):
+            return False
+        wc = torch.randn((3, 12, 2, 3), generator=gen)
+        return np.array_equal(bits(orc.pack_conv_weight_u8(wc), 12), (wc >= 0).permute(0, 2, 3, 1).numpy())
+
+    check("u8_vs_torch", u8_vs_torch)
     for name, pin in BACKWARD_PINS.items():
         check(name, lambda pin=pin: pin(orc))
     return failed
