@@ -32,14 +32,14 @@ LIB_PATH = os.environ.get("BNN_LIBRARY") or os.path.join(_PKG, "libbnn.so")
 NOALLOC_SCRATCH_BYTES = 32 << 20
 
 # bnn_dtype / bnn_path / bnn_status codes of include/bnn.h
-F32, F16, BF16, I32, U32_PACKED = 0, 1, 2, 3, 4
+F32, F16, BF16, I32, U32_PACKED, U8_PACKED = 0, 1, 2, 3, 4, 5
 PATH_AUTO, PATH_XOR, PATH_MFMA, PATH_MFMA_FP4 = 0, 1, 2, 3
 OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIGN, ERR_WORKSPACE, ERR_PATH, ERR_HIP = range(8)
 
 EXPORTS = ("bnn_pack_sign", "bnn_pack_sign_nchw", "bnn_pack_sign_shift", "bnn_pack_sign_nchw_shift",
            "bnn_abs_mean_scale", "bnn_abs_mean_workspace_bytes", "bnn_w_pack", "bnn_w_pack_conv",
            "bnn_conv2d_ex", "bnn_quant_i8_nhwc", "bnn_quant_i8_weight", "bnn_w8a8_conv2d", "bnn_gemm", "bnn_conv2d",
-           "bnn_gemm_noalloc", "bnn_gemm_workspace_bytes", "bnn_conv2d_workspace_bytes", "bnn_gemm_auto_path",
+           "bnn_gemm_noalloc", "bnn_u8_to_words", "bnn_gemm_workspace_bytes", "bnn_conv2d_workspace_bytes", "bnn_gemm_auto_path",
            "bnn_conv2d_auto_path", "bnn_last_path", "bnn_status_string",
            "bnn_linear_grad_input", "bnn_linear_grad_input_workspace_bytes", "bnn_linear_grad_weight",
            "bnn_linear_grad_weight_i8", "bnn_linear_grad_weight_i8_workspace_bytes",
@@ -76,6 +76,7 @@ def _bind(path: str) -> ctypes.CDLL:
         "bnn_conv2d_ex": ([P, I, I64, I64, I64, I64, P, I64, D, D] + [I] * 9 + [P, I, P, SZ, P], I),
         "bnn_gemm": ([P, I, P, I64, I64, I64, D, D, I, P, I, P, SZ, P], I),
         "bnn_gemm_noalloc": ([P, I, P, I64, I64, I64, D, D, I, P, I, P], I),
+        "bnn_u8_to_words": ([P, I64, I64, P, P], I),
         "bnn_conv2d": ([P, I, I64, I64, I64, I64, P, I64, D, D, I, I, I, I, I, P, I, P, SZ, P], I),
         "bnn_gemm_workspace_bytes": ([I64, I64, I], SZ),
         "bnn_conv2d_workspace_bytes": ([I64, I64, I64, I64, I], SZ),
@@ -141,15 +142,23 @@ _OUT_DTYPES = (torch.float32, torch.float16, torch.bfloat16, torch.int32)
 
 
 def _packed_len(x: torch.Tensor, n: int | None, what: str) -> int:
-    """Sign count of a packed int32 tensor whose last axis holds the words: n when given (it
-    must need exactly that many words), else 32 per word."""
+    """Sign count of a packed tensor whose last axis holds the containers (int32 words of 32
+    signs, or uint8 bytes of 8): n when given (it must need exactly that many containers), else
+    32 or 8 per container."""
+    per = 32 if x.dtype == torch.int32 else 8
     cw = x.shape[-1]
     if n is None:
-        return 32 * cw
+        return per * cw
     n = int(n)
-    if n < 1 or words(n) != cw:
-        raise ValueError(f"{what} = {n} needs {words(max(n, 1))} packed words, x holds {cw}")
+    if n < 1 or (n + per - 1) // per != cw:
+        raise ValueError(f"{what} = {n} needs {(max(n, 1) + per - 1) // per} packed containers of "
+                         f"{per} signs, x holds {cw}")
     return n
+
+
+def _packed_code(x: torch.Tensor):
+    """U32_PACKED for int32 words, U8_PACKED for uint8 containers, None for float input."""
+    return {torch.int32: U32_PACKED, torch.uint8: U8_PACKED}.get(x.dtype)
 
 
 def _same_device(name: str, t: torch.Tensor, ref: torch.Tensor):
@@ -305,6 +314,26 @@ def w_pack(weight: torch.Tensor) -> torch.Tensor:
     return out
 
 
+def u8_to_words(src: torch.Tensor, bits: int | None = None,
+                out: torch.Tensor | None = None) -> torch.Tensor:
+    """8-bit sign containers [..., ceil(bits/8)] uint8 (the CUTLASS layer's container type) ->
+    int32 words [..., ceil(bits/32)] with the bits past `bits` cleared; bits defaults to 8 per
+    byte. Serves weights ([o, kh, kw, ceil(c/8)] -> w_packed) and activations alike."""
+    src = _dev(src, "src")
+    if src.dtype != torch.uint8 or src.dim() < 1:
+        raise TypeError("src must be a uint8 tensor whose last axis holds the containers")
+    bits = _packed_len(src, bits, "bits")
+    rows = src.numel() // src.shape[-1] if src.shape[-1] else 0
+    if out is None:
+        out = torch.empty((*src.shape[:-1], words(bits)), dtype=torch.int32, device=src.device)
+    else:
+        _expect(out, "out", torch.int32, (*src.shape[:-1], words(bits)))
+        _same_device("out", out, src)
+    _check(lib.bnn_u8_to_words(src.data_ptr(), rows, bits, out.data_ptr(), _stream(src)),
+           "bnn_u8_to_words")
+    return out
+
+
 def _workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
@@ -318,9 +347,9 @@ def gemm(x: torch.Tensor, w_packed: torch.Tensor, scale_a: float, scale_w: float
          workspace: torch.Tensor | None = None) -> torch.Tensor:
     """Binary linear forward: out = scale_a*scale_w * sgn(x) @ sgn(W)^T.
 
-    x is [m, k] float (packed here) or int32 [m, ceil(k/32)] already packed (then k
-    defaults to 32 * x.shape[1]; pass k when it is not a multiple of 32). w_packed is
-    int32 [n, ceil(k/32)] from w_pack.
+    x is [m, k] float (packed here), int32 [m, ceil(k/32)] already packed (then k defaults to
+    32 * x.shape[1]; pass k when it is not a multiple of 32), or uint8 [m, ceil(k/8)] 8-bit
+    containers (k defaults to 8 * x.shape[1]). w_packed is int32 [n, ceil(k/32)] from w_pack.
     out_dtype defaults to x's dtype (float32 for packed x); torch.int32 gives
     the raw accumulators.
     """
@@ -329,11 +358,11 @@ def gemm(x: torch.Tensor, w_packed: torch.Tensor, scale_a: float, scale_w: float
     _same_device("w_packed", w_packed, x)
     if x.dim() != 2:
         raise ValueError(f"x must be 2-D [m, k] (or packed [m, words]), got {x.dim()}-D")
-    packed = x.dtype == torch.int32
+    packed = _packed_code(x) is not None
     m = x.shape[0]
     if packed:
         k = _packed_len(x, k, "k")
-        xcode = U32_PACKED
+        xcode = _packed_code(x)
     else:
         k = x.shape[1]
         xcode = _dtype_code(x, "x")
@@ -373,10 +402,10 @@ def gemm_noalloc(x: torch.Tensor, w_packed: torch.Tensor, scale_a: float, scale_
     _same_device("w_packed", w_packed, x)
     if x.dim() != 2 or w_packed.dim() != 2:
         raise ValueError("x and w_packed must be 2-D")
-    packed = x.dtype == torch.int32
+    packed = _packed_code(x) is not None
     m = x.shape[0]
     k = _packed_len(x, k, "k") if packed else x.shape[1]
-    xcode = U32_PACKED if packed else _dtype_code(x, "x")
+    xcode = _packed_code(x) if packed else _dtype_code(x, "x")
     n = w_packed.shape[0]
     _expect(w_packed, "w_packed", torch.int32, (n, words(k)))
     _expect(out, "out", _OUT_DTYPES, (m, n))
@@ -401,8 +430,9 @@ def conv2d(x: torch.Tensor, w_packed: torch.Tensor, scale_a: float, scale_w: flo
            workspace: torch.Tensor | None = None) -> torch.Tensor:
     """Binary conv2d forward, NCHW in and out; padded taps contribute 0.
 
-    x is [n, c, h, w] float, or int32 [n, h, w, ceil(c/32)] already packed by
-    pack_sign_nchw. w_packed is int32 [o, kh, kw, ceil(c/32)] from w_pack. kernel_size,
+    x is [n, c, h, w] float, int32 [n, h, w, ceil(c/32)] already packed by pack_sign_nchw, or
+    uint8 [n, h, w, ceil(c/8)] 8-bit containers (pass channels when c is not a multiple of the
+    container width). w_packed is int32 [o, kh, kw, ceil(c/32)] from w_pack. kernel_size,
     stride, padding and dilation are ints (bnn_conv2d) or (rows, columns) pairs
     (bnn_conv2d_ex).
     """
@@ -411,11 +441,11 @@ def conv2d(x: torch.Tensor, w_packed: torch.Tensor, scale_a: float, scale_w: flo
     _same_device("w_packed", w_packed, x)
     if x.dim() != 4:
         raise ValueError(f"x must be 4-D (NCHW float or packed [n, h, w, words]), got {x.dim()}-D")
-    packed = x.dtype == torch.int32
+    packed = _packed_code(x) is not None
     if packed:
         n, h, w, cw = x.shape
         c = _packed_len(x, channels, "channels")
-        xcode = U32_PACKED
+        xcode = _packed_code(x)
     else:
         n, c, h, w = x.shape
         xcode = _dtype_code(x, "x")

@@ -20,6 +20,11 @@ namespace {
 thread_local int g_last_path = 0;
 
 bool float_dtype(int d) { return d == BNN_F32 || d == BNN_F16 || d == BNN_BF16; }
+// Already-packed activations: 32-bit words, or the CUTLASS layer's 8-bit containers.
+bool packed_dtype(int d) { return d == BNN_U32_PACKED || d == BNN_U8_PACKED; }
+// 8-bit containers of a whole number of 32-bit words are those words byte for byte and are
+// read in place; other lengths are repacked into the workspace.
+bool u8_in_place(int x_dtype, int64_t bits) { return x_dtype == BNN_U8_PACKED && bits % 32 == 0; }
 bool half_dtype(int d) { return d == BNN_F16 || d == BNN_BF16; }
 bool out_dtype_ok(int d) { return float_dtype(d) || d == BNN_I32; }
 int elem_bytes(int d) { return d == BNN_F32 ? 4 : 2; }
@@ -137,13 +142,24 @@ const char* bnn_status_string(int s) {
 int bnn_last_path(void) { return g_last_path; }
 
 size_t bnn_gemm_workspace_bytes(int64_t m, int64_t k, int x_dtype) {
-  if (x_dtype == BNN_U32_PACKED || m <= 0 || k <= 0) return 0;
+  if (x_dtype == BNN_U32_PACKED || u8_in_place(x_dtype, k) || m <= 0 || k <= 0) return 0;
   return (size_t)m * (size_t)words_of(k) * 4u;
 }
 
 size_t bnn_conv2d_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w, int x_dtype) {
-  if (x_dtype == BNN_U32_PACKED || n <= 0 || c <= 0 || h <= 0 || w <= 0) return 0;
+  if (x_dtype == BNN_U32_PACKED || u8_in_place(x_dtype, c) || n <= 0 || c <= 0 || h <= 0 || w <= 0)
+    return 0;
   return (size_t)n * (size_t)h * (size_t)w * (size_t)words_of(c) * 4u;
+}
+
+bnn_status bnn_u8_to_words(const uint8_t* src, int64_t rows, int64_t bits, uint32_t* dst,
+                           void* stream) {
+  if (rows < 0 || bits < 1 || !bits_fit(bits)) return BNN_ERR_SHAPE;
+  if (!int_fits(rows) || !int_fits(words_of(bits)) || rows * words_of(bits) < 0) return BNN_ERR_SHAPE;
+  if (rows == 0) return BNN_OK;
+  if (!src || !dst) return BNN_ERR_NULL;
+  if (!aligned(dst, 4)) return BNN_ERR_ALIGN;
+  return hip_status(bnn::launch_u8_to_words(src, rows, bits, dst, static_cast<hipStream_t>(stream)));
 }
 
 int bnn_gemm_auto_path(int64_t m, int64_t n, int64_t k) {
@@ -286,7 +302,7 @@ bnn_status bnn_conv2d_ex(const void* x, int x_dtype, int64_t n, int64_t c, int64
                          double scale_w, int kernel_h, int kernel_w, int stride_h, int stride_w,
                          int pad_h, int pad_w, int dil_h, int dil_w, int path, void* out,
                          int out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  if (!(float_dtype(x_dtype) || x_dtype == BNN_U32_PACKED) || !out_dtype_ok(out_dtype))
+  if (!(float_dtype(x_dtype) || packed_dtype(x_dtype)) || !out_dtype_ok(out_dtype))
     return BNN_ERR_DTYPE;
   if (n < 0 || out_channels < 0 || c <= 0 || h <= 0 || w <= 0) return BNN_ERR_SHAPE;
   if (kernel_h < 1 || kernel_w < 1 || stride_h < 1 || stride_w < 1 || dil_h < 1 || dil_w < 1 ||
@@ -306,9 +322,9 @@ bnn_status bnn_conv2d_ex(const void* x, int x_dtype, int64_t n, int64_t c, int64
   if (path == BNN_PATH_MFMA_FP4 && taps * c > bnn::kMaxFp4K) return BNN_ERR_PATH;
   if (n == 0 || out_channels == 0) return BNN_OK;
   if (!x || !w_packed || !out) return BNN_ERR_NULL;
-  const bool packed = x_dtype == BNN_U32_PACKED;
-  if (!aligned(x, packed ? 4 : 16) || !aligned(w_packed, 4) || !aligned(out, 16))
-    return BNN_ERR_ALIGN;
+  const bool words_in = x_dtype == BNN_U32_PACKED || u8_in_place(x_dtype, c);
+  const int x_align = words_in ? 4 : x_dtype == BNN_U8_PACKED ? 1 : 16;
+  if (!aligned(x, x_align) || !aligned(w_packed, 4) || !aligned(out, 16)) return BNN_ERR_ALIGN;
   const size_t need = bnn_conv2d_workspace_bytes(n, c, h, w, x_dtype);
   if (need > 0 && (!workspace || workspace_bytes < need)) return BNN_ERR_WORKSPACE;
   if (need > 0 && !aligned(workspace, 4)) return BNN_ERR_ALIGN;
@@ -316,9 +332,12 @@ bnn_status bnn_conv2d_ex(const void* x, int x_dtype, int64_t n, int64_t c, int64
   const int use = path == BNN_PATH_AUTO ? auto_path(taps * c) : path;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const uint32_t* a = static_cast<const uint32_t*>(x);
-  if (!packed) {
+  if (!words_in) {
     uint32_t* ws = static_cast<uint32_t*>(workspace);
-    const hipError_t e = bnn::launch_pack_nchw(x, x_dtype, n, c, h, w, ws, s);
+    const hipError_t e =
+        x_dtype == BNN_U8_PACKED
+            ? bnn::launch_u8_to_words(static_cast<const uint8_t*>(x), n * h * w, c, ws, s)
+            : bnn::launch_pack_nchw(x, x_dtype, n, c, h, w, ws, s);
     if (e != hipSuccess) return BNN_ERR_HIP;
     a = ws;
   }
@@ -510,7 +529,7 @@ bnn_status gemm_impl(const void* x, int x_dtype, const uint32_t* w_packed, int64
                      int64_t k, double scale_a, double scale_w, int path, void* out,
                      int out_dtype, void* workspace, size_t workspace_bytes, bool use_scratch,
                      void* stream) {
-  if (!(float_dtype(x_dtype) || x_dtype == BNN_U32_PACKED) || !out_dtype_ok(out_dtype))
+  if (!(float_dtype(x_dtype) || packed_dtype(x_dtype)) || !out_dtype_ok(out_dtype))
     return BNN_ERR_DTYPE;
   if (m < 0 || n < 0 || k < 1) return BNN_ERR_SHAPE;
   if (!int_fits(m) || !int_fits(n) || !bits_fit(k)) return BNN_ERR_SHAPE;
@@ -518,9 +537,9 @@ bnn_status gemm_impl(const void* x, int x_dtype, const uint32_t* w_packed, int64
   if (path == BNN_PATH_MFMA_FP4 && k > bnn::kMaxFp4K) return BNN_ERR_PATH;
   if (m == 0 || n == 0) return BNN_OK;
   if (!x || !w_packed || !out) return BNN_ERR_NULL;
-  const bool packed = x_dtype == BNN_U32_PACKED;
-  if (!aligned(x, packed ? 4 : elem_bytes(x_dtype)) || !aligned(w_packed, 4) || !aligned(out, 16))
-    return BNN_ERR_ALIGN;
+  const bool words_in = x_dtype == BNN_U32_PACKED || u8_in_place(x_dtype, k);
+  const int x_align = words_in ? 4 : x_dtype == BNN_U8_PACKED ? 1 : elem_bytes(x_dtype);
+  if (!aligned(x, x_align) || !aligned(w_packed, 4) || !aligned(out, 16)) return BNN_ERR_ALIGN;
   const size_t need = bnn_gemm_workspace_bytes(m, k, x_dtype);
   if (use_scratch) {
     // every argument is checked by now; resolving the scratch address enqueues nothing
@@ -537,9 +556,12 @@ bnn_status gemm_impl(const void* x, int x_dtype, const uint32_t* w_packed, int64
   const int use = path == BNN_PATH_AUTO ? auto_path(k) : path;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const uint32_t* a = static_cast<const uint32_t*>(x);
-  if (!packed) {
+  if (!words_in) {
     uint32_t* ws = static_cast<uint32_t*>(workspace);
-    const hipError_t e = pack_rows_any(x, x_dtype, m, k, nullptr, 0, false, ws, s);
+    const hipError_t e =
+        x_dtype == BNN_U8_PACKED
+            ? bnn::launch_u8_to_words(static_cast<const uint8_t*>(x), m, k, ws, s)
+            : pack_rows_any(x, x_dtype, m, k, nullptr, 0, false, ws, s);
     if (e != hipSuccess) return BNN_ERR_HIP;
     a = ws;
   }

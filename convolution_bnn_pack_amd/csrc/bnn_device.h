@@ -9,7 +9,7 @@
 namespace bnn {
 
 // Element / output type codes (numerically equal to include/bnn.h's bnn_dtype).
-enum : int { kF32 = 0, kF16 = 1, kBF16 = 2, kI32 = 3, kPacked = 4 };
+enum : int { kF32 = 0, kF16 = 1, kBF16 = 2, kI32 = 3, kPacked = 4, kPackedU8 = 5 };
 
 // Sign bit of one element, from its raw IEEE bits: 1 when the value is >= 0
 // (+0, -0, positive numbers, +inf), 0 otherwise (negative numbers, -inf, any

@@ -42,6 +42,11 @@ hipError_t launch_abs_mean(const void* x, int dtype, int64_t count, double facto
 hipError_t launch_pack_conv_weight(const void* w, int dtype, int64_t o, int64_t c, int kh, int kw,
                                    uint32_t* out, hipStream_t stream);
 
+// 8-bit sign containers [rows][ceil(bits/8)] bytes -> words [rows][ceil(bits/32)] (little-endian
+// byte order, bits at or past `bits` cleared).
+hipError_t launch_u8_to_words(const uint8_t* src, int64_t rows, int64_t bits, uint32_t* dst,
+                              hipStream_t stream);
+
 // XOR + popcount contraction on the vector ALUs.
 hipError_t launch_xor(const Contraction& p, bool conv, int out_dtype, hipStream_t stream);
 

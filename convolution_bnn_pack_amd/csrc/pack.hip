@@ -703,4 +703,45 @@ hipError_t launch_pack_conv_weight(const void* w, int dtype, int64_t o, int64_t 
   return hipGetLastError();
 }
 
+namespace {
+
+// 8-bit containers -> 32-bit words. Row r of src holds ceil(bits/8) bytes, bit j of byte q
+// being sign 8q + j; row r of dst gets ceil(bits/32) words, word q = bytes 4q .. 4q + 3 in
+// little-endian order (bytes past the row read as 0), and bits at or past `bits` in the last
+// word are cleared, so a container whose unused high bits are not zero still gives words with
+// the zero tail the contraction relies on. One thread per output word.
+__global__ __launch_bounds__(256) void u8_to_words_kernel(const uint8_t* __restrict__ src,
+                                                          uint32_t* __restrict__ dst,
+                                                          int64_t total, int64_t nbytes,
+                                                          int64_t nwords, uint32_t last_mask) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / nwords, q = i - r * nwords;
+    const uint8_t* row = src + r * nbytes;
+    uint32_t w = 0;
+#pragma unroll
+    for (int b = 0; b < 4; b++) {
+      const int64_t at = 4 * q + b;
+      if (at < nbytes) w |= (uint32_t)row[at] << (8 * b);
+    }
+    if (q == nwords - 1) w &= last_mask;
+    dst[i] = w;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_u8_to_words(const uint8_t* src, int64_t rows, int64_t bits, uint32_t* dst,
+                              hipStream_t stream) {
+  const int64_t nbytes = (bits + 7) / 8, nwords = (bits + 31) / 32;
+  const int64_t total = rows * nwords;
+  if (total == 0) return hipSuccess;
+  const uint32_t last_mask = bits % 32 == 0 ? 0xFFFFFFFFu : (1u << (bits % 32)) - 1u;
+  const int64_t blocks = (total + 255) / 256;
+  const dim3 grid((unsigned)(blocks < 65536 ? blocks : 65536)), block(256);
+  hipLaunchKernelGGL(u8_to_words_kernel, grid, block, 0, stream, src, dst, total, nbytes, nwords,
+                     last_mask);
+  return hipGetLastError();
+}
+
 }  // namespace bnn

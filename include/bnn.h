@@ -70,7 +70,14 @@ typedef enum {
   BNN_F16 = 1,
   BNN_BF16 = 2,
   BNN_I32 = 3,        /* output only: the raw integer accumulators, unscaled */
-  BNN_U32_PACKED = 4  /* input only: activations already packed by bnn_pack_sign / bnn_pack_sign_nchw */
+  BNN_U32_PACKED = 4, /* input only: activations already packed by bnn_pack_sign / bnn_pack_sign_nchw */
+  BNN_U8_PACKED = 5   /* input only: activations packed in 8-bit containers, the container type of the
+                         CUTLASS conv layer (bits_binary_word = 8; BinaryConv2dCutlass.__init__ and
+                         _check_forward on the qconv/binary/cutlass/layer page): a row (linear) or a
+                         pixel (conv) is ceil(n/8) bytes, bit j of byte q = sign 8q + j (1 for +1),
+                         bits past n 0 or ignored; n = k or c. With n % 32 == 0 the bytes are read in
+                         place as 32-bit words (4-byte alignment needed, no workspace); otherwise
+                         they are repacked into the workspace first. */
 } bnn_dtype;
 
 /* Kernel choice; mirrors the layers' bmm_type argument (BMM.ADAPTIVE is the default there). */
@@ -91,6 +98,17 @@ typedef enum {
  * k >= 1; rows == 0 is a no-op. */
 bnn_status bnn_pack_sign(const void* x, int x_dtype, int64_t rows, int64_t k,
                          uint32_t* x_packed, void* stream);
+
+/* 8-bit containers -> 32-bit words (weights or activations packed for the CUTLASS layer, whose
+ * container type is uint8_t: BinaryConv2dCutlass.__init__ on the qconv/binary/cutlass/layer page).
+ *   src  [rows, ceil(bits/8)] bytes, bit j of byte q = sign 8q + j; any alignment.
+ *   dst  [rows, ceil(bits/32)] uint32 out, 4-byte aligned; word q = bytes 4q..4q+3 little-endian
+ *        (bytes past the row read as 0) with the bits at or past `bits` cleared, so the words carry
+ *        the zero tail the contractions expect even when the containers' unused bits are not 0.
+ * Conv weights [o, kh, kw, ceil(c/8)] are rows = o*kh*kw, bits = c; NHWC activations rows =
+ * n*h*w, bits = c; linear rows have bits = k. bits >= 1; rows == 0 is a no-op. */
+bnn_status bnn_u8_to_words(const uint8_t* src, int64_t rows, int64_t bits, uint32_t* dst,
+                           void* stream);
 
 /* Sign + pack of NCHW activations along channels.
  *   x        [n, c, h, w] in x_dtype (BNN_F32/F16/BF16), 16-byte aligned.
@@ -149,7 +167,8 @@ bnn_status bnn_w_pack(const void* weight, int w_dtype, int64_t out_features, int
 
 /* Binary linear forward: out[m][n] = scale_a * scale_w * sum_k sgn(x[m][k]) * sgn(W[n][k]).
  *   x         [m, k] in BNN_F32/F16/BF16 (packed here into the workspace), or
- *             [m, ceil(k/32)] BNN_U32_PACKED (already packed, bits past k 0; no workspace needed).
+ *             [m, ceil(k/32)] BNN_U32_PACKED (already packed, bits past k 0; no workspace needed),
+ *             or [m, ceil(k/8)] bytes BNN_U8_PACKED (8-bit containers, see bnn_dtype).
  *   w_packed  [n, ceil(k/32)] from bnn_w_pack(kernel_size = 0).
  *   out       [m, n] in out_dtype: BNN_F32/F16/BF16 (scaled) or BNN_I32 (raw accumulators).
  *   path      a bnn_path value.
@@ -165,8 +184,9 @@ bnn_status bnn_gemm(const void* x, int x_dtype, const uint32_t* w_packed, int64_
  * activations are packed into a static device array of BNN_NOALLOC_SCRATCH_BYTES bytes that
  * the library holds on every device it runs on until the process ends; the call itself
  * allocates and frees nothing. Arguments, layouts, results and errors as bnn_gemm, plus:
- *   - m * ceil(k/32) * 4 > BNN_NOALLOC_SCRATCH_BYTES (float x) -> BNN_ERR_WORKSPACE, nothing
- *     enqueued; packed x (BNN_U32_PACKED) needs no scratch and has no such limit;
+ *   - m * ceil(k/32) * 4 > BNN_NOALLOC_SCRATCH_BYTES when x needs packing (float x, or 8-bit
+ *     containers with k % 32 != 0) -> BNN_ERR_WORKSPACE, nothing enqueued; x already in words
+ *     (BNN_U32_PACKED, or BNN_U8_PACKED with k % 32 == 0) needs no scratch and has no limit;
  *   - the array belongs to the current device, which must be the device of `stream`; its
  *     address is looked up on the first call on each device (BNN_ERR_HIP if that fails);
  *   - every call on a device shares that device's array and it keeps the last call's
@@ -178,7 +198,8 @@ bnn_status bnn_gemm_noalloc(const void* x, int x_dtype, const uint32_t* w_packed
                             void* out, int out_dtype, void* stream);
 
 /* Binary conv2d forward (square kernel, symmetric stride/padding/dilation).
- *   x         NCHW [n, c, h, w] in BNN_F32/F16/BF16, or [n, h, w, ceil(c/32)] BNN_U32_PACKED.
+ *   x         NCHW [n, c, h, w] in BNN_F32/F16/BF16, or [n, h, w, ceil(c/32)] BNN_U32_PACKED, or
+ *             [n, h, w, ceil(c/8)] bytes BNN_U8_PACKED (8-bit containers, see bnn_dtype).
  *   w_packed  [out_channels, k, k, ceil(c/32)] from bnn_w_pack(kernel_size = k).
  *   out       NCHW [n, out_channels, Ho, Wo] in out_dtype (BNN_F32/F16/BF16/I32),
  *             Ho = floor((h + 2*padding - dilation*(k-1) - 1)/stride + 1), likewise Wo.

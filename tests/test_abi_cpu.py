@@ -90,6 +90,28 @@ def test_gemm_argument_checks(bnn):
     assert _gemm(bnn, k=(1 << 31) - 32, path=bnn.PATH_MFMA, x=None) == bnn.ERR_NULL
 
 
+def test_u8_container_argument_checks(bnn):
+    # 8-bit containers: any alignment when they are repacked (k % 32 != 0), 4 bytes when the
+    # bytes are read in place as words (k % 32 == 0, no workspace needed)
+    assert _gemm(bnn, x_dtype=bnn.U8_PACKED, k=40, x=FAKE + 1, w=None) == bnn.ERR_NULL
+    assert _gemm(bnn, x_dtype=bnn.U8_PACKED, k=64, x=FAKE + 1) == bnn.ERR_ALIGN
+    assert _gemm(bnn, x_dtype=bnn.U8_PACKED, k=64, x=FAKE + 4, ws=None, w=None) == bnn.ERR_NULL
+    assert _gemm(bnn, x_dtype=bnn.U8_PACKED, k=40, ws=None) == bnn.ERR_WORKSPACE
+    assert bnn.lib.bnn_gemm_workspace_bytes(64, 40, bnn.U8_PACKED) == 64 * 2 * 4
+    assert bnn.lib.bnn_gemm_workspace_bytes(64, 64, bnn.U8_PACKED) == 0
+    assert bnn.lib.bnn_conv2d_workspace_bytes(2, 40, 5, 5, bnn.U8_PACKED) == 2 * 5 * 5 * 2 * 4
+    assert bnn.lib.bnn_conv2d_workspace_bytes(2, 96, 5, 5, bnn.U8_PACKED) == 0
+    assert _conv(bnn, x_dtype=bnn.U8_PACKED, c=40, x=FAKE + 3, wp=None) == bnn.ERR_NULL
+    assert _conv(bnn, x_dtype=bnn.U8_PACKED, c=64, x=FAKE + 2) == bnn.ERR_ALIGN
+    assert _conv(bnn, x_dtype=bnn.U8_PACKED, c=40, ws=None) == bnn.ERR_WORKSPACE
+    u8 = bnn.lib.bnn_u8_to_words
+    assert u8(FAKE, 4, 0, FAKE, None) == bnn.ERR_SHAPE
+    assert u8(FAKE, -1, 8, FAKE, None) == bnn.ERR_SHAPE
+    assert u8(FAKE, 0, 8, None, None) == bnn.OK
+    assert u8(None, 4, 8, FAKE, None) == bnn.ERR_NULL
+    assert u8(FAKE + 1, 4, 8, FAKE + 2, None) == bnn.ERR_ALIGN
+
+
 def _conv(bnn, **kw):
     a = dict(x=FAKE, x_dtype=bnn.F32, n=2, c=64, h=14, w=14, wp=FAKE, o=32, sa=1.0, sw=1.0, ks=3,
              s=1, p=1, d=1, path=bnn.PATH_AUTO, out=FAKE, out_dtype=bnn.F32, ws=FAKE,

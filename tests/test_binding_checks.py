@@ -56,6 +56,8 @@ def test_gemm_rejects_mismatched_tensors(bnn):
         bnn.gemm(_z(m, 3, dtype=I32), wp, 1.0, 1.0, k=k)
     with pytest.raises(_Launched):
         bnn.gemm(x, wp, 1.0, 1.0, out=_z(m, n, dtype=torch.float16))
+    with pytest.raises(_Launched):
+        bnn.gemm(_z(m, 9, dtype=torch.uint8), wp, 1.0, 1.0, k=k)
     bad = [
         dict(w_packed=_z(n, 2, dtype=I32)),                 # too few words for k
         dict(w_packed=_z(n, 4, dtype=I32)),                 # too many
@@ -69,6 +71,8 @@ def test_gemm_rejects_mismatched_tensors(bnn):
         dict(x=_z(m, 3, dtype=I32), k=100),                 # k needs 4 words
         dict(x=_z(m, 3, dtype=I32), k=0),
         dict(x=_z(2, m, k)),                                # 3-D activations
+        dict(x=_z(m, 8, dtype=torch.uint8), k=k),           # 8-bit containers: 9 bytes needed
+        dict(x=_z(m, 9, dtype=torch.uint8), k=64),
         dict(out_dtype=torch.float64),
     ]
     for case in bad:
@@ -85,6 +89,8 @@ def test_conv2d_rejects_mismatched_tensors(bnn):
         bnn.conv2d(x, wp, 1.0, 1.0, 3, 1, 1, 1)
     with pytest.raises(_Launched):
         bnn.conv2d(_z(n, h, w, 2, dtype=I32), wp, 1.0, 1.0, 3, 1, 1, 1, channels=c)
+    with pytest.raises(_Launched):
+        bnn.conv2d(_z(n, h, w, 5, dtype=torch.uint8), wp, 1.0, 1.0, 3, 1, 1, 1, channels=c)
     with pytest.raises(_Launched):       # rectangular kernel through the general entry point
         bnn.conv2d(x, _z(o, 1, 3, 2, dtype=I32), 1.0, 1.0, (1, 3), 1, (0, 1), 1)
     bad = [
@@ -99,6 +105,7 @@ def test_conv2d_rejects_mismatched_tensors(bnn):
         dict(x=_z(n, h, w, 1, dtype=I32), channels=c),      # packed x too short
         dict(x=_z(n, h, w, 2, dtype=I32), channels=65),     # needs 3 words
         dict(x=_z(n, c, h)),                                # 3-D
+        dict(x=_z(n, h, w, 4, dtype=torch.uint8), channels=c),   # 5 bytes per pixel needed
         dict(out_dtype=torch.uint8),
     ]
     for case in bad:
