@@ -363,6 +363,10 @@ bnn_status bnn_conv2d_ex(const void* x, int x_dtype, int64_t n, int64_t c, int64
   p.PW = pad_w;
   p.DH = dil_h;
   p.DW = dil_w;
+  p.div_hw = bnn::FastDiv((uint32_t)(ho * wo));
+  p.div_wo = bnn::FastDiv((uint32_t)wo);
+  p.div_cw = bnn::FastDiv((uint32_t)p.CW);
+  p.div_kwd = bnn::FastDiv((uint32_t)kernel_w);
   const hipError_t e = run_path(use, p, true, out_dtype, s);
   if (e != hipSuccess) return BNN_ERR_HIP;
   g_last_path = use;

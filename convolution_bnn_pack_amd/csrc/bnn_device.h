@@ -136,6 +136,29 @@ template <> struct OutType<kBF16> {
   }
 };
 
+// Division of a non-negative int by a divisor fixed for the whole launch, without a division
+// instruction: unsigned division by an invariant integer (Granlund and Montgomery, "Division by
+// invariant integers using multiplication", 1994, figure 4.1). With l = ceil(log2 d) and
+// m = floor(2^32 (2^l - d) / d) + 1, the quotient of any 0 <= n < 2^32 is
+// (t + ((n - t) >> min(l, 1))) >> max(l - 1, 0) with t = the high word of m * n: a multiply
+// and four cheap operations instead of the ~30-instruction integer division sequence.
+struct FastDiv {
+  uint32_t d = 1, m = 1, s1 = 0, s2 = 0;
+  FastDiv() = default;
+  explicit FastDiv(uint32_t div) : d(div) {
+    uint32_t l = 0;
+    while ((uint64_t(1) << l) < div) l++;
+    m = (uint32_t)(((uint64_t(1) << 32) * ((uint64_t(1) << l) - div)) / div + 1);
+    s1 = l > 0 ? 1 : 0;
+    s2 = l > 0 ? l - 1 : 0;
+  }
+  __device__ __forceinline__ int div(int n) const {
+    const uint32_t un = (uint32_t)n;
+    const uint32_t t = __umulhi(m, un);
+    return (int)((t + ((un - t) >> s1)) >> s2);
+  }
+};
+
 // Shape of one contraction, shared by the GEMM and the implicit-im2col conv.
 // Linear: A is packed activations [M][KW], W is packed weights [N][KW].
 // Conv:   A is packed activations [B][H][W][CW] read through the implicit
@@ -154,6 +177,8 @@ struct Contraction {
   // conv only
   // kernel KH x KWD, stride (SH, SW), padding (PH, PW), dilation (DH, DW) along (rows, columns)
   int H, W, CW, Ho, Wo, KH, KWD, SH, SW, PH, PW, DH, DW;
+  // the same divisors for FastDiv: Ho * Wo, Wo, CW, KWD
+  FastDiv div_hw, div_wo, div_cw, div_kwd;
 };
 
 }  // namespace bnn

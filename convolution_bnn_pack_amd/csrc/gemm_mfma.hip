@@ -108,9 +108,9 @@ struct PixelCoord {
 
 __device__ __forceinline__ PixelCoord pixel_coord(const Contraction& p, int m) {
   const int hw = p.Ho * p.Wo;
-  const int b = m / hw;
+  const int b = p.div_hw.div(m);
   const int r = m - b * hw;
-  const int oh = r / p.Wo;
+  const int oh = p.div_wo.div(r);
   const int ow = r - oh * p.Wo;
   return {b, oh * p.SH - p.PH, ow * p.SW - p.PW};
 }
@@ -145,9 +145,9 @@ template <int NW, bool CONV, bool VEC>
 __device__ __forceinline__ void load_a(const Contraction& p, int m, bool mok, const PixelCoord& pc,
                                        int q0, uint32_t r[NW], bool ok[NW]) {
   if constexpr (CONV) {
-    int tap = q0 / p.CW;
+    int tap = p.div_cw.div(q0);
     int cw = q0 - tap * p.CW;
-    int kh = tap / p.KWD;
+    int kh = p.div_kwd.div(tap);
     int kw = tap - kh * p.KWD;
     if constexpr (VEC) {
       // the NW words share one tap
@@ -290,7 +290,7 @@ __device__ __forceinline__ void store_tile(const Contraction& p, const Acc (&acc
               const uint32_t r0 = (uint32_t)__shfl_xor((int)s0, 32), r1 = (uint32_t)__shfl_xor((int)s1, 32);
               const int mg = m0 + wm * T::WTM + fm * 32 + 16 * j + 8 * half;
               if (mg < p.M) {
-                const int b = mg / hw, pix = mg - b * hw;
+                const int b = p.div_hw.div(mg), pix = mg - b * hw;
                 const uint4 v = half ? make_uint4(r0, r1, q[1][0], q[1][1]) : make_uint4(q[0][0], q[0][1], r0, r1);
                 *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.out) + ((int64_t)b * p.N + n) * hw + pix) = v;
               }
@@ -308,7 +308,7 @@ __device__ __forceinline__ void store_tile(const Contraction& p, const Acc (&acc
           const int4 bk = {rowk(ml), rowk(ml + 1), rowk(ml + 2), rowk(ml + 3)};
           const int v0 = bk.x + 2 * acc_int(fn, fm, 4 * g), v1 = bk.y + 2 * acc_int(fn, fm, 4 * g + 1);
           const int v2 = bk.z + 2 * acc_int(fn, fm, 4 * g + 2), v3 = bk.w + 2 * acc_int(fn, fm, 4 * g + 3);
-          const int b = m / hw, pix = m - b * hw;
+          const int b = p.div_hw.div(m), pix = m - b * hw;
           if (quad) {
             store4<OUT>(p.out, ((int64_t)b * p.N + n) * hw + pix, v0, v1, v2, v3, p.alpha);
           } else {
@@ -317,7 +317,7 @@ __device__ __forceinline__ void store_tile(const Contraction& p, const Acc (&acc
             for (int i = 0; i < 4; i++) {
               const int mi = m + i;
               if (mi >= p.M) break;
-              const int bi = mi / hw, pi = mi - bi * hw;
+              const int bi = p.div_hw.div(mi), pi = mi - bi * hw;
               store1<OUT>(p.out, ((int64_t)bi * p.N + n) * hw + pi, vals[i], p.alpha);
             }
           }
@@ -567,6 +567,41 @@ __global__ __launch_bounds__(T::THREADS) void mfma_kernel(Contraction p) {
     }
   };
 
+  // One MFMA of k-step fragments of parity par into acc[fn][fm].
+  auto mfma = [&](int par, int fn, int fm) __attribute__((always_inline)) {
+    if constexpr (T::F4) {
+      // only the first four dwords of each operand carry fp4 data
+      const v4i w4 = fw[par][fn], a4 = fa[par][fm];
+      const v8i w8 = {w4[0], w4[1], w4[2], w4[3], 0, 0, 0, 0};
+      const v8i a8 = {a4[0], a4[1], a4[2], a4[3], 0, 0, 0, 0};
+      // linear: D = W * A^T (a lane holds four features of one row); conv: D = A * W^T (a
+      // lane holds four pixels of one feature, contiguous in NCHW)
+      if constexpr (CONV)
+        acc[fn][fm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            a8, w8, acc[fn][fm], kFmtFp4, kFmtFp4, 0, kScaleOne, 0, kScaleOne);
+      else
+        acc[fn][fm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            w8, a8, acc[fn][fm], kFmtFp4, kFmtFp4, 0, kScaleOne, 0, kScaleOne);
+    } else {
+      if constexpr (CONV)
+        acc[fn][fm] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[par][fm], fw[par][fn], acc[fn][fm],
+                                                             0, 0, 0);
+      else
+        acc[fn][fm] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fw[par][fn], fa[par][fm], acc[fn][fm],
+                                                             0, 0, 0);
+    }
+  };
+  // XB (one tile per workgroup): the MFMAs of a stage's last k-step run at the start of the
+  // next stage, after its barrier -- their fragments are already in registers -- so the
+  // matrix cores have a k-step of work while the waves fetch the new stage's first fragments
+  // (otherwise every wave leaves the barrier waiting on LDS reads at the same moment). Slot
+  // group g = i / MPK of a stage then holds k-step g - 1 (g = 0: the previous stage's last),
+  // and k-step g's fragments are read at group g's first slot. Before the first stage the
+  // carried-over fragments are zero operands (they add exactly 0); after the last stage its
+  // final k-step is drained before the epilogue.
+  constexpr bool XB = !PERS;
+  constexpr int LASTPAR = (T::KSTEPS - 1) & 1;
+  static_assert(!XB || T::KSTEPS % 2 == 0, "carried k-step and k-step 0 use different fragment sets");
   // One stage: the MFMAs over the current LDS buffer, interleaved slot by slot with the
   // reads of the next k-step's fragments and the expansion of the next stage into the
   // other buffer; the global loads for stage s + PD go out first. Each slot is closed by
@@ -588,34 +623,23 @@ __global__ __launch_bounds__(T::THREADS) void mfma_kernel(Contraction p) {
     prepare((PH + 1) % T::PD);
 #pragma unroll
     for (int i = 0; i < NM; i++) {
-      const int kk = i / MPK, j = i % MPK;
+      const int g = i / MPK, j = i % MPK;
       const int fn = j / T::FM, fm = j % T::FM;
-      if constexpr (T::F4) {
-        // only the first four dwords of each operand carry fp4 data
-        const v4i w4 = fw[kk & 1][fn], a4 = fa[kk & 1][fm];
-        const v8i w8 = {w4[0], w4[1], w4[2], w4[3], 0, 0, 0, 0};
-        const v8i a8 = {a4[0], a4[1], a4[2], a4[3], 0, 0, 0, 0};
-        // linear: D = W * A^T (a lane holds four features of one row); conv: D = A * W^T (a
-        // lane holds four pixels of one feature, contiguous in NCHW)
-        if constexpr (CONV)
-          acc[fn][fm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              a8, w8, acc[fn][fm], kFmtFp4, kFmtFp4, 0, kScaleOne, 0, kScaleOne);
-        else
-          acc[fn][fm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              w8, a8, acc[fn][fm], kFmtFp4, kFmtFp4, 0, kScaleOne, 0, kScaleOne);
-      } else {
-        if constexpr (CONV)
-          acc[fn][fm] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[kk & 1][fm], fw[kk & 1][fn],
-                                                               acc[fn][fm], 0, 0, 0);
-        else
-          acc[fn][fm] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fw[kk & 1][fn], fa[kk & 1][fm],
-                                                               acc[fn][fm], 0, 0, 0);
-      }
-      // the next k-step's RPK fragment reads all go out in its first slot, a whole k-step
-      // of MFMAs ahead of their use
-      if (kk + 1 < T::KSTEPS && j == 0) {
+      if constexpr (XB) {
+        mfma(g == 0 ? LASTPAR : (g - 1) & 1, fn, fm);
+        // k-step g's fragments go out in group g's first slot, a group of MFMAs ahead of use
+        if (g >= 1 && j == 0) {
 #pragma unroll
-        for (int f = 0; f < RPK; f++) read_frag(cur, kk + 1, f);
+          for (int f = 0; f < RPK; f++) read_frag(cur, g, f);
+        }
+      } else {
+        mfma(g & 1, fn, fm);
+        // the next k-step's RPK fragment reads all go out in its first slot, a whole k-step
+        // of MFMAs ahead of their use
+        if (g + 1 < T::KSTEPS && j == 0) {
+#pragma unroll
+          for (int f = 0; f < RPK; f++) read_frag(cur, g + 1, f);
+        }
       }
 #pragma unroll
       for (int u = i * NU / NM; u < (i + 1) * NU / NM; u++) expand_unit(nxt, u);
@@ -644,6 +668,12 @@ __global__ __launch_bounds__(T::THREADS) void mfma_kernel(Contraction p) {
   prepare(0);
 #pragma unroll
   for (int u = 0; u < NU; u++) expand_unit(lds0, u);
+  if constexpr (XB) {
+#pragma unroll
+    for (int f = 0; f < T::FM; f++) fa[LASTPAR][f] = v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int f = 0; f < T::FN; f++) fw[LASTPAR][f] = v4i{0, 0, 0, 0};
+  }
   __syncthreads();
   int s = 0;
   for (; s + T::UNROLL <= nstream; s += T::UNROLL) {
@@ -668,6 +698,11 @@ __global__ __launch_bounds__(T::THREADS) void mfma_kernel(Contraction p) {
     if (s + 4 < nstream) stage(std::integral_constant<int, 4>{}, s + 4);
   }
 
+  if constexpr (XB) {
+    // drain: the last stage's final k-step
+#pragma unroll
+    for (int j = 0; j < MPK; j++) mfma(LASTPAR, j / T::FM, j % T::FM);
+  }
   if constexpr (!PERS) {
     // rowk_part counted 32 signs per real A word; with a last word per row (linear) or per
     // tap (conv) that holds only KB % 32 signs, the row's K_valid is lower by
@@ -774,6 +809,9 @@ hipError_t launch_tile(const Contraction& p, int out_dtype, hipStream_t stream) 
 // whose MFMA and expansion streams the hardware interleaves. A stage is 128 reductions
 // (4 words) for int8 and 256 (8 words) for fp4: the same LDS row of 128 bytes and the
 // same number of MFMAs per stage.
+#ifndef BNN_MFMA_L_WAVES_N
+#define BNN_MFMA_L_WAVES_N 4
+#endif
 #ifndef BNN_MFMA_PD_CF4
 #define BNN_MFMA_PD_CF4 2
 #endif
@@ -785,7 +823,8 @@ struct Tiles {
   static constexpr int KS = F4 ? 8 : 4;
   static constexpr int PD_M = F4 && CONV ? BNN_MFMA_PD_CF4 : BNN_MFMA_PD_M;
   using M = Tile<128, 256, KS, PD_M, 2, BNN_MFMA_WAVES_N, F4>;
-  using L = std::conditional_t<F4 && CONV, M, Tile<256, 256, KS, BNN_MFMA_PD_L, 2, BNN_MFMA_WAVES_N, F4>>;
+  using L = std::conditional_t<F4 && CONV, M,
+                               Tile<256, 256, KS, BNN_MFMA_PD_L, 2, BNN_MFMA_L_WAVES_N, F4>>;
   using S = Tile<128, 128, KS, PD_M, 2, BNN_MFMA_WAVES_N, F4>;
   // fp4 layers whose 64 x 128 tiles fit in one round of workgroups: 64 x 128 tiles, 1 x 4
   // waves, twice the workgroups of 128 x 128 (the 32x256x14x14 stage-3 conv: 12.6 -> 10.7 us,

@@ -33,9 +33,9 @@ struct PixelCoord {
 
 __device__ __forceinline__ PixelCoord pixel_coord(const Contraction& p, int m) {
   const int hw = p.Ho * p.Wo;
-  const int b = m / hw;
+  const int b = p.div_hw.div(m);
   const int r = m - b * hw;
-  const int oh = r / p.Wo;
+  const int oh = p.div_wo.div(r);
   const int ow = r - oh * p.Wo;
   return {b, oh * p.SH - p.PH, ow * p.SW - p.PW};
 }
@@ -51,9 +51,9 @@ __device__ __forceinline__ void load_a4(const Contraction& p, int m, const Pixel
       r[i] = (m < p.M && q < p.KW) ? p.a[(int64_t)m * p.KW + q] : 0u;
     }
   } else {
-    int tap = q0 / p.CW;
+    int tap = p.div_cw.div(q0);
     int cw = q0 - tap * p.CW;
-    int kh = tap / p.KWD;
+    int kh = p.div_kwd.div(tap);
     int kw = tap - kh * p.KWD;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
