@@ -56,6 +56,12 @@ BWD_WORKLOADS = {
     "bwd_linear_2048x4096x4096_f16": "linear_2048x4096x4096_f16",
     "bwd_linear_16384x8192x8192_bf16": "linear_16384x8192x8192_bf16",
 }
+# straight-through conv backward (grad_input through columns + col2im with the clip mask and
+# grad_scale_a, grad_weight against the unfolded input with its int8 codes): name -> conv workload
+BWD_CONV_WORKLOADS = {
+    "bwd_conv_128x128x28x28_s2_f16": "conv_down_s2_f16",
+    "bwd_conv_128x128x28x28_d2_f16": "conv_dil2_f16",
+}
 PACK_WORKLOAD = "pack_linear_16384x8192_bf16"
 # kernel kinds: source file, kernel function name, roofline peak and arithmetic type
 KERNEL_SOURCES = {"mfma": "gemm_mfma.hip", "mfma_fp4": "gemm_mfma.hip", "xor": "gemm_xor.hip",
@@ -257,12 +263,15 @@ def main():
     pack_only = args.workload in CODEC_WORKLOADS
     w8a8 = args.workload in W8A8_WORKLOADS
     bwd = args.workload in BWD_WORKLOADS
+    bwd_conv = args.workload in BWD_CONV_WORKLOADS
     codec_kind, base, shift_dt = CODEC_WORKLOADS.get(args.workload, (None, None, None))
     if w8a8:
         base, amax_x, amax_w = W8A8_WORKLOADS[args.workload]
     if bwd:
         base = BWD_WORKLOADS[args.workload]
-    wl = synth.WORKLOADS[base if (pack_only or w8a8 or bwd) else args.workload]
+    if bwd_conv:
+        base = BWD_CONV_WORKLOADS[args.workload]
+    wl = synth.WORKLOADS[base if (pack_only or w8a8 or bwd or bwd_conv) else args.workload]
     log(f"workload {args.workload}: generating inputs")
     x, w, sa, sw = synth.make_inputs(wl, draw_weight=not pack_only)
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
@@ -353,6 +362,35 @@ def main():
         path_used = None
         kernels = {"pack": [pack], "core": [core], "core_q": [core_q]}
         step_fns = [pack, core_q]
+    elif bwd_conv:
+        # step: grad_input (g to [O][pixels], the column contraction, col2im with the clip mask and
+        # grad_scale_a) and grad_weight with its int8 codes (im2col of x, the contraction, amax,
+        # coder); W is the layer's float weight in the gradient's dtype
+        m, n, k = wl.gemm_mnk()            # m = batch*Ho*Wo, n = O, k = C*kh*kw
+        ops = 2 * 2.0 * m * n * k
+        w = w.to(x.dtype).contiguous()
+        ho, wo = wl.out_shape()[2:]
+        gcpu = synth.make_grad(wl.batch * wl.o * ho * wo, 1, wl.x_dtype, wl.seed + 70).view(
+            wl.batch, wl.o, ho, wo)
+        gd, wd = gcpu.to(dev), w.to(dev)
+        geo = (wl.batch, wl.c, wl.h, wl.w, wl.o, wl.ks, wl.ks, wl.stride, wl.stride, wl.padding,
+               wl.padding, wl.dilation, wl.dilation)
+        gi = torch.empty((wl.batch, wl.c, wl.h, wl.w), dtype=torch.float32, device=dev)
+        gsa = torch.empty((), dtype=torch.float64, device=dev)
+        gw = torch.empty((wl.o, wl.c, wl.ks, wl.ks), dtype=torch.float32, device=dev)
+        gq = torch.empty((wl.o, wl.c, wl.ks, wl.ks), dtype=torch.int8, device=dev)
+        gamax = torch.empty((), dtype=torch.float32, device=dev)
+        wsi = torch.empty(lib.bnn_conv2d_grad_input_workspace_bytes(*geo), dtype=torch.uint8, device=dev)
+        wsw = torch.empty(lib.bnn_conv2d_grad_weight_workspace_bytes(*geo), dtype=torch.uint8, device=dev)
+        pack = lambda i: lib.bnn_conv2d_grad_input(gd.data_ptr(), wd.data_ptr(), xd.data_ptr(), xcode,
+                                                   *geo, sa, sw, gi.data_ptr(), gsa.data_ptr(),
+                                                   wsi.data_ptr(), wsi.numel(), cur_stream())
+        core = lambda i: lib.bnn_conv2d_grad_weight(gd.data_ptr(), xd.data_ptr(), xcode, *geo, sa,
+                                                    gw.data_ptr(), gq.data_ptr(), gamax.data_ptr(),
+                                                    wsw.data_ptr(), wsw.numel(), cur_stream())
+        path_used = None
+        kernels = {"pack": [pack], "core": [core]}
+        step_fns = [pack, core]
     elif w8a8:
         # step: activation codes (NCHW -> NHWC int8), then the int8 conv; weight codes are made
         # once ahead, as the layer's weights are
@@ -428,6 +466,30 @@ def main():
         want_q = torch.round(gw[cols].cpu() / step).clamp(-127, 127).to(torch.int8)
         parity = parity and amax_v == float(gw.abs().max().cpu())
         parity = parity and bool(torch.equal(gq[cols].cpu(), want_q))
+        log(f"parity spot check vs oracle (within the fp32 summation bound): {parity}")
+    elif bwd_conv:
+        import oracle
+        # two images end to end (grad_input of those images, the weight gradient summed over
+        # them), recomputed on the device for the same two images: exact sums bound as in the tests
+        imgs = [0, wl.batch - 1]
+        g2, x2 = gcpu[imgs].contiguous(), x[imgs].contiguous()
+        ref_i, ref_sa, ref_w = oracle.conv2d_grad(g2, w, x2, wl.stride, wl.padding, wl.dilation, sa, sw)
+        gi2, _ = bnn.conv2d_grad_input(g2.to(dev), wd, x2.to(dev), sa, sw, wl.stride, wl.padding,
+                                       wl.dilation)
+        gw2 = bnn.conv2d_grad_weight(g2.to(dev), x2.to(dev), wl.ks, sa, wl.stride, wl.padding,
+                                     wl.dilation)
+        torch.cuda.synchronize()
+        t_in = wl.o * wl.ks * wl.ks + 2
+        ho, wo = wl.out_shape()[2:]
+        t_w = 2 * ho * wo + 2
+        abs_in, _, _ = oracle.conv2d_grad(g2.abs(), torch.ones_like(w), torch.zeros_like(x2),
+                                          wl.stride, wl.padding, wl.dilation, sa, sw)
+        _, _, abs_w = oracle.conv2d_grad(g2.abs(), torch.ones_like(w), torch.ones_like(x2),
+                                         wl.stride, wl.padding, wl.dilation, sa, sw)
+        U = 2.0 ** -24
+        ok_i = bool(((gi2.cpu().double() - ref_i).abs() <= t_in * U * abs_in + U * ref_i.abs()).all())
+        ok_w = bool(((gw2.cpu().double() - ref_w).abs() <= t_w * U * abs_w + U * ref_w.abs()).all())
+        parity = ok_i and ok_w
         log(f"parity spot check vs oracle (within the fp32 summation bound): {parity}")
     elif w8a8:
         import oracle
@@ -509,6 +571,24 @@ def main():
         metric, unit = {"abs_mean": ("abs-mean scale bandwidth", "GB/s")}.get(
             codec_kind, ("sign+pack bandwidth", "GB/s"))
         dtype = "f64" if codec_kind == "abs_mean" else "u32"
+    elif bwd_conv:
+        # each entry point runs one 2*M*N*K-flop contraction plus its layout kernels; the roofline
+        # line is the slower call's contraction measured as part of that call (an upper bound on
+        # the contraction's own time)
+        kind = "bwd"
+        name, dom_ms = max((("grad_input", kern_ms["pack"]), ("grad_weight", kern_ms["core"])),
+                           key=lambda t: t[1])
+        achieved = ops / 2 / (dom_ms * 1e-3) / 1e12
+        peak = PEAKS[kind]
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": None,
+                "kernel": f"{name} call (transpose + bwd_gemm_kernel + layout kernels)",
+                "kernel_ms": round(dom_ms, 5),
+                "grad_input_call_ms": round(kern_ms["pack"], 5),
+                "grad_weight_i8_call_ms": round(kern_ms["core"], 5)}
+        value = ops / (ms_per_step * 1e-3) / 1e12
+        metric, unit = "conv backward TFLOP/s (2 contractions of 2*M*N*K)", "TFLOP/s"
+        dtype = wl.x_dtype
     elif bwd:
         # both launches are 2*M*N*K-flop contractions; the slower one is the roofline kernel
         kind = "bwd"
@@ -547,7 +627,11 @@ def main():
                    "timing": "HIP graph of the timed steps, replayed once untimed then once timed"},
         "roofline": roof,
     }
-    if bwd:
+    if bwd_conv:
+        result["config"].update({"m": m, "n": n, "k": k, "dtype": wl.x_dtype,
+                                 "outputs": "grad_input fp32 NCHW, grad_scale_a f64, grad_weight fp32 OIHW and its int8 codes + amax"})
+        result["parity_spot_check"] = parity
+    elif bwd:
         result["config"].update({"m": m, "n": n, "k": k, "dtype": wl.x_dtype,
                                  "outputs": "grad_input fp32 [m, k], grad_scale_a f64, grad_weight fp32 [n, k] and its int8 codes + amax"})
         result["parity_spot_check"] = parity
@@ -567,7 +651,19 @@ def main():
         torch.cuda.synchronize()
         result["copy_calibration_bytes"] = n
         del src, dst
-    if not args.no_cpu_baseline and bwd:
+    if not args.no_cpu_baseline and bwd_conv:
+        import oracle
+        nimg = 2
+        log(f"cpu baseline (oracle on host cores, both gradients of {nimg} images)")
+        t0 = time.perf_counter()
+        oracle.conv2d_grad(gcpu[:nimg].contiguous(), w, x[:nimg].contiguous(), wl.stride, wl.padding,
+                           wl.dilation, sa, sw)
+        dt_cpu = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": round(ops * nimg / wl.batch / dt_cpu / 1e12, 6),
+                                  "unit": "TFLOP/s", "cores": oracle.num_threads(),
+                                  "cpu_model": cpu_model(), "kind": "oracle",
+                                  "sample": f"both gradients of the first {nimg} of {wl.batch} images ({dt_cpu:.2f} s)"}
+    elif not args.no_cpu_baseline and bwd:
         import oracle
         rows = min(m, 4096)         # about 2-10 s of host work at the layer sizes
         log(f"cpu baseline (oracle on host cores, grad_input of {rows} rows)")

@@ -39,7 +39,9 @@ OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIGN, ERR_WORKSPACE, ERR_PATH, ERR_HIP 
 EXPORTS = ("bnn_pack_sign", "bnn_pack_sign_nchw", "bnn_pack_sign_shift", "bnn_pack_sign_nchw_shift",
            "bnn_abs_mean_scale", "bnn_abs_mean_workspace_bytes", "bnn_w_pack", "bnn_w_pack_conv",
            "bnn_conv2d_ex", "bnn_quant_i8_nhwc", "bnn_quant_i8_weight", "bnn_w8a8_conv2d", "bnn_gemm", "bnn_conv2d",
-           "bnn_gemm_noalloc", "bnn_u8_to_words", "bnn_gemm_workspace_bytes", "bnn_conv2d_workspace_bytes", "bnn_gemm_auto_path",
+           "bnn_gemm_noalloc", "bnn_u8_to_words", "bnn_conv2d_grad_input",
+           "bnn_conv2d_grad_input_workspace_bytes", "bnn_conv2d_grad_weight",
+           "bnn_conv2d_grad_weight_workspace_bytes", "bnn_gemm_workspace_bytes", "bnn_conv2d_workspace_bytes", "bnn_gemm_auto_path",
            "bnn_conv2d_auto_path", "bnn_last_path", "bnn_status_string",
            "bnn_linear_grad_input", "bnn_linear_grad_input_workspace_bytes", "bnn_linear_grad_weight",
            "bnn_linear_grad_weight_i8", "bnn_linear_grad_weight_i8_workspace_bytes",
@@ -77,6 +79,10 @@ def _bind(path: str) -> ctypes.CDLL:
         "bnn_gemm": ([P, I, P, I64, I64, I64, D, D, I, P, I, P, SZ, P], I),
         "bnn_gemm_noalloc": ([P, I, P, I64, I64, I64, D, D, I, P, I, P], I),
         "bnn_u8_to_words": ([P, I64, I64, P, P], I),
+        "bnn_conv2d_grad_input": ([P, P, P, I] + [I64] * 5 + [I] * 8 + [F, F, P, P, P, SZ, P], I),
+        "bnn_conv2d_grad_input_workspace_bytes": ([I64] * 5 + [I] * 8, SZ),
+        "bnn_conv2d_grad_weight": ([P, P, I] + [I64] * 5 + [I] * 8 + [F, P, P, P, P, SZ, P], I),
+        "bnn_conv2d_grad_weight_workspace_bytes": ([I64] * 5 + [I] * 8, SZ),
         "bnn_conv2d": ([P, I, I64, I64, I64, I64, P, I64, D, D, I, I, I, I, I, P, I, P, SZ, P], I),
         "bnn_gemm_workspace_bytes": ([I64, I64, I], SZ),
         "bnn_conv2d_workspace_bytes": ([I64, I64, I64, I64, I], SZ),
@@ -664,3 +670,88 @@ def quant_grad_i8(grad: torch.Tensor):
     _check(lib.bnn_quant_grad_i8(g.data_ptr(), g.numel(), codes.data_ptr(), amax.data_ptr(), ws.data_ptr(),
                                  _nbytes(ws), _stream(g)), "bnn_quant_grad_i8")
     return codes, amax
+
+
+def _conv_bwd_geom(g, x, kernel_hw, stride, padding, dilation):
+    """(n, c, h, w, o, kh, kw, sh, sw, ph, pw, dh, dw) after checking that g has the conv output's
+    shape for x."""
+    if g.dim() != 4 or x.dim() != 4:
+        raise ValueError("grad_out and x must be 4-D (NCHW)")
+    n, c, h, w = x.shape
+    kh, kw = kernel_hw
+    (sh, sw), (ph, pw), (dh, dw) = _pair(stride, "stride"), _pair(padding, "padding"), _pair(dilation, "dilation")
+    ho = (h + 2 * ph - dh * (kh - 1) - 1) // sh + 1 if sh > 0 else 0
+    wo = (w + 2 * pw - dw * (kw - 1) - 1) // sw + 1 if sw > 0 else 0
+    o = g.shape[1]
+    if tuple(g.shape) != (n, o, ho, wo):
+        raise ValueError(f"grad_out must have shape {(n, o, ho, wo)}, got {tuple(g.shape)}")
+    return n, c, h, w, o, kh, kw, sh, sw, ph, pw, dh, dw
+
+
+def conv2d_grad_input(grad_out: torch.Tensor, weight: torch.Tensor, x: torch.Tensor,
+                      scale_a: float, scale_w: float, stride=1, padding=0, dilation=1,
+                      out: torch.Tensor | None = None, grad_scale_a: torch.Tensor | None = None,
+                      workspace: torch.Tensor | None = None):
+    """Straight-through backward of the binarized conv, input side: grad_out [n, o, Ho, Wo],
+    weight [o, c, kh, kw] (the float weight) and x [n, c, h, w] of one 16-bit dtype. Returns
+    (grad_input fp32 [n, c, h, w], grad_scale_a 0-dim float64), both on the device."""
+    g, wt, x = _dev(grad_out, "grad_out"), _dev(weight, "weight"), _dev(x, "x")
+    dt = _half_pair(g, "grad_out")
+    if wt.dtype != g.dtype or x.dtype != g.dtype:
+        raise TypeError("grad_out, weight and x must share one dtype")
+    _same_device("weight", wt, g)
+    _same_device("x", x, g)
+    if wt.dim() != 4 or wt.shape[1] != x.shape[1] or wt.shape[0] != g.shape[1]:
+        raise ValueError(f"weight must be [o, c, kh, kw] for grad_out {tuple(g.shape)} and x {tuple(x.shape)}")
+    geo = _conv_bwd_geom(g, x, tuple(wt.shape[2:]), stride, padding, dilation)
+    n, c, h, w = geo[:4]
+    if out is None:
+        out = torch.empty((n, c, h, w), dtype=torch.float32, device=g.device)
+    else:
+        _expect(out, "out", torch.float32, (n, c, h, w))
+        _same_device("out", out, g)
+    if grad_scale_a is None:
+        grad_scale_a = torch.empty((), dtype=torch.float64, device=g.device)
+    else:
+        _expect(grad_scale_a, "grad_scale_a", torch.float64, ())
+        _same_device("grad_scale_a", grad_scale_a, g)
+    need = lib.bnn_conv2d_grad_input_workspace_bytes(*geo)
+    if workspace is None:
+        workspace = _workspace(need, g.device)
+    else:
+        _dev(workspace, "workspace")
+        _same_device("workspace", workspace, g)
+    _check(lib.bnn_conv2d_grad_input(g.data_ptr(), wt.data_ptr(), x.data_ptr(), dt, *geo,
+                                     float(scale_a), float(scale_w), out.data_ptr(),
+                                     grad_scale_a.data_ptr(), workspace.data_ptr(),
+                                     _nbytes(workspace), _stream(g)), "bnn_conv2d_grad_input")
+    return out, grad_scale_a
+
+
+def conv2d_grad_weight(grad_out: torch.Tensor, x: torch.Tensor, kernel_size, scale_a: float,
+                       stride=1, padding=0, dilation=1, codes: bool = False,
+                       workspace: torch.Tensor | None = None):
+    """Straight-through backward of the binarized conv, weight side: fp32 [o, c, kh, kw] =
+    scale_a * conv2d_weight(sign(x), grad_out). With codes=True returns (grad_w, int8 codes,
+    amax 0-dim float32): the int8 gradient the page keeps (amax = max|grad_w|)."""
+    g, x = _dev(grad_out, "grad_out"), _dev(x, "x")
+    dt = _half_pair(g, "grad_out")
+    if x.dtype != g.dtype:
+        raise TypeError("grad_out and x must share one dtype")
+    _same_device("x", x, g)
+    geo = _conv_bwd_geom(g, x, _pair(kernel_size, "kernel_size"), stride, padding, dilation)
+    n, c, h, w, o, kh, kw = geo[:7]
+    gw = torch.empty((o, c, kh, kw), dtype=torch.float32, device=g.device)
+    q = torch.empty((o, c, kh, kw), dtype=torch.int8, device=g.device) if codes else None
+    amax = torch.empty((), dtype=torch.float32, device=g.device) if codes else None
+    need = lib.bnn_conv2d_grad_weight_workspace_bytes(*geo)
+    if workspace is None:
+        workspace = _workspace(need, g.device)
+    else:
+        _dev(workspace, "workspace")
+        _same_device("workspace", workspace, g)
+    _check(lib.bnn_conv2d_grad_weight(g.data_ptr(), x.data_ptr(), dt, *geo, float(scale_a),
+                                      gw.data_ptr(), q.data_ptr() if codes else None,
+                                      amax.data_ptr() if codes else None, workspace.data_ptr(),
+                                      _nbytes(workspace), _stream(g)), "bnn_conv2d_grad_weight")
+    return (gw, q, amax) if codes else gw

@@ -345,6 +345,118 @@ hipError_t launch_bwd(bool bf, const BwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---- Conv backward (BinaryConv2dForward.backward on the qconv/binary/cutlass/layer page): the
+// page's conv2d_input and conv2d_weight, each lowered to the contraction above.
+//   grad_input: cols[pix][c*T + t] = scale_w * sum_o g[b][o][pix] * sign(W[o][c][t]) for every
+//   output pixel pix = (b, oh, ow) and tap t = kh*KW + kw, then each input element gathers the
+//   columns whose tap lands on it (col2im), is multiplied by the clip mask, and adds its
+//   grad_input * sign(x) to its workgroup's double sum.
+//   grad_weight: GW[o][c*T + t] = scale_a * sum_pix g[b][o][pix] * sign(xcol[pix][c*T + t]),
+//   xcol the unfolded input (0 where the tap falls in the padding), i.e. OIHW directly.
+// g is first copied to [O][B*Ho*Wo] so both contractions read it as a plain matrix.
+
+struct ConvGeom {
+  int B, C, H, W, O, KH, KW, SH, SW, PH, PW, DH, DW, Ho, Wo;
+};
+
+// g NCHW [B][O][Ho*Wo] -> gT [O][B*Ho*Wo]: one contiguous run of Ho*Wo per (b, o), copied by a
+// workgroup per run.
+__global__ __launch_bounds__(kThreads) void conv_g_transpose_kernel(const uint16_t* __restrict__ g,
+                                                                   uint16_t* __restrict__ gT,
+                                                                   int B, int O, int hw) {
+  const int64_t runs = (int64_t)B * O;
+  for (int64_t run = blockIdx.x; run < runs; run += gridDim.x) {
+    const int b = (int)(run / O), o = (int)(run - (int64_t)b * O);
+    const uint16_t* src = g + run * hw;
+    uint16_t* dst = gT + ((int64_t)o * B + b) * hw;
+    for (int i = threadIdx.x; i < hw; i += kThreads) dst[i] = src[i];
+  }
+}
+
+// xcol[pix][c*T + t] = x[b][c][oh*SH - PH + kh*DH][ow*SW - PW + kw*DW], 0 outside the input. A
+// thread per (c, pix), pixels fastest, so neighbouring threads read neighbouring input columns.
+__global__ __launch_bounds__(kThreads) void conv_im2col_kernel(const uint16_t* __restrict__ x,
+                                                              uint16_t* __restrict__ xcol,
+                                                              ConvGeom q) {
+  const int T = q.KH * q.KW, hwo = q.Ho * q.Wo;
+  const int64_t pixels = (int64_t)q.B * hwo, J = (int64_t)q.C * T;
+  const int64_t total = pixels * q.C;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * kThreads) {
+    const int c = (int)(i / pixels);
+    const int64_t pix = i - (int64_t)c * pixels;
+    const int b = (int)(pix / hwo), r = (int)(pix - (int64_t)b * hwo);
+    const int oh = r / q.Wo, ow = r - oh * q.Wo;
+    const uint16_t* plane = x + ((int64_t)b * q.C + c) * q.H * q.W;
+    uint16_t* dst = xcol + pix * J + (int64_t)c * T;
+    for (int kh = 0; kh < q.KH; kh++) {
+      const int ih = oh * q.SH - q.PH + kh * q.DH;
+      for (int kw = 0; kw < q.KW; kw++) {
+        const int iw = ow * q.SW - q.PW + kw * q.DW;
+        const bool in = ih >= 0 && ih < q.H && iw >= 0 && iw < q.W;
+        dst[kh * q.KW + kw] = in ? plane[(int64_t)ih * q.W + iw] : (uint16_t)0;
+      }
+    }
+  }
+}
+
+// grad_in[b][c][ih][iw] = mid(x) * sum of cols[(b, oh, ow)][c*T + t] over the taps t whose output
+// pixel (oh, ow) = ((ih + PH - kh*DH) / SH, (iw + PW - kw*DW) / SW) exists (exact divisions, in
+// range), in tap order; each workgroup writes its double sum of grad_in * sign(x) (a fixed grid,
+// so the order of every sum is fixed).
+template <bool BF>
+__global__ __launch_bounds__(kThreads) void conv_col2im_kernel(const float* __restrict__ cols,
+                                                              const uint16_t* __restrict__ x,
+                                                              float* __restrict__ grad_in,
+                                                              double* __restrict__ part, ConvGeom q,
+                                                              float scale_a) {
+  const int T = q.KH * q.KW;
+  const int64_t J = (int64_t)q.C * T;
+  const int64_t total = (int64_t)q.B * q.C * q.H * q.W;
+  double sum = 0.0;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * kThreads) {
+    const int iw = (int)(i % q.W);
+    const int64_t r1 = i / q.W;
+    const int ih = (int)(r1 % q.H);
+    const int64_t r2 = r1 / q.H;
+    const int c = (int)(r2 % q.C), b = (int)(r2 / q.C);
+    float v = 0.0f;
+    for (int kh = 0; kh < q.KH; kh++) {
+      const int nh = ih + q.PH - kh * q.DH;
+      if (nh < 0 || nh % q.SH != 0 || nh / q.SH >= q.Ho) continue;
+      const int oh = nh / q.SH;
+      for (int kw = 0; kw < q.KW; kw++) {
+        const int nw = iw + q.PW - kw * q.DW;
+        if (nw < 0 || nw % q.SW != 0 || nw / q.SW >= q.Wo) continue;
+        const int ow = nw / q.SW;
+        v += cols[(((int64_t)b * q.Ho + oh) * q.Wo + ow) * J + (int64_t)c * T + kh * q.KW + kw];
+      }
+    }
+    const float xv = widen16<BF>(x[i]);
+    const float qv = xv / scale_a;
+    v *= 1.0f - (qv < -1.0f ? 1.0f : 0.0f) - (qv > 1.0f ? 1.0f : 0.0f);
+    grad_in[i] = v;
+    const double sg = xv != xv ? (double)NAN : (xv > 0.0f ? 1.0 : (xv < 0.0f ? -1.0 : 0.0));
+    sum += (double)v * sg;
+  }
+  __shared__ double red[kThreads];
+  red[threadIdx.x] = sum;
+  __syncthreads();
+  for (int h = kThreads / 2; h > 0; h >>= 1) {
+    if ((int)threadIdx.x < h) red[threadIdx.x] += red[threadIdx.x + h];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) part[blockIdx.x] = red[0];
+}
+
+constexpr int kCol2imBlocks = 2048;
+
+int64_t grid_of(int64_t total, int64_t cap) {
+  const int64_t b = (total + kThreads - 1) / kThreads;
+  return b < 1 ? 1 : (b > cap ? cap : b);
+}
+
 }  // namespace
 
 int64_t bwd_grad_input_parts(int64_t m, int64_t k) {
@@ -387,6 +499,62 @@ hipError_t launch_linear_grad_weight(const void* g, const void* x, bool bf, int6
   BwdArgs a{static_cast<const uint16_t*>(g), static_cast<const uint16_t*>(x), nullptr, grad_w,
             nullptr, (int)n, (int)k, (int)m, scale_a, scale_a};
   return launch_bwd<true, false>(bf, a, s);
+}
+
+// ---- conv backward launchers
+
+int64_t conv_col2im_parts(int64_t n, int64_t c, int64_t h, int64_t w) {
+  return grid_of(n * c * h * w, kCol2imBlocks);
+}
+
+hipError_t launch_conv_grad_input(const void* g, const void* w, const void* x, bool bf,
+                                  const int geom[15], float scale_a, float scale_w, float* grad_in,
+                                  uint16_t* gT, float* cols, double* part, double* grad_scale_a,
+                                  hipStream_t s) {
+  const ConvGeom q{geom[0], geom[1], geom[2], geom[3], geom[4], geom[5], geom[6], geom[7],
+                   geom[8], geom[9], geom[10], geom[11], geom[12], geom[13], geom[14]};
+  const int hwo = q.Ho * q.Wo, T = q.KH * q.KW;
+  hipLaunchKernelGGL(conv_g_transpose_kernel, dim3((unsigned)grid_of((int64_t)q.B * q.O * kThreads, 8192)),
+                     dim3(kThreads), 0, s, static_cast<const uint16_t*>(g), gT, q.B, q.O, hwo);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // cols [B*Ho*Wo][C*T] = scale_w * gT^T @ sign(W viewed as [O][C*T])
+  BwdArgs a{gT, static_cast<const uint16_t*>(w), nullptr, cols, nullptr, q.B * hwo, q.C * T, q.O,
+            scale_w, scale_a};
+  e = launch_bwd<true, false>(bf, a, s);
+  if (e != hipSuccess) return e;
+  const int64_t total = (int64_t)q.B * q.C * q.H * q.W;
+  const int parts = (int)grid_of(total, kCol2imBlocks);
+  if (bf)
+    hipLaunchKernelGGL(conv_col2im_kernel<true>, dim3(parts), dim3(kThreads), 0, s, cols,
+                       static_cast<const uint16_t*>(x), grad_in, part, q, scale_a);
+  else
+    hipLaunchKernelGGL(conv_col2im_kernel<false>, dim3(parts), dim3(kThreads), 0, s, cols,
+                       static_cast<const uint16_t*>(x), grad_in, part, q, scale_a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_scale_a_kernel, dim3(1), dim3(kThreads), 0, s, part, parts,
+                     (double)total, grad_scale_a);
+  return hipGetLastError();
+}
+
+hipError_t launch_conv_grad_weight(const void* g, const void* x, bool bf, const int geom[15],
+                                   float scale_a, float* grad_w, uint16_t* gT, uint16_t* xcol,
+                                   hipStream_t s) {
+  const ConvGeom q{geom[0], geom[1], geom[2], geom[3], geom[4], geom[5], geom[6], geom[7],
+                   geom[8], geom[9], geom[10], geom[11], geom[12], geom[13], geom[14]};
+  const int hwo = q.Ho * q.Wo, T = q.KH * q.KW;
+  hipLaunchKernelGGL(conv_g_transpose_kernel, dim3((unsigned)grid_of((int64_t)q.B * q.O * kThreads, 8192)),
+                     dim3(kThreads), 0, s, static_cast<const uint16_t*>(g), gT, q.B, q.O, hwo);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(conv_im2col_kernel, dim3((unsigned)grid_of((int64_t)q.B * hwo * q.C, 16384)),
+                     dim3(kThreads), 0, s, static_cast<const uint16_t*>(x), xcol, q);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // GW [O][C*T] = scale_a * gT @ sign(xcol)
+  BwdArgs a{gT, xcol, nullptr, grad_w, nullptr, q.O, q.C * T, q.B * hwo, scale_a, scale_a};
+  return launch_bwd<false, false>(bf, a, s);
 }
 
 }  // namespace bnn

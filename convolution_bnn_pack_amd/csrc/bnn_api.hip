@@ -526,6 +526,138 @@ bnn_status bnn_quant_grad_i8(const float* grad, int64_t count, int8_t* codes, fl
                                            codes, static_cast<hipStream_t>(stream)));
 }
 
+// ---- conv backward (BinaryConv2dForward.backward)
+
+}  // extern "C"
+
+namespace {
+
+// Geometry of the conv backward; BNN_OK when every size is usable: 16-bit dtype, positive sizes,
+// a non-empty output, B*Ho*Wo and C*KH*KW multiples of 8 (16-byte operand loads), every count in
+// int range.
+struct ConvBwd {
+  int geom[15];
+  int64_t pixels, J, in_count;
+};
+
+bnn_status conv_bwd_geom(int64_t n, int64_t c, int64_t h, int64_t w, int64_t o, int kernel_h,
+                         int kernel_w, int stride_h, int stride_w, int pad_h, int pad_w, int dil_h,
+                         int dil_w, ConvBwd* q) {
+  if (n < 1 || c < 1 || h < 1 || w < 1 || o < 1) return BNN_ERR_SHAPE;
+  if (kernel_h < 1 || kernel_w < 1 || stride_h < 1 || stride_w < 1 || dil_h < 1 || dil_w < 1 ||
+      pad_h < 0 || pad_w < 0)
+    return BNN_ERR_SHAPE;
+  const int64_t ho = out_size(h, kernel_h, stride_h, pad_h, dil_h);
+  const int64_t wo = out_size(w, kernel_w, stride_w, pad_w, dil_w);
+  if (ho <= 0 || wo <= 0) return BNN_ERR_SHAPE;
+  const int64_t pixels = n * ho * wo, J = c * (int64_t)kernel_h * kernel_w;
+  if (pixels % 8 != 0 || J % 8 != 0) return BNN_ERR_SHAPE;
+  if (!int_fits(pixels) || !int_fits(J) || !int_fits(pixels * J) || !int_fits(o * pixels) ||
+      !int_fits(n * c * h * w) || !int_fits(o * J) || !int_fits(h + 2 * (int64_t)pad_h) ||
+      !int_fits(w + 2 * (int64_t)pad_w))
+    return BNN_ERR_SHAPE;
+  const int64_t vals[15] = {n, c, h, w, o, kernel_h, kernel_w, stride_h, stride_w, pad_h, pad_w,
+                            dil_h, dil_w, ho, wo};
+  for (int i = 0; i < 15; i++) q->geom[i] = (int)vals[i];
+  q->pixels = pixels;
+  q->J = J;
+  q->in_count = n * c * h * w;
+  return BNN_OK;
+}
+
+size_t round256(size_t v) { return (v + 255) / 256 * 256; }
+
+}  // namespace
+
+extern "C" {
+
+size_t bnn_conv2d_grad_input_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w,
+                                             int64_t out_channels, int kernel_h, int kernel_w,
+                                             int stride_h, int stride_w, int pad_h, int pad_w,
+                                             int dil_h, int dil_w) {
+  ConvBwd q;
+  if (conv_bwd_geom(n, c, h, w, out_channels, kernel_h, kernel_w, stride_h, stride_w, pad_h, pad_w,
+                    dil_h, dil_w, &q) != BNN_OK)
+    return 0;
+  return round256((size_t)out_channels * q.pixels * 2) + round256((size_t)q.pixels * q.J * 4) +
+         (size_t)bnn::conv_col2im_parts(n, c, h, w) * sizeof(double);
+}
+
+bnn_status bnn_conv2d_grad_input(const void* grad_out, const void* weight, const void* x,
+                                 int dtype, int64_t n, int64_t c, int64_t h, int64_t w,
+                                 int64_t out_channels, int kernel_h, int kernel_w, int stride_h,
+                                 int stride_w, int pad_h, int pad_w, int dil_h, int dil_w,
+                                 float scale_a, float scale_w, float* grad_in,
+                                 double* grad_scale_a, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  if (!half_dtype(dtype)) return BNN_ERR_DTYPE;
+  ConvBwd q;
+  const bnn_status st = conv_bwd_geom(n, c, h, w, out_channels, kernel_h, kernel_w, stride_h,
+                                      stride_w, pad_h, pad_w, dil_h, dil_w, &q);
+  if (st != BNN_OK) return st;
+  if (!grad_out || !weight || !x || !grad_in || !grad_scale_a) return BNN_ERR_NULL;
+  if (!aligned(grad_out, 2) || !aligned(weight, 16) || !aligned(x, 2) || !aligned(grad_in, 4) ||
+      !aligned(grad_scale_a, 8))
+    return BNN_ERR_ALIGN;
+  const size_t need = bnn_conv2d_grad_input_workspace_bytes(n, c, h, w, out_channels, kernel_h,
+                                                            kernel_w, stride_h, stride_w, pad_h,
+                                                            pad_w, dil_h, dil_w);
+  if (!workspace || workspace_bytes < need) return BNN_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return BNN_ERR_ALIGN;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint16_t* gT = reinterpret_cast<uint16_t*>(ws);
+  float* cols = reinterpret_cast<float*>(ws + round256((size_t)out_channels * q.pixels * 2));
+  double* part = reinterpret_cast<double*>(reinterpret_cast<uint8_t*>(cols) +
+                                           round256((size_t)q.pixels * q.J * 4));
+  return hip_status(bnn::launch_conv_grad_input(grad_out, weight, x, dtype == BNN_BF16, q.geom,
+                                                scale_a, scale_w, grad_in, gT, cols, part,
+                                                grad_scale_a, static_cast<hipStream_t>(stream)));
+}
+
+size_t bnn_conv2d_grad_weight_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w,
+                                              int64_t out_channels, int kernel_h, int kernel_w,
+                                              int stride_h, int stride_w, int pad_h, int pad_w,
+                                              int dil_h, int dil_w) {
+  ConvBwd q;
+  if (conv_bwd_geom(n, c, h, w, out_channels, kernel_h, kernel_w, stride_h, stride_w, pad_h, pad_w,
+                    dil_h, dil_w, &q) != BNN_OK)
+    return 0;
+  return round256((size_t)out_channels * q.pixels * 2) + round256((size_t)q.pixels * q.J * 2) +
+         (size_t)bnn::bwd_quant_grad_parts(out_channels * q.J) * sizeof(float);
+}
+
+bnn_status bnn_conv2d_grad_weight(const void* grad_out, const void* x, int dtype, int64_t n,
+                                  int64_t c, int64_t h, int64_t w, int64_t out_channels,
+                                  int kernel_h, int kernel_w, int stride_h, int stride_w,
+                                  int pad_h, int pad_w, int dil_h, int dil_w, float scale_a,
+                                  float* grad_w, int8_t* grad_w_q, float* amax, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (!half_dtype(dtype)) return BNN_ERR_DTYPE;
+  ConvBwd q;
+  const bnn_status st = conv_bwd_geom(n, c, h, w, out_channels, kernel_h, kernel_w, stride_h,
+                                      stride_w, pad_h, pad_w, dil_h, dil_w, &q);
+  if (st != BNN_OK) return st;
+  if (!grad_out || !x || !grad_w) return BNN_ERR_NULL;
+  if ((grad_w_q == nullptr) != (amax == nullptr)) return BNN_ERR_NULL;
+  if (!aligned(grad_out, 2) || !aligned(x, 2) || !aligned(grad_w, 16)) return BNN_ERR_ALIGN;
+  if (grad_w_q && (!aligned(grad_w_q, 4) || !aligned(amax, 4))) return BNN_ERR_ALIGN;
+  const size_t need = bnn_conv2d_grad_weight_workspace_bytes(n, c, h, w, out_channels, kernel_h,
+                                                             kernel_w, stride_h, stride_w, pad_h,
+                                                             pad_w, dil_h, dil_w);
+  if (!workspace || workspace_bytes < need) return BNN_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return BNN_ERR_ALIGN;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint16_t* gT = reinterpret_cast<uint16_t*>(ws);
+  uint8_t* xc = ws + round256((size_t)out_channels * q.pixels * 2);
+  float* qpart = reinterpret_cast<float*>(xc + round256((size_t)q.pixels * q.J * 2));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = bnn::launch_conv_grad_weight(grad_out, x, dtype == BNN_BF16, q.geom, scale_a,
+                                                    grad_w, gT, reinterpret_cast<uint16_t*>(xc), s);
+  if (e != hipSuccess) return BNN_ERR_HIP;
+  if (!grad_w_q) return BNN_OK;
+  return hip_status(bnn::launch_quant_grad(grad_w, out_channels * q.J, qpart, amax, grad_w_q, s));
+}
+
 }  // extern "C"
 
 namespace {

@@ -59,6 +59,11 @@
 
 #include "launch.h"
 
+// Tuning knob: fp4 convs with more tiles than resident workgroups run persistent workgroups.
+#ifndef BNN_CONV_PERS
+#define BNN_CONV_PERS 1
+#endif
+
 namespace bnn {
 namespace {
 
@@ -760,7 +765,7 @@ hipError_t launch_tile_o(const Contraction& p, hipStream_t stream) {
     // int8 256 x 256 conv tile would spill with the extra state). Channel counts that are
     // not a whole number of words take the one-tile-per-workgroup kernel, which corrects
     // K_valid for the short last word of each tap.
-    const int slots = p.KB == 32 * p.CW ? persistent_slots<T, OUT, VEC>() : 0;
+    const int slots = BNN_CONV_PERS && p.KB == 32 * p.CW ? persistent_slots<T, OUT, VEC>() : 0;
     if (slots > 0 && tiles > slots) {
       hipLaunchKernelGGL((mfma_kernel<T, OUT, CONV, VEC, true>), dim3((unsigned)slots), block, 0,
                          stream, p);
@@ -852,6 +857,14 @@ template <bool CONV, bool F4>
 hipError_t launch_mfma_t(const Contraction& p, int out_dtype, hipStream_t stream) {
   constexpr int64_t kMinTiles = BNN_MFMA_MIN_TILES;  // one workgroup per compute unit
   using TS = Tiles<F4, CONV>;
+#if defined(BNN_CONV_TILE)
+  // tuning builds: one fixed fp4 conv tile (1: 128 x 256, 2: 128 x 128, 3: 64 x 128)
+  if constexpr (CONV && F4) {
+    if (BNN_CONV_TILE == 1) return launch_tile<typename TS::M, CONV>(p, out_dtype, stream);
+    if (BNN_CONV_TILE == 2) return launch_tile<typename TS::S, CONV>(p, out_dtype, stream);
+    if (BNN_CONV_TILE == 3) return launch_tile<typename TS::T64, CONV>(p, out_dtype, stream);
+  }
+#endif
   if (F4 && p.N <= 64 && count_tiles(p, 256, 64) >= kMinTiles)
     return launch_tile<typename TS::N64, CONV>(p, out_dtype, stream);
   if (count_tiles(p, 256, 256) >= kMinTiles)

@@ -318,6 +318,50 @@ bnn_status bnn_quant_grad_i8(const float* grad, int64_t count, int8_t* codes, fl
 size_t bnn_gemm_workspace_bytes(int64_t m, int64_t k, int x_dtype);
 size_t bnn_conv2d_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w, int x_dtype);
 
+/* Straight-through backward of the binarized conv (BinaryConv2dForward.backward on the
+ * qconv/binary/cutlass/layer page): the page's conv2d_input with sign(W) * scale_w, the clip mask
+ * of x / scale_a, grad_scale_a, and conv2d_weight with sign(x) * scale_a, whose int8 codes the
+ * page takes last. sign is torch.sign (0 for +-0, NaN for NaN).
+ *   grad_out [n, out_channels, Ho, Wo], weight [out_channels, c, kernel_h, kernel_w] (the float
+ *   weight) and x [n, c, h, w] (the layer input) share one 16-bit dtype (BNN_F16 or BNN_BF16);
+ *   Ho, Wo by the forward's formula from the per-axis stride / padding / dilation.
+ *   n*Ho*Wo and c*kernel_h*kernel_w must be multiples of 8, every other size >= 1 (else
+ *   BNN_ERR_SHAPE). weight 16-byte aligned, grad_out and x 2-byte aligned.
+ *
+ * grad_input: grad_in [n, c, h, w] fp32 = mid(x) * sum over (o, kh, kw) of grad_out at the output
+ * pixel whose tap (kh, kw) reads that input element, times sign(W[o][c][kh][kw]) * scale_w; mid is
+ * 0 where the fp32 quotient x / scale_a is below -1 or above 1, else 1. grad_scale_a (one double) =
+ * sum(grad_in * sign(x)) / sqrt(n*c*h*w), summed in a fixed order (deterministic).
+ *   workspace: bnn_conv2d_grad_input_workspace_bytes(...) bytes, 256-byte aligned. */
+size_t bnn_conv2d_grad_input_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w,
+                                             int64_t out_channels, int kernel_h, int kernel_w,
+                                             int stride_h, int stride_w, int pad_h, int pad_w,
+                                             int dil_h, int dil_w);
+bnn_status bnn_conv2d_grad_input(const void* grad_out, const void* weight, const void* x,
+                                 int dtype, int64_t n, int64_t c, int64_t h, int64_t w,
+                                 int64_t out_channels, int kernel_h, int kernel_w, int stride_h,
+                                 int stride_w, int pad_h, int pad_w, int dil_h, int dil_w,
+                                 float scale_a, float scale_w, float* grad_in,
+                                 double* grad_scale_a, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/* grad_weight: grad_w [out_channels, c, kernel_h, kernel_w] fp32 (16-byte aligned) = scale_a *
+ * sum over (b, oh, ow) of grad_out[b][o][oh][ow] * sign(x at tap (kh, kw) of that output pixel),
+ * padded taps contributing 0. With grad_w_q and amax given (both or neither), also the int8 codes
+ * the page takes (per-tensor symmetric: amax = max|grad_w|, code = clamp(rint(v / (amax / 127)),
+ * +-127), a NaN quotient coding as 0), as bnn_quant_grad_i8 computes them.
+ *   workspace: bnn_conv2d_grad_weight_workspace_bytes(...) bytes, 256-byte aligned. */
+size_t bnn_conv2d_grad_weight_workspace_bytes(int64_t n, int64_t c, int64_t h, int64_t w,
+                                              int64_t out_channels, int kernel_h, int kernel_w,
+                                              int stride_h, int stride_w, int pad_h, int pad_w,
+                                              int dil_h, int dil_w);
+bnn_status bnn_conv2d_grad_weight(const void* grad_out, const void* x, int dtype, int64_t n,
+                                  int64_t c, int64_t h, int64_t w, int64_t out_channels,
+                                  int kernel_h, int kernel_w, int stride_h, int stride_w,
+                                  int pad_h, int pad_w, int dil_h, int dil_w, float scale_a,
+                                  float* grad_w, int8_t* grad_w_q, float* amax, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
 /* The path that bnn_gemm / bnn_conv2d would take for a shape under BNN_PATH_AUTO (it depends only on
  * the reduction length K = k, or kernel_size^2 * c). */
 int bnn_gemm_auto_path(int64_t m, int64_t n, int64_t k);
