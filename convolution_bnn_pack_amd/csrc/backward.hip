@@ -48,6 +48,10 @@ struct BwdArgs {
   int I, J, R;
   float scale;        // scale_w (grad_input) or scale_a (grad_weight)
   float scale_a;      // divisor of the clip test
+  // split reduction: workgroup group s sums r in [s * rchunk, (s + 1) * rchunk) and writes its
+  // partial result to out + s * out_split (rchunk = R: one group, the plain contraction)
+  int rchunk = 0;
+  int64_t out_split = 0;
 };
 
 // torch.sign of a 16-bit float, as bits of the same format.
@@ -109,7 +113,9 @@ __device__ inline void mfma(const uint16_t* pa, const uint16_t* pb, f32x16& acc)
 #ifndef BWD_WAVES
 #define BWD_WAVES 3
 #endif
-template <bool BF, bool AT, bool GI>
+// SF: the sign is taken of F (false: F is used as it is, for a caller whose A already holds
+// signs).
+template <bool BF, bool AT, bool GI, bool SF = true>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BWD_WAVES)))
 void bwd_gemm_kernel(BwdArgs p) {
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][kBM * kPitch];
@@ -117,7 +123,13 @@ void bwd_gemm_kernel(BwdArgs p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int tiles_j = (p.J + kBN - 1) / kBN;
-  const int i0 = (int)(blockIdx.x / tiles_j) * kBM, j0 = (int)(blockIdx.x % tiles_j) * kBN;
+  const int tiles = ((p.I + kBM - 1) / kBM) * tiles_j;
+  const int split = (int)blockIdx.x / tiles, tile = (int)blockIdx.x - split * tiles;
+  const int i0 = (tile / tiles_j) * kBM, j0 = (tile % tiles_j) * kBN;
+  // this workgroup's reduction range [r_lo, r_hi) and output slice
+  const int r_lo = split * p.rchunk;
+  const int r_hi = min(p.R, r_lo + p.rchunk);
+  float* const out = p.out + split * p.out_split;
   const uint4 zero = make_uint4(0, 0, 0, 0);
 
   // Per stage: A [I][R] in 16-byte chunks (row, 8 consecutive r); A [R][I] and F [R][J] in
@@ -138,7 +150,7 @@ void bwd_gemm_kernel(BwdArgs p) {
 #pragma unroll
       for (int u = 0; u < kNA; u++) {
         const int c = tid + u * kThreads, row = c / kRowChunks, r = r0 + (c % kRowChunks) * 8;
-        ra[u] = (i0 + row < p.I && r < p.R) ? ldg16(p.a + (int64_t)(i0 + row) * p.R + r) : zero;
+        ra[u] = (i0 + row < p.I && r < r_hi) ? ldg16(p.a + (int64_t)(i0 + row) * p.R + r) : zero;
       }
     } else {
 #pragma unroll
@@ -147,7 +159,7 @@ void bwd_gemm_kernel(BwdArgs p) {
 #pragma unroll
         for (int h = 0; h < 2; h++) {
           const int r = r0 + 2 * pair_of(c) + h;
-          ra[2 * u + h] = (r < p.R && i < p.I) ? ldg16(p.a + (int64_t)r * p.I + i) : zero;
+          ra[2 * u + h] = (r < r_hi && i < p.I) ? ldg16(p.a + (int64_t)r * p.I + i) : zero;
         }
       }
     }
@@ -157,7 +169,7 @@ void bwd_gemm_kernel(BwdArgs p) {
 #pragma unroll
       for (int h = 0; h < 2; h++) {
         const int r = r0 + 2 * pair_of(c) + h;
-        rf[2 * u + h] = (r < p.R && j < p.J) ? ldg16(p.f + (int64_t)r * p.J + j) : zero;
+        rf[2 * u + h] = (r < r_hi && j < p.J) ? ldg16(p.f + (int64_t)r * p.J + j) : zero;
       }
     }
   };
@@ -184,7 +196,8 @@ void bwd_gemm_kernel(BwdArgs p) {
 #pragma unroll
       for (int e = 0; e < 8; e++)
         *reinterpret_cast<uint32_t*>(&sB[buf][(jj + e) * kPitch + rr]) =
-            sign_bits<BF>(u16_of(rf[2 * u], e)) | (sign_bits<BF>(u16_of(rf[2 * u + 1], e)) << 16);
+            SF ? sign_bits<BF>(u16_of(rf[2 * u], e)) | (sign_bits<BF>(u16_of(rf[2 * u + 1], e)) << 16)
+               : (uint32_t)u16_of(rf[2 * u], e) | ((uint32_t)u16_of(rf[2 * u + 1], e) << 16);
     }
   };
 
@@ -196,16 +209,16 @@ void bwd_gemm_kernel(BwdArgs p) {
 #pragma unroll
       for (int v = 0; v < 16; v++) acc[a][b][v] = 0.0f;
 
-  const int nk = (p.R + kBK - 1) / kBK;
+  const int nk = r_hi > r_lo ? (r_hi - r_lo + kBK - 1) / kBK : 0;
   if (nk > 0) {
-    load(0);
+    load(r_lo);
     store(0);
   }
   __syncthreads();
   const int half = (lane >> 5) * 8, l32 = lane & 31;
   for (int kt = 0; kt < nk; kt++) {
     const int buf = kt & 1;
-    if (kt + 1 < nk) load((kt + 1) * kBK);
+    if (kt + 1 < nk) load(r_lo + (kt + 1) * kBK);
 #pragma unroll
     for (int ks = 0; ks < kBK; ks += 16) {
 #pragma unroll
@@ -239,7 +252,7 @@ void bwd_gemm_kernel(BwdArgs p) {
           const double s = xv != xv ? (double)NAN : (xv > 0.0f ? 1.0 : (xv < 0.0f ? -1.0 : 0.0));
           part += (double)val * s;
         }
-        stg4(p.out + o, val);
+        stg4(out + o, val);
       }
     }
   if constexpr (GI) {
@@ -334,25 +347,48 @@ int amax_parts(int64_t n4) {
   return (int)(blocks < 1 ? 1 : (blocks > kAmaxParts ? kAmaxParts : blocks));
 }
 
-template <bool AT, bool GI>
-hipError_t launch_bwd(bool bf, const BwdArgs& a, hipStream_t s) {
+// A reduction of length R cut into at most `splits` chunks of whole kBK-stages: chunk length
+// rchunk and the number of chunks used (asking again for `used` chunks gives the same plan).
+struct SplitPlan {
+  int rchunk, used;
+};
+SplitPlan split_plan(int64_t R, int splits) {
+  if (R <= 0) return {1, 1};
+  if (splits < 1) splits = 1;
+  const int64_t stages = (R + kBK - 1) / kBK;
+  const int64_t per = (stages + splits - 1) / splits;
+  const int64_t chunk = per * kBK > R ? R : per * kBK;
+  return {(int)chunk, (int)((R + chunk - 1) / chunk)};
+}
+
+// splits > 1 (no grad_input epilogue): the reduction range is cut as split_plan(R, splits) says,
+// each chunk writing its partial contraction to out + s * I * J.
+template <bool AT, bool GI, bool SF = true>
+hipError_t launch_bwd(bool bf, BwdArgs a, hipStream_t s, int splits = 1) {
   const int64_t tiles = (int64_t)((a.I + kBM - 1) / kBM) * ((a.J + kBN - 1) / kBN);
   if (tiles == 0) return hipSuccess;
+  const SplitPlan plan = split_plan(a.R, GI ? 1 : splits);
+  a.rchunk = plan.rchunk;
+  a.out_split = (int64_t)a.I * a.J;
+  const dim3 grid((unsigned)(tiles * plan.used));
   if (bf)
-    hipLaunchKernelGGL((bwd_gemm_kernel<true, AT, GI>), dim3((unsigned)tiles), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((bwd_gemm_kernel<true, AT, GI, SF>), grid, dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((bwd_gemm_kernel<false, AT, GI>), dim3((unsigned)tiles), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((bwd_gemm_kernel<false, AT, GI, SF>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 // ---- Conv backward (BinaryConv2dForward.backward on the qconv/binary/cutlass/layer page): the
 // page's conv2d_input and conv2d_weight, each lowered to the contraction above.
-//   grad_input: cols[pix][c*T + t] = scale_w * sum_o g[b][o][pix] * sign(W[o][c][t]) for every
-//   output pixel pix = (b, oh, ow) and tap t = kh*KW + kw, then each input element gathers the
-//   columns whose tap lands on it (col2im), is multiplied by the clip mask, and adds its
-//   grad_input * sign(x) to its workgroup's double sum.
+//   grad_input: colsT[c*T + t][pix] = scale_w * sum_o sign(W[o][c][t]) * g[b][o][pix] for every
+//   output pixel pix = (b, oh, ow) and tap t = kh*KW + kw (sign(W) formed once, the columns
+//   stored pixel-contiguous so the gather below reads them in runs), then each input element
+//   gathers the columns whose tap lands on it (col2im), is multiplied by the clip mask, and adds
+//   its grad_input * sign(x) to its workgroup's double sum.
 //   grad_weight: GW[o][c*T + t] = scale_a * sum_pix g[b][o][pix] * sign(xcol[pix][c*T + t]),
-//   xcol the unfolded input (0 where the tap falls in the padding), i.e. OIHW directly.
+//   xcol the unfolded input (0 where the tap falls in the padding), i.e. OIHW directly; the
+//   pixel axis is long and the output small, so the contraction is split along the pixels and
+//   the partial results are summed in a fixed order.
 // g is first copied to [O][B*Ho*Wo] so both contractions read it as a plain matrix.
 
 struct ConvGeom {
@@ -374,33 +410,64 @@ __global__ __launch_bounds__(kThreads) void conv_g_transpose_kernel(const uint16
 }
 
 // xcol[pix][c*T + t] = x[b][c][oh*SH - PH + kh*DH][ow*SW - PW + kw*DW], 0 outside the input. A
-// thread per (c, pix), pixels fastest, so neighbouring threads read neighbouring input columns.
+// thread fills 8 consecutive columns of one pixel with one 16-byte store (C*T is a multiple of
+// 8), so a wave writes 1 KB of consecutive bytes; the gathered reads of x hit the caches.
 __global__ __launch_bounds__(kThreads) void conv_im2col_kernel(const uint16_t* __restrict__ x,
                                                               uint16_t* __restrict__ xcol,
-                                                              ConvGeom q) {
+                                                              ConvGeom q, FastDiv div_t,
+                                                              FastDiv div_kw) {
   const int T = q.KH * q.KW, hwo = q.Ho * q.Wo;
-  const int64_t pixels = (int64_t)q.B * hwo, J = (int64_t)q.C * T;
-  const int64_t total = pixels * q.C;
+  const int64_t pixels = (int64_t)q.B * hwo;
+  const int J = q.C * T, J8 = J / 8;
+  const int64_t total = pixels * J8;
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total;
        i += (int64_t)gridDim.x * kThreads) {
-    const int c = (int)(i / pixels);
-    const int64_t pix = i - (int64_t)c * pixels;
+    const int64_t pix = i / J8;
+    const int j0 = (int)(i - pix * J8) * 8;
     const int b = (int)(pix / hwo), r = (int)(pix - (int64_t)b * hwo);
     const int oh = r / q.Wo, ow = r - oh * q.Wo;
-    const uint16_t* plane = x + ((int64_t)b * q.C + c) * q.H * q.W;
-    uint16_t* dst = xcol + pix * J + (int64_t)c * T;
-    for (int kh = 0; kh < q.KH; kh++) {
-      const int ih = oh * q.SH - q.PH + kh * q.DH;
-      for (int kw = 0; kw < q.KW; kw++) {
-        const int iw = ow * q.SW - q.PW + kw * q.DW;
+    uint32_t v[4];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      uint32_t pair = 0;
+#pragma unroll
+      for (int h = 0; h < 2; h++) {
+        const int jj = j0 + e + h;
+        const int c = div_t.div(jj), t = jj - c * T;
+        const int kh = div_kw.div(t), kw = t - kh * q.KW;
+        const int ih = oh * q.SH - q.PH + kh * q.DH, iw = ow * q.SW - q.PW + kw * q.DW;
         const bool in = ih >= 0 && ih < q.H && iw >= 0 && iw < q.W;
-        dst[kh * q.KW + kw] = in ? plane[(int64_t)ih * q.W + iw] : (uint16_t)0;
+        const uint32_t val = in ? x[(((int64_t)b * q.C + c) * q.H + ih) * q.W + iw] : 0u;
+        pair |= val << (16 * h);
       }
+      v[e / 2] = pair;
     }
+    *reinterpret_cast<uint4*>(xcol + pix * J + j0) = make_uint4(v[0], v[1], v[2], v[3]);
   }
 }
 
-// grad_in[b][c][ih][iw] = mid(x) * sum of cols[(b, oh, ow)][c*T + t] over the taps t whose output
+// out[i] = torch.sign of the 16-bit w[i], as bits of the same format.
+template <bool BF>
+__global__ __launch_bounds__(kThreads) void sign16_kernel(const uint16_t* __restrict__ w,
+                                                         uint16_t* __restrict__ out, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * kThreads)
+    out[i] = (uint16_t)sign_bits<BF>(w[i]);
+}
+
+// grad_w[i] = sum over the splits s = 0, 1, ... of part[s][i], in that order.
+__global__ __launch_bounds__(kThreads) void split_sum_kernel(const float* __restrict__ part,
+                                                            float* __restrict__ out, int64_t n,
+                                                            int splits) {
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * kThreads) {
+    float v = 0.0f;
+    for (int sp = 0; sp < splits; sp++) v += part[(int64_t)sp * n + i];
+    out[i] = v;
+  }
+}
+
+// grad_in[b][c][ih][iw] = mid(x) * sum of colsT[c*T + t][(b, oh, ow)] over the taps t whose output
 // pixel (oh, ow) = ((ih + PH - kh*DH) / SH, (iw + PW - kw*DW) / SW) exists (exact divisions, in
 // range), in tap order; each workgroup writes its double sum of grad_in * sign(x) (a fixed grid,
 // so the order of every sum is fixed).
@@ -411,7 +478,7 @@ __global__ __launch_bounds__(kThreads) void conv_col2im_kernel(const float* __re
                                                               double* __restrict__ part, ConvGeom q,
                                                               float scale_a) {
   const int T = q.KH * q.KW;
-  const int64_t J = (int64_t)q.C * T;
+  const int64_t pixels = (int64_t)q.B * q.Ho * q.Wo;
   const int64_t total = (int64_t)q.B * q.C * q.H * q.W;
   double sum = 0.0;
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total;
@@ -430,7 +497,7 @@ __global__ __launch_bounds__(kThreads) void conv_col2im_kernel(const float* __re
         const int nw = iw + q.PW - kw * q.DW;
         if (nw < 0 || nw % q.SW != 0 || nw / q.SW >= q.Wo) continue;
         const int ow = nw / q.SW;
-        v += cols[(((int64_t)b * q.Ho + oh) * q.Wo + ow) * J + (int64_t)c * T + kh * q.KW + kw];
+        v += cols[((int64_t)c * T + kh * q.KW + kw) * pixels + ((int64_t)b * q.Ho + oh) * q.Wo + ow];
       }
     }
     const float xv = widen16<BF>(x[i]);
@@ -507,21 +574,34 @@ int64_t conv_col2im_parts(int64_t n, int64_t c, int64_t h, int64_t w) {
   return grid_of(n * c * h * w, kCol2imBlocks);
 }
 
+int conv_wgrad_splits(int64_t o, int64_t j, int64_t pixels) {
+  const int64_t tiles = ((o + kBM - 1) / kBM) * ((j + kBN - 1) / kBN);
+  int64_t sp = (512 + tiles - 1) / tiles;   // about two workgroups per compute unit
+  // the number of chunks of whole stages launch_bwd actually makes of that request
+  return split_plan(pixels, sp > 0x7fffffff ? 0x7fffffff : (int)sp).used;
+}
+
 hipError_t launch_conv_grad_input(const void* g, const void* w, const void* x, bool bf,
                                   const int geom[15], float scale_a, float scale_w, float* grad_in,
-                                  uint16_t* gT, float* cols, double* part, double* grad_scale_a,
-                                  hipStream_t s) {
+                                  uint16_t* gT, uint16_t* wsign, float* cols, double* part,
+                                  double* grad_scale_a, hipStream_t s) {
   const ConvGeom q{geom[0], geom[1], geom[2], geom[3], geom[4], geom[5], geom[6], geom[7],
                    geom[8], geom[9], geom[10], geom[11], geom[12], geom[13], geom[14]};
-  const int hwo = q.Ho * q.Wo, T = q.KH * q.KW;
+  const int hwo = q.Ho * q.Wo, T = q.KH * q.KW, J = q.C * T;
   hipLaunchKernelGGL(conv_g_transpose_kernel, dim3((unsigned)grid_of((int64_t)q.B * q.O * kThreads, 8192)),
                      dim3(kThreads), 0, s, static_cast<const uint16_t*>(g), gT, q.B, q.O, hwo);
+  const int64_t nw = (int64_t)q.O * J;
+  if (bf)
+    hipLaunchKernelGGL(sign16_kernel<true>, dim3((unsigned)grid_of(nw, 4096)), dim3(kThreads), 0, s,
+                       static_cast<const uint16_t*>(w), wsign, nw);
+  else
+    hipLaunchKernelGGL(sign16_kernel<false>, dim3((unsigned)grid_of(nw, 4096)), dim3(kThreads), 0, s,
+                       static_cast<const uint16_t*>(w), wsign, nw);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // cols [B*Ho*Wo][C*T] = scale_w * gT^T @ sign(W viewed as [O][C*T])
-  BwdArgs a{gT, static_cast<const uint16_t*>(w), nullptr, cols, nullptr, q.B * hwo, q.C * T, q.O,
-            scale_w, scale_a};
-  e = launch_bwd<true, false>(bf, a, s);
+  // colsT [C*T][B*Ho*Wo] = scale_w * sign(W)^T @ gT: A = sign(W) stored [O][C*T], F = gT used as is
+  BwdArgs a{wsign, gT, nullptr, cols, nullptr, J, q.B * hwo, q.O, scale_w, scale_a};
+  e = launch_bwd<true, false, false>(bf, a, s);
   if (e != hipSuccess) return e;
   const int64_t total = (int64_t)q.B * q.C * q.H * q.W;
   const int parts = (int)grid_of(total, kCol2imBlocks);
@@ -540,21 +620,27 @@ hipError_t launch_conv_grad_input(const void* g, const void* w, const void* x, b
 
 hipError_t launch_conv_grad_weight(const void* g, const void* x, bool bf, const int geom[15],
                                    float scale_a, float* grad_w, uint16_t* gT, uint16_t* xcol,
-                                   hipStream_t s) {
+                                   float* split_part, hipStream_t s) {
   const ConvGeom q{geom[0], geom[1], geom[2], geom[3], geom[4], geom[5], geom[6], geom[7],
                    geom[8], geom[9], geom[10], geom[11], geom[12], geom[13], geom[14]};
-  const int hwo = q.Ho * q.Wo, T = q.KH * q.KW;
+  const int hwo = q.Ho * q.Wo, T = q.KH * q.KW, J = q.C * T;
   hipLaunchKernelGGL(conv_g_transpose_kernel, dim3((unsigned)grid_of((int64_t)q.B * q.O * kThreads, 8192)),
                      dim3(kThreads), 0, s, static_cast<const uint16_t*>(g), gT, q.B, q.O, hwo);
+  hipLaunchKernelGGL(conv_im2col_kernel, dim3((unsigned)grid_of((int64_t)q.B * hwo * (J / 8), 16384)),
+                     dim3(kThreads), 0, s, static_cast<const uint16_t*>(x), xcol, q,
+                     FastDiv((uint32_t)T), FastDiv((uint32_t)q.KW));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(conv_im2col_kernel, dim3((unsigned)grid_of((int64_t)q.B * hwo * q.C, 16384)),
-                     dim3(kThreads), 0, s, static_cast<const uint16_t*>(x), xcol, q);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  // GW [O][C*T] = scale_a * gT @ sign(xcol)
-  BwdArgs a{gT, xcol, nullptr, grad_w, nullptr, q.O, q.C * T, q.B * hwo, scale_a, scale_a};
-  return launch_bwd<false, false>(bf, a, s);
+  // GW [O][C*T] = scale_a * gT @ sign(xcol), split along the pixels, then the splits summed
+  const int splits = conv_wgrad_splits(q.O, J, (int64_t)q.B * hwo);
+  BwdArgs a{gT, xcol, nullptr, splits > 1 ? split_part : grad_w, nullptr, q.O, J, q.B * hwo,
+            scale_a, scale_a};
+  e = launch_bwd<false, false>(bf, a, s, splits);
+  if (e != hipSuccess || splits == 1) return e;
+  const int64_t n = (int64_t)q.O * J;
+  hipLaunchKernelGGL(split_sum_kernel, dim3((unsigned)grid_of(n, 4096)), dim3(kThreads), 0, s,
+                     split_part, grad_w, n, splits);
+  return hipGetLastError();
 }
 
 }  // namespace bnn

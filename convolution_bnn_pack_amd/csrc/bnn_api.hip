@@ -579,7 +579,8 @@ size_t bnn_conv2d_grad_input_workspace_bytes(int64_t n, int64_t c, int64_t h, in
   if (conv_bwd_geom(n, c, h, w, out_channels, kernel_h, kernel_w, stride_h, stride_w, pad_h, pad_w,
                     dil_h, dil_w, &q) != BNN_OK)
     return 0;
-  return round256((size_t)out_channels * q.pixels * 2) + round256((size_t)q.pixels * q.J * 4) +
+  return round256((size_t)out_channels * q.pixels * 2) + round256((size_t)out_channels * q.J * 2) +
+         round256((size_t)q.pixels * q.J * 4) +
          (size_t)bnn::conv_col2im_parts(n, c, h, w) * sizeof(double);
 }
 
@@ -606,11 +607,13 @@ bnn_status bnn_conv2d_grad_input(const void* grad_out, const void* weight, const
   if (!aligned(workspace, 256)) return BNN_ERR_ALIGN;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   uint16_t* gT = reinterpret_cast<uint16_t*>(ws);
-  float* cols = reinterpret_cast<float*>(ws + round256((size_t)out_channels * q.pixels * 2));
-  double* part = reinterpret_cast<double*>(reinterpret_cast<uint8_t*>(cols) +
-                                           round256((size_t)q.pixels * q.J * 4));
+  uint8_t* at = ws + round256((size_t)out_channels * q.pixels * 2);
+  uint16_t* wsign = reinterpret_cast<uint16_t*>(at);
+  at += round256((size_t)out_channels * q.J * 2);
+  float* cols = reinterpret_cast<float*>(at);
+  double* part = reinterpret_cast<double*>(at + round256((size_t)q.pixels * q.J * 4));
   return hip_status(bnn::launch_conv_grad_input(grad_out, weight, x, dtype == BNN_BF16, q.geom,
-                                                scale_a, scale_w, grad_in, gT, cols, part,
+                                                scale_a, scale_w, grad_in, gT, wsign, cols, part,
                                                 grad_scale_a, static_cast<hipStream_t>(stream)));
 }
 
@@ -622,7 +625,9 @@ size_t bnn_conv2d_grad_weight_workspace_bytes(int64_t n, int64_t c, int64_t h, i
   if (conv_bwd_geom(n, c, h, w, out_channels, kernel_h, kernel_w, stride_h, stride_w, pad_h, pad_w,
                     dil_h, dil_w, &q) != BNN_OK)
     return 0;
+  const int splits = bnn::conv_wgrad_splits(out_channels, q.J, q.pixels);
   return round256((size_t)out_channels * q.pixels * 2) + round256((size_t)q.pixels * q.J * 2) +
+         (splits > 1 ? round256((size_t)splits * out_channels * q.J * 4) : 0) +
          (size_t)bnn::bwd_quant_grad_parts(out_channels * q.J) * sizeof(float);
 }
 
@@ -649,10 +654,15 @@ bnn_status bnn_conv2d_grad_weight(const void* grad_out, const void* x, int dtype
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   uint16_t* gT = reinterpret_cast<uint16_t*>(ws);
   uint8_t* xc = ws + round256((size_t)out_channels * q.pixels * 2);
-  float* qpart = reinterpret_cast<float*>(xc + round256((size_t)q.pixels * q.J * 2));
+  const int splits = bnn::conv_wgrad_splits(out_channels, q.J, q.pixels);
+  float* split_part = reinterpret_cast<float*>(xc + round256((size_t)q.pixels * q.J * 2));
+  float* qpart = reinterpret_cast<float*>(
+      reinterpret_cast<uint8_t*>(split_part) +
+      (splits > 1 ? round256((size_t)splits * out_channels * q.J * 4) : 0));
   hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = bnn::launch_conv_grad_weight(grad_out, x, dtype == BNN_BF16, q.geom, scale_a,
-                                                    grad_w, gT, reinterpret_cast<uint16_t*>(xc), s);
+                                                    grad_w, gT, reinterpret_cast<uint16_t*>(xc),
+                                                    split_part, s);
   if (e != hipSuccess) return BNN_ERR_HIP;
   if (!grad_w_q) return BNN_OK;
   return hip_status(bnn::launch_quant_grad(grad_w, out_channels * q.J, qpart, amax, grad_w_q, s));

@@ -90,15 +90,18 @@ hipError_t launch_linear_grad_weight(const void* g, const void* x, bool bf, int6
 
 // Straight-through conv backward. geom = {B, C, H, W, O, KH, KW, SH, SW, PH, PW, DH, DW, Ho, Wo};
 // g [B][O][Ho][Wo], W [O][C][KH][KW] and x [B][C][H][W] of one 16-bit dtype; B*Ho*Wo and C*KH*KW
-// multiples of 8. grad_input: gT [O][B*Ho*Wo] u16 and cols [B*Ho*Wo][C*KH*KW] fp32 scratch,
-// conv_col2im_parts(B, C, H, W) doubles of part; grad_weight: gT and xcol [B*Ho*Wo][C*KH*KW] u16.
+// multiples of 8. grad_input scratch: gT [O][B*Ho*Wo] u16, wsign [O][C*KH*KW] u16, cols
+// [C*KH*KW][B*Ho*Wo] fp32, conv_col2im_parts(B, C, H, W) doubles of part. grad_weight scratch: gT,
+// xcol [B*Ho*Wo][C*KH*KW] u16 and, with conv_wgrad_splits(O, C*KH*KW, B*Ho*Wo) > 1, that many
+// partial [O][C*KH*KW] fp32 results.
 int64_t conv_col2im_parts(int64_t n, int64_t c, int64_t h, int64_t w);
+int conv_wgrad_splits(int64_t o, int64_t j, int64_t pixels);
 hipError_t launch_conv_grad_input(const void* g, const void* w, const void* x, bool bf,
                                   const int geom[15], float scale_a, float scale_w, float* grad_in,
-                                  uint16_t* gT, float* cols, double* part, double* grad_scale_a,
-                                  hipStream_t s);
+                                  uint16_t* gT, uint16_t* wsign, float* cols, double* part,
+                                  double* grad_scale_a, hipStream_t s);
 hipError_t launch_conv_grad_weight(const void* g, const void* x, bool bf, const int geom[15],
                                    float scale_a, float* grad_w, uint16_t* gT, uint16_t* xcol,
-                                   hipStream_t s);
+                                   float* split_part, hipStream_t s);
 
 }  // namespace bnn
