@@ -59,6 +59,11 @@
 
 #include "launch.h"
 
+// Tuning knob: a scheduling fence after every BNN_MFMA_SLOT_FENCE MFMA slots (0: none).
+#ifndef BNN_MFMA_SLOT_FENCE
+#define BNN_MFMA_SLOT_FENCE 4
+#endif
+
 // Tuning knob: fp4 convs with more tiles than resident workgroups run persistent workgroups.
 #ifndef BNN_CONV_PERS
 #define BNN_CONV_PERS 1
@@ -648,7 +653,8 @@ __global__ __launch_bounds__(T::THREADS) void mfma_kernel(Contraction p) {
       }
 #pragma unroll
       for (int u = i * NU / NM; u < (i + 1) * NU / NM; u++) expand_unit(nxt, u);
-      __builtin_amdgcn_sched_barrier(0);
+      if (BNN_MFMA_SLOT_FENCE > 0 && (i + 1) % (BNN_MFMA_SLOT_FENCE > 0 ? BNN_MFMA_SLOT_FENCE : 1) == 0)
+        __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
     if constexpr (PERS) {
