@@ -264,8 +264,35 @@ __device__ __forceinline__ void store_tile(const Contraction& p, const Acc (&acc
     // halves of their pixel quads so each stores eight consecutive pixels (16 bytes) at once
     constexpr bool HALF16 = OUT == kF16 || OUT == kBF16;
     const bool oct = HALF16 && (hw & 7) == 0;
-    auto bits16 = [&](int v) -> uint32_t {
-      const float f = (float)v * p.alpha;
+    // Everything that depends on the pixel but not on the feature is done once per tile
+    // rather than once per feature block: the row bases rowk (K_valid - 2 popA of each of the
+    // lane's 4 x 4 pixels per 32-pixel block) and the pixels' offsets in the output.
+    // Floating-point outputs take the dot product as fma(2, acc, rowk) in fp32: both terms
+    // are integers of magnitude at most K <= 2^24 and so is their sum, so it is exact, and
+    // the result is the same as converting the integer sum.
+    constexpr bool FDOT = OUT != kI32 && T::F4;
+    using RK = std::conditional_t<FDOT, float, int>;
+    RK rk[T::FM][16];
+#pragma unroll
+    for (int fm = 0; fm < T::FM; fm++)
+#pragma unroll
+      for (int e = 0; e < 16; e++) {
+        const int v = rowk(wm * T::WTM + fm * 32 + 8 * (e >> 2) + 4 * half + (e & 3));
+        rk[fm][e] = (RK)v;
+      }
+    auto dot = [&](int fn, int fm, int e) {
+      if constexpr (FDOT)
+        return __builtin_fmaf(2.0f, acc[fn][fm][e], rk[fm][e]);
+      else
+        return rk[fm][e] + 2 * acc_int(fn, fm, e);
+    };
+    auto scaled = [&](int fn, int fm, int e) -> float {
+      if constexpr (FDOT)
+        return dot(fn, fm, e) * p.alpha;
+      else
+        return (float)dot(fn, fm, e) * p.alpha;
+    };
+    auto bits16 = [&](float f) -> uint32_t {
       if constexpr (OUT == kF16) {
         const __half h = __float2half_rn(f);
         return *reinterpret_cast<const uint16_t*>(&h);
@@ -274,12 +301,97 @@ __device__ __forceinline__ void store_tile(const Contraction& p, const Acc (&acc
         return *reinterpret_cast<const uint16_t*>(&h);
       }
     };
+    const int64_t plane = (int64_t)p.N * hw;  // output elements per image
+    using O = OutType<OUT>;
+    typename O::type* const out = reinterpret_cast<typename O::type*>(p.out);
+    // Staged write-out (planes a multiple of 4). Stored straight from the MFMA layout, each
+    // store instruction would put 32 features x 8..32 bytes into 32 channel planes, a
+    // fraction of a memory line each. Instead each wave turns one 32-feature block around in
+    // its own 4 KiB of LDS (32 rows of 128 bytes, one per feature, holding PXS consecutive
+    // pixels) and stores it back row-wise: LPC lanes per feature, 8 or 16 bytes each, so
+    // an instruction writes whole 128-byte runs of 64 / LPC channel planes. Rows are
+    // XOR-swizzled in 16-byte chunks (chunk k of row r at k ^ (r & 7)) to spread the
+    // column-wise writes over the banks. `lds0` is a free buffer of T::BUF bytes.
+    constexpr int ESZ = (int)sizeof(typename O::type);
+    constexpr int PXS = 128 / ESZ < T::WTM ? 128 / ESZ : T::WTM;  // pixels per staged row
+    constexpr int FMS = PXS / 32;                                 // MFMA blocks per row
+    constexpr int NWAVES = T::WGM * T::WGN;
+    constexpr bool STAGED = PXS * ESZ == 128 && NWAVES * 4096 <= T::BUF;
+    if constexpr (STAGED) {
+      if (quad) {
+        const int pl = (ESZ == 2 && !oct) ? 4 : 16 / ESZ;  // pixels per lane store
+        const int lpc = PXS / pl;                           // lanes per feature row
+        const int cpi = 64 / lpc;                           // feature rows per instruction
+        uint8_t* const st = lds0 + wave * 4096;
+        auto at = [&](int r, int byte) { return st + r * 128 + (((byte >> 4) ^ (r & 7)) << 4) + (byte & 15); };
 #pragma unroll
-    for (int fn = 0; fn < T::FN; fn++) {
-      const int n = n0 + wn * T::WTN + fn * 32 + fr;
-      if (n >= p.N) continue;  // uniform over the lane pair fr, fr + 32
-      if constexpr (HALF16) {
-        if (oct) {
+        for (int f0 = 0; f0 < T::FM; f0 += FMS) {
+          // this lane's pixel run of the read-back, the same for every feature
+          const int mrun = m0 + wm * T::WTM + f0 * 32 + (lane % lpc) * pl;
+          const bool mok = mrun < p.M;
+          const int b = p.div_hw.div(mok ? mrun : 0);
+          typename O::type* const orun = out + (int64_t)b * plane + (mrun - b * hw);
+          const int rbyte = (lane % lpc) * pl * ESZ;
+#pragma unroll
+          for (int fn = 0; fn < T::FN; fn++) {
+#pragma unroll
+            for (int ff = 0; ff < FMS; ff++)
+#pragma unroll
+              for (int g = 0; g < 4; g++) {
+                const int fm = f0 + ff, e = 4 * g;
+                uint8_t* const dst = at(fr, (ff * 32 + 8 * g + 4 * half) * ESZ);
+                if constexpr (OUT == kI32) {
+                  *reinterpret_cast<int4*>(dst) = make_int4(dot(fn, fm, e), dot(fn, fm, e + 1),
+                                                            dot(fn, fm, e + 2), dot(fn, fm, e + 3));
+                } else if constexpr (OUT == kF32) {
+                  *reinterpret_cast<float4*>(dst) = make_float4(scaled(fn, fm, e), scaled(fn, fm, e + 1),
+                                                                scaled(fn, fm, e + 2), scaled(fn, fm, e + 3));
+                } else {
+                  *reinterpret_cast<uint2*>(dst) =
+                      make_uint2(bits16(scaled(fn, fm, e)) | (bits16(scaled(fn, fm, e + 1)) << 16),
+                                 bits16(scaled(fn, fm, e + 2)) | (bits16(scaled(fn, fm, e + 3)) << 16));
+                }
+              }
+            // the rows are private to this wave and its LDS accesses complete in order
+            __builtin_amdgcn_wave_barrier();
+            const int nb = n0 + wn * T::WTN + fn * 32;
+            for (int i = 0; i < 32 / cpi; i++) {
+              const int r = lane / lpc + cpi * i;
+              const bool ok = mok && nb + r < p.N;
+              typename O::type* const dst = orun + (int64_t)(nb + r) * hw;
+              if (pl * ESZ == 16) {
+                const uint4 v = *reinterpret_cast<const uint4*>(at(r, rbyte));
+                if (ok) *reinterpret_cast<uint4*>(dst) = v;
+              } else {
+                const uint2 v = *reinterpret_cast<const uint2*>(at(r, rbyte));
+                if (ok) *reinterpret_cast<uint2*>(dst) = v;
+              }
+            }
+            __builtin_amdgcn_wave_barrier();
+          }
+        }
+        return;
+      }
+    }
+    if constexpr (HALF16) {
+      if (oct) {
+        // 16-pixel runs: pixels m0 + wm*WTM + fm*32 + 16j + 8*half + 0..7 leave from this lane
+        int64_t off[T::FM][2];
+        bool mok[T::FM][2];
+#pragma unroll
+        for (int fm = 0; fm < T::FM; fm++)
+#pragma unroll
+          for (int j = 0; j < 2; j++) {
+            const int mg = m0 + wm * T::WTM + fm * 32 + 16 * j + 8 * half;
+            mok[fm][j] = mg < p.M;
+            const int b = p.div_hw.div(mok[fm][j] ? mg : 0);
+            off[fm][j] = (int64_t)b * plane + (mg - b * hw);
+          }
+#pragma unroll
+        for (int fn = 0; fn < T::FN; fn++) {
+          const int n = n0 + wn * T::WTN + fn * 32 + fr;
+          if (n >= p.N) continue;  // uniform over the lane pair fr, fr + 32
+          typename O::type* const col = out + (int64_t)n * hw;
 #pragma unroll
           for (int fm = 0; fm < T::FM; fm++)
 #pragma unroll
@@ -289,48 +401,80 @@ __device__ __forceinline__ void store_tile(const Contraction& p, const Acc (&acc
 #pragma unroll
               for (int gg = 0; gg < 2; gg++) {
                 const int g = 2 * j + gg;
-                const int ml = wm * T::WTM + fm * 32 + 8 * g + 4 * half;
                 uint32_t h4[4];
 #pragma unroll
-                for (int i = 0; i < 4; i++) h4[i] = bits16(rowk(ml + i) + 2 * acc_int(fn, fm, 4 * g + i));
+                for (int i = 0; i < 4; i++) h4[i] = bits16(scaled(fn, fm, 4 * g + i));
                 q[gg][0] = h4[0] | (h4[1] << 16);
                 q[gg][1] = h4[2] | (h4[3] << 16);
               }
               const uint32_t s0 = half ? q[0][0] : q[1][0], s1 = half ? q[0][1] : q[1][1];
               const uint32_t r0 = (uint32_t)__shfl_xor((int)s0, 32), r1 = (uint32_t)__shfl_xor((int)s1, 32);
-              const int mg = m0 + wm * T::WTM + fm * 32 + 16 * j + 8 * half;
-              if (mg < p.M) {
-                const int b = p.div_hw.div(mg), pix = mg - b * hw;
+              if (mok[fm][j]) {
                 const uint4 v = half ? make_uint4(r0, r1, q[1][0], q[1][1]) : make_uint4(q[0][0], q[0][1], r0, r1);
-                *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.out) + ((int64_t)b * p.N + n) * hw + pix) = v;
+                *reinterpret_cast<uint4*>(col + off[fm][j]) = v;
               }
             }
-          continue;
         }
+        return;
       }
+    }
+    if (quad) {
+      int64_t off[T::FM][4];
+      bool mok[T::FM][4];
 #pragma unroll
       for (int fm = 0; fm < T::FM; fm++)
 #pragma unroll
         for (int g = 0; g < 4; g++) {
-          const int ml = wm * T::WTM + fm * 32 + 8 * g + 4 * half;
-          const int m = m0 + ml;
-          if (m >= p.M) continue;
-          const int4 bk = {rowk(ml), rowk(ml + 1), rowk(ml + 2), rowk(ml + 3)};
-          const int v0 = bk.x + 2 * acc_int(fn, fm, 4 * g), v1 = bk.y + 2 * acc_int(fn, fm, 4 * g + 1);
-          const int v2 = bk.z + 2 * acc_int(fn, fm, 4 * g + 2), v3 = bk.w + 2 * acc_int(fn, fm, 4 * g + 3);
-          const int b = p.div_hw.div(m), pix = m - b * hw;
-          if (quad) {
-            store4<OUT>(p.out, ((int64_t)b * p.N + n) * hw + pix, v0, v1, v2, v3, p.alpha);
-          } else {
-            const int vals[4] = {v0, v1, v2, v3};
+          const int m = m0 + wm * T::WTM + fm * 32 + 8 * g + 4 * half;
+          mok[fm][g] = m < p.M;
+          const int b = p.div_hw.div(mok[fm][g] ? m : 0);
+          off[fm][g] = (int64_t)b * plane + (m - b * hw);
+        }
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-              const int mi = m + i;
-              if (mi >= p.M) break;
-              const int bi = p.div_hw.div(mi), pi = mi - bi * hw;
-              store1<OUT>(p.out, ((int64_t)bi * p.N + n) * hw + pi, vals[i], p.alpha);
+      for (int fn = 0; fn < T::FN; fn++) {
+        const int n = n0 + wn * T::WTN + fn * 32 + fr;
+        if (n >= p.N) continue;
+        typename O::type* const col = out + (int64_t)n * hw;
+#pragma unroll
+        for (int fm = 0; fm < T::FM; fm++)
+#pragma unroll
+          for (int g = 0; g < 4; g++) {
+            if (!mok[fm][g]) continue;
+            typename O::type* const dst = col + off[fm][g];
+            if constexpr (OUT == kI32) {
+              *reinterpret_cast<int4*>(dst) = make_int4(dot(fn, fm, 4 * g), dot(fn, fm, 4 * g + 1),
+                                                        dot(fn, fm, 4 * g + 2), dot(fn, fm, 4 * g + 3));
+            } else if constexpr (OUT == kF32) {
+              *reinterpret_cast<float4*>(dst) = make_float4(scaled(fn, fm, 4 * g), scaled(fn, fm, 4 * g + 1),
+                                                            scaled(fn, fm, 4 * g + 2), scaled(fn, fm, 4 * g + 3));
+            } else {
+              const uint32_t lo = bits16(scaled(fn, fm, 4 * g)) | (bits16(scaled(fn, fm, 4 * g + 1)) << 16);
+              const uint32_t hi = bits16(scaled(fn, fm, 4 * g + 2)) | (bits16(scaled(fn, fm, 4 * g + 3)) << 16);
+              *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
             }
           }
+      }
+      return;
+    }
+    // planes of any size: element stores, each pixel's image found on its own
+#pragma unroll
+    for (int fn = 0; fn < T::FN; fn++) {
+      const int n = n0 + wn * T::WTN + fn * 32 + fr;
+      if (n >= p.N) continue;
+#pragma unroll
+      for (int fm = 0; fm < T::FM; fm++)
+#pragma unroll
+        for (int e = 0; e < 16; e++) {
+          const int m = m0 + wm * T::WTM + fm * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
+          if (m >= p.M) continue;
+          const int b = p.div_hw.div(m);
+          const int64_t idx = (int64_t)b * plane + (int64_t)n * hw + (m - b * hw);
+          if constexpr (OUT == kI32)
+            out[idx] = dot(fn, fm, e);
+          else if constexpr (OUT == kF32)
+            out[idx] = scaled(fn, fm, e);
+          else
+            reinterpret_cast<uint16_t*>(p.out)[idx] = (uint16_t)bits16(scaled(fn, fm, e));
         }
     }
   } else {
@@ -558,7 +702,8 @@ __global__ __launch_bounds__(T::THREADS) void mfma_kernel(Contraction p) {
 
   // epilogue of the tile whose last stage just ended (persistent: tile ct)
   int ct = 0, cs = 0;
-  auto tile_epilogue = [&](int i) __attribute__((always_inline)) {
+  // free: an LDS buffer (T::BUF bytes) that no wave reads or writes during the epilogue
+  auto tile_epilogue = [&](int i, uint8_t* free) __attribute__((always_inline)) {
     int m0, n0;
     tile_origin(i, m0, n0);
     if constexpr (PERS) {
@@ -571,9 +716,9 @@ __global__ __launch_bounds__(T::THREADS) void mfma_kernel(Contraction p) {
             for (int j = 0; j < T::A_TPR; j++) v += slots[ml * T::A_TPR + j];
             return v;
           },
-          lds0, lds1, m0, n0, wm, wn);
+          free, nullptr, m0, n0, wm, wn);
     } else {
-      store_tile<T, OUT, CONV>(p, acc, [&](int ml) { return rowk[ml]; }, lds0, lds1, m0, n0, wm, wn);
+      store_tile<T, OUT, CONV>(p, acc, [&](int ml) { return rowk[ml]; }, free, lds1, m0, n0, wm, wn);
     }
   };
 
@@ -622,7 +767,7 @@ __global__ __launch_bounds__(T::THREADS) void mfma_kernel(Contraction p) {
   // clamped, invalid words.
   auto stage = [&](auto phase, int s) {
     constexpr int PH = decltype(phase)::value;
-    const uint8_t* cur = (PH & 1) ? lds1 : lds0;
+    uint8_t* cur = (PH & 1) ? lds1 : lds0;
     uint8_t* nxt = (PH & 1) ? lds0 : lds1;
     if constexpr (PERS)
       load_next(PH % T::PD);
@@ -659,7 +804,10 @@ __global__ __launch_bounds__(T::THREADS) void mfma_kernel(Contraction p) {
     __syncthreads();
     if constexpr (PERS) {
       if (++cs == nstages) {
-        tile_epilogue(ct);
+        // the finished stage's buffer is free until the next stage expands into it; the
+        // barrier keeps that expansion off the rows other waves still stage through
+        tile_epilogue(ct, cur);
+        __syncthreads();
         clear_acc();
         cs = 0;
         ++ct;
@@ -737,7 +885,7 @@ __global__ __launch_bounds__(T::THREADS) void mfma_kernel(Contraction p) {
     }
     atomicAdd(&rowk[a_row], rowk_part);
     __syncthreads();
-    tile_epilogue(0);
+    tile_epilogue(0, lds0);
   }
 }
 
@@ -864,11 +1012,13 @@ hipError_t launch_mfma_t(const Contraction& p, int out_dtype, hipStream_t stream
   constexpr int64_t kMinTiles = BNN_MFMA_MIN_TILES;  // one workgroup per compute unit
   using TS = Tiles<F4, CONV>;
 #if defined(BNN_CONV_TILE)
-  // tuning builds: one fixed fp4 conv tile (1: 128 x 256, 2: 128 x 128, 3: 64 x 128)
+  // tuning builds: one fixed fp4 conv tile (1: 128 x 256, 2: 128 x 128, 3: 64 x 128, 4: see below)
   if constexpr (CONV && F4) {
     if (BNN_CONV_TILE == 1) return launch_tile<typename TS::M, CONV>(p, out_dtype, stream);
     if (BNN_CONV_TILE == 2) return launch_tile<typename TS::S, CONV>(p, out_dtype, stream);
     if (BNN_CONV_TILE == 3) return launch_tile<typename TS::T64, CONV>(p, out_dtype, stream);
+    if (BNN_CONV_TILE == 4)  // 128 x 128, 2 x 2 waves: two workgroups per compute unit
+      return launch_tile<Tile<128, 128, TS::KS, TS::PD_M, 2, 2, F4>, CONV>(p, out_dtype, stream);
   }
 #endif
   if (F4 && p.N <= 64 && count_tiles(p, 256, 64) >= kMinTiles)

@@ -7,6 +7,7 @@
 // row lands in bit j of word q, bit value 1 when the element is >= 0.
 #include "launch.h"
 
+
 namespace bnn {
 namespace {
 
@@ -386,13 +387,33 @@ __global__ __launch_bounds__(256) void abs_mean_final_kernel(const double* __res
   if (threadIdx.x == 0) out[0] = factor * (t / count);
 }
 
+// 8 x 8 bit transpose of a matrix held as two dwords, row r in byte r (lo: rows 0-3, hi:
+// rows 4-7), bit c of a row = column c: afterwards byte c holds column c, bit r = row r.
+// Three rounds swap ever larger off-diagonal blocks (1x1 inside 2x2, 2x2 inside 4x4, 4x4
+// inside 8x8; the delta-swap method, see Warren, Hacker's Delight, section 7-3).
+__device__ __forceinline__ void transpose8x8(uint32_t& lo, uint32_t& hi) {
+  uint32_t t;
+  t = (lo ^ (lo >> 7)) & 0x00AA00AAu;
+  lo ^= t ^ (t << 7);
+  t = (hi ^ (hi >> 7)) & 0x00AA00AAu;
+  hi ^= t ^ (t << 7);
+  t = (lo ^ (lo >> 14)) & 0x0000CCCCu;
+  lo ^= t ^ (t << 14);
+  t = (hi ^ (hi >> 14)) & 0x0000CCCCu;
+  hi ^= t ^ (t << 14);
+  t = (lo ^ (hi << 4)) & 0xF0F0F0F0u;
+  lo ^= t;
+  hi ^= t >> 4;
+}
+
 // NCHW pack over the flattened (image, pixel) axis, for planes whose pixel count is a
 // multiple of the 16-byte vector width V (and a 16-byte aligned tensor): a workgroup packs
 // word q of 64*V consecutive pixels of the whole batch, each lane's V pixels lying in one
 // image, so no chunk is left partly empty at the end of an image plane (with 28x28 planes
-// and 512-pixel chunks per image, a quarter of the lanes idled). Otherwise as
-// pack_nchw_kernel: wave w loads channels 8w..8w+7 of the word with eight 16-byte loads
-// in flight, bytes meet in LDS, words leave in pixel order.
+// and 512-pixel chunks per image, a quarter of the lanes idled). Wave w loads channels
+// 8w..8w+7 of the word (eight 16-byte loads in flight, each load instruction reading 1 KiB
+// of one channel plane), an 8 x 8 bit transpose turns the channel bytes into pixel bytes,
+// the four waves' bytes meet in LDS and the words leave in pixel order.
 template <int DT, int V, int BDT>
 __global__ __launch_bounds__(256) void pack_nchw_flat_kernel(const void* __restrict__ x,
                                                              uint32_t* __restrict__ out, int C,
@@ -411,37 +432,47 @@ __global__ __launch_bounds__(256) void pack_nchw_flat_kernel(const void* __restr
     float shift[8];
     if constexpr (BDT >= 0) {
 #pragma unroll
-      for (int c = 0; c < 8; c++) shift[c] = c < nch ? elem_f32<BDT>(bias, c0 + c) + 0.0f : 0.0f;
+      for (int c = 0; c < 8; c++) shift[c] = elem_f32<BDT>(bias, c < nch ? c0 + c : 0) + 0.0f;
     }
     for (int ch = blockIdx.x; ch < nchunks; ch += gridDim.x) {
+      // all eight loads go out before any is used (a load behind a branch would be waited
+      // for on the spot); lanes past the end read pixel 0, missing channels (none, or fewer
+      // than 8, exist in a last, partly filled word) re-read channel 0, and both give 0 bits
       const int f0 = ch * PIX + lane * V;
       const bool ok = f0 < P;
-      const int b = ok ? f0 / HW : 0;
-      const int pix = f0 - b * HW;
-      const char* src0 = reinterpret_cast<const char*>(x) + (((int64_t)b * C + c0) * HW + pix) * ES;
-      uint32_t bits[8];
+      const int fc = ok ? f0 : 0;
+      const int b = fc / HW;
+      const int pix = fc - b * HW;
+      const char* img = reinterpret_cast<const char*>(x) + ((int64_t)b * C * HW + pix) * ES;
+      u32x4 vin[8];
+#pragma unroll
+      for (int c = 0; c < 8; c++)
+        vin[c] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(img + (int64_t)(c < nch ? c0 + c : 0) * HW * ES));
+      // keep the scheduler from sinking each load to its use
+      __builtin_amdgcn_sched_barrier(0);
+      // byte c of (lo, hi) = the V pixel bits of channel c0 + c
+      uint32_t lo = 0, hi = 0;
 #pragma unroll
       for (int c = 0; c < 8; c++) {
-        if (ok && c < nch) {
-          const u32x4 v = __builtin_nontemporal_load(
-              reinterpret_cast<const u32x4*>(src0 + (int64_t)c * HW * ES));
-          if constexpr (BDT >= 0)
-            bits[c] = vec_bits_shift<DT, V, false>(v, &shift[c]);
-          else
-            bits[c] = vec_bits<DT>(v);
-        } else {
-          bits[c] = 0u;
-        }
+        uint32_t bb;
+        if constexpr (BDT >= 0)
+          bb = vec_bits_shift<DT, V, false>(vin[c], &shift[c]);
+        else
+          bb = vec_bits<DT>(vin[c]);
+        bb = (ok && c < nch) ? bb : 0u;
+        if (c < 4)
+          lo |= bb << (8 * c);
+        else
+          hi |= bb << (8 * (c - 4));
       }
+      transpose8x8(lo, hi);  // now byte v = the 8 channel bits of pixel v
       uint8_t* wbytes = reinterpret_cast<uint8_t*>(words);
 #pragma unroll
-      for (int v = 0; v < V; v++) {
-        uint32_t byte = 0;
-#pragma unroll
-        for (int c = 0; c < 8; c++) byte |= ((bits[c] >> v) & 1u) << c;
-        wbytes[(lane * V + v) * 4 + wave] = (uint8_t)byte;
-      }
+      for (int v = 0; v < V; v++)
+        wbytes[(lane * V + v) * 4 + wave] = (uint8_t)((v < 4 ? lo : hi) >> (8 * (v & 3)));
       __syncthreads();
+#pragma unroll
       for (int i = threadIdx.x; i < PIX; i += 256) {
         const int f = ch * PIX + i;
         if (f < P) out[(int64_t)f * CW + q] = words[i];
@@ -511,8 +542,8 @@ void launch_nchw_b(dim3 grid, const void* x, uint32_t* out, int64_t c, int64_t H
 template <int DT, int V, int BDT>
 void launch_nchw_flat_t(dim3 grid, const void* x, uint32_t* out, int64_t c, int64_t HW, int64_t CW,
                         int64_t P, const void* bias, hipStream_t stream) {
-  hipLaunchKernelGGL((pack_nchw_flat_kernel<DT, V, BDT>), grid, dim3(256), 0, stream, x, out, (int)c,
-                     (int)HW, (int)CW, (int)P, bias);
+  hipLaunchKernelGGL((pack_nchw_flat_kernel<DT, V, BDT>), grid, dim3(256), 0, stream, x,
+                     out, (int)c, (int)HW, (int)CW, (int)P, bias);
 }
 
 template <int DT, int V>

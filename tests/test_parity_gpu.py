@@ -53,8 +53,11 @@ def test_pack_rows_bit_exact(bnn, orc, tdt):
 @pytest.mark.parametrize("tdt", [torch.float32, torch.float16, torch.bfloat16])
 def test_pack_nchw_bit_exact(bnn, orc, tdt):
     g = torch.Generator().manual_seed(22)
+    # 16-byte vector path (pixel planes a multiple of 8) with partly filled last words, more
+    # than eight words per pixel (two passes of the slab kernel) and many pixel chunks
     for shape in [(1, 32, 1, 1), (2, 64, 5, 3), (3, 96, 7, 9), (2, 256, 14, 14), (1, 128, 28, 28),
-                  (2, 32, 4, 4), (1, 64, 3, 8)]:
+                  (2, 32, 4, 4), (1, 64, 3, 8), (3, 40, 4, 8), (2, 300, 2, 8), (1, 520, 4, 4),
+                  (5, 8, 8, 8), (9, 128, 12, 12), (2, 200, 8, 6)]:
         x = synth.inject_edges(torch.randn(shape, generator=g).to(tdt), sum(shape), max(1, math.prod(shape) // 20))
         _say(f"pack_nchw {tdt} {shape}")
         got = bnn.pack_sign_nchw(x.to(DEV)).cpu()

@@ -63,7 +63,7 @@ def test_pack_rows_shift_bit_exact(bnn, orc, xdt, bdt):
 def test_pack_nchw_shift_bit_exact(bnn, orc, xdt, bdt):
     # pixel counts that take the 16-byte vector path and ones that do not
     for shape in [(1, 32, 1, 1), (2, 64, 5, 3), (3, 96, 7, 9), (2, 256, 14, 14), (1, 128, 28, 28),
-                  (2, 32, 4, 4)]:
+                  (2, 32, 4, 4), (3, 40, 4, 8), (2, 300, 2, 8), (5, 8, 8, 8)]:
         seed = sum(shape) * 3 + len(xdt) + 7 * len(bdt)
         g = torch.Generator().manual_seed(seed)
         x = synth.inject_edges(torch.randn(shape, generator=g).to(DT[xdt]), seed, max(1, math.prod(shape) // 25))
