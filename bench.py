@@ -227,6 +227,87 @@ def cpu_baseline(wl, x, w):
             "sample": f"{sample} ({dt:.2f} s, sign + contraction + scale)"}
 
 
+# Shapes of the path table (--path-table): linear (m, n, k) and conv
+# (batch, c, h, w, out_channels, kernel, stride, padding, dilation).
+PATH_TABLE_LINEAR = [(64, 256, 512), (128, 256, 1024), (256, 256, 1024), (256, 512, 2048),
+                     (512, 512, 2048), (512, 1024, 2048), (1024, 1024, 1024), (1024, 1024, 4096),
+                     (1024, 2048, 4096), (2048, 2048, 2048), (2048, 4096, 4096), (4096, 4096, 4096),
+                     (8192, 8192, 8192), (64, 4096, 4096), (16, 8192, 8192)]
+PATH_TABLE_CONV = [(1, 64, 14, 14, 64, 3, 1, 1, 1), (8, 64, 28, 28, 64, 3, 1, 1, 1),
+                   (32, 256, 14, 14, 256, 3, 1, 1, 1), (128, 128, 28, 28, 256, 3, 2, 1, 1),
+                   (128, 128, 28, 28, 256, 3, 1, 2, 2), (16, 512, 7, 7, 512, 3, 1, 1, 1),
+                   (64, 64, 56, 56, 64, 3, 1, 1, 1), (8, 256, 14, 14, 256, 1, 1, 0, 1)]
+
+
+def path_table():
+    """Kernel time of the three contraction paths (XOR, int8 MFMA, fp4 MFMA) over linear and conv
+    shapes on random packed words (f16 output; HIP events around a graph of 50 back-to-back
+    launches), and the path AUTO picks; prints a markdown table."""
+    import torch
+
+    import convolution_bnn_pack_amd as bnn
+
+    dev = torch.device("cuda:0")
+    lib = bnn.lib
+    gen = torch.Generator(device=dev).manual_seed(0)
+
+    def words(*shape):
+        return torch.randint(-2 ** 31, 2 ** 31 - 1, shape, dtype=torch.int32, device=dev, generator=gen)
+
+    def time_call(f, reps=50):
+        for _ in range(3):
+            assert f() == 0
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                f()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
+
+    paths = [("XOR", bnn.PATH_XOR), ("int8", bnn.PATH_MFMA), ("fp4", bnn.PATH_MFMA_FP4)]
+    names = {bnn.PATH_XOR: "XOR", bnn.PATH_MFMA: "int8", bnn.PATH_MFMA_FP4: "fp4"}
+    print("| layer | MACs | XOR us | int8 us | fp4 us | AUTO | fastest |")
+    print("|---|---|---|---|---|---|---|")
+    for shape in PATH_TABLE_LINEAR + PATH_TABLE_CONV:
+        if len(shape) == 3:
+            m, n, k = shape
+            xp, wp = words(m, k // 32), words(n, k // 32)
+            out = torch.empty((m, n), dtype=torch.float16, device=dev)
+            label, macs = f"linear {m}x{n}x{k}", m * n * k
+            auto = lib.bnn_gemm_auto_path(m, n, k)
+
+            def call(path):
+                return lambda: lib.bnn_gemm(xp.data_ptr(), bnn.U32_PACKED, wp.data_ptr(), m, n, k, 1.0, 1.0,
+                                            path, out.data_ptr(), bnn.F16, None, 0,
+                                            torch.cuda.current_stream().cuda_stream)
+        else:
+            b, c, h, w, o, ks, st, pd, dl = shape
+            ho = (h + 2 * pd - dl * (ks - 1) - 1) // st + 1
+            wo = (w + 2 * pd - dl * (ks - 1) - 1) // st + 1
+            cw = (c + 31) // 32
+            xp, wp = words(b, h, w, cw), words(o, ks, ks, cw)
+            out = torch.empty((b, o, ho, wo), dtype=torch.float16, device=dev)
+            label = f"conv {b}x{c}x{h}x{w}->{o}, {ks}x{ks} s{st} p{pd} d{dl}"
+            macs = b * ho * wo * o * c * ks * ks
+            auto = lib.bnn_conv2d_auto_path(b, c, h, w, o, ks, st, pd, dl)
+
+            def call(path):
+                return lambda: lib.bnn_conv2d(xp.data_ptr(), bnn.U32_PACKED, b, c, h, w, wp.data_ptr(), o, 1.0,
+                                              1.0, ks, st, pd, dl, path, out.data_ptr(), bnn.F16, None, 0,
+                                              torch.cuda.current_stream().cuda_stream)
+        t = {name: time_call(call(code)) for name, code in paths}
+        best = min(t, key=t.get)
+        print(f"| {label} | {macs:.3g} | {t['XOR']:.1f} | {t['int8']:.1f} | {t['fp4']:.1f} | "
+              f"{names.get(auto, auto)} | {best} |", flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -244,7 +325,13 @@ def main():
                          "bytes per launch of the workload's dominant kernel in profiles/traffic.json")
     ap.add_argument("--copy-kernel", default="copyBuffer",
                     help="substring naming the copy kernel in the counter files")
+    ap.add_argument("--path-table", action="store_true",
+                    help="time the three contraction paths over a set of linear and conv shapes "
+                         "and print a markdown table (nothing else runs)")
     args = ap.parse_args()
+    if args.path_table:
+        path_table()
+        return
     if args.pmc_summary:
         pmc_summary(args)
         return
