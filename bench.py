@@ -44,6 +44,9 @@ CODEC_WORKLOADS = {
     "pack_nchw_32x256x14x14_f32": ("pack_nchw", "conv_resnet18_s3_f32", None),
     "pack_shift_nchw_128x128x28x28_f16": ("pack_nchw", "conv_down_s2_f16", "f16"),
     "abs_mean_16384x8192_bf16": ("abs_mean", "linear_16384x8192x8192_bf16", None),
+    # one-pass prologue: the shifted pack and the lazy scale's sum of |x| from one read of x
+    "prologue_linear_16384x8192_bf16": ("prologue", "linear_16384x8192x8192_bf16", "f32"),
+    "prologue_nchw_128x128x28x28_f16": ("prologue_nchw", "conv_down_s2_f16", "f16"),
 }
 # W8A8 conv workloads (the blog's quantized im2col + GEMM): name -> (conv workload, amax_x, amax_w)
 W8A8_WORKLOADS = {
@@ -67,15 +70,16 @@ PACK_WORKLOAD = "pack_linear_16384x8192_bf16"
 KERNEL_SOURCES = {"mfma": "gemm_mfma.hip", "mfma_fp4": "gemm_mfma.hip", "xor": "gemm_xor.hip",
                   "w8a8": "w8a8.hip", "bwd": "backward.hip",
                   "pack": "pack.hip", "pack_shift": "pack.hip", "pack_nchw": "pack.hip",
-                  "abs_mean": "pack.hip"}
+                  "abs_mean": "pack.hip", "prologue": "pack.hip", "prologue_nchw": "pack.hip"}
 KERNEL_NAMES = {"mfma": "mfma_kernel", "mfma_fp4": "mfma_kernel", "xor": "xor_kernel",
                 "w8a8": "w8a8_conv_kernel", "bwd": "bwd_gemm_kernel",
                 "pack": "pack_rows_kernel", "pack_shift": "pack_rows_shift_kernel",
-                "pack_nchw": "pack_nchw_flat_kernel", "abs_mean": "abs_sum_kernel"}
+                "pack_nchw": "pack_nchw_flat_kernel", "abs_mean": "abs_sum_kernel",
+                "prologue": "pack_rows_shift_kernel", "prologue_nchw": "pack_nchw_flat_kernel"}
 PEAKS = {"mfma": PEAK_MFMA_I8_TOPS, "mfma_fp4": PEAK_MFMA_F4_TOPS, "xor": PEAK_VALU_BINARY_TOPS,
          "w8a8": PEAK_MFMA_I8_TOPS, "bwd": PEAK_MFMA_BF16_TFLOPS}
 DTYPES = {"mfma": "i8", "mfma_fp4": "fp4(e2m1)", "xor": "u32", "w8a8": "i8"}
-CODEC_KINDS = ("pack", "pack_shift", "pack_nchw", "abs_mean")
+CODEC_KINDS = ("pack", "pack_shift", "pack_nchw", "abs_mean", "prologue", "prologue_nchw")
 
 
 def kernel_kind(name):
@@ -402,6 +406,20 @@ def main():
             fn = lambda i: lib.bnn_pack_sign_nchw_shift(xs[i % ncopy].data_ptr(), xcode, wl.batch,
                                                         wl.c, wl.h, wl.w, bias.data_ptr(), bcode,
                                                         xp.data_ptr(), cur_stream())
+        elif codec_kind == "prologue":
+            scale_out = torch.empty((), dtype=torch.float64, device=dev)
+            ws = torch.empty(lib.bnn_pack_sign_shift_abs_mean_workspace_bytes(wl.m, wl.k),
+                             dtype=torch.uint8, device=dev)
+            fn = lambda i: lib.bnn_pack_sign_shift_abs_mean(
+                xs[i % ncopy].data_ptr(), xcode, wl.m, wl.k, bias.data_ptr(), bcode, bias.numel(), 2.0,
+                xp.data_ptr(), scale_out.data_ptr(), ws.data_ptr(), ws.numel(), cur_stream())
+        elif codec_kind == "prologue_nchw":
+            scale_out = torch.empty((), dtype=torch.float64, device=dev)
+            ws = torch.empty(lib.bnn_pack_sign_nchw_shift_abs_mean_workspace_bytes(
+                xcode, wl.batch, wl.c, wl.h, wl.w), dtype=torch.uint8, device=dev)
+            fn = lambda i: lib.bnn_pack_sign_nchw_shift_abs_mean(
+                xs[i % ncopy].data_ptr(), xcode, wl.batch, wl.c, wl.h, wl.w, bias.data_ptr(), bcode, 2.0,
+                xp.data_ptr(), scale_out.data_ptr(), ws.data_ptr(), ws.numel(), cur_stream())
         else:
             count = xd.numel()
             scale_out = torch.empty((), dtype=torch.float64, device=dev)
@@ -415,7 +433,7 @@ def main():
         bytes_per = xbytes + words * 4
         if bias is not None:
             bytes_per += bias.numel() * bias.element_size()
-        if codec_kind == "abs_mean":
+        if codec_kind in ("abs_mean", "prologue", "prologue_nchw"):
             bytes_per += 2 * ws.numel() + 8
         kernels = {"pack": [fn]}
         step_fns = kernels["pack"]
@@ -655,7 +673,9 @@ def main():
                 "traffic": traffic_for(codec_kind, args.workload),
                 "kernel": KERNEL_NAMES[codec_kind], "kernel_ms": round(dom_ms, 5)}
         value = bytes_per / (ms_per_step * 1e-3) / 1e9
-        metric, unit = {"abs_mean": ("abs-mean scale bandwidth", "GB/s")}.get(
+        metric, unit = {"abs_mean": ("abs-mean scale bandwidth", "GB/s"),
+                        "prologue": ("one-pass prologue bandwidth", "GB/s"),
+                        "prologue_nchw": ("one-pass prologue bandwidth", "GB/s")}.get(
             codec_kind, ("sign+pack bandwidth", "GB/s"))
         dtype = "f64" if codec_kind == "abs_mean" else "u32"
     elif bwd_conv:

@@ -37,7 +37,9 @@ PATH_AUTO, PATH_XOR, PATH_MFMA, PATH_MFMA_FP4 = 0, 1, 2, 3
 OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIGN, ERR_WORKSPACE, ERR_PATH, ERR_HIP = range(8)
 
 EXPORTS = ("bnn_pack_sign", "bnn_pack_sign_nchw", "bnn_pack_sign_shift", "bnn_pack_sign_nchw_shift",
-           "bnn_abs_mean_scale", "bnn_abs_mean_workspace_bytes", "bnn_w_pack", "bnn_w_pack_conv",
+           "bnn_abs_mean_scale", "bnn_abs_mean_workspace_bytes", "bnn_pack_sign_shift_abs_mean",
+           "bnn_pack_sign_shift_abs_mean_workspace_bytes", "bnn_pack_sign_nchw_shift_abs_mean",
+           "bnn_pack_sign_nchw_shift_abs_mean_workspace_bytes", "bnn_w_pack", "bnn_w_pack_conv",
            "bnn_conv2d_ex", "bnn_quant_i8_nhwc", "bnn_quant_i8_weight", "bnn_w8a8_conv2d", "bnn_gemm", "bnn_conv2d",
            "bnn_gemm_noalloc", "bnn_u8_to_words", "bnn_conv2d_grad_input",
            "bnn_conv2d_grad_input_workspace_bytes", "bnn_conv2d_grad_weight",
@@ -63,6 +65,10 @@ def _bind(path: str) -> ctypes.CDLL:
         "bnn_pack_sign_nchw_shift": ([P, I, I64, I64, I64, I64, P, I, P, P], I),
         "bnn_abs_mean_scale": ([P, I, I64, D, P, P, SZ, P], I),
         "bnn_abs_mean_workspace_bytes": ([I64], SZ),
+        "bnn_pack_sign_shift_abs_mean": ([P, I, I64, I64, P, I, I64, D, P, P, P, SZ, P], I),
+        "bnn_pack_sign_shift_abs_mean_workspace_bytes": ([I64, I64], SZ),
+        "bnn_pack_sign_nchw_shift_abs_mean": ([P, I, I64, I64, I64, I64, P, I, D, P, P, P, SZ, P], I),
+        "bnn_pack_sign_nchw_shift_abs_mean_workspace_bytes": ([I, I64, I64, I64, I64], SZ),
         "bnn_linear_grad_input": ([P, P, P, I, I64, I64, I64, F, F, P, P, P, SZ, P], I),
         "bnn_linear_grad_input_workspace_bytes": ([I64, I64], SZ),
         "bnn_linear_grad_weight": ([P, P, I, I64, I64, I64, F, P, P], I),
@@ -294,6 +300,77 @@ def abs_mean_scale(x: torch.Tensor, factor: float, out: torch.Tensor | None = No
                                   _nbytes(workspace), _stream(x)),
            "bnn_abs_mean_scale")
     return out
+
+
+def _scale_out(out, x):
+    if out is None:
+        return torch.empty((), dtype=torch.float64, device=x.device)
+    _expect(out, "scale_out", torch.float64, ())
+    _same_device("scale_out", out, x)
+    return out
+
+
+def _prologue_workspace(workspace, need, x):
+    if workspace is None:
+        return _workspace(need, x.device)
+    _dev(workspace, "workspace")
+    _same_device("workspace", workspace, x)
+    return workspace
+
+
+def pack_sign_shift_abs_mean(x: torch.Tensor, bias: torch.Tensor, factor: float,
+                             out: torch.Tensor | None = None, scale_out: torch.Tensor | None = None,
+                             workspace: torch.Tensor | None = None):
+    """One-pass prologue of the linear layer: (pack_sign_shift(x, bias), factor * mean|x|) from a
+    single read of x; the scale is a 0-dim float64 device tensor."""
+    x = _dev(x, "x")
+    bias = _bias(bias, x)
+    k = x.shape[-1]
+    rows = x.numel() // k if k else 0
+    if bias.numel() not in (1, k):
+        raise ValueError(f"bias must hold one value or one per column ({k}), got {bias.numel()}")
+    if out is None:
+        out = torch.empty((*x.shape[:-1], words(k)), dtype=torch.int32, device=x.device)
+    else:
+        _expect(out, "out", torch.int32, (*x.shape[:-1], words(k)))
+        _same_device("out", out, x)
+    scale_out = _scale_out(scale_out, x)
+    workspace = _prologue_workspace(workspace, lib.bnn_pack_sign_shift_abs_mean_workspace_bytes(rows, k), x)
+    _check(lib.bnn_pack_sign_shift_abs_mean(x.data_ptr(), _dtype_code(x, "x"), rows, k, bias.data_ptr(),
+                                            _dtype_code(bias, "bias"), bias.numel(), float(factor),
+                                            out.data_ptr(), scale_out.data_ptr(), workspace.data_ptr(),
+                                            _nbytes(workspace), _stream(x)),
+           "bnn_pack_sign_shift_abs_mean")
+    return out, scale_out
+
+
+def pack_sign_nchw_shift_abs_mean(x: torch.Tensor, bias: torch.Tensor, factor: float,
+                                  out: torch.Tensor | None = None, scale_out: torch.Tensor | None = None,
+                                  workspace: torch.Tensor | None = None):
+    """One-pass prologue of the conv layer: (pack_sign_nchw_shift(x, bias), factor * mean|x|)
+    from a single read of x; the scale is a 0-dim float64 device tensor."""
+    x = _dev(x, "x")
+    bias = _bias(bias, x)
+    if x.dim() != 4:
+        raise ValueError(f"x must be NCHW (4-D), got {x.dim()}-D")
+    n, c, h, w = x.shape
+    if bias.numel() != c:
+        raise ValueError(f"bias must hold one value per channel ({c}), got {bias.numel()}")
+    if out is None:
+        out = torch.empty((n, h, w, words(c)), dtype=torch.int32, device=x.device)
+    else:
+        _expect(out, "out", torch.int32, (n, h, w, words(c)))
+        _same_device("out", out, x)
+    scale_out = _scale_out(scale_out, x)
+    code = _dtype_code(x, "x")
+    need = lib.bnn_pack_sign_nchw_shift_abs_mean_workspace_bytes(code, n, c, h, w)
+    workspace = _prologue_workspace(workspace, need, x)
+    _check(lib.bnn_pack_sign_nchw_shift_abs_mean(x.data_ptr(), code, n, c, h, w, bias.data_ptr(),
+                                                 _dtype_code(bias, "bias"), float(factor), out.data_ptr(),
+                                                 scale_out.data_ptr(), workspace.data_ptr(),
+                                                 _nbytes(workspace), _stream(x)),
+           "bnn_pack_sign_nchw_shift_abs_mean")
+    return out, scale_out
 
 
 def w_pack(weight: torch.Tensor) -> torch.Tensor:

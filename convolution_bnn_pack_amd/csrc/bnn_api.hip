@@ -251,6 +251,72 @@ bnn_status bnn_abs_mean_scale(const void* x, int x_dtype, int64_t count, double 
                                          static_cast<hipStream_t>(stream)));
 }
 
+size_t bnn_pack_sign_shift_abs_mean_workspace_bytes(int64_t rows, int64_t k) {
+  if (rows <= 0 || k <= 0) return 0;
+  const int64_t fused = k % 32 == 0 ? bnn::pack_rows_shift_abs_parts(rows, k / 32) : 0;
+  const int64_t two = bnn::abs_mean_parts(rows * k);
+  return (size_t)(fused > two ? fused : two) * sizeof(double);
+}
+
+bnn_status bnn_pack_sign_shift_abs_mean(const void* x, int x_dtype, int64_t rows, int64_t k,
+                                        const void* bias, int bias_dtype, int64_t bias_len,
+                                        double factor, uint32_t* x_packed, double* scale_out,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (!float_dtype(x_dtype) || !float_dtype(bias_dtype)) return BNN_ERR_DTYPE;
+  if (rows <= 0 || k <= 0) return BNN_ERR_SHAPE;
+  if (bias_len != 1 && bias_len != k) return BNN_ERR_SHAPE;
+  if (!x || !bias || !x_packed || !scale_out) return BNN_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(x_packed, 4) || !aligned(bias, elem_bytes(bias_dtype)) ||
+      !aligned(scale_out, 8))
+    return BNN_ERR_ALIGN;
+  if (!workspace || workspace_bytes < bnn_pack_sign_shift_abs_mean_workspace_bytes(rows, k))
+    return BNN_ERR_WORKSPACE;
+  if (!aligned(workspace, 8)) return BNN_ERR_ALIGN;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool percol = bias_len == k && k > 1;
+  double* part = static_cast<double*>(workspace);
+  if (k % 32 == 0)
+    return hip_status(bnn::launch_pack_rows_shift_abs(x, x_dtype, rows, k / 32, bias, bias_dtype,
+                                                      percol, x_packed, factor, part, scale_out, s));
+  // rows that are not whole words: the two passes
+  const hipError_t e = pack_rows_any(x, x_dtype, rows, k, bias, bias_dtype, percol, x_packed, s);
+  if (e != hipSuccess) return BNN_ERR_HIP;
+  return hip_status(bnn::launch_abs_mean(x, x_dtype, rows * k, factor, part, scale_out, s));
+}
+
+size_t bnn_pack_sign_nchw_shift_abs_mean_workspace_bytes(int x_dtype, int64_t n, int64_t c,
+                                                         int64_t h, int64_t w) {
+  if (!float_dtype(x_dtype) || n <= 0 || c <= 0 || h <= 0 || w <= 0) return 0;
+  const int64_t fused = bnn::pack_nchw_abs_parts(x_dtype, n, c, h, w);
+  const int64_t two = bnn::abs_mean_parts(n * c * h * w);
+  return (size_t)(fused > two ? fused : two) * sizeof(double);
+}
+
+bnn_status bnn_pack_sign_nchw_shift_abs_mean(const void* x, int x_dtype, int64_t n, int64_t c,
+                                             int64_t h, int64_t w, const void* bias, int bias_dtype,
+                                             double factor, uint32_t* x_packed, double* scale_out,
+                                             void* workspace, size_t workspace_bytes, void* stream) {
+  if (!float_dtype(x_dtype) || !float_dtype(bias_dtype)) return BNN_ERR_DTYPE;
+  if (n <= 0 || c <= 0 || h <= 0 || w <= 0) return BNN_ERR_SHAPE;
+  if (!int_fits(h * w) || !int_fits(n * words_of(c)) || !int_fits(n * h * w)) return BNN_ERR_SHAPE;
+  if (!x || !bias || !x_packed || !scale_out) return BNN_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(x_packed, 4) || !aligned(bias, elem_bytes(bias_dtype)) ||
+      !aligned(scale_out, 8))
+    return BNN_ERR_ALIGN;
+  if (!workspace || workspace_bytes < bnn_pack_sign_nchw_shift_abs_mean_workspace_bytes(x_dtype, n, c, h, w))
+    return BNN_ERR_WORKSPACE;
+  if (!aligned(workspace, 8)) return BNN_ERR_ALIGN;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  double* part = static_cast<double*>(workspace);
+  if (bnn::pack_nchw_abs_fused(x_dtype, h, w, x))
+    return hip_status(bnn::launch_pack_nchw_shift_abs(x, x_dtype, n, c, h, w, x_packed, bias,
+                                                      bias_dtype, factor, part, scale_out, s));
+  // pixel planes that are not a multiple of the vector width: the two passes
+  const hipError_t e = bnn::launch_pack_nchw(x, x_dtype, n, c, h, w, x_packed, s, bias, bias_dtype);
+  if (e != hipSuccess) return BNN_ERR_HIP;
+  return hip_status(bnn::launch_abs_mean(x, x_dtype, n * c * h * w, factor, part, scale_out, s));
+}
+
 bnn_status bnn_w_pack(const void* weight, int w_dtype, int64_t out_features, int64_t in_features,
                       int kernel_size, uint32_t* w_packed, void* stream) {
   if (!float_dtype(w_dtype)) return BNN_ERR_DTYPE;

@@ -38,6 +38,22 @@ int abs_mean_parts(int64_t count);
 hipError_t launch_abs_mean(const void* x, int dtype, int64_t count, double factor, double* partial,
                            double* out, hipStream_t stream);
 
+// One-pass prologue: the shifted row pack (k = 32 * KW, 16-byte aligned x) that also leaves
+// factor * mean|x| in scale_out[0], through pack_rows_shift_abs_parts(rows, KW) partial sums.
+int64_t pack_rows_shift_abs_parts(int64_t rows, int64_t KW);
+hipError_t launch_pack_rows_shift_abs(const void* x, int dtype, int64_t rows, int64_t KW,
+                                      const void* bias, int bdtype, bool percol, uint32_t* out,
+                                      double factor, double* partial, double* scale_out,
+                                      hipStream_t stream);
+// The same for the shifted NCHW pack, when pack_nchw_abs_fused (pixel planes a multiple of the
+// 16-byte vector width, x 16-byte aligned); pack_nchw_abs_parts partial sums.
+bool pack_nchw_abs_fused(int dtype, int64_t h, int64_t w, const void* x);
+int64_t pack_nchw_abs_parts(int dtype, int64_t b, int64_t c, int64_t h, int64_t w);
+hipError_t launch_pack_nchw_shift_abs(const void* x, int dtype, int64_t b, int64_t c, int64_t h,
+                                      int64_t w, uint32_t* out, const void* bias, int bdtype,
+                                      double factor, double* partial, double* scale_out,
+                                      hipStream_t stream);
+
 // OIHW conv weight pack: [o][c][kh][kw] -> [o][kh][kw][ceil(c/32)].
 hipError_t launch_pack_conv_weight(const void* w, int dtype, int64_t o, int64_t c, int kh, int kw,
                                    uint32_t* out, hipStream_t stream);

@@ -133,6 +133,32 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(const u32x4* __restrict_
   }
 }
 
+// Sum of v over a 256-thread workgroup (fixed order); the result is valid in thread 0.
+__device__ __forceinline__ double block_sum_256(double v, double* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  double t = 0.0;
+  if (threadIdx.x == 0) t = (red[0] + red[1]) + (red[2] + red[3]);
+  return t;
+}
+
+// Sum of the magnitudes of a 16-byte vector's elements, in double (a fixed pairwise tree).
+template <int DT>
+__device__ __forceinline__ double vec_abs_sum(u32x4 v) {
+  constexpr int EPL = (DT == kF32) ? 4 : 8;
+  double t[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; e++) t[e] = (double)fabsf(vec_elem<DT>(v, e));
+#pragma unroll
+  for (int w = EPL / 2; w >= 1; w /= 2)
+#pragma unroll
+    for (int e = 0; e < w; e++) t[e] = t[e] + t[e + w];
+  return t[0];
+}
+
 // Row pack with the shift. Same lane layout as pack_rows_kernel, but a workgroup's
 // waves stay on one 64-word column chunk (blockIdx.x) and walk down the rows
 // (blockIdx.y, then the grid's row stride, two rows per step), so each lane loads the
@@ -140,11 +166,16 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(const u32x4* __restrict_
 // visits. PERCOL: one shift per column (bias[k]); otherwise bias[0] for every element.
 // Loads use clamped addresses (always in bounds) so none sits behind a branch; words
 // past the row end or rows past the last are simply not stored.
-template <int DT, int BDT, bool PERCOL>
+// ABS (the one-pass prologue): the same read also sums |x| (unshifted) in double, each
+// vector by the fixed pairwise tree, each lane in its fixed order of rows, the clamped
+// re-reads left out; the workgroup's sum goes to partial[blockIdx.y * gridDim.x +
+// blockIdx.x]. The grid depends only on rows and KW, so the order of every addition does.
+template <int DT, int BDT, bool PERCOL, bool ABS = false>
 __global__ __launch_bounds__(256) void pack_rows_shift_kernel(const u32x4* __restrict__ x,
                                                               const void* __restrict__ bias,
                                                               uint32_t* __restrict__ out,
-                                                              int64_t rows, int64_t KW) {
+                                                              int64_t rows, int64_t KW,
+                                                              double* __restrict__ partial = nullptr) {
   constexpr int EPL = (DT == kF32) ? 4 : 8;
   constexpr int LPW = 32 / EPL;
   constexpr int WPI = 64 / LPW;
@@ -165,6 +196,7 @@ __global__ __launch_bounds__(256) void pack_rows_shift_kernel(const u32x4* __res
   }
   const int64_t myq = q0 + pos * WPI + grp;
   const int64_t step = (int64_t)gridDim.y * 4;
+  double abs0 = 0.0, abs1 = 0.0;
   for (int64_t r = (int64_t)blockIdx.y * 4 + (threadIdx.x >> 6); r < rows; r += 2 * step) {
     const int64_t r1 = r + step < rows ? r + step : r;
     u32x4 v0[LPW], v1[LPW];
@@ -172,6 +204,15 @@ __global__ __launch_bounds__(256) void pack_rows_shift_kernel(const u32x4* __res
     for (int j = 0; j < LPW; j++) {
       v0[j] = __builtin_nontemporal_load(&x[(r * KW + qc[j]) * LPW + pos]);
       v1[j] = __builtin_nontemporal_load(&x[(r1 * KW + qc[j]) * LPW + pos]);
+    }
+    if constexpr (ABS) {
+#pragma unroll
+      for (int j = 0; j < LPW; j++) {
+        if (q0 + j * WPI + grp < KW) {
+          abs0 += vec_abs_sum<DT>(v0[j]);
+          if (r + step < rows) abs1 += vec_abs_sum<DT>(v1[j]);
+        }
+      }
     }
     uint32_t w0 = 0, w1 = 0;
 #pragma unroll
@@ -193,6 +234,11 @@ __global__ __launch_bounds__(256) void pack_rows_shift_kernel(const u32x4* __res
       __builtin_nontemporal_store(w0, out + r * KW + myq);
       if (r + step < rows) __builtin_nontemporal_store(w1, out + (r + step) * KW + myq);
     }
+  }
+  if constexpr (ABS) {
+    __shared__ double red[4];
+    const double t = block_sum_256(abs0 + abs1, red);
+    if (threadIdx.x == 0) partial[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] = t;
   }
 }
 
@@ -324,31 +370,6 @@ __global__ __launch_bounds__(256) void pack_nchw_kernel(const void* __restrict__
 // Stage 2: one workgroup adds the partials in a fixed order and writes
 // factor * (sum / count). The grid size depends only on count, so the result is
 // the same on every run.
-// Sum of v over a 256-thread workgroup (fixed order); the result is valid in thread 0.
-__device__ __forceinline__ double block_sum_256(double v, double* red) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  double t = 0.0;
-  if (threadIdx.x == 0) t = (red[0] + red[1]) + (red[2] + red[3]);
-  return t;
-}
-
-// Sum of the magnitudes of a 16-byte vector's elements, in double (a fixed pairwise tree).
-template <int DT>
-__device__ __forceinline__ double vec_abs_sum(u32x4 v) {
-  constexpr int EPL = (DT == kF32) ? 4 : 8;
-  double t[EPL];
-#pragma unroll
-  for (int e = 0; e < EPL; e++) t[e] = (double)fabsf(vec_elem<DT>(v, e));
-#pragma unroll
-  for (int w = EPL / 2; w >= 1; w /= 2)
-#pragma unroll
-    for (int e = 0; e < w; e++) t[e] = t[e] + t[e + w];
-  return t[0];
-}
 
 template <int DT>
 __global__ __launch_bounds__(256) void abs_sum_kernel(const u32x4* __restrict__ x, int64_t nvec,
@@ -414,11 +435,15 @@ __device__ __forceinline__ void transpose8x8(uint32_t& lo, uint32_t& hi) {
 // 8w..8w+7 of the word (eight 16-byte loads in flight, each load instruction reading 1 KiB
 // of one channel plane), an 8 x 8 bit transpose turns the channel bytes into pixel bytes,
 // the four waves' bytes meet in LDS and the words leave in pixel order.
-template <int DT, int V, int BDT>
+// ABS (the one-pass prologue): the same loads also give the sum of |x| in double (each vector
+// by the fixed pairwise tree, the re-reads of missing channels and pixels left out), one
+// partial per workgroup at partial[blockIdx.y * gridDim.x + blockIdx.x].
+template <int DT, int V, int BDT, bool ABS = false>
 __global__ __launch_bounds__(256) void pack_nchw_flat_kernel(const void* __restrict__ x,
                                                              uint32_t* __restrict__ out, int C,
                                                              int HW, int CW, int P,
-                                                             const void* __restrict__ bias) {
+                                                             const void* __restrict__ bias,
+                                                             double* __restrict__ partial = nullptr) {
   constexpr int ES = (DT == kF32) ? 4 : 2;
   constexpr int PIX = 64 * V;
   static_assert(V * ES == 16, "one 16-byte vector per lane and channel");
@@ -426,6 +451,7 @@ __global__ __launch_bounds__(256) void pack_nchw_flat_kernel(const void* __restr
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nchunks = (P + PIX - 1) / PIX;
+  double absacc = 0.0;
   for (int q = blockIdx.y; q < CW; q += gridDim.y) {
     const int c0 = 32 * q + 8 * wave;
     const int nch = C - c0 < 8 ? C - c0 : 8;  // fewer only in a last, partly filled word
@@ -451,6 +477,11 @@ __global__ __launch_bounds__(256) void pack_nchw_flat_kernel(const void* __restr
             reinterpret_cast<const u32x4*>(img + (int64_t)(c < nch ? c0 + c : 0) * HW * ES));
       // keep the scheduler from sinking each load to its use
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (ABS) {
+#pragma unroll
+        for (int c = 0; c < 8; c++)
+          if (ok && c < nch) absacc += vec_abs_sum<DT>(vin[c]);
+      }
       // byte c of (lo, hi) = the V pixel bits of channel c0 + c
       uint32_t lo = 0, hi = 0;
 #pragma unroll
@@ -479,6 +510,11 @@ __global__ __launch_bounds__(256) void pack_nchw_flat_kernel(const void* __restr
       }
       __syncthreads();
     }
+  }
+  if constexpr (ABS) {
+    __shared__ double red[4];
+    const double t = block_sum_256(absacc, red);
+    if (threadIdx.x == 0) partial[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] = t;
   }
 }
 
@@ -541,20 +577,30 @@ void launch_nchw_b(dim3 grid, const void* x, uint32_t* out, int64_t c, int64_t H
 
 template <int DT, int V, int BDT>
 void launch_nchw_flat_t(dim3 grid, const void* x, uint32_t* out, int64_t c, int64_t HW, int64_t CW,
-                        int64_t P, const void* bias, hipStream_t stream) {
-  hipLaunchKernelGGL((pack_nchw_flat_kernel<DT, V, BDT>), grid, dim3(256), 0, stream, x,
-                     out, (int)c, (int)HW, (int)CW, (int)P, bias);
+                        int64_t P, const void* bias, double* partial, hipStream_t stream) {
+  if (partial)
+    hipLaunchKernelGGL((pack_nchw_flat_kernel<DT, V, BDT, true>), grid, dim3(256), 0, stream, x,
+                       out, (int)c, (int)HW, (int)CW, (int)P, bias, partial);
+  else
+    hipLaunchKernelGGL((pack_nchw_flat_kernel<DT, V, BDT>), grid, dim3(256), 0, stream, x,
+                       out, (int)c, (int)HW, (int)CW, (int)P, bias, nullptr);
 }
 
 template <int DT, int V>
 void launch_nchw_flat_b(dim3 grid, const void* x, uint32_t* out, int64_t c, int64_t HW, int64_t CW,
-                        int64_t P, const void* bias, int bdtype, hipStream_t stream) {
+                        int64_t P, const void* bias, int bdtype, double* partial, hipStream_t stream) {
   switch (bdtype) {
-    case kF32: launch_nchw_flat_t<DT, V, kF32>(grid, x, out, c, HW, CW, P, bias, stream); break;
-    case kF16: launch_nchw_flat_t<DT, V, kF16>(grid, x, out, c, HW, CW, P, bias, stream); break;
-    case kBF16: launch_nchw_flat_t<DT, V, kBF16>(grid, x, out, c, HW, CW, P, bias, stream); break;
-    default: launch_nchw_flat_t<DT, V, -1>(grid, x, out, c, HW, CW, P, nullptr, stream); break;
+    case kF32: launch_nchw_flat_t<DT, V, kF32>(grid, x, out, c, HW, CW, P, bias, partial, stream); break;
+    case kF16: launch_nchw_flat_t<DT, V, kF16>(grid, x, out, c, HW, CW, P, bias, partial, stream); break;
+    case kBF16: launch_nchw_flat_t<DT, V, kBF16>(grid, x, out, c, HW, CW, P, bias, partial, stream); break;
+    default: launch_nchw_flat_t<DT, V, -1>(grid, x, out, c, HW, CW, P, nullptr, partial, stream); break;
   }
+}
+
+// Grid of the flat NCHW pack: pixel chunks of 64 16-byte vectors by channel words.
+dim3 nchw_flat_grid(int64_t P, int64_t CW, int V) {
+  const int64_t fchunks = (P + 64 * V - 1) / (64 * V);
+  return dim3((unsigned)(fchunks < 65535 ? fchunks : 65535), (unsigned)(CW < 65535 ? CW : 65535));
 }
 
 }  // namespace
@@ -574,12 +620,11 @@ hipError_t launch_pack_nchw(const void* x, int dtype, int64_t b, int64_t c, int6
   if (vec) {
     // flattened pixel chunks (the sizes fit in int: the C ABI checks n*h*w*ceil(c/32))
     const int64_t P = b * HW;
-    const int64_t fchunks = (P + 64 * V - 1) / (64 * V);
-    const dim3 fgrid((unsigned)(fchunks < 65535 ? fchunks : 65535), (unsigned)(CW < 65535 ? CW : 65535));
+    const dim3 fgrid = nchw_flat_grid(P, CW, V);
     switch (dtype) {
-      case kF32: launch_nchw_flat_b<kF32, 4>(fgrid, x, out, c, HW, CW, P, bias, bdtype, stream); break;
-      case kF16: launch_nchw_flat_b<kF16, 8>(fgrid, x, out, c, HW, CW, P, bias, bdtype, stream); break;
-      default: launch_nchw_flat_b<kBF16, 8>(fgrid, x, out, c, HW, CW, P, bias, bdtype, stream); break;
+      case kF32: launch_nchw_flat_b<kF32, 4>(fgrid, x, out, c, HW, CW, P, bias, bdtype, nullptr, stream); break;
+      case kF16: launch_nchw_flat_b<kF16, 8>(fgrid, x, out, c, HW, CW, P, bias, bdtype, nullptr, stream); break;
+      default: launch_nchw_flat_b<kBF16, 8>(fgrid, x, out, c, HW, CW, P, bias, bdtype, nullptr, stream); break;
     }
   } else {
     switch (dtype) {
@@ -593,26 +638,51 @@ hipError_t launch_pack_nchw(const void* x, int dtype, int64_t b, int64_t c, int6
 
 namespace {
 
-template <int DT, int BDT>
+template <int DT, int BDT, bool ABS>
 void launch_rows_shift_t(dim3 grid, const void* x, const void* bias, bool percol, uint32_t* out,
-                         int64_t rows, int64_t KW, hipStream_t stream) {
+                         int64_t rows, int64_t KW, double* partial, hipStream_t stream) {
   const u32x4* xv = reinterpret_cast<const u32x4*>(x);
   if (percol)
-    hipLaunchKernelGGL((pack_rows_shift_kernel<DT, BDT, true>), grid, dim3(256), 0, stream, xv, bias,
-                       out, rows, KW);
+    hipLaunchKernelGGL((pack_rows_shift_kernel<DT, BDT, true, ABS>), grid, dim3(256), 0, stream, xv,
+                       bias, out, rows, KW, partial);
   else
-    hipLaunchKernelGGL((pack_rows_shift_kernel<DT, BDT, false>), grid, dim3(256), 0, stream, xv,
-                       bias, out, rows, KW);
+    hipLaunchKernelGGL((pack_rows_shift_kernel<DT, BDT, false, ABS>), grid, dim3(256), 0, stream, xv,
+                       bias, out, rows, KW, partial);
 }
 
-template <int DT>
+template <int DT, bool ABS>
 void launch_rows_shift_b(dim3 grid, const void* x, const void* bias, int bdtype, bool percol,
-                         uint32_t* out, int64_t rows, int64_t KW, hipStream_t stream) {
+                         uint32_t* out, int64_t rows, int64_t KW, double* partial, hipStream_t stream) {
   switch (bdtype) {
-    case kF32: launch_rows_shift_t<DT, kF32>(grid, x, bias, percol, out, rows, KW, stream); break;
-    case kF16: launch_rows_shift_t<DT, kF16>(grid, x, bias, percol, out, rows, KW, stream); break;
-    default: launch_rows_shift_t<DT, kBF16>(grid, x, bias, percol, out, rows, KW, stream); break;
+    case kF32: launch_rows_shift_t<DT, kF32, ABS>(grid, x, bias, percol, out, rows, KW, partial, stream); break;
+    case kF16: launch_rows_shift_t<DT, kF16, ABS>(grid, x, bias, percol, out, rows, KW, partial, stream); break;
+    default: launch_rows_shift_t<DT, kBF16, ABS>(grid, x, bias, percol, out, rows, KW, partial, stream); break;
   }
+}
+
+// Grid of the shifted row pack: one column of workgroups per 64-word chunk, about 4096
+// workgroups in all (16 waves per compute unit), each wave walking its rows.
+dim3 rows_shift_grid(int64_t rows, int64_t KW) {
+  const int64_t nchunk = (KW + 63) / 64;
+  int64_t gy = (4096 + nchunk - 1) / nchunk;
+  const int64_t row_groups = (rows + 3) / 4;
+  if (gy > row_groups) gy = row_groups;
+  if (gy > 65535) gy = 65535;
+  if (gy < 1) gy = 1;
+  return dim3((unsigned)nchunk, (unsigned)gy);
+}
+
+template <bool ABS>
+hipError_t launch_rows_shift_any(const void* x, int dtype, int64_t rows, int64_t KW, const void* bias,
+                                 int bdtype, bool percol, uint32_t* out, double* partial,
+                                 hipStream_t stream) {
+  const dim3 grid = rows_shift_grid(rows, KW);
+  switch (dtype) {
+    case kF32: launch_rows_shift_b<kF32, ABS>(grid, x, bias, bdtype, percol, out, rows, KW, partial, stream); break;
+    case kF16: launch_rows_shift_b<kF16, ABS>(grid, x, bias, bdtype, percol, out, rows, KW, partial, stream); break;
+    default: launch_rows_shift_b<kBF16, ABS>(grid, x, bias, bdtype, percol, out, rows, KW, partial, stream); break;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -621,19 +691,25 @@ hipError_t launch_pack_rows_shift(const void* x, int dtype, int64_t rows, int64_
                                   const void* bias, int bdtype, bool percol, uint32_t* out,
                                   hipStream_t stream) {
   if (rows <= 0 || KW <= 0) return hipSuccess;
-  const int64_t nchunk = (KW + 63) / 64;
-  // about 4096 workgroups in all (16 waves per compute unit), each wave walking its rows
-  int64_t gy = (4096 + nchunk - 1) / nchunk;
-  const int64_t row_groups = (rows + 3) / 4;
-  if (gy > row_groups) gy = row_groups;
-  if (gy > 65535) gy = 65535;
-  if (gy < 1) gy = 1;
-  const dim3 grid((unsigned)nchunk, (unsigned)gy);
-  switch (dtype) {
-    case kF32: launch_rows_shift_b<kF32>(grid, x, bias, bdtype, percol, out, rows, KW, stream); break;
-    case kF16: launch_rows_shift_b<kF16>(grid, x, bias, bdtype, percol, out, rows, KW, stream); break;
-    default: launch_rows_shift_b<kBF16>(grid, x, bias, bdtype, percol, out, rows, KW, stream); break;
-  }
+  return launch_rows_shift_any<false>(x, dtype, rows, KW, bias, bdtype, percol, out, nullptr, stream);
+}
+
+int64_t pack_rows_shift_abs_parts(int64_t rows, int64_t KW) {
+  if (rows <= 0 || KW <= 0) return 1;
+  const dim3 g = rows_shift_grid(rows, KW);
+  return (int64_t)g.x * g.y;
+}
+
+hipError_t launch_pack_rows_shift_abs(const void* x, int dtype, int64_t rows, int64_t KW,
+                                      const void* bias, int bdtype, bool percol, uint32_t* out,
+                                      double factor, double* partial, double* scale_out,
+                                      hipStream_t stream) {
+  hipError_t e = launch_rows_shift_any<true>(x, dtype, rows, KW, bias, bdtype, percol, out, partial,
+                                             stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(abs_mean_final_kernel, dim3(1), dim3(256), 0, stream, partial,
+                     (int)pack_rows_shift_abs_parts(rows, KW), (double)rows * KW * 32, factor,
+                     scale_out);
   return hipGetLastError();
 }
 
@@ -685,6 +761,36 @@ hipError_t launch_pack_rows_ragged(const void* x, int dtype, int64_t rows, int64
     case kF16: launch_ragged_b<kF16>(grid, x, bias, bdtype, percol, out, rows, k, KW, stream); break;
     default: launch_ragged_b<kBF16>(grid, x, bias, bdtype, percol, out, rows, k, KW, stream); break;
   }
+  return hipGetLastError();
+}
+
+bool pack_nchw_abs_fused(int dtype, int64_t h, int64_t w, const void* x) {
+  const int vfull = dtype == kF32 ? 4 : 8;
+  return (h * w) % vfull == 0 && (reinterpret_cast<uintptr_t>(x) % 16) == 0;
+}
+
+int64_t pack_nchw_abs_parts(int dtype, int64_t b, int64_t c, int64_t h, int64_t w) {
+  const int V = dtype == kF32 ? 4 : 8;
+  const dim3 g = nchw_flat_grid(b * h * w, (c + 31) / 32, V);
+  return (int64_t)g.x * g.y;
+}
+
+hipError_t launch_pack_nchw_shift_abs(const void* x, int dtype, int64_t b, int64_t c, int64_t h,
+                                      int64_t w, uint32_t* out, const void* bias, int bdtype,
+                                      double factor, double* partial, double* scale_out,
+                                      hipStream_t stream) {
+  const int64_t HW = h * w, CW = (c + 31) / 32, P = b * HW;
+  const int V = dtype == kF32 ? 4 : 8;
+  const dim3 fgrid = nchw_flat_grid(P, CW, V);
+  switch (dtype) {
+    case kF32: launch_nchw_flat_b<kF32, 4>(fgrid, x, out, c, HW, CW, P, bias, bdtype, partial, stream); break;
+    case kF16: launch_nchw_flat_b<kF16, 8>(fgrid, x, out, c, HW, CW, P, bias, bdtype, partial, stream); break;
+    default: launch_nchw_flat_b<kBF16, 8>(fgrid, x, out, c, HW, CW, P, bias, bdtype, partial, stream); break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(abs_mean_final_kernel, dim3(1), dim3(256), 0, stream, partial,
+                     (int)((int64_t)fgrid.x * fgrid.y), (double)(b * c * HW), factor, scale_out);
   return hipGetLastError();
 }
 

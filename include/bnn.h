@@ -158,6 +158,36 @@ bnn_status bnn_abs_mean_scale(const void* x, int x_dtype, int64_t count, double 
                               void* stream);
 size_t bnn_abs_mean_workspace_bytes(int64_t count);
 
+/* One-pass prologue (the layer's first forward, while scale_a is still zero): bnn_pack_sign_shift
+ * and bnn_abs_mean_scale of the same x in a single read of x (set_activation of BinaryLinearCuda:
+ * the shifted sign feeds the contraction, the lazy scale_a = factor * mean|x| is taken of the
+ * unshifted input). x_packed exactly as bnn_pack_sign_shift; *scale_out as bnn_abs_mean_scale
+ * (a sum in double in a fixed order that depends only on rows and k, within about rows * k * 2^-53
+ * relative of the sequential sum, the same on every run; it may differ in the last bits from
+ * bnn_abs_mean_scale's, whose order is another). x 16-byte aligned; rows >= 1, k >= 1 (the mean of
+ * no elements is undefined: BNN_ERR_SHAPE); bias and its length as bnn_pack_sign_shift.
+ *   workspace at least bnn_pack_sign_shift_abs_mean_workspace_bytes(rows, k) bytes, 8-byte aligned.
+ * Rows that are a whole number of words take one kernel for both results; other row lengths
+ * take the two passes. */
+bnn_status bnn_pack_sign_shift_abs_mean(const void* x, int x_dtype, int64_t rows, int64_t k,
+                                        const void* bias, int bias_dtype, int64_t bias_len,
+                                        double factor, uint32_t* x_packed, double* scale_out,
+                                        void* workspace, size_t workspace_bytes, void* stream);
+size_t bnn_pack_sign_shift_abs_mean_workspace_bytes(int64_t rows, int64_t k);
+
+/* The same for NCHW activations (set_activation of BinaryConv2dCutlass): x_packed exactly as
+ * bnn_pack_sign_nchw_shift, *scale_out = factor * mean|x| over all n*c*h*w elements; n >= 1.
+ * Pixel planes whose size is a multiple of the 16-byte vector width take one kernel for both
+ * results, others the two passes.
+ *   workspace at least bnn_pack_sign_nchw_shift_abs_mean_workspace_bytes(x_dtype, n, c, h, w)
+ *             bytes, 8-byte aligned. */
+bnn_status bnn_pack_sign_nchw_shift_abs_mean(const void* x, int x_dtype, int64_t n, int64_t c,
+                                             int64_t h, int64_t w, const void* bias, int bias_dtype,
+                                             double factor, uint32_t* x_packed, double* scale_out,
+                                             void* workspace, size_t workspace_bytes, void* stream);
+size_t bnn_pack_sign_nchw_shift_abs_mean_workspace_bytes(int x_dtype, int64_t n, int64_t c,
+                                                         int64_t h, int64_t w);
+
 /* Weight pack (run once per layer, ahead of the forward).
  *   kernel_size == 0: linear weight [out_features, in_features] -> [out_features, ceil(in_features/32)].
  *   kernel_size >= 1: conv weight OIHW [out_features, in_features, k, k] -> [out_features, k, k, ceil(in_features/32)].

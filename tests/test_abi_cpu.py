@@ -248,6 +248,32 @@ def test_prologue_argument_checks(bnn):
     assert L.bnn_abs_mean_scale(FAKE, bnn.F32, 1 << 20, 2.0, FAKE + 4, FAKE, need, None) == bnn.ERR_ALIGN
     assert L.bnn_abs_mean_scale(FAKE, bnn.F32, 1 << 20, 2.0, FAKE, FAKE, need - 1, None) == bnn.ERR_WORKSPACE
     assert L.bnn_abs_mean_scale(FAKE, bnn.F32, 1 << 20, 2.0, FAKE, None, need, None) == bnn.ERR_WORKSPACE
+    # one-pass prologue: rows >= 1 (a mean needs elements), x 16-byte aligned, the bias rules of
+    # the shifted pack, a workspace at least the query, which covers both the one-kernel and
+    # the two-pass form
+    need = L.bnn_pack_sign_shift_abs_mean_workspace_bytes(16384, 8192)
+    assert need >= L.bnn_abs_mean_workspace_bytes(16384 * 8192) and need % 8 == 0
+    assert L.bnn_pack_sign_shift_abs_mean_workspace_bytes(0, 64) == 0
+    assert L.bnn_pack_sign_shift_abs_mean_workspace_bytes(5, 33) == L.bnn_abs_mean_workspace_bytes(5 * 33)
+    ps = L.bnn_pack_sign_shift_abs_mean
+    assert ps(FAKE, bnn.F16, 0, 64, FAKE, bnn.F32, 1, 2.0, FAKE, FAKE, FAKE, need, None) == bnn.ERR_SHAPE
+    assert ps(FAKE, bnn.F16, 4, 64, FAKE, bnn.F32, 2, 2.0, FAKE, FAKE, FAKE, need, None) == bnn.ERR_SHAPE
+    assert ps(FAKE, bnn.I32, 4, 64, FAKE, bnn.F32, 1, 2.0, FAKE, FAKE, FAKE, need, None) == bnn.ERR_DTYPE
+    assert ps(FAKE, bnn.F16, 4, 64, FAKE, bnn.F32, 1, 2.0, FAKE, None, FAKE, need, None) == bnn.ERR_NULL
+    assert ps(FAKE + 2, bnn.F16, 4, 64, FAKE, bnn.F32, 1, 2.0, FAKE, FAKE, FAKE, need, None) == bnn.ERR_ALIGN
+    assert ps(FAKE, bnn.F16, 4, 64, FAKE, bnn.F32, 1, 2.0, FAKE, FAKE + 4, FAKE, need, None) == bnn.ERR_ALIGN
+    small = L.bnn_pack_sign_shift_abs_mean_workspace_bytes(4, 64)
+    assert ps(FAKE, bnn.F16, 4, 64, FAKE, bnn.F32, 1, 2.0, FAKE, FAKE, FAKE, small - 1, None) == bnn.ERR_WORKSPACE
+    assert ps(FAKE, bnn.F16, 4, 64, FAKE, bnn.F32, 1, 2.0, FAKE, FAKE, None, small, None) == bnn.ERR_WORKSPACE
+    need = L.bnn_pack_sign_nchw_shift_abs_mean_workspace_bytes(bnn.F16, 128, 128, 28, 28)
+    assert need >= L.bnn_abs_mean_workspace_bytes(128 * 128 * 28 * 28) and need % 8 == 0
+    assert L.bnn_pack_sign_nchw_shift_abs_mean_workspace_bytes(bnn.I32, 1, 32, 4, 4) == 0
+    pn = L.bnn_pack_sign_nchw_shift_abs_mean
+    assert pn(FAKE, bnn.F16, 0, 32, 4, 4, FAKE, bnn.F16, 2.0, FAKE, FAKE, FAKE, need, None) == bnn.ERR_SHAPE
+    assert pn(FAKE, bnn.F16, 1, 32, 4, 4, FAKE, 7, 2.0, FAKE, FAKE, FAKE, need, None) == bnn.ERR_DTYPE
+    assert pn(FAKE, bnn.F16, 1, 32, 4, 4, FAKE, bnn.F16, 2.0, None, FAKE, FAKE, need, None) == bnn.ERR_NULL
+    assert pn(FAKE + 8, bnn.F16, 1, 32, 4, 4, FAKE, bnn.F16, 2.0, FAKE, FAKE, FAKE, need, None) == bnn.ERR_ALIGN
+    assert pn(FAKE, bnn.F16, 1, 32, 4, 4, FAKE, bnn.F16, 2.0, FAKE, FAKE, FAKE, 0, None) == bnn.ERR_WORKSPACE
 
 
 def test_shift_kernels_keep_subnormals():
