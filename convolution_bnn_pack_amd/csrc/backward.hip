@@ -467,37 +467,133 @@ __global__ __launch_bounds__(kThreads) void split_sum_kernel(const float* __rest
   }
 }
 
+// The same unfolding, 32 pixels (consecutive rows of xcol) per workgroup through LDS, for column
+// counts whose 32 rows fit in LDS. Gathered straight into 16-byte stores, each lane's 8 columns are
+// 8 different channel planes or taps, so a load instruction touches 64 memory lines. Here the 32
+// lanes of a half-wave take the 32 pixels of one column pair: consecutive output pixels of one row
+// read neighbouring input elements, a line or two per instruction. Each pair goes to LDS as one
+// dword (rows of RS = (J/2) | 1 dwords: an odd stride keeps the 32 rows in 32 banks); then the
+// tile's 32 * J * 2 contiguous bytes of xcol leave as 16-byte stores. Column counts with
+// RS > kIm2colMaxRS take the direct gather above.
+constexpr int kIm2colPix = 32;
+constexpr int kIm2colMaxRS = 640;  // 80 KiB of LDS: two workgroups per compute unit
+__global__ __launch_bounds__(kThreads) void conv_im2col_tile_kernel(const uint16_t* __restrict__ x,
+                                                                   uint16_t* __restrict__ xcol,
+                                                                   ConvGeom q, FastDiv div_t,
+                                                                   FastDiv div_kw, FastDiv div_hwo,
+                                                                   FastDiv div_wo, FastDiv div_j8) {
+  __shared__ uint32_t tile[kIm2colPix * kIm2colMaxRS];
+  const int T = q.KH * q.KW, J = q.C * T, JP = J / 2, RS = JP | 1;
+  const int hwo = q.Ho * q.Wo, pixels = q.B * hwo;
+  const int ntiles = (pixels + kIm2colPix - 1) / kIm2colPix;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int p = lane & 31, sub = lane >> 5;
+  for (int tl = blockIdx.x; tl < ntiles; tl += gridDim.x) {
+    const int pix = tl * kIm2colPix + p;
+    const bool pok = pix < pixels;
+    const int b = div_hwo.div(pok ? pix : 0), r = (pok ? pix : 0) - b * hwo;
+    const int oh = div_wo.div(r), ow = r - oh * q.Wo;
+    const int ihb = oh * q.SH - q.PH, iwb = ow * q.SW - q.PW;
+    const uint16_t* xb = x + (int64_t)b * q.C * q.H * q.W;
+    // column pairs jp = 2 * wave + sub + 8 * i, kU pairs at a time: all 2 * kU loads go out
+    // (clamped to element 0 where the tap falls outside, so none sits behind a branch) before
+    // any is used
+    constexpr int kU = 8;
+    for (int jb = 2 * wave + sub; jb < JP; jb += 8 * kU) {
+      uint32_t val[kU][2];
+      bool in[kU][2];
+#pragma unroll
+      for (int u = 0; u < kU; u++)
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+          const int jp = jb + 8 * u, j = 2 * jp + h;
+          const int c = div_t.div(j), t = j - c * T;
+          const int kh = div_kw.div(t), kw = t - kh * q.KW;
+          const int ih = ihb + kh * q.DH, iw = iwb + kw * q.DW;
+          in[u][h] = pok && jp < JP && ih >= 0 && ih < q.H && iw >= 0 && iw < q.W;
+          val[u][h] = xb[in[u][h] ? ((int64_t)c * q.H + ih) * q.W + iw : 0];
+        }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < kU; u++) {
+        const int jp = jb + 8 * u;
+        if (jp < JP)
+          tile[p * RS + jp] = (in[u][0] ? val[u][0] : 0u) | ((in[u][1] ? val[u][1] : 0u) << 16);
+      }
+    }
+    __syncthreads();
+    const int rows = pixels - tl * kIm2colPix < kIm2colPix ? pixels - tl * kIm2colPix : kIm2colPix;
+    const int J8 = J / 8, nchunk = rows * J8;
+    uint16_t* dst = xcol + (int64_t)tl * kIm2colPix * J;
+    for (int k = threadIdx.x; k < nchunk; k += kThreads) {
+      const int row = div_j8.div(k), cq = k - row * J8;
+      const uint32_t* src = tile + row * RS + 4 * cq;
+      *reinterpret_cast<uint4*>(dst + (int64_t)k * 8) = make_uint4(src[0], src[1], src[2], src[3]);
+    }
+    __syncthreads();
+  }
+}
+
 // grad_in[b][c][ih][iw] = mid(x) * sum of colsT[c*T + t][(b, oh, ow)] over the taps t whose output
 // pixel (oh, ow) = ((ih + PH - kh*DH) / SH, (iw + PW - kw*DW) / SW) exists (exact divisions, in
 // range), in tap order; each workgroup writes its double sum of grad_in * sign(x) (a fixed grid,
 // so the order of every sum is fixed).
-template <bool BF>
+// Divisions by launch-invariant sizes of the col2im gather (every index fits in int: the C ABI
+// checks n*c*h*w and the column matrix's size).
+struct Col2imDivs {
+  FastDiv w, h, c, sh, sw, kw;
+};
+
+// SMALL: at most 9 taps (kh * kw <= 9), gathered with all loads in flight.
+template <bool BF, bool SMALL>
 __global__ __launch_bounds__(kThreads) void conv_col2im_kernel(const float* __restrict__ cols,
                                                               const uint16_t* __restrict__ x,
                                                               float* __restrict__ grad_in,
                                                               double* __restrict__ part, ConvGeom q,
-                                                              float scale_a) {
+                                                              Col2imDivs dv, float scale_a) {
   const int T = q.KH * q.KW;
-  const int64_t pixels = (int64_t)q.B * q.Ho * q.Wo;
-  const int64_t total = (int64_t)q.B * q.C * q.H * q.W;
+  const int pixels = q.B * q.Ho * q.Wo;
+  const int total = q.B * q.C * q.H * q.W;
   double sum = 0.0;
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * kThreads) {
-    const int iw = (int)(i % q.W);
-    const int64_t r1 = i / q.W;
-    const int ih = (int)(r1 % q.H);
-    const int64_t r2 = r1 / q.H;
-    const int c = (int)(r2 % q.C), b = (int)(r2 / q.C);
+  for (int64_t ii = (int64_t)blockIdx.x * kThreads + threadIdx.x; ii < total;
+       ii += (int64_t)gridDim.x * kThreads) {
+    const int i = (int)ii;
+    const int r1 = dv.w.div(i), iw = i - r1 * q.W;
+    const int r2 = dv.h.div(r1), ih = r1 - r2 * q.H;
+    const int b = dv.c.div(r2), c = r2 - b * q.C;
+    const float* col_c = cols + (int64_t)c * T * pixels + b * q.Ho * q.Wo;
     float v = 0.0f;
-    for (int kh = 0; kh < q.KH; kh++) {
-      const int nh = ih + q.PH - kh * q.DH;
-      if (nh < 0 || nh % q.SH != 0 || nh / q.SH >= q.Ho) continue;
-      const int oh = nh / q.SH;
-      for (int kw = 0; kw < q.KW; kw++) {
-        const int nw = iw + q.PW - kw * q.DW;
-        if (nw < 0 || nw % q.SW != 0 || nw / q.SW >= q.Wo) continue;
-        const int ow = nw / q.SW;
-        v += cols[((int64_t)c * T + kh * q.KW + kw) * pixels + ((int64_t)b * q.Ho + oh) * q.Wo + ow];
+    if constexpr (SMALL) {
+      // up to 9 taps: every tap's column is loaded (clamped to the plane's first pixel where the
+      // tap has no output pixel) before any is added, then the valid ones are added in tap
+      // order (adding +0 for the others leaves v unchanged: v starts at +0 and is never -0)
+      float tv[9];
+      bool ok[9];
+#pragma unroll
+      for (int t = 0; t < 9; t++) {
+        const int kh = t < T ? dv.kw.div(t) : 0, kw = t - kh * q.KW;
+        const int nh = ih + q.PH - kh * q.DH, nw = iw + q.PW - kw * q.DW;
+        const int oh = dv.sh.div(nh < 0 ? 0 : nh), ow = dv.sw.div(nw < 0 ? 0 : nw);
+        ok[t] = t < T && nh >= 0 && nw >= 0 && oh * q.SH == nh && ow * q.SW == nw && oh < q.Ho &&
+                ow < q.Wo;
+        tv[t] = col_c[ok[t] ? (int64_t)t * pixels + oh * q.Wo + ow : 0];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < 9; t++) v += ok[t] ? tv[t] : 0.0f;
+    } else {
+      for (int kh = 0; kh < q.KH; kh++) {
+        const int nh = ih + q.PH - kh * q.DH;
+        if (nh < 0) continue;
+        const int oh = dv.sh.div(nh);
+        if (oh * q.SH != nh || oh >= q.Ho) continue;
+        for (int kw = 0; kw < q.KW; kw++) {
+          const int nw = iw + q.PW - kw * q.DW;
+          if (nw < 0) continue;
+          const int ow = dv.sw.div(nw);
+          if (ow * q.SW != nw || ow >= q.Wo) continue;
+          v += col_c[(int64_t)(kh * q.KW + kw) * pixels + oh * q.Wo + ow];
+        }
       }
     }
     const float xv = widen16<BF>(x[i]);
@@ -605,12 +701,24 @@ hipError_t launch_conv_grad_input(const void* g, const void* w, const void* x, b
   if (e != hipSuccess) return e;
   const int64_t total = (int64_t)q.B * q.C * q.H * q.W;
   const int parts = (int)grid_of(total, kCol2imBlocks);
-  if (bf)
-    hipLaunchKernelGGL(conv_col2im_kernel<true>, dim3(parts), dim3(kThreads), 0, s, cols,
-                       static_cast<const uint16_t*>(x), grad_in, part, q, scale_a);
-  else
-    hipLaunchKernelGGL(conv_col2im_kernel<false>, dim3(parts), dim3(kThreads), 0, s, cols,
-                       static_cast<const uint16_t*>(x), grad_in, part, q, scale_a);
+  const Col2imDivs dv{FastDiv((uint32_t)q.W), FastDiv((uint32_t)q.H), FastDiv((uint32_t)q.C),
+                      FastDiv((uint32_t)q.SH), FastDiv((uint32_t)q.SW), FastDiv((uint32_t)q.KW)};
+  const uint16_t* xs = static_cast<const uint16_t*>(x);
+  if (T <= 9) {
+    if (bf)
+      hipLaunchKernelGGL((conv_col2im_kernel<true, true>), dim3(parts), dim3(kThreads), 0, s, cols, xs,
+                         grad_in, part, q, dv, scale_a);
+    else
+      hipLaunchKernelGGL((conv_col2im_kernel<false, true>), dim3(parts), dim3(kThreads), 0, s, cols, xs,
+                         grad_in, part, q, dv, scale_a);
+  } else {
+    if (bf)
+      hipLaunchKernelGGL((conv_col2im_kernel<true, false>), dim3(parts), dim3(kThreads), 0, s, cols, xs,
+                         grad_in, part, q, dv, scale_a);
+    else
+      hipLaunchKernelGGL((conv_col2im_kernel<false, false>), dim3(parts), dim3(kThreads), 0, s, cols, xs,
+                         grad_in, part, q, dv, scale_a);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_scale_a_kernel, dim3(1), dim3(kThreads), 0, s, part, parts,
@@ -626,9 +734,17 @@ hipError_t launch_conv_grad_weight(const void* g, const void* x, bool bf, const 
   const int hwo = q.Ho * q.Wo, T = q.KH * q.KW, J = q.C * T;
   hipLaunchKernelGGL(conv_g_transpose_kernel, dim3((unsigned)grid_of((int64_t)q.B * q.O * kThreads, 8192)),
                      dim3(kThreads), 0, s, static_cast<const uint16_t*>(g), gT, q.B, q.O, hwo);
-  hipLaunchKernelGGL(conv_im2col_kernel, dim3((unsigned)grid_of((int64_t)q.B * hwo * (J / 8), 16384)),
-                     dim3(kThreads), 0, s, static_cast<const uint16_t*>(x), xcol, q,
-                     FastDiv((uint32_t)T), FastDiv((uint32_t)q.KW));
+  if (((J / 2) | 1) <= kIm2colMaxRS) {
+    const int64_t ntiles = ((int64_t)q.B * hwo + kIm2colPix - 1) / kIm2colPix;
+    hipLaunchKernelGGL(conv_im2col_tile_kernel, dim3((unsigned)(ntiles < 65535 ? ntiles : 65535)),
+                       dim3(kThreads), 0, s, static_cast<const uint16_t*>(x), xcol, q,
+                       FastDiv((uint32_t)T), FastDiv((uint32_t)q.KW), FastDiv((uint32_t)hwo),
+                       FastDiv((uint32_t)q.Wo), FastDiv((uint32_t)(J / 8)));
+  } else {
+    hipLaunchKernelGGL(conv_im2col_kernel, dim3((unsigned)grid_of((int64_t)q.B * hwo * (J / 8), 16384)),
+                       dim3(kThreads), 0, s, static_cast<const uint16_t*>(x), xcol, q,
+                       FastDiv((uint32_t)T), FastDiv((uint32_t)q.KW));
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // GW [O][C*T] = scale_a * gT @ sign(xcol), split along the pixels, then the splits summed
