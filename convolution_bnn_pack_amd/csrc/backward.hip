@@ -397,15 +397,25 @@ struct ConvGeom {
 
 // g NCHW [B][O][Ho*Wo] -> gT [O][B*Ho*Wo]: one contiguous run of Ho*Wo per (b, o), copied by a
 // workgroup per run.
+// VW-byte vectors (VW / 2 elements, hw a multiple of them): thread t copies vector t of the
+// flattened (run, vector) space, so a wave moves 64 * VW consecutive bytes whatever the run length.
+template <int VW>
 __global__ __launch_bounds__(kThreads) void conv_g_transpose_kernel(const uint16_t* __restrict__ g,
                                                                    uint16_t* __restrict__ gT,
-                                                                   int B, int O, int hw) {
-  const int64_t runs = (int64_t)B * O;
-  for (int64_t run = blockIdx.x; run < runs; run += gridDim.x) {
-    const int b = (int)(run / O), o = (int)(run - (int64_t)b * O);
-    const uint16_t* src = g + run * hw;
-    uint16_t* dst = gT + ((int64_t)o * B + b) * hw;
-    for (int i = threadIdx.x; i < hw; i += kThreads) dst[i] = src[i];
+                                                                   int B, int O, int hw,
+                                                                   FastDiv div_vpr, FastDiv div_o) {
+  using V = std::conditional_t<VW == 16, uint4, std::conditional_t<VW == 8, uint2,
+                               std::conditional_t<VW == 4, uint32_t, uint16_t>>>;
+  constexpr int E = VW / 2;
+  const int vpr = hw / E;
+  const int64_t total = (int64_t)B * O * vpr;
+  for (int64_t v = (int64_t)blockIdx.x * kThreads + threadIdx.x; v < total;
+       v += (int64_t)gridDim.x * kThreads) {
+    // total < 2^31: the C ABI checks o * pixels
+    const int run = div_vpr.div((int)v), within = (int)v - run * vpr;
+    const int b = div_o.div(run), o = run - b * O;
+    const V val = *reinterpret_cast<const V*>(g + (int64_t)run * hw + within * E);
+    *reinterpret_cast<V*>(gT + ((int64_t)o * B + b) * hw + within * E) = val;
   }
 }
 
@@ -666,6 +676,23 @@ hipError_t launch_linear_grad_weight(const void* g, const void* x, bool bf, int6
 
 // ---- conv backward launchers
 
+// g NCHW -> gT [O][B*Ho*Wo] with the widest vectors that the plane size and g's alignment allow
+// (gT, in the workspace, is 256-byte aligned).
+void launch_g_transpose(const uint16_t* g, uint16_t* gT, int B, int O, int hw, hipStream_t s) {
+  const uintptr_t ga = reinterpret_cast<uintptr_t>(g);
+  int e = 8;
+  while (e > 1 && (hw % e != 0 || ga % (2 * e) != 0)) e /= 2;
+  const int64_t total = (int64_t)B * O * (hw / e);
+  const dim3 grid((unsigned)grid_of(total, 16384)), block(kThreads);
+  const FastDiv dv((uint32_t)(hw / e)), dO((uint32_t)O);
+  switch (e) {
+    case 8: hipLaunchKernelGGL(conv_g_transpose_kernel<16>, grid, block, 0, s, g, gT, B, O, hw, dv, dO); break;
+    case 4: hipLaunchKernelGGL(conv_g_transpose_kernel<8>, grid, block, 0, s, g, gT, B, O, hw, dv, dO); break;
+    case 2: hipLaunchKernelGGL(conv_g_transpose_kernel<4>, grid, block, 0, s, g, gT, B, O, hw, dv, dO); break;
+    default: hipLaunchKernelGGL(conv_g_transpose_kernel<2>, grid, block, 0, s, g, gT, B, O, hw, dv, dO); break;
+  }
+}
+
 int64_t conv_col2im_parts(int64_t n, int64_t c, int64_t h, int64_t w) {
   return grid_of(n * c * h * w, kCol2imBlocks);
 }
@@ -684,8 +711,7 @@ hipError_t launch_conv_grad_input(const void* g, const void* w, const void* x, b
   const ConvGeom q{geom[0], geom[1], geom[2], geom[3], geom[4], geom[5], geom[6], geom[7],
                    geom[8], geom[9], geom[10], geom[11], geom[12], geom[13], geom[14]};
   const int hwo = q.Ho * q.Wo, T = q.KH * q.KW, J = q.C * T;
-  hipLaunchKernelGGL(conv_g_transpose_kernel, dim3((unsigned)grid_of((int64_t)q.B * q.O * kThreads, 8192)),
-                     dim3(kThreads), 0, s, static_cast<const uint16_t*>(g), gT, q.B, q.O, hwo);
+  launch_g_transpose(static_cast<const uint16_t*>(g), gT, q.B, q.O, hwo, s);
   const int64_t nw = (int64_t)q.O * J;
   if (bf)
     hipLaunchKernelGGL(sign16_kernel<true>, dim3((unsigned)grid_of(nw, 4096)), dim3(kThreads), 0, s,
@@ -732,8 +758,7 @@ hipError_t launch_conv_grad_weight(const void* g, const void* x, bool bf, const 
   const ConvGeom q{geom[0], geom[1], geom[2], geom[3], geom[4], geom[5], geom[6], geom[7],
                    geom[8], geom[9], geom[10], geom[11], geom[12], geom[13], geom[14]};
   const int hwo = q.Ho * q.Wo, T = q.KH * q.KW, J = q.C * T;
-  hipLaunchKernelGGL(conv_g_transpose_kernel, dim3((unsigned)grid_of((int64_t)q.B * q.O * kThreads, 8192)),
-                     dim3(kThreads), 0, s, static_cast<const uint16_t*>(g), gT, q.B, q.O, hwo);
+  launch_g_transpose(static_cast<const uint16_t*>(g), gT, q.B, q.O, hwo, s);
   if (((J / 2) | 1) <= kIm2colMaxRS) {
     const int64_t ntiles = ((int64_t)q.B * hwo + kIm2colPix - 1) / kIm2colPix;
     hipLaunchKernelGGL(conv_im2col_tile_kernel, dim3((unsigned)(ntiles < 65535 ? ntiles : 65535)),

@@ -182,3 +182,21 @@ def test_workload_shapes(bnn, oracle_lib, name, images):
     assert torch.equal(gi.double(), gi_ref), name
     assert torch.equal(gw.double(), gw_ref), name
     assert gsa == gsa_ref
+
+
+def test_grad_out_only_element_aligned(bnn, oracle_lib):
+    """A grad_out that is only 2-byte aligned takes the narrow copy into the workspace (the plane
+    size alone would allow 16-byte vectors)."""
+    geom = (2, 16, 8, 8, 24, (3, 3), 1, 1, 1)
+    g, wt, x = _inputs(11, geom, torch.float16, dyadic=True)
+    _, _, _, _, _, k, s, p, d = geom
+    gi_ref, gsa_ref, gw_ref = oracle_lib.conv2d_grad(g, wt, x, s, p, d, 0.5, 0.25)
+    buf = torch.empty(g.numel() + 1, dtype=g.dtype, device=DEV)
+    gd = buf[1:].view(g.shape)
+    gd.copy_(g.to(DEV))
+    assert gd.data_ptr() % 4 == 2
+    gi, gsa = bnn.conv2d_grad_input(gd, wt.to(DEV), x.to(DEV), 0.5, 0.25, s, p, d)
+    gw = bnn.conv2d_grad_weight(gd, x.to(DEV), k, 0.5, s, p, d)
+    torch.cuda.synchronize()
+    assert torch.equal(gi.cpu().double(), gi_ref) and torch.equal(gw.cpu().double(), gw_ref)
+    assert float(gsa.cpu()) == gsa_ref
