@@ -198,7 +198,7 @@ bnn_status bnn_pack_sign_nchw(const void* x, int x_dtype, int64_t n, int64_t c, 
   if (!int_fits(h * w) || !int_fits(n * words_of(c))) return BNN_ERR_SHAPE;
   if (n == 0) return BNN_OK;
   if (!x || !x_packed) return BNN_ERR_NULL;
-  if (!aligned(x, 16) || !aligned(x_packed, 4)) return BNN_ERR_ALIGN;
+  if (!aligned(x, elem_bytes(x_dtype)) || !aligned(x_packed, 4)) return BNN_ERR_ALIGN;
   return hip_status(bnn::launch_pack_nchw(x, x_dtype, n, c, h, w, x_packed,
                                           static_cast<hipStream_t>(stream)));
 }
@@ -231,7 +231,8 @@ bnn_status bnn_pack_sign_nchw_shift(const void* x, int x_dtype, int64_t n, int64
   if (!int_fits(h * w) || !int_fits(n * words_of(c))) return BNN_ERR_SHAPE;
   if (n == 0) return BNN_OK;
   if (!x || !bias || !x_packed) return BNN_ERR_NULL;
-  if (!aligned(x, 16) || !aligned(x_packed, 4) || !aligned(bias, elem_bytes(bias_dtype)))
+  if (!aligned(x, elem_bytes(x_dtype)) || !aligned(x_packed, 4) ||
+      !aligned(bias, elem_bytes(bias_dtype)))
     return BNN_ERR_ALIGN;
   return hip_status(bnn::launch_pack_nchw(x, x_dtype, n, c, h, w, x_packed,
                                           static_cast<hipStream_t>(stream), bias, bias_dtype));
@@ -389,7 +390,9 @@ bnn_status bnn_conv2d_ex(const void* x, int x_dtype, int64_t n, int64_t c, int64
   if (n == 0 || out_channels == 0) return BNN_OK;
   if (!x || !w_packed || !out) return BNN_ERR_NULL;
   const bool words_in = x_dtype == BNN_U32_PACKED || u8_in_place(x_dtype, c);
-  const int x_align = words_in ? 4 : x_dtype == BNN_U8_PACKED ? 1 : 16;
+  // float x needs only its element alignment: unaligned tensors (a sliced batch) take the
+  // element-wise NCHW pack
+  const int x_align = words_in ? 4 : x_dtype == BNN_U8_PACKED ? 1 : elem_bytes(x_dtype);
   if (!aligned(x, x_align) || !aligned(w_packed, 4) || !aligned(out, 16)) return BNN_ERR_ALIGN;
   const size_t need = bnn_conv2d_workspace_bytes(n, c, h, w, x_dtype);
   if (need > 0 && (!workspace || workspace_bytes < need)) return BNN_ERR_WORKSPACE;

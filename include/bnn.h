@@ -111,7 +111,9 @@ bnn_status bnn_u8_to_words(const uint8_t* src, int64_t rows, int64_t bits, uint3
                            void* stream);
 
 /* Sign + pack of NCHW activations along channels.
- *   x        [n, c, h, w] in x_dtype (BNN_F32/F16/BF16), 16-byte aligned.
+ *   x        [n, c, h, w] in x_dtype (BNN_F32/F16/BF16), aligned to its element size (a 16-byte
+ *            aligned tensor whose pixel planes are a multiple of the 16-byte vector width takes
+ *            the vector kernel, any other the element-wise one, e.g. a slice of a batch).
  *   x_packed [n, h, w, ceil(c/32)] uint32 out; bit j of word q = (x[n][32q+j][h][w] >= 0), 0 past c.
  * c >= 1. */
 bnn_status bnn_pack_sign_nchw(const void* x, int x_dtype, int64_t n, int64_t c, int64_t h,
@@ -228,8 +230,9 @@ bnn_status bnn_gemm_noalloc(const void* x, int x_dtype, const uint32_t* w_packed
                             void* out, int out_dtype, void* stream);
 
 /* Binary conv2d forward (square kernel, symmetric stride/padding/dilation).
- *   x         NCHW [n, c, h, w] in BNN_F32/F16/BF16, or [n, h, w, ceil(c/32)] BNN_U32_PACKED, or
- *             [n, h, w, ceil(c/8)] bytes BNN_U8_PACKED (8-bit containers, see bnn_dtype).
+ *   x         NCHW [n, c, h, w] in BNN_F32/F16/BF16 (aligned to its element size, packed here into
+ *             the workspace as bnn_pack_sign_nchw does), or [n, h, w, ceil(c/32)] BNN_U32_PACKED,
+ *             or [n, h, w, ceil(c/8)] bytes BNN_U8_PACKED (8-bit containers, see bnn_dtype).
  *   w_packed  [out_channels, k, k, ceil(c/32)] from bnn_w_pack(kernel_size = k).
  *   out       NCHW [n, out_channels, Ho, Wo] in out_dtype (BNN_F32/F16/BF16/I32),
  *             Ho = floor((h + 2*padding - dilation*(k-1) - 1)/stride + 1), likewise Wo.

@@ -210,7 +210,8 @@ def test_pack_argument_checks(bnn):
     assert L.bnn_pack_sign(FAKE + 2, bnn.F32, 4, 32, FAKE, None) == bnn.ERR_ALIGN
     assert L.bnn_pack_sign(None, bnn.F32, 0, 32, None, None) == bnn.OK
     assert L.bnn_pack_sign_nchw(None, bnn.F16, 1, 40, 4, 4, FAKE, None) == bnn.ERR_NULL
-    assert L.bnn_pack_sign_nchw(MISALIGNED, bnn.F16, 1, 40, 4, 4, FAKE, None) == bnn.ERR_ALIGN
+    assert L.bnn_pack_sign_nchw(FAKE + 1, bnn.F16, 1, 40, 4, 4, FAKE, None) == bnn.ERR_ALIGN   # odd byte
+    assert L.bnn_pack_sign_nchw(FAKE, bnn.F16, 1, 40, 4, 4, FAKE + 2, None) == bnn.ERR_ALIGN
     assert L.bnn_pack_sign_nchw(FAKE, bnn.F16, 1, 32, 0, 4, FAKE, None) == bnn.ERR_SHAPE
     assert L.bnn_w_pack(None, bnn.F32, 8, 48, 0, FAKE, None) == bnn.ERR_NULL
     assert L.bnn_w_pack(FAKE, bnn.F32, 8, 0, 0, FAKE, None) == bnn.ERR_SHAPE

@@ -351,3 +351,25 @@ def test_graph_replay_matches_eager(bnn):
             torch.cuda.synchronize()
             assert torch.equal(out, eager), (path, r)
             assert torch.equal(out_c, eager_c), (path, r)
+
+
+@pytest.mark.parametrize("tdt", [torch.float32, torch.float16, torch.bfloat16])
+def test_nchw_input_aligned_to_element_only(bnn, orc, tdt):
+    """A float NCHW tensor that is only element-aligned (a view that starts one element into its
+    buffer) packs through the element-wise kernel and convolves like an aligned copy."""
+    g = torch.Generator().manual_seed(29)
+    shape = (2, 40, 8, 8)                                # planes a multiple of the vector width
+    x = synth.inject_edges(torch.randn(shape, generator=g).to(tdt), 29, 200)
+    buf = torch.empty(x.numel() + 1, dtype=tdt, device=DEV)
+    xd = buf[1:].view(shape)
+    xd.copy_(x.to(DEV))
+    assert xd.data_ptr() % 16 != 0
+    assert torch.equal(bnn.pack_sign_nchw(xd).cpu(), orc.pack_nchw(x))
+    bias = synth.make_shift(40, "f32", 30)
+    assert torch.equal(bnn.pack_sign_nchw_shift(xd, bias.to(DEV)).cpu(), orc.pack_nchw_shift(x, bias))
+    w = torch.randn((24, 40, 3, 3), generator=g)
+    wp = bnn.w_pack(w.to(DEV))
+    want = orc.conv2d_acc(x, w, 1, 1, 1)
+    for path in ("xor", "mfma", "mfma_fp4"):
+        got = bnn.conv2d(xd, wp, 1.0, 1.0, 3, 1, 1, 1, path=path, out_dtype=torch.int32).cpu()
+        assert torch.equal(got, want), path
