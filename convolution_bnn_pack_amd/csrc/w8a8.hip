@@ -118,6 +118,7 @@ struct W8A8Conv {
   void* out;        // NCHW
   int M, N, K, C, H, W, Ho, Wo, KWD, SH, SW, PH, PW, DH, DW;
   float alpha;
+  FastDiv div_c, div_kwd, div_hw, div_wo;  // by C, the kernel width, Ho*Wo and Wo
 };
 
 template <int OUT>
@@ -132,38 +133,45 @@ __global__ __launch_bounds__(kThreads) void w8a8_conv_kernel(W8A8Conv p) {
   const int lrow = tid / kTPR, lj = (tid % kTPR) * kLPT;
   const int am = m0 + lrow, wnr = n0 + lrow;
   const bool amok = am < p.M, wnok = wnr < p.N;
-  int ab = 0, aih = 0, aiw = 0;  // image and top-left input coordinate of this A row
-  if (amok) {
-    const int hw = p.Ho * p.Wo;
-    ab = am / hw;
-    const int r = am - ab * hw;
-    const int oh = r / p.Wo, ow = r - oh * p.Wo;
-    aih = oh * p.SH - p.PH;
-    aiw = ow * p.SW - p.PW;
-  }
-  auto load_stage = [&](int s, uint4 (&ra)[kLPT], uint4 (&rw)[kLPT]) {
+  // image and top-left input coordinate of this A row (row 0's for rows past M)
+  const int hw = p.Ho * p.Wo;
+  const int ab = p.div_hw.div(amok ? am : 0);
+  const int ar = (amok ? am : 0) - ab * hw;
+  const int aoh = p.div_wo.div(ar), aow = ar - aoh * p.Wo;
+  const int aih = aoh * p.SH - p.PH, aiw = aow * p.SW - p.PW;
+  const int8_t* wrow = p.w + (int64_t)(wnok ? wnr : 0) * p.K;
+  // Every chunk is loaded unconditionally from an address clamped into the tensor (chunk 0 of
+  // the pixel or weight row) and its validity kept beside it; the zeroing waits for the store
+  // to LDS a stage later. A load behind a branch makes the compiler wait for all loads at the
+  // next use (it can no longer count them), which would drain the prefetch every stage.
+  auto load_stage = [&](int s, uint4 (&ra)[kLPT], uint4 (&rw)[kLPT], bool (&oa)[kLPT],
+                        bool (&ow)[kLPT]) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < kLPT; i++) {
       const int r0 = s * kSK + 16 * (lj + i);
-      ra[i] = make_uint4(0u, 0u, 0u, 0u);
-      rw[i] = make_uint4(0u, 0u, 0u, 0u);
-      if (r0 < p.K) {
-        if (amok) {
-          const int tap = r0 / p.C, c = r0 - tap * p.C;
-          const int kh = tap / p.KWD, kw = tap - kh * p.KWD;
-          const int ih = aih + kh * p.DH, iw = aiw + kw * p.DW;
-          if (ih >= 0 && ih < p.H && iw >= 0 && iw < p.W)
-            ra[i] = *reinterpret_cast<const uint4*>(p.a + (((int64_t)ab * p.H + ih) * p.W + iw) * p.C + c);
-        }
-        if (wnok) rw[i] = *reinterpret_cast<const uint4*>(p.w + (int64_t)wnr * p.K + r0);
-      }
+      const bool kin = r0 < p.K;
+      const int rk = kin ? r0 : 0;
+      const int tap = p.div_c.div(rk), c = rk - tap * p.C;
+      const int kh = p.div_kwd.div(tap), kw = tap - kh * p.KWD;
+      const int ih = aih + kh * p.DH, iw = aiw + kw * p.DW;
+      oa[i] = kin && amok && ih >= 0 && ih < p.H && iw >= 0 && iw < p.W;
+      ow[i] = kin && wnok;
+      const int64_t aoff = oa[i] ? (((int64_t)ab * p.H + ih) * p.W + iw) * p.C + c : 0;
+      ra[i] = *reinterpret_cast<const uint4*>(p.a + aoff);
+      rw[i] = *reinterpret_cast<const uint4*>(wrow + rk);
     }
   };
-  auto store_stage = [&](int buf, const uint4 (&ra)[kLPT], const uint4 (&rw)[kLPT]) {
+  auto store_stage = [&](int buf, const uint4 (&ra)[kLPT], const uint4 (&rw)[kLPT],
+                         const bool (&oa)[kLPT], const bool (&ow)[kLPT]) __attribute__((always_inline)) {
+    // masks rather than a select of whole vectors (which the compiler turns into a select of
+    // addresses and a round trip through scratch memory)
 #pragma unroll
     for (int i = 0; i < kLPT; i++) {
-      *reinterpret_cast<uint4*>(&lds[buf][lrow * kRow + 16 * (lj + i)]) = ra[i];
-      *reinterpret_cast<uint4*>(&lds[buf][(kBM + lrow) * kRow + 16 * (lj + i)]) = rw[i];
+      const uint32_t ma = oa[i] ? ~0u : 0u, mw = ow[i] ? ~0u : 0u;
+      *reinterpret_cast<uint4*>(&lds[buf][lrow * kRow + 16 * (lj + i)]) =
+          make_uint4(ra[i].x & ma, ra[i].y & ma, ra[i].z & ma, ra[i].w & ma);
+      *reinterpret_cast<uint4*>(&lds[buf][(kBM + lrow) * kRow + 16 * (lj + i)]) =
+          make_uint4(rw[i].x & mw, rw[i].y & mw, rw[i].z & mw, rw[i].w & mw);
     }
   };
 
@@ -180,7 +188,8 @@ __global__ __launch_bounds__(kThreads) void w8a8_conv_kernel(W8A8Conv p) {
   // raw chunks two stages ahead: stage t is fetched into register set t % 2 two stages
   // before its MFMAs, and stored to LDS buffer t % 2 right after the MFMAs of stage t - 1
   uint4 ra[2][kLPT], rw[2][kLPT];
-  auto compute = [&](int buf) {
+  bool oa[2][kLPT], ow[2][kLPT];
+  auto compute = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int kk = 0; kk < kSK / 32; kk++) {
       v4i fa[kFM], fw[kFN];
@@ -199,16 +208,17 @@ __global__ __launch_bounds__(kThreads) void w8a8_conv_kernel(W8A8Conv p) {
   };
   // one stage: fetch stage s + 2 into set PH (stage s's set, already in LDS), run stage s from
   // buffer PH, store stage s + 1 (set PH ^ 1) into buffer PH ^ 1; PH = s % 2 at compile time
-  auto stage = [&](auto phase, int s) {
+  auto stage = [&](auto phase, int s) __attribute__((always_inline)) {
     constexpr int PH = decltype(phase)::value;
-    if (s + 2 < nstages) load_stage(s + 2, ra[PH], rw[PH]);
+    // past the last stage the loads fetch clamped, invalid chunks that are never stored
+    load_stage(s + 2, ra[PH], rw[PH], oa[PH], ow[PH]);
     compute(PH);
-    if (s + 1 < nstages) store_stage(PH ^ 1, ra[PH ^ 1], rw[PH ^ 1]);
+    if (s + 1 < nstages) store_stage(PH ^ 1, ra[PH ^ 1], rw[PH ^ 1], oa[PH ^ 1], ow[PH ^ 1]);
     __syncthreads();
   };
-  load_stage(0, ra[0], rw[0]);
-  if (nstages > 1) load_stage(1, ra[1], rw[1]);
-  store_stage(0, ra[0], rw[0]);
+  load_stage(0, ra[0], rw[0], oa[0], ow[0]);
+  load_stage(1, ra[1], rw[1], oa[1], ow[1]);
+  store_stage(0, ra[0], rw[0], oa[0], ow[0]);
   __syncthreads();
   int s = 0;
   for (; s + 2 <= nstages; s += 2) {
@@ -219,7 +229,6 @@ __global__ __launch_bounds__(kThreads) void w8a8_conv_kernel(W8A8Conv p) {
 
   // epilogue: lane (fr, half) holds channel n = n0 + wn*kWTN + fn*32 + fr and, in e = 4g..4g+3,
   // the pixels m = m0 + wm*kWTM + fm*32 + 8g + 4*half + 0..3
-  const int hw = p.Ho * p.Wo;
 #pragma unroll
   for (int fn = 0; fn < kFN; fn++) {
     const int n = n0 + wn * kWTN + fn * 32 + fr;
@@ -230,7 +239,7 @@ __global__ __launch_bounds__(kThreads) void w8a8_conv_kernel(W8A8Conv p) {
       for (int g = 0; g < 4; g++) {
         const int m = m0 + wm * kWTM + fm * 32 + 8 * g + 4 * half;
         if (m >= p.M) continue;
-        const int b = m / hw, pix = m - b * hw;
+        const int b = p.div_hw.div(m), pix = m - b * hw;
         const int v0 = acc[fn][fm][4 * g], v1 = acc[fn][fm][4 * g + 1];
         const int v2 = acc[fn][fm][4 * g + 2], v3 = acc[fn][fm][4 * g + 3];
         if ((hw & 3) == 0) {
@@ -305,6 +314,10 @@ hipError_t launch_w8a8_conv(const int8_t* xq, const int8_t* wq, void* out, int o
   p.DH = dh;
   p.DW = dw;
   p.alpha = alpha;
+  p.div_c = FastDiv((uint32_t)c);
+  p.div_kwd = FastDiv((uint32_t)kw);
+  p.div_hw = FastDiv((uint32_t)(ho * wo));
+  p.div_wo = FastDiv((uint32_t)wo);
   if (p.M == 0 || p.N == 0) return hipSuccess;
   const int64_t tiles = (int64_t)((p.M + kBM - 1) / kBM) * ((p.N + kBN - 1) / kBN);
   const dim3 grid((unsigned)tiles), block(kThreads);
