@@ -52,13 +52,22 @@ __global__ __launch_bounds__(256) void quant_nhwc_kernel(const void* __restrict_
   const int p0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;  // pixel lane, channel group
   const int p = p0 + tx;
-  if (p < P) {
-    const int b = p / HW, pix = p - b * HW;
-#pragma unroll 4
-    for (int k = 0; k < 16; k++) {
-      const int cl = ty + 4 * k, c = c0 + cl;
-      tile[tx][cl] = c < C ? quant_code(load_f32<DT>(x, ((int64_t)b * C + c) * HW + pix), step) : 0;
-    }
+  // all 16 loads go out before any is used: addresses clamped into the tensor (the last pixel
+  // or channel), the codes of clamped elements replaced by 0 afterwards (a load behind a
+  // branch is waited for on the spot)
+  const int pc = p < P ? p : P - 1;
+  const int b = pc / HW, pix = pc - b * HW;
+  float v[16];
+#pragma unroll
+  for (int k = 0; k < 16; k++) {
+    const int c = c0 + ty + 4 * k;
+    v[k] = load_f32<DT>(x, ((int64_t)b * C + (c < C ? c : C - 1)) * HW + pix);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int k = 0; k < 16; k++) {
+    const int cl = ty + 4 * k;
+    tile[tx][cl] = (p < P && c0 + cl < C) ? quant_code(v[k], step) : 0;
   }
   __syncthreads();
   // write: thread -> (pixel row, 16-byte column); 64 pixels x 4 columns = 256 stores
