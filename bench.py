@@ -159,8 +159,14 @@ def pmc_summary(args):
         scale = (args.copy_mib << 20) / 1024.0 / copy_kib if args.copy_mib else 1.0
         for k in ([kind] if kind else ["mfma", "mfma_fp4", "xor", "w8a8", "bwd"]):
             # the workload's kernel is the instantiation launched most often (the parity spot
-            # check adds single launches of other output types)
-            cands = [(len(vs), name) for name, vs in vals.items() if kernel_kind(name) == k]
+            # check adds single launches of other output types); a codec workload names its
+            # kernel (kinds that share a kernel function, e.g. the one-pass prologue, differ by
+            # instantiation only)
+            def is_k(name):
+                if kind:
+                    return KERNEL_NAMES[k] + "<" in name or KERNEL_NAMES[k] + "(" in name
+                return kernel_kind(name) == k
+            cands = [(len(vs), name) for name, vs in vals.items() if is_k(name)]
             if not cands:
                 continue
             _, name = max(cands)
