@@ -104,22 +104,31 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const void* __restric
   out[idx] = quant_code(load_f32<DT>(w, (o * C + c) * T + t), step);
 }
 
-// Implicit-im2col int8 contraction. Tile 128 output pixels x 128 output channels, eight
-// waves in a 2 x 4 grid (two per SIMD), each a 64 x 32 sub-tile of 2 x 1 blocks of
+// Implicit-im2col int8 contraction. Tile 128 output pixels x BN (128 or 256) output channels,
+// eight waves in a 2 x 4 grid (two per SIMD), each a 64 x BN/4 sub-tile of 2 x BN/128 blocks of
 // v_mfma_i32_32x32x32_i8. A stage is 128 reduction bytes (four MFMA k-steps): the A tile
 // (pixels) and the W tile (channels) are loaded as 16-byte chunks into registers, written
 // to one of two LDS buffers (rows padded to 144 bytes to spread the banks), and consumed
 // after one barrier while the next stage's chunks are in flight. The MFMA computes
 // D = A * W^T, so a lane's four consecutive accumulators are four consecutive pixels of
 // one output channel (as in the binary conv tiles).
-constexpr int kBM = 128, kBN = 128, kSK = 128, kRow = kSK + 16;
+constexpr int kBM = 128, kSK = 128, kRow = kSK + 16;
 constexpr int kThreads = 512, kWGM = 2, kWGN = 4;              // wave grid
-constexpr int kWTM = kBM / kWGM, kWTN = kBN / kWGN;            // wave sub-tile
-constexpr int kFM = kWTM / 32, kFN = kWTN / 32;                // MFMA blocks per wave
+constexpr int kWTM = kBM / kWGM;                               // wave sub-tile rows
+constexpr int kFM = kWTM / 32;                                 // MFMA blocks per wave along pixels
 constexpr int kCPR = kSK / 16;                                 // 16-byte chunks per row and stage
-constexpr int kLPT = kCPR * kBM / kThreads;                    // chunks per thread (A, and W)
-constexpr int kTPR = kCPR / kLPT;                              // loader threads per row
-static_assert(kBM == kBN && kLPT * kTPR == kCPR && kTPR * kBM == kThreads, "loader split");
+// Output channels per tile: BN = 256 (64 x 64 per wave, 2 x 2 blocks: 4 fragment reads per 4
+// MFMAs) when the layer has more than 128 output channels, else 128 (64 x 32, 3 reads per 2).
+// Loader split: every thread takes LPT consecutive chunks of one row of A (BM rows) and of W
+// (BN rows) per stage.
+template <int BN>
+struct W8Tile {
+  static constexpr int WTN = BN / kWGN, FN = WTN / 32;
+  static constexpr int LPTA = kCPR * kBM / kThreads, TPRA = kCPR / LPTA;
+  static constexpr int LPTW = kCPR * BN / kThreads, TPRW = kCPR / LPTW;
+  static_assert(LPTA * TPRA == kCPR && TPRA * kBM == kThreads && LPTW * TPRW == kCPR &&
+                    TPRW * BN == kThreads, "loader split");
+};
 
 struct W8A8Conv {
   const int8_t* a;  // NHWC codes
@@ -130,17 +139,20 @@ struct W8A8Conv {
   FastDiv div_c, div_kwd, div_hw, div_wo;  // by C, the kernel width, Ho*Wo and Wo
 };
 
-template <int OUT>
+template <int OUT, int BN>
 __global__ __launch_bounds__(kThreads) void w8a8_conv_kernel(W8A8Conv p) {
+  using TL = W8Tile<BN>;
+  constexpr int kBN = BN, kWTN = TL::WTN, kFN = TL::FN, LA = TL::LPTA, LW = TL::LPTW;
   __shared__ __attribute__((aligned(16))) int8_t lds[2][(kBM + kBN) * kRow];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave % kWGM, wn = wave / kWGM;
   const int tiles_n = (p.N + kBN - 1) / kBN;
   const int m0 = (blockIdx.x / tiles_n) * kBM, n0 = (blockIdx.x % tiles_n) * kBN;
 
-  // loader: chunks lj .. lj + kLPT - 1 of row lrow
-  const int lrow = tid / kTPR, lj = (tid % kTPR) * kLPT;
-  const int am = m0 + lrow, wnr = n0 + lrow;
+  // loaders: chunks ljA .. ljA + LA - 1 of A row lrowA, chunks ljW .. ljW + LW - 1 of W row lrowW
+  const int lrowA = tid / TL::TPRA, ljA = (tid % TL::TPRA) * LA;
+  const int lrowW = tid / TL::TPRW, ljW = (tid % TL::TPRW) * LW;
+  const int am = m0 + lrowA, wnr = n0 + lrowW;
   const bool amok = am < p.M, wnok = wnr < p.N;
   // image and top-left input coordinate of this A row (row 0's for rows past M)
   const int hw = p.Ho * p.Wo;
@@ -153,33 +165,42 @@ __global__ __launch_bounds__(kThreads) void w8a8_conv_kernel(W8A8Conv p) {
   // the pixel or weight row) and its validity kept beside it; the zeroing waits for the store
   // to LDS a stage later. A load behind a branch makes the compiler wait for all loads at the
   // next use (it can no longer count them), which would drain the prefetch every stage.
-  auto load_stage = [&](int s, uint4 (&ra)[kLPT], uint4 (&rw)[kLPT], bool (&oa)[kLPT],
-                        bool (&ow)[kLPT]) __attribute__((always_inline)) {
+  auto load_stage = [&](int s, uint4 (&ra)[LA], uint4 (&rw)[LW], bool (&oa)[LA],
+                        bool (&ow)[LW]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < kLPT; i++) {
-      const int r0 = s * kSK + 16 * (lj + i);
+    for (int i = 0; i < LA; i++) {
+      const int r0 = s * kSK + 16 * (ljA + i);
       const bool kin = r0 < p.K;
       const int rk = kin ? r0 : 0;
       const int tap = p.div_c.div(rk), c = rk - tap * p.C;
       const int kh = p.div_kwd.div(tap), kw = tap - kh * p.KWD;
       const int ih = aih + kh * p.DH, iw = aiw + kw * p.DW;
       oa[i] = kin && amok && ih >= 0 && ih < p.H && iw >= 0 && iw < p.W;
-      ow[i] = kin && wnok;
       const int64_t aoff = oa[i] ? (((int64_t)ab * p.H + ih) * p.W + iw) * p.C + c : 0;
       ra[i] = *reinterpret_cast<const uint4*>(p.a + aoff);
-      rw[i] = *reinterpret_cast<const uint4*>(wrow + rk);
+    }
+#pragma unroll
+    for (int i = 0; i < LW; i++) {
+      const int r0 = s * kSK + 16 * (ljW + i);
+      const bool kin = r0 < p.K;
+      ow[i] = kin && wnok;
+      rw[i] = *reinterpret_cast<const uint4*>(wrow + (kin ? r0 : 0));
     }
   };
-  auto store_stage = [&](int buf, const uint4 (&ra)[kLPT], const uint4 (&rw)[kLPT],
-                         const bool (&oa)[kLPT], const bool (&ow)[kLPT]) __attribute__((always_inline)) {
+  auto store_stage = [&](int buf, const uint4 (&ra)[LA], const uint4 (&rw)[LW],
+                         const bool (&oa)[LA], const bool (&ow)[LW]) __attribute__((always_inline)) {
     // masks rather than a select of whole vectors (which the compiler turns into a select of
     // addresses and a round trip through scratch memory)
 #pragma unroll
-    for (int i = 0; i < kLPT; i++) {
-      const uint32_t ma = oa[i] ? ~0u : 0u, mw = ow[i] ? ~0u : 0u;
-      *reinterpret_cast<uint4*>(&lds[buf][lrow * kRow + 16 * (lj + i)]) =
+    for (int i = 0; i < LA; i++) {
+      const uint32_t ma = oa[i] ? ~0u : 0u;
+      *reinterpret_cast<uint4*>(&lds[buf][lrowA * kRow + 16 * (ljA + i)]) =
           make_uint4(ra[i].x & ma, ra[i].y & ma, ra[i].z & ma, ra[i].w & ma);
-      *reinterpret_cast<uint4*>(&lds[buf][(kBM + lrow) * kRow + 16 * (lj + i)]) =
+    }
+#pragma unroll
+    for (int i = 0; i < LW; i++) {
+      const uint32_t mw = ow[i] ? ~0u : 0u;
+      *reinterpret_cast<uint4*>(&lds[buf][(kBM + lrowW) * kRow + 16 * (ljW + i)]) =
           make_uint4(rw[i].x & mw, rw[i].y & mw, rw[i].z & mw, rw[i].w & mw);
     }
   };
@@ -196,8 +217,8 @@ __global__ __launch_bounds__(kThreads) void w8a8_conv_kernel(W8A8Conv p) {
   const int nstages = (p.K + kSK - 1) / kSK;
   // raw chunks two stages ahead: stage t is fetched into register set t % 2 two stages
   // before its MFMAs, and stored to LDS buffer t % 2 right after the MFMAs of stage t - 1
-  uint4 ra[2][kLPT], rw[2][kLPT];
-  bool oa[2][kLPT], ow[2][kLPT];
+  uint4 ra[2][LA], rw[2][LW];
+  bool oa[2][LA], ow[2][LW];
   auto compute = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int kk = 0; kk < kSK / 32; kk++) {
@@ -299,6 +320,19 @@ hipError_t launch_quant_weight(const void* w, int dtype, int64_t o, int64_t c, i
   return hipGetLastError();
 }
 
+template <int BN>
+hipError_t launch_w8a8_t(const W8A8Conv& p, int out_dtype, hipStream_t stream) {
+  const int64_t tiles = (int64_t)((p.M + kBM - 1) / kBM) * ((p.N + BN - 1) / BN);
+  const dim3 grid((unsigned)tiles), block(kThreads);
+  switch (out_dtype) {
+    case kF32: hipLaunchKernelGGL((w8a8_conv_kernel<kF32, BN>), grid, block, 0, stream, p); break;
+    case kF16: hipLaunchKernelGGL((w8a8_conv_kernel<kF16, BN>), grid, block, 0, stream, p); break;
+    case kBF16: hipLaunchKernelGGL((w8a8_conv_kernel<kBF16, BN>), grid, block, 0, stream, p); break;
+    default: hipLaunchKernelGGL((w8a8_conv_kernel<kI32, BN>), grid, block, 0, stream, p); break;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_w8a8_conv(const int8_t* xq, const int8_t* wq, void* out, int out_dtype,
                             int64_t n, int64_t c, int64_t h, int64_t w, int64_t o, int64_t ho,
                             int64_t wo, int kh, int kw, int sh, int sw, int ph, int pw, int dh,
@@ -328,15 +362,13 @@ hipError_t launch_w8a8_conv(const int8_t* xq, const int8_t* wq, void* out, int o
   p.div_hw = FastDiv((uint32_t)(ho * wo));
   p.div_wo = FastDiv((uint32_t)wo);
   if (p.M == 0 || p.N == 0) return hipSuccess;
-  const int64_t tiles = (int64_t)((p.M + kBM - 1) / kBM) * ((p.N + kBN - 1) / kBN);
-  const dim3 grid((unsigned)tiles), block(kThreads);
-  switch (out_dtype) {
-    case kF32: hipLaunchKernelGGL(w8a8_conv_kernel<kF32>, grid, block, 0, stream, p); break;
-    case kF16: hipLaunchKernelGGL(w8a8_conv_kernel<kF16>, grid, block, 0, stream, p); break;
-    case kBF16: hipLaunchKernelGGL(w8a8_conv_kernel<kBF16>, grid, block, 0, stream, p); break;
-    default: hipLaunchKernelGGL(w8a8_conv_kernel<kI32>, grid, block, 0, stream, p); break;
-  }
-  return hipGetLastError();
+  // 256-wide tiles when they fill at most one round of the 256 compute units (one workgroup
+  // each: 108 KiB of LDS); with more tiles the 128-wide ones, two per compute unit, balance
+  // better (measured on the 128 x 128 x 28 x 28 -> 256 layers: strided 20.0 -> 19.0 us with 256,
+  // dilated 60.6 -> 66 us)
+  const int64_t tiles256 = (int64_t)((p.M + kBM - 1) / kBM) * ((p.N + 255) / 256);
+  return p.N > 128 && tiles256 <= 256 ? launch_w8a8_t<256>(p, out_dtype, stream)
+                                      : launch_w8a8_t<128>(p, out_dtype, stream);
 }
 
 }  // namespace bnn
