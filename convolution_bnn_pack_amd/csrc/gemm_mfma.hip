@@ -913,7 +913,9 @@ template <class T, int OUT, bool CONV, bool VEC>
 hipError_t launch_tile_o(const Contraction& p, hipStream_t stream) {
   const int64_t tiles = (int64_t)((p.M + T::BM - 1) / T::BM) * ((p.N + T::BN - 1) / T::BN);
   const dim3 block(T::THREADS);
-  if constexpr (CONV && T::F4) {
+  if constexpr (CONV && T::F4 && T::THREADS == 512) {
+    // (8-wave tiles only: the 4-wave conv tile runs two workgroups per compute unit instead,
+    // so one's epilogue overlaps the other's loop)
     // more fp4 conv tiles than fit at once: one persistent workgroup per resident slot
     // streams its tiles back to back instead of running them in separate rounds (the
     // int8 256 x 256 conv tile would spill with the extra state). Channel counts that are
@@ -985,6 +987,11 @@ struct Tiles {
   using L = std::conditional_t<F4 && CONV, M,
                                Tile<256, 256, KS, BNN_MFMA_PD_L, 2, BNN_MFMA_L_WAVES_N, F4>>;
   using S = Tile<128, 128, KS, PD_M, 2, BNN_MFMA_WAVES_N, F4>;
+  // fp4 convs with two or more rounds of 128 x 256 tiles: 128 x 128 tiles of 2 x 2 waves (the
+  // same 64 x 64 per wave), two workgroups per compute unit, one tile each: 40.2 -> 37.5 us on
+  // the dilated 128 x 128 x 28 x 28 -> 256 layer against persistent 128 x 256 tiles (the strided
+  // layer, one round, stays on those: 13.2 against 14.0 us)
+  using C2 = Tile<128, 128, KS, PD_M, 2, 2, F4>;
   // fp4 layers whose 64 x 128 tiles fit in one round of workgroups: 64 x 128 tiles, 1 x 4
   // waves, twice the workgroups of 128 x 128 (the 32x256x14x14 stage-3 conv: 12.6 -> 10.7 us,
   // linear layers from 64x256x512 to 1024x2048x4096: 13-20 % faster; a 1536x2048x2048 layer,
@@ -1017,12 +1024,13 @@ hipError_t launch_mfma_t(const Contraction& p, int out_dtype, hipStream_t stream
     if (BNN_CONV_TILE == 1) return launch_tile<typename TS::M, CONV>(p, out_dtype, stream);
     if (BNN_CONV_TILE == 2) return launch_tile<typename TS::S, CONV>(p, out_dtype, stream);
     if (BNN_CONV_TILE == 3) return launch_tile<typename TS::T64, CONV>(p, out_dtype, stream);
-    if (BNN_CONV_TILE == 4)  // 128 x 128, 2 x 2 waves: two workgroups per compute unit
-      return launch_tile<Tile<128, 128, TS::KS, TS::PD_M, 2, 2, F4>, CONV>(p, out_dtype, stream);
+    if (BNN_CONV_TILE == 4) return launch_tile<typename TS::C2, CONV>(p, out_dtype, stream);
   }
 #endif
   if (F4 && p.N <= 64 && count_tiles(p, 256, 64) >= kMinTiles)
     return launch_tile<typename TS::N64, CONV>(p, out_dtype, stream);
+  if (CONV && F4 && count_tiles(p, 128, 256) >= 2 * kMinTiles)
+    return launch_tile<typename TS::C2, CONV>(p, out_dtype, stream);
   if (count_tiles(p, 256, 256) >= kMinTiles)
     return launch_tile<typename TS::L, CONV, std::conditional_t<F4, typename TS::M, typename TS::L>>(
         p, out_dtype, stream);

@@ -210,6 +210,28 @@ def test_persistent_conv_tiles(bnn, orc):
         check_scaled(out, acc, y, f"persistent conv {b}x{c}x{h}x{w}")
 
 
+def test_two_round_conv_tiles(bnn, orc):
+    """Conv shapes with two or more rounds of fp4 128 x 256 tiles, which run as 128 x 128 tiles of
+    four waves, two workgroups per compute unit (ragged last tile, ragged N, planes whose size is
+    not a multiple of 4 or 8): full oracle check."""
+    g = torch.Generator().manual_seed(73)
+    cases = [(88, 32, 28, 28, 256, 3, 1, 1, 1),    # 539 row tiles, planes of 784
+             (96, 32, 27, 27, 200, 3, 1, 1, 1),    # 547 row tiles, ragged N, planes of 729
+             (84, 64, 28, 28, 136, 3, 1, 2, 2)]    # dilated, 515 row tiles
+    for (b, c, h, w, o, ks, st, pd, dl) in cases:
+        x = torch.randn((b, c, h, w), generator=g).half()
+        wt = torch.randn((o, c, ks, ks), generator=g).half()
+        acc = orc.conv2d_acc(x, wt, st, pd, dl)
+        y = orc.scale(acc, 0.75, 0.5)
+        xd, wp = x.to(DEV), bnn.w_pack(wt.to(DEV))
+        _say(f"two-round conv {b}x{c}x{h}x{w} -> {o}, k{ks} d{dl}")
+        got = bnn.conv2d(xd, wp, 0.75, 0.5, ks, st, pd, dl, path="mfma_fp4", out_dtype=torch.int32)
+        assert torch.equal(got.cpu(), acc), (b, c, h, w, o, ks)
+        for odt in (torch.float16, torch.float32):
+            out = bnn.conv2d(xd, wp, 0.75, 0.5, ks, st, pd, dl, path="mfma_fp4", out_dtype=odt)
+            check_scaled(out, acc, y, f"two-round conv {b}x{c}x{h}x{w} {odt}")
+
+
 # ----------------------------------------------------------------------------- sweeps and edges
 
 def test_random_linear_sweep(bnn, orc):
