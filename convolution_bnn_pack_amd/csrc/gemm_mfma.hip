@@ -59,6 +59,11 @@
 
 #include "launch.h"
 
+// Tuning knob: m-tiles per band of the tile order (0 or 1: row-major tiles).
+#ifndef BNN_MFMA_GROUP_M
+#define BNN_MFMA_GROUP_M 4
+#endif
+
 // Tuning knob: a scheduling fence after every BNN_MFMA_SLOT_FENCE MFMA slots (0: none).
 #ifndef BNN_MFMA_SLOT_FENCE
 #define BNN_MFMA_SLOT_FENCE 4
@@ -221,13 +226,24 @@ __device__ __forceinline__ void load_w(const Contraction& p, int n, int q0, uint
 }
 
 // Tile slot (the workgroup index, or slot + i * grid for a persistent workgroup) ->
-// (m-tile, n-tile): contiguous runs of tiles per XCD (slot % 8), n fastest.
+// (m-tile, n-tile): contiguous runs of tiles per XCD (slot % 8); within a run, bands of
+// BNN_MFMA_GROUP_M m-tiles walked m fastest (0: plain rows, n fastest), so the tiles an XCD runs
+// at once share fewer operand panels in its L2.
 __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int slot, int& tm, int& tn) {
   const int total = tiles_m * tiles_n;
   int t = slot;
   if ((total & 7) == 0) t = (t & 7) * (total >> 3) + (t >> 3);
-  tm = t / tiles_n;
-  tn = t - tm * tiles_n;
+  if (BNN_MFMA_GROUP_M > 1) {
+    const int band = BNN_MFMA_GROUP_M * tiles_n;
+    const int g = t / band, r = t - g * band;
+    const int m0 = g * BNN_MFMA_GROUP_M;
+    const int gm = tiles_m - m0 < BNN_MFMA_GROUP_M ? tiles_m - m0 : BNN_MFMA_GROUP_M;
+    tn = r / gm;
+    tm = m0 + (r - tn * gm);
+  } else {
+    tm = t / tiles_n;
+    tn = t - tm * tiles_n;
+  }
 }
 
 // One LDS fragment read (16 bytes per lane) of row r, reduction chunk c.
