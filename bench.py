@@ -92,8 +92,8 @@ def kernel_kind(name):
         if KERNEL_NAMES[kind] + "<" in name or KERNEL_NAMES[kind] + "(" in name:
             return kind
     if "mfma_kernel<" in name:
-        # the tile's last template argument is the fp4 flag
-        m = re.search(r"Tile<[^>]*, (true|false)>", name)
+        # the tile's seventh template argument is the fp4 flag
+        m = re.search(r"Tile<(?:\d+, ){6}(true|false)", name)
         return "mfma_fp4" if m and m.group(1) == "true" else "mfma"
     return None
 

@@ -86,10 +86,11 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 constexpr int kFmtFp4 = 4;
 constexpr int kScaleOne = 127;
 
-template <int BM_, int BN_, int KS_, int PD_, int WGM_, int WGN_, bool F4_>
+template <int BM_, int BN_, int KS_, int PD_, int WGM_, int WGN_, bool F4_, int OCC_ = 1>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, KS = KS_;
   static constexpr bool F4 = F4_;                   // fp4 (e2m1) operands instead of int8
+  static constexpr int OCC = OCC_;                  // waves per SIMD the registers must allow
   static constexpr int PD = PD_;                    // stages of raw words in flight (register sets)
   static constexpr int UNROLL = PD % 2 == 0 ? PD : 2 * PD;  // lcm(2, PD): LDS parity x register set
   static constexpr int WGM = WGM_, WGN = WGN_;      // wave grid: WGM waves along A rows, WGN along W rows
@@ -565,7 +566,7 @@ __device__ __forceinline__ void store_tile(const Contraction& p, const Acc (&acc
 // 2*popA are kept per loader thread in LDS slots of two tile parities, so no LDS atomics
 // or clearing are needed between tiles.
 template <class T, int OUT, bool CONV, bool VEC, bool PERS>
-__global__ __launch_bounds__(T::THREADS) void mfma_kernel(Contraction p) {
+__global__ __launch_bounds__(T::THREADS, T::OCC) void mfma_kernel(Contraction p) {
   static_assert(!PERS || CONV, "persistent tiles use the direct (unstaged) conv epilogue");
   // two distinct arrays (not one array indexed by stage parity) so the compiler can
   // tell the expansion's writes from the fragment reads
@@ -1004,10 +1005,12 @@ struct Tiles {
                                Tile<256, 256, KS, BNN_MFMA_PD_L, 2, BNN_MFMA_L_WAVES_N, F4>>;
   using S = Tile<128, 128, KS, PD_M, 2, BNN_MFMA_WAVES_N, F4>;
   // fp4 convs with two or more rounds of 128 x 256 tiles: 128 x 128 tiles of 2 x 2 waves (the
-  // same 64 x 64 per wave), two workgroups per compute unit, one tile each: 40.2 -> 37.5 us on
-  // the dilated 128 x 128 x 28 x 28 -> 256 layer against persistent 128 x 256 tiles (the strided
-  // layer, one round, stays on those: 13.2 against 14.0 us)
-  using C2 = Tile<128, 128, KS, PD_M, 2, 2, F4>;
+  // same 64 x 64 per wave), one tile per workgroup, stages of 4 words (32 KiB of LDS) and at most
+  // 168 registers per lane so that three workgroups share a compute unit: on the dilated
+  // 128 x 128 x 28 x 28 -> 256 layer 40.2 us with persistent 128 x 256 tiles, 37.5 with these
+  // tiles at 8-word stages (two workgroups per compute unit), 34.0 at three (the strided layer,
+  // one round of 128 x 256 tiles, stays on those: 13.7 against 14.3 us)
+  using C2 = Tile<128, 128, F4 && CONV ? 4 : KS, PD_M, 2, 2, F4, F4 && CONV ? 3 : 1>;
   // fp4 layers whose 64 x 128 tiles fit in one round of workgroups: 64 x 128 tiles, 1 x 4
   // waves, twice the workgroups of 128 x 128 (the 32x256x14x14 stage-3 conv: 12.6 -> 10.7 us,
   // linear layers from 64x256x512 to 1024x2048x4096: 13-20 % faster; a 1536x2048x2048 layer,
