@@ -85,9 +85,9 @@ CODEC_KINDS = ("pack", "pack_shift", "pack_nchw", "abs_mean", "prologue", "prolo
 def kernel_kind(name):
     """Kind of a demangled kernel name from a rocprofv3 counter file (None: not ours)."""
     if "bwd_gemm_kernel<" in name:
-        # template arguments <bf16, A transposed, grad_input epilogue>: the roofline line of the
-        # backward is the grad_input contraction
-        return "bwd" if re.search(r"bwd_gemm_kernel<\w+, false, true>", name) else None
+        # template arguments <bf16, A transposed, grad_input epilogue, ...>: the roofline line of
+        # the backward is the grad_input contraction
+        return "bwd" if re.search(r"bwd_gemm_kernel<\w+, false, true[,>]", name) else None
     for kind in CODEC_KINDS + ("xor", "w8a8"):
         if KERNEL_NAMES[kind] + "<" in name or KERNEL_NAMES[kind] + "(" in name:
             return kind
