@@ -179,6 +179,8 @@ struct Contraction {
   int H, W, CW, Ho, Wo, KH, KWD, SH, SW, PH, PW, DH, DW;
   // the same divisors for FastDiv: Ho * Wo, Wo, CW, KWD
   FastDiv div_hw, div_wo, div_cw, div_kwd;
+  // matrix-core kernel: tiles along N of the launched tile shape (set by its launcher)
+  FastDiv div_tn;
 };
 
 }  // namespace bnn

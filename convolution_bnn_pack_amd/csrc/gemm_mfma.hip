@@ -59,9 +59,13 @@
 
 #include "launch.h"
 
-// Tuning knob: m-tiles per band of the tile order (0 or 1: row-major tiles).
+// Tuning knobs: m-tiles per band of the linear tile order (0 or 1: row-major tiles), and the
+// fewest tiles a linear grid needs for the bands to apply.
 #ifndef BNN_MFMA_GROUP_M
 #define BNN_MFMA_GROUP_M 4
+#endif
+#ifndef BNN_MFMA_GROUP_MIN_TILES
+#define BNN_MFMA_GROUP_MIN_TILES 1024
 #endif
 
 // Tuning knob: a scheduling fence after every BNN_MFMA_SLOT_FENCE MFMA slots (0: none).
@@ -227,22 +231,33 @@ __device__ __forceinline__ void load_w(const Contraction& p, int n, int q0, uint
 }
 
 // Tile slot (the workgroup index, or slot + i * grid for a persistent workgroup) ->
-// (m-tile, n-tile): contiguous runs of tiles per XCD (slot % 8); within a run, bands of
-// BNN_MFMA_GROUP_M m-tiles walked m fastest (0: plain rows, n fastest), so the tiles an XCD runs
-// at once share fewer operand panels in its L2.
-__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int slot, int& tm, int& tn) {
+// (m-tile, n-tile): contiguous runs of tiles per XCD (slot % 8); within a run, plain rows (n
+// fastest) or, for linear grids of at least BNN_MFMA_GROUP_MIN_TILES tiles (four or more rounds),
+// bands of BNN_MFMA_GROUP_M m-tiles walked m fastest, so the tiles an XCD runs at once share fewer
+// operand panels in its L2 (smaller grids lose more to the band arithmetic than they save).
+template <bool CONV>
+__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, const FastDiv& div_tn,
+                                            int slot, int& tm, int& tn) {
+  static_assert((BNN_MFMA_GROUP_M & (BNN_MFMA_GROUP_M - 1)) == 0, "bands of a power of two");
   const int total = tiles_m * tiles_n;
   int t = slot;
   if ((total & 7) == 0) t = (t & 7) * (total >> 3) + (t >> 3);
-  if (BNN_MFMA_GROUP_M > 1) {
-    const int band = BNN_MFMA_GROUP_M * tiles_n;
-    const int g = t / band, r = t - g * band;
-    const int m0 = g * BNN_MFMA_GROUP_M;
-    const int gm = tiles_m - m0 < BNN_MFMA_GROUP_M ? tiles_m - m0 : BNN_MFMA_GROUP_M;
-    tn = r / gm;
-    tm = m0 + (r - tn * gm);
+  if (!CONV && BNN_MFMA_GROUP_M > 1 && total >= BNN_MFMA_GROUP_MIN_TILES) {
+    constexpr int G = BNN_MFMA_GROUP_M > 1 ? BNN_MFMA_GROUP_M : 1;
+    constexpr int GS = G == 2 ? 1 : G == 4 ? 2 : G == 8 ? 3 : G == 16 ? 4 : 0;
+    const int g = div_tn.div(t >> GS);  // band: t / (G * tiles_n)
+    const int r = t - g * G * tiles_n;
+    const int m0 = g * G;
+    if (tiles_m - m0 >= G) {
+      tn = r >> GS;
+      tm = m0 + (r & (G - 1));
+    } else {  // the last, partial band
+      const int gm = tiles_m - m0;
+      tn = r / gm;
+      tm = m0 + (r - tn * gm);
+    }
   } else {
-    tm = t / tiles_n;
+    tm = div_tn.div(t);
     tn = t - tm * tiles_n;
   }
 }
@@ -592,7 +607,7 @@ __global__ __launch_bounds__(T::THREADS, T::OCC) void mfma_kernel(Contraction p)
   const int ntl = PERS ? (total - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x : 1;
   auto tile_origin = [&](int i, int& m0, int& n0) __attribute__((always_inline)) {
     int tm, tn;
-    tile_coords(tiles_m, tiles_n, (int)blockIdx.x + i * (int)gridDim.x, tm, tn);
+    tile_coords<CONV>(tiles_m, tiles_n, p.div_tn, (int)blockIdx.x + i * (int)gridDim.x, tm, tn);
     m0 = tm * T::BM;
     n0 = tn * T::BN;
   };
@@ -927,7 +942,9 @@ int persistent_slots() {
 }
 
 template <class T, int OUT, bool CONV, bool VEC>
-hipError_t launch_tile_o(const Contraction& p, hipStream_t stream) {
+hipError_t launch_tile_o(const Contraction& p0, hipStream_t stream) {
+  Contraction p = p0;
+  p.div_tn = FastDiv((uint32_t)((p.N + T::BN - 1) / T::BN));
   const int64_t tiles = (int64_t)((p.M + T::BM - 1) / T::BM) * ((p.N + T::BN - 1) / T::BN);
   const dim3 block(T::THREADS);
   if constexpr (CONV && T::F4 && T::THREADS == 512) {
