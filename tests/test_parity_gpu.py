@@ -189,6 +189,25 @@ def test_tile_variants_full(bnn, orc):
         assert torch.equal(got.cpu(), acc), path
 
 
+def test_banded_tile_order(bnn, orc):
+    """Linear grids of 1024 or more tiles walk bands of four m-tiles: 37 x 28 tiles of 256 x 256
+    (a last band of one m-tile; the count is not a multiple of 8, so no per-XCD runs) and, with
+    K = 96 (three words, no vector loads: 128 x 256 tiles), 66 x 32 tiles with ragged M and N (a
+    last band of two m-tiles, per-XCD runs); every accumulator against the oracle, so a tile
+    visited twice or never fails."""
+    g = torch.Generator().manual_seed(67)
+    for m, n, k in [(37 * 256, 28 * 256, 128), (32 * 256 + 100, 31 * 256 + 40, 96)]:
+        x = torch.randn((m, k), generator=g).half()
+        w = torch.randn((n, k), generator=g).half()
+        acc = orc.linear_acc(x, w)
+        xd, wp = x.to(DEV), bnn.w_pack(w.to(DEV))
+        _say(f"banded tile order {m}x{n}x{k}")
+        got = bnn.gemm(xd, wp, 1.0, 1.0, path="mfma_fp4", out_dtype=torch.int32)
+        torch.cuda.synchronize()
+        assert torch.equal(got.cpu(), acc), (m, n, k)
+        del got
+
+
 def test_persistent_conv_tiles(bnn, orc):
     """Conv shapes with more fp4 128 x 256 tiles than the GPU holds at once, which run as
     persistent workgroups streaming several tiles each (tile boundaries at every stage
@@ -212,8 +231,8 @@ def test_persistent_conv_tiles(bnn, orc):
 
 def test_two_round_conv_tiles(bnn, orc):
     """Conv shapes with two or more rounds of fp4 128 x 256 tiles, which run as 128 x 128 tiles of
-    four waves, two workgroups per compute unit (ragged last tile, ragged N, planes whose size is
-    not a multiple of 4 or 8): full oracle check."""
+    four waves with 4-word stages, three workgroups per compute unit (ragged last tile, ragged N,
+    planes whose size is not a multiple of 4 or 8): full oracle check."""
     g = torch.Generator().manual_seed(73)
     cases = [(88, 32, 28, 28, 256, 3, 1, 1, 1),    # 539 row tiles, planes of 784
              (96, 32, 27, 27, 200, 3, 1, 1, 1),    # 547 row tiles, ragged N, planes of 729
