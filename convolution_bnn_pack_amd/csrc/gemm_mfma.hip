@@ -68,6 +68,12 @@
 #define BNN_MFMA_GROUP_MIN_TILES 1024
 #endif
 
+// Tuning knob: conv A words of the tiles that share a compute unit three ways addressed by a
+// per-thread tap walk (1) or, like the other tiles, by dividing each stage's reduction index (0).
+#ifndef BNN_CONV_INC
+#define BNN_CONV_INC 1
+#endif
+
 // Tuning knob: a scheduling fence after every BNN_MFMA_SLOT_FENCE MFMA slots (0: none).
 #ifndef BNN_MFMA_SLOT_FENCE
 #define BNN_MFMA_SLOT_FENCE 4
@@ -618,6 +624,20 @@ __global__ __launch_bounds__(T::THREADS, T::OCC) void mfma_kernel(Contraction p)
   int am = 0, wn_row = 0;
   bool amok = false;
   PixelCoord pc{0, 0, 0};
+  // Conv tap walk (vector loads): this thread's next A load is word cw of tap (kh, kw) of its
+  // pixel, at activation row ih = ihb + kh*DH, column iw = iwb + kw*DW and word offset
+  // pix + toff + cw (pix: the pixel's (b, ihb, iwb) origin, toff: (kh*DH*W + kw*DW)*CW); each
+  // load advances it by one stage (KS words) with additions only, instead of two invariant
+  // divisions and three 64-bit products. Taken by the tiles sized for three workgroups per
+  // compute unit, whose loop is bound by vector-ALU issue (the dilated 128x128x28x28 -> 256
+  // layer: 33.3 -> 32.2 us); on the one-workgroup tiles it cost 1.5 %.
+  constexpr bool INC = CONV && VEC && BNN_CONV_INC && T::OCC > 1;
+  int tw_cw = 0, tw_kw = 0, tw_ih = 0, tw_iw = 0;
+  int64_t tw_pix = 0, tw_toff = 0;
+  // word offset steps of the walk: to the next kernel column, and from a row's last column to
+  // the next row's first
+  const int64_t tw_dcol = (int64_t)p.DW * p.CW;
+  const int64_t tw_drow = ((int64_t)p.DH * p.W - (int64_t)(p.KWD - 1) * p.DW) * p.CW;
   auto loader_tile = [&](int i) __attribute__((always_inline)) {  // A row, pixel and W row of this thread in tile i
     int m0, n0;
     tile_origin(i, m0, n0);
@@ -625,6 +645,16 @@ __global__ __launch_bounds__(T::THREADS, T::OCC) void mfma_kernel(Contraction p)
     wn_row = n0 + w_row;
     amok = am < p.M;
     if constexpr (CONV) pc = pixel_coord(p, amok ? am : 0);
+    if constexpr (INC) {
+      const int tap = p.div_cw.div(a_q);
+      tw_cw = a_q - tap * p.CW;
+      const int kh = p.div_kwd.div(tap);
+      tw_kw = tap - kh * p.KWD;
+      tw_ih = pc.ihb + kh * p.DH;
+      tw_iw = pc.iwb + tw_kw * p.DW;
+      tw_toff = ((int64_t)kh * p.DH * p.W + (int64_t)tw_kw * p.DW) * p.CW;
+      tw_pix = (((int64_t)pc.b * p.H + pc.ihb) * p.W + pc.iwb) * p.CW;
+    }
   };
   loader_tile(0);
   if constexpr (!PERS)
@@ -634,8 +664,31 @@ __global__ __launch_bounds__(T::THREADS, T::OCC) void mfma_kernel(Contraction p)
   // raw words of PD stages in flight; stage t lives in register set t % PD
   uint32_t ra[T::PD][T::A_WPT], rw[T::PD][T::W_WPT];
   bool oka[T::PD][T::A_WPT], okw[T::PD][T::W_WPT];
-  auto load_words = [&](int set, int q0) {
-    load_a<T::A_WPT, CONV, VEC>(p, am, amok, pc, q0 + a_q, ra[set], oka[set]);
+  auto load_words = [&](int set, int q0) __attribute__((always_inline)) {
+    if constexpr (INC) {
+      // q0 is always the walk's stage: loads go out stage by stage, and a new tile restarts
+      // the walk in loader_tile; this thread's words start at q0 + a_q (past K in a short
+      // last stage)
+      const bool tok = amok && q0 + a_q < p.KW && (unsigned)tw_ih < (unsigned)p.H &&
+                       (unsigned)tw_iw < (unsigned)p.W;
+      load_vec<T::A_WPT>(p.a + (tok ? tw_pix + tw_toff + tw_cw : 0), ra[set]);
+#pragma unroll
+      for (int i = 0; i < T::A_WPT; i++) oka[set][i] = tok;
+      tw_cw += T::KS;
+      // (every step updates every field, by value selects: stores on only one side of a
+      // branch would let the compiler select between the fields' addresses and keep them in
+      // scratch memory)
+      while (tw_cw >= p.CW) {
+        tw_cw -= p.CW;
+        const bool wrap = tw_kw + 1 == p.KWD;
+        tw_kw = wrap ? 0 : tw_kw + 1;
+        tw_iw = wrap ? pc.iwb : tw_iw + p.DW;
+        tw_ih += wrap ? p.DH : 0;
+        tw_toff += wrap ? tw_drow : tw_dcol;
+      }
+    } else {
+      load_a<T::A_WPT, CONV, VEC>(p, am, amok, pc, q0 + a_q, ra[set], oka[set]);
+    }
     load_w<T::W_WPT, VEC>(p, wn_row, q0 + w_q, rw[set], okw[set]);
   };
   // persistent stream position of the next loads: tile lt, stage ls
