@@ -1001,8 +1001,8 @@ hipError_t launch_tile_o(const Contraction& p0, hipStream_t stream) {
   const int64_t tiles = (int64_t)((p.M + T::BM - 1) / T::BM) * ((p.N + T::BN - 1) / T::BN);
   const dim3 block(T::THREADS);
   if constexpr (CONV && T::F4 && T::THREADS == 512) {
-    // (8-wave tiles only: the 4-wave conv tile runs two workgroups per compute unit instead,
-    // so one's epilogue overlaps the other's loop)
+    // (8-wave tiles only: the 4-wave conv tile runs three workgroups per compute unit instead,
+    // so one's epilogue overlaps the others' loops)
     // more fp4 conv tiles than fit at once: one persistent workgroup per resident slot
     // streams its tiles back to back instead of running them in separate rounds (the
     // int8 256 x 256 conv tile would spill with the extra state). Channel counts that are
