@@ -402,8 +402,22 @@ __global__ __launch_bounds__(256) void abs_mean_final_kernel(const double* __res
                                                              double factor,
                                                              double* __restrict__ out) {
   __shared__ double red[4];
+  // each thread adds partials threadIdx.x, +256, +512, ... in that order; sixteen of them are
+  // loaded at once (clamped, unconditional loads; the ones past the end add +0, which leaves
+  // the non-negative sum unchanged) so the loads' latency is paid once per sixteen, not each
+  constexpr int U = 16;
   double acc = 0.0;
-  for (int i = threadIdx.x; i < nparts; i += 256) acc += partial[i];
+  for (int i0 = threadIdx.x; i0 < nparts; i0 += 256 * U) {
+    double v[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const int i = i0 + 256 * u;
+      const double x = partial[i < nparts ? i : nparts - 1];
+      v[u] = i < nparts ? x : 0.0;
+    }
+#pragma unroll
+    for (int u = 0; u < U; u++) acc += v[u];
+  }
   const double t = block_sum_256(acc, red);
   if (threadIdx.x == 0) out[0] = factor * (t / count);
 }
